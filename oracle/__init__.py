@@ -1,0 +1,138 @@
+"""ctypes loader for the CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py``; the product package never imports it.  See ``oracle.h`` for
+the definitions and the readings of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from oracle.build import build
+            build()
+        lib = C.CDLL(LIB_PATH)
+        P = C.c_void_p
+        i64, i32 = C.c_int64, C.c_int32
+        lib.oracle_build_graph.argtypes = [i64, P, i32, P, i32, C.POINTER(P)]
+        lib.oracle_graph_free.argtypes = [P]
+        lib.oracle_graph_n.argtypes = [P]
+        lib.oracle_graph_n.restype = i64
+        lib.oracle_graph_nnz.argtypes = [P]
+        lib.oracle_graph_nnz.restype = i64
+        lib.oracle_graph_export.argtypes = [P, P, P, P]
+        lib.oracle_num_configs.argtypes = [i32, i32]
+        lib.oracle_num_configs.restype = i64
+        lib.oracle_count_3pcf.argtypes = [P, P, i64, i32, P, P, P, P]
+        lib.oracle_count_3pcf_exact.argtypes = [P, P, i64, i32, P, P, P]
+        lib.oracle_count_4pcf_parity.argtypes = [P, P, i64, i32, P, P, P]
+        lib.oracle_forward_degrees.argtypes = [P, P]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def num_configs(order: int, nbins: int) -> int:
+    return int(_load().oracle_num_configs(order, nbins))
+
+
+class Graph:
+    """Oracle neighbour graph (caller's labels, full symmetric adjacency, rows ascending)."""
+
+    def __init__(self, xyz: np.ndarray, edges_sq, nthreads: int = 0):
+        lib = _load()
+        self.xyz = np.ascontiguousarray(xyz, dtype=np.int32).reshape(-1, 3)
+        self.edges = np.ascontiguousarray(np.asarray(edges_sq, dtype=np.int64))
+        self.nbins = int(self.edges.size - 1)
+        h = C.c_void_p()
+        rc = lib.oracle_build_graph(self.xyz.shape[0], _ptr(self.xyz), self.nbins,
+                                    _ptr(self.edges), nthreads, C.byref(h))
+        if rc:
+            raise ValueError(f"oracle_build_graph failed ({rc})")
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.oracle_graph_free(self._h)
+            self._h = None
+
+    @property
+    def n(self) -> int:
+        return int(_lib.oracle_graph_n(self._h))
+
+    @property
+    def nnz(self) -> int:
+        return int(_lib.oracle_graph_nnz(self._h))
+
+    def export(self):
+        rp = np.empty(self.n + 1, np.int64)
+        col = np.empty(max(self.nnz, 1), np.int32)
+        b = np.empty(max(self.nnz, 1), np.uint8)
+        assert _lib.oracle_graph_export(self._h, _ptr(rp), _ptr(col), _ptr(b)) == 0
+        return rp, col[: self.nnz], b[: self.nnz]
+
+    def forward_degrees(self) -> np.ndarray:
+        d = np.empty(self.n, np.int32)
+        assert _lib.oracle_forward_degrees(self._h, _ptr(d)) == 0
+        return d
+
+    def count_3pcf(self, w: np.ndarray | None = None, hub_stride: int = 1, nthreads: int = 0):
+        """Returns (counts uint64[n_cfg], weighted fp64[n_cfg] or None, scale s, walks)."""
+        ncfg = num_configs(3, self.nbins)
+        counts = np.zeros(ncfg, np.uint64)
+        weighted = None if w is None else np.zeros(ncfg, np.float64)
+        wa = None if w is None else np.ascontiguousarray(w, dtype=np.float64)
+        s = C.c_int32(0)
+        walks = C.c_uint64(0)
+        rc = _lib.oracle_count_3pcf(self._h, _ptr(wa), hub_stride, nthreads, _ptr(counts),
+                                    _ptr(weighted), C.byref(s), C.byref(walks))
+        if rc:
+            raise ValueError(f"oracle_count_3pcf failed ({rc})")
+        return counts, weighted, int(s.value), int(walks.value)
+
+    def count_3pcf_exact(self, w: np.ndarray, hub_stride: int = 1, nthreads: int = 0):
+        """Returns (counts, exact integer sums of q as Python ints, scale s)."""
+        ncfg = num_configs(3, self.nbins)
+        counts = np.zeros(ncfg, np.uint64)
+        q = np.zeros(2 * ncfg, np.int64)
+        wa = np.ascontiguousarray(w, dtype=np.float64)
+        s = C.c_int32(0)
+        rc = _lib.oracle_count_3pcf_exact(self._h, _ptr(wa), hub_stride, nthreads, _ptr(counts),
+                                          _ptr(q), C.byref(s))
+        if rc:
+            raise ValueError(f"oracle_count_3pcf_exact failed ({rc})")
+        u = q.view(np.uint64)
+        sums = []
+        for c in range(ncfg):
+            v = int(u[2 * c]) | (int(u[2 * c + 1]) << 64)
+            if v >= 1 << 127:
+                v -= 1 << 128
+            sums.append(v)
+        return counts, sums, int(s.value)
+
+    def count_4pcf_parity(self, hub_stride: int = 1, nthreads: int = 0):
+        """Returns (even uint64[n_cfg], odd int64[n_cfg], number of 4-cliques)."""
+        ncfg = num_configs(4, self.nbins)
+        even = np.zeros(ncfg, np.uint64)
+        odd = np.zeros(ncfg, np.int64)
+        cl = C.c_uint64(0)
+        rc = _lib.oracle_count_4pcf_parity(self._h, _ptr(self.xyz), hub_stride, nthreads,
+                                           _ptr(even), _ptr(odd), C.byref(cl))
+        if rc:
+            raise ValueError(f"oracle_count_4pcf_parity failed ({rc})")
+        return even, odd, int(cl.value)

@@ -1,0 +1,93 @@
+"""Brute-force definitions for tiny point sets: every pair, every triple, every 4-set.
+
+These pin the oracle.  They share no code with it: pairwise squared distances come from NumPy,
+triangles and tetrahedra from exhaustive loops over index combinations, configuration ranks from
+``itertools.combinations_with_replacement`` (which yields nondecreasing tuples in lexicographic
+order), and weighted sums from exact rational arithmetic (``fractions.Fraction``).
+"""
+from __future__ import annotations
+
+import itertools
+from fractions import Fraction
+
+import numpy as np
+
+
+def sq_dists(xyz: np.ndarray) -> np.ndarray:
+    x = xyz.astype(np.int64)
+    d = x[:, None, :] - x[None, :, :]
+    return (d * d).sum(axis=2)
+
+
+def adjacency(xyz: np.ndarray, edges) -> tuple[np.ndarray, np.ndarray]:
+    """(A bool [n,n], B int [n,n]) with A[i,j] iff i != j and e_0 <= d^2 < e_nb, B the bin."""
+    e = np.asarray(edges, dtype=np.int64)
+    d2 = sq_dists(xyz)
+    n = xyz.shape[0]
+    a = (d2 >= e[0]) & (d2 < e[-1]) & ~np.eye(n, dtype=bool)
+    b = np.searchsorted(e, d2, side="right") - 1
+    return a, b
+
+
+def config_index(nbins: int, k: int) -> dict:
+    return {t: r for r, t in enumerate(itertools.combinations_with_replacement(range(nbins), k))}
+
+
+def triangles(xyz: np.ndarray, edges, w=None):
+    """Every pairwise-adjacent triple once.  Returns (counts, weighted_fl, weighted_exact) where
+    weighted_fl sums fl(fl(w1*w2)*w3) (weights ascending) exactly and rounds once, and
+    weighted_exact is the correctly rounded exact real sum of w_i w_j w_k."""
+    a, b = adjacency(xyz, edges)
+    nb = len(edges) - 1
+    idx = config_index(nb, 3)
+    counts = np.zeros(len(idx), np.uint64)
+    acc_fl = [Fraction(0)] * len(idx)
+    acc_ex = [Fraction(0)] * len(idx)
+    n = xyz.shape[0]
+    for i, j, k in itertools.combinations(range(n), 3):
+        if a[i, j] and a[i, k] and a[j, k]:
+            c = idx[tuple(sorted((int(b[i, j]), int(b[i, k]), int(b[j, k]))))]
+            counts[c] += 1
+            if w is not None:
+                w1, w2, w3 = sorted((float(w[i]), float(w[j]), float(w[k])))
+                acc_fl[c] += Fraction((w1 * w2) * w3)
+                acc_ex[c] += Fraction(w[i]) * Fraction(w[j]) * Fraction(w[k])
+    if w is None:
+        return counts, None, None
+    return counts, np.array([float(x) for x in acc_fl]), np.array([float(x) for x in acc_ex])
+
+
+def _det3(m) -> int:
+    return (m[0][0] * (m[1][1] * m[2][2] - m[1][2] * m[2][1])
+            - m[0][1] * (m[1][0] * m[2][2] - m[1][2] * m[2][0])
+            + m[0][2] * (m[1][0] * m[2][1] - m[1][1] * m[2][0]))
+
+
+def chirality(pts) -> int:
+    """Sign of the signed volume with vertices ordered by their summed squared edge lengths;
+    0 if two such sums tie or the volume is zero.  ``pts`` are four integer 3-vectors."""
+    p = [tuple(int(c) for c in q) for q in pts]
+    key = [sum(sum((p[v][t] - p[u][t]) ** 2 for t in range(3)) for u in range(4)) for v in range(4)]
+    order = sorted(range(4), key=lambda v: key[v])
+    if len(set(key)) < 4:
+        return 0
+    o = [p[v] for v in order]
+    m = [[o[r + 1][t] - o[0][t] for t in range(3)] for r in range(3)]
+    v = _det3(m)
+    return (v > 0) - (v < 0)
+
+
+def cliques4(xyz: np.ndarray, edges):
+    """Every pairwise-adjacent 4-set once: (even uint64[n_cfg], odd int64[n_cfg])."""
+    a, b = adjacency(xyz, edges)
+    nb = len(edges) - 1
+    idx = config_index(nb, 6)
+    even = np.zeros(len(idx), np.uint64)
+    odd = np.zeros(len(idx), np.int64)
+    n = xyz.shape[0]
+    for q in itertools.combinations(range(n), 4):
+        if all(a[u, v] for u, v in itertools.combinations(q, 2)):
+            c = idx[tuple(sorted(int(b[u, v]) for u, v in itertools.combinations(q, 2)))]
+            even[c] += 1
+            odd[c] += chirality([xyz[v] for v in q])
+    return even, odd

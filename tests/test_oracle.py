@@ -1,0 +1,368 @@
+"""Pins for the CPU oracle, each against something other than the oracle itself: brute force over
+every triple / 4-set, exact rational sums, closed forms, library routines (scipy sparse products,
+networkx) and invariances that the definitions imply.  CPU only.
+"""
+from __future__ import annotations
+
+import itertools
+from math import comb
+
+import numpy as np
+import pytest
+
+import brute
+import oracle
+from workloads import GRID, linear_edges_sq, rng_for
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+def small_cloud(seed, n, box, nclump=0):
+    """n points in a small box (so many are neighbours), optionally with coincident points."""
+    rng = rng_for(seed)
+    lo = rng.integers(0, GRID - box + 1)
+    xyz = lo + rng.integers(0, box, size=(n, 3))
+    if nclump:
+        xyz[rng.integers(0, n, nclump)] = xyz[0]
+    return np.ascontiguousarray(xyz.astype(np.int32))
+
+
+def rank3(nb):
+    return brute.config_index(nb, 3)
+
+
+def rank6(nb):
+    return brute.config_index(nb, 6)
+
+
+# ------------------------------------------------------------------ graph vs brute force
+
+@pytest.mark.parametrize("seed,n,box,nb", [(1, 40, 2000, 1), (2, 90, 3000, 4), (3, 120, (1 << 20) - 1, 7),
+                                           (4, 70, 600, 3)])
+def test_graph_matches_brute_force(seed, n, box, nb):
+    xyz = small_cloud(seed, n, box, nclump=3)
+    edges = linear_edges_sq(box // 2 + 7, nb)
+    g = oracle.Graph(xyz, edges)
+    rp, col, b = g.export()
+    a, bb = brute.adjacency(xyz, edges)
+    for i in range(n):
+        row = col[rp[i]:rp[i + 1]]
+        assert np.all(np.diff(row) > 0), "rows must be strictly ascending (Eq. 1)"
+        np.testing.assert_array_equal(row, np.nonzero(a[i])[0])
+        np.testing.assert_array_equal(b[rp[i]:rp[i + 1]], bb[i, row])
+
+
+def test_graph_exact_boundaries():
+    # points at squared distance exactly e_b land in bin b; exactly r^2 is not a neighbour
+    edges = np.array([0, 100, 400, 900], np.int64)
+    base = np.array([5000, 5000, 5000])
+    pts = [base, base + [10, 0, 0], base + [0, 20, 0], base + [0, 0, 30], base + [0, 0, 29]]
+    xyz = np.array(pts, np.int32)
+    g = oracle.Graph(xyz, edges)
+    rp, col, b = g.export()
+    row0 = dict(zip(col[rp[0]:rp[1]].tolist(), b[rp[0]:rp[1]].tolist()))
+    assert row0 == {1: 1, 2: 2, 4: 2}  # d2=100 -> bin 1, 400 -> bin 2, 900 excluded, 841 -> bin 2
+
+
+# ------------------------------------------------------------------ 3pCF vs brute force
+
+@pytest.mark.parametrize("seed,n,box,nb", [(11, 30, 1500, 1), (12, 80, 2500, 3), (13, 120, 4000, 6),
+                                           (14, 60, 800, 10)])
+def test_3pcf_matches_brute_force(seed, n, box, nb):
+    xyz = small_cloud(seed, n, box, nclump=2)
+    edges = linear_edges_sq(box // 2, nb)
+    w = 0.5 + rng_for(seed + 100).random(n)
+    cnt_b, wfl_b, wex_b = brute.triangles(xyz, edges, w)
+    g = oracle.Graph(xyz, edges)
+    cnt, wsum, s, walks = g.count_3pcf(w)
+    np.testing.assert_array_equal(cnt, cnt_b)
+    np.testing.assert_array_equal(wsum, wfl_b)  # same products, exact sum, one rounding
+    np.testing.assert_allclose(wsum, wex_b, rtol=1e-15, atol=0)
+    assert s == 55
+    assert walks == g.nnz // 2
+    cnt2, _, _, _ = g.count_3pcf(None, nthreads=1)
+    np.testing.assert_array_equal(cnt2, cnt_b)
+
+
+def test_3pcf_signed_weights_match_brute_force():
+    # signed weights as in the data-minus-random estimator (§II.1); products are exact at this scale
+    xyz = small_cloud(21, 70, 2500)
+    edges = linear_edges_sq(1300, 4)
+    rng = rng_for(22)
+    w = np.where(rng.random(70) < 0.5, -1.0, 1.0) * (0.25 + rng.random(70))
+    cnt_b, wfl_b, _ = brute.triangles(xyz, edges, w)
+    g = oracle.Graph(xyz, edges)
+    cnt, wsum, s, _ = g.count_3pcf(w)
+    np.testing.assert_array_equal(cnt, cnt_b)
+    np.testing.assert_array_equal(wsum, wfl_b)
+
+
+# ------------------------------------------------------------------ 4pCF vs brute force
+
+@pytest.mark.parametrize("seed,n,box,nb", [(31, 24, 1500, 1), (32, 32, 2500, 2), (33, 36, 3000, 4)])
+def test_4pcf_matches_brute_force(seed, n, box, nb):
+    xyz = small_cloud(seed, n, box, nclump=0)
+    edges = linear_edges_sq(box * 3 // 4, nb)
+    even_b, odd_b = brute.cliques4(xyz, edges)
+    g = oracle.Graph(xyz, edges)
+    even, odd, ncl = g.count_4pcf_parity()
+    np.testing.assert_array_equal(even, even_b)
+    np.testing.assert_array_equal(odd, odd_b)
+    assert ncl == int(even_b.sum())
+    assert ncl > 0
+
+
+# ------------------------------------------------------------------ closed forms
+
+def test_clique_closed_form():
+    # K points within a tiny ball: every pair is a neighbour in bin 0 -> C(K,3) / C(K,4)
+    k = 25
+    rng = rng_for(41)
+    xyz = (500000 + rng.integers(0, 40, size=(k, 3))).astype(np.int32)
+    edges = np.array([0, 10_000, 40_000], np.int64)
+    g = oracle.Graph(xyz, edges)
+    cnt, _, _, _ = g.count_3pcf()
+    assert cnt[rank3(2)[(0, 0, 0)]] == comb(k, 3) and cnt.sum() == comb(k, 3)
+    even, odd, _ = g.count_4pcf_parity()
+    assert even[rank6(2)[(0,) * 6]] == comb(k, 4) and even.sum() == comb(k, 4)
+
+
+def regular_tetra(a):
+    return np.array([[0, 0, 0], [a, a, 0], [a, 0, a], [0, a, a]], np.int64)
+
+
+def test_regular_tetrahedra_closed_form():
+    # K isolated regular tetrahedra (all six d^2 = 2a^2): 4K triangles and K cliques in the
+    # (b,b,b) / (b,)*6 configuration; every vertex key ties, so the odd channel is zero.
+    a, k, nb = 1000, 12, 5
+    edges = linear_edges_sq(2000, nb)  # r = 2000 > a*sqrt(2) = 1414
+    b = int(np.searchsorted(edges, 2 * a * a, side="right") - 1)
+    units = [regular_tetra(a) + [50_000 * (t + 1), 50_000, 70_000] for t in range(k)]
+    xyz = np.concatenate(units).astype(np.int32)
+    g = oracle.Graph(xyz, edges)
+    cnt, _, _, _ = g.count_3pcf()
+    assert cnt[rank3(nb)[(b, b, b)]] == 4 * k and cnt.sum() == 4 * k
+    even, odd, _ = g.count_4pcf_parity()
+    assert even[rank6(nb)[(b,) * 6]] == k and even.sum() == k
+    assert np.all(odd == 0)
+
+
+def test_isolated_pairs_have_no_triangles():
+    # the pages' isolated-pair regression case (§IV.8): pairs far apart -> zero triangles
+    xyz = np.array([[t * 10_000, 0, 0] for t in range(50)] + [[t * 10_000 + 5, 0, 0] for t in range(50)],
+                   np.int32)
+    g = oracle.Graph(xyz, linear_edges_sq(100, 3))
+    assert g.nnz == 100
+    cnt, _, _, _ = g.count_3pcf()
+    assert cnt.sum() == 0
+
+
+SCALENE = np.array([[0, 0, 0], [1000, 0, 0], [130, 1700, 0], [410, 520, 2300]], np.int64)
+
+
+def proper_rotations():
+    """The 24 proper rotations of the cube (signed permutation matrices with det +1)."""
+    out = []
+    for perm in itertools.permutations(range(3)):
+        for signs in itertools.product((1, -1), repeat=3):
+            m = np.zeros((3, 3), np.int64)
+            for r, c in enumerate(perm):
+                m[r, c] = signs[r]
+            if round(np.linalg.det(m)) == 1:
+                out.append(m)
+    return out
+
+
+def test_parity_injection_count_level_identity():
+    # §IV.9: isolated scalene tetrahedra, n_l of one handedness and n_r mirrored; the odd channel
+    # at the injected configuration is exactly +-(n_l - n_r), the even channel n_l + n_r.
+    rots = proper_rotations()
+    mirror = np.diag([-1, 1, 1])
+    n_l, n_r = 17, 6
+    units = []
+    rng = rng_for(51)
+    for t in range(n_l + n_r):
+        rot = rots[int(rng.integers(len(rots)))]
+        shape = SCALENE @ rot.T
+        if t >= n_l:
+            shape = shape @ mirror.T
+        units.append(shape - shape.min(axis=0) + [40_000 * (t + 1), 200_000, 300_000])
+    xyz = np.concatenate(units).astype(np.int32)
+    nb = 6
+    edges = linear_edges_sq(3200, nb)
+    g = oracle.Graph(xyz, edges)
+    even, odd, ncl = g.count_4pcf_parity()
+    assert ncl == n_l + n_r
+    c = int(np.nonzero(even)[0][0])
+    assert even[c] == n_l + n_r and even.sum() == n_l + n_r
+    assert abs(int(odd[c])) == n_l - n_r and int(odd.sum()) == int(odd[c])
+    s = brute.chirality(SCALENE)
+    assert s != 0 and int(odd[c]) == s * (n_l - n_r)
+
+
+# ------------------------------------------------------------------ library cross-checks
+
+def uniform_graph(seed=61, n=3000, box=200_000, r=20_000, nb=8):
+    rng = rng_for(seed)
+    xyz = (300_000 + rng.integers(0, box, size=(n, 3))).astype(np.int32)
+    return xyz, linear_edges_sq(r, nb)
+
+
+def test_total_equals_trace_a_cubed():
+    # the histogram total is the number of triangles = trace(A^3)/6 (scipy sparse products)
+    import scipy.sparse as sp
+    xyz, edges = uniform_graph()
+    g = oracle.Graph(xyz, edges)
+    rp, col, _ = g.export()
+    a = sp.csr_matrix((np.ones(col.size, np.int64), col, rp), shape=(g.n, g.n))
+    t = int((a @ a).multiply(a).sum()) // 6
+    cnt, _, _, _ = g.count_3pcf()
+    assert int(cnt.sum()) == t and t > 1000
+    # and = sum over undirected edges of common neighbours / 3
+    deg = g.forward_degrees()
+    assert int(deg.sum()) == g.nnz // 2
+
+
+def test_totals_match_networkx():
+    import networkx as nx
+    xyz, edges = uniform_graph(seed=62, n=700, box=120_000, r=22_000)
+    g = oracle.Graph(xyz, edges)
+    rp, col, _ = g.export()
+    G = nx.Graph()
+    G.add_nodes_from(range(g.n))
+    for i in range(g.n):
+        G.add_edges_from((i, int(j)) for j in col[rp[i]:rp[i + 1]] if j > i)
+    tri = sum(nx.triangles(G).values()) // 3
+    k4 = sum(1 for c in nx.enumerate_all_cliques(G) if len(c) == 4)
+    cnt, _, _, _ = g.count_3pcf()
+    even, _, ncl = g.count_4pcf_parity()
+    assert int(cnt.sum()) == tri and int(even.sum()) == k4 == ncl and k4 > 100
+
+
+# ------------------------------------------------------------------ invariances
+
+def cluster_set(seed=71, n=900):
+    rng = rng_for(seed)
+    centres = 200_000 + rng.integers(0, 400_000, size=(30, 3))
+    xyz = centres[rng.integers(0, 30, n)] + rng.normal(0, 4000, size=(n, 3))
+    return np.clip(np.rint(xyz), 0, GRID - 1).astype(np.int32)
+
+
+def all_outputs(xyz, edges, w):
+    g = oracle.Graph(xyz, edges)
+    cnt, ws, _, _ = g.count_3pcf(w)
+    even, odd, _ = g.count_4pcf_parity()
+    return cnt, ws, even, odd
+
+
+def test_relabelling_invariance():
+    xyz = cluster_set()
+    edges = linear_edges_sq(9000, 6)
+    w = 0.5 + rng_for(72).random(xyz.shape[0])
+    base = all_outputs(xyz, edges, w)
+    perm = rng_for(73).permutation(xyz.shape[0])
+    other = all_outputs(np.ascontiguousarray(xyz[perm]), edges, w[perm])
+    for x, y in zip(base, other):
+        np.testing.assert_array_equal(x, y)
+    assert base[3].any(), "need a non-zero odd channel for this check to mean anything"
+
+
+def test_mirror_and_axis_symmetries():
+    xyz = cluster_set(74)
+    edges = linear_edges_sq(9000, 6)
+    cnt, _, even, odd = all_outputs(xyz, edges, None)
+    assert np.abs(odd).sum() > 0
+    mirrored = xyz.copy()
+    mirrored[:, 0] = GRID - 1 - mirrored[:, 0]
+    c2, _, e2, o2 = all_outputs(mirrored, edges, None)
+    np.testing.assert_array_equal(c2, cnt)
+    np.testing.assert_array_equal(e2, even)
+    np.testing.assert_array_equal(o2, -odd)
+    swapped = np.ascontiguousarray(xyz[:, [1, 0, 2]])
+    _, _, e3, o3 = all_outputs(swapped, edges, None)
+    np.testing.assert_array_equal(e3, even)
+    np.testing.assert_array_equal(o3, -odd)
+    cyc = np.ascontiguousarray(xyz[:, [1, 2, 0]])
+    _, _, e4, o4 = all_outputs(cyc, edges, None)
+    np.testing.assert_array_equal(e4, even)
+    np.testing.assert_array_equal(o4, odd)
+
+
+def test_translation_and_scaling():
+    xyz = cluster_set(75)
+    edges = linear_edges_sq(9000, 6)
+    cnt, _, even, odd = all_outputs(xyz, edges, None)
+    shift = np.array([1234, -5678, 91011])
+    moved = xyz.astype(np.int64) + shift
+    assert moved.min() >= 0 and moved.max() < GRID
+    c2, _, e2, o2 = all_outputs(moved.astype(np.int32), edges, None)
+    np.testing.assert_array_equal(c2, cnt)
+    np.testing.assert_array_equal(e2, even)
+    np.testing.assert_array_equal(o2, odd)
+    half = (xyz // 2 * 2).astype(np.int64)  # even coordinates, then scale up by 2 with edges x4
+    ch, _, eh, oh = all_outputs((half // 2).astype(np.int32), edges, None)
+    cd, _, ed, od = all_outputs(half.astype(np.int32), edges * 4, None)
+    np.testing.assert_array_equal(ch, cd)
+    np.testing.assert_array_equal(eh, ed)
+    np.testing.assert_array_equal(oh, od)
+
+
+def test_constant_weights():
+    xyz = cluster_set(76, 600)
+    edges = linear_edges_sq(9000, 5)
+    g = oracle.Graph(xyz, edges)
+    cnt, w1, _, _ = g.count_3pcf(np.ones(g.n))
+    np.testing.assert_array_equal(w1, cnt.astype(np.float64))
+    _, w2, s, _ = g.count_3pcf(np.full(g.n, 2.0))
+    np.testing.assert_array_equal(w2, 8.0 * cnt.astype(np.float64))
+    _, wz, _, _ = g.count_3pcf(np.zeros(g.n))
+    assert np.all(wz == 0)
+
+
+def test_exact_sums_are_the_rounded_weighted_output():
+    xyz = cluster_set(77, 500)
+    edges = linear_edges_sq(9000, 4)
+    w = 0.5 + rng_for(78).random(xyz.shape[0])
+    g = oracle.Graph(xyz, edges)
+    cnt, sums, s = g.count_3pcf_exact(w)
+    _, wsum, s2, _ = g.count_3pcf(w)
+    assert s == s2 == 55
+    for c in range(cnt.size):
+        assert wsum[c] == float(sums[c]) * 2.0 ** -s  # Python int -> float is correctly rounded
+
+
+def test_hub_stride_partitions_by_smallest_label():
+    xyz, edges = uniform_graph(seed=79, n=1500)
+    g = oracle.Graph(xyz, edges)
+    full, _, _, walks = g.count_3pcf()
+    part, _, _, w2 = g.count_3pcf(hub_stride=3)
+    assert np.all(part <= full) and 0 < part.sum() < full.sum() and 0 < w2 < walks
+
+
+def test_degenerate_inputs():
+    edges = linear_edges_sq(1000, 3)
+    for n in (0, 1, 2):
+        xyz = np.zeros((n, 3), np.int32)
+        g = oracle.Graph(xyz, edges)
+        cnt, _, _, _ = g.count_3pcf()
+        even, odd, _ = g.count_4pcf_parity()
+        assert cnt.sum() == 0 and even.sum() == 0
+    with pytest.raises(ValueError):
+        oracle.Graph(np.array([[GRID, 0, 0]], np.int32), edges)
+    with pytest.raises(ValueError):
+        oracle.Graph(np.zeros((3, 3), np.int32), np.array([0, 5, 5], np.int64))
+
+
+def test_coplanar_tetrahedra_have_no_chirality():
+    # §III.2: zero signed volume -> zero weight in the odd channel, even channel unaffected.
+    # Scalene planar quadrilaterals (distinct vertex keys), several orientations.
+    planar = np.array([[0, 0, 0], [1000, 0, 0], [130, 1700, 0], [900, 1300, 0]], np.int64)
+    assert len({sum(int(((planar[v] - planar[u]) ** 2).sum()) for u in range(4)) for v in range(4)}) == 4
+    units = []
+    for t, rot in enumerate(proper_rotations()[:10]):
+        shape = planar @ rot.T
+        units.append(shape - shape.min(axis=0) + [60_000 * (t + 1), 300_000, 300_000])
+    xyz = np.concatenate(units).astype(np.int32)
+    g = oracle.Graph(xyz, linear_edges_sq(3000, 4))
+    even, odd, ncl = g.count_4pcf_parity()
+    assert ncl == 10 and even.sum() == 10 and np.all(odd == 0)
