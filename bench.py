@@ -1,0 +1,167 @@
+"""Benchmark of the graph 3pCF hot path on one MI355X.
+
+One step = the whole path on one resident synthetic workload: build the neighbour graph on the GPU
+(cell list, pair search, CSR emit, degree statistics, hub order), count the binned triangles
+(weighted when the workload has weights), and release the graph.  Inputs (coordinates, weights)
+are in HBM before the timed region starts.
+
+Prints one JSON line: triplets/s for the whole step (value), hub-spoke merge-walks/s, the
+enumeration kernel's algorithmic-bytes roofline, and the CPU oracle timed on a bounded sample of
+the same workload on this host's cores.
+
+    python bench.py [--config C2] [--steps 5] [--warmup 1] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+# CPU-baseline sample per workload: (sub-box side as a fraction of the grid, hub stride)
+CPU_SAMPLE = {"C1": (1.0, 1), "C2": (1.0, 1), "C3": (1 / 3, 16), "C4": (1.0, 2), "C5": (1 / 3, 4)}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="C2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the counter has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import graph_triangle_counting_amd as gtc
+    import workloads
+
+    cfg = workloads.get(args.config)
+    if cfg.order != 3:
+        print("bench.py measures the 3pCF path; pick a 3pCF workload (C1, C2, C3, C5)",
+              file=sys.stderr)
+        sys.exit(2)
+    log(f"[bench] generating {cfg.key} {cfg.name} n={cfg.n}")
+    xyz_np, w_np = cfg.generate()
+    edges = cfg.edges_sq()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    xyz = torch.from_numpy(xyz_np).to(dev)
+    w = None if w_np is None else torch.from_numpy(w_np).to(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        g = gtc.Graph(xyz, edges)
+        c, ws, st = g.count_3pcf(w)
+        gst = g.stats()
+        g.close()
+        return st, gst
+
+    for k in range(args.warmup):
+        st, gst = step()
+        log(f"[bench] warmup {k}: build {gst['build_ms']:.2f} ms, kernel {st['kernel_ms']:.2f} ms, "
+            f"T={st['triangles']}")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    kms, bms, tris, walks, qalg = [], [], [], [], []
+    for k in range(args.steps):
+        st, gst = step()
+        kms.append(st["kernel_ms"])
+        bms.append(gst["build_ms"])
+        tris.append(st["triangles"])
+        walks.append(st["merge_walks"])
+        qalg.append(st["q_alg_bytes"])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = 1e3 * elapsed / args.steps
+    assert len(set(tris)) == 1, "triangle counts differ between steps"
+    T = tris[0]
+    value = T * args.steps / elapsed
+    k_avg = sum(kms) / len(kms)
+    achieved = qalg[0] / (k_avg * 1e-3) / 1e9
+    log(f"[bench] {args.steps} steps: {ms_step:.2f} ms/step, build {sum(bms)/len(bms):.2f} ms, "
+        f"kernel {k_avg:.3f} ms, T={T}, E={st['edges']}")
+
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "k_triplet", "kernel_ms": k_avg, "q_alg_bytes": qalg[0]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, xyz_np, w_np, args.cpu_threads)
+
+    out = {
+        "metric": "triplets counted/sec and hub-spoke merge-walks/sec (3pCF), 1 MI355X",
+        "value": value,
+        "unit": "triplets/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int64+f64" if cfg.weighted else "int64",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.key} {cfg.name}", "n_points": cfg.n, "kind": cfg.kind,
+                   "r_max": cfg.r, "nbins": cfg.nbins, "weighted": cfg.weighted,
+                   "mean_degree_target": cfg.target_degree, "edges": st["edges"],
+                   "triangles": T, "merge_walks": walks[0]},
+        "merge_walks_per_s": walks[0] * args.steps / elapsed,
+        "kernel_triplets_per_s": T / (k_avg * 1e-3),
+        "build_ms": sum(bms) / len(bms),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, xyz, w, threads):
+    """The oracle, as it is, on a bounded sample of the same workload, on this host's cores."""
+    import numpy as np
+
+    import oracle
+    frac, stride = CPU_SAMPLE[cfg.key]
+    if frac < 1.0:
+        xyz, w = cfg.crop(xyz, w, frac)
+    nthreads = threads or (os.cpu_count() or 1)
+    try:
+        nthreads = min(nthreads, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        pass
+    log(f"[bench] cpu baseline: oracle on {xyz.shape[0]} points, hub stride {stride}, "
+        f"{nthreads} threads")
+    t0 = time.perf_counter()
+    g = oracle.Graph(xyz, cfg.edges_sq(), nthreads=nthreads)
+    tb = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    c, _, _, walks = g.count_3pcf(w, hub_stride=stride, nthreads=nthreads)
+    tc = time.perf_counter() - t0
+    T = int(np.asarray(c, dtype=np.uint64).sum())
+    sample = (f"{'full point set' if frac >= 1 else f'central sub-box of side {frac:.3f} L, full density'}"
+              f" ({xyz.shape[0]} points); triangles of every {stride}-th hub label"
+              f"{' (all hubs)' if stride == 1 else ''}; count phase {tc:.2f} s, graph build "
+              f"{tb:.2f} s")
+    return {"value": T / tc, "unit": "triplets/s", "cores": nthreads, "kind": "oracle",
+            "sample": sample, "merge_walks_per_s": walks / tc, "triangles": T,
+            "count_s": tc, "build_s": tb}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+"""Python binding of libgtc, the MI355X graph 3pCF / 4pCF counter (GRAMSCI v2 method).
+
+Argument marshalling only: every step of the counting runs in the HIP kernels of libgtc.so,
+called through its C ABI (include/gtc.h).  PyTorch supplies device memory and the current
+stream.  Importing succeeds without the library (so CPU-only tooling can inspect the package),
+but every call raises if libgtc.so is absent: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libgtc.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "gtc.h")
+
+GTC_OK, GTC_E_INVALID, GTC_E_OOM, GTC_E_HIP, GTC_E_OVERFLOW, GTC_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+
+
+class GtcError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{detail} (status {status})")
+        self.status = status
+
+
+class Options(C.Structure):
+    _fields_ = [("tile_bytes", C.c_int64), ("host_csr", C.c_int32), ("drop_coords", C.c_int32)]
+
+
+class Stats(C.Structure):
+    _fields_ = [("n", C.c_int64), ("edges", C.c_int64), ("max_out_degree", C.c_int64),
+                ("merge_walks", C.c_int64), ("spoke_elements", C.c_int64), ("tiles", C.c_int64),
+                ("windows", C.c_int64), ("triangles", C.c_uint64), ("cliques4", C.c_uint64),
+                ("q_alg_bytes", C.c_double), ("weight_scale", C.c_int32),
+                ("reserved", C.c_int32), ("build_ms", C.c_double), ("kernel_ms", C.c_double),
+                ("count_ms", C.c_double), ("h2d_ms", C.c_double)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libgtc.so (built in-tree by graph_triangle_counting_amd/_build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python graph_triangle_counting_amd/_build.py`")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+        L.gtc_build_graph.argtypes = [P, i64, P, i32, C.POINTER(Options), P, C.POINTER(P)]
+        L.gtc_count_3pcf.argtypes = [P, P, P, P, C.POINTER(Stats), P]
+        L.gtc_count_4pcf_parity.argtypes = [P, P, P, C.POINTER(Stats), P]
+        L.gtc_num_configs.argtypes = [i32, i32]
+        L.gtc_num_configs.restype = i64
+        L.gtc_config_bins.argtypes = [i32, i32, P]
+        L.gtc_graph_export.argtypes = [P, P, P, P, P]
+        L.gtc_graph_stats.argtypes = [P, C.POINTER(Stats)]
+        L.gtc_graph_free.argtypes = [P]
+        L.gtc_graph_free.restype = None
+        L.gtc_status_string.argtypes = [C.c_int]
+        L.gtc_status_string.restype = C.c_char_p
+        L.gtc_last_error.argtypes = []
+        L.gtc_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != GTC_OK:
+        raise GtcError(rc, lib().gtc_last_error().decode())
+
+
+def _stream_ptr(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _dptr(t):
+    return C.c_void_p(t.data_ptr())
+
+
+def num_configs(order: int, nbins: int) -> int:
+    v = lib().gtc_num_configs(order, nbins)
+    if v < 0:
+        raise ValueError(f"no configurations for order {order}, nbins {nbins}")
+    return int(v)
+
+
+def config_bins(order: int, nbins: int) -> np.ndarray:
+    """Bins of every configuration in rank order: int32 [n_cfg, 3 or 6]."""
+    k = 3 if order == 3 else 6
+    out = np.empty((num_configs(order, nbins), k), np.int32)
+    _check(lib().gtc_config_bins(order, nbins, out.ctypes.data_as(C.c_void_p)))
+    return out
+
+
+class Graph:
+    """Neighbour graph on the current GPU (owned by libgtc; freed by close() or on deletion)."""
+
+    def __init__(self, xyz, edges_sq, tile_bytes: int = 0, host_csr: bool = False,
+                 drop_coords: bool = False, stream=None):
+        import torch
+        if not (isinstance(xyz, torch.Tensor) and xyz.is_cuda and xyz.dtype == torch.int32
+                and xyz.dim() == 2 and xyz.shape[1] == 3):
+            raise TypeError("xyz must be a CUDA int32 tensor of shape [n, 3]")
+        self._xyz = xyz.contiguous()
+        e = np.ascontiguousarray(np.asarray(edges_sq, dtype=np.int64))
+        self.nbins = int(e.size - 1)
+        self.edges = e
+        self.n = int(xyz.shape[0])
+        opt = Options(int(tile_bytes), int(bool(host_csr)), int(bool(drop_coords)))
+        h = C.c_void_p()
+        self._stream = stream
+        _check(lib().gtc_build_graph(_dptr(self._xyz) if self.n else None, self.n,
+                                     e.ctypes.data_as(C.c_void_p), self.nbins, C.byref(opt),
+                                     _stream_ptr(stream), C.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            lib().gtc_graph_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def stats(self) -> dict:
+        st = Stats()
+        _check(lib().gtc_graph_stats(self._h, C.byref(st)))
+        return st.as_dict()
+
+    def count_3pcf(self, w=None, out=None, out_weighted=None):
+        """Binned triangle counts.  Returns (counts int64 [n_cfg] on the GPU, holding the uint64
+        bit pattern; weighted fp64 [n_cfg] or None; stats dict)."""
+        import torch
+        ncfg = num_configs(3, self.nbins)
+        dev = self._xyz.device
+        counts = out if out is not None else torch.empty(ncfg, dtype=torch.int64, device=dev)
+        weighted = None
+        if w is not None:
+            if not (w.is_cuda and w.dtype == torch.float64 and w.numel() == self.n):
+                raise TypeError("w must be a CUDA float64 tensor of length n")
+            w = w.contiguous()
+            weighted = out_weighted if out_weighted is not None else \
+                torch.empty(ncfg, dtype=torch.float64, device=dev)
+        st = Stats()
+        _check(lib().gtc_count_3pcf(self._h, _dptr(w) if w is not None else None, _dptr(counts),
+                                    _dptr(weighted) if weighted is not None else None,
+                                    C.byref(st), _stream_ptr(self._stream)))
+        return counts, weighted, st.as_dict()
+
+    def count_4pcf_parity(self):
+        """Binned 4-clique counts: (even int64 [n_cfg] holding uint64 bits, odd int64, stats)."""
+        import torch
+        ncfg = num_configs(4, self.nbins)
+        dev = self._xyz.device
+        even = torch.empty(ncfg, dtype=torch.int64, device=dev)
+        odd = torch.empty(ncfg, dtype=torch.int64, device=dev)
+        st = Stats()
+        _check(lib().gtc_count_4pcf_parity(self._h, _dptr(even), _dptr(odd), C.byref(st),
+                                           _stream_ptr(self._stream)))
+        return even, odd, st.as_dict()
+
+    def export(self):
+        """Forward CSR in internal labels plus the internal -> original permutation (host)."""
+        st = self.stats()
+        e = int(st["edges"])
+        rp = np.empty(self.n + 1, np.int64)
+        col = np.empty(max(e, 1), np.int32)
+        b = np.empty(max(e, 1), np.uint8)
+        perm = np.empty(max(self.n, 1), np.int32)
+        p = lambda a: a.ctypes.data_as(C.c_void_p)
+        _check(lib().gtc_graph_export(self._h, p(rp), p(col), p(b), p(perm)))
+        return rp, col[:e], b[:e], perm[: self.n]
+
+
+def build_graph(xyz, edges_sq, **kw) -> Graph:
+    return Graph(xyz, edges_sq, **kw)
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/gtc.h declares."""
+    import re
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(gtc_\w+)\s*\(", src, flags=re.M)))

@@ -1,0 +1,297 @@
+// api.hip - the extern "C" boundary of libgtc: argument checks, handle lifetime, dispatch.
+#include <chrono>
+#include <cstdio>
+#include <new>
+#include <vector>
+
+#include "gtc_internal.h"
+
+namespace gtc {
+const char *last_error();
+int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s);
+int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
+                      gtc_stats *st, hipStream_t s);
+int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
+                      hipStream_t s);
+void free_graph_buffers(gtc_graph_s *G);
+
+static int64_t binom(int64_t n, int64_t k) {
+    if (k < 0 || n < k) return 0;
+    int64_t r = 1;
+    for (int64_t t = 1; t <= k; ++t) r = r * (n - k + t) / t;
+    return r;
+}
+
+void free_graph_buffers(gtc_graph_s *G) {
+    hipStream_t s = G->stream;
+    dev_free(G->xyz_s, s);
+    dev_free(G->key_s, s);
+    dev_free(G->perm, s);
+    dev_free(G->cell_start, s);
+    dev_free(G->row_ptr, s);
+    dev_free(G->col, s);
+    dev_free(G->bin, s);
+    dev_free(G->deg, s);
+    dev_free(G->work, s);
+    dev_free(G->hubs, s);
+    dev_free(G->d_edges, s);
+    G->xyz_s = nullptr;
+    G->key_s = nullptr;
+    G->perm = G->cell_start = G->col = G->deg = G->hubs = nullptr;
+    G->row_ptr = G->work = G->d_edges = nullptr;
+    G->bin = nullptr;
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+    int prev = -1;
+    int rc = GTC_OK;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) {
+            rc = GTC_E_HIP;
+            set_error("hipGetDevice failed (no usable GPU?)");
+            prev = -1;
+            return;
+        }
+        if (dev >= 0 && dev != prev && hipSetDevice(dev) != hipSuccess) {
+            rc = GTC_E_HIP;
+            set_error("hipSetDevice(%d) failed", dev);
+        }
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+static void fill_graph_stats(const gtc_graph_s *G, gtc_stats *st) {
+    st->n = G->n;
+    st->edges = G->E;
+    st->max_out_degree = G->max_deg;
+    st->windows = 1;
+    st->spoke_elements = G->spoke_elements;
+    st->build_ms = G->build_ms;
+}
+
+}  // namespace gtc
+
+using namespace gtc;
+
+extern "C" {
+
+int64_t gtc_num_configs(int32_t order, int32_t nbins) {
+    if (order == 3 && nbins >= 1 && nbins <= GTC_MAX_BINS) return binom(nbins + 2, 3);
+    if (order == 4 && nbins >= 1 && nbins <= GTC_MAX_BINS_4PCF) return binom(nbins + 5, 6);
+    return -1;
+}
+
+int gtc_config_bins(int32_t order, int32_t nbins, int32_t *h_bins) {
+    const int64_t ncfg = gtc_num_configs(order, nbins);
+    if (ncfg < 0 || !h_bins) {
+        set_error("gtc_config_bins: order must be 3 or 4 with nbins in range, h_bins non-NULL");
+        return GTC_E_INVALID;
+    }
+    const int k = order == 3 ? 3 : 6;
+    int v[6] = {0, 0, 0, 0, 0, 0};
+    for (int64_t c = 0; c < ncfg; ++c) {
+        for (int t = 0; t < k; ++t) h_bins[c * k + t] = v[t];
+        // next nondecreasing tuple in lexicographic order
+        int t = k - 1;
+        while (t >= 0 && v[t] == nbins - 1) --t;
+        if (t < 0) break;
+        ++v[t];
+        for (int u = t + 1; u < k; ++u) v[u] = v[t];
+    }
+    return GTC_OK;
+}
+
+int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, int32_t nbins,
+                    const gtc_options *opt, void *hip_stream, gtc_graph *out) {
+    if (!out) {
+        set_error("gtc_build_graph: out is NULL");
+        return GTC_E_INVALID;
+    }
+    *out = nullptr;
+    if (n < 0 || n >= ((int64_t)1 << 31)) {
+        set_error("gtc_build_graph: n = %lld outside [0, 2^31)", (long long)n);
+        return GTC_E_INVALID;
+    }
+    if (n > 0 && !d_xyz) {
+        set_error("gtc_build_graph: d_xyz is NULL");
+        return GTC_E_INVALID;
+    }
+    if (!h_edges_sq || nbins < 1 || nbins > GTC_MAX_BINS) {
+        set_error("gtc_build_graph: need h_edges_sq and nbins in [1, %d]", GTC_MAX_BINS);
+        return GTC_E_INVALID;
+    }
+    if (h_edges_sq[0] < 0) {
+        set_error("gtc_build_graph: e_0 must be >= 0");
+        return GTC_E_INVALID;
+    }
+    for (int b = 0; b < nbins; ++b)
+        if (h_edges_sq[b + 1] <= h_edges_sq[b]) {
+            set_error("gtc_build_graph: bin edges must increase strictly (e_%d >= e_%d)", b, b + 1);
+            return GTC_E_INVALID;
+        }
+    const int64_t dmax = 3 * (int64_t)kGridSide * kGridSide + 1;
+    if (h_edges_sq[nbins] > dmax) {
+        set_error("gtc_build_graph: e_nbins beyond the largest squared distance on the grid");
+        return GTC_E_INVALID;
+    }
+    gtc_options o{};
+    if (opt) o = *opt;
+    if (o.tile_bytes < 0 || (o.host_csr && o.tile_bytes <= 0)) {
+        set_error("gtc_build_graph: tile_bytes must be >= 0, and > 0 when host_csr is set");
+        return GTC_E_INVALID;
+    }
+    if (o.tile_bytes > 0 || o.host_csr) {
+        set_error("gtc_build_graph: hub-window tiling is not available in this build");
+        return GTC_E_UNSUPPORTED;
+    }
+    DeviceGuard dg(-1);
+    if (dg.rc) return dg.rc;
+    {
+        // keep freed stream-ordered allocations cached in the pool instead of returning them to
+        // the driver at every synchronisation (builds and counts allocate per call)
+        int dev = 0;
+        hipMemPool_t pool;
+        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+            uint64_t thr = UINT64_MAX;
+            (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &thr);
+        }
+        (void)hipGetLastError();
+    }
+
+    auto t0 = std::chrono::steady_clock::now();
+    gtc_graph_s *G = new (std::nothrow) gtc_graph_s();
+    if (!G) {
+        set_error("gtc_build_graph: host allocation failed");
+        return GTC_E_OOM;
+    }
+    (void)hipGetDevice(&G->device);
+    G->stream = reinterpret_cast<hipStream_t>(hip_stream);
+    G->n = n;
+    G->nb = nbins;
+    for (int b = 0; b <= nbins; ++b) G->edges[b] = h_edges_sq[b];
+    int rc = build_graph_device(G, d_xyz, G->stream);
+    if (rc == GTC_OK && o.drop_coords) {
+        dev_free(G->xyz_s, G->stream);
+        G->xyz_s = nullptr;
+        G->coords_kept = false;
+    }
+    if (rc == GTC_OK) {
+        hipError_t e = hipStreamSynchronize(G->stream);
+        if (e != hipSuccess) rc = hip_fail(e, "hipStreamSynchronize", __FILE__, __LINE__);
+    }
+    if (rc != GTC_OK) {
+        free_graph_buffers(G);
+        (void)hipStreamSynchronize(G->stream);
+        delete G;
+        return rc;
+    }
+    G->build_ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    *out = G;
+    return GTC_OK;
+}
+
+int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d_weighted,
+                   gtc_stats *st, void *hip_stream) {
+    if (!g || !d_counts || (d_w && !d_weighted)) {
+        set_error("gtc_count_3pcf: need a graph, d_counts, and d_weighted when d_w is given");
+        return GTC_E_INVALID;
+    }
+    DeviceGuard dg(g->device);
+    if (dg.rc) return dg.rc;
+    auto t0 = std::chrono::steady_clock::now();
+    gtc_stats local{};
+    fill_graph_stats(g, &local);
+    int rc = count_3pcf_device(g, d_w, d_counts, d_weighted, &local,
+                               reinterpret_cast<hipStream_t>(hip_stream));
+    local.count_ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    if (rc == GTC_OK && st) *st = local;
+    return rc;
+}
+
+int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
+                          void *hip_stream) {
+    if (!g || !d_even || !d_odd) {
+        set_error("gtc_count_4pcf_parity: need a graph, d_even and d_odd");
+        return GTC_E_INVALID;
+    }
+    if (g->nb > GTC_MAX_BINS_4PCF) {
+        set_error("gtc_count_4pcf_parity: nbins %d > %d", g->nb, GTC_MAX_BINS_4PCF);
+        return GTC_E_INVALID;
+    }
+    if (!g->coords_kept) {
+        set_error("gtc_count_4pcf_parity: the graph was built with drop_coords");
+        return GTC_E_INVALID;
+    }
+    DeviceGuard dg(g->device);
+    if (dg.rc) return dg.rc;
+    auto t0 = std::chrono::steady_clock::now();
+    gtc_stats local{};
+    fill_graph_stats(g, &local);
+    int rc = count_4pcf_device(g, d_even, d_odd, &local, reinterpret_cast<hipStream_t>(hip_stream));
+    local.count_ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    if (rc == GTC_OK && st) *st = local;
+    return rc;
+}
+
+int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h_bin,
+                     int32_t *h_perm) {
+    if (!g) {
+        set_error("gtc_graph_export: graph is NULL");
+        return GTC_E_INVALID;
+    }
+    DeviceGuard dg(g->device);
+    if (dg.rc) return dg.rc;
+    hipStream_t s = g->stream;
+    if (h_row_ptr)
+        GTC_HIP_CHECK(hipMemcpyAsync(h_row_ptr, g->row_ptr, sizeof(int64_t) * (g->n + 1),
+                                     hipMemcpyDeviceToHost, s));
+    if (h_col && g->E)
+        GTC_HIP_CHECK(hipMemcpyAsync(h_col, g->col, sizeof(int32_t) * g->E, hipMemcpyDeviceToHost, s));
+    if (h_bin && g->E)
+        GTC_HIP_CHECK(hipMemcpyAsync(h_bin, g->bin, g->E, hipMemcpyDeviceToHost, s));
+    if (h_perm && g->n)
+        GTC_HIP_CHECK(hipMemcpyAsync(h_perm, g->perm, sizeof(int32_t) * g->n, hipMemcpyDeviceToHost, s));
+    GTC_HIP_CHECK(hipStreamSynchronize(s));
+    return GTC_OK;
+}
+
+int gtc_graph_stats(gtc_graph g, gtc_stats *st) {
+    if (!g || !st) {
+        set_error("gtc_graph_stats: need a graph and st");
+        return GTC_E_INVALID;
+    }
+    *st = gtc_stats{};
+    fill_graph_stats(g, st);
+    return GTC_OK;
+}
+
+void gtc_graph_free(gtc_graph g) {
+    if (!g) return;
+    DeviceGuard dg(g->device);
+    free_graph_buffers(g);
+    (void)hipStreamSynchronize(g->stream);
+    delete g;
+}
+
+const char *gtc_status_string(int status) {
+    switch (status) {
+        case GTC_OK: return "ok";
+        case GTC_E_INVALID: return "invalid argument";
+        case GTC_E_OOM: return "out of memory";
+        case GTC_E_HIP: return "HIP runtime error";
+        case GTC_E_OVERFLOW: return "count overflow";
+        case GTC_E_UNSUPPORTED: return "unsupported";
+        default: return "unknown status";
+    }
+}
+
+const char *gtc_last_error(void) { return gtc::last_error(); }
+
+}  // extern "C"

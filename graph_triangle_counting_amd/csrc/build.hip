@@ -1,0 +1,433 @@
+// build.hip - the neighbour graph on the GPU (GRAMSCI v2 §II.1, Eq.(1); CSR layout §III.5.1).
+//
+// The pages build a kd-tree on the CPU; here the points are bucketed into cubic cells of side
+// >= r_max by a counting sort (keys, atomics, scan, scatter), and each point's forward neighbours
+// (larger internal label) are found in its own cell and the 13 forward neighbour cells.  Visiting
+// those cells in increasing key order emits every row already ascending, so no sort is needed.
+// Two passes over the same traversal: count (degrees, then a 64-bit scan to row offsets), emit.
+#include <algorithm>
+#include <cmath>
+
+#include "gtc_internal.h"
+
+namespace gtc {
+
+// forward neighbour cells (dz, dy, dx) > (0, 0, 0), in increasing key order
+__constant__ int8_t kFwd[13][3] = {{0, 0, 1},  {0, 1, -1},  {0, 1, 0},  {0, 1, 1},  {1, -1, -1},
+                                   {1, -1, 0}, {1, -1, 1},  {1, 0, -1}, {1, 0, 0},  {1, 0, 1},
+                                   {1, 1, -1}, {1, 1, 0},   {1, 1, 1}};
+
+__global__ void k_cellkey(const int32_t *__restrict__ xyz, int64_t n, Grid gr,
+                          int32_t *__restrict__ key, int32_t *__restrict__ slot,
+                          int32_t *__restrict__ cell_count, int32_t *__restrict__ err) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    int x = xyz[3 * i], y = xyz[3 * i + 1], z = xyz[3 * i + 2];
+    if ((unsigned)x >= (unsigned)kGridSide || (unsigned)y >= (unsigned)kGridSide ||
+        (unsigned)z >= (unsigned)kGridSide) {
+        atomicOr(err, 1);
+        x = y = z = 0;
+    }
+    const int k = ((z / gr.cs) * gr.g + y / gr.cs) * gr.g + x / gr.cs;
+    key[i] = k;
+    slot[i] = atomicAdd(&cell_count[k], 1);
+}
+
+__global__ void k_scatter(const int32_t *__restrict__ xyz, int64_t n,
+                          const int32_t *__restrict__ key, const int32_t *__restrict__ slot,
+                          const int32_t *__restrict__ cell_start, int32_t *__restrict__ perm,
+                          int4 *__restrict__ xyz_s, int32_t *__restrict__ key_s) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int k = key[i];
+    const int pos = cell_start[k] + slot[i];
+    perm[pos] = (int32_t)i;
+    xyz_s[pos] = make_int4(xyz[3 * i], xyz[3 * i + 1], xyz[3 * i + 2], k);
+    key_s[pos] = k;
+}
+
+struct PairArgs {
+    const int4 *xyz_s;
+    const int32_t *cell_start;
+    const int64_t *edges;  // [nb+1]
+    int32_t nb;
+    int32_t n;
+    Grid gr;
+    int32_t *deg;            // count pass output
+    const int64_t *row_ptr;  // emit pass input
+    int32_t *col;
+    uint8_t *bin;
+};
+
+// Exact squared distance as a double: coordinates differ by < 2^20, squares are < 2^40 and the
+// sum < 2^42, so every step is exact in fp64.
+__device__ __forceinline__ double sq_dist(const int4 a, const int4 b) {
+    const double dx = (double)(a.x - b.x), dy = (double)(a.y - b.y), dz = (double)(a.z - b.z);
+    return dx * dx + dy * dy + dz * dz;
+}
+
+template <bool EMIT>
+__global__ void __launch_bounds__(256) k_pairs(PairArgs a) {
+    __shared__ double se[GTC_MAX_BINS + 1];
+    for (int t = threadIdx.x; t <= a.nb; t += blockDim.x) se[t] = (double)a.edges[t];
+    __syncthreads();
+    const int64_t ii = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (ii >= a.n) return;
+    const int32_t i = (int32_t)ii;
+    const int4 pi = a.xyz_s[i];
+    const int32_t c = pi.w, g = a.gr.g;
+    const int32_t cz = c / (g * g), cy = (c / g) % g, cx = c % g;
+    const double e0 = se[0], emax = se[a.nb];
+    int32_t cnt = 0;
+    int64_t w = EMIT ? a.row_ptr[i] : 0;
+    const int nb = a.nb;
+    auto scan = [&](int32_t lo, int32_t hi) {
+        for (int32_t j = lo; j < hi; ++j) {
+            const double d2 = sq_dist(a.xyz_s[j], pi);
+            if (d2 >= e0 && d2 < emax) {
+                if (EMIT) {
+                    int l = 0, h = nb;  // se[l] <= d2 < se[h]
+                    while (h - l > 1) {
+                        const int m = (l + h) >> 1;
+                        if (d2 >= se[m]) l = m; else h = m;
+                    }
+                    a.col[w] = j;
+                    a.bin[w] = (uint8_t)l;
+                    ++w;
+                } else {
+                    ++cnt;
+                }
+            }
+        }
+    };
+    scan(i + 1, a.cell_start[c + 1]);
+    for (int s = 0; s < 13; ++s) {
+        const int x = cx + kFwd[s][2], y = cy + kFwd[s][1], z = cz + kFwd[s][0];
+        if (x < 0 || y < 0 || x >= g || y >= g || z >= g) continue;
+        const int32_t cc = (z * g + y) * g + x;
+        scan(a.cell_start[cc], a.cell_start[cc + 1]);
+    }
+    if (!EMIT) a.deg[i] = cnt;
+}
+
+// Per-hub statistics, sixteen lanes per hub: work[i] = sum of d+(j) over the row of i, and the
+// graph maxima / totals that size the enumeration kernels.
+struct StatsOut {
+    unsigned long long max_deg;
+    unsigned long long max_domain;
+    unsigned long long spoke_elements;
+    unsigned long long walks;
+    unsigned long long n_hubs;
+};
+
+__global__ void __launch_bounds__(256)
+    k_degstats(int32_t n, const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col,
+               const int32_t *__restrict__ deg, const int32_t *__restrict__ key_s,
+               const int32_t *__restrict__ cell_start, Grid gr, int64_t *__restrict__ work,
+               StatsOut *out) {
+    constexpr int L = 16;
+    const int sub = threadIdx.x & (L - 1);
+    const int64_t hub0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / L;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x / L;
+    unsigned long long my_max_deg = 0, my_max_dom = 0, my_sum = 0, my_walks = 0, my_hubs = 0;
+    for (int64_t h = hub0; h < n; h += stride) {
+        const int64_t b = row_ptr[h], e = row_ptr[h + 1];
+        int64_t s = 0;
+        for (int64_t t = b + sub; t < e; t += L) s += deg[col[t]];
+#pragma unroll
+        for (int d = L / 2; d > 0; d >>= 1) s += __shfl_xor(s, d, L);
+        if (sub == 0) {
+            work[h] = s;
+            const int64_t m = e - b;
+            my_max_deg = m > (int64_t)my_max_deg ? m : my_max_deg;
+            my_sum += s;
+            HubDomain dom;
+            hub_domain((int32_t)h, key_s[h], gr, cell_start, dom);
+            my_max_dom = dom.size > (int64_t)my_max_dom ? dom.size : my_max_dom;
+            if (m >= 2 && s > 0) {
+                my_walks += m;
+                my_hubs += 1;
+            }
+        }
+    }
+    if (sub == 0) {
+        atomicMax(&out->max_deg, my_max_deg);
+        atomicMax(&out->max_domain, my_max_dom);
+        atomicAdd(&out->spoke_elements, my_sum);
+        atomicAdd(&out->walks, my_walks);
+        atomicAdd(&out->n_hubs, my_hubs);
+    }
+}
+
+// Heavy-first hub order: hubs with a possible triangle (d+ >= 2, work > 0) bucketed by
+// floor(log2(work)), buckets in decreasing order.  Block-aggregated counting sort.
+constexpr int kBuckets = 64;
+
+__device__ __forceinline__ int hub_bucket(int64_t m, int64_t w) {
+    if (m < 2 || w <= 0) return -1;
+    return kBuckets - 1 - (63 - __clzll((unsigned long long)w));  // heavier -> smaller bucket
+}
+
+__global__ void __launch_bounds__(256)
+    k_bucket_count(int32_t n, const int64_t *__restrict__ row_ptr, const int64_t *__restrict__ work,
+                   unsigned int *__restrict__ bucket_count) {
+    __shared__ unsigned int loc[kBuckets];
+    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) loc[t] = 0;
+    __syncthreads();
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < n) {
+        const int b = hub_bucket(row_ptr[i + 1] - row_ptr[i], work[i]);
+        if (b >= 0) atomicAdd(&loc[b], 1u);
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x)
+        if (loc[t]) atomicAdd(&bucket_count[t], loc[t]);
+}
+
+__global__ void k_bucket_offsets(unsigned int *bucket_count /* in: counts, out: fill cursor */) {
+    if (threadIdx.x == 0) {
+        unsigned int acc = 0;
+        for (int t = 0; t < kBuckets; ++t) {
+            const unsigned int c = bucket_count[t];
+            bucket_count[t] = acc;
+            acc += c;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(256)
+    k_bucket_scatter(int32_t n, const int64_t *__restrict__ row_ptr,
+                     const int64_t *__restrict__ work, unsigned int *__restrict__ cursor,
+                     int32_t *__restrict__ hubs) {
+    __shared__ unsigned int loc[kBuckets];
+    __shared__ unsigned int base[kBuckets];
+    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) loc[t] = 0;
+    __syncthreads();
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    int b = -1;
+    unsigned int r = 0;
+    if (i < n) {
+        b = hub_bucket(row_ptr[i + 1] - row_ptr[i], work[i]);
+        if (b >= 0) r = atomicAdd(&loc[b], 1u);
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x)
+        base[t] = loc[t] ? atomicAdd(&cursor[t], loc[t]) : 0u;
+    __syncthreads();
+    if (b >= 0) hubs[base[b] + r] = (int32_t)i;
+}
+
+// ------------------------------------------------------------------ host orchestration
+
+static Grid choose_grid(int64_t n, int64_t r2) {
+    // integer cell side cs = ceil(sqrt(r2)), so two neighbours are at most one cell apart per axis
+    int64_t cs = (int64_t)std::sqrt((double)r2);
+    while (cs * cs < r2) ++cs;
+    while (cs > 1 && (cs - 1) * (cs - 1) >= r2) --cs;
+    if (cs < 1) cs = 1;
+    int64_t g = (kGridSide + cs - 1) / cs;
+    // at most ~2n cells (at least 1) and 512 per axis: finer cells than that only cost memory
+    int64_t cap = 1;
+    while ((cap + 1) * (cap + 1) * (cap + 1) <= 2 * (n > 0 ? n : 1) && cap < 512) ++cap;
+    if (g > cap) {
+        g = cap;
+        cs = (kGridSide + g - 1) / g;
+    }
+    Grid gr;
+    gr.g = (int32_t)g;
+    gr.cs = (int32_t)cs;
+    gr.ncell = g * g * g;
+    return gr;
+}
+
+static inline unsigned grid_for(int64_t n, int threads) {
+    return (unsigned)((n + threads - 1) / threads);
+}
+
+int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
+    const int64_t n = G->n;
+    G->grid = choose_grid(n, G->edges[G->nb]);
+    const Grid gr = G->grid;
+
+    GTC_TRY(dev_alloc_n(&G->d_edges, G->nb + 1, s));
+    GTC_HIP_CHECK(hipMemcpyAsync(G->d_edges, G->edges, sizeof(int64_t) * (G->nb + 1),
+                                 hipMemcpyHostToDevice, s));
+    GTC_TRY(dev_alloc_n(&G->cell_start, gr.ncell + 1, s));
+    GTC_TRY(dev_alloc_n(&G->perm, n, s));
+    GTC_TRY(dev_alloc_n(&G->xyz_s, n, s));
+    GTC_TRY(dev_alloc_n(&G->key_s, n, s));
+    GTC_TRY(dev_alloc_n(&G->row_ptr, n + 1, s));
+    GTC_TRY(dev_alloc_n(&G->deg, n, s));
+    GTC_TRY(dev_alloc_n(&G->work, n, s));
+
+    // scratch: keys, slots, cell counts, error flag, stats
+    int32_t *key = nullptr, *slot = nullptr, *ccount = nullptr, *err = nullptr;
+    StatsOut *d_stats = nullptr;
+    unsigned int *bucket = nullptr;
+    int rc = GTC_OK;
+    auto cleanup = [&]() {
+        dev_free(key, s);
+        dev_free(slot, s);
+        dev_free(ccount, s);
+        dev_free(err, s);
+        dev_free(d_stats, s);
+        dev_free(bucket, s);
+    };
+#define STEP(expr)            \
+    do {                      \
+        rc = (expr);          \
+        if (rc) {             \
+            cleanup();        \
+            return rc;        \
+        }                     \
+    } while (0)
+#define STEP_HIP(call)                                                   \
+    do {                                                                 \
+        hipError_t e_ = (call);                                          \
+        if (e_ != hipSuccess) {                                          \
+            rc = hip_fail(e_, #call, __FILE__, __LINE__);                \
+            cleanup();                                                   \
+            return rc;                                                   \
+        }                                                                \
+    } while (0)
+
+    STEP(dev_alloc_n(&key, n, s));
+    STEP(dev_alloc_n(&slot, n, s));
+    STEP(dev_alloc_n(&ccount, gr.ncell, s));
+    STEP(dev_alloc_n(&err, 1, s));
+    STEP(dev_alloc_n(&d_stats, 1, s));
+    STEP(dev_alloc_n(&bucket, kBuckets, s));
+    STEP(fill_u32(reinterpret_cast<uint32_t *>(ccount), gr.ncell, 0u, s));
+    STEP(fill_u32(reinterpret_cast<uint32_t *>(err), 1, 0u, s));
+    STEP(fill_u64(reinterpret_cast<uint64_t *>(d_stats), sizeof(StatsOut) / 8, 0ull, s));
+    STEP(fill_u32(bucket, kBuckets, 0u, s));
+
+    if (n > 0) {
+        hipLaunchKernelGGL(k_cellkey, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, gr, key,
+                           slot, ccount, err);
+        STEP_HIP(hipGetLastError());
+    }
+    STEP(exclusive_scan_i32_to_i32(ccount, G->cell_start, gr.ncell, s));
+    if (n > 0) {
+        hipLaunchKernelGGL(k_scatter, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, key, slot,
+                           G->cell_start, G->perm, G->xyz_s, G->key_s);
+        STEP_HIP(hipGetLastError());
+    }
+
+    PairArgs pa{};
+    pa.xyz_s = G->xyz_s;
+    pa.cell_start = G->cell_start;
+    pa.edges = G->d_edges;
+    pa.nb = G->nb;
+    pa.n = (int32_t)n;
+    pa.gr = gr;
+    pa.deg = G->deg;
+    if (n > 0) {
+        hipLaunchKernelGGL(k_pairs<false>, dim3(grid_for(n, 256)), dim3(256), 0, s, pa);
+        STEP_HIP(hipGetLastError());
+    }
+    STEP(exclusive_scan_i32_to_i64(G->deg, G->row_ptr, n, s));
+
+    int32_t h_err = 0;
+    STEP_HIP(hipMemcpyAsync(&G->E, G->row_ptr + n, sizeof(int64_t), hipMemcpyDeviceToHost, s));
+    STEP_HIP(hipMemcpyAsync(&h_err, err, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+    STEP_HIP(hipStreamSynchronize(s));
+    if (h_err) {
+        set_error("a coordinate is outside [0, 2^20)");
+        cleanup();
+        return GTC_E_INVALID;
+    }
+    STEP(dev_alloc_n(&G->col, G->E, s));
+    STEP(dev_alloc_n(&G->bin, G->E, s));
+    pa.row_ptr = G->row_ptr;
+    pa.col = G->col;
+    pa.bin = G->bin;
+    if (n > 0) {
+        hipLaunchKernelGGL(k_pairs<true>, dim3(grid_for(n, 256)), dim3(256), 0, s, pa);
+        STEP_HIP(hipGetLastError());
+        const int64_t dsb = std::min<int64_t>((n * 16 + 255) / 256, 65535);
+        hipLaunchKernelGGL(k_degstats, dim3((unsigned)dsb), dim3(256), 0, s, (int32_t)n, G->row_ptr,
+                           G->col, G->deg, G->key_s, G->cell_start, gr, G->work, d_stats);
+        STEP_HIP(hipGetLastError());
+    }
+    StatsOut hs{};
+    STEP_HIP(hipMemcpyAsync(&hs, d_stats, sizeof(hs), hipMemcpyDeviceToHost, s));
+    STEP_HIP(hipStreamSynchronize(s));
+    G->max_deg = (int64_t)hs.max_deg;
+    G->max_domain = (int64_t)hs.max_domain;
+    G->spoke_elements = (int64_t)hs.spoke_elements;
+    G->walks = (int64_t)hs.walks;
+    G->n_hubs = (int64_t)hs.n_hubs;
+
+    STEP(dev_alloc_n(&G->hubs, G->n_hubs, s));
+    if (n > 0 && G->n_hubs > 0) {
+        hipLaunchKernelGGL(k_bucket_count, dim3(grid_for(n, 256)), dim3(256), 0, s, (int32_t)n,
+                           G->row_ptr, G->work, bucket);
+        hipLaunchKernelGGL(k_bucket_offsets, dim3(1), dim3(64), 0, s, bucket);
+        hipLaunchKernelGGL(k_bucket_scatter, dim3(grid_for(n, 256)), dim3(256), 0, s, (int32_t)n,
+                           G->row_ptr, G->work, bucket, G->hubs);
+        STEP_HIP(hipGetLastError());
+    }
+    cleanup();
+#undef STEP
+#undef STEP_HIP
+    return GTC_OK;
+}
+
+// Weights into internal order: w_s[pos] = w[perm[pos]], and max |w| (bit pattern of a
+// non-negative double orders like its value) plus a flag for non-finite values.
+__global__ void k_gather_weights(int64_t n, const double *__restrict__ w,
+                                 const int32_t *__restrict__ perm, double *__restrict__ w_s,
+                                 unsigned long long *__restrict__ maxabs_bits,
+                                 int32_t *__restrict__ bad) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    unsigned long long m = 0;
+    if (i < n) {
+        const double v = w[perm[i]];
+        w_s[i] = v;
+        if (!isfinite(v)) atomicOr(bad, 1);
+        m = (unsigned long long)__double_as_longlong(fabs(v));
+    }
+    for (int d = kWave / 2; d > 0; d >>= 1) {
+        const unsigned long long o = __shfl_xor(m, d, kWave);
+        m = o > m ? o : m;
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0 && m) atomicMax(maxabs_bits, m);
+}
+
+int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, double *maxabs,
+                   hipStream_t s) {
+    unsigned long long *d_m = nullptr;
+    int32_t *d_bad = nullptr;
+    GTC_TRY(dev_alloc_n(&d_m, 1, s));
+    int rc = dev_alloc_n(&d_bad, 1, s);
+    if (!rc) rc = fill_u64(reinterpret_cast<uint64_t *>(d_m), 1, 0ull, s);
+    if (!rc) rc = fill_u32(reinterpret_cast<uint32_t *>(d_bad), 1, 0u, s);
+    unsigned long long hm = 0;
+    int32_t hb = 0;
+    if (!rc && G->n > 0) {
+        hipLaunchKernelGGL(k_gather_weights, dim3(grid_for(G->n, 256)), dim3(256), 0, s, G->n, d_w,
+                           G->perm, w_s, d_m, d_bad);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) rc = hip_fail(e, "k_gather_weights", __FILE__, __LINE__);
+    }
+    if (!rc) {
+        hipError_t e = hipMemcpyAsync(&hm, d_m, sizeof(hm), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipMemcpyAsync(&hb, d_bad, sizeof(hb), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) rc = hip_fail(e, "weight readback", __FILE__, __LINE__);
+    }
+    dev_free(d_m, s);
+    dev_free(d_bad, s);
+    if (rc) return rc;
+    if (hb) {
+        set_error("a weight is not finite");
+        return GTC_E_INVALID;
+    }
+    double v;
+    std::memcpy(&v, &hm, sizeof(v));
+    *maxabs = v;
+    return GTC_OK;
+}
+
+}  // namespace gtc

@@ -1,0 +1,341 @@
+// clique4.hip - binned 4-clique (tetrahedron) counts split by parity (GRAMSCI v2 §II.2,
+// §III.1.1, §III.2, per-hub local connectivity matrix §III.5.2).
+//
+// One wavefront per hub i.  With N+(i) = {j_0 < ... < j_{m-1}} the wave builds the hub's local
+// connectivity among its forward neighbours: bit b of row a is set iff j_a ~ j_b (a < b).  Row a
+// comes from one walk of N+(j_a) against the hub, exactly the triangle walk of the 3pCF kernel,
+// with the LDS hub map holding row positions.  This replaces the pages' three-pointer walk per
+// (i, j1, j2) by one walk per (i, j1) plus bitset intersections: every tetrahedron i < j_a < j_b
+// < j_c is a set bit c of row_a AND row_b.  The pages keep this matrix in a global scratch slot
+// per gang; it lives in LDS here.
+//
+// Per tetrahedron: the six edge bins, sorted and ranked (combinatorial number system over
+// nondecreasing 6-tuples), and the parity sign: vertices ordered by the sum of their squared edge
+// lengths, exact int64 signed volume (r01 x r02) . r03 (Eq.(3)), zero for a tie or zero volume.
+#include <algorithm>
+#include <vector>
+
+#include "gtc_internal.h"
+
+namespace gtc {
+
+struct CliqueArgs {
+    const int64_t *row_ptr;
+    const int32_t *col;
+    const uint8_t *bin;
+    const int32_t *hubs;
+    int32_t n_hubs;
+    int32_t nb, ncfg;
+    int32_t map_bytes;     // per-wave position map (uint16 per domain label), multiple of 16
+    int32_t max_m;         // longest forward row
+    int32_t words;         // 32-bit words per bitset row = ceil(max_m / 32)
+    const int4 *xyz_s;
+    const int32_t *cell_start;
+    Grid gr;
+    unsigned int *queue;
+    unsigned long long *even;  // [ncfg]
+    unsigned long long *odd;   // [ncfg], two's complement int64
+    unsigned int flush_at;
+};
+
+__device__ __forceinline__ void wave_lds_sync4() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__host__ __device__ inline size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+
+// per-workgroup part: even u32[ncfg], odd i32[ncfg], binomials C[22][8]
+__host__ __device__ inline size_t clique_lds_fixed(int ncfg) {
+    return align16(4 * (size_t)ncfg) * 2 + 22 * 8 * 4;
+}
+// per-wave part: position map, row coordinates, hub-edge bins, bitset rows
+__host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int words) {
+    return (size_t)map_bytes + align16(16 * (size_t)max_m) + align16((size_t)max_m) +
+           align16(4 * (size_t)max_m * words);
+}
+
+__device__ __forceinline__ int64_t d2i(int4 p, int4 q) {
+    const int64_t dx = p.x - q.x, dy = p.y - q.y, dz = p.z - q.z;
+    return dx * dx + dy * dy + dz * dz;
+}
+
+template <class T>
+__device__ __forceinline__ void cswap(T &a, T &b) {
+    const T lo = a < b ? a : b, hi = a < b ? b : a;
+    a = lo;
+    b = hi;
+}
+
+__device__ __forceinline__ int chirality(int4 p[4], int64_t key[4]) {
+    // order the four vertices by key (insertion sort, swapping points along)
+#pragma unroll
+    for (int x = 1; x < 4; ++x)
+#pragma unroll
+        for (int y = x; y > 0; --y)
+            if (key[y - 1] > key[y]) {
+                const int64_t tk = key[y]; key[y] = key[y - 1]; key[y - 1] = tk;
+                const int4 tp = p[y]; p[y] = p[y - 1]; p[y - 1] = tp;
+            }
+    if (key[0] == key[1] || key[1] == key[2] || key[2] == key[3]) return 0;
+    const int64_t ax = p[1].x - p[0].x, ay = p[1].y - p[0].y, az = p[1].z - p[0].z;
+    const int64_t bx = p[2].x - p[0].x, by = p[2].y - p[0].y, bz = p[2].z - p[0].z;
+    const int64_t cx = p[3].x - p[0].x, cy = p[3].y - p[0].y, cz = p[3].z - p[0].z;
+    const int64_t v = cx * (ay * bz - az * by) + cy * (az * bx - ax * bz) + cz * (ax * by - ay * bx);
+    return (v > 0) - (v < 0);
+}
+
+__device__ __forceinline__ int edge_bin(int64_t d2, const int64_t *se, int nb) {
+    int l = 0, h = nb;  // se[l] <= d2 < se[h]
+    while (h - l > 1) {
+        const int md = (l + h) >> 1;
+        if (d2 >= se[md]) l = md; else h = md;
+    }
+    return l;
+}
+
+__global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *edges) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int64_t se[GTC_MAX_BINS_4PCF + 1];
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    uint32_t *ev = reinterpret_cast<uint32_t *>(smem);
+    int32_t *od = reinterpret_cast<int32_t *>(smem + align16(4 * (size_t)a.ncfg));
+    int32_t *binom = reinterpret_cast<int32_t *>(smem + 2 * align16(4 * (size_t)a.ncfg));
+    unsigned char *wbase = smem + clique_lds_fixed(a.ncfg) +
+                           (size_t)wid * clique_lds_wave(a.map_bytes, a.max_m, a.words);
+    uint16_t *pmap = reinterpret_cast<uint16_t *>(wbase);
+    int4 *rc = reinterpret_cast<int4 *>(wbase + a.map_bytes);
+    uint8_t *rbin = wbase + a.map_bytes + align16(16 * (size_t)a.max_m);
+    uint32_t *adj = reinterpret_cast<uint32_t *>(wbase + a.map_bytes + align16(16 * (size_t)a.max_m) +
+                                                 align16((size_t)a.max_m));
+    const int N = a.nb + 5;  // 6-combinations of [0, N) <-> nondecreasing 6-tuples of [0, nb)
+
+    for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
+        ev[t] = 0;
+        od[t] = 0;
+    }
+    for (int t = threadIdx.x; t <= a.nb; t += blockDim.x) se[t] = edges[t];
+    for (int t = threadIdx.x; t < 22 * 8; t += blockDim.x) {
+        const int x = t / 8, r = t % 8;
+        int64_t c = 1;
+        for (int u = 1; u <= r; ++u) c = c * (x - r + u) / u;  // C(x-r+u, u), exact at each step
+        binom[t] = (r <= x) ? (int32_t)c : 0;
+    }
+    __syncthreads();
+
+    unsigned int wave_cl = 0;
+    for (;;) {
+        unsigned int hq = 0;
+        if (lane == 0) hq = atomicAdd(a.queue, 1u);
+        hq = __builtin_amdgcn_readfirstlane(__shfl(hq, 0, kWave));
+        if (hq >= (unsigned int)a.n_hubs) break;
+        const int32_t i = __builtin_amdgcn_readfirstlane(a.hubs[hq]);
+        const int64_t rb = a.row_ptr[i];
+        const int32_t m = (int32_t)(a.row_ptr[i + 1] - rb);
+        if (m < 3) continue;
+        const int4 pi = a.xyz_s[i];
+        HubDomain dom;
+        hub_domain(i, pi.w, a.gr, a.cell_start, dom);
+        const int W = (m + 31) >> 5;
+
+        uint32_t *pm32 = reinterpret_cast<uint32_t *>(pmap);
+        for (int t = lane; t < ((dom.size + 1) >> 1); t += kWave) pm32[t] = 0u;
+        for (int t = lane; t < m * W; t += kWave) adj[t] = 0u;
+        wave_lds_sync4();
+        const int32_t *hrow = a.col + rb;
+        for (int p = lane; p < m; p += kWave) {
+            const int32_t k = hrow[p];
+            int32_t d = dom.delta[0];
+#pragma unroll
+            for (int t = 1; t < 5; ++t)
+                if (k >= dom.lo[t]) d = dom.delta[t];
+            pmap[k + d] = (uint16_t)(p + 1);
+            rc[p] = a.xyz_s[k];
+            rbin[p] = a.bin[rb + p];
+        }
+        wave_lds_sync4();
+        const int32_t hub_hi = hrow[m - 1];
+
+        // local connectivity: for every spoke a, walk N+(j_a) against the hub map
+        for (int sp = 0; sp < m - 1; ++sp) {
+            const int32_t j = hrow[sp];
+            const int64_t jb = a.row_ptr[j], je = a.row_ptr[j + 1];
+            for (int64_t e = jb + lane; e < je; e += kWave) {
+                const int32_t k = a.col[e];
+                if (k > hub_hi) break;
+                int32_t d = dom.delta[0], lim = dom.hi[0];
+#pragma unroll
+                for (int t = 1; t < 5; ++t)
+                    if (k >= dom.lo[t]) { d = dom.delta[t]; lim = dom.hi[t]; }
+                if (k < lim) {
+                    const int32_t v = pmap[k + d];
+                    if (v) {
+                        const int b = v - 1;
+                        atomicOr(&adj[sp * W + (b >> 5)], 1u << (b & 31));
+                    }
+                }
+            }
+        }
+        wave_lds_sync4();
+
+        // tetrahedra: for each local edge (a, b), common bits c of rows a and b
+        unsigned int my_cl = 0;
+        for (int t = lane; t < m * W; t += kWave) {
+            const int ra = t / W, wa = t - ra * W;
+            uint32_t bits = adj[t];
+            while (bits) {
+                const int rbb = wa * 32 + __builtin_ctz(bits);
+                bits &= bits - 1;
+                for (int w2 = (rbb + 1) >> 5; w2 < W; ++w2) {
+                    uint32_t cm = adj[ra * W + w2] & adj[rbb * W + w2];
+                    while (cm) {
+                        const int rcc = w2 * 32 + __builtin_ctz(cm);
+                        cm &= cm - 1;
+                        int4 p[4] = {pi, rc[ra], rc[rbb], rc[rcc]};
+                        const int64_t dab = d2i(p[1], p[2]), dac = d2i(p[1], p[3]), dbc = d2i(p[2], p[3]);
+                        const int64_t dia = d2i(p[0], p[1]), dib = d2i(p[0], p[2]), dic = d2i(p[0], p[3]);
+                        int bb[6] = {rbin[ra], rbin[rbb], rbin[rcc], edge_bin(dab, se, a.nb),
+                                     edge_bin(dac, se, a.nb), edge_bin(dbc, se, a.nb)};
+                        // sorting network for six values
+                        cswap(bb[1], bb[2]); cswap(bb[4], bb[5]); cswap(bb[0], bb[2]);
+                        cswap(bb[3], bb[5]); cswap(bb[0], bb[1]); cswap(bb[3], bb[4]);
+                        cswap(bb[1], bb[4]); cswap(bb[0], bb[3]); cswap(bb[2], bb[5]);
+                        cswap(bb[1], bb[3]); cswap(bb[2], bb[4]); cswap(bb[2], bb[3]);
+                        int rank = 0, prev = -1;
+#pragma unroll
+                        for (int q = 0; q < 6; ++q) {
+                            const int cq = bb[q] + q;  // strictly increasing combination element
+                            rank += binom[(N - prev - 1) * 8 + (6 - q)] - binom[(N - cq) * 8 + (6 - q)];
+                            prev = cq;
+                        }
+                        int64_t key[4] = {dia + dib + dic, dia + dab + dac, dib + dab + dbc,
+                                          dic + dac + dbc};
+                        const int sgn = chirality(p, key);
+                        atomicAdd(&ev[rank], 1u);
+                        if (sgn) atomicAdd(&od[rank], sgn);
+                        ++my_cl;
+                    }
+                }
+            }
+        }
+        unsigned int tot = my_cl;
+#pragma unroll
+        for (int dd = kWave / 2; dd > 0; dd >>= 1) tot += __shfl_xor(tot, dd, kWave);
+        wave_cl += tot;
+        if (wave_cl >= a.flush_at) {
+            for (int t = lane; t < a.ncfg; t += kWave) {
+                const uint32_t v = atomicExch(&ev[t], 0u);
+                if (v) atomicAdd(&a.even[t], (unsigned long long)v);
+                const int32_t o = atomicExch(&od[t], 0);
+                if (o) atomicAdd(&a.odd[t], (unsigned long long)(long long)o);
+            }
+            wave_cl = 0;
+        }
+        wave_lds_sync4();
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
+        const uint32_t v = ev[t];
+        if (v) atomicAdd(&a.even[t], (unsigned long long)v);
+        const int32_t o = od[t];
+        if (o) atomicAdd(&a.odd[t], (unsigned long long)(long long)o);
+    }
+}
+
+int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
+                      hipStream_t s) {
+    const int64_t ncfg = gtc_num_configs(4, G->nb);
+    GTC_TRY(fill_u64(d_even, ncfg, 0ull, s));
+    GTC_TRY(fill_u64(reinterpret_cast<uint64_t *>(d_odd), ncfg, 0ull, s));
+    if (G->max_deg >= 65535) {
+        set_error("4pCF: a forward row of %lld entries exceeds the 16-bit position map",
+                  (long long)G->max_deg);
+        return GTC_E_UNSUPPORTED;
+    }
+    CliqueArgs a{};
+    a.row_ptr = G->row_ptr;
+    a.col = G->col;
+    a.bin = G->bin;
+    a.hubs = G->hubs;
+    a.n_hubs = (int32_t)G->n_hubs;
+    a.nb = G->nb;
+    a.ncfg = (int32_t)ncfg;
+    a.map_bytes = (int32_t)align16(2 * (size_t)std::max<int64_t>(G->max_domain, 1));
+    a.max_m = (int32_t)std::max<int64_t>(G->max_deg, 1);
+    a.words = (a.max_m + 31) / 32;
+    a.xyz_s = G->xyz_s;
+    a.cell_start = G->cell_start;
+    a.gr = G->grid;
+    a.even = reinterpret_cast<unsigned long long *>(d_even);
+    a.odd = reinterpret_cast<unsigned long long *>(d_odd);
+
+    int dev = 0, cus = 0, ldsmax = 0;
+    GTC_HIP_CHECK(hipGetDevice(&dev));
+    GTC_HIP_CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    GTC_HIP_CHECK(hipDeviceGetAttribute(&ldsmax, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+    const size_t fixed = clique_lds_fixed(a.ncfg), per = clique_lds_wave(a.map_bytes, a.max_m, a.words);
+    int waves = 4;
+    const size_t static_lds = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
+    while (waves > 1 && static_lds + fixed + waves * per > (size_t)ldsmax) waves >>= 1;
+    const size_t lds = fixed + waves * per;
+    if (static_lds + lds > (size_t)ldsmax) {
+        set_error("4pCF needs %zu bytes of LDS per workgroup (longest row %d, hub domain %d); the "
+                  "device allows %d", lds, a.max_m, a.map_bytes / 2, ldsmax);
+        return GTC_E_UNSUPPORTED;
+    }
+    const unsigned long long mm = (unsigned long long)a.max_m;
+    const unsigned long long max_hub = mm * (mm - 1) * (mm - 2) / 6;
+    const unsigned long long budget = 0x7fffffffull / (unsigned long long)waves;
+    if (max_hub >= budget / 2) {
+        set_error("4pCF: a hub with %d forward neighbours could overflow the 32-bit LDS bins", a.max_m);
+        return GTC_E_UNSUPPORTED;
+    }
+    a.flush_at = (unsigned int)(budget - max_hub);
+
+    unsigned int *queue = nullptr;
+    GTC_TRY(dev_alloc_n(&queue, 1, s));
+    int rc = fill_u32(queue, 1, 0u, s);
+    a.queue = queue;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    float kms = 0.f;
+    if (!rc && G->n_hubs > 0) {
+        if (lds > 65536)
+            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_clique4),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        int per_cu = 0;
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(&k_clique4), waves * kWave, lds);
+        if (per_cu < 1) per_cu = 1;
+        int64_t blocks = std::min<int64_t>((int64_t)cus * per_cu, (G->n_hubs + waves - 1) / waves);
+        (void)hipEventCreate(&e0);
+        (void)hipEventCreate(&e1);
+        (void)hipEventRecord(e0, s);
+        hipLaunchKernelGGL(k_clique4, dim3((unsigned)std::max<int64_t>(blocks, 1)),
+                           dim3(waves * kWave), lds, s, a, (const int64_t *)G->d_edges);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) rc = hip_fail(e, "k_clique4 launch", __FILE__, __LINE__);
+        (void)hipEventRecord(e1, s);
+    }
+    std::vector<unsigned long long> h_even(ncfg);
+    if (!rc) {
+        hipError_t e = hipMemcpyAsync(h_even.data(), d_even, 8 * ncfg, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) rc = hip_fail(e, "4pCF readback", __FILE__, __LINE__);
+        if (!rc && e0) (void)hipEventElapsedTime(&kms, e0, e1);
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    dev_free(queue, s);
+    if (rc) return rc;
+    unsigned long long cl = 0;
+    for (auto v : h_even) cl += v;
+    if (st) {
+        st->cliques4 = cl;
+        st->merge_walks = G->walks;
+        st->tiles = G->n_hubs > 0 ? 1 : 0;
+        st->kernel_ms = kms;
+    }
+    return GTC_OK;
+}
+
+}  // namespace gtc

@@ -1,0 +1,176 @@
+// util.hip - error reporting, stream-ordered device memory, fills and exclusive scans.
+#include <cstdarg>
+#include <cstdio>
+
+#include "gtc_internal.h"
+
+namespace gtc {
+
+static thread_local char g_last_error[1024] = "";
+
+void set_error(const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+}
+
+const char *last_error() { return g_last_error; }
+
+int hip_fail(hipError_t e, const char *what, const char *file, int line) {
+    set_error("%s failed: %s (%s:%d)", what, hipGetErrorString(e), file, line);
+    return (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? GTC_E_OOM : GTC_E_HIP;
+}
+
+int dev_alloc(void **p, size_t bytes, hipStream_t s) {
+    *p = nullptr;
+    hipError_t e = hipMallocAsync(p, bytes, s);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        set_error("device allocation of %zu bytes failed: %s", bytes, hipGetErrorString(e));
+        return GTC_E_OOM;
+    }
+    return GTC_OK;
+}
+
+void dev_free(void *p, hipStream_t s) {
+    if (p) (void)hipFreeAsync(p, s);
+}
+
+// ------------------------------------------------------------------ fills (kernels, not memset:
+// they stay correct if a caller captures the stream into a graph)
+template <class T>
+__global__ void k_fill(T *p, int64_t n, T v) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+template <class T>
+static int fill(T *p, int64_t n, T v, hipStream_t s) {
+    if (n <= 0) return GTC_OK;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_fill<T>, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+    GTC_HIP_CHECK(hipGetLastError());
+    return GTC_OK;
+}
+
+int fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t s) { return fill<uint64_t>(p, n, v, s); }
+int fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s) { return fill<uint32_t>(p, n, v, s); }
+
+// ------------------------------------------------------------------ exclusive scan
+// Three passes: per-block totals, a scan of the totals (recursive), per-block rescans.
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 8;
+constexpr int kScanTile = kScanThreads * kScanItems;
+
+template <class T>
+__device__ T block_exclusive_scan(T v, T *wave_tot, T &block_total) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    T inc = v;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        T o = __shfl_up(inc, d, kWave);
+        if (lane >= d) inc += o;
+    }
+    if (lane == kWave - 1) wave_tot[wid] = inc;
+    __syncthreads();
+    T off = 0, tot = 0;
+    for (int w = 0; w < kScanThreads / kWave; ++w) {
+        if (w < wid) off += wave_tot[w];
+        tot += wave_tot[w];
+    }
+    __syncthreads();
+    block_total = tot;
+    return off + inc - v;
+}
+
+template <class Tin, class Tout>
+__global__ void __launch_bounds__(kScanThreads) k_tile_sums(const Tin *in, int64_t n, Tout *sums) {
+    __shared__ Tout wt[kScanThreads / kWave];
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+    Tout acc = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+        int64_t i = base + (int64_t)k * kScanThreads + threadIdx.x;
+        if (i < n) acc += (Tout)in[i];
+    }
+    Tout tot;
+    block_exclusive_scan<Tout>(acc, wt, tot);
+    if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+}
+
+template <class Tin, class Tout>
+__global__ void __launch_bounds__(kScanThreads)
+    k_tile_scan(const Tin *in, int64_t n, const Tout *tile_off, Tout *out) {
+    __shared__ Tout buf[kScanTile];
+    __shared__ Tout wt[kScanThreads / kWave];
+    const int64_t base = (int64_t)blockIdx.x * kScanTile;
+    for (int k = 0; k < kScanItems; ++k) {
+        int t = k * kScanThreads + threadIdx.x;
+        int64_t i = base + t;
+        buf[t] = i < n ? (Tout)in[i] : (Tout)0;
+    }
+    __syncthreads();
+    Tout loc[kScanItems];
+    Tout acc = 0;
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+        loc[k] = acc;
+        acc += buf[threadIdx.x * kScanItems + k];
+    }
+    Tout tot;
+    Tout off = block_exclusive_scan<Tout>(acc, wt, tot) + (tile_off ? tile_off[blockIdx.x] : 0);
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) buf[threadIdx.x * kScanItems + k] = loc[k] + off;
+    __syncthreads();
+    for (int k = 0; k < kScanItems; ++k) {
+        int t = k * kScanThreads + threadIdx.x;
+        int64_t i = base + t;
+        if (i < n) out[i] = buf[t];
+        if (i == n) out[n] = buf[t];  // total, when n is not a multiple of the tile
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0 && (n % kScanTile) == 0 && n > 0)
+        out[n] = off + tot;  // n is a tile multiple: the total sits past the last tile
+}
+
+template <class Tin, class Tout>
+static int exclusive_scan(const Tin *in, Tout *out, int64_t n, hipStream_t s) {
+    if (n <= 0) return fill<Tout>(out, 1, (Tout)0, s);
+    const int64_t tiles = (n + kScanTile - 1) / kScanTile;
+    if (tiles > INT32_MAX) {
+        set_error("scan of %lld items is too long", (long long)n);
+        return GTC_E_UNSUPPORTED;
+    }
+    if (tiles == 1) {
+        hipLaunchKernelGGL((k_tile_scan<Tin, Tout>), dim3(1), dim3(kScanThreads), 0, s, in, n,
+                           (const Tout *)nullptr, out);
+        GTC_HIP_CHECK(hipGetLastError());
+        return GTC_OK;
+    }
+    Tout *sums = nullptr, *offs = nullptr;
+    GTC_TRY(dev_alloc_n(&sums, tiles, s));
+    int rc = dev_alloc_n(&offs, tiles + 1, s);
+    if (rc) { dev_free(sums, s); return rc; }
+    hipLaunchKernelGGL((k_tile_sums<Tin, Tout>), dim3((unsigned)tiles), dim3(kScanThreads), 0, s,
+                       in, n, sums);
+    rc = exclusive_scan<Tout, Tout>(sums, offs, tiles, s);
+    if (!rc)
+        hipLaunchKernelGGL((k_tile_scan<Tin, Tout>), dim3((unsigned)tiles), dim3(kScanThreads), 0,
+                           s, in, n, (const Tout *)offs, out);
+    dev_free(sums, s);
+    dev_free(offs, s);
+    if (rc) return rc;
+    GTC_HIP_CHECK(hipGetLastError());
+    return GTC_OK;
+}
+
+int exclusive_scan_i32_to_i64(const int32_t *in, int64_t *out, int64_t n, hipStream_t s) {
+    return exclusive_scan<int32_t, int64_t>(in, out, n, s);
+}
+int exclusive_scan_i32_to_i32(const int32_t *in, int32_t *out, int64_t n, hipStream_t s) {
+    return exclusive_scan<int32_t, int32_t>(in, out, n, s);
+}
+
+}  // namespace gtc

@@ -1,0 +1,156 @@
+/* gtc.h - C ABI of libgtc, the MI355X (gfx950) graph 3-point / 4-point correlation counter.
+ *
+ * The method is GRAMSCI v2, "Fast Graph-based Higher-Order Clustering Statistics on the GPU"
+ * (arXiv 2607.06604): a fixed-radius neighbour graph stored as sorted adjacency rows with a
+ * radial-bin byte per edge (§II.1, Eq.(1); CSR layout §III.5.1), hub-and-spoke triangle and
+ * tetrahedron enumeration by sorted-list intersection (§II.2, §III.1, §III.1.1), counts binned by
+ * side-length configuration (§V.1) and a parity split of the tetrahedra by the sign of the signed
+ * volume (§III.2, Eq.(3)); graphs larger than a tile are processed in hub windows (§III.5.3).
+ *
+ * Conventions for every function:
+ *   - Return value: GTC_OK (0) or a negative gtc_status.  No exception or abort crosses the ABI.
+ *     gtc_last_error() gives a human-readable detail of the last failure on the calling thread.
+ *   - Pointers named d_* are device pointers on the current HIP device; h_* are host pointers.
+ *     The caller owns every buffer it passes; outputs are overwritten, never accumulated.
+ *   - hip_stream is a hipStream_t (NULL = the null stream).  Work is ordered on it.  The count
+ *     functions return after their outputs are complete (they synchronise the stream);
+ *     gtc_build_graph synchronises once to size the edge arrays.
+ *   - Argument checks that need no device data (null pointers, sizes, bin edges) fail with
+ *     GTC_E_INVALID before any HIP call is made.
+ *
+ * Definitions (exact integer arithmetic throughout):
+ *   - points: n integer triples in [0, 2^20)^3; d2(i,j) = sum of squared coordinate differences.
+ *   - edges_sq: nbins+1 integers e_0 < e_1 < ... < e_nbins, e_0 >= 0.  i and j (i != j) are
+ *     neighbours iff e_0 <= d2 < e_nbins, and the edge is in bin b iff e_b <= d2 < e_{b+1}.
+ *   - each triangle (4-clique) is counted once.  Its configuration is the nondecreasing triple
+ *     (6-tuple) of its edge bins; configurations are ranked from 0 in lexicographic order, which is
+ *     the nested-loop order b1 = 0..nb-1, b2 = b1..nb-1, ... (the Fig. 8 configuration key).
+ *   - weighted 3pCF: per triangle p = fl(fl(w1*w2)*w3) with its three weights in ascending
+ *     order (fp64, separately rounded products).  weighted[c] is the exact sum over the
+ *     configuration's triangles of q = rint(p * 2^s), rounded once to fp64, times 2^-s.
+ *     s = 57 - e where a = max |w| over all n weights, M = fl(fl(a*a)*a) = f * 2^e with
+ *     f in [0.5, 1) (s = 0 when M = 0).  q is exact whenever p's last significant bit is at least
+ *     2^-s, e.g. for all weights in [0.5, 1.5).
+ *   - parity: the four vertices of a tetrahedron are ordered by key(v) = sum of d2 to the other
+ *     three, ascending; V = det[x1 - x0; x2 - x0; x3 - x0] (rows), i.e. (r01 x r02) . r03 of
+ *     Eq.(3).  even[c] counts every tetrahedron; odd[c] adds +1 for V > 0, -1 for V < 0 and 0 if
+ *     V == 0 or two keys are equal (no label-free handedness, the §III.2 degenerate rule).
+ */
+#ifndef GTC_H
+#define GTC_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GTC_OK = 0,
+    GTC_E_INVALID = -1,     /* bad argument or input value */
+    GTC_E_OOM = -2,         /* device or pinned-host allocation failed */
+    GTC_E_HIP = -3,         /* a HIP runtime call failed (detail in gtc_last_error) */
+    GTC_E_OVERFLOW = -4,    /* a count does not fit the library's fixed-width types */
+    GTC_E_UNSUPPORTED = -5  /* valid input outside what this build handles (detail given) */
+} gtc_status;
+
+#define GTC_MAX_BINS 255       /* 3pCF: nbins in [1, 255] */
+#define GTC_MAX_BINS_4PCF 16   /* parity 4pCF: nbins in [1, 16] */
+#define GTC_GRID_BITS 20       /* coordinates in [0, 2^20) */
+
+/* Opaque neighbour graph, owned by the library (device CSR in internal labels, see
+ * gtc_graph_export).  Free with gtc_graph_free. */
+typedef struct gtc_graph_s *gtc_graph;
+
+/* Build options.  A zero-initialised struct (or NULL) means: resident CSR, coordinates kept. */
+typedef struct {
+    /* 0: every row resident in one window.  > 0: rows are split into hub windows whose CSR
+     * (5 bytes per edge) is at most tile_bytes (a single longer row gets a window of its own), and
+     * counting runs as a loop over (hub window, search window) tiles (§III.5.3). */
+    int64_t tile_bytes;
+    /* nonzero (with tile_bytes > 0): the CSR lives in pinned host memory and only the active
+     * windows of a tile are copied to the device (out-of-core mode, §III.5.3). */
+    int32_t host_csr;
+    /* nonzero: drop the sorted coordinates after the build (gtc_count_4pcf_parity then fails
+     * with GTC_E_INVALID).  Zero keeps them. */
+    int32_t drop_coords;
+} gtc_options;
+
+/* Run statistics.  Counts refer to one call; byte figures are algorithmic (see the
+ * description of q_alg_bytes), times are HIP-event times on the call's stream. */
+typedef struct {
+    int64_t n;                 /* points */
+    int64_t edges;             /* undirected edges E (= forward edges, stored once) */
+    int64_t max_out_degree;    /* max forward degree d+(i) = |{j in N(i): j > i}| */
+    int64_t merge_walks;       /* hub-spoke intersections performed (forward edges walked) */
+    int64_t spoke_elements;    /* sum over walks of d+(j): spoke-row elements available to walk */
+    int64_t tiles;             /* kernel launches of the enumeration (1 when resident) */
+    int64_t windows;           /* hub windows */
+    uint64_t triangles;        /* triangles counted (3pCF) */
+    uint64_t cliques4;         /* 4-cliques counted (4pCF) */
+    double q_alg_bytes;        /* 3pCF algorithmic bytes: 5E + 4*sum d+(j) over walks + triangles */
+    int32_t weight_scale;      /* s of the weighted sums (0 when unweighted) */
+    int32_t reserved;
+    double build_ms;           /* gtc_build_graph: whole call */
+    double kernel_ms;          /* enumeration kernels only (sum over tiles) */
+    double count_ms;           /* count call: whole call */
+    double h2d_ms;             /* out-of-core window copies */
+} gtc_stats;
+
+/* Build the neighbour graph of n points (§II.1, Eq.(1)).
+ *   d_xyz     device int32 [n][3], coordinates in [0, 2^20) (checked on the device:
+ *             GTC_E_INVALID if any is outside).  Not retained: the graph keeps its own copy.
+ *   n         0 <= n < 2^31.
+ *   h_edges_sq host int64 [nbins+1], strictly increasing, e_0 >= 0, e_nbins <= 3*2^40 + 1.
+ *   nbins     1..GTC_MAX_BINS.
+ *   opt       may be NULL.
+ *   out       receives the handle (NULL on failure).
+ * Internal labels are the cell-sorted order (cells of side >= r_max); rows hold the forward
+ * neighbours (j > i) ascending, with a bin byte per edge. */
+int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, int32_t nbins,
+                    const gtc_options *opt, void *hip_stream, gtc_graph *out);
+
+/* Binned triangle counts, the 3pCF numerator (§II.2, merge intersection §III.1).
+ *   d_w        device fp64 [n] weights in the caller's (original) labels, or NULL.  Must be
+ *              finite (GTC_E_INVALID otherwise).
+ *   d_counts   device uint64 [gtc_num_configs(3, nbins)].
+ *   d_weighted device fp64 [same], required iff d_w != NULL.
+ *   st         may be NULL. */
+int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d_weighted,
+                   gtc_stats *st, void *hip_stream);
+
+/* Binned 4-clique counts split by parity (§II.2, §III.1.1, §III.2).  Needs nbins <=
+ * GTC_MAX_BINS_4PCF and the coordinates (not dropped).
+ *   d_even     device uint64 [gtc_num_configs(4, nbins)]: every tetrahedron.
+ *   d_odd      device int64  [same]: signed handedness sum. */
+int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
+                          void *hip_stream);
+
+/* Number of configurations: C(nbins+2, 3) for order 3, C(nbins+5, 6) for order 4; -1 if the
+ * order or nbins is out of range. */
+int64_t gtc_num_configs(int32_t order, int32_t nbins);
+
+/* The bins of every configuration in rank order: h_bins int32 [n_cfg][order == 3 ? 3 : 6]
+ * (host), each row nondecreasing. */
+int gtc_config_bins(int32_t order, int32_t nbins, int32_t *h_bins);
+
+/* Copy the graph out to host memory (for tests and inspection).
+ *   h_row_ptr int64 [n+1], h_col int32 [E], h_bin uint8 [E]: forward CSR in internal labels;
+ *   h_perm    int32 [n]: h_perm[internal] = original label.  Any pointer may be NULL. */
+int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h_bin,
+                     int32_t *h_perm);
+
+/* Graph-level statistics (n, edges, max_out_degree, windows, spoke_elements, build_ms). */
+int gtc_graph_stats(gtc_graph g, gtc_stats *st);
+
+/* Free a graph (NULL is a no-op).  Device memory is released in order on the build stream. */
+void gtc_graph_free(gtc_graph g);
+
+/* Static description of a status code, and the detail of the last failure on this thread. */
+const char *gtc_status_string(int status);
+const char *gtc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GTC_H */

@@ -1,0 +1,98 @@
+"""The C ABI on the CPU: the library loads, exports everything include/gtc.h declares, and rejects
+bad arguments with GTC_E_INVALID before touching a GPU.  Configuration tables are checked against
+itertools (nondecreasing tuples in lexicographic order)."""
+import ctypes as C
+import itertools
+import subprocess
+from math import comb
+
+import numpy as np
+import pytest
+
+import graph_triangle_counting_amd as gtc
+
+
+def test_library_exports_every_declared_function():
+    declared = gtc.header_functions()
+    assert len(declared) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", gtc.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    L = gtc.lib()
+    for f in declared:
+        assert hasattr(L, f)
+
+
+def test_num_configs():
+    for nb in (1, 2, 10, 30, 255):
+        assert gtc.num_configs(3, nb) == comb(nb + 2, 3)
+    for nb in (1, 4, 8, 16):
+        assert gtc.num_configs(4, nb) == comb(nb + 5, 6)
+    assert gtc.lib().gtc_num_configs(4, 17) == -1
+    assert gtc.lib().gtc_num_configs(3, 0) == -1
+    assert gtc.lib().gtc_num_configs(5, 3) == -1
+
+
+@pytest.mark.parametrize("order,nb", [(3, 1), (3, 7), (3, 20), (4, 3), (4, 8)])
+def test_config_bins_lexicographic(order, nb):
+    k = 3 if order == 3 else 6
+    want = np.array(list(itertools.combinations_with_replacement(range(nb), k)), np.int32)
+    np.testing.assert_array_equal(gtc.config_bins(order, nb), want)
+
+
+def _build(xyz_ptr, n, edges, nb, opt=None):
+    L = gtc.lib()
+    h = C.c_void_p()
+    e = np.ascontiguousarray(edges, dtype=np.int64) if edges is not None else None
+    rc = L.gtc_build_graph(xyz_ptr, n, e.ctypes.data_as(C.c_void_p) if e is not None else None,
+                           nb, C.byref(opt) if opt else None, None, C.byref(h))
+    return rc, h
+
+
+def test_build_rejects_bad_arguments_without_gpu():
+    fake = C.c_void_p(0x1000)  # never dereferenced: every case fails before any device work
+    cases = [
+        (None, 10, [0, 5, 10], 2),            # null coordinates with n > 0
+        (fake, -1, [0, 5, 10], 2),            # negative n
+        (fake, 1 << 31, [0, 5, 10], 2),       # n too large
+        (fake, 10, None, 2),                  # null edges
+        (fake, 10, [0, 5, 10], 0),            # nbins 0
+        (fake, 10, [0] + list(range(1, 257)), 256),  # nbins > 255
+        (fake, 10, [-1, 5, 10], 2),           # negative first edge
+        (fake, 10, [0, 5, 5], 2),             # not strictly increasing
+        (fake, 10, [0, 10, 5], 2),
+        (fake, 10, [0, 5, 3 * (1 << 40) + 2], 2),  # beyond the largest squared distance
+    ]
+    for ptr, n, edges, nb in cases:
+        rc, h = _build(ptr, n, edges, nb)
+        assert rc == gtc.GTC_E_INVALID, (n, edges, nb)
+        assert not h.value
+        assert gtc.lib().gtc_last_error()
+    rc, _ = _build(fake, 10, [0, 5, 10], 2, gtc.Options(-5, 0, 0))
+    assert rc == gtc.GTC_E_INVALID
+    rc, _ = _build(fake, 10, [0, 5, 10], 2, gtc.Options(0, 1, 0))
+    assert rc == gtc.GTC_E_INVALID
+    L = gtc.lib()
+    assert L.gtc_build_graph(fake, 10, None, 2, None, None, None) == gtc.GTC_E_INVALID
+
+
+def test_count_rejects_bad_arguments_without_gpu():
+    L = gtc.lib()
+    st = gtc.Stats()
+    fake = C.c_void_p(0x1000)
+    assert L.gtc_count_3pcf(None, None, fake, None, C.byref(st), None) == gtc.GTC_E_INVALID
+    assert L.gtc_count_4pcf_parity(None, fake, fake, C.byref(st), None) == gtc.GTC_E_INVALID
+    assert L.gtc_graph_export(None, None, None, None, None) == gtc.GTC_E_INVALID
+    assert L.gtc_graph_stats(None, C.byref(st)) == gtc.GTC_E_INVALID
+    L.gtc_graph_free(None)  # no-op
+    assert L.gtc_config_bins(3, 5, None) == gtc.GTC_E_INVALID
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.gtc_status_string(code)
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        gtc.Graph(torch.zeros((4, 3), dtype=torch.int32), [0, 10])
