@@ -120,12 +120,27 @@ struct StatsOut {
     unsigned long long n_hubs;
 };
 
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) {
+        const unsigned long long o = __shfl_xor(v, d, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
 __global__ void __launch_bounds__(256)
     k_degstats(int32_t n, const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col,
                const int32_t *__restrict__ deg, const int32_t *__restrict__ key_s,
                const int32_t *__restrict__ cell_start, Grid gr, int64_t *__restrict__ work,
                StatsOut *out) {
     constexpr int L = 16;
+    __shared__ unsigned long long red[5][256 / kWave];
     const int sub = threadIdx.x & (L - 1);
     const int64_t hub0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / L;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x / L;
@@ -150,12 +165,35 @@ __global__ void __launch_bounds__(256)
             }
         }
     }
-    if (sub == 0) {
-        atomicMax(&out->max_deg, my_max_deg);
-        atomicMax(&out->max_domain, my_max_dom);
-        atomicAdd(&out->spoke_elements, my_sum);
-        atomicAdd(&out->walks, my_walks);
-        atomicAdd(&out->n_hubs, my_hubs);
+    // block reduction, then one atomic per quantity per block
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    my_max_deg = wave_max_u64(my_max_deg);
+    my_max_dom = wave_max_u64(my_max_dom);
+    my_sum = wave_sum_u64(my_sum);
+    my_walks = wave_sum_u64(my_walks);
+    my_hubs = wave_sum_u64(my_hubs);
+    if (lane == 0) {
+        red[0][wid] = my_max_deg;
+        red[1][wid] = my_max_dom;
+        red[2][wid] = my_sum;
+        red[3][wid] = my_walks;
+        red[4][wid] = my_hubs;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long v[5] = {0, 0, 0, 0, 0};
+        for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+            v[0] = red[0][w] > v[0] ? red[0][w] : v[0];
+            v[1] = red[1][w] > v[1] ? red[1][w] : v[1];
+            v[2] += red[2][w];
+            v[3] += red[3][w];
+            v[4] += red[4][w];
+        }
+        atomicMax(&out->max_deg, v[0]);
+        atomicMax(&out->max_domain, v[1]);
+        atomicAdd(&out->spoke_elements, v[2]);
+        atomicAdd(&out->walks, v[3]);
+        atomicAdd(&out->n_hubs, v[4]);
     }
 }
 
@@ -345,7 +383,7 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     if (n > 0) {
         hipLaunchKernelGGL(k_pairs<true>, dim3(grid_for(n, 256)), dim3(256), 0, s, pa);
         STEP_HIP(hipGetLastError());
-        const int64_t dsb = std::min<int64_t>((n * 16 + 255) / 256, 65535);
+        const int64_t dsb = std::min<int64_t>((n * 16 + 255) / 256, 2048);
         hipLaunchKernelGGL(k_degstats, dim3((unsigned)dsb), dim3(256), 0, s, (int32_t)n, G->row_ptr,
                            G->col, G->deg, G->key_s, G->cell_start, gr, G->work, d_stats);
         STEP_HIP(hipGetLastError());

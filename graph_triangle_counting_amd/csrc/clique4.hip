@@ -45,9 +45,9 @@ __device__ __forceinline__ void wave_lds_sync4() {
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) / 16 * 16; }
 
-// per-workgroup part: even u32[ncfg], odd i32[ncfg], binomials C[22][8]
-__host__ __device__ inline size_t clique_lds_fixed(int ncfg) {
-    return align16(4 * (size_t)ncfg) * 2 + 22 * 8 * 4;
+// per-workgroup part: even u32[ncfg], odd i32[ncfg] (unless the bins are global), binomials C[22][8]
+__host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh) {
+    return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 22 * 8 * 4;
 }
 // per-wave part: position map, row coordinates, hub-edge bins, bitset rows
 __host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int words) {
@@ -94,14 +94,17 @@ __device__ __forceinline__ int edge_bin(int64_t d2, const int64_t *se, int nb) {
     return l;
 }
 
+// GH: bins go straight to global memory (configuration counts too large for LDS).
+template <bool GH>
 __global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *edges) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int64_t se[GTC_MAX_BINS_4PCF + 1];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    const size_t hist_bytes = GH ? 0 : align16(4 * (size_t)a.ncfg);
     uint32_t *ev = reinterpret_cast<uint32_t *>(smem);
-    int32_t *od = reinterpret_cast<int32_t *>(smem + align16(4 * (size_t)a.ncfg));
-    int32_t *binom = reinterpret_cast<int32_t *>(smem + 2 * align16(4 * (size_t)a.ncfg));
-    unsigned char *wbase = smem + clique_lds_fixed(a.ncfg) +
+    int32_t *od = reinterpret_cast<int32_t *>(smem + hist_bytes);
+    int32_t *binom = reinterpret_cast<int32_t *>(smem + 2 * hist_bytes);
+    unsigned char *wbase = smem + clique_lds_fixed(a.ncfg, GH) +
                            (size_t)wid * clique_lds_wave(a.map_bytes, a.max_m, a.words);
     uint16_t *pmap = reinterpret_cast<uint16_t *>(wbase);
     int4 *rc = reinterpret_cast<int4 *>(wbase + a.map_bytes);
@@ -110,10 +113,11 @@ __global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *ed
                                                  align16((size_t)a.max_m));
     const int N = a.nb + 5;  // 6-combinations of [0, N) <-> nondecreasing 6-tuples of [0, nb)
 
-    for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
-        ev[t] = 0;
-        od[t] = 0;
-    }
+    if (!GH)
+        for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
+            ev[t] = 0;
+            od[t] = 0;
+        }
     for (int t = threadIdx.x; t <= a.nb; t += blockDim.x) se[t] = edges[t];
     for (int t = threadIdx.x; t < 22 * 8; t += blockDim.x) {
         const int x = t / 8, r = t % 8;
@@ -211,8 +215,13 @@ __global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *ed
                         int64_t key[4] = {dia + dib + dic, dia + dab + dac, dib + dab + dbc,
                                           dic + dac + dbc};
                         const int sgn = chirality(p, key);
-                        atomicAdd(&ev[rank], 1u);
-                        if (sgn) atomicAdd(&od[rank], sgn);
+                        if (GH) {
+                            atomicAdd(&a.even[rank], 1ull);
+                            if (sgn) atomicAdd(&a.odd[rank], (unsigned long long)(long long)sgn);
+                        } else {
+                            atomicAdd(&ev[rank], 1u);
+                            if (sgn) atomicAdd(&od[rank], sgn);
+                        }
                         ++my_cl;
                     }
                 }
@@ -222,7 +231,7 @@ __global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *ed
 #pragma unroll
         for (int dd = kWave / 2; dd > 0; dd >>= 1) tot += __shfl_xor(tot, dd, kWave);
         wave_cl += tot;
-        if (wave_cl >= a.flush_at) {
+        if (!GH && wave_cl >= a.flush_at) {
             for (int t = lane; t < a.ncfg; t += kWave) {
                 const uint32_t v = atomicExch(&ev[t], 0u);
                 if (v) atomicAdd(&a.even[t], (unsigned long long)v);
@@ -233,6 +242,7 @@ __global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *ed
         }
         wave_lds_sync4();
     }
+    if (GH) return;
     __syncthreads();
     for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
         const uint32_t v = ev[t];
@@ -273,7 +283,9 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     GTC_HIP_CHECK(hipGetDevice(&dev));
     GTC_HIP_CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     GTC_HIP_CHECK(hipDeviceGetAttribute(&ldsmax, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
-    const size_t fixed = clique_lds_fixed(a.ncfg), per = clique_lds_wave(a.map_bytes, a.max_m, a.words);
+    // LDS bins unless they would take more than half of a workgroup's LDS
+    const bool GH = clique_lds_fixed(a.ncfg, false) > (size_t)ldsmax / 2;
+    const size_t fixed = clique_lds_fixed(a.ncfg, GH), per = clique_lds_wave(a.map_bytes, a.max_m, a.words);
     int waves = 4;
     const size_t static_lds = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
     while (waves > 1 && static_lds + fixed + waves * per > (size_t)ldsmax) waves >>= 1;
@@ -286,11 +298,11 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     const unsigned long long mm = (unsigned long long)a.max_m;
     const unsigned long long max_hub = mm * (mm - 1) * (mm - 2) / 6;
     const unsigned long long budget = 0x7fffffffull / (unsigned long long)waves;
-    if (max_hub >= budget / 2) {
+    if (!GH && max_hub >= budget / 2) {
         set_error("4pCF: a hub with %d forward neighbours could overflow the 32-bit LDS bins", a.max_m);
         return GTC_E_UNSUPPORTED;
     }
-    a.flush_at = (unsigned int)(budget - max_hub);
+    a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub);
 
     unsigned int *queue = nullptr;
     GTC_TRY(dev_alloc_n(&queue, 1, s));
@@ -299,19 +311,22 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     hipEvent_t e0 = nullptr, e1 = nullptr;
     float kms = 0.f;
     if (!rc && G->n_hubs > 0) {
+        const void *kfn = GH ? reinterpret_cast<const void *>(&k_clique4<true>)
+                             : reinterpret_cast<const void *>(&k_clique4<false>);
         if (lds > 65536)
-            (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_clique4),
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            (void)hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         int per_cu = 0;
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&k_clique4), waves * kWave, lds);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, waves * kWave, lds);
         if (per_cu < 1) per_cu = 1;
         int64_t blocks = std::min<int64_t>((int64_t)cus * per_cu, (G->n_hubs + waves - 1) / waves);
         (void)hipEventCreate(&e0);
         (void)hipEventCreate(&e1);
         (void)hipEventRecord(e0, s);
-        hipLaunchKernelGGL(k_clique4, dim3((unsigned)std::max<int64_t>(blocks, 1)),
-                           dim3(waves * kWave), lds, s, a, (const int64_t *)G->d_edges);
+        const dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(waves * kWave);
+        if (GH)
+            hipLaunchKernelGGL(k_clique4<true>, grid, block, lds, s, a, (const int64_t *)G->d_edges);
+        else
+            hipLaunchKernelGGL(k_clique4<false>, grid, block, lds, s, a, (const int64_t *)G->d_edges);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) rc = hip_fail(e, "k_clique4 launch", __FILE__, __LINE__);
         (void)hipEventRecord(e1, s);

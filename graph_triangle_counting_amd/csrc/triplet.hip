@@ -17,7 +17,9 @@
 // accumulators, so the sum is exact and independent of order (the pages accumulate fp atomics,
 // §III.5.2, and see order-dependent last digits, §IV.8).
 #include <algorithm>
+#include <climits>
 #include <cmath>
+#include <vector>
 
 #include "gtc_internal.h"
 
@@ -37,7 +39,9 @@ struct TripletArgs {
     const int32_t *hubs;  // hubs of this launch, heaviest first
     int32_t n_hubs;
     int32_t nb, ncfg;
-    int32_t map_bytes;  // per-wave map, multiple of 16, >= every hub's domain size
+    int32_t map_bytes;   // per-wave map (bytes), multiple of 16, covers every hub's domain
+    int32_t wave_bytes;  // per-wave LDS region: map, spoke chunk, (weighted) hub row
+    int32_t max_m;       // longest forward row
     const int32_t *key_s;
     const int32_t *cell_start;
     const int64_t *work;
@@ -70,9 +74,13 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 
 // LDS layout: counts u32[ncfg] | (weighted) lo u64[ncfg], hi u64[ncfg] | A i32[256], B i32[256]
 //             | nw maps of map_bytes
-__host__ __device__ inline size_t triplet_lds_fixed(int ncfg, bool weighted) {
-    size_t b = align_up(sizeof(uint32_t) * ncfg, 16);
-    if (weighted) b += 2 * align_up(sizeof(unsigned long long) * ncfg, 16);
+// (with a global histogram, GH, only the rank tables and the maps are in LDS)
+__host__ __device__ inline size_t triplet_lds_fixed(int ncfg, bool weighted, bool gh) {
+    size_t b = 0;
+    if (!gh) {
+        b += align_up(sizeof(uint32_t) * ncfg, 16);
+        if (weighted) b += 2 * align_up(sizeof(unsigned long long) * ncfg, 16);
+    }
     return b + 2 * 256 * sizeof(int32_t);
 }
 
@@ -93,15 +101,37 @@ __device__ void flush_hist(const TripletArgs &a, uint32_t *hc, unsigned long lon
     }
 }
 
-template <bool W>
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Per-wave LDS region: hub map | chunk of 64 spokes | (weighted) the hub row's bins and weights.
+//   map    : u8 bin+1 per domain label, or (weighted) u16 row position+1
+//   chunk  : cpre u32[65] flat start of each spoke's row, cbase i64[64] (row start - flat start),
+//            cbij u8[64] spoke bins, (weighted) cw f64[64] spoke weights
+constexpr int kChunkPre = 0, kChunkBase = 272, kChunkBij = 784, kChunkW = 848;
+__host__ __device__ inline size_t chunk_bytes(bool weighted) { return weighted ? 1360 : 848; }
+__host__ __device__ inline size_t hubrow_bytes(bool weighted, int max_m) {
+    return weighted ? align_up(8 * (size_t)max_m, 16) + align_up((size_t)max_m, 16) : 0;
+}
+
+constexpr int kUnroll = 4;  // loads in flight per lane
+
+// GH: bins go straight to the global histogram (configuration counts too large for LDS).
+template <bool W, bool GH>
 __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     size_t off = 0;
     uint32_t *hc = reinterpret_cast<uint32_t *>(smem);
-    off += align_up(sizeof(uint32_t) * a.ncfg, 16);
+    if (!GH) off += align_up(sizeof(uint32_t) * a.ncfg, 16);
     unsigned long long *hlo = nullptr, *hhi = nullptr;
-    if (W) {
+    if (W && !GH) {
         hlo = reinterpret_cast<unsigned long long *>(smem + off);
         off += align_up(sizeof(unsigned long long) * a.ncfg, 16);
         hhi = reinterpret_cast<unsigned long long *>(smem + off);
@@ -110,12 +140,22 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
     int32_t *rA = reinterpret_cast<int32_t *>(smem + off);
     int32_t *rB = rA + 256;
     off += 2 * 256 * sizeof(int32_t);
-    uint8_t *map = smem + off + (size_t)wid * a.map_bytes;
+    unsigned char *wb = smem + off + (size_t)wid * a.wave_bytes;
+    uint8_t *map8 = wb;
+    uint16_t *map16 = reinterpret_cast<uint16_t *>(wb);
+    unsigned char *ck = wb + a.map_bytes;
+    uint32_t *cpre = reinterpret_cast<uint32_t *>(ck + kChunkPre);
+    int64_t *cbase = reinterpret_cast<int64_t *>(ck + kChunkBase);
+    uint8_t *cbij = ck + kChunkBij;
+    double *cw = reinterpret_cast<double *>(ck + kChunkW);
+    double *rw = reinterpret_cast<double *>(ck + chunk_bytes(true));
+    uint8_t *rbn = ck + chunk_bytes(true) + align_up(8 * (size_t)a.max_m, 16);
 
-    for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
-        hc[t] = 0;
-        if (W) hlo[t] = hhi[t] = 0;
-    }
+    if (!GH)
+        for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
+            hc[t] = 0;
+            if (W) hlo[t] = hhi[t] = 0;
+        }
     if (threadIdx.x == 0) rank3_tables(a.nb, rA, rB);
     __syncthreads();
 
@@ -131,9 +171,10 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
         HubDomain dom;
         hub_domain(i, a.key_s[i], a.gr, a.cell_start, dom);
 
-        // hub side of the walk: clear the map over the domain, then mark N+(i) with bin + 1
-        uint32_t *map32 = reinterpret_cast<uint32_t *>(map);
-        for (int t = lane; t < ((dom.size + 3) >> 2); t += kWave) map32[t] = 0u;
+        // hub side of the walk: clear the map over the domain, then mark N+(i)
+        uint32_t *map32 = reinterpret_cast<uint32_t *>(wb);
+        const int map_words = ((W ? 2 : 1) * dom.size + 3) >> 2;
+        for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
         wave_lds_sync();
         const int32_t *hrow = a.col_h + (rb - a.base_h);
         const uint8_t *hbin = a.bin_h + (rb - a.base_h);
@@ -143,10 +184,17 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
 #pragma unroll
             for (int t = 1; t < 5; ++t)
                 if (k >= dom.lo[t]) d = dom.delta[t];
-            map[k + d] = (uint8_t)(hbin[p] + 1);
+            if (W) {
+                map16[k + d] = (uint16_t)(p + 1);
+                rw[p] = a.w_s[k];
+                rbn[p] = hbin[p];
+            } else {
+                map8[k + d] = (uint8_t)(hbin[p] + 1);
+            }
         }
         wave_lds_sync();
         const int32_t hub_hi = hrow[m - 1];
+        const double wi = W ? a.w_s[i] : 0.0;
 
         // spokes of this tile: hub-row positions [p_lo, p_hi) with j in [s_lo, s_hi)
         int32_t p_lo = 0, p_hi = m;
@@ -159,74 +207,110 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
             p_hi = l;
         }
 
-        // lane groups of G lanes share a spoke; G follows the hub's mean spoke-row length
-        const int64_t avg = a.work[i] / m;
-        const int lg = avg >= 48 ? 6 : avg >= 24 ? 5 : avg >= 12 ? 4 : 3;
-        const int G = 1 << lg, ng = kWave >> lg, gl = lane & (G - 1);
-        int32_t p = p_lo + (lane >> lg);
-        int64_t e = 0, ee = 0;
-        int32_t bij = 0;
-        double wi = 0.0, wj = 0.0;
-        if (W) wi = a.w_s[i];
-        auto load_spoke = [&]() {
-            const int32_t j = hrow[p];
-            bij = hbin[p];
-            e = a.row_ptr[j] + gl;
-            ee = a.row_ptr[j + 1];
-            if (W) wj = a.w_s[j];
-        };
-        if (p < p_hi) load_spoke();
         unsigned int my_hits = 0;
-        while (p < p_hi) {
-            bool adv = true;
-            if (e < ee) {
-                const int32_t k = a.col_s[e - a.base_s];
-                if (k <= hub_hi) {
-                    adv = false;
+        // spokes in chunks of 64: lane q fetches spoke q's row bounds, a wave scan lays the 64
+        // spoke rows end to end, and the lanes walk that flat range with kUnroll loads in flight.
+        for (int32_t p0 = p_lo; p0 < p_hi; p0 += kWave) {
+            const int32_t p = p0 + lane;
+            int64_t sb = 0;
+            int32_t len = 0, bj = 0;
+            double wj = 0.0;
+            if (p < p_hi) {
+                const int32_t j = hrow[p];
+                bj = hbin[p];
+                sb = a.row_ptr[j];
+                len = (int32_t)(a.row_ptr[j + 1] - sb);
+                if (W) wj = a.w_s[j];
+            }
+            const int32_t incl = wave_incl_scan(len, lane);
+            const int32_t total = __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));
+            cpre[lane] = (uint32_t)(incl - len);
+            if (lane == kWave - 1) cpre[kWave] = (uint32_t)incl;
+            cbase[lane] = sb - (incl - len);
+            cbij[lane] = (uint8_t)bj;
+            if (W) cw[lane] = wj;
+            wave_lds_sync();
+            // owner spoke of flat index t: the last q with cpre[q] <= t (then t < cpre[q+1])
+            int q = 0;
+            {
+                int hi = kWave;
+                while (hi - q > 1) {
+                    const int md = (q + hi) >> 1;
+                    if ((int32_t)cpre[md] <= lane) q = md; else hi = md;
+                }
+            }
+            for (int32_t t0 = 0; t0 < total; t0 += kWave * kUnroll) {
+                int32_t kk[kUnroll], bb[kUnroll], qq[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int32_t t = t0 + u * kWave + lane;
+                    kk[u] = INT32_MAX;
+                    bb[u] = 0;
+                    qq[u] = q;
+                    if (t < total) {
+                        while ((int32_t)cpre[q + 1] <= t) ++q;
+                        qq[u] = q;
+                        const int64_t e = cbase[q] + t - a.base_s;
+                        kk[u] = a.col_s[e];
+                        bb[u] = a.bin_s[e];
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int32_t k = kk[u];
+                    if (k > hub_hi) continue;  // past the hub's last neighbour (or no element)
                     int32_t d = dom.delta[0], lim = dom.hi[0];
 #pragma unroll
                     for (int t = 1; t < 5; ++t)
                         if (k >= dom.lo[t]) { d = dom.delta[t]; lim = dom.hi[t]; }
-                    if (k < lim) {
-                        const uint32_t v = map[k + d];
-                        if (v) {
-                            const int32_t bik = (int32_t)v - 1, bjk = a.bin_s[e - a.base_s];
-                            const int32_t x = min(bij, min(bik, bjk)), z = max(bij, max(bik, bjk));
-                            const int32_t y = bij + bik + bjk - x - z;
-                            const int32_t c = rA[x] + rB[y] + z;
-                            atomicAdd(&hc[c], 1u);
-                            if (W) {
-                                const double wk = a.w_s[k];
-                                const double x1 = fmin(wi, wj), x2 = fmax(wi, wj);
-                                const double w1 = fmin(x1, wk), tt = fmax(x1, wk);
-                                const double w2 = fmin(x2, tt), w3 = fmax(x2, tt);
-                                const double pr = __dmul_rn(__dmul_rn(w1, w2), w3);
-                                const double q = rint(__dmul_rn(pr, a.two_s));      // exact integer
-                                const double qh = floor(__dmul_rn(q, 0x1p-28));    // in [-2^29, 2^29)
-                                const double ql = __fma_rn(-qh, 0x1p28, q);        // in [0, 2^28)
-                                atomicAdd(&hlo[c], (unsigned long long)ql);
-                                atomicAdd(&hhi[c], (unsigned long long)((long long)qh + (1ll << 29)));
-                            }
-                            ++my_hits;
+                    if (k >= lim) continue;  // in a gap between the hub's stencil runs
+                    const uint32_t v = W ? (uint32_t)map16[k + d] : (uint32_t)map8[k + d];
+                    if (!v) continue;
+                    const int32_t bij = cbij[qq[u]];
+                    const int32_t bik = W ? (int32_t)rbn[v - 1] : (int32_t)v - 1;
+                    const int32_t bjk = bb[u];
+                    const int32_t x = min(bij, min(bik, bjk)), z = max(bij, max(bik, bjk));
+                    const int32_t y = bij + bik + bjk - x - z;
+                    const int32_t c = rA[x] + rB[y] + z;
+                    if (GH) atomicAdd(&a.counts[c], 1ull);
+                    else atomicAdd(&hc[c], 1u);
+                    if (W) {
+                        const double wjj = cw[qq[u]], wk = rw[v - 1];
+                        const double x1 = fmin(wi, wjj), x2 = fmax(wi, wjj);
+                        const double w1 = fmin(x1, wk), tt = fmax(x1, wk);
+                        const double w2 = fmin(x2, tt), w3 = fmax(x2, tt);
+                        const double pr = __dmul_rn(__dmul_rn(w1, w2), w3);
+                        const double qv = rint(__dmul_rn(pr, a.two_s));     // exact integer
+                        const double qh = floor(__dmul_rn(qv, 0x1p-28));   // in [-2^29, 2^29)
+                        const double ql = __fma_rn(-qh, 0x1p28, qv);       // in [0, 2^28)
+                        const unsigned long long ul = (unsigned long long)ql;
+                        const unsigned long long uh = (unsigned long long)((long long)qh + (1ll << 29));
+                        if (GH) {
+                            add_u128(&a.limbs[4 * c], ul);
+                            add_u128(&a.limbs[4 * c + 2], uh);
+                        } else {
+                            atomicAdd(&hlo[c], ul);
+                            atomicAdd(&hhi[c], uh);
                         }
                     }
-                    e += G;
+                    ++my_hits;
                 }
             }
-            if (adv) {
-                p += ng;
-                if (p < p_hi) load_spoke();
-            }
+            wave_lds_sync();  // the next chunk overwrites the chunk arrays
         }
-        wave_hits += wave_sum(my_hits);
-        if (wave_hits >= a.flush_at) {
-            flush_hist<W>(a, hc, hlo, hhi, lane, kWave);
-            wave_hits = 0;
+        if (!GH) {
+            wave_hits += wave_sum(my_hits);
+            if (wave_hits >= a.flush_at) {
+                flush_hist<W>(a, hc, hlo, hhi, lane, kWave);
+                wave_hits = 0;
+            }
         }
         wave_lds_sync();  // this wave's map reads complete before the next hub clears it
     }
-    __syncthreads();
-    flush_hist<W>(a, hc, hlo, hhi, threadIdx.x, blockDim.x);
+    if (!GH) {
+        __syncthreads();
+        flush_hist<W>(a, hc, hlo, hhi, threadIdx.x, blockDim.x);
+    }
 }
 
 // ------------------------------------------------------------------ host side
@@ -252,26 +336,26 @@ struct TripletPlan {
     int blocks = 0;      // persistent grid
 };
 
-template <bool W>
+template <bool W, bool GH>
 static int plan_triplet(const TripletArgs &a, int64_t n_hubs, TripletPlan &pl) {
     DeviceLimits dl;
     GTC_TRY(device_limits(dl));
-    const size_t fixed = triplet_lds_fixed(a.ncfg, W);
+    const size_t fixed = triplet_lds_fixed(a.ncfg, W, GH);
     int waves = 4;
-    while (waves > 1 && fixed + (size_t)waves * a.map_bytes > dl.lds_per_block) waves >>= 1;
-    const size_t lds = fixed + (size_t)waves * a.map_bytes;
+    while (waves > 1 && fixed + (size_t)waves * a.wave_bytes > dl.lds_per_block) waves >>= 1;
+    const size_t lds = fixed + (size_t)waves * a.wave_bytes;
     if (lds > dl.lds_per_block) {
-        set_error("3pCF needs %zu bytes of LDS per workgroup (histogram %d configs, hub domain %d "
-                  "labels); the device allows %zu",
-                  lds, a.ncfg, a.map_bytes, dl.lds_per_block);
+        set_error("3pCF needs %zu bytes of LDS per workgroup (histogram %d configs, %d bytes per "
+                  "wave); the device allows %zu",
+                  lds, a.ncfg, a.wave_bytes, dl.lds_per_block);
         return GTC_E_UNSUPPORTED;
     }
     if (lds > 65536)
-        GTC_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void *>(&k_triplet<W>),
+        GTC_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void *>(&k_triplet<W, GH>),
                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
     int per_cu = 0;
     GTC_HIP_CHECK(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void *>(&k_triplet<W>), waves * kWave, lds));
+        &per_cu, reinterpret_cast<const void *>(&k_triplet<W, GH>), waves * kWave, lds));
     if (per_cu < 1) per_cu = 1;
     int64_t blocks = (int64_t)dl.cus * per_cu;
     const int64_t need = (n_hubs + waves - 1) / waves;
@@ -283,9 +367,9 @@ static int plan_triplet(const TripletArgs &a, int64_t n_hubs, TripletPlan &pl) {
     return GTC_OK;
 }
 
-template <bool W>
+template <bool W, bool GH>
 static int launch_triplet(const TripletArgs &a, const TripletPlan &pl, hipStream_t s) {
-    hipLaunchKernelGGL(k_triplet<W>, dim3(pl.blocks), dim3(pl.waves * kWave), pl.lds, s, a);
+    hipLaunchKernelGGL((k_triplet<W, GH>), dim3(pl.blocks), dim3(pl.waves * kWave), pl.lds, s, a);
     GTC_HIP_CHECK(hipGetLastError());
     return GTC_OK;
 }
@@ -362,7 +446,15 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.n_hubs = (int32_t)G->n_hubs;
     a.nb = nb;
     a.ncfg = (int32_t)ncfg;
-    a.map_bytes = (int32_t)align_up((size_t)std::max<int64_t>(G->max_domain, 1), 16);
+    a.max_m = (int32_t)std::max<int64_t>(G->max_deg, 1);
+    a.map_bytes = (int32_t)align_up((W ? 2 : 1) * (size_t)std::max<int64_t>(G->max_domain, 1), 16);
+    a.wave_bytes = (int32_t)(a.map_bytes + chunk_bytes(W) + hubrow_bytes(W, a.max_m));
+    if (W && G->max_deg >= 65535) {
+        set_error("weighted 3pCF: a forward row of %lld entries exceeds the 16-bit position map",
+                  (long long)G->max_deg);
+        cleanup();
+        return GTC_E_UNSUPPORTED;
+    }
     a.key_s = G->key_s;
     a.cell_start = G->cell_start;
     a.work = G->work;
@@ -375,21 +467,27 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
 
     float kms = 0.f;
     if (G->n_hubs > 0) {
+        // LDS histogram unless it would take more than half of a workgroup's LDS
+        DeviceLimits dl;
+        STEP(device_limits(dl));
+        const bool GH = triplet_lds_fixed(a.ncfg, W, false) > dl.lds_per_block / 2;
         TripletPlan pl;
-        STEP(W ? plan_triplet<true>(a, G->n_hubs, pl) : plan_triplet<false>(a, G->n_hubs, pl));
+        STEP(W ? (GH ? plan_triplet<true, true>(a, G->n_hubs, pl) : plan_triplet<true, false>(a, G->n_hubs, pl))
+               : (GH ? plan_triplet<false, true>(a, G->n_hubs, pl) : plan_triplet<false, false>(a, G->n_hubs, pl)));
         // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long max_hub_hits =
             (unsigned long long)G->max_deg * (unsigned long long)(G->max_deg - 1) / 2;
         const unsigned long long budget = 0xffffffffull / (unsigned long long)pl.waves;
-        if (max_hub_hits >= budget / 2) {
+        if (!GH && max_hub_hits >= budget / 2) {
             set_error("a hub has %lld forward neighbours; its triangles could overflow the 32-bit "
                       "LDS histogram", (long long)G->max_deg);
             cleanup();
             return GTC_E_UNSUPPORTED;
         }
-        a.flush_at = (unsigned int)(budget - max_hub_hits);
+        a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub_hits);
         STEP_HIP(hipEventRecord(ev0, s));
-        STEP(W ? launch_triplet<true>(a, pl, s) : launch_triplet<false>(a, pl, s));
+        STEP(W ? (GH ? launch_triplet<true, true>(a, pl, s) : launch_triplet<true, false>(a, pl, s))
+               : (GH ? launch_triplet<false, true>(a, pl, s) : launch_triplet<false, false>(a, pl, s)));
         STEP_HIP(hipEventRecord(ev1, s));
     }
     std::vector<unsigned long long> h_counts(ncfg), h_limbs(W ? 4 * ncfg : 0);

@@ -28,7 +28,7 @@ def say(*a):
 @pytest.mark.parametrize("kind,seed,n,r,nb", [
     ("uniform", 1, 3000, 60_000, 5),
     ("clustered", 2, 6000, 9_000, 7),
-    ("uniform", 3, 700, 400_000, 3),     # few cells per axis (g < 3 path)
+    ("uniform", 3, 700, 600_000, 3),     # two cells per axis (g < 3 path)
     ("clustered", 4, 5000, 300, 2),      # tiny radius: grid capped, cells much larger than r
 ])
 def test_graph_matches_oracle(gpu_available, kind, seed, n, r, nb):
