@@ -40,7 +40,12 @@ def main():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the counter has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr)
@@ -100,7 +105,9 @@ def main():
 
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "kernel": "k_triplet", "kernel_ms": k_avg, "q_alg_bytes": qalg[0]}
+                "kernel": "k_triplet", "kernel_ms": k_avg, "q_alg_bytes": qalg[0],
+                "launch": {"waves_per_wg": st["launch_waves"], "workgroups": st["launch_blocks"],
+                           "lds_bytes": st["launch_lds_bytes"]}}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -130,6 +137,19 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def copy_calibration(nbytes: int):
+    """A plain device copy of a known size: what FETCH_SIZE / WRITE_SIZE read for it scales the
+    counters of the enumeration kernel to bytes."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 3}), flush=True)
 
 
 def cpu_baseline(cfg, xyz, w, threads):

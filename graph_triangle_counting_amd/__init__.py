@@ -34,11 +34,13 @@ class Stats(C.Structure):
                 ("merge_walks", C.c_int64), ("spoke_elements", C.c_int64), ("tiles", C.c_int64),
                 ("windows", C.c_int64), ("triangles", C.c_uint64), ("cliques4", C.c_uint64),
                 ("q_alg_bytes", C.c_double), ("weight_scale", C.c_int32),
-                ("reserved", C.c_int32), ("build_ms", C.c_double), ("kernel_ms", C.c_double),
+                ("launch_waves", C.c_int32), ("launch_blocks", C.c_int32),
+                ("launch_lds_bytes", C.c_int32), ("launch_mode", C.c_int32),
+                ("launch_reserved", C.c_int32), ("build_ms", C.c_double), ("kernel_ms", C.c_double),
                 ("count_ms", C.c_double), ("h2d_ms", C.c_double)]
 
     def as_dict(self) -> dict:
-        return {f: getattr(self, f) for f, _ in self._fields_ if f != "reserved"}
+        return {f: getattr(self, f) for f, _ in self._fields_}
 
 
 _lib = None

@@ -33,12 +33,14 @@ void free_graph_buffers(gtc_graph_s *G) {
     dev_free(G->bin, s);
     dev_free(G->deg, s);
     dev_free(G->work, s);
+    dev_free(G->slot_off, s);
     dev_free(G->hubs, s);
     dev_free(G->d_edges, s);
     G->xyz_s = nullptr;
     G->key_s = nullptr;
     G->perm = G->cell_start = G->col = G->deg = G->hubs = nullptr;
     G->row_ptr = G->work = G->d_edges = nullptr;
+    G->slot_off = nullptr;
     G->bin = nullptr;
 }
 

@@ -57,6 +57,7 @@ struct PairArgs {
     const int64_t *row_ptr;  // emit pass input
     int32_t *col;
     uint8_t *bin;
+    uint32_t *slot_off;      // emit pass: [n][16] start of each forward cell slot in the row
 };
 
 // Exact squared distance as a double: coordinates differ by < 2^20, squares are < 2^40 and the
@@ -100,14 +101,28 @@ __global__ void __launch_bounds__(256) k_pairs(PairArgs a) {
             }
         }
     };
+    // slot 0: own cell (labels above i); slots 1..13: the forward cells in key order.  The emit
+    // pass records where each slot starts in the row (empty slots for cells outside the grid).
+    uint32_t so[16];
+    const int64_t w0 = w;
+    so[0] = 0;
     scan(i + 1, a.cell_start[c + 1]);
     for (int s = 0; s < 13; ++s) {
+        so[s + 1] = (uint32_t)(w - w0);
         const int x = cx + kFwd[s][2], y = cy + kFwd[s][1], z = cz + kFwd[s][0];
         if (x < 0 || y < 0 || x >= g || y >= g || z >= g) continue;
         const int32_t cc = (z * g + y) * g + x;
         scan(a.cell_start[cc], a.cell_start[cc + 1]);
     }
-    if (!EMIT) a.deg[i] = cnt;
+    if (!EMIT) {
+        a.deg[i] = cnt;
+    } else {
+        so[14] = (uint32_t)(w - w0);
+        so[15] = 0;
+        uint4 *dst = reinterpret_cast<uint4 *>(a.slot_off + (int64_t)i * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[q] = make_uint4(so[4 * q], so[4 * q + 1], so[4 * q + 2], so[4 * q + 3]);
+    }
 }
 
 // Per-hub statistics, sixteen lanes per hub: work[i] = sum of d+(j) over the row of i, and the
@@ -118,6 +133,7 @@ struct StatsOut {
     unsigned long long spoke_elements;
     unsigned long long walks;
     unsigned long long n_hubs;
+    unsigned long long max_band;
 };
 
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
@@ -140,11 +156,12 @@ __global__ void __launch_bounds__(256)
                const int32_t *__restrict__ cell_start, Grid gr, int64_t *__restrict__ work,
                StatsOut *out) {
     constexpr int L = 16;
-    __shared__ unsigned long long red[5][256 / kWave];
+    __shared__ unsigned long long red[6][256 / kWave];
     const int sub = threadIdx.x & (L - 1);
     const int64_t hub0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / L;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x / L;
-    unsigned long long my_max_deg = 0, my_max_dom = 0, my_sum = 0, my_walks = 0, my_hubs = 0;
+    unsigned long long my_max_deg = 0, my_max_dom = 0, my_sum = 0, my_walks = 0, my_hubs = 0,
+                       my_max_band = 0;
     for (int64_t h = hub0; h < n; h += stride) {
         const int64_t b = row_ptr[h], e = row_ptr[h + 1];
         int64_t s = 0;
@@ -159,6 +176,10 @@ __global__ void __launch_bounds__(256)
             HubDomain dom;
             hub_domain((int32_t)h, key_s[h], gr, cell_start, dom);
             my_max_dom = dom.size > (int64_t)my_max_dom ? dom.size : my_max_dom;
+            for (int t = 0; t < 5; ++t) {
+                const unsigned long long bs = (unsigned long long)(dom.hi[t] - dom.lo[t]);
+                my_max_band = bs > my_max_band ? bs : my_max_band;
+            }
             if (m >= 2 && s > 0) {
                 my_walks += m;
                 my_hubs += 1;
@@ -172,7 +193,9 @@ __global__ void __launch_bounds__(256)
     my_sum = wave_sum_u64(my_sum);
     my_walks = wave_sum_u64(my_walks);
     my_hubs = wave_sum_u64(my_hubs);
+    my_max_band = wave_max_u64(my_max_band);
     if (lane == 0) {
+        red[5][wid] = my_max_band;
         red[0][wid] = my_max_deg;
         red[1][wid] = my_max_dom;
         red[2][wid] = my_sum;
@@ -181,19 +204,21 @@ __global__ void __launch_bounds__(256)
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned long long v[5] = {0, 0, 0, 0, 0};
+        unsigned long long v[6] = {0, 0, 0, 0, 0, 0};
         for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
             v[0] = red[0][w] > v[0] ? red[0][w] : v[0];
             v[1] = red[1][w] > v[1] ? red[1][w] : v[1];
             v[2] += red[2][w];
             v[3] += red[3][w];
             v[4] += red[4][w];
+            v[5] = red[5][w] > v[5] ? red[5][w] : v[5];
         }
         atomicMax(&out->max_deg, v[0]);
         atomicMax(&out->max_domain, v[1]);
         atomicAdd(&out->spoke_elements, v[2]);
         atomicAdd(&out->walks, v[3]);
         atomicAdd(&out->n_hubs, v[4]);
+        atomicMax(&out->max_band, v[5]);
     }
 }
 
@@ -297,6 +322,7 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     GTC_TRY(dev_alloc_n(&G->row_ptr, n + 1, s));
     GTC_TRY(dev_alloc_n(&G->deg, n, s));
     GTC_TRY(dev_alloc_n(&G->work, n, s));
+    GTC_TRY(dev_alloc_n(&G->slot_off, 16 * (size_t)n, s));
 
     // scratch: keys, slots, cell counts, error flag, stats
     int32_t *key = nullptr, *slot = nullptr, *ccount = nullptr, *err = nullptr;
@@ -380,6 +406,7 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     pa.row_ptr = G->row_ptr;
     pa.col = G->col;
     pa.bin = G->bin;
+    pa.slot_off = G->slot_off;
     if (n > 0) {
         hipLaunchKernelGGL(k_pairs<true>, dim3(grid_for(n, 256)), dim3(256), 0, s, pa);
         STEP_HIP(hipGetLastError());
@@ -396,6 +423,7 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     G->spoke_elements = (int64_t)hs.spoke_elements;
     G->walks = (int64_t)hs.walks;
     G->n_hubs = (int64_t)hs.n_hubs;
+    G->max_band = (int64_t)hs.max_band;
 
     STEP(dev_alloc_n(&G->hubs, G->n_hubs, s));
     if (n > 0 && G->n_hubs > 0) {

@@ -310,6 +310,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     a.queue = queue;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     float kms = 0.f;
+    int32_t launched_blocks = 0;
     if (!rc && G->n_hubs > 0) {
         const void *kfn = GH ? reinterpret_cast<const void *>(&k_clique4<true>)
                              : reinterpret_cast<const void *>(&k_clique4<false>);
@@ -323,6 +324,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         (void)hipEventCreate(&e1);
         (void)hipEventRecord(e0, s);
         const dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(waves * kWave);
+        launched_blocks = (int32_t)grid.x;
         if (GH)
             hipLaunchKernelGGL(k_clique4<true>, grid, block, lds, s, a, (const int64_t *)G->d_edges);
         else
@@ -345,6 +347,9 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     unsigned long long cl = 0;
     for (auto v : h_even) cl += v;
     if (st) {
+        st->launch_waves = waves;
+        st->launch_blocks = launched_blocks;
+        st->launch_lds_bytes = (int32_t)lds;
         st->cliques4 = cl;
         st->merge_walks = G->walks;
         st->tiles = G->n_hubs > 0 ? 1 : 0;

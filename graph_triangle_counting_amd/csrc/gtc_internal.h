@@ -10,6 +10,8 @@
 //   bin        uint8 [E]     radial bin of each edge (§II.1)
 //   deg        int32 [n]     forward degree d+(i)
 //   work       int64 [n]     sum of d+(j) over the row of i (spoke elements of hub i)
+//   slot_off   u32 [n][16]   where each of the 14 forward cell slots of row i starts (own cell,
+//                            then the 13 forward cells in key order); [14] is the row length
 //   hubs       int32 [n_hubs] hubs with at least one possible triangle, heaviest first
 #pragma once
 
@@ -144,6 +146,7 @@ struct gtc_graph_s {
     uint8_t *bin = nullptr;
     int32_t *deg = nullptr;
     int64_t *work = nullptr;
+    uint32_t *slot_off = nullptr;  // [n][16]: start of each forward cell slot in the row, [14] = end
     int32_t *hubs = nullptr;
     int64_t *d_edges = nullptr;  // device copy of the bin edges
     // scalars
@@ -151,6 +154,7 @@ struct gtc_graph_s {
     int64_t n_hubs = 0;
     int64_t max_deg = 0;
     int64_t max_domain = 0;
+    int64_t max_band = 0;        // longest label range of one key run of a hub domain
     int64_t spoke_elements = 0;  // sum of work over all hubs
     int64_t walks = 0;           // sum of d+(i) over hubs in the hub list
     bool coords_kept = true;

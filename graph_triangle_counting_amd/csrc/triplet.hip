@@ -19,6 +19,8 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "gtc_internal.h"
@@ -45,6 +47,8 @@ struct TripletArgs {
     const int32_t *key_s;
     const int32_t *cell_start;
     const int64_t *work;
+    const uint32_t *slot_off;  // [n][16] forward cell slot starts of every row
+    uint8_t band[145];         // banded walk: tlo[14][5], thi[14][5], smax[5]
     Grid gr;
     const double *w_s;  // weights, internal order (weighted only)
     double two_s;       // 2^s
@@ -81,7 +85,7 @@ __host__ __device__ inline size_t triplet_lds_fixed(int ncfg, bool weighted, boo
         b += align_up(sizeof(uint32_t) * ncfg, 16);
         if (weighted) b += 2 * align_up(sizeof(unsigned long long) * ncfg, 16);
     }
-    return b + 2 * 256 * sizeof(int32_t);
+    return b + 2 * 256 * sizeof(int32_t) + 160;  // rank tables, band table
 }
 
 // Exchange the workgroup histogram out to global memory.  Safe while other waves keep adding:
@@ -113,18 +117,29 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // Per-wave LDS region: hub map | chunk of 64 spokes | (weighted) the hub row's bins and weights.
 //   map    : u8 bin+1 per domain label, or (weighted) u16 row position+1
 //   chunk  : cpre u32[65] flat start of each spoke's row, cbase i64[64] (row start - flat start),
-//            cbij u8[64] spoke bins, (weighted) cw f64[64] spoke weights
-constexpr int kChunkPre = 0, kChunkBase = 272, kChunkBij = 784, kChunkW = 848;
-__host__ __device__ inline size_t chunk_bytes(bool weighted) { return weighted ? 1360 : 848; }
+//            cbij u8[64] spoke bins (weighted hubs read bins and weights from the hub row)
+constexpr int kChunkPre = 0, kChunkBase = 272, kChunkBij = 784;
+__host__ __device__ inline size_t chunk_bytes(bool) { return 848; }
 __host__ __device__ inline size_t hubrow_bytes(bool weighted, int max_m) {
     return weighted ? align_up(8 * (size_t)max_m, 16) + align_up((size_t)max_m, 16) : 0;
 }
 
-constexpr int kUnroll = 4;  // loads in flight per lane
+constexpr int kUnroll = 8;  // loads in flight per lane
 
-// GH: bins go straight to the global histogram (configuration counts too large for LDS).
-template <bool W, bool GH>
-__global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
+// Banded walk (grids of at least 3 cells per axis).  A hub's forward stencil is five key runs
+// ("bands"); band q holds the hub-row slots [kBandSlot[q], kBandSlot[q+1]) (own cell and the
+// next cell, then three rows of three cells).  A spoke sitting in hub slot s has its own forward
+// cell slots [tlo, thi) = band table[s][q] inside band q, so its elements there form one
+// contiguous piece of its row, found from the row's slot offsets, and every label in that piece
+// lies in band q's label range: the map offset is a single subtraction.
+__host__ __device__ constexpr int band_slot(int q) { return q == 0 ? 0 : 3 * q - 1; }
+
+// LDS fixed part: histogram | rank tables A, B (i32[256] each) | band table (tlo, thi [14][5],
+// smax [5]) | per-wave regions
+constexpr size_t kBandTableBytes = 160;
+
+template <bool W, bool GH, bool BANDED>
+__global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     size_t off = 0;
@@ -140,6 +155,8 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
     int32_t *rA = reinterpret_cast<int32_t *>(smem + off);
     int32_t *rB = rA + 256;
     off += 2 * 256 * sizeof(int32_t);
+    uint8_t *btab = smem + off;  // tlo[14*5] | thi[14*5] | smax[5]
+    off += kBandTableBytes;
     unsigned char *wb = smem + off + (size_t)wid * a.wave_bytes;
     uint8_t *map8 = wb;
     uint16_t *map16 = reinterpret_cast<uint16_t *>(wb);
@@ -147,7 +164,6 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
     uint32_t *cpre = reinterpret_cast<uint32_t *>(ck + kChunkPre);
     int64_t *cbase = reinterpret_cast<int64_t *>(ck + kChunkBase);
     uint8_t *cbij = ck + kChunkBij;
-    double *cw = reinterpret_cast<double *>(ck + kChunkW);
     double *rw = reinterpret_cast<double *>(ck + chunk_bytes(true));
     uint8_t *rbn = ck + chunk_bytes(true) + align_up(8 * (size_t)a.max_m, 16);
 
@@ -157,6 +173,8 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
             if (W) hlo[t] = hhi[t] = 0;
         }
     if (threadIdx.x == 0) rank3_tables(a.nb, rA, rB);
+    if (BANDED)
+        for (int t = threadIdx.x; t < 145; t += blockDim.x) btab[t] = a.band[t];
     __syncthreads();
 
     unsigned int wave_hits = 0;
@@ -170,31 +188,16 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
         const int32_t m = (int32_t)(re - rb);
         HubDomain dom;
         hub_domain(i, a.key_s[i], a.gr, a.cell_start, dom);
-
-        // hub side of the walk: clear the map over the domain, then mark N+(i)
-        uint32_t *map32 = reinterpret_cast<uint32_t *>(wb);
-        const int map_words = ((W ? 2 : 1) * dom.size + 3) >> 2;
-        for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
-        wave_lds_sync();
         const int32_t *hrow = a.col_h + (rb - a.base_h);
         const uint8_t *hbin = a.bin_h + (rb - a.base_h);
-        for (int p = lane; p < m; p += kWave) {
-            const int32_t k = hrow[p];
-            int32_t d = dom.delta[0];
-#pragma unroll
-            for (int t = 1; t < 5; ++t)
-                if (k >= dom.lo[t]) d = dom.delta[t];
-            if (W) {
-                map16[k + d] = (uint16_t)(p + 1);
-                rw[p] = a.w_s[k];
-                rbn[p] = hbin[p];
-            } else {
-                map8[k + d] = (uint8_t)(hbin[p] + 1);
-            }
-        }
-        wave_lds_sync();
         const int32_t hub_hi = hrow[m - 1];
         const double wi = W ? a.w_s[i] : 0.0;
+        if (W) {
+            for (int p = lane; p < m; p += kWave) {
+                rw[p] = a.w_s[hrow[p]];
+                rbn[p] = hbin[p];
+            }
+        }
 
         // spokes of this tile: hub-row positions [p_lo, p_hi) with j in [s_lo, s_hi)
         int32_t p_lo = 0, p_hi = m;
@@ -208,27 +211,27 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
         }
 
         unsigned int my_hits = 0;
-        // spokes in chunks of 64: lane q fetches spoke q's row bounds, a wave scan lays the 64
-        // spoke rows end to end, and the lanes walk that flat range with kUnroll loads in flight.
-        for (int32_t p0 = p_lo; p0 < p_hi; p0 += kWave) {
-            const int32_t p = p0 + lane;
-            int64_t sb = 0;
-            int32_t len = 0, bj = 0;
-            double wj = 0.0;
-            if (p < p_hi) {
-                const int32_t j = hrow[p];
-                bj = hbin[p];
-                sb = a.row_ptr[j];
-                len = (int32_t)(a.row_ptr[j + 1] - sb);
-                if (W) wj = a.w_s[j];
-            }
+        // run bounds as plain scalars (a select over the arrays is lowered to a stack copy)
+        const int32_t l1 = dom.lo[1], l2 = dom.lo[2], l3 = dom.lo[3], l4 = dom.lo[4];
+        const int32_t d0 = dom.delta[0], d1 = dom.delta[1], d2 = dom.delta[2], d3 = dom.delta[3],
+                      d4 = dom.delta[4];
+        const int32_t h0 = dom.hi[0], h1 = dom.hi[1], h2 = dom.hi[2], h3 = dom.hi[3],
+                      h4 = dom.hi[4];
+
+        // Walk the rows of (up to) 64 spokes laid end to end: lane q describes spoke p0 + q by
+        // its element range [sb, sb + len) and bin bj.  A wave scan gives each spoke's start in
+        // the flat range; the lanes stream the range with kUnroll loads in flight each, map every
+        // label k to its hub-map offset and bin every hit.  Banded: the map holds labels
+        // [blo, blo + bsize); otherwise it holds the whole domain, found by comparisons.
+        auto walk = [&](int32_t p0, int64_t sb, int32_t len, int32_t bj, int32_t blo,
+                        int32_t bsize) __attribute__((always_inline)) {
             const int32_t incl = wave_incl_scan(len, lane);
             const int32_t total = __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));
+            if (total == 0) return;
             cpre[lane] = (uint32_t)(incl - len);
             if (lane == kWave - 1) cpre[kWave] = (uint32_t)incl;
             cbase[lane] = sb - (incl - len);
-            cbij[lane] = (uint8_t)bj;
-            if (W) cw[lane] = wj;
+            if (!W) cbij[lane] = (uint8_t)bj;
             wave_lds_sync();
             // owner spoke of flat index t: the last q with cpre[q] <= t (then t < cpre[q+1])
             int q = 0;
@@ -244,7 +247,7 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int32_t t = t0 + u * kWave + lane;
-                    kk[u] = INT32_MAX;
+                    kk[u] = -1;
                     bb[u] = 0;
                     qq[u] = q;
                     if (t < total) {
@@ -258,15 +261,21 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int32_t k = kk[u];
-                    if (k > hub_hi) continue;  // past the hub's last neighbour (or no element)
-                    int32_t d = dom.delta[0], lim = dom.hi[0];
-#pragma unroll
-                    for (int t = 1; t < 5; ++t)
-                        if (k >= dom.lo[t]) { d = dom.delta[t]; lim = dom.hi[t]; }
-                    if (k >= lim) continue;  // in a gap between the hub's stencil runs
-                    const uint32_t v = W ? (uint32_t)map16[k + d] : (uint32_t)map8[k + d];
+                    if (k < 0) continue;
+                    int32_t mo;
+                    if constexpr (BANDED) {
+                        mo = k - blo;
+                        if ((uint32_t)mo >= (uint32_t)bsize) continue;
+                    } else {
+                        if (k > hub_hi) continue;  // past the hub's last neighbour
+                        const int32_t d = k >= l4 ? d4 : k >= l3 ? d3 : k >= l2 ? d2 : k >= l1 ? d1 : d0;
+                        const int32_t lim = k >= l4 ? h4 : k >= l3 ? h3 : k >= l2 ? h2 : k >= l1 ? h1 : h0;
+                        if (k >= lim) continue;  // in a gap between the runs
+                        mo = k + d;
+                    }
+                    const uint32_t v = W ? (uint32_t)map16[mo] : (uint32_t)map8[mo];
                     if (!v) continue;
-                    const int32_t bij = cbij[qq[u]];
+                    const int32_t bij = W ? (int32_t)rbn[p0 + qq[u]] : (int32_t)cbij[qq[u]];
                     const int32_t bik = W ? (int32_t)rbn[v - 1] : (int32_t)v - 1;
                     const int32_t bjk = bb[u];
                     const int32_t x = min(bij, min(bik, bjk)), z = max(bij, max(bik, bjk));
@@ -275,8 +284,8 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
                     if (GH) atomicAdd(&a.counts[c], 1ull);
                     else atomicAdd(&hc[c], 1u);
                     if (W) {
-                        const double wjj = cw[qq[u]], wk = rw[v - 1];
-                        const double x1 = fmin(wi, wjj), x2 = fmax(wi, wjj);
+                        const double wj = rw[p0 + qq[u]], wk = rw[v - 1];
+                        const double x1 = fmin(wi, wj), x2 = fmax(wi, wj);
                         const double w1 = fmin(x1, wk), tt = fmax(x1, wk);
                         const double w2 = fmin(x2, tt), w3 = fmax(x2, tt);
                         const double pr = __dmul_rn(__dmul_rn(w1, w2), w3);
@@ -297,7 +306,79 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
                 }
             }
             wave_lds_sync();  // the next chunk overwrites the chunk arrays
+        };
+
+        uint32_t *map32 = reinterpret_cast<uint32_t *>(wb);
+        if constexpr (!BANDED) {
+            // one map over the whole domain: k -> run by comparisons against the run starts
+            const int map_words = ((W ? 2 : 1) * dom.size + 3) >> 2;
+            for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
+            wave_lds_sync();
+            for (int p = lane; p < m; p += kWave) {
+                const int32_t k = hrow[p];
+                const int32_t d = k >= l4 ? d4 : k >= l3 ? d3 : k >= l2 ? d2 : k >= l1 ? d1 : d0;
+                if (W) map16[k + d] = (uint16_t)(p + 1);
+                else map8[k + d] = (uint8_t)(hbin[p] + 1);
+            }
+            wave_lds_sync();
+            for (int32_t p0 = p_lo; p0 < p_hi; p0 += kWave) {
+                const int32_t p = p0 + lane;
+                int64_t sb = 0;
+                int32_t len = 0, bj = 0;
+                if (p < p_hi) {
+                    const int32_t j = hrow[p];
+                    if (!W) bj = hbin[p];
+                    sb = a.row_ptr[j];
+                    len = (int32_t)(a.row_ptr[j + 1] - sb);
+                }
+                walk(p0, sb, len, bj, 0, 0);
+            }
+        } else {
+            const uint32_t *hso = a.slot_off + (int64_t)i * 16;  // hub row slot starts, [14] = m
+            for (int bq = 0; bq < 5; ++bq) {
+                const int32_t hp_lo = (int32_t)hso[band_slot(bq)], hp_hi = (int32_t)hso[band_slot(bq + 1)];
+                if (hp_lo == hp_hi) continue;  // no neighbour of the hub in this band: no triangle
+                const int32_t sp_hi = min(p_hi, (int32_t)hso[btab[140 + bq]]);
+                if (p_lo >= sp_hi) continue;
+                // run bq's label range, selected without indexing (keeps dom in registers)
+                int32_t blo = dom.lo[0], bhi = dom.hi[0];
+#pragma unroll
+                for (int t = 1; t < 5; ++t)
+                    if (bq == t) { blo = dom.lo[t]; bhi = dom.hi[t]; }
+                const int32_t bsize = bhi - blo;
+                const int map_words = ((W ? 2 : 1) * bsize + 3) >> 2;
+                for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
+                wave_lds_sync();
+                for (int p = hp_lo + lane; p < hp_hi; p += kWave) {
+                    const int32_t k = hrow[p];
+                    if (W) map16[k - blo] = (uint16_t)(p + 1);
+                    else map8[k - blo] = (uint8_t)(hbin[p] + 1);
+                }
+                wave_lds_sync();
+                for (int32_t p0 = p_lo; p0 < sp_hi; p0 += kWave) {
+                    const int32_t p = p0 + lane;
+                    int64_t sb = 0;
+                    int32_t len = 0, bj = 0;
+                    if (p < sp_hi) {
+                        int sj = 0;  // hub slot of position p
+#pragma unroll
+                        for (int t = 1; t < 14; ++t) sj += (int32_t)hso[t] <= p;
+                        const int tlo = btab[sj * 5 + bq], thi = btab[70 + sj * 5 + bq];
+                        if (tlo < thi) {
+                            const int32_t j = hrow[p];
+                            if (!W) bj = hbin[p];
+                            const uint32_t *jso = a.slot_off + (int64_t)j * 16;
+                            const uint32_t beg = jso[tlo];
+                            sb = a.row_ptr[j] + beg;
+                            len = (int32_t)(jso[thi] - beg);
+                        }
+                    }
+                    walk(p0, sb, len, bj, blo, bsize);
+                }
+                wave_lds_sync();  // map reads done before the next band refills it
+            }
         }
+
         if (!GH) {
             wave_hits += wave_sum(my_hits);
             if (wave_hits >= a.flush_at) {
@@ -305,7 +386,7 @@ __global__ void __launch_bounds__(256) k_triplet(TripletArgs a) {
                 wave_hits = 0;
             }
         }
-        wave_lds_sync();  // this wave's map reads complete before the next hub clears it
+        wave_lds_sync();  // this wave's LDS reads complete before the next hub rewrites them
     }
     if (!GH) {
         __syncthreads();
@@ -336,42 +417,85 @@ struct TripletPlan {
     int blocks = 0;      // persistent grid
 };
 
-template <bool W, bool GH>
-static int plan_triplet(const TripletArgs &a, int64_t n_hubs, TripletPlan &pl) {
+static const void *triplet_kernel(bool w, bool gh, bool banded) {
+#define GTC_K(W_, GH_, B_) reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_>)
+    if (w) return gh ? (banded ? GTC_K(true, true, true) : GTC_K(true, true, false))
+                     : (banded ? GTC_K(true, false, true) : GTC_K(true, false, false));
+    return gh ? (banded ? GTC_K(false, true, true) : GTC_K(false, true, false))
+              : (banded ? GTC_K(false, false, true) : GTC_K(false, false, false));
+#undef GTC_K
+}
+
+// Workgroup shape: the waves of a workgroup share one LDS histogram and each owns a hub map, so
+// more waves per workgroup amortise the histogram.  Pick the shape with the most resident waves
+// per CU (LDS and registers, from the occupancy API) whose histogram exchange budget still covers
+// the largest hub.
+static int plan_triplet(const void *kfn, const TripletArgs &a, size_t fixed, bool gh,
+                        int64_t n_hubs, unsigned long long max_hub_hits, TripletPlan &pl) {
     DeviceLimits dl;
     GTC_TRY(device_limits(dl));
-    const size_t fixed = triplet_lds_fixed(a.ncfg, W, GH);
-    int waves = 4;
-    while (waves > 1 && fixed + (size_t)waves * a.wave_bytes > dl.lds_per_block) waves >>= 1;
-    const size_t lds = fixed + (size_t)waves * a.wave_bytes;
-    if (lds > dl.lds_per_block) {
-        set_error("3pCF needs %zu bytes of LDS per workgroup (histogram %d configs, %d bytes per "
-                  "wave); the device allows %zu",
-                  lds, a.ncfg, a.wave_bytes, dl.lds_per_block);
+    int best_waves = 0, best_per_cu = 0;
+    size_t best_lds = 0;
+    for (int waves = 16; waves >= 1; waves >>= 1) {
+        const size_t lds = fixed + (size_t)waves * a.wave_bytes;
+        if (lds > dl.lds_per_block) continue;
+        if (!gh && max_hub_hits >= (0xffffffffull / (unsigned long long)waves) / 2) continue;
+        if (lds > 65536)
+            GTC_HIP_CHECK(hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+        int per_cu = 0;
+        GTC_HIP_CHECK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, waves * kWave, lds));
+        if (per_cu * waves > best_per_cu * best_waves) {
+            best_waves = waves;
+            best_per_cu = per_cu;
+            best_lds = lds;
+        }
+    }
+    if (best_waves == 0) {
+        set_error("3pCF needs more LDS per workgroup than the device allows (histogram %d configs, "
+                  "%d bytes per wave, %zu available) or a hub is too large for 32-bit LDS bins",
+                  a.ncfg, a.wave_bytes, dl.lds_per_block);
         return GTC_E_UNSUPPORTED;
     }
-    if (lds > 65536)
-        GTC_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void *>(&k_triplet<W, GH>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-    int per_cu = 0;
-    GTC_HIP_CHECK(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void *>(&k_triplet<W, GH>), waves * kWave, lds));
-    if (per_cu < 1) per_cu = 1;
-    int64_t blocks = (int64_t)dl.cus * per_cu;
-    const int64_t need = (n_hubs + waves - 1) / waves;
+    int64_t blocks = (int64_t)dl.cus * best_per_cu;
+    const int64_t need = (n_hubs + best_waves - 1) / best_waves;
     if (blocks > need) blocks = need;
     if (blocks < 1) blocks = 1;
-    pl.waves = waves;
-    pl.lds = lds;
+    pl.waves = best_waves;
+    pl.lds = best_lds;
     pl.blocks = (int)blocks;
     return GTC_OK;
 }
 
-template <bool W, bool GH>
-static int launch_triplet(const TripletArgs &a, const TripletPlan &pl, hipStream_t s) {
-    hipLaunchKernelGGL((k_triplet<W, GH>), dim3(pl.blocks), dim3(pl.waves * kWave), pl.lds, s, a);
-    GTC_HIP_CHECK(hipGetLastError());
+static int launch_triplet(const void *kfn, TripletArgs &a, const TripletPlan &pl, hipStream_t s) {
+    void *args[] = {&a};
+    GTC_HIP_CHECK(hipLaunchKernel(kfn, dim3(pl.blocks), dim3(pl.waves * kWave), args, pl.lds, s));
     return GTC_OK;
+}
+
+// Band table of the banded walk for a grid of g >= 3 cells per axis: for a spoke in hub slot s,
+// its forward cell slots [tlo, thi) whose keys fall in the hub's key run q; and smax[q], the first
+// hub slot whose spokes cannot reach run q.  Key offsets of the 14 forward slots relative to the
+// cell: own cell, +x, then the rows (dz, dy) = (0, 1), (1, -1), (1, 0), (1, 1) of three cells.
+static void band_table(int64_t g, uint8_t out[145]) {
+    const int64_t gg = g * g;
+    const int64_t off[14] = {0, 1, g - 1, g, g + 1, gg - g - 1, gg - g, gg - g + 1,
+                             gg - 1, gg, gg + 1, gg + g - 1, gg + g, gg + g + 1};
+    const int64_t lo[5] = {0, g - 1, gg - g - 1, gg - 1, gg + g - 1};
+    for (int q = 0; q < 5; ++q) {
+        const int64_t hi = lo[q] + (q == 0 ? 2 : 3);
+        int smax = 0;
+        for (int sj = 0; sj < 14; ++sj) {
+            int tlo = 14, thi = 14;
+            for (int t = 13; t >= 0; --t) {
+                if (off[sj] + off[t] >= lo[q]) tlo = t;
+                if (off[sj] + off[t] >= hi) thi = t;
+            }
+            out[sj * 5 + q] = (uint8_t)tlo;
+            out[70 + sj * 5 + q] = (uint8_t)thi;
+            if (off[sj] < hi) smax = sj + 1;
+        }
+        out[140 + q] = (uint8_t)smax;
+    }
 }
 
 int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, double *maxabs,
@@ -446,8 +570,20 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.n_hubs = (int32_t)G->n_hubs;
     a.nb = nb;
     a.ncfg = (int32_t)ncfg;
+    // Walk mode: banded (per key run, one-subtraction map offsets) for grids of >= 3 cells per axis
+    // with long spoke rows; otherwise one map over the whole hub domain.  GTC_TRIPLET_MODE=flat or
+    // banded forces a mode (banded needs >= 3 cells per axis).
+    const double avg_len = G->walks > 0 ? (double)G->spoke_elements / (double)G->walks : 0.0;
+    bool banded = G->grid.g >= 3 && avg_len >= 64.0;
+    if (const char *env = std::getenv("GTC_TRIPLET_MODE")) {
+        if (!std::strcmp(env, "flat")) banded = false;
+        else if (!std::strcmp(env, "banded")) banded = G->grid.g >= 3;
+    }
+    if (banded) band_table(G->grid.g, a.band);
+    a.slot_off = G->slot_off;
     a.max_m = (int32_t)std::max<int64_t>(G->max_deg, 1);
-    a.map_bytes = (int32_t)align_up((W ? 2 : 1) * (size_t)std::max<int64_t>(G->max_domain, 1), 16);
+    const int64_t map_labels = std::max<int64_t>(banded ? G->max_band : G->max_domain, 1);
+    a.map_bytes = (int32_t)align_up((W ? 2 : 1) * (size_t)map_labels, 16);
     a.wave_bytes = (int32_t)(a.map_bytes + chunk_bytes(W) + hubrow_bytes(W, a.max_m));
     if (W && G->max_deg >= 65535) {
         set_error("weighted 3pCF: a forward row of %lld entries exceeds the 16-bit position map",
@@ -466,28 +602,25 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.limbs = limbs;
 
     float kms = 0.f;
+    TripletPlan used{};
     if (G->n_hubs > 0) {
-        // LDS histogram unless it would take more than half of a workgroup's LDS
+        // LDS histogram unless it would take more than half of a workgroup's LDS, or a single hub
+        // could overflow its 32-bit bins
         DeviceLimits dl;
         STEP(device_limits(dl));
-        const bool GH = triplet_lds_fixed(a.ncfg, W, false) > dl.lds_per_block / 2;
-        TripletPlan pl;
-        STEP(W ? (GH ? plan_triplet<true, true>(a, G->n_hubs, pl) : plan_triplet<true, false>(a, G->n_hubs, pl))
-               : (GH ? plan_triplet<false, true>(a, G->n_hubs, pl) : plan_triplet<false, false>(a, G->n_hubs, pl)));
-        // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long max_hub_hits =
             (unsigned long long)G->max_deg * (unsigned long long)(G->max_deg - 1) / 2;
+        const bool GH = triplet_lds_fixed(a.ncfg, W, false) > dl.lds_per_block / 2 ||
+                        max_hub_hits >= 0x7fffffffull / 2;
+        TripletPlan pl;
+        const void *kfn = triplet_kernel(W, GH, banded);
+        STEP(plan_triplet(kfn, a, triplet_lds_fixed(a.ncfg, W, GH), GH, G->n_hubs, max_hub_hits, pl));
+        // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long budget = 0xffffffffull / (unsigned long long)pl.waves;
-        if (!GH && max_hub_hits >= budget / 2) {
-            set_error("a hub has %lld forward neighbours; its triangles could overflow the 32-bit "
-                      "LDS histogram", (long long)G->max_deg);
-            cleanup();
-            return GTC_E_UNSUPPORTED;
-        }
         a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub_hits);
+        used = pl;
         STEP_HIP(hipEventRecord(ev0, s));
-        STEP(W ? (GH ? launch_triplet<true, true>(a, pl, s) : launch_triplet<true, false>(a, pl, s))
-               : (GH ? launch_triplet<false, true>(a, pl, s) : launch_triplet<false, false>(a, pl, s)));
+        STEP(launch_triplet(kfn, a, pl, s));
         STEP_HIP(hipEventRecord(ev1, s));
     }
     std::vector<unsigned long long> h_counts(ncfg), h_limbs(W ? 4 * ncfg : 0);
@@ -514,6 +647,10 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         st->tiles = G->n_hubs > 0 ? 1 : 0;
         st->kernel_ms = kms;
         st->weight_scale = scale;
+        st->launch_waves = used.waves;
+        st->launch_blocks = used.blocks;
+        st->launch_lds_bytes = (int32_t)used.lds;
+        st->launch_mode = banded ? 1 : 0;
         st->q_alg_bytes = 5.0 * (double)G->E + 4.0 * (double)G->spoke_elements + (double)tri;
     }
     cleanup();

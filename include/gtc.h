@@ -90,7 +90,11 @@ typedef struct {
     uint64_t cliques4;         /* 4-cliques counted (4pCF) */
     double q_alg_bytes;        /* 3pCF algorithmic bytes: 5E + 4*sum d+(j) over walks + triangles */
     int32_t weight_scale;      /* s of the weighted sums (0 when unweighted) */
-    int32_t reserved;
+    int32_t launch_waves;      /* enumeration kernel: waves per workgroup */
+    int32_t launch_blocks;     /* enumeration kernel: persistent workgroups */
+    int32_t launch_lds_bytes;  /* enumeration kernel: LDS per workgroup */
+    int32_t launch_mode;       /* 3pCF walk: 0 one map over the hub domain, 1 banded by key run */
+    int32_t launch_reserved;
     double build_ms;           /* gtc_build_graph: whole call */
     double kernel_ms;          /* enumeration kernels only (sum over tiles) */
     double count_ms;           /* count call: whole call */

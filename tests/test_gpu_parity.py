@@ -70,6 +70,23 @@ def test_3pcf_matches_oracle(gpu_available, kind, seed, n, r, nb, weighted):
         np.testing.assert_array_equal(ws, ows)
 
 
+@pytest.mark.parametrize("mode", ["flat", "banded"])
+@pytest.mark.parametrize("kind,seed,n,r,nb,weighted", CASES_3[1:4])
+def test_3pcf_walk_modes(gpu_available, monkeypatch, mode, kind, seed, n, r, nb, weighted):
+    # the two spoke walks (one map over the hub domain / one map per key run) agree with the oracle
+    say("3pcf mode", mode, kind, seed, n, r, nb, weighted)
+    monkeypatch.setenv("GTC_TRIPLET_MODE", mode)
+    xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 60, 2500)
+    edges = linear_edges_sq(r, nb)
+    w = 0.5 + rng_for(seed + 1000).random(n) if weighted else None
+    c, ws, st = hip_3pcf(xyz, edges, w)
+    assert st["launch_mode"] == (1 if mode == "banded" else 0)
+    oc, ows, s, _ = oracle.Graph(xyz, edges).count_3pcf(w)
+    np.testing.assert_array_equal(c, oc)
+    if weighted:
+        np.testing.assert_array_equal(ws, ows)
+
+
 def test_3pcf_c1_full(gpu_available):
     cfg = workloads.get("C1")
     xyz, w = cfg.generate()
