@@ -70,6 +70,10 @@ def main():
     ap.add_argument("--config", default="C2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--tile-bytes", type=int, default=0,
+                    help="hub-window budget in CSR bytes (0: one resident window)")
+    ap.add_argument("--host-csr", action="store_true",
+                    help="out-of-core: keep the CSR in pinned host memory, stream windows")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (HBM counter calibration)")
     args = ap.parse_args()
@@ -102,7 +106,7 @@ def main():
     torch.cuda.synchronize()
 
     def step():
-        g = gtc.Graph(xyz, edges)
+        g = gtc.Graph(xyz, edges, tile_bytes=args.tile_bytes, host_csr=args.host_csr)
         c, ws, st = g.count_3pcf(w)
         gst = g.stats()
         g.close()
@@ -131,9 +135,10 @@ def main():
     k_avg = sum(kms) / len(kms)
     achieved = qalg[0] / (k_avg * 1e-3) / 1e9
     log(f"[bench] {args.steps} steps: {ms_step:.2f} ms/step, build {sum(bms)/len(bms):.2f} ms, "
-        f"kernel {k_avg:.3f} ms, T={T}, E={st['edges']}")
+        f"kernel {k_avg:.3f} ms, T={T}, E={st['edges']}, windows {st['windows']}, "
+        f"tiles {st['tiles']}, h2d {st['h2d_ms']:.1f} ms")
 
-    traffic = measured_traffic(cfg.key)
+    traffic = measured_traffic(cfg.key) if args.tile_bytes == 0 else None
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "traffic_gbs": None if traffic is None else traffic / (k_avg * 1e-3) / 1e9,
@@ -161,7 +166,8 @@ def main():
         "config": {"workload": f"{cfg.key} {cfg.name}", "n_points": cfg.n, "kind": cfg.kind,
                    "r_max": cfg.r, "nbins": cfg.nbins, "weighted": cfg.weighted,
                    "mean_degree_target": cfg.target_degree, "edges": st["edges"],
-                   "triangles": T, "merge_walks": walks[0]},
+                   "triangles": T, "merge_walks": walks[0], "tile_bytes": args.tile_bytes,
+                   "host_csr": args.host_csr, "windows": st["windows"], "tiles": st["tiles"]},
         "merge_walks_per_s": walks[0] * args.steps / elapsed,
         "kernel_triplets_per_s": T / (k_avg * 1e-3),
         "build_ms": sum(bms) / len(bms),

@@ -42,6 +42,13 @@ void free_graph_buffers(gtc_graph_s *G) {
     G->row_ptr = G->work = G->d_edges = nullptr;
     G->slot_off = nullptr;
     G->bin = nullptr;
+    if (G->h_col || G->h_bin) {
+        (void)hipStreamSynchronize(s);  // copies into the pinned CSR have finished
+        if (G->h_col) (void)hipHostFree(G->h_col);
+        if (G->h_bin) (void)hipHostFree(G->h_bin);
+        G->h_col = nullptr;
+        G->h_bin = nullptr;
+    }
 }
 
 // Restores the caller's current device on scope exit.
@@ -70,7 +77,7 @@ static void fill_graph_stats(const gtc_graph_s *G, gtc_stats *st) {
     st->n = G->n;
     st->edges = G->E;
     st->max_out_degree = G->max_deg;
-    st->windows = 1;
+    st->windows = G->win.empty() ? 1 : (int64_t)G->win.size() - 1;
     st->spoke_elements = G->spoke_elements;
     st->build_ms = G->build_ms;
 }
@@ -146,10 +153,6 @@ int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, 
         set_error("gtc_build_graph: tile_bytes must be >= 0, and > 0 when host_csr is set");
         return GTC_E_INVALID;
     }
-    if (o.tile_bytes > 0 || o.host_csr) {
-        set_error("gtc_build_graph: hub-window tiling is not available in this build");
-        return GTC_E_UNSUPPORTED;
-    }
     DeviceGuard dg(-1);
     if (dg.rc) return dg.rc;
     {
@@ -174,6 +177,8 @@ int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, 
     G->stream = reinterpret_cast<hipStream_t>(hip_stream);
     G->n = n;
     G->nb = nbins;
+    G->tile_bytes = o.tile_bytes;
+    G->host_csr = o.host_csr != 0;
     for (int b = 0; b <= nbins; ++b) G->edges[b] = h_edges_sq[b];
     int rc = build_graph_device(G, d_xyz, G->stream);
     if (rc == GTC_OK && o.drop_coords) {
@@ -230,6 +235,11 @@ int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_sta
         set_error("gtc_count_4pcf_parity: the graph was built with drop_coords");
         return GTC_E_INVALID;
     }
+    if (g->host_csr) {
+        set_error("gtc_count_4pcf_parity: out-of-core (host_csr) graphs are not supported by the "
+                  "4-clique kernel, which needs every spoke row of a hub at once");
+        return GTC_E_UNSUPPORTED;
+    }
     DeviceGuard dg(g->device);
     if (dg.rc) return dg.rc;
     auto t0 = std::chrono::steady_clock::now();
@@ -254,10 +264,15 @@ int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h
     if (h_row_ptr)
         GTC_HIP_CHECK(hipMemcpyAsync(h_row_ptr, g->row_ptr, sizeof(int64_t) * (g->n + 1),
                                      hipMemcpyDeviceToHost, s));
-    if (h_col && g->E)
-        GTC_HIP_CHECK(hipMemcpyAsync(h_col, g->col, sizeof(int32_t) * g->E, hipMemcpyDeviceToHost, s));
-    if (h_bin && g->E)
-        GTC_HIP_CHECK(hipMemcpyAsync(h_bin, g->bin, g->E, hipMemcpyDeviceToHost, s));
+    if (g->host_csr) {  // out-of-core graph: the CSR is already in host memory
+        if (h_col && g->E) std::memcpy(h_col, g->h_col, sizeof(int32_t) * g->E);
+        if (h_bin && g->E) std::memcpy(h_bin, g->h_bin, g->E);
+    } else {
+        if (h_col && g->E)
+            GTC_HIP_CHECK(hipMemcpyAsync(h_col, g->col, sizeof(int32_t) * g->E, hipMemcpyDeviceToHost, s));
+        if (h_bin && g->E)
+            GTC_HIP_CHECK(hipMemcpyAsync(h_bin, g->bin, g->E, hipMemcpyDeviceToHost, s));
+    }
     if (h_perm && g->n)
         GTC_HIP_CHECK(hipMemcpyAsync(h_perm, g->perm, sizeof(int32_t) * g->n, hipMemcpyDeviceToHost, s));
     GTC_HIP_CHECK(hipStreamSynchronize(s));
@@ -280,6 +295,20 @@ void gtc_graph_free(gtc_graph g) {
     free_graph_buffers(g);
     (void)hipStreamSynchronize(g->stream);
     delete g;
+}
+
+int64_t gtc_plan_windows(const int64_t *h_row_ptr, int64_t n, int64_t tile_bytes,
+                         int64_t *h_bounds) {
+    if (!h_row_ptr || !h_bounds || n < 0 || tile_bytes <= 0) {
+        set_error("gtc_plan_windows: need row offsets, a bounds array, n >= 0 and tile_bytes > 0");
+        return GTC_E_INVALID;
+    }
+    for (int64_t i = 0; i < n; ++i)
+        if (h_row_ptr[i + 1] < h_row_ptr[i]) {
+            set_error("gtc_plan_windows: row offsets decrease at row %lld", (long long)i);
+            return GTC_E_INVALID;
+        }
+    return plan_windows(h_row_ptr, n, tile_bytes, h_bounds);
 }
 
 const char *gtc_status_string(int status) {

@@ -53,8 +53,10 @@ struct PairArgs {
     int32_t nb;
     int32_t n;
     Grid gr;
+    int32_t h_lo, h_hi;      // hubs of this launch: labels [h_lo, h_hi)
     int32_t *deg;            // count pass output
     const int64_t *row_ptr;  // emit pass input
+    int64_t col_base;        // emit pass: entry e of the CSR is col[e - col_base] (window buffer)
     int32_t *col;
     uint8_t *bin;
     uint32_t *slot_off;      // emit pass: [n][16] start of each forward cell slot in the row
@@ -72,15 +74,15 @@ __global__ void __launch_bounds__(256) k_pairs(PairArgs a) {
     __shared__ double se[GTC_MAX_BINS + 1];
     for (int t = threadIdx.x; t <= a.nb; t += blockDim.x) se[t] = (double)a.edges[t];
     __syncthreads();
-    const int64_t ii = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (ii >= a.n) return;
+    const int64_t ii = a.h_lo + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (ii >= a.h_hi) return;
     const int32_t i = (int32_t)ii;
     const int4 pi = a.xyz_s[i];
     const int32_t c = pi.w, g = a.gr.g;
     const int32_t cz = c / (g * g), cy = (c / g) % g, cx = c % g;
     const double e0 = se[0], emax = se[a.nb];
     int32_t cnt = 0;
-    int64_t w = EMIT ? a.row_ptr[i] : 0;
+    int64_t w = EMIT ? a.row_ptr[i] - a.col_base : 0;
     const int nb = a.nb;
     auto scan = [&](int32_t lo, int32_t hi) {
         for (int32_t j = lo; j < hi; ++j) {
@@ -151,21 +153,21 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 }
 
 __global__ void __launch_bounds__(256)
-    k_degstats(int32_t n, const int64_t *__restrict__ row_ptr, const int32_t *__restrict__ col,
-               const int32_t *__restrict__ deg, const int32_t *__restrict__ key_s,
-               const int32_t *__restrict__ cell_start, Grid gr, int64_t *__restrict__ work,
-               StatsOut *out) {
+    k_degstats(int32_t h_lo, int32_t h_hi, const int64_t *__restrict__ row_ptr,
+               const int32_t *__restrict__ col, int64_t col_base, const int32_t *__restrict__ deg,
+               const int32_t *__restrict__ key_s, const int32_t *__restrict__ cell_start, Grid gr,
+               int64_t *__restrict__ work, StatsOut *out, unsigned long long *win_last) {
     constexpr int L = 16;
     __shared__ unsigned long long red[6][256 / kWave];
     const int sub = threadIdx.x & (L - 1);
-    const int64_t hub0 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / L;
+    const int64_t hub0 = h_lo + (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / L;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x / L;
     unsigned long long my_max_deg = 0, my_max_dom = 0, my_sum = 0, my_walks = 0, my_hubs = 0,
-                       my_max_band = 0;
-    for (int64_t h = hub0; h < n; h += stride) {
+                       my_max_band = 0, my_last = 0;
+    for (int64_t h = hub0; h < h_hi; h += stride) {
         const int64_t b = row_ptr[h], e = row_ptr[h + 1];
         int64_t s = 0;
-        for (int64_t t = b + sub; t < e; t += L) s += deg[col[t]];
+        for (int64_t t = b + sub; t < e; t += L) s += deg[col[t - col_base]];
 #pragma unroll
         for (int d = L / 2; d > 0; d >>= 1) s += __shfl_xor(s, d, L);
         if (sub == 0) {
@@ -184,6 +186,10 @@ __global__ void __launch_bounds__(256)
                 my_walks += m;
                 my_hubs += 1;
             }
+            if (m > 0) {  // largest spoke label of the window: bounds its search windows
+                const unsigned long long last = (unsigned long long)col[e - 1 - col_base];
+                my_last = last > my_last ? last : my_last;
+            }
         }
     }
     // block reduction, then one atomic per quantity per block
@@ -194,6 +200,8 @@ __global__ void __launch_bounds__(256)
     my_walks = wave_sum_u64(my_walks);
     my_hubs = wave_sum_u64(my_hubs);
     my_max_band = wave_max_u64(my_max_band);
+    my_last = wave_max_u64(my_last);
+    if (lane == 0) atomicMax(win_last, my_last);
     if (lane == 0) {
         red[5][wid] = my_max_band;
         red[0][wid] = my_max_deg;
@@ -386,6 +394,8 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     pa.n = (int32_t)n;
     pa.gr = gr;
     pa.deg = G->deg;
+    pa.h_lo = 0;
+    pa.h_hi = (int32_t)n;
     if (n > 0) {
         hipLaunchKernelGGL(k_pairs<false>, dim3(grid_for(n, 256)), dim3(256), 0, s, pa);
         STEP_HIP(hipGetLastError());
@@ -401,39 +411,127 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         cleanup();
         return GTC_E_INVALID;
     }
-    STEP(dev_alloc_n(&G->col, G->E, s));
-    STEP(dev_alloc_n(&G->bin, G->E, s));
+    // hub windows: one window unless a tile budget is set (§III.5.3)
+    G->win.assign({0, n});
+    G->max_window_edges = G->E;
+    if (G->tile_bytes > 0 && n > 0) {
+        G->h_row_ptr.resize(n + 1);
+        STEP_HIP(hipMemcpyAsync(G->h_row_ptr.data(), G->row_ptr, sizeof(int64_t) * (n + 1),
+                                hipMemcpyDeviceToHost, s));
+        STEP_HIP(hipStreamSynchronize(s));
+        std::vector<int64_t> bounds(n + 2);
+        const int64_t Wn = plan_windows(G->h_row_ptr.data(), n, G->tile_bytes, bounds.data());
+        G->win.assign(bounds.begin(), bounds.begin() + Wn + 1);
+        G->max_window_edges = 0;
+        for (int64_t k = 0; k < Wn; ++k)
+            G->max_window_edges = std::max(G->max_window_edges,
+                                           G->h_row_ptr[G->win[k + 1]] - G->h_row_ptr[G->win[k]]);
+    }
+    const int64_t W = (int64_t)G->win.size() - 1;
+    unsigned long long *win_last = nullptr;
+    int32_t *st_col = nullptr;
+    uint8_t *st_bin = nullptr;
+    auto cleanup2 = [&]() {
+        dev_free(win_last, s);
+        dev_free(st_col, s);
+        dev_free(st_bin, s);
+    };
+#define STEP2(expr) do { rc = (expr); if (rc) { cleanup2(); cleanup(); return rc; } } while (0)
+#define STEP2_HIP(call) do { hipError_t e_ = (call); if (e_ != hipSuccess) { rc = hip_fail(e_, #call, __FILE__, __LINE__); cleanup2(); cleanup(); return rc; } } while (0)
+    STEP2(dev_alloc_n(&win_last, W, s));
+    STEP2(fill_u64(reinterpret_cast<uint64_t *>(win_last), W, 0ull, s));
+    if (G->host_csr) {
+        // out-of-core: the CSR lives in pinned host memory; each window is emitted into a device
+        // staging buffer and copied out
+        STEP2_HIP(hipHostMalloc(reinterpret_cast<void **>(&G->h_col),
+                                sizeof(int32_t) * std::max<int64_t>(G->E, 1), hipHostMallocDefault));
+        STEP2_HIP(hipHostMalloc(reinterpret_cast<void **>(&G->h_bin), std::max<int64_t>(G->E, 1),
+                                hipHostMallocDefault));
+        STEP2(dev_alloc_n(&st_col, G->max_window_edges, s));
+        STEP2(dev_alloc_n(&st_bin, G->max_window_edges, s));
+    } else {
+        STEP2(dev_alloc_n(&G->col, G->E, s));
+        STEP2(dev_alloc_n(&G->bin, G->E, s));
+    }
     pa.row_ptr = G->row_ptr;
-    pa.col = G->col;
-    pa.bin = G->bin;
     pa.slot_off = G->slot_off;
-    if (n > 0) {
-        hipLaunchKernelGGL(k_pairs<true>, dim3(grid_for(n, 256)), dim3(256), 0, s, pa);
-        STEP_HIP(hipGetLastError());
-        const int64_t dsb = std::min<int64_t>((n * 16 + 255) / 256, 2048);
-        hipLaunchKernelGGL(k_degstats, dim3((unsigned)dsb), dim3(256), 0, s, (int32_t)n, G->row_ptr,
-                           G->col, G->deg, G->key_s, G->cell_start, gr, G->work, d_stats);
-        STEP_HIP(hipGetLastError());
+    for (int64_t k = 0; k < W && n > 0; ++k) {
+        const int64_t lo = G->win[k], hi = G->win[k + 1];
+        if (hi <= lo) continue;
+        const int64_t e_lo = G->host_csr ? G->h_row_ptr[lo] : 0;
+        pa.h_lo = (int32_t)lo;
+        pa.h_hi = (int32_t)hi;
+        pa.col_base = e_lo;
+        pa.col = G->host_csr ? st_col : G->col;
+        pa.bin = G->host_csr ? st_bin : G->bin;
+        hipLaunchKernelGGL(k_pairs<true>, dim3(grid_for(hi - lo, 256)), dim3(256), 0, s, pa);
+        STEP2_HIP(hipGetLastError());
+        const int64_t dsb = std::min<int64_t>(((hi - lo) * 16 + 255) / 256, 2048);
+        hipLaunchKernelGGL(k_degstats, dim3((unsigned)dsb), dim3(256), 0, s, (int32_t)lo,
+                           (int32_t)hi, G->row_ptr, (const int32_t *)pa.col, e_lo, G->deg, G->key_s,
+                           G->cell_start, gr, G->work, d_stats, win_last + k);
+        STEP2_HIP(hipGetLastError());
+        if (G->host_csr) {
+            const int64_t ne = G->h_row_ptr[hi] - e_lo;
+            if (ne > 0) {
+                STEP2_HIP(hipMemcpyAsync(G->h_col + e_lo, st_col, sizeof(int32_t) * ne,
+                                         hipMemcpyDeviceToHost, s));
+                STEP2_HIP(hipMemcpyAsync(G->h_bin + e_lo, st_bin, ne, hipMemcpyDeviceToHost, s));
+            }
+        }
     }
     StatsOut hs{};
-    STEP_HIP(hipMemcpyAsync(&hs, d_stats, sizeof(hs), hipMemcpyDeviceToHost, s));
-    STEP_HIP(hipStreamSynchronize(s));
+    std::vector<unsigned long long> h_last(W);
+    STEP2_HIP(hipMemcpyAsync(&hs, d_stats, sizeof(hs), hipMemcpyDeviceToHost, s));
+    STEP2_HIP(hipMemcpyAsync(h_last.data(), win_last, sizeof(unsigned long long) * W,
+                             hipMemcpyDeviceToHost, s));
+    STEP2_HIP(hipStreamSynchronize(s));
     G->max_deg = (int64_t)hs.max_deg;
     G->max_domain = (int64_t)hs.max_domain;
     G->spoke_elements = (int64_t)hs.spoke_elements;
     G->walks = (int64_t)hs.walks;
     G->n_hubs = (int64_t)hs.n_hubs;
     G->max_band = (int64_t)hs.max_band;
+    // search windows of each hub window: from itself to the window of its largest spoke label
+    G->win_smax.assign(W, 0);
+    for (int64_t k = 0; k < W; ++k) {
+        const int64_t last = std::max<int64_t>((int64_t)h_last[k], G->win[k]);
+        const int64_t t = std::upper_bound(G->win.begin(), G->win.end(), last) - G->win.begin() - 1;
+        G->win_smax[k] = (int32_t)std::min<int64_t>(std::max<int64_t>(t, k), W - 1);
+    }
 
-    STEP(dev_alloc_n(&G->hubs, G->n_hubs, s));
+    STEP2(dev_alloc_n(&G->hubs, G->n_hubs, s));
     if (n > 0 && G->n_hubs > 0) {
         hipLaunchKernelGGL(k_bucket_count, dim3(grid_for(n, 256)), dim3(256), 0, s, (int32_t)n,
                            G->row_ptr, G->work, bucket);
         hipLaunchKernelGGL(k_bucket_offsets, dim3(1), dim3(64), 0, s, bucket);
         hipLaunchKernelGGL(k_bucket_scatter, dim3(grid_for(n, 256)), dim3(256), 0, s, (int32_t)n,
                            G->row_ptr, G->work, bucket, G->hubs);
-        STEP_HIP(hipGetLastError());
+        STEP2_HIP(hipGetLastError());
     }
+    // per-window hub lists: a stable partition of the heavy-first list by window
+    G->win_hubs.assign(W + 1, 0);
+    G->win_hubs[W] = G->n_hubs;
+    if (W > 1 && G->n_hubs > 0) {
+        std::vector<int32_t> h(G->n_hubs), out(G->n_hubs);
+        STEP2_HIP(hipMemcpyAsync(h.data(), G->hubs, sizeof(int32_t) * G->n_hubs,
+                                 hipMemcpyDeviceToHost, s));
+        STEP2_HIP(hipStreamSynchronize(s));
+        auto window_of = [&](int64_t lab) {
+            return (int64_t)(std::upper_bound(G->win.begin(), G->win.end(), lab) - G->win.begin() - 1);
+        };
+        std::vector<int64_t> cnt(W + 1, 0);
+        for (int32_t v : h) ++cnt[window_of(v) + 1];
+        for (int64_t k = 0; k < W; ++k) cnt[k + 1] += cnt[k];
+        for (int64_t k = 0; k <= W; ++k) G->win_hubs[k] = cnt[k];
+        for (int32_t v : h) out[cnt[window_of(v)]++] = v;
+        STEP2_HIP(hipMemcpyAsync(G->hubs, out.data(), sizeof(int32_t) * G->n_hubs,
+                                 hipMemcpyHostToDevice, s));
+        STEP2_HIP(hipStreamSynchronize(s));
+    }
+    cleanup2();
+#undef STEP2
+#undef STEP2_HIP
     cleanup();
 #undef STEP
 #undef STEP_HIP

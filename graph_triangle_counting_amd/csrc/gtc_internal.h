@@ -19,6 +19,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "gtc.h"
 
@@ -53,6 +54,9 @@ int dev_alloc_n(T **p, size_t count, hipStream_t s) {
 }
 int fill_u64(uint64_t *p, int64_t count, uint64_t value, hipStream_t s);
 int fill_u32(uint32_t *p, int64_t count, uint32_t value, hipStream_t s);
+
+// hub windows: bounds[0..W] of consecutive rows whose CSR (5 bytes per edge) fits tile_bytes
+int64_t plan_windows(const int64_t *row_ptr, int64_t n, int64_t tile_bytes, int64_t *bounds);
 
 // exclusive scan of n int32 values: out[0..n], out[n] = total
 int exclusive_scan_i32_to_i64(const int32_t *in, int64_t *out, int64_t n, hipStream_t s);
@@ -159,4 +163,15 @@ struct gtc_graph_s {
     int64_t walks = 0;           // sum of d+(i) over hubs in the hub list
     bool coords_kept = true;
     double build_ms = 0.0;
+    // hub windows (§III.5.3): label bounds win[0..W], one window [0, n) unless tiled
+    int64_t tile_bytes = 0;
+    std::vector<int64_t> win;       // W+1 label bounds
+    std::vector<int64_t> win_hubs;  // W+1 offsets into hubs: window k's hubs, heaviest first
+    std::vector<int32_t> win_smax;  // last window holding a spoke of window k's hubs
+    std::vector<int64_t> h_row_ptr; // host copy of row_ptr (tiled graphs)
+    int64_t max_window_edges = 0;
+    // out-of-core: the CSR in pinned host memory, only windows go to the device
+    bool host_csr = false;
+    int32_t *h_col = nullptr;
+    uint8_t *h_bin = nullptr;
 };

@@ -553,8 +553,6 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     }
     STEP(dev_alloc_n(&queue, 1, s));
     STEP(fill_u32(queue, 1, 0u, s));
-    STEP_HIP(hipEventCreate(&ev0));
-    STEP_HIP(hipEventCreate(&ev1));
 
     TripletArgs a{};
     a.row_ptr = G->row_ptr;
@@ -601,42 +599,122 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.counts = reinterpret_cast<unsigned long long *>(d_counts);
     a.limbs = limbs;
 
-    float kms = 0.f;
+    float kms = 0.f, h2d_ms = 0.f;
     TripletPlan used{};
+    int64_t tiles_run = 0;
+    // window buffers of an out-of-core graph: [0] hub window, [1] search window
+    int32_t *wcol[2] = {nullptr, nullptr};
+    uint8_t *wbin[2] = {nullptr, nullptr};
+    std::vector<hipEvent_t> kev, cev;  // kernel and copy event pairs
+    auto cleanup_tiles = [&]() {
+        for (int b2 = 0; b2 < 2; ++b2) {
+            dev_free(wcol[b2], s);
+            dev_free(wbin[b2], s);
+        }
+        for (auto e : kev) (void)hipEventDestroy(e);
+        for (auto e : cev) (void)hipEventDestroy(e);
+        kev.clear();
+        cev.clear();
+    };
+#define TSTEP(expr) do { rc = (expr); if (rc) { cleanup_tiles(); cleanup(); return rc; } } while (0)
+#define TSTEP_HIP(call) do { hipError_t e_ = (call); if (e_ != hipSuccess) { rc = hip_fail(e_, #call, __FILE__, __LINE__); cleanup_tiles(); cleanup(); return rc; } } while (0)
+    auto event_pair = [&](std::vector<hipEvent_t> &v) -> int {
+        hipEvent_t e0, e1;
+        GTC_HIP_CHECK(hipEventCreate(&e0));
+        GTC_HIP_CHECK(hipEventCreate(&e1));
+        v.push_back(e0);
+        v.push_back(e1);
+        return GTC_OK;
+    };
     if (G->n_hubs > 0) {
         // LDS histogram unless it would take more than half of a workgroup's LDS, or a single hub
         // could overflow its 32-bit bins
         DeviceLimits dl;
-        STEP(device_limits(dl));
+        TSTEP(device_limits(dl));
         const unsigned long long max_hub_hits =
             (unsigned long long)G->max_deg * (unsigned long long)(G->max_deg - 1) / 2;
         const bool GH = triplet_lds_fixed(a.ncfg, W, false) > dl.lds_per_block / 2 ||
                         max_hub_hits >= 0x7fffffffull / 2;
         TripletPlan pl;
         const void *kfn = triplet_kernel(W, GH, banded);
-        STEP(plan_triplet(kfn, a, triplet_lds_fixed(a.ncfg, W, GH), GH, G->n_hubs, max_hub_hits, pl));
+        TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(a.ncfg, W, GH), GH, G->n_hubs, max_hub_hits, pl));
         // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long budget = 0xffffffffull / (unsigned long long)pl.waves;
         a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub_hits);
         used = pl;
-        STEP_HIP(hipEventRecord(ev0, s));
-        STEP(launch_triplet(kfn, a, pl, s));
-        STEP_HIP(hipEventRecord(ev1, s));
+
+        // Tile loop (§III.5.3): hub window h against search windows s = h .. smax(h).  A walk
+        // (i, j) runs in the tile (window of i, window of j) only; a resident untiled graph is one
+        // tile over all spokes.
+        const int64_t nw = (int64_t)G->win.size() - 1;
+        const bool ooc = G->host_csr;
+        const std::vector<int64_t> &hr = G->h_row_ptr;
+        if (ooc)
+            for (int b2 = 0; b2 < 2; ++b2) {
+                TSTEP(dev_alloc_n(&wcol[b2], G->max_window_edges, s));
+                TSTEP(dev_alloc_n(&wbin[b2], G->max_window_edges, s));
+            }
+        auto load_window = [&](int64_t w, int b2) -> int {
+            const int64_t e0 = hr[G->win[w]], ne = hr[G->win[w + 1]] - e0;
+            if (ne <= 0) return GTC_OK;
+            GTC_TRY(event_pair(cev));
+            GTC_HIP_CHECK(hipEventRecord(cev[cev.size() - 2], s));
+            GTC_HIP_CHECK(hipMemcpyAsync(wcol[b2], G->h_col + e0, sizeof(int32_t) * ne,
+                                         hipMemcpyHostToDevice, s));
+            GTC_HIP_CHECK(hipMemcpyAsync(wbin[b2], G->h_bin + e0, ne, hipMemcpyHostToDevice, s));
+            GTC_HIP_CHECK(hipEventRecord(cev.back(), s));
+            return GTC_OK;
+        };
+        for (int64_t h = 0; h < nw; ++h) {
+            const int64_t nh = G->win_hubs[h + 1] - G->win_hubs[h];
+            if (nh == 0) continue;
+            if (ooc) TSTEP(load_window(h, 0));
+            a.hubs = G->hubs + G->win_hubs[h];
+            a.n_hubs = (int32_t)nh;
+            a.col_h = ooc ? wcol[0] : G->col;
+            a.bin_h = ooc ? wbin[0] : G->bin;
+            a.base_h = ooc ? hr[G->win[h]] : 0;
+            for (int64_t sw = h; sw <= G->win_smax[h]; ++sw) {
+                if (ooc && sw != h) TSTEP(load_window(sw, 1));
+                a.col_s = ooc ? (sw == h ? wcol[0] : wcol[1]) : G->col;
+                a.bin_s = ooc ? (sw == h ? wbin[0] : wbin[1]) : G->bin;
+                a.base_s = ooc ? hr[G->win[sw]] : 0;
+                a.s_lo = nw == 1 ? 0 : (int32_t)G->win[sw];
+                a.s_hi = nw == 1 ? (int32_t)G->n : (int32_t)G->win[sw + 1];
+                TSTEP(fill_u32(queue, 1, 0u, s));
+                TripletPlan tp = pl;
+                tp.blocks = (int)std::min<int64_t>(pl.blocks, (nh + pl.waves - 1) / pl.waves);
+                TSTEP(event_pair(kev));
+                TSTEP_HIP(hipEventRecord(kev[kev.size() - 2], s));
+                TSTEP(launch_triplet(kfn, a, tp, s));
+                TSTEP_HIP(hipEventRecord(kev.back(), s));
+                ++tiles_run;
+            }
+        }
     }
     std::vector<unsigned long long> h_counts(ncfg), h_limbs(W ? 4 * ncfg : 0);
-    STEP_HIP(hipMemcpyAsync(h_counts.data(), d_counts, sizeof(uint64_t) * ncfg,
-                            hipMemcpyDeviceToHost, s));
+    TSTEP_HIP(hipMemcpyAsync(h_counts.data(), d_counts, sizeof(uint64_t) * ncfg,
+                             hipMemcpyDeviceToHost, s));
     if (W)
-        STEP_HIP(hipMemcpyAsync(h_limbs.data(), limbs, sizeof(unsigned long long) * 4 * ncfg,
+        TSTEP_HIP(hipMemcpyAsync(h_limbs.data(), limbs, sizeof(unsigned long long) * 4 * ncfg,
                                 hipMemcpyDeviceToHost, s));
-    STEP_HIP(hipStreamSynchronize(s));
-    if (G->n_hubs > 0) STEP_HIP(hipEventElapsedTime(&kms, ev0, ev1));
+    TSTEP_HIP(hipStreamSynchronize(s));
+    for (size_t e = 0; e + 1 < kev.size(); e += 2) {
+        float t = 0.f;
+        TSTEP_HIP(hipEventElapsedTime(&t, kev[e], kev[e + 1]));
+        kms += t;
+    }
+    for (size_t e = 0; e + 1 < cev.size(); e += 2) {
+        float t = 0.f;
+        TSTEP_HIP(hipEventElapsedTime(&t, cev[e], cev[e + 1]));
+        h2d_ms += t;
+    }
     if (W) {
         std::vector<double> h_w(ncfg);
         for (int64_t c = 0; c < ncfg; ++c) h_w[c] = limbs_to_double(&h_limbs[4 * c], h_counts[c], scale);
-        STEP_HIP(hipMemcpyAsync(d_weighted, h_w.data(), sizeof(double) * ncfg,
+        TSTEP_HIP(hipMemcpyAsync(d_weighted, h_w.data(), sizeof(double) * ncfg,
                                 hipMemcpyHostToDevice, s));
-        STEP_HIP(hipStreamSynchronize(s));
+        TSTEP_HIP(hipStreamSynchronize(s));
     }
     unsigned long long tri = 0;
     for (auto v : h_counts) tri += v;
@@ -644,7 +722,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         st->triangles = tri;
         st->merge_walks = G->walks;
         st->spoke_elements = G->spoke_elements;
-        st->tiles = G->n_hubs > 0 ? 1 : 0;
+        st->tiles = tiles_run;
+        st->h2d_ms = h2d_ms;
         st->kernel_ms = kms;
         st->weight_scale = scale;
         st->launch_waves = used.waves;
@@ -653,9 +732,12 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         st->launch_mode = banded ? 1 : 0;
         st->q_alg_bytes = 5.0 * (double)G->E + 4.0 * (double)G->spoke_elements + (double)tri;
     }
+    cleanup_tiles();
     cleanup();
 #undef STEP
 #undef STEP_HIP
+#undef TSTEP
+#undef TSTEP_HIP
     return GTC_OK;
 }
 

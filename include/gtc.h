@@ -124,7 +124,8 @@ int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d
                    gtc_stats *st, void *hip_stream);
 
 /* Binned 4-clique counts split by parity (§II.2, §III.1.1, §III.2).  Needs nbins <=
- * GTC_MAX_BINS_4PCF and the coordinates (not dropped).
+ * GTC_MAX_BINS_4PCF and the coordinates (not dropped); GTC_E_UNSUPPORTED for out-of-core
+ * (host_csr) graphs.
  *   d_even     device uint64 [gtc_num_configs(4, nbins)]: every tetrahedron.
  *   d_odd      device int64  [same]: signed handedness sum. */
 int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
@@ -143,6 +144,18 @@ int gtc_config_bins(int32_t order, int32_t nbins, int32_t *h_bins);
  *   h_perm    int32 [n]: h_perm[internal] = original label.  Any pointer may be NULL. */
 int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h_bin,
                      int32_t *h_perm);
+
+/* Hub windows of the tile loop (§III.5.3), for inspection and tests; host only, needs no GPU.
+ *   h_row_ptr host int64 [n+1] forward CSR offsets (nondecreasing).
+ *   tile_bytes > 0: budget per window at 5 bytes per edge; a row longer than the budget gets a
+ *              window of its own.
+ *   h_bounds  host int64 [n+1] (at least 2): receives the label bounds 0 = b_0 < ... < b_W = n of
+ *              consecutive rows (b_1 = 0 when n = 0).
+ * Returns W >= 1, or GTC_E_INVALID.  gtc_build_graph uses the same windows; tile (h, s) then
+ * walks the spokes of hub window h that lie in window s, for s from h to the window of the
+ * largest spoke label of window h, so every forward edge is walked in exactly one tile. */
+int64_t gtc_plan_windows(const int64_t *h_row_ptr, int64_t n, int64_t tile_bytes,
+                         int64_t *h_bounds);
 
 /* Graph-level statistics (n, edges, max_out_degree, windows, spoke_elements, build_ms). */
 int gtc_graph_stats(gtc_graph g, gtc_stats *st);
