@@ -91,16 +91,18 @@ __host__ __device__ inline size_t triplet_lds_fixed(int ncfg, bool weighted, boo
 // Exchange the workgroup histogram out to global memory.  Safe while other waves keep adding:
 // each bin is swapped for zero atomically, so every increment is flushed exactly once.
 template <bool W>
-__device__ void flush_hist(const TripletArgs &a, uint32_t *hc, unsigned long long *hlo,
-                           unsigned long long *hhi, int first, int step) {
-    for (int t = first; t < a.ncfg; t += step) {
+__device__ __forceinline__ void flush_hist(int ncfg, unsigned long long *counts,
+                                           unsigned long long *limbs, uint32_t *hc,
+                                           unsigned long long *hlo, unsigned long long *hhi,
+                                           int first, int step) {
+    for (int t = first; t < ncfg; t += step) {
         const uint32_t v = atomicExch(&hc[t], 0u);
-        if (v) atomicAdd(&a.counts[t], (unsigned long long)v);
+        if (v) atomicAdd(&counts[t], (unsigned long long)v);
         if (W) {
             const unsigned long long l = atomicExch(&hlo[t], 0ull);
-            if (l) add_u128(&a.limbs[4 * t], l);
+            if (l) add_u128(&limbs[4 * t], l);
             const unsigned long long h = atomicExch(&hhi[t], 0ull);
-            if (h) add_u128(&a.limbs[4 * t + 2], h);
+            if (h) add_u128(&limbs[4 * t + 2], h);
         }
     }
 }
@@ -124,7 +126,8 @@ __host__ __device__ inline size_t hubrow_bytes(bool weighted, int max_m) {
     return weighted ? align_up(8 * (size_t)max_m, 16) + align_up((size_t)max_m, 16) : 0;
 }
 
-constexpr int kUnroll = 8;  // loads in flight per lane
+// spoke-row loads in flight per lane
+constexpr int kUnroll = 8;
 
 // Banded walk (grids of at least 3 cells per axis).  A hub's forward stencil is five key runs
 // ("bands"); band q holds the hub-row slots [kBandSlot[q], kBandSlot[q+1]) (own cell and the
@@ -173,7 +176,16 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             if (W) hlo[t] = hhi[t] = 0;
         }
     if (threadIdx.x == 0) rank3_tables(a.nb, rA, rB);
-    if (BANDED)
+    // fields the walk uses, as plain values (capturing the argument struct by reference would
+    // make the compiler keep the whole struct live in registers)
+    const int32_t ncfg = a.ncfg;
+    const int32_t *const col_s = a.col_s;
+    const uint8_t *const bin_s = a.bin_s;
+    const int64_t base_s = a.base_s;
+    unsigned long long *const g_counts = a.counts;
+    unsigned long long *const g_limbs = a.limbs;
+    const double two_s = a.two_s;
+    if constexpr (BANDED)
         for (int t = threadIdx.x; t < 145; t += blockDim.x) btab[t] = a.band[t];
     __syncthreads();
 
@@ -217,6 +229,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                       d4 = dom.delta[4];
         const int32_t h0 = dom.hi[0], h1 = dom.hi[1], h2 = dom.hi[2], h3 = dom.hi[3],
                       h4 = dom.hi[4];
+        const int32_t e1 = d1 - d0, e2 = d2 - d1, e3 = d3 - d2, e4 = d4 - d3;
+        const int32_t g1 = h1 - h0, g2 = h2 - h1, g3 = h3 - h2, g4 = h4 - h3;
 
         // Walk the rows of (up to) 64 spokes laid end to end: lane q describes spoke p0 + q by
         // its element range [sb, sb + len) and bin bj.  A wave scan gives each spoke's start in
@@ -233,7 +247,9 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             cbase[lane] = sb - (incl - len);
             if (!W) cbij[lane] = (uint8_t)bj;
             wave_lds_sync();
-            // owner spoke of flat index t: the last q with cpre[q] <= t (then t < cpre[q+1])
+            // owner spoke of flat index t: the last q with cpre[q] <= t (then t < cpre[q+1]).  The
+            // owner's end and row pointers stay in registers; LDS is read again only when t
+            // crosses into the next spoke.
             int q = 0;
             {
                 int hi = kWave;
@@ -242,7 +258,81 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     if ((int32_t)cpre[md] <= lane) q = md; else hi = md;
                 }
             }
-            for (int32_t t0 = 0; t0 < total; t0 += kWave * kUnroll) {
+            int32_t qend = (int32_t)cpre[q + 1];
+            const int32_t *cp = col_s + (cbase[q] - base_s);  // flat element t is cp[t]
+            const uint8_t *bp = bin_s + (cbase[q] - base_s);
+            auto seek = [&](int32_t t) __attribute__((always_inline)) {
+                if (t >= qend) {
+                    do {
+                        ++q;
+                        qend = (int32_t)cpre[q + 1];
+                    } while (t >= qend);
+                    cp = col_s + (cbase[q] - base_s);
+                    bp = bin_s + (cbase[q] - base_s);
+                }
+            };
+            auto process = [&](int32_t k, int32_t bjk, int32_t qu) __attribute__((always_inline)) {
+                int32_t mo;
+                if constexpr (BANDED) {
+                    mo = k - blo;  // k = -1 (no element) falls outside as well
+                    if ((uint32_t)mo >= (uint32_t)bsize) return;
+                } else {
+                    if ((uint32_t)k > (uint32_t)hub_hi) return;  // past the hub's last neighbour
+                    // run of k from the run starts (nondecreasing), as sums of differences:
+                    // a choice between captured variables would be folded into a pointer
+                    // select that keeps the lambda closures in scratch
+                    const bool r1 = k >= l1, r2 = k >= l2, r3 = k >= l3, r4 = k >= l4;
+                    const int32_t d = d0 + (r1 ? e1 : 0) + (r2 ? e2 : 0) + (r3 ? e3 : 0) + (r4 ? e4 : 0);
+                    const int32_t lim = h0 + (r1 ? g1 : 0) + (r2 ? g2 : 0) + (r3 ? g3 : 0) + (r4 ? g4 : 0);
+                    if (k >= lim) return;  // in a gap between the runs
+                    mo = k + d;
+                }
+                const uint32_t v = W ? (uint32_t)map16[mo] : (uint32_t)map8[mo];
+                if (!v) return;
+                const int32_t bij = W ? (int32_t)rbn[p0 + qu] : (int32_t)cbij[qu];
+                const int32_t bik = W ? (int32_t)rbn[v - 1] : (int32_t)v - 1;
+                const int32_t x = min(bij, min(bik, bjk)), z = max(bij, max(bik, bjk));
+                const int32_t y = bij + bik + bjk - x - z;
+                const int32_t c = rA[x] + rB[y] + z;
+                if (GH) atomicAdd(&g_counts[c], 1ull);
+                else atomicAdd(&hc[c], 1u);
+                if (W) {
+                    const double wj = rw[p0 + qu], wk = rw[v - 1];
+                    const double x1 = fmin(wi, wj), x2 = fmax(wi, wj);
+                    const double w1 = fmin(x1, wk), tt = fmax(x1, wk);
+                    const double w2 = fmin(x2, tt), w3 = fmax(x2, tt);
+                    const double pr = __dmul_rn(__dmul_rn(w1, w2), w3);
+                    const double qv = rint(__dmul_rn(pr, two_s));     // exact integer
+                    const double qh = floor(__dmul_rn(qv, 0x1p-28));   // in [-2^29, 2^29)
+                    const double ql = __fma_rn(-qh, 0x1p28, qv);       // in [0, 2^28)
+                    const unsigned long long ul = (unsigned long long)ql;
+                    const unsigned long long uh = (unsigned long long)((long long)qh + (1ll << 29));
+                    if (GH) {
+                        add_u128(&g_limbs[4 * c], ul);
+                        add_u128(&g_limbs[4 * c + 2], uh);
+                    } else {
+                        atomicAdd(&hlo[c], ul);
+                        atomicAdd(&hhi[c], uh);
+                    }
+                }
+                ++my_hits;
+            };
+            // whole blocks of kWave * kUnroll elements need no bounds checks; then one checked tail
+            int32_t t0 = 0;
+            for (; t0 + kWave * kUnroll <= total; t0 += kWave * kUnroll) {
+                int32_t kk[kUnroll], bb[kUnroll], qq[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int32_t t = t0 + u * kWave + lane;
+                    seek(t);
+                    qq[u] = q;
+                    kk[u] = cp[(uint32_t)t];
+                    bb[u] = bp[(uint32_t)t];
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) process(kk[u], bb[u], qq[u]);
+            }
+            if (t0 < total) {
                 int32_t kk[kUnroll], bb[kUnroll], qq[kUnroll];
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
@@ -251,59 +341,14 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     bb[u] = 0;
                     qq[u] = q;
                     if (t < total) {
-                        while ((int32_t)cpre[q + 1] <= t) ++q;
+                        seek(t);
                         qq[u] = q;
-                        const int64_t e = cbase[q] + t - a.base_s;
-                        kk[u] = a.col_s[e];
-                        bb[u] = a.bin_s[e];
+                        kk[u] = cp[(uint32_t)t];
+                        bb[u] = bp[(uint32_t)t];
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int32_t k = kk[u];
-                    if (k < 0) continue;
-                    int32_t mo;
-                    if constexpr (BANDED) {
-                        mo = k - blo;
-                        if ((uint32_t)mo >= (uint32_t)bsize) continue;
-                    } else {
-                        if (k > hub_hi) continue;  // past the hub's last neighbour
-                        const int32_t d = k >= l4 ? d4 : k >= l3 ? d3 : k >= l2 ? d2 : k >= l1 ? d1 : d0;
-                        const int32_t lim = k >= l4 ? h4 : k >= l3 ? h3 : k >= l2 ? h2 : k >= l1 ? h1 : h0;
-                        if (k >= lim) continue;  // in a gap between the runs
-                        mo = k + d;
-                    }
-                    const uint32_t v = W ? (uint32_t)map16[mo] : (uint32_t)map8[mo];
-                    if (!v) continue;
-                    const int32_t bij = W ? (int32_t)rbn[p0 + qq[u]] : (int32_t)cbij[qq[u]];
-                    const int32_t bik = W ? (int32_t)rbn[v - 1] : (int32_t)v - 1;
-                    const int32_t bjk = bb[u];
-                    const int32_t x = min(bij, min(bik, bjk)), z = max(bij, max(bik, bjk));
-                    const int32_t y = bij + bik + bjk - x - z;
-                    const int32_t c = rA[x] + rB[y] + z;
-                    if (GH) atomicAdd(&a.counts[c], 1ull);
-                    else atomicAdd(&hc[c], 1u);
-                    if (W) {
-                        const double wj = rw[p0 + qq[u]], wk = rw[v - 1];
-                        const double x1 = fmin(wi, wj), x2 = fmax(wi, wj);
-                        const double w1 = fmin(x1, wk), tt = fmax(x1, wk);
-                        const double w2 = fmin(x2, tt), w3 = fmax(x2, tt);
-                        const double pr = __dmul_rn(__dmul_rn(w1, w2), w3);
-                        const double qv = rint(__dmul_rn(pr, a.two_s));     // exact integer
-                        const double qh = floor(__dmul_rn(qv, 0x1p-28));   // in [-2^29, 2^29)
-                        const double ql = __fma_rn(-qh, 0x1p28, qv);       // in [0, 2^28)
-                        const unsigned long long ul = (unsigned long long)ql;
-                        const unsigned long long uh = (unsigned long long)((long long)qh + (1ll << 29));
-                        if (GH) {
-                            add_u128(&a.limbs[4 * c], ul);
-                            add_u128(&a.limbs[4 * c + 2], uh);
-                        } else {
-                            atomicAdd(&hlo[c], ul);
-                            atomicAdd(&hhi[c], uh);
-                        }
-                    }
-                    ++my_hits;
-                }
+                for (int u = 0; u < kUnroll; ++u) process(kk[u], bb[u], qq[u]);
             }
             wave_lds_sync();  // the next chunk overwrites the chunk arrays
         };
@@ -316,7 +361,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             wave_lds_sync();
             for (int p = lane; p < m; p += kWave) {
                 const int32_t k = hrow[p];
-                const int32_t d = k >= l4 ? d4 : k >= l3 ? d3 : k >= l2 ? d2 : k >= l1 ? d1 : d0;
+                const int32_t d = d0 + (k >= l1 ? e1 : 0) + (k >= l2 ? e2 : 0) + (k >= l3 ? e3 : 0) +
+                                  (k >= l4 ? e4 : 0);
                 if (W) map16[k + d] = (uint16_t)(p + 1);
                 else map8[k + d] = (uint8_t)(hbin[p] + 1);
             }
@@ -382,7 +428,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         if (!GH) {
             wave_hits += wave_sum(my_hits);
             if (wave_hits >= a.flush_at) {
-                flush_hist<W>(a, hc, hlo, hhi, lane, kWave);
+                flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, lane, kWave);
                 wave_hits = 0;
             }
         }
@@ -390,7 +436,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     }
     if (!GH) {
         __syncthreads();
-        flush_hist<W>(a, hc, hlo, hhi, threadIdx.x, blockDim.x);
+        flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, threadIdx.x, blockDim.x);
     }
 }
 
