@@ -25,17 +25,9 @@ static int64_t binom(int64_t n, int64_t k) {
 void free_graph_buffers(gtc_graph_s *G) {
     hipStream_t s = G->stream;
     dev_free(G->xyz_s, s);
-    dev_free(G->key_s, s);
-    dev_free(G->perm, s);
-    dev_free(G->cell_start, s);
-    dev_free(G->row_ptr, s);
-    dev_free(G->col, s);
-    dev_free(G->bin, s);
-    dev_free(G->deg, s);
-    dev_free(G->work, s);
-    dev_free(G->slot_off, s);
-    dev_free(G->hubs, s);
-    dev_free(G->d_edges, s);
+    dev_free(G->arena_pts, s);
+    dev_free(G->arena_csr, s);
+    G->arena_pts = G->arena_csr = nullptr;
     G->xyz_s = nullptr;
     G->key_s = nullptr;
     G->perm = G->cell_start = G->col = G->deg = G->hubs = nullptr;

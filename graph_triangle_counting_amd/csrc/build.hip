@@ -232,33 +232,26 @@ __global__ void __launch_bounds__(256)
 
 // Heavy-first hub order: hubs with a possible triangle (d+ >= 2, work > 0) bucketed by
 // floor(log2(work)), buckets in decreasing order.  Block-aggregated counting sort.
-constexpr int kBuckets = 64;
-
-__device__ __forceinline__ int hub_bucket(int64_t m, int64_t w) {
-    if (m < 2 || w <= 0) return -1;
-    return kBuckets - 1 - (63 - __clzll((unsigned long long)w));  // heavier -> smaller bucket
-}
-
 __global__ void __launch_bounds__(256)
     k_bucket_count(int32_t n, const int64_t *__restrict__ row_ptr, const int64_t *__restrict__ work,
                    unsigned int *__restrict__ bucket_count) {
-    __shared__ unsigned int loc[kBuckets];
-    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) loc[t] = 0;
+    __shared__ unsigned int loc[kHubClasses];
+    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x) loc[t] = 0;
     __syncthreads();
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i < n) {
-        const int b = hub_bucket(row_ptr[i + 1] - row_ptr[i], work[i]);
+        const int b = hub_class(row_ptr[i + 1] - row_ptr[i], work[i]);
         if (b >= 0) atomicAdd(&loc[b], 1u);
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x)
+    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x)
         if (loc[t]) atomicAdd(&bucket_count[t], loc[t]);
 }
 
 __global__ void k_bucket_offsets(unsigned int *bucket_count /* in: counts, out: fill cursor */) {
     if (threadIdx.x == 0) {
         unsigned int acc = 0;
-        for (int t = 0; t < kBuckets; ++t) {
+        for (int t = 0; t < kHubClasses; ++t) {
             const unsigned int c = bucket_count[t];
             bucket_count[t] = acc;
             acc += c;
@@ -270,22 +263,52 @@ __global__ void __launch_bounds__(256)
     k_bucket_scatter(int32_t n, const int64_t *__restrict__ row_ptr,
                      const int64_t *__restrict__ work, unsigned int *__restrict__ cursor,
                      int32_t *__restrict__ hubs) {
-    __shared__ unsigned int loc[kBuckets];
-    __shared__ unsigned int base[kBuckets];
-    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x) loc[t] = 0;
+    __shared__ unsigned int loc[kHubClasses];
+    __shared__ unsigned int base[kHubClasses];
+    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x) loc[t] = 0;
     __syncthreads();
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     int b = -1;
     unsigned int r = 0;
     if (i < n) {
-        b = hub_bucket(row_ptr[i + 1] - row_ptr[i], work[i]);
+        b = hub_class(row_ptr[i + 1] - row_ptr[i], work[i]);
         if (b >= 0) r = atomicAdd(&loc[b], 1u);
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < kBuckets; t += blockDim.x)
+    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x)
         base[t] = loc[t] ? atomicAdd(&cursor[t], loc[t]) : 0u;
     __syncthreads();
     if (b >= 0) hubs[base[b] + r] = (int32_t)i;
+}
+
+__global__ void __launch_bounds__(256)
+    k_class_count(const int32_t *__restrict__ hubs, int64_t n_hubs,
+                  const int64_t *__restrict__ row_ptr, const int64_t *__restrict__ work,
+                  uint32_t *__restrict__ counts) {
+    __shared__ uint32_t loc[kHubClasses];
+    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x) loc[t] = 0;
+    __syncthreads();
+    for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < n_hubs;
+         p += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t i = hubs[p];
+        const int c = hub_class(row_ptr[i + 1] - row_ptr[i], work[i]);
+        if (c >= 0) atomicAdd(&loc[c], 1u);
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x)
+        if (loc[t]) atomicAdd(&counts[t], loc[t]);
+}
+
+int hub_class_counts(const int32_t *hubs, int64_t n_hubs, const int64_t *row_ptr,
+                     const int64_t *work, uint32_t *counts, hipStream_t s) {
+    GTC_TRY(fill_u32(counts, kHubClasses, 0u, s));
+    if (n_hubs <= 0) return GTC_OK;
+    int64_t blocks = (n_hubs + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(k_class_count, dim3((unsigned)blocks), dim3(256), 0, s, hubs, n_hubs,
+                       row_ptr, work, counts);
+    GTC_HIP_CHECK(hipGetLastError());
+    return GTC_OK;
 }
 
 // ------------------------------------------------------------------ host orchestration
@@ -320,31 +343,30 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     G->grid = choose_grid(n, G->edges[G->nb]);
     const Grid gr = G->grid;
 
-    GTC_TRY(dev_alloc_n(&G->d_edges, G->nb + 1, s));
+    // the graph's per-point arrays (hubs: at most one per point)
+    GTC_TRY(carve_alloc(&G->arena_pts, s, [&](Carver &c) {
+        c.take(&G->d_edges, G->nb + 1);
+        c.take(&G->cell_start, gr.ncell + 1);
+        c.take(&G->perm, n);
+        c.take(&G->key_s, n);
+        c.take(&G->row_ptr, n + 1);
+        c.take(&G->deg, n);
+        c.take(&G->work, n);
+        c.take(&G->slot_off, 16 * (size_t)n);
+        c.take(&G->hubs, n);
+    }));
+    GTC_TRY(dev_alloc_n(&G->xyz_s, n, s));
     GTC_HIP_CHECK(hipMemcpyAsync(G->d_edges, G->edges, sizeof(int64_t) * (G->nb + 1),
                                  hipMemcpyHostToDevice, s));
-    GTC_TRY(dev_alloc_n(&G->cell_start, gr.ncell + 1, s));
-    GTC_TRY(dev_alloc_n(&G->perm, n, s));
-    GTC_TRY(dev_alloc_n(&G->xyz_s, n, s));
-    GTC_TRY(dev_alloc_n(&G->key_s, n, s));
-    GTC_TRY(dev_alloc_n(&G->row_ptr, n + 1, s));
-    GTC_TRY(dev_alloc_n(&G->deg, n, s));
-    GTC_TRY(dev_alloc_n(&G->work, n, s));
-    GTC_TRY(dev_alloc_n(&G->slot_off, 16 * (size_t)n, s));
 
-    // scratch: keys, slots, cell counts, error flag, stats
+    // build scratch: keys, slots, cell counts, error flag, stats, class counts, scan partials
     int32_t *key = nullptr, *slot = nullptr, *ccount = nullptr, *err = nullptr;
     StatsOut *d_stats = nullptr;
     unsigned int *bucket = nullptr;
+    int64_t *scan_ws = nullptr;
+    void *scratch = nullptr;
     int rc = GTC_OK;
-    auto cleanup = [&]() {
-        dev_free(key, s);
-        dev_free(slot, s);
-        dev_free(ccount, s);
-        dev_free(err, s);
-        dev_free(d_stats, s);
-        dev_free(bucket, s);
-    };
+    auto cleanup = [&]() { dev_free(scratch, s); };
 #define STEP(expr)            \
     do {                      \
         rc = (expr);          \
@@ -363,23 +385,27 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         }                                                                \
     } while (0)
 
-    STEP(dev_alloc_n(&key, n, s));
-    STEP(dev_alloc_n(&slot, n, s));
-    STEP(dev_alloc_n(&ccount, gr.ncell, s));
-    STEP(dev_alloc_n(&err, 1, s));
-    STEP(dev_alloc_n(&d_stats, 1, s));
-    STEP(dev_alloc_n(&bucket, kBuckets, s));
+    const size_t scan_ws_bytes = std::max(scan_workspace_bytes(n), scan_workspace_bytes(gr.ncell));
+    STEP(carve_alloc(&scratch, s, [&](Carver &c) {
+        c.take(&key, n);
+        c.take(&slot, n);
+        c.take(&ccount, gr.ncell);
+        c.take(&err, 1);
+        c.take(&d_stats, 1);
+        c.take(&bucket, kHubClasses);
+        c.take(&scan_ws, scan_ws_bytes / sizeof(int64_t));
+    }));
     STEP(fill_u32(reinterpret_cast<uint32_t *>(ccount), gr.ncell, 0u, s));
     STEP(fill_u32(reinterpret_cast<uint32_t *>(err), 1, 0u, s));
     STEP(fill_u64(reinterpret_cast<uint64_t *>(d_stats), sizeof(StatsOut) / 8, 0ull, s));
-    STEP(fill_u32(bucket, kBuckets, 0u, s));
+    STEP(fill_u32(bucket, kHubClasses, 0u, s));
 
     if (n > 0) {
         hipLaunchKernelGGL(k_cellkey, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, gr, key,
                            slot, ccount, err);
         STEP_HIP(hipGetLastError());
     }
-    STEP(exclusive_scan_i32_to_i32(ccount, G->cell_start, gr.ncell, s));
+    STEP(exclusive_scan_i32_to_i32(ccount, G->cell_start, gr.ncell, scan_ws, s));
     if (n > 0) {
         hipLaunchKernelGGL(k_scatter, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, key, slot,
                            G->cell_start, G->perm, G->xyz_s, G->key_s);
@@ -400,7 +426,7 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         hipLaunchKernelGGL(k_pairs<false>, dim3(grid_for(n, 256)), dim3(256), 0, s, pa);
         STEP_HIP(hipGetLastError());
     }
-    STEP(exclusive_scan_i32_to_i64(G->deg, G->row_ptr, n, s));
+    STEP(exclusive_scan_i32_to_i64(G->deg, G->row_ptr, n, scan_ws, s));
 
     int32_t h_err = 0;
     STEP_HIP(hipMemcpyAsync(&G->E, G->row_ptr + n, sizeof(int64_t), hipMemcpyDeviceToHost, s));
@@ -431,14 +457,17 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     unsigned long long *win_last = nullptr;
     int32_t *st_col = nullptr;
     uint8_t *st_bin = nullptr;
-    auto cleanup2 = [&]() {
-        dev_free(win_last, s);
-        dev_free(st_col, s);
-        dev_free(st_bin, s);
-    };
+    void *scratch2 = nullptr;
+    auto cleanup2 = [&]() { dev_free(scratch2, s); };
 #define STEP2(expr) do { rc = (expr); if (rc) { cleanup2(); cleanup(); return rc; } } while (0)
 #define STEP2_HIP(call) do { hipError_t e_ = (call); if (e_ != hipSuccess) { rc = hip_fail(e_, #call, __FILE__, __LINE__); cleanup2(); cleanup(); return rc; } } while (0)
-    STEP2(dev_alloc_n(&win_last, W, s));
+    STEP2(carve_alloc(&scratch2, s, [&](Carver &c) {
+        c.take(&win_last, W);
+        if (G->host_csr) {  // staging of one window's rows on their way to the pinned CSR
+            c.take(&st_col, G->max_window_edges);
+            c.take(&st_bin, G->max_window_edges);
+        }
+    }));
     STEP2(fill_u64(reinterpret_cast<uint64_t *>(win_last), W, 0ull, s));
     if (G->host_csr) {
         // out-of-core: the CSR lives in pinned host memory; each window is emitted into a device
@@ -447,11 +476,11 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
                                 sizeof(int32_t) * std::max<int64_t>(G->E, 1), hipHostMallocDefault));
         STEP2_HIP(hipHostMalloc(reinterpret_cast<void **>(&G->h_bin), std::max<int64_t>(G->E, 1),
                                 hipHostMallocDefault));
-        STEP2(dev_alloc_n(&st_col, G->max_window_edges, s));
-        STEP2(dev_alloc_n(&st_bin, G->max_window_edges, s));
     } else {
-        STEP2(dev_alloc_n(&G->col, G->E, s));
-        STEP2(dev_alloc_n(&G->bin, G->E, s));
+        STEP2(carve_alloc(&G->arena_csr, s, [&](Carver &c) {
+            c.take(&G->col, G->E);
+            c.take(&G->bin, G->E);
+        }));
     }
     pa.row_ptr = G->row_ptr;
     pa.slot_off = G->slot_off;
@@ -500,7 +529,6 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         G->win_smax[k] = (int32_t)std::min<int64_t>(std::max<int64_t>(t, k), W - 1);
     }
 
-    STEP2(dev_alloc_n(&G->hubs, G->n_hubs, s));
     if (n > 0 && G->n_hubs > 0) {
         hipLaunchKernelGGL(k_bucket_count, dim3(grid_for(n, 256)), dim3(256), 0, s, (int32_t)n,
                            G->row_ptr, G->work, bucket);
@@ -559,13 +587,9 @@ __global__ void k_gather_weights(int64_t n, const double *__restrict__ w,
     if ((threadIdx.x & (kWave - 1)) == 0 && m) atomicMax(maxabs_bits, m);
 }
 
-int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, double *maxabs,
-                   hipStream_t s) {
-    unsigned long long *d_m = nullptr;
-    int32_t *d_bad = nullptr;
-    GTC_TRY(dev_alloc_n(&d_m, 1, s));
-    int rc = dev_alloc_n(&d_bad, 1, s);
-    if (!rc) rc = fill_u64(reinterpret_cast<uint64_t *>(d_m), 1, 0ull, s);
+int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, unsigned long long *d_m,
+                   int32_t *d_bad, double *maxabs, hipStream_t s) {
+    int rc = fill_u64(reinterpret_cast<uint64_t *>(d_m), 1, 0ull, s);
     if (!rc) rc = fill_u32(reinterpret_cast<uint32_t *>(d_bad), 1, 0u, s);
     unsigned long long hm = 0;
     int32_t hb = 0;
@@ -581,8 +605,6 @@ int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, double 
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) rc = hip_fail(e, "weight readback", __FILE__, __LINE__);
     }
-    dev_free(d_m, s);
-    dev_free(d_bad, s);
     if (rc) return rc;
     if (hb) {
         set_error("a weight is not finite");

@@ -32,7 +32,9 @@ struct CliqueArgs {
     const int4 *xyz_s;
     const int32_t *cell_start;
     Grid gr;
-    unsigned int *queue;
+    unsigned int *queue;         // class counters, kQueueStride words apart
+    const unsigned int *qcount;  // [kHubClasses] hubs per class in the hub list
+    unsigned int batch_cap;      // largest batch of hubs per take
     unsigned long long *even;  // [ncfg]
     unsigned long long *odd;   // [ncfg], two's complement int64
     unsigned int flush_at;
@@ -128,11 +130,11 @@ __global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *ed
     __syncthreads();
 
     unsigned int wave_cl = 0;
+    HubQueue hub_queue;
+    hub_queue.init(a.qcount, a.batch_cap, lane);
     for (;;) {
-        unsigned int hq = 0;
-        if (lane == 0) hq = atomicAdd(a.queue, 1u);
-        hq = __builtin_amdgcn_readfirstlane(__shfl(hq, 0, kWave));
-        if (hq >= (unsigned int)a.n_hubs) break;
+        uint32_t hq;
+        if (!hub_queue.next(a.queue, lane, hq)) break;
         const int32_t i = __builtin_amdgcn_readfirstlane(a.hubs[hq]);
         const int64_t rb = a.row_ptr[i];
         const int32_t m = (int32_t)(a.row_ptr[i + 1] - rb);
@@ -304,10 +306,16 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     }
     a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub);
 
-    unsigned int *queue = nullptr;
-    GTC_TRY(dev_alloc_n(&queue, 1, s));
-    int rc = fill_u32(queue, 1, 0u, s);
+    unsigned int *queue = nullptr, *qcount = nullptr;
+    void *scratch = nullptr;
+    GTC_TRY(carve_alloc(&scratch, s, [&](Carver &c) {
+        c.take(&queue, (size_t)kHubClasses * kQueueStride);
+        c.take(&qcount, kHubClasses);
+    }));
+    int rc = fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s);
+    if (!rc) rc = hub_class_counts(G->hubs, G->n_hubs, G->row_ptr, G->work, qcount, s);
     a.queue = queue;
+    a.qcount = qcount;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     float kms = 0.f;
     int32_t launched_blocks = 0;
@@ -324,6 +332,10 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         (void)hipEventCreate(&e1);
         (void)hipEventRecord(e0, s);
         const dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(waves * kWave);
+        // one hub per take: a hub's 4-clique work grows like the cube of its row, which the
+        // spoke-element classes predict poorly, and the takes (a few thousand per ms) are far
+        // below what one counter serves
+        a.batch_cap = 1;
         launched_blocks = (int32_t)grid.x;
         if (GH)
             hipLaunchKernelGGL(k_clique4<true>, grid, block, lds, s, a, (const int64_t *)G->d_edges);
@@ -342,7 +354,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     }
     if (e0) (void)hipEventDestroy(e0);
     if (e1) (void)hipEventDestroy(e1);
-    dev_free(queue, s);
+    dev_free(scratch, s);
     if (rc) return rc;
     unsigned long long cl = 0;
     for (auto v : h_even) cl += v;

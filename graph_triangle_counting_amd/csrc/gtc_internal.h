@@ -52,15 +52,43 @@ template <class T>
 int dev_alloc_n(T **p, size_t count, hipStream_t s) {
     return dev_alloc(reinterpret_cast<void **>(p), sizeof(T) * (count ? count : 1), s);
 }
+// Several arrays in one device allocation.  A pass with no base only sizes the block; a pass over
+// the allocated base hands the arrays out, each 256-byte aligned.  One allocation and one free
+// per group of arrays: the stream-ordered pool's per-call cost (up to ~2 ms for some frees) is
+// paid once per group instead of once per array.
+struct Carver {
+    unsigned char *base = nullptr;
+    size_t off = 0;
+    template <class T>
+    void take(T **p, size_t count) {
+        if (base) *p = reinterpret_cast<T *>(base + off);
+        off += (sizeof(T) * (count ? count : 1) + 255) & ~(size_t)255;
+    }
+};
+
+// Allocate the arrays that layout(Carver &) takes, as one block (*block, freed with dev_free).
+template <class F>
+int carve_alloc(void **block, hipStream_t s, F &&layout) {
+    Carver size_pass;
+    layout(size_pass);
+    GTC_TRY(dev_alloc(block, size_pass.off, s));
+    Carver give;
+    give.base = static_cast<unsigned char *>(*block);
+    layout(give);
+    return GTC_OK;
+}
+
 int fill_u64(uint64_t *p, int64_t count, uint64_t value, hipStream_t s);
 int fill_u32(uint32_t *p, int64_t count, uint32_t value, hipStream_t s);
 
 // hub windows: bounds[0..W] of consecutive rows whose CSR (5 bytes per edge) fits tile_bytes
 int64_t plan_windows(const int64_t *row_ptr, int64_t n, int64_t tile_bytes, int64_t *bounds);
 
-// exclusive scan of n int32 values: out[0..n], out[n] = total
-int exclusive_scan_i32_to_i64(const int32_t *in, int64_t *out, int64_t n, hipStream_t s);
-int exclusive_scan_i32_to_i32(const int32_t *in, int32_t *out, int64_t n, hipStream_t s);
+// exclusive scan of n int32 values: out[0..n], out[n] = total.  ws: scan_workspace_bytes(n) bytes
+// of device scratch (partial sums of the tiles).
+size_t scan_workspace_bytes(int64_t n);
+int exclusive_scan_i32_to_i64(const int32_t *in, int64_t *out, int64_t n, void *ws, hipStream_t s);
+int exclusive_scan_i32_to_i32(const int32_t *in, int32_t *out, int64_t n, void *ws, hipStream_t s);
 
 // ------------------------------------------------------------------ cell grid
 struct Grid {
@@ -109,6 +137,88 @@ __device__ __forceinline__ void hub_domain(int32_t i, int32_t c, const Grid &gr,
     d.size = base;
 }
 
+// ------------------------------------------------------------------ hub queue
+// Hub lists are ordered heaviest first by class: class c holds the hubs whose spoke-element work w
+// has floor(log2 w) = 63 - c.  Enumeration waves take hubs from one counter per class, in class
+// order, a batch at a time: one hub per take in the classes of 2^15 elements and more, up to 64
+// hubs per take in the light classes.  A single shared counter taken once per hub serialises in
+// the L2 atomic unit at about one take per 10 ns, which alone costs ~10 ms per million hubs.
+constexpr int kHubClasses = 64;
+constexpr int kQueueStride = 64;  // u32 words between class counters (a 256-byte line each)
+constexpr int kBatchWorkLog2 = 15;
+
+__device__ __forceinline__ int hub_class(int64_t m, int64_t w) {
+    if (m < 2 || w <= 0) return -1;
+    return kHubClasses - 1 - (63 - __clzll((unsigned long long)w));
+}
+
+__host__ __device__ inline uint32_t class_batch(int c, uint32_t cap) {
+    const int e = 63 - c;  // the class's work is at least 2^e
+    if (e >= kBatchWorkLog2) return 1u;
+    const int b = kBatchWorkLog2 - e;
+    const uint32_t v = 1u << (b < 6 ? b : 6);
+    return v < cap ? v : cap;
+}
+
+// Largest batch that still leaves every wave of the launch about 16 takes: a power of two in
+// [1, 64], so that the last batches do not leave a few waves working long after the rest.
+inline uint32_t batch_cap(int64_t n_hubs, int64_t total_waves) {
+    const int64_t per = total_waves > 0 ? n_hubs / (total_waves * 16) : 1;
+    uint32_t cap = 1;
+    while (cap < 64 && (int64_t)(cap * 2) <= per) cap *= 2;
+    return cap;
+}
+
+// counts[c] = hubs of class c in hubs[0, n_hubs) (counts zeroed here)
+int hub_class_counts(const int32_t *hubs, int64_t n_hubs, const int64_t *row_ptr,
+                     const int64_t *work, uint32_t *counts, hipStream_t s);
+
+// Per-wave view of the class queue.  Every lane holds the hub-list range of class `lane`.
+struct HubQueue {
+    uint32_t cbeg, cend;  // lane c: positions [cbeg, cend) of class c
+    uint32_t pos, end;    // current batch (wave-uniform)
+    int cls;              // current class (wave-uniform)
+    uint32_t cap;         // batch cap of this launch
+
+    __device__ __forceinline__ void init(const uint32_t *counts, uint32_t batch_cap, int lane) {
+        const uint32_t c = counts[lane];
+        uint32_t incl = c;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint32_t o = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += o;
+        }
+        cbeg = incl - c;
+        cend = incl;
+        pos = end = 0;
+        cls = 0;
+        cap = batch_cap;
+    }
+
+    // Next hub-list position for this wave; false once every class is drained.
+    __device__ __forceinline__ bool next(uint32_t *counters, int lane, uint32_t &hq) {
+        while (pos >= end) {
+            if (cls >= kHubClasses) return false;
+            const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)cbeg, cls);
+            const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)cend, cls);
+            if (b < e) {
+                const uint32_t batch = class_batch(cls, cap);
+                uint32_t t = 0;
+                if (lane == 0) t = atomicAdd(&counters[cls * kQueueStride], batch);
+                t = (uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(t, 0, kWave));
+                if (t < e - b) {
+                    pos = b + t;
+                    end = e - pos < batch ? e : pos + batch;
+                    break;
+                }
+            }
+            ++cls;
+        }
+        hq = pos++;
+        return true;
+    }
+};
+
 // ------------------------------------------------------------------ configuration ranks
 // Rank of a nondecreasing triple (x <= y <= z) among all nondecreasing triples over [0, nb) in
 // lexicographic order:  rank = F(x) + P(y) - P(x) + (z - y), where F(x) = sum_{t<x} C(nb-t+1, 2)
@@ -140,8 +250,11 @@ struct gtc_graph_s {
     int32_t nb = 0;
     int64_t edges[GTC_MAX_BINS + 1] = {};
     gtc::Grid grid{};
-    // device arrays
-    int4 *xyz_s = nullptr;     // (x, y, z, cell key); dropped on request after the build
+    // device arrays: xyz_s in a block of its own (dropped on request after the build), the other
+    // per-point arrays in arena_pts, the CSR (col, bin) in arena_csr
+    void *arena_pts = nullptr;
+    void *arena_csr = nullptr;
+    int4 *xyz_s = nullptr;     // (x, y, z, cell key)
     int32_t *key_s = nullptr;  // cell key of each point (kept)
     int32_t *perm = nullptr;
     int32_t *cell_start = nullptr;

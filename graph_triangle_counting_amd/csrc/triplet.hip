@@ -52,7 +52,9 @@ struct TripletArgs {
     Grid gr;
     const double *w_s;  // weights, internal order (weighted only)
     double two_s;       // 2^s
-    unsigned int *queue;
+    unsigned int *queue;         // class counters, kQueueStride words apart
+    const unsigned int *qcount;  // [kHubClasses] hubs per class in this launch's hub list
+    unsigned int batch_cap;      // largest batch of hubs per take
     unsigned long long *counts;  // [ncfg]
     unsigned long long *limbs;   // [ncfg][4]: 128-bit sum of low limbs, 128-bit sum of high limbs
     unsigned int flush_at;       // hits a wave may add between exchanges of the LDS histogram
@@ -116,14 +118,16 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
     return v;
 }
 
-// Per-wave LDS region: hub map | chunk of 64 spokes | (weighted) the hub row's bins and weights.
-//   map    : u8 bin+1 per domain label, or (weighted) u16 row position+1
-//   chunk  : cpre u32[65] flat start of each spoke's row, cbase i64[64] (row start - flat start),
-//            cbij u8[64] spoke bins (weighted hubs read bins and weights from the hub row)
-constexpr int kChunkPre = 0, kChunkBase = 272, kChunkBij = 784;
-__host__ __device__ inline size_t chunk_bytes(bool) { return 848; }
+// Per-wave LDS region: hub map | chunk of 64 spokes | (weighted) the hub row's weights.
+//   map    : u8 bin+1 per domain label, or (weighted) u32 (row position+1) | bin << 16
+//   chunk  : cpre u32[65] flat start of each spoke's row, cbase i64[64] (row start - flat start,
+//            relative to the CSR slice), cbij u8[64] spoke bins, and (weighted) cw f64[64][2]: the
+//            hub and spoke weights of each spoke, ascending
+constexpr int kChunkPre = 0, kChunkBase = 272, kChunkBij = 784, kChunkW = 848;
+__host__ __device__ inline size_t chunk_bytes(bool weighted) { return weighted ? 1872 : 848; }
+__host__ __device__ inline size_t map_entry_bytes(bool weighted) { return weighted ? 4 : 1; }
 __host__ __device__ inline size_t hubrow_bytes(bool weighted, int max_m) {
-    return weighted ? align_up(8 * (size_t)max_m, 16) + align_up((size_t)max_m, 16) : 0;
+    return weighted ? align_up(8 * (size_t)max_m, 16) : 0;
 }
 
 // spoke-row loads in flight per lane
@@ -162,13 +166,13 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     off += kBandTableBytes;
     unsigned char *wb = smem + off + (size_t)wid * a.wave_bytes;
     uint8_t *map8 = wb;
-    uint16_t *map16 = reinterpret_cast<uint16_t *>(wb);
+    uint32_t *mapw = reinterpret_cast<uint32_t *>(wb);
     unsigned char *ck = wb + a.map_bytes;
     uint32_t *cpre = reinterpret_cast<uint32_t *>(ck + kChunkPre);
     int64_t *cbase = reinterpret_cast<int64_t *>(ck + kChunkBase);
     uint8_t *cbij = ck + kChunkBij;
+    double2 *cw = reinterpret_cast<double2 *>(ck + kChunkW);
     double *rw = reinterpret_cast<double *>(ck + chunk_bytes(true));
-    uint8_t *rbn = ck + chunk_bytes(true) + align_up(8 * (size_t)a.max_m, 16);
 
     if (!GH)
         for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
@@ -190,11 +194,11 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     __syncthreads();
 
     unsigned int wave_hits = 0;
+    HubQueue hub_queue;
+    hub_queue.init(a.qcount, a.batch_cap, lane);
     for (;;) {
-        unsigned int hq = 0;
-        if (lane == 0) hq = atomicAdd(a.queue, 1u);
-        hq = __builtin_amdgcn_readfirstlane(__shfl(hq, 0, kWave));
-        if (hq >= (unsigned int)a.n_hubs) break;
+        uint32_t hq;
+        if (!hub_queue.next(a.queue, lane, hq)) break;
         const int32_t i = __builtin_amdgcn_readfirstlane(a.hubs[hq]);
         const int64_t rb = a.row_ptr[i], re = a.row_ptr[i + 1];
         const int32_t m = (int32_t)(re - rb);
@@ -204,12 +208,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         const uint8_t *hbin = a.bin_h + (rb - a.base_h);
         const int32_t hub_hi = hrow[m - 1];
         const double wi = W ? a.w_s[i] : 0.0;
-        if (W) {
-            for (int p = lane; p < m; p += kWave) {
-                rw[p] = a.w_s[hrow[p]];
-                rbn[p] = hbin[p];
-            }
-        }
+        if (W)
+            for (int p = lane; p < m; p += kWave) rw[p] = a.w_s[hrow[p]];
 
         // spokes of this tile: hub-row positions [p_lo, p_hi) with j in [s_lo, s_hi)
         int32_t p_lo = 0, p_hi = m;
@@ -244,8 +244,12 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             if (total == 0) return;
             cpre[lane] = (uint32_t)(incl - len);
             if (lane == kWave - 1) cpre[kWave] = (uint32_t)incl;
-            cbase[lane] = sb - (incl - len);
-            if (!W) cbij[lane] = (uint8_t)bj;
+            cbase[lane] = sb - base_s - (incl - len);
+            cbij[lane] = (uint8_t)bj;
+            if (W) {
+                const double wj = len > 0 ? rw[p0 + lane] : 0.0;
+                cw[lane] = make_double2(fmin(wi, wj), fmax(wi, wj));
+            }
             wave_lds_sync();
             // owner spoke of flat index t: the last q with cpre[q] <= t (then t < cpre[q+1]).  The
             // owner's end and row pointers stay in registers; LDS is read again only when t
@@ -259,19 +263,21 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 }
             }
             int32_t qend = (int32_t)cpre[q + 1];
-            const int32_t *cp = col_s + (cbase[q] - base_s);  // flat element t is cp[t]
-            const uint8_t *bp = bin_s + (cbase[q] - base_s);
+            const int32_t *cp = col_s + cbase[q];  // flat element t is cp[t]
+            const uint8_t *bp = bin_s + cbase[q];
+            int32_t own = q | ((int32_t)cbij[q] << 8);  // owner spoke and its bin
             auto seek = [&](int32_t t) __attribute__((always_inline)) {
                 if (t >= qend) {
                     do {
                         ++q;
                         qend = (int32_t)cpre[q + 1];
                     } while (t >= qend);
-                    cp = col_s + (cbase[q] - base_s);
-                    bp = bin_s + (cbase[q] - base_s);
+                    cp = col_s + cbase[q];
+                    bp = bin_s + cbase[q];
+                    own = q | ((int32_t)cbij[q] << 8);
                 }
             };
-            auto process = [&](int32_t k, int32_t bjk, int32_t qu) __attribute__((always_inline)) {
+            auto process = [&](int32_t k, int32_t bjk, int32_t ow) __attribute__((always_inline)) {
                 int32_t mo;
                 if constexpr (BANDED) {
                     mo = k - blo;  // k = -1 (no element) falls outside as well
@@ -287,26 +293,27 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     if (k >= lim) return;  // in a gap between the runs
                     mo = k + d;
                 }
-                const uint32_t v = W ? (uint32_t)map16[mo] : (uint32_t)map8[mo];
+                const uint32_t v = W ? mapw[mo] : (uint32_t)map8[mo];
                 if (!v) return;
-                const int32_t bij = W ? (int32_t)rbn[p0 + qu] : (int32_t)cbij[qu];
-                const int32_t bik = W ? (int32_t)rbn[v - 1] : (int32_t)v - 1;
+                const int32_t bij = ow >> 8;
+                const int32_t bik = W ? (int32_t)(v >> 16) : (int32_t)v - 1;
                 const int32_t x = min(bij, min(bik, bjk)), z = max(bij, max(bik, bjk));
                 const int32_t y = bij + bik + bjk - x - z;
                 const int32_t c = rA[x] + rB[y] + z;
                 if (GH) atomicAdd(&g_counts[c], 1ull);
                 else atomicAdd(&hc[c], 1u);
                 if (W) {
-                    const double wj = rw[p0 + qu], wk = rw[v - 1];
-                    const double x1 = fmin(wi, wj), x2 = fmax(wi, wj);
-                    const double w1 = fmin(x1, wk), tt = fmax(x1, wk);
-                    const double w2 = fmin(x2, tt), w3 = fmax(x2, tt);
+                    // the three weights ascending: the spoke's pair is sorted already
+                    const double2 ij = cw[ow & 0xff];
+                    const double wk = rw[(v & 0xffffu) - 1];
+                    const double w1 = fmin(ij.x, wk), tt = fmax(ij.x, wk);
+                    const double w2 = fmin(ij.y, tt), w3 = fmax(ij.y, tt);
                     const double pr = __dmul_rn(__dmul_rn(w1, w2), w3);
-                    const double qv = rint(__dmul_rn(pr, two_s));     // exact integer
+                    const double qv = rint(__dmul_rn(pr, two_s));     // exact integer, |qv| < 2^57
                     const double qh = floor(__dmul_rn(qv, 0x1p-28));   // in [-2^29, 2^29)
                     const double ql = __fma_rn(-qh, 0x1p28, qv);       // in [0, 2^28)
-                    const unsigned long long ul = (unsigned long long)ql;
-                    const unsigned long long uh = (unsigned long long)((long long)qh + (1ll << 29));
+                    const unsigned long long ul = (uint32_t)ql;
+                    const unsigned long long uh = (uint32_t)((int32_t)qh + (1 << 29));
                     if (GH) {
                         add_u128(&g_limbs[4 * c], ul);
                         add_u128(&g_limbs[4 * c + 2], uh);
@@ -325,7 +332,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 for (int u = 0; u < kUnroll; ++u) {
                     const int32_t t = t0 + u * kWave + lane;
                     seek(t);
-                    qq[u] = q;
+                    qq[u] = own;
                     kk[u] = cp[(uint32_t)t];
                     bb[u] = bp[(uint32_t)t];
                 }
@@ -339,10 +346,10 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     const int32_t t = t0 + u * kWave + lane;
                     kk[u] = -1;
                     bb[u] = 0;
-                    qq[u] = q;
+                    qq[u] = own;
                     if (t < total) {
                         seek(t);
-                        qq[u] = q;
+                        qq[u] = own;
                         kk[u] = cp[(uint32_t)t];
                         bb[u] = bp[(uint32_t)t];
                     }
@@ -356,14 +363,14 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         uint32_t *map32 = reinterpret_cast<uint32_t *>(wb);
         if constexpr (!BANDED) {
             // one map over the whole domain: k -> run by comparisons against the run starts
-            const int map_words = ((W ? 2 : 1) * dom.size + 3) >> 2;
+            const int map_words = W ? dom.size : (dom.size + 3) >> 2;
             for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
             wave_lds_sync();
             for (int p = lane; p < m; p += kWave) {
                 const int32_t k = hrow[p];
                 const int32_t d = d0 + (k >= l1 ? e1 : 0) + (k >= l2 ? e2 : 0) + (k >= l3 ? e3 : 0) +
                                   (k >= l4 ? e4 : 0);
-                if (W) map16[k + d] = (uint16_t)(p + 1);
+                if (W) mapw[k + d] = (uint32_t)(p + 1) | ((uint32_t)hbin[p] << 16);
                 else map8[k + d] = (uint8_t)(hbin[p] + 1);
             }
             wave_lds_sync();
@@ -373,7 +380,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 int32_t len = 0, bj = 0;
                 if (p < p_hi) {
                     const int32_t j = hrow[p];
-                    if (!W) bj = hbin[p];
+                    bj = hbin[p];
                     sb = a.row_ptr[j];
                     len = (int32_t)(a.row_ptr[j + 1] - sb);
                 }
@@ -392,12 +399,12 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 for (int t = 1; t < 5; ++t)
                     if (bq == t) { blo = dom.lo[t]; bhi = dom.hi[t]; }
                 const int32_t bsize = bhi - blo;
-                const int map_words = ((W ? 2 : 1) * bsize + 3) >> 2;
+                const int map_words = W ? bsize : (bsize + 3) >> 2;
                 for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
                 wave_lds_sync();
                 for (int p = hp_lo + lane; p < hp_hi; p += kWave) {
                     const int32_t k = hrow[p];
-                    if (W) map16[k - blo] = (uint16_t)(p + 1);
+                    if (W) mapw[k - blo] = (uint32_t)(p + 1) | ((uint32_t)hbin[p] << 16);
                     else map8[k - blo] = (uint8_t)(hbin[p] + 1);
                 }
                 wave_lds_sync();
@@ -412,7 +419,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                         const int tlo = btab[sj * 5 + bq], thi = btab[70 + sj * 5 + bq];
                         if (tlo < thi) {
                             const int32_t j = hrow[p];
-                            if (!W) bj = hbin[p];
+                            bj = hbin[p];
                             const uint32_t *jso = a.slot_off + (int64_t)j * 16;
                             const uint32_t beg = jso[tlo];
                             sb = a.row_ptr[j] + beg;
@@ -544,8 +551,8 @@ static void band_table(int64_t g, uint8_t out[145]) {
     }
 }
 
-int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, double *maxabs,
-                   hipStream_t s);
+int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, unsigned long long *d_m,
+                   int32_t *d_bad, double *maxabs, hipStream_t s);
 
 // Scale exponent of the exact weighted sums: s = 57 - e, with M = fl(fl(a*a)*a) = f 2^e,
 // f in [0.5, 1), for a = max |w|; then |p * 2^s| < 2^57 for every triangle product p.
@@ -573,32 +580,42 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     const int64_t ncfg = gtc_num_configs(3, nb);
     GTC_TRY(fill_u64(d_counts, ncfg, 0ull, s));
 
+    // one block for the call's device scratch: internal-order weights, sum limbs, the hub class
+    // queue, and (out-of-core) the hub and search window buffers
     double *w_s = nullptr;
-    unsigned long long *limbs = nullptr;
-    unsigned int *queue = nullptr;
+    unsigned long long *limbs = nullptr, *d_maxabs = nullptr;
+    int32_t *d_bad = nullptr;
+    unsigned int *queue = nullptr, *qcount = nullptr;
+    int32_t *wcol[2] = {nullptr, nullptr};
+    uint8_t *wbin[2] = {nullptr, nullptr};
+    void *scratch = nullptr;
     int rc = GTC_OK;
     int scale = 0;
-    hipEvent_t ev0 = nullptr, ev1 = nullptr;
-    auto cleanup = [&]() {
-        dev_free(w_s, s);
-        dev_free(limbs, s);
-        dev_free(queue, s);
-        if (ev0) (void)hipEventDestroy(ev0);
-        if (ev1) (void)hipEventDestroy(ev1);
-    };
+    auto cleanup = [&]() { dev_free(scratch, s); };
 #define STEP(expr) do { rc = (expr); if (rc) { cleanup(); return rc; } } while (0)
 #define STEP_HIP(call) do { hipError_t e_ = (call); if (e_ != hipSuccess) { rc = hip_fail(e_, #call, __FILE__, __LINE__); cleanup(); return rc; } } while (0)
 
+    STEP(carve_alloc(&scratch, s, [&](Carver &c) {
+        if (W) {
+            c.take(&w_s, G->n);
+            c.take(&limbs, 4 * ncfg);
+            c.take(&d_maxabs, 1);
+            c.take(&d_bad, 1);
+        }
+        c.take(&queue, (size_t)kHubClasses * kQueueStride);
+        c.take(&qcount, kHubClasses);
+        if (G->host_csr)
+            for (int b2 = 0; b2 < 2; ++b2) {
+                c.take(&wcol[b2], G->max_window_edges);
+                c.take(&wbin[b2], G->max_window_edges);
+            }
+    }));
     if (W) {
         double maxabs = 0.0;
-        STEP(dev_alloc_n(&w_s, G->n, s));
-        STEP(gather_weights(G, d_w, w_s, &maxabs, s));
+        STEP(gather_weights(G, d_w, w_s, d_maxabs, d_bad, &maxabs, s));
         scale = weight_scale_for(maxabs);
-        STEP(dev_alloc_n(&limbs, 4 * ncfg, s));
         STEP(fill_u64(reinterpret_cast<uint64_t *>(limbs), 4 * ncfg, 0ull, s));
     }
-    STEP(dev_alloc_n(&queue, 1, s));
-    STEP(fill_u32(queue, 1, 0u, s));
 
     TripletArgs a{};
     a.row_ptr = G->row_ptr;
@@ -627,7 +644,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.slot_off = G->slot_off;
     a.max_m = (int32_t)std::max<int64_t>(G->max_deg, 1);
     const int64_t map_labels = std::max<int64_t>(banded ? G->max_band : G->max_domain, 1);
-    a.map_bytes = (int32_t)align_up((W ? 2 : 1) * (size_t)map_labels, 16);
+    a.map_bytes = (int32_t)align_up(map_entry_bytes(W) * (size_t)map_labels, 16);
     a.wave_bytes = (int32_t)(a.map_bytes + chunk_bytes(W) + hubrow_bytes(W, a.max_m));
     if (W && G->max_deg >= 65535) {
         set_error("weighted 3pCF: a forward row of %lld entries exceeds the 16-bit position map",
@@ -642,21 +659,16 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.w_s = w_s;
     a.two_s = std::ldexp(1.0, scale);
     a.queue = queue;
+    a.qcount = qcount;
     a.counts = reinterpret_cast<unsigned long long *>(d_counts);
     a.limbs = limbs;
 
     float kms = 0.f, h2d_ms = 0.f;
     TripletPlan used{};
     int64_t tiles_run = 0;
-    // window buffers of an out-of-core graph: [0] hub window, [1] search window
-    int32_t *wcol[2] = {nullptr, nullptr};
-    uint8_t *wbin[2] = {nullptr, nullptr};
+    // window buffers of an out-of-core graph (in the scratch block): [0] hub window, [1] search
     std::vector<hipEvent_t> kev, cev;  // kernel and copy event pairs
     auto cleanup_tiles = [&]() {
-        for (int b2 = 0; b2 < 2; ++b2) {
-            dev_free(wcol[b2], s);
-            dev_free(wbin[b2], s);
-        }
         for (auto e : kev) (void)hipEventDestroy(e);
         for (auto e : cev) (void)hipEventDestroy(e);
         kev.clear();
@@ -695,11 +707,6 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         const int64_t nw = (int64_t)G->win.size() - 1;
         const bool ooc = G->host_csr;
         const std::vector<int64_t> &hr = G->h_row_ptr;
-        if (ooc)
-            for (int b2 = 0; b2 < 2; ++b2) {
-                TSTEP(dev_alloc_n(&wcol[b2], G->max_window_edges, s));
-                TSTEP(dev_alloc_n(&wbin[b2], G->max_window_edges, s));
-            }
         auto load_window = [&](int64_t w, int b2) -> int {
             const int64_t e0 = hr[G->win[w]], ne = hr[G->win[w + 1]] - e0;
             if (ne <= 0) return GTC_OK;
@@ -717,6 +724,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             if (ooc) TSTEP(load_window(h, 0));
             a.hubs = G->hubs + G->win_hubs[h];
             a.n_hubs = (int32_t)nh;
+            TSTEP(hub_class_counts(a.hubs, nh, G->row_ptr, G->work, qcount, s));
             a.col_h = ooc ? wcol[0] : G->col;
             a.bin_h = ooc ? wbin[0] : G->bin;
             a.base_h = ooc ? hr[G->win[h]] : 0;
@@ -727,9 +735,10 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
                 a.base_s = ooc ? hr[G->win[sw]] : 0;
                 a.s_lo = nw == 1 ? 0 : (int32_t)G->win[sw];
                 a.s_hi = nw == 1 ? (int32_t)G->n : (int32_t)G->win[sw + 1];
-                TSTEP(fill_u32(queue, 1, 0u, s));
+                TSTEP(fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s));
                 TripletPlan tp = pl;
                 tp.blocks = (int)std::min<int64_t>(pl.blocks, (nh + pl.waves - 1) / pl.waves);
+                a.batch_cap = batch_cap(nh, (int64_t)tp.blocks * tp.waves);
                 TSTEP(event_pair(kev));
                 TSTEP_HIP(hipEventRecord(kev[kev.size() - 2], s));
                 TSTEP(launch_triplet(kfn, a, tp, s));

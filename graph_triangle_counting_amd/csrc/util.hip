@@ -135,8 +135,18 @@ __global__ void __launch_bounds__(kScanThreads)
         out[n] = off + tot;  // n is a tile multiple: the total sits past the last tile
 }
 
+// Scratch of a scan of n items: the tile totals and their scan, for every level of recursion.
+template <class Tout>
+static size_t scan_ws_elems(int64_t n) {
+    const int64_t tiles = (n + kScanTile - 1) / kScanTile;
+    if (n <= 0 || tiles <= 1) return 0;
+    return (size_t)(2 * tiles + 1) + scan_ws_elems<Tout>(tiles);
+}
+
+size_t scan_workspace_bytes(int64_t n) { return sizeof(int64_t) * scan_ws_elems<int64_t>(n); }
+
 template <class Tin, class Tout>
-static int exclusive_scan(const Tin *in, Tout *out, int64_t n, hipStream_t s) {
+static int exclusive_scan(const Tin *in, Tout *out, int64_t n, Tout *ws, hipStream_t s) {
     if (n <= 0) return fill<Tout>(out, 1, (Tout)0, s);
     const int64_t tiles = (n + kScanTile - 1) / kScanTile;
     if (tiles > INT32_MAX) {
@@ -149,28 +159,21 @@ static int exclusive_scan(const Tin *in, Tout *out, int64_t n, hipStream_t s) {
         GTC_HIP_CHECK(hipGetLastError());
         return GTC_OK;
     }
-    Tout *sums = nullptr, *offs = nullptr;
-    GTC_TRY(dev_alloc_n(&sums, tiles, s));
-    int rc = dev_alloc_n(&offs, tiles + 1, s);
-    if (rc) { dev_free(sums, s); return rc; }
+    Tout *sums = ws, *offs = ws + tiles;
     hipLaunchKernelGGL((k_tile_sums<Tin, Tout>), dim3((unsigned)tiles), dim3(kScanThreads), 0, s,
                        in, n, sums);
-    rc = exclusive_scan<Tout, Tout>(sums, offs, tiles, s);
-    if (!rc)
-        hipLaunchKernelGGL((k_tile_scan<Tin, Tout>), dim3((unsigned)tiles), dim3(kScanThreads), 0,
-                           s, in, n, (const Tout *)offs, out);
-    dev_free(sums, s);
-    dev_free(offs, s);
-    if (rc) return rc;
+    GTC_TRY((exclusive_scan<Tout, Tout>(sums, offs, tiles, ws + 2 * tiles + 1, s)));
+    hipLaunchKernelGGL((k_tile_scan<Tin, Tout>), dim3((unsigned)tiles), dim3(kScanThreads), 0, s,
+                       in, n, (const Tout *)offs, out);
     GTC_HIP_CHECK(hipGetLastError());
     return GTC_OK;
 }
 
-int exclusive_scan_i32_to_i64(const int32_t *in, int64_t *out, int64_t n, hipStream_t s) {
-    return exclusive_scan<int32_t, int64_t>(in, out, n, s);
+int exclusive_scan_i32_to_i64(const int32_t *in, int64_t *out, int64_t n, void *ws, hipStream_t s) {
+    return exclusive_scan<int32_t, int64_t>(in, out, n, static_cast<int64_t *>(ws), s);
 }
-int exclusive_scan_i32_to_i32(const int32_t *in, int32_t *out, int64_t n, hipStream_t s) {
-    return exclusive_scan<int32_t, int32_t>(in, out, n, s);
+int exclusive_scan_i32_to_i32(const int32_t *in, int32_t *out, int64_t n, void *ws, hipStream_t s) {
+    return exclusive_scan<int32_t, int32_t>(in, out, n, static_cast<int32_t *>(ws), s);
 }
 
 }  // namespace gtc
