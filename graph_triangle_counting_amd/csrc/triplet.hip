@@ -201,19 +201,38 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         if (!hub_queue.next(a.queue, lane, hq)) break;
         const int32_t i = __builtin_amdgcn_readfirstlane(a.hubs[hq]);
         const int64_t rb = a.row_ptr[i], re = a.row_ptr[i + 1];
+        const int32_t key_i = a.key_s[i];
+        const double wi = W ? a.w_s[i] : 0.0;
         const int32_t m = (int32_t)(re - rb);
-        HubDomain dom;
-        hub_domain(i, a.key_s[i], a.gr, a.cell_start, dom);
         const int32_t *hrow = a.col_h + (rb - a.base_h);
         const uint8_t *hbin = a.bin_h + (rb - a.base_h);
-        const int32_t hub_hi = hrow[m - 1];
-        const double wi = W ? a.w_s[i] : 0.0;
+        // The first 64 positions of the hub row with their spoke rows (and weights), loaded in one
+        // pass: the hub map, the hub weights and the first chunk of spokes take them from here,
+        // which keeps a hub's set-up to four dependent rounds of global loads.
+        int32_t j0 = 0, b0 = 0, len0 = 0;
+        int64_t sb0 = 0;
+        double wj0 = 0.0;
+        // (Banded hubs are long and read their spokes per band: they skip this.)
+        if (!BANDED && lane < m) {
+            j0 = hrow[lane];
+            b0 = hbin[lane];
+        }
+        HubDomain dom;
+        hub_domain(i, key_i, a.gr, a.cell_start, dom);
+        if (!BANDED && lane < m) {
+            sb0 = a.row_ptr[j0];
+            len0 = (int32_t)(a.row_ptr[j0 + 1] - sb0);
+            if (W) wj0 = a.w_s[j0];
+        }
+        const int32_t hub_lo = BANDED ? hrow[0] : __shfl(j0, 0, kWave);
+        const int32_t hub_hi = !BANDED && m <= kWave ? __shfl(j0, m - 1, kWave) : hrow[m - 1];
         if (W)
-            for (int p = lane; p < m; p += kWave) rw[p] = a.w_s[hrow[p]];
+            for (int p = lane; p < m; p += kWave)
+                rw[p] = !BANDED && p < kWave ? wj0 : a.w_s[hrow[p]];
 
         // spokes of this tile: hub-row positions [p_lo, p_hi) with j in [s_lo, s_hi)
         int32_t p_lo = 0, p_hi = m;
-        if (a.s_lo > hrow[0] || a.s_hi <= hub_hi) {
+        if (a.s_lo > hub_lo || a.s_hi <= hub_hi) {
             int32_t l = 0, h = m;
             while (l < h) { const int32_t md = (l + h) >> 1; if (hrow[md] < a.s_lo) l = md + 1; else h = md; }
             p_lo = l;
@@ -367,11 +386,12 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
             wave_lds_sync();
             for (int p = lane; p < m; p += kWave) {
-                const int32_t k = hrow[p];
+                const int32_t k = p < kWave ? j0 : hrow[p];
+                const int32_t bk = p < kWave ? b0 : hbin[p];
                 const int32_t d = d0 + (k >= l1 ? e1 : 0) + (k >= l2 ? e2 : 0) + (k >= l3 ? e3 : 0) +
                                   (k >= l4 ? e4 : 0);
-                if (W) mapw[k + d] = (uint32_t)(p + 1) | ((uint32_t)hbin[p] << 16);
-                else map8[k + d] = (uint8_t)(hbin[p] + 1);
+                if (W) mapw[k + d] = (uint32_t)(p + 1) | ((uint32_t)bk << 16);
+                else map8[k + d] = (uint8_t)(bk + 1);
             }
             wave_lds_sync();
             for (int32_t p0 = p_lo; p0 < p_hi; p0 += kWave) {
@@ -379,10 +399,16 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 int64_t sb = 0;
                 int32_t len = 0, bj = 0;
                 if (p < p_hi) {
-                    const int32_t j = hrow[p];
-                    bj = hbin[p];
-                    sb = a.row_ptr[j];
-                    len = (int32_t)(a.row_ptr[j + 1] - sb);
+                    if (p0 == 0) {  // positions 0..63: loaded with the hub
+                        bj = b0;
+                        sb = sb0;
+                        len = len0;
+                    } else {
+                        const int32_t j = hrow[p];
+                        bj = hbin[p];
+                        sb = a.row_ptr[j];
+                        len = (int32_t)(a.row_ptr[j + 1] - sb);
+                    }
                 }
                 walk(p0, sb, len, bj, 0, 0);
             }
@@ -404,8 +430,9 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 wave_lds_sync();
                 for (int p = hp_lo + lane; p < hp_hi; p += kWave) {
                     const int32_t k = hrow[p];
-                    if (W) mapw[k - blo] = (uint32_t)(p + 1) | ((uint32_t)hbin[p] << 16);
-                    else map8[k - blo] = (uint8_t)(hbin[p] + 1);
+                    const int32_t bk = hbin[p];
+                    if (W) mapw[k - blo] = (uint32_t)(p + 1) | ((uint32_t)bk << 16);
+                    else map8[k - blo] = (uint8_t)(bk + 1);
                 }
                 wave_lds_sync();
                 for (int32_t p0 = p_lo; p0 < sp_hi; p0 += kWave) {
