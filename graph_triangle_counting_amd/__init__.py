@@ -63,7 +63,7 @@ def lib() -> C.CDLL:
         L.gtc_config_bins.argtypes = [i32, i32, P]
         L.gtc_graph_export.argtypes = [P, P, P, P, P]
         L.gtc_graph_stats.argtypes = [P, C.POINTER(Stats)]
-        L.gtc_plan_windows.argtypes = [P, i64, i64, P]
+        L.gtc_plan_windows.argtypes = [P, i64, i64, i32, P]
         L.gtc_plan_windows.restype = i64
         L.gtc_graph_free.argtypes = [P]
         L.gtc_graph_free.restype = None

@@ -256,18 +256,31 @@ int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h
     if (h_row_ptr)
         GTC_HIP_CHECK(hipMemcpyAsync(h_row_ptr, g->row_ptr, sizeof(int64_t) * (g->n + 1),
                                      hipMemcpyDeviceToHost, s));
+    // packed entries come out through the label array (or a host buffer) and are split below
+    std::vector<int32_t> words;
+    int32_t *w_dst = h_col;
+    if (g->packed && h_bin && !h_col && g->E) {
+        words.resize(g->E);
+        w_dst = words.data();
+    }
     if (g->host_csr) {  // out-of-core graph: the CSR is already in host memory
-        if (h_col && g->E) std::memcpy(h_col, g->h_col, sizeof(int32_t) * g->E);
-        if (h_bin && g->E) std::memcpy(h_bin, g->h_bin, g->E);
+        if (w_dst && g->E) std::memcpy(w_dst, g->h_col, sizeof(int32_t) * g->E);
+        if (!g->packed && h_bin && g->E) std::memcpy(h_bin, g->h_bin, g->E);
     } else {
-        if (h_col && g->E)
-            GTC_HIP_CHECK(hipMemcpyAsync(h_col, g->col, sizeof(int32_t) * g->E, hipMemcpyDeviceToHost, s));
-        if (h_bin && g->E)
+        if (w_dst && g->E)
+            GTC_HIP_CHECK(hipMemcpyAsync(w_dst, g->col, sizeof(int32_t) * g->E, hipMemcpyDeviceToHost, s));
+        if (!g->packed && h_bin && g->E)
             GTC_HIP_CHECK(hipMemcpyAsync(h_bin, g->bin, g->E, hipMemcpyDeviceToHost, s));
     }
     if (h_perm && g->n)
         GTC_HIP_CHECK(hipMemcpyAsync(h_perm, g->perm, sizeof(int32_t) * g->n, hipMemcpyDeviceToHost, s));
     GTC_HIP_CHECK(hipStreamSynchronize(s));
+    if (g->packed && w_dst)
+        for (int64_t e = 0; e < g->E; ++e) {
+            const uint32_t w = (uint32_t)w_dst[e];
+            if (h_bin) h_bin[e] = (uint8_t)(w >> 24);
+            if (h_col) h_col[e] = (int32_t)(w & kLabelMask);
+        }
     return GTC_OK;
 }
 
@@ -290,9 +303,10 @@ void gtc_graph_free(gtc_graph g) {
 }
 
 int64_t gtc_plan_windows(const int64_t *h_row_ptr, int64_t n, int64_t tile_bytes,
-                         int64_t *h_bounds) {
-    if (!h_row_ptr || !h_bounds || n < 0 || tile_bytes <= 0) {
-        set_error("gtc_plan_windows: need row offsets, a bounds array, n >= 0 and tile_bytes > 0");
+                         int32_t entry_bytes, int64_t *h_bounds) {
+    if (!h_row_ptr || !h_bounds || n < 0 || tile_bytes <= 0 || entry_bytes <= 0) {
+        set_error("gtc_plan_windows: need row offsets, a bounds array, n >= 0, tile_bytes > 0 "
+                  "and entry_bytes > 0");
         return GTC_E_INVALID;
     }
     for (int64_t i = 0; i < n; ++i)
@@ -300,7 +314,7 @@ int64_t gtc_plan_windows(const int64_t *h_row_ptr, int64_t n, int64_t tile_bytes
             set_error("gtc_plan_windows: row offsets decrease at row %lld", (long long)i);
             return GTC_E_INVALID;
         }
-    return plan_windows(h_row_ptr, n, tile_bytes, h_bounds);
+    return plan_windows(h_row_ptr, n, tile_bytes, entry_bytes, h_bounds);
 }
 
 const char *gtc_status_string(int status) {

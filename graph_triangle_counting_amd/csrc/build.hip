@@ -7,6 +7,8 @@
 // Two passes over the same traversal: count (degrees, then a 64-bit scan to row offsets), emit.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
+#include <cstring>
 
 #include "gtc_internal.h"
 
@@ -58,7 +60,7 @@ struct PairArgs {
     const int64_t *row_ptr;  // emit pass input
     int64_t col_base;        // emit pass: entry e of the CSR is col[e - col_base] (window buffer)
     int32_t *col;
-    uint8_t *bin;
+    uint8_t *bin;            // null: packed entries (bin in the top byte of col)
     uint32_t *slot_off;      // emit pass: [n][16] start of each forward cell slot in the row
 };
 
@@ -94,8 +96,12 @@ __global__ void __launch_bounds__(256) k_pairs(PairArgs a) {
                         const int m = (l + h) >> 1;
                         if (d2 >= se[m]) l = m; else h = m;
                     }
-                    a.col[w] = j;
-                    a.bin[w] = (uint8_t)l;
+                    if (a.bin) {
+                        a.col[w] = j;
+                        a.bin[w] = (uint8_t)l;
+                    } else {
+                        a.col[w] = (int32_t)pack_entry(j, l);
+                    }
                     ++w;
                 } else {
                     ++cnt;
@@ -154,7 +160,8 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
 
 __global__ void __launch_bounds__(256)
     k_degstats(int32_t h_lo, int32_t h_hi, const int64_t *__restrict__ row_ptr,
-               const int32_t *__restrict__ col, int64_t col_base, const int32_t *__restrict__ deg,
+               const int32_t *__restrict__ col, int64_t col_base, uint32_t label_mask,
+               const int32_t *__restrict__ deg,
                const int32_t *__restrict__ key_s, const int32_t *__restrict__ cell_start, Grid gr,
                int64_t *__restrict__ work, StatsOut *out, unsigned long long *win_last) {
     constexpr int L = 16;
@@ -167,7 +174,7 @@ __global__ void __launch_bounds__(256)
     for (int64_t h = hub0; h < h_hi; h += stride) {
         const int64_t b = row_ptr[h], e = row_ptr[h + 1];
         int64_t s = 0;
-        for (int64_t t = b + sub; t < e; t += L) s += deg[col[t - col_base]];
+        for (int64_t t = b + sub; t < e; t += L) s += deg[(uint32_t)col[t - col_base] & label_mask];
 #pragma unroll
         for (int d = L / 2; d > 0; d >>= 1) s += __shfl_xor(s, d, L);
         if (sub == 0) {
@@ -187,7 +194,8 @@ __global__ void __launch_bounds__(256)
                 my_hubs += 1;
             }
             if (m > 0) {  // largest spoke label of the window: bounds its search windows
-                const unsigned long long last = (unsigned long long)col[e - 1 - col_base];
+                const unsigned long long last =
+                    (unsigned long long)((uint32_t)col[e - 1 - col_base] & label_mask);
                 my_last = last > my_last ? last : my_last;
             }
         }
@@ -340,6 +348,10 @@ static inline unsigned grid_for(int64_t n, int threads) {
 
 int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     const int64_t n = G->n;
+    // packed CSR entries when labels fit 24 bits (GTC_CSR_LAYOUT=split keeps two arrays)
+    G->packed = n <= kPackedMaxN;
+    if (const char *env = std::getenv("GTC_CSR_LAYOUT"))
+        if (!std::strcmp(env, "split")) G->packed = false;
     G->grid = choose_grid(n, G->edges[G->nb]);
     const Grid gr = G->grid;
 
@@ -446,7 +458,8 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
                                 hipMemcpyDeviceToHost, s));
         STEP_HIP(hipStreamSynchronize(s));
         std::vector<int64_t> bounds(n + 2);
-        const int64_t Wn = plan_windows(G->h_row_ptr.data(), n, G->tile_bytes, bounds.data());
+        const int64_t Wn = plan_windows(G->h_row_ptr.data(), n, G->tile_bytes, G->packed ? 4 : 5,
+                                        bounds.data());
         G->win.assign(bounds.begin(), bounds.begin() + Wn + 1);
         G->max_window_edges = 0;
         for (int64_t k = 0; k < Wn; ++k)
@@ -465,7 +478,7 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         c.take(&win_last, W);
         if (G->host_csr) {  // staging of one window's rows on their way to the pinned CSR
             c.take(&st_col, G->max_window_edges);
-            c.take(&st_bin, G->max_window_edges);
+            if (!G->packed) c.take(&st_bin, G->max_window_edges);
         }
     }));
     STEP2(fill_u64(reinterpret_cast<uint64_t *>(win_last), W, 0ull, s));
@@ -474,12 +487,13 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         // staging buffer and copied out
         STEP2_HIP(hipHostMalloc(reinterpret_cast<void **>(&G->h_col),
                                 sizeof(int32_t) * std::max<int64_t>(G->E, 1), hipHostMallocDefault));
-        STEP2_HIP(hipHostMalloc(reinterpret_cast<void **>(&G->h_bin), std::max<int64_t>(G->E, 1),
-                                hipHostMallocDefault));
+        if (!G->packed)
+            STEP2_HIP(hipHostMalloc(reinterpret_cast<void **>(&G->h_bin),
+                                    std::max<int64_t>(G->E, 1), hipHostMallocDefault));
     } else {
         STEP2(carve_alloc(&G->arena_csr, s, [&](Carver &c) {
             c.take(&G->col, G->E);
-            c.take(&G->bin, G->E);
+            if (!G->packed) c.take(&G->bin, G->E);
         }));
     }
     pa.row_ptr = G->row_ptr;
@@ -497,7 +511,8 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         STEP2_HIP(hipGetLastError());
         const int64_t dsb = std::min<int64_t>(((hi - lo) * 16 + 255) / 256, 2048);
         hipLaunchKernelGGL(k_degstats, dim3((unsigned)dsb), dim3(256), 0, s, (int32_t)lo,
-                           (int32_t)hi, G->row_ptr, (const int32_t *)pa.col, e_lo, G->deg, G->key_s,
+                           (int32_t)hi, G->row_ptr, (const int32_t *)pa.col, e_lo,
+                           G->packed ? kLabelMask : 0xffffffffu, G->deg, G->key_s,
                            G->cell_start, gr, G->work, d_stats, win_last + k);
         STEP2_HIP(hipGetLastError());
         if (G->host_csr) {
@@ -505,7 +520,8 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
             if (ne > 0) {
                 STEP2_HIP(hipMemcpyAsync(G->h_col + e_lo, st_col, sizeof(int32_t) * ne,
                                          hipMemcpyDeviceToHost, s));
-                STEP2_HIP(hipMemcpyAsync(G->h_bin + e_lo, st_bin, ne, hipMemcpyDeviceToHost, s));
+                if (!G->packed)
+                    STEP2_HIP(hipMemcpyAsync(G->h_bin + e_lo, st_bin, ne, hipMemcpyDeviceToHost, s));
             }
         }
     }

@@ -22,7 +22,8 @@ namespace gtc {
 struct CliqueArgs {
     const int64_t *row_ptr;
     const int32_t *col;
-    const uint8_t *bin;
+    const uint8_t *bin;    // null: packed entries, the bin in the top byte of col
+    uint32_t label_mask;   // label bits of a col word
     const int32_t *hubs;
     int32_t n_hubs;
     int32_t nb, ncfg;
@@ -150,24 +151,25 @@ __global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *ed
         wave_lds_sync4();
         const int32_t *hrow = a.col + rb;
         for (int p = lane; p < m; p += kWave) {
-            const int32_t k = hrow[p];
+            const uint32_t w = (uint32_t)hrow[p];
+            const int32_t k = (int32_t)(w & a.label_mask);
             int32_t d = dom.delta[0];
 #pragma unroll
             for (int t = 1; t < 5; ++t)
                 if (k >= dom.lo[t]) d = dom.delta[t];
             pmap[k + d] = (uint16_t)(p + 1);
             rc[p] = a.xyz_s[k];
-            rbin[p] = a.bin[rb + p];
+            rbin[p] = a.bin ? a.bin[rb + p] : (uint8_t)(w >> 24);
         }
         wave_lds_sync4();
-        const int32_t hub_hi = hrow[m - 1];
+        const int32_t hub_hi = (int32_t)((uint32_t)hrow[m - 1] & a.label_mask);
 
         // local connectivity: for every spoke a, walk N+(j_a) against the hub map
         for (int sp = 0; sp < m - 1; ++sp) {
-            const int32_t j = hrow[sp];
+            const int32_t j = (int32_t)((uint32_t)hrow[sp] & a.label_mask);
             const int64_t jb = a.row_ptr[j], je = a.row_ptr[j + 1];
             for (int64_t e = jb + lane; e < je; e += kWave) {
-                const int32_t k = a.col[e];
+                const int32_t k = (int32_t)((uint32_t)a.col[e] & a.label_mask);
                 if (k > hub_hi) break;
                 int32_t d = dom.delta[0], lim = dom.hi[0];
 #pragma unroll
@@ -268,6 +270,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     a.row_ptr = G->row_ptr;
     a.col = G->col;
     a.bin = G->bin;
+    a.label_mask = G->packed ? kLabelMask : 0xffffffffu;
     a.hubs = G->hubs;
     a.n_hubs = (int32_t)G->n_hubs;
     a.nb = G->nb;

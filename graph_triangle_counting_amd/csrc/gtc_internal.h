@@ -6,8 +6,9 @@
 //   perm       int32 [n]     internal -> original label
 //   cell_start int32 [ncell+1] first internal label of each cell (cells in key order)
 //   row_ptr    int64 [n+1]   forward CSR offsets (64-bit: edge counts pass 2^31, §III.5.1)
-//   col        int32 [E]     forward neighbours j > i, ascending per row (Eq.(1))
-//   bin        uint8 [E]     radial bin of each edge (§II.1)
+//   col        int32 [E]     forward neighbours j > i, ascending per row (Eq.(1)); in a packed
+//                            graph (n <= 2^24) each word also holds the edge's bin in its top byte
+//   bin        uint8 [E]     radial bin of each edge (§II.1); absent (null) in a packed graph
 //   deg        int32 [n]     forward degree d+(i)
 //   work       int64 [n]     sum of d+(j) over the row of i (spoke elements of hub i)
 //   slot_off   u32 [n][16]   where each of the 14 forward cell slots of row i starts (own cell,
@@ -81,14 +82,40 @@ int carve_alloc(void **block, hipStream_t s, F &&layout) {
 int fill_u64(uint64_t *p, int64_t count, uint64_t value, hipStream_t s);
 int fill_u32(uint32_t *p, int64_t count, uint32_t value, hipStream_t s);
 
-// hub windows: bounds[0..W] of consecutive rows whose CSR (5 bytes per edge) fits tile_bytes
-int64_t plan_windows(const int64_t *row_ptr, int64_t n, int64_t tile_bytes, int64_t *bounds);
+// hub windows: bounds[0..W] of consecutive rows whose CSR (entry_bytes per edge) fits tile_bytes
+int64_t plan_windows(const int64_t *row_ptr, int64_t n, int64_t tile_bytes, int64_t entry_bytes,
+                     int64_t *bounds);
 
 // exclusive scan of n int32 values: out[0..n], out[n] = total.  ws: scan_workspace_bytes(n) bytes
 // of device scratch (partial sums of the tiles).
 size_t scan_workspace_bytes(int64_t n);
 int exclusive_scan_i32_to_i64(const int32_t *in, int64_t *out, int64_t n, void *ws, hipStream_t s);
 int exclusive_scan_i32_to_i32(const int32_t *in, int32_t *out, int64_t n, void *ws, hipStream_t s);
+
+// ------------------------------------------------------------------ CSR entries
+// A packed CSR keeps each entry in one 32-bit word: the neighbour label in the low 24 bits, the
+// bin in the high 8.  It needs labels below 2^24 and moves 4 bytes per entry where a label array
+// plus a bin array move 5.
+constexpr int64_t kPackedMaxN = (int64_t)1 << 24;
+constexpr uint32_t kLabelMask = 0xffffffu;
+
+__host__ __device__ inline uint32_t pack_entry(int32_t j, int32_t b) {
+    return (uint32_t)j | ((uint32_t)b << 24);
+}
+
+// entry e of a CSR (col, bin): its neighbour label and bin
+template <bool PK>
+__device__ __forceinline__ void csr_entry(const int32_t *col, const uint8_t *bin, int64_t e,
+                                          int32_t &k, int32_t &b) {
+    const int32_t w = col[e];
+    if (PK) {
+        k = (int32_t)((uint32_t)w & kLabelMask);
+        b = (int32_t)((uint32_t)w >> 24);
+    } else {
+        k = w;
+        b = bin[e];
+    }
+}
 
 // ------------------------------------------------------------------ cell grid
 struct Grid {
@@ -259,6 +286,7 @@ struct gtc_graph_s {
     int32_t *perm = nullptr;
     int32_t *cell_start = nullptr;
     int64_t *row_ptr = nullptr;
+    bool packed = false;       // col holds packed entries and bin is null (labels below 2^24)
     int32_t *col = nullptr;
     uint8_t *bin = nullptr;
     int32_t *deg = nullptr;

@@ -29,7 +29,7 @@ namespace gtc {
 
 struct TripletArgs {
     const int64_t *row_ptr;  // global row offsets [n+1]
-    // hub window: rows of hubs, entry e at col_h[e - base_h]
+    // hub window: rows of hubs, entry e at col_h[e - base_h] (bin_h null: packed entries)
     const int32_t *col_h;
     const uint8_t *bin_h;
     int64_t base_h;
@@ -145,7 +145,7 @@ __host__ __device__ constexpr int band_slot(int q) { return q == 0 ? 0 : 3 * q -
 // smax [5]) | per-wave regions
 constexpr size_t kBandTableBytes = 160;
 
-template <bool W, bool GH, bool BANDED>
+template <bool W, bool GH, bool BANDED, bool PK>
 __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
@@ -213,10 +213,11 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         int64_t sb0 = 0;
         double wj0 = 0.0;
         // (Banded hubs are long and read their spokes per band: they skip this.)
-        if (!BANDED && lane < m) {
-            j0 = hrow[lane];
-            b0 = hbin[lane];
-        }
+        // label of hub-row position p (packed entries carry the bin in the top byte)
+        auto hlab = [&](int p) __attribute__((always_inline)) {
+            return PK ? (int32_t)((uint32_t)hrow[p] & kLabelMask) : hrow[p];
+        };
+        if (!BANDED && lane < m) csr_entry<PK>(hrow, hbin, lane, j0, b0);
         HubDomain dom;
         hub_domain(i, key_i, a.gr, a.cell_start, dom);
         if (!BANDED && lane < m) {
@@ -224,20 +225,20 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             len0 = (int32_t)(a.row_ptr[j0 + 1] - sb0);
             if (W) wj0 = a.w_s[j0];
         }
-        const int32_t hub_lo = BANDED ? hrow[0] : __shfl(j0, 0, kWave);
-        const int32_t hub_hi = !BANDED && m <= kWave ? __shfl(j0, m - 1, kWave) : hrow[m - 1];
+        const int32_t hub_lo = BANDED ? hlab(0) : __shfl(j0, 0, kWave);
+        const int32_t hub_hi = !BANDED && m <= kWave ? __shfl(j0, m - 1, kWave) : hlab(m - 1);
         if (W)
             for (int p = lane; p < m; p += kWave)
-                rw[p] = !BANDED && p < kWave ? wj0 : a.w_s[hrow[p]];
+                rw[p] = !BANDED && p < kWave ? wj0 : a.w_s[hlab(p)];
 
         // spokes of this tile: hub-row positions [p_lo, p_hi) with j in [s_lo, s_hi)
         int32_t p_lo = 0, p_hi = m;
         if (a.s_lo > hub_lo || a.s_hi <= hub_hi) {
             int32_t l = 0, h = m;
-            while (l < h) { const int32_t md = (l + h) >> 1; if (hrow[md] < a.s_lo) l = md + 1; else h = md; }
+            while (l < h) { const int32_t md = (l + h) >> 1; if (hlab(md) < a.s_lo) l = md + 1; else h = md; }
             p_lo = l;
             h = m;
-            while (l < h) { const int32_t md = (l + h) >> 1; if (hrow[md] < a.s_hi) l = md + 1; else h = md; }
+            while (l < h) { const int32_t md = (l + h) >> 1; if (hlab(md) < a.s_hi) l = md + 1; else h = md; }
             p_hi = l;
         }
 
@@ -283,7 +284,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             }
             int32_t qend = (int32_t)cpre[q + 1];
             const int32_t *cp = col_s + cbase[q];  // flat element t is cp[t]
-            const uint8_t *bp = bin_s + cbase[q];
+            const uint8_t *bp = PK ? nullptr : bin_s + cbase[q];
             int32_t own = q | ((int32_t)cbij[q] << 8);  // owner spoke and its bin
             auto seek = [&](int32_t t) __attribute__((always_inline)) {
                 if (t >= qend) {
@@ -292,7 +293,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                         qend = (int32_t)cpre[q + 1];
                     } while (t >= qend);
                     cp = col_s + cbase[q];
-                    bp = bin_s + cbase[q];
+                    if (!PK) bp = bin_s + cbase[q];
                     own = q | ((int32_t)cbij[q] << 8);
                 }
             };
@@ -352,8 +353,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     const int32_t t = t0 + u * kWave + lane;
                     seek(t);
                     qq[u] = own;
-                    kk[u] = cp[(uint32_t)t];
-                    bb[u] = bp[(uint32_t)t];
+                    csr_entry<PK>(cp, bp, (uint32_t)t, kk[u], bb[u]);
                 }
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) process(kk[u], bb[u], qq[u]);
@@ -369,8 +369,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     if (t < total) {
                         seek(t);
                         qq[u] = own;
-                        kk[u] = cp[(uint32_t)t];
-                        bb[u] = bp[(uint32_t)t];
+                        csr_entry<PK>(cp, bp, (uint32_t)t, kk[u], bb[u]);
                     }
                 }
 #pragma unroll
@@ -386,8 +385,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
             wave_lds_sync();
             for (int p = lane; p < m; p += kWave) {
-                const int32_t k = p < kWave ? j0 : hrow[p];
-                const int32_t bk = p < kWave ? b0 : hbin[p];
+                int32_t k = j0, bk = b0;
+                if (p >= kWave) csr_entry<PK>(hrow, hbin, p, k, bk);
                 const int32_t d = d0 + (k >= l1 ? e1 : 0) + (k >= l2 ? e2 : 0) + (k >= l3 ? e3 : 0) +
                                   (k >= l4 ? e4 : 0);
                 if (W) mapw[k + d] = (uint32_t)(p + 1) | ((uint32_t)bk << 16);
@@ -404,8 +403,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                         sb = sb0;
                         len = len0;
                     } else {
-                        const int32_t j = hrow[p];
-                        bj = hbin[p];
+                        int32_t j;
+                        csr_entry<PK>(hrow, hbin, p, j, bj);
                         sb = a.row_ptr[j];
                         len = (int32_t)(a.row_ptr[j + 1] - sb);
                     }
@@ -429,8 +428,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
                 wave_lds_sync();
                 for (int p = hp_lo + lane; p < hp_hi; p += kWave) {
-                    const int32_t k = hrow[p];
-                    const int32_t bk = hbin[p];
+                    int32_t k, bk;
+                    csr_entry<PK>(hrow, hbin, p, k, bk);
                     if (W) mapw[k - blo] = (uint32_t)(p + 1) | ((uint32_t)bk << 16);
                     else map8[k - blo] = (uint8_t)(bk + 1);
                 }
@@ -445,8 +444,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                         for (int t = 1; t < 14; ++t) sj += (int32_t)hso[t] <= p;
                         const int tlo = btab[sj * 5 + bq], thi = btab[70 + sj * 5 + bq];
                         if (tlo < thi) {
-                            const int32_t j = hrow[p];
-                            bj = hbin[p];
+                            int32_t j;
+                            csr_entry<PK>(hrow, hbin, p, j, bj);
                             const uint32_t *jso = a.slot_off + (int64_t)j * 16;
                             const uint32_t beg = jso[tlo];
                             sb = a.row_ptr[j] + beg;
@@ -497,8 +496,10 @@ struct TripletPlan {
     int blocks = 0;      // persistent grid
 };
 
-static const void *triplet_kernel(bool w, bool gh, bool banded) {
-#define GTC_K(W_, GH_, B_) reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_>)
+static const void *triplet_kernel(bool w, bool gh, bool banded, bool pk) {
+#define GTC_K(W_, GH_, B_)                                                                  \
+    (pk ? reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_, true>)                    \
+        : reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_, false>))
     if (w) return gh ? (banded ? GTC_K(true, true, true) : GTC_K(true, true, false))
                      : (banded ? GTC_K(true, false, true) : GTC_K(true, false, false));
     return gh ? (banded ? GTC_K(false, true, true) : GTC_K(false, true, false))
@@ -634,7 +635,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         if (G->host_csr)
             for (int b2 = 0; b2 < 2; ++b2) {
                 c.take(&wcol[b2], G->max_window_edges);
-                c.take(&wbin[b2], G->max_window_edges);
+                if (!G->packed) c.take(&wbin[b2], G->max_window_edges);
             }
     }));
     if (W) {
@@ -721,7 +722,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         const bool GH = triplet_lds_fixed(a.ncfg, W, false) > dl.lds_per_block / 2 ||
                         max_hub_hits >= 0x7fffffffull / 2;
         TripletPlan pl;
-        const void *kfn = triplet_kernel(W, GH, banded);
+        const void *kfn = triplet_kernel(W, GH, banded, G->packed);
         TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(a.ncfg, W, GH), GH, G->n_hubs, max_hub_hits, pl));
         // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long budget = 0xffffffffull / (unsigned long long)pl.waves;
@@ -741,7 +742,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             GTC_HIP_CHECK(hipEventRecord(cev[cev.size() - 2], s));
             GTC_HIP_CHECK(hipMemcpyAsync(wcol[b2], G->h_col + e0, sizeof(int32_t) * ne,
                                          hipMemcpyHostToDevice, s));
-            GTC_HIP_CHECK(hipMemcpyAsync(wbin[b2], G->h_bin + e0, ne, hipMemcpyHostToDevice, s));
+            if (!G->packed)
+                GTC_HIP_CHECK(hipMemcpyAsync(wbin[b2], G->h_bin + e0, ne, hipMemcpyHostToDevice, s));
             GTC_HIP_CHECK(hipEventRecord(cev.back(), s));
             return GTC_OK;
         };

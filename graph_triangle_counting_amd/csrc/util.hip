@@ -180,21 +180,23 @@ int exclusive_scan_i32_to_i32(const int32_t *in, int32_t *out, int64_t n, void *
 
 namespace gtc {
 
-// Greedy hub windows: consecutive rows while their CSR (5 bytes per edge: 32-bit neighbour and
-// 8-bit bin) fits tile_bytes; a row larger than the budget gets a window of its own.
-int64_t plan_windows(const int64_t *row_ptr, int64_t n, int64_t tile_bytes, int64_t *bounds) {
+// Greedy hub windows: consecutive rows while their CSR (entry_bytes per edge: a packed 32-bit
+// entry, or a 32-bit neighbour plus an 8-bit bin) fits tile_bytes; a row larger than the budget
+// gets a window of its own.
+int64_t plan_windows(const int64_t *row_ptr, int64_t n, int64_t tile_bytes, int64_t entry_bytes,
+                     int64_t *bounds) {
     int64_t W = 0;
     bounds[0] = 0;
     int64_t a = 0;
     while (a < n) {
         // largest b with 5 * (row_ptr[b] - row_ptr[a]) <= tile_bytes (row_ptr is nondecreasing)
         int64_t lo = a + 1, hi = n;
-        if (5 * (row_ptr[lo] - row_ptr[a]) > tile_bytes) {
+        if (entry_bytes * (row_ptr[lo] - row_ptr[a]) > tile_bytes) {
             hi = lo;
         } else {
             while (lo < hi) {
                 const int64_t md = lo + (hi - lo + 1) / 2;
-                if (5 * (row_ptr[md] - row_ptr[a]) <= tile_bytes) lo = md; else hi = md - 1;
+                if (entry_bytes * (row_ptr[md] - row_ptr[a]) <= tile_bytes) lo = md; else hi = md - 1;
             }
         }
         a = hi;

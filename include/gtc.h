@@ -64,9 +64,10 @@ typedef struct gtc_graph_s *gtc_graph;
 
 /* Build options.  A zero-initialised struct (or NULL) means: resident CSR, coordinates kept. */
 typedef struct {
-    /* 0: every row resident in one window.  > 0: rows are split into hub windows whose CSR
-     * (5 bytes per edge) is at most tile_bytes (a single longer row gets a window of its own), and
-     * counting runs as a loop over (hub window, search window) tiles (§III.5.3). */
+    /* 0: every row resident in one window.  > 0: rows are split into hub windows whose CSR is at
+     * most tile_bytes (a single longer row gets a window of its own), and counting runs as a loop
+     * over (hub window, search window) tiles (§III.5.3).  The CSR takes 4 bytes per edge when
+     * n <= 2^24 (label and bin packed in one word) and 5 bytes per edge otherwise. */
     int64_t tile_bytes;
     /* nonzero (with tile_bytes > 0): the CSR lives in pinned host memory and only the active
      * windows of a tile are copied to the device (out-of-core mode, §III.5.3). */
@@ -140,22 +141,24 @@ int64_t gtc_num_configs(int32_t order, int32_t nbins);
 int gtc_config_bins(int32_t order, int32_t nbins, int32_t *h_bins);
 
 /* Copy the graph out to host memory (for tests and inspection).
- *   h_row_ptr int64 [n+1], h_col int32 [E], h_bin uint8 [E]: forward CSR in internal labels;
+ *   h_row_ptr int64 [n+1], h_col int32 [E], h_bin uint8 [E]: forward CSR in internal labels
+ *   (unpacked: labels and bins come out separately whatever the device layout);
  *   h_perm    int32 [n]: h_perm[internal] = original label.  Any pointer may be NULL. */
 int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h_bin,
                      int32_t *h_perm);
 
 /* Hub windows of the tile loop (§III.5.3), for inspection and tests; host only, needs no GPU.
  *   h_row_ptr host int64 [n+1] forward CSR offsets (nondecreasing).
- *   tile_bytes > 0: budget per window at 5 bytes per edge; a row longer than the budget gets a
- *              window of its own.
+ *   tile_bytes > 0: budget per window in CSR bytes; a row longer than the budget gets a window
+ *              of its own.
+ *   entry_bytes > 0: CSR bytes per edge (gtc_build_graph: 4 when n <= 2^24, else 5).
  *   h_bounds  host int64 [n+1] (at least 2): receives the label bounds 0 = b_0 < ... < b_W = n of
  *              consecutive rows (b_1 = 0 when n = 0).
  * Returns W >= 1, or GTC_E_INVALID.  gtc_build_graph uses the same windows; tile (h, s) then
  * walks the spokes of hub window h that lie in window s, for s from h to the window of the
  * largest spoke label of window h, so every forward edge is walked in exactly one tile. */
 int64_t gtc_plan_windows(const int64_t *h_row_ptr, int64_t n, int64_t tile_bytes,
-                         int64_t *h_bounds);
+                         int32_t entry_bytes, int64_t *h_bounds);
 
 /* Graph-level statistics (n, edges, max_out_degree, windows, spoke_elements, build_ms). */
 int gtc_graph_stats(gtc_graph g, gtc_stats *st);

@@ -98,19 +98,18 @@ def test_python_binding_requires_gpu_tensors():
         gtc.Graph(torch.zeros((4, 3), dtype=torch.int32), [0, 10])
 
 
-def _plan(row_ptr, tile_bytes):
+def _plan(row_ptr, tile_bytes, entry_bytes=5):
     L = gtc.lib()
     rp = np.ascontiguousarray(row_ptr, dtype=np.int64)
     n = rp.size - 1
     out = np.zeros(n + 2, np.int64)
-    W = L.gtc_plan_windows(rp.ctypes.data_as(C.c_void_p), n, tile_bytes, out.ctypes.data_as(C.c_void_p))
+    W = L.gtc_plan_windows(rp.ctypes.data_as(C.c_void_p), n, tile_bytes, entry_bytes,
+                           out.ctypes.data_as(C.c_void_p))
     return W, out[:W + 1]
 
 
 def test_plan_windows_partitions_rows_greedily():
     L = gtc.lib()
-    L.gtc_plan_windows.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p]
-    L.gtc_plan_windows.restype = C.c_int64
     rng = np.random.default_rng(5)
     for trial in range(40):
         n = int(rng.integers(1, 400))
@@ -118,18 +117,22 @@ def test_plan_windows_partitions_rows_greedily():
         deg[rng.integers(0, n, 3)] = 500  # a few rows longer than small budgets
         rp = np.concatenate([[0], np.cumsum(deg)])
         budget = int(rng.integers(1, 5 * 800))
-        W, b = _plan(rp, budget)
+        eb = 4 if trial % 2 else 5  # packed entries, or label + bin arrays
+        W, b = _plan(rp, budget, eb)
         assert W >= 1 and b[0] == 0 and b[-1] == n and np.all(np.diff(b) > 0)
         for k in range(W):
             rows = b[k + 1] - b[k]
-            size = 5 * (rp[b[k + 1]] - rp[b[k]])
+            size = eb * (rp[b[k + 1]] - rp[b[k]])
             assert size <= budget or rows == 1, (trial, k)
             if b[k + 1] < n:  # greedy: one more row would not fit
-                assert 5 * (rp[b[k + 1] + 1] - rp[b[k]]) > budget
+                assert eb * (rp[b[k + 1] + 1] - rp[b[k]]) > budget
     W, b = _plan(np.zeros(1, np.int64), 100)
     assert W == 1 and list(b) == [0, 0]
-    assert L.gtc_plan_windows(None, 3, 10, None) == gtc.GTC_E_INVALID
+    assert L.gtc_plan_windows(None, 3, 10, 5, None) == gtc.GTC_E_INVALID
     bad = np.array([0, 5, 3], np.int64)
     out = np.zeros(4, np.int64)
-    assert L.gtc_plan_windows(bad.ctypes.data_as(C.c_void_p), 2, 10,
+    assert L.gtc_plan_windows(bad.ctypes.data_as(C.c_void_p), 2, 10, 5,
+                              out.ctypes.data_as(C.c_void_p)) == gtc.GTC_E_INVALID
+    good = np.array([0, 5, 7], np.int64)
+    assert L.gtc_plan_windows(good.ctypes.data_as(C.c_void_p), 2, 10, 0,
                               out.ctypes.data_as(C.c_void_p)) == gtc.GTC_E_INVALID

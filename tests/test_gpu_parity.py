@@ -44,6 +44,18 @@ def test_graph_matches_oracle(gpu_available, kind, seed, n, r, nb):
     np.testing.assert_array_equal(got, want)
 
 
+def test_graph_split_layout_exports_the_same_edges(gpu_available, monkeypatch):
+    # a label array plus a bin array (the layout of graphs above 2^24 points) holds the same graph
+    xyz = clustered(5, 8000, 40, 3000)
+    edges = linear_edges_sq(9_000, 6)
+    want = edge_set_from_oracle(oracle.Graph(xyz, edges))
+    monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
+    g = gtc.Graph(to_gpu(xyz), edges)
+    got = edge_set_from_gpu(g)
+    g.close()
+    np.testing.assert_array_equal(got, want)
+
+
 # ------------------------------------------------------------------ 3pCF
 
 CASES_3 = [
@@ -70,12 +82,16 @@ def test_3pcf_matches_oracle(gpu_available, kind, seed, n, r, nb, weighted):
         np.testing.assert_array_equal(ws, ows)
 
 
+@pytest.mark.parametrize("layout", ["packed", "split"])
 @pytest.mark.parametrize("mode", ["flat", "banded"])
 @pytest.mark.parametrize("kind,seed,n,r,nb,weighted", CASES_3[1:4])
-def test_3pcf_walk_modes(gpu_available, monkeypatch, mode, kind, seed, n, r, nb, weighted):
-    # the two spoke walks (one map over the hub domain / one map per key run) agree with the oracle
-    say("3pcf mode", mode, kind, seed, n, r, nb, weighted)
+def test_3pcf_walk_modes(gpu_available, monkeypatch, layout, mode, kind, seed, n, r, nb, weighted):
+    # the two spoke walks (one map over the hub domain / one map per key run), on both CSR layouts
+    # (label and bin in one word / a label array and a bin array), agree with the oracle
+    say("3pcf mode", mode, layout, kind, seed, n, r, nb, weighted)
     monkeypatch.setenv("GTC_TRIPLET_MODE", mode)
+    if layout == "split":
+        monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
     xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 60, 2500)
     edges = linear_edges_sq(r, nb)
     w = 0.5 + rng_for(seed + 1000).random(n) if weighted else None
@@ -195,9 +211,12 @@ CASES_4 = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["packed", "split"])
 @pytest.mark.parametrize("kind,seed,n,r,nb", CASES_4)
-def test_4pcf_matches_oracle(gpu_available, kind, seed, n, r, nb):
-    say("4pcf", kind, seed, n, r, nb)
+def test_4pcf_matches_oracle(gpu_available, monkeypatch, layout, kind, seed, n, r, nb):
+    say("4pcf", layout, kind, seed, n, r, nb)
+    if layout == "split":
+        monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
     xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 50, 2000)
     edges = linear_edges_sq(r, nb)
     e, o, st = hip_4pcf(xyz, edges)

@@ -24,9 +24,13 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["packed", "split"])
 @pytest.mark.parametrize("host_csr", [False, True])
 @pytest.mark.parametrize("kind,seed,n,r,nb,weighted", CASES)
-def test_tiled_equals_resident_and_oracle(gpu_available, kind, seed, n, r, nb, weighted, host_csr):
+def test_tiled_equals_resident_and_oracle(gpu_available, monkeypatch, kind, seed, n, r, nb,
+                                          weighted, host_csr, layout):
+    if layout == "split":
+        monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
     xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 60, 2500)
     edges = linear_edges_sq(r, nb)
     w = 0.5 + rng_for(seed + 7).random(n) if weighted else None
