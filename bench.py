@@ -73,7 +73,12 @@ def main():
     ap.add_argument("--tile-bytes", type=int, default=0,
                     help="hub-window budget in CSR bytes (0: one resident window)")
     ap.add_argument("--host-csr", action="store_true",
-                    help="out-of-core: keep the CSR in pinned host memory, stream windows")
+                    help="out-of-core: keep the CSR in pinned host memory, stream windows "
+                         "(same as --csr-mode host)")
+    ap.add_argument("--csr-mode", choices=["device", "host", "rebuild"], default=None,
+                    help="where the CSR is kept: device memory, pinned host memory (windows "
+                         "uploaded per tile) or nowhere (windows emitted again per tile); the "
+                         "last two need --tile-bytes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (HBM counter calibration)")
     args = ap.parse_args()
@@ -101,12 +106,13 @@ def main():
     edges = cfg.edges_sq()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    csr_mode = args.csr_mode or ("host" if args.host_csr else "device")
     xyz = torch.from_numpy(xyz_np).to(dev)
     w = None if w_np is None else torch.from_numpy(w_np).to(dev)
     torch.cuda.synchronize()
 
     def step():
-        g = gtc.Graph(xyz, edges, tile_bytes=args.tile_bytes, host_csr=args.host_csr)
+        g = gtc.Graph(xyz, edges, tile_bytes=args.tile_bytes, csr_mode=csr_mode)
         c, ws, st = g.count_3pcf(w)
         gst = g.stats()
         g.close()
@@ -167,7 +173,7 @@ def main():
                    "r_max": cfg.r, "nbins": cfg.nbins, "weighted": cfg.weighted,
                    "mean_degree_target": cfg.target_degree, "edges": st["edges"],
                    "triangles": T, "merge_walks": walks[0], "tile_bytes": args.tile_bytes,
-                   "host_csr": args.host_csr, "windows": st["windows"], "tiles": st["tiles"]},
+                   "csr_mode": csr_mode, "windows": st["windows"], "tiles": st["tiles"]},
         "merge_walks_per_s": walks[0] * args.steps / elapsed,
         "kernel_triplets_per_s": T / (k_avg * 1e-3),
         "build_ms": sum(bms) / len(bms),

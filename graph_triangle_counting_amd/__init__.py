@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(PKG, "libgtc.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "gtc.h")
 
 GTC_OK, GTC_E_INVALID, GTC_E_OOM, GTC_E_HIP, GTC_E_OVERFLOW, GTC_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+# where the CSR is kept (gtc_options.csr_mode)
+CSR_MODES = {"device": 0, "host": 1, "rebuild": 2}
 
 
 class GtcError(RuntimeError):
@@ -26,7 +28,7 @@ class GtcError(RuntimeError):
 
 
 class Options(C.Structure):
-    _fields_ = [("tile_bytes", C.c_int64), ("host_csr", C.c_int32), ("drop_coords", C.c_int32)]
+    _fields_ = [("tile_bytes", C.c_int64), ("csr_mode", C.c_int32), ("drop_coords", C.c_int32)]
 
 
 class Stats(C.Structure):
@@ -109,7 +111,9 @@ class Graph:
     """Neighbour graph on the current GPU (owned by libgtc; freed by close() or on deletion)."""
 
     def __init__(self, xyz, edges_sq, tile_bytes: int = 0, host_csr: bool = False,
-                 drop_coords: bool = False, stream=None):
+                 drop_coords: bool = False, stream=None, csr_mode: str | None = None):
+        """csr_mode: "device" (default), "host" (pinned host CSR; host_csr=True is the same) or
+        "rebuild" (no stored CSR, windows emitted again per tile); the last two need tile_bytes."""
         import torch
         if not (isinstance(xyz, torch.Tensor) and xyz.is_cuda and xyz.dtype == torch.int32
                 and xyz.dim() == 2 and xyz.shape[1] == 3):
@@ -119,7 +123,8 @@ class Graph:
         self.nbins = int(e.size - 1)
         self.edges = e
         self.n = int(xyz.shape[0])
-        opt = Options(int(tile_bytes), int(bool(host_csr)), int(bool(drop_coords)))
+        mode = CSR_MODES[csr_mode] if csr_mode is not None else (1 if host_csr else 0)
+        opt = Options(int(tile_bytes), mode, int(bool(drop_coords)))
         h = C.c_void_p()
         self._stream = stream
         _check(lib().gtc_build_graph(_dptr(self._xyz) if self.n else None, self.n,

@@ -141,8 +141,18 @@ int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, 
     }
     gtc_options o{};
     if (opt) o = *opt;
-    if (o.tile_bytes < 0 || (o.host_csr && o.tile_bytes <= 0)) {
-        set_error("gtc_build_graph: tile_bytes must be >= 0, and > 0 when host_csr is set");
+    if (o.csr_mode < GTC_CSR_DEVICE || o.csr_mode > GTC_CSR_REBUILD) {
+        set_error("gtc_build_graph: csr_mode %d is not one of 0 (device), 1 (host), 2 (rebuild)",
+                  o.csr_mode);
+        return GTC_E_INVALID;
+    }
+    if (o.tile_bytes < 0 || (o.csr_mode != GTC_CSR_DEVICE && o.tile_bytes <= 0)) {
+        set_error("gtc_build_graph: tile_bytes must be >= 0, and > 0 for an out-of-core csr_mode");
+        return GTC_E_INVALID;
+    }
+    if (o.csr_mode == GTC_CSR_REBUILD && o.drop_coords) {
+        set_error("gtc_build_graph: csr_mode GTC_CSR_REBUILD re-emits windows from the coordinates, "
+                  "which drop_coords would drop");
         return GTC_E_INVALID;
     }
     DeviceGuard dg(-1);
@@ -170,7 +180,8 @@ int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, 
     G->n = n;
     G->nb = nbins;
     G->tile_bytes = o.tile_bytes;
-    G->host_csr = o.host_csr != 0;
+    G->host_csr = o.csr_mode == GTC_CSR_HOST;
+    G->rebuild = o.csr_mode == GTC_CSR_REBUILD;
     for (int b = 0; b <= nbins; ++b) G->edges[b] = h_edges_sq[b];
     int rc = build_graph_device(G, d_xyz, G->stream);
     if (rc == GTC_OK && o.drop_coords) {
@@ -227,9 +238,9 @@ int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_sta
         set_error("gtc_count_4pcf_parity: the graph was built with drop_coords");
         return GTC_E_INVALID;
     }
-    if (g->host_csr) {
-        set_error("gtc_count_4pcf_parity: out-of-core (host_csr) graphs are not supported by the "
-                  "4-clique kernel, which needs every spoke row of a hub at once");
+    if (g->host_csr || g->rebuild) {
+        set_error("gtc_count_4pcf_parity: out-of-core (csr_mode 1 or 2) graphs are not supported "
+                  "by the 4-clique kernel, which needs every spoke row of a hub at once");
         return GTC_E_UNSUPPORTED;
     }
     DeviceGuard dg(g->device);
@@ -266,6 +277,32 @@ int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h
     if (g->host_csr) {  // out-of-core graph: the CSR is already in host memory
         if (w_dst && g->E) std::memcpy(w_dst, g->h_col, sizeof(int32_t) * g->E);
         if (!g->packed && h_bin && g->E) std::memcpy(h_bin, g->h_bin, g->E);
+    } else if (g->rebuild) {  // no stored CSR: emit each window again and copy it out
+        if ((w_dst || (!g->packed && h_bin)) && g->E) {
+            int32_t *wc = nullptr;
+            uint8_t *wb = nullptr;
+            void *blk = nullptr;
+            GTC_TRY(carve_alloc(&blk, s, [&](Carver &c) {
+                c.take(&wc, g->max_window_edges);
+                if (!g->packed) c.take(&wb, g->max_window_edges);
+            }));
+            int rc = GTC_OK;
+            for (int64_t w = 0; w + 1 < (int64_t)g->win.size() && rc == GTC_OK; ++w) {
+                const int64_t e0 = g->h_row_ptr[g->win[w]];
+                const int64_t ne = g->h_row_ptr[g->win[w + 1]] - e0;
+                if (ne <= 0) continue;
+                rc = emit_window(g, w, wc, wb, s);
+                hipError_t e = hipSuccess;
+                if (rc == GTC_OK && w_dst)
+                    e = hipMemcpyAsync(w_dst + e0, wc, sizeof(int32_t) * ne, hipMemcpyDeviceToHost, s);
+                if (rc == GTC_OK && e == hipSuccess && !g->packed && h_bin)
+                    e = hipMemcpyAsync(h_bin + e0, wb, ne, hipMemcpyDeviceToHost, s);
+                if (rc == GTC_OK && e == hipSuccess) e = hipStreamSynchronize(s);
+                if (e != hipSuccess) rc = hip_fail(e, "window export", __FILE__, __LINE__);
+            }
+            dev_free(blk, s);
+            if (rc) return rc;
+        }
     } else {
         if (w_dst && g->E)
             GTC_HIP_CHECK(hipMemcpyAsync(w_dst, g->col, sizeof(int32_t) * g->E, hipMemcpyDeviceToHost, s));

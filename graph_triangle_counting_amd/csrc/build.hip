@@ -62,6 +62,7 @@ struct PairArgs {
     int32_t *col;
     uint8_t *bin;            // null: packed entries (bin in the top byte of col)
     uint32_t *slot_off;      // emit pass: [n][16] start of each forward cell slot in the row
+                             // (null: not written)
 };
 
 // Exact squared distance as a double: coordinates differ by < 2^20, squares are < 2^40 and the
@@ -124,7 +125,7 @@ __global__ void __launch_bounds__(256) k_pairs(PairArgs a) {
     }
     if (!EMIT) {
         a.deg[i] = cnt;
-    } else {
+    } else if (a.slot_off) {  // (null when a window is emitted again for counting)
         so[14] = (uint32_t)(w - w0);
         so[15] = 0;
         uint4 *dst = reinterpret_cast<uint4 *>(a.slot_off + (int64_t)i * 16);
@@ -238,55 +239,71 @@ __global__ void __launch_bounds__(256)
     }
 }
 
-// Heavy-first hub order: hubs with a possible triangle (d+ >= 2, work > 0) bucketed by
-// floor(log2(work)), buckets in decreasing order.  Block-aggregated counting sort.
+// Hub lists: hubs with a possible triangle (d+ >= 2, work > 0), grouped by hub window and, within
+// a window, heaviest first by class (floor(log2(work)), hub_class).  A counting sort on the key
+// window * kHubClasses + class, aggregated per block in LDS when the keys fit there.
+constexpr int kLdsKeys = 4096;
+
+__device__ __forceinline__ int hub_key(int64_t i, const int64_t *__restrict__ row_ptr,
+                                       const int64_t *__restrict__ work,
+                                       const int64_t *__restrict__ win, int32_t nwin) {
+    const int c = hub_class(row_ptr[i + 1] - row_ptr[i], work[i]);
+    if (c < 0) return -1;
+    int lo = 0, hi = nwin;  // window k holds labels [win[k], win[k+1])
+    while (hi - lo > 1) {
+        const int md = (lo + hi) >> 1;
+        if (win[md] <= i) lo = md; else hi = md;
+    }
+    return lo * kHubClasses + c;
+}
+
 __global__ void __launch_bounds__(256)
     k_bucket_count(int32_t n, const int64_t *__restrict__ row_ptr, const int64_t *__restrict__ work,
-                   unsigned int *__restrict__ bucket_count) {
-    __shared__ unsigned int loc[kHubClasses];
-    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x) loc[t] = 0;
+                   const int64_t *__restrict__ win, int32_t nwin, int32_t nkeys,
+                   int32_t *__restrict__ count) {
+    extern __shared__ int32_t loc[];
+    const bool lds = nkeys <= kLdsKeys;
+    if (lds)
+        for (int t = threadIdx.x; t < nkeys; t += blockDim.x) loc[t] = 0;
     __syncthreads();
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i < n) {
-        const int b = hub_class(row_ptr[i + 1] - row_ptr[i], work[i]);
-        if (b >= 0) atomicAdd(&loc[b], 1u);
+        const int b = hub_key(i, row_ptr, work, win, nwin);
+        if (b >= 0) atomicAdd(lds ? &loc[b] : &count[b], 1);
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x)
-        if (loc[t]) atomicAdd(&bucket_count[t], loc[t]);
-}
-
-__global__ void k_bucket_offsets(unsigned int *bucket_count /* in: counts, out: fill cursor */) {
-    if (threadIdx.x == 0) {
-        unsigned int acc = 0;
-        for (int t = 0; t < kHubClasses; ++t) {
-            const unsigned int c = bucket_count[t];
-            bucket_count[t] = acc;
-            acc += c;
-        }
-    }
+    if (lds)
+        for (int t = threadIdx.x; t < nkeys; t += blockDim.x)
+            if (loc[t]) atomicAdd(&count[t], loc[t]);
 }
 
 __global__ void __launch_bounds__(256)
     k_bucket_scatter(int32_t n, const int64_t *__restrict__ row_ptr,
-                     const int64_t *__restrict__ work, unsigned int *__restrict__ cursor,
+                     const int64_t *__restrict__ work, const int64_t *__restrict__ win,
+                     int32_t nwin, int32_t nkeys, int32_t *__restrict__ cursor,
                      int32_t *__restrict__ hubs) {
-    __shared__ unsigned int loc[kHubClasses];
-    __shared__ unsigned int base[kHubClasses];
-    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x) loc[t] = 0;
+    extern __shared__ int32_t sh[];
+    const bool lds = nkeys <= kLdsKeys;
+    int32_t *loc = sh, *base = sh + (lds ? nkeys : 0);
+    if (lds)
+        for (int t = threadIdx.x; t < nkeys; t += blockDim.x) loc[t] = 0;
     __syncthreads();
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     int b = -1;
-    unsigned int r = 0;
+    int32_t r = 0;
     if (i < n) {
-        b = hub_class(row_ptr[i + 1] - row_ptr[i], work[i]);
-        if (b >= 0) r = atomicAdd(&loc[b], 1u);
+        b = hub_key(i, row_ptr, work, win, nwin);
+        if (b >= 0 && lds) r = atomicAdd(&loc[b], 1);
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < kHubClasses; t += blockDim.x)
-        base[t] = loc[t] ? atomicAdd(&cursor[t], loc[t]) : 0u;
-    __syncthreads();
-    if (b >= 0) hubs[base[b] + r] = (int32_t)i;
+    if (lds) {
+        for (int t = threadIdx.x; t < nkeys; t += blockDim.x)
+            base[t] = loc[t] ? atomicAdd(&cursor[t], loc[t]) : 0;
+        __syncthreads();
+        if (b >= 0) hubs[base[b] + r] = (int32_t)i;
+    } else if (b >= 0) {
+        hubs[atomicAdd(&cursor[b], 1)] = (int32_t)i;
+    }
 }
 
 __global__ void __launch_bounds__(256)
@@ -374,7 +391,6 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     // build scratch: keys, slots, cell counts, error flag, stats, class counts, scan partials
     int32_t *key = nullptr, *slot = nullptr, *ccount = nullptr, *err = nullptr;
     StatsOut *d_stats = nullptr;
-    unsigned int *bucket = nullptr;
     int64_t *scan_ws = nullptr;
     void *scratch = nullptr;
     int rc = GTC_OK;
@@ -404,13 +420,11 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         c.take(&ccount, gr.ncell);
         c.take(&err, 1);
         c.take(&d_stats, 1);
-        c.take(&bucket, kHubClasses);
         c.take(&scan_ws, scan_ws_bytes / sizeof(int64_t));
     }));
     STEP(fill_u32(reinterpret_cast<uint32_t *>(ccount), gr.ncell, 0u, s));
     STEP(fill_u32(reinterpret_cast<uint32_t *>(err), 1, 0u, s));
     STEP(fill_u64(reinterpret_cast<uint64_t *>(d_stats), sizeof(StatsOut) / 8, 0ull, s));
-    STEP(fill_u32(bucket, kHubClasses, 0u, s));
 
     if (n > 0) {
         hipLaunchKernelGGL(k_cellkey, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, gr, key,
@@ -468,17 +482,41 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     }
     const int64_t W = (int64_t)G->win.size() - 1;
     unsigned long long *win_last = nullptr;
-    int32_t *st_col = nullptr;
-    uint8_t *st_bin = nullptr;
+    // out-of-core staging: two buffers, so that one window's download to the pinned CSR (on a
+    // copy stream) overlaps the next window's emit
+    int32_t *st_col[2] = {nullptr, nullptr};
+    uint8_t *st_bin[2] = {nullptr, nullptr};
+    hipStream_t cs = nullptr;
+    hipEvent_t emitted[2] = {nullptr, nullptr}, copied[2] = {nullptr, nullptr};
+    bool copy_pending[2] = {false, false};
+    const int64_t nkeys = W * kHubClasses;  // hub-list keys: window * classes + class
+    int32_t *key_count = nullptr, *key_start = nullptr;
+    int64_t *d_win = nullptr, *key_scan_ws = nullptr;
     void *scratch2 = nullptr;
-    auto cleanup2 = [&]() { dev_free(scratch2, s); };
+    auto cleanup2 = [&]() {
+        if (cs) {
+            (void)hipStreamSynchronize(cs);
+            (void)hipStreamDestroy(cs);
+        }
+        for (int b = 0; b < 2; ++b) {
+            if (emitted[b]) (void)hipEventDestroy(emitted[b]);
+            if (copied[b]) (void)hipEventDestroy(copied[b]);
+        }
+        dev_free(scratch2, s);
+    };
 #define STEP2(expr) do { rc = (expr); if (rc) { cleanup2(); cleanup(); return rc; } } while (0)
 #define STEP2_HIP(call) do { hipError_t e_ = (call); if (e_ != hipSuccess) { rc = hip_fail(e_, #call, __FILE__, __LINE__); cleanup2(); cleanup(); return rc; } } while (0)
     STEP2(carve_alloc(&scratch2, s, [&](Carver &c) {
         c.take(&win_last, W);
-        if (G->host_csr) {  // staging of one window's rows on their way to the pinned CSR
-            c.take(&st_col, G->max_window_edges);
-            if (!G->packed) c.take(&st_bin, G->max_window_edges);
+        c.take(&key_count, nkeys);
+        c.take(&key_start, nkeys + 1);
+        c.take(&d_win, W + 1);
+        c.take(&key_scan_ws, scan_workspace_bytes(nkeys) / sizeof(int64_t));
+        if (G->windowed()) {  // staging of a window's rows (on their way to the pinned CSR)
+            for (int b = 0; b < 2; ++b) {
+                c.take(&st_col[b], G->max_window_edges);
+                if (!G->packed) c.take(&st_bin[b], G->max_window_edges);
+            }
         }
     }));
     STEP2(fill_u64(reinterpret_cast<uint64_t *>(win_last), W, 0ull, s));
@@ -490,7 +528,12 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         if (!G->packed)
             STEP2_HIP(hipHostMalloc(reinterpret_cast<void **>(&G->h_bin),
                                     std::max<int64_t>(G->E, 1), hipHostMallocDefault));
-    } else {
+        STEP2_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+        for (int b = 0; b < 2; ++b) {
+            STEP2_HIP(hipEventCreateWithFlags(&emitted[b], hipEventDisableTiming));
+            STEP2_HIP(hipEventCreateWithFlags(&copied[b], hipEventDisableTiming));
+        }
+    } else if (!G->rebuild) {  // (rebuild: the emit pass only feeds the statistics)
         STEP2(carve_alloc(&G->arena_csr, s, [&](Carver &c) {
             c.take(&G->col, G->E);
             if (!G->packed) c.take(&G->bin, G->E);
@@ -501,12 +544,15 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     for (int64_t k = 0; k < W && n > 0; ++k) {
         const int64_t lo = G->win[k], hi = G->win[k + 1];
         if (hi <= lo) continue;
-        const int64_t e_lo = G->host_csr ? G->h_row_ptr[lo] : 0;
+        const int64_t e_lo = G->windowed() ? G->h_row_ptr[lo] : 0;
+        const int sb = (int)(k & 1);  // staging buffer of this window
+        if (G->host_csr && copy_pending[sb])  // its previous window has been downloaded
+            STEP2_HIP(hipStreamWaitEvent(s, copied[sb], 0));
         pa.h_lo = (int32_t)lo;
         pa.h_hi = (int32_t)hi;
         pa.col_base = e_lo;
-        pa.col = G->host_csr ? st_col : G->col;
-        pa.bin = G->host_csr ? st_bin : G->bin;
+        pa.col = G->windowed() ? st_col[sb] : G->col;
+        pa.bin = G->windowed() ? st_bin[sb] : G->bin;
         hipLaunchKernelGGL(k_pairs<true>, dim3(grid_for(hi - lo, 256)), dim3(256), 0, s, pa);
         STEP2_HIP(hipGetLastError());
         const int64_t dsb = std::min<int64_t>(((hi - lo) * 16 + 255) / 256, 2048);
@@ -518,10 +564,15 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         if (G->host_csr) {
             const int64_t ne = G->h_row_ptr[hi] - e_lo;
             if (ne > 0) {
-                STEP2_HIP(hipMemcpyAsync(G->h_col + e_lo, st_col, sizeof(int32_t) * ne,
-                                         hipMemcpyDeviceToHost, s));
+                STEP2_HIP(hipEventRecord(emitted[sb], s));
+                STEP2_HIP(hipStreamWaitEvent(cs, emitted[sb], 0));
+                STEP2_HIP(hipMemcpyAsync(G->h_col + e_lo, st_col[sb], sizeof(int32_t) * ne,
+                                         hipMemcpyDeviceToHost, cs));
                 if (!G->packed)
-                    STEP2_HIP(hipMemcpyAsync(G->h_bin + e_lo, st_bin, ne, hipMemcpyDeviceToHost, s));
+                    STEP2_HIP(hipMemcpyAsync(G->h_bin + e_lo, st_bin[sb], ne,
+                                             hipMemcpyDeviceToHost, cs));
+                STEP2_HIP(hipEventRecord(copied[sb], cs));
+                copy_pending[sb] = true;
             }
         }
     }
@@ -545,40 +596,71 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         G->win_smax[k] = (int32_t)std::min<int64_t>(std::max<int64_t>(t, k), W - 1);
     }
 
-    if (n > 0 && G->n_hubs > 0) {
-        hipLaunchKernelGGL(k_bucket_count, dim3(grid_for(n, 256)), dim3(256), 0, s, (int32_t)n,
-                           G->row_ptr, G->work, bucket);
-        hipLaunchKernelGGL(k_bucket_offsets, dim3(1), dim3(64), 0, s, bucket);
-        hipLaunchKernelGGL(k_bucket_scatter, dim3(grid_for(n, 256)), dim3(256), 0, s, (int32_t)n,
-                           G->row_ptr, G->work, bucket, G->hubs);
-        STEP2_HIP(hipGetLastError());
-    }
-    // per-window hub lists: a stable partition of the heavy-first list by window
+    // hub lists by (window, class): window k's hubs are hubs[win_hubs[k], win_hubs[k+1])
     G->win_hubs.assign(W + 1, 0);
     G->win_hubs[W] = G->n_hubs;
-    if (W > 1 && G->n_hubs > 0) {
-        std::vector<int32_t> h(G->n_hubs), out(G->n_hubs);
-        STEP2_HIP(hipMemcpyAsync(h.data(), G->hubs, sizeof(int32_t) * G->n_hubs,
-                                 hipMemcpyDeviceToHost, s));
-        STEP2_HIP(hipStreamSynchronize(s));
-        auto window_of = [&](int64_t lab) {
-            return (int64_t)(std::upper_bound(G->win.begin(), G->win.end(), lab) - G->win.begin() - 1);
-        };
-        std::vector<int64_t> cnt(W + 1, 0);
-        for (int32_t v : h) ++cnt[window_of(v) + 1];
-        for (int64_t k = 0; k < W; ++k) cnt[k + 1] += cnt[k];
-        for (int64_t k = 0; k <= W; ++k) G->win_hubs[k] = cnt[k];
-        for (int32_t v : h) out[cnt[window_of(v)]++] = v;
-        STEP2_HIP(hipMemcpyAsync(G->hubs, out.data(), sizeof(int32_t) * G->n_hubs,
+    if (n > 0 && G->n_hubs > 0) {
+        if (nkeys > INT32_MAX / 2) {
+            set_error("too many hub windows (%lld)", (long long)W);
+            cleanup2();
+            cleanup();
+            return GTC_E_UNSUPPORTED;
+        }
+        STEP2_HIP(hipMemcpyAsync(d_win, G->win.data(), sizeof(int64_t) * (W + 1),
                                  hipMemcpyHostToDevice, s));
+        STEP2(fill_u32(reinterpret_cast<uint32_t *>(key_count), nkeys, 0u, s));
+        const size_t lds_keys = nkeys <= kLdsKeys ? sizeof(int32_t) * (size_t)nkeys : 0;
+        hipLaunchKernelGGL(k_bucket_count, dim3(grid_for(n, 256)), dim3(256), lds_keys, s,
+                           (int32_t)n, G->row_ptr, G->work, d_win, (int32_t)W, (int32_t)nkeys,
+                           key_count);
+        STEP2_HIP(hipGetLastError());
+        STEP2(exclusive_scan_i32_to_i32(key_count, key_start, nkeys, key_scan_ws, s));
+        std::vector<int32_t> h_start(nkeys + 1);
+        STEP2_HIP(hipMemcpyAsync(h_start.data(), key_start, sizeof(int32_t) * (nkeys + 1),
+                                 hipMemcpyDeviceToHost, s));
+        hipLaunchKernelGGL(k_bucket_scatter, dim3(grid_for(n, 256)), dim3(256), 2 * lds_keys, s,
+                           (int32_t)n, G->row_ptr, G->work, d_win, (int32_t)W, (int32_t)nkeys,
+                           key_start, G->hubs);
+        STEP2_HIP(hipGetLastError());
         STEP2_HIP(hipStreamSynchronize(s));
+        for (int64_t k = 0; k < W; ++k) G->win_hubs[k] = h_start[k * kHubClasses];
+        if (h_start[nkeys] != G->n_hubs) {
+            set_error("hub list: %d hubs bucketed, %lld expected", h_start[nkeys],
+                      (long long)G->n_hubs);
+            cleanup2();
+            cleanup();
+            return GTC_E_HIP;
+        }
     }
+    if (cs) STEP2_HIP(hipStreamSynchronize(cs));  // the pinned CSR is complete
     cleanup2();
 #undef STEP2
 #undef STEP2_HIP
     cleanup();
 #undef STEP
 #undef STEP_HIP
+    return GTC_OK;
+}
+
+int emit_window(const gtc_graph_s *G, int64_t w, int32_t *col, uint8_t *bin, hipStream_t s) {
+    const int64_t lo = G->win[w], hi = G->win[w + 1];
+    if (hi <= lo) return GTC_OK;
+    PairArgs pa{};
+    pa.xyz_s = G->xyz_s;
+    pa.cell_start = G->cell_start;
+    pa.edges = G->d_edges;
+    pa.nb = G->nb;
+    pa.n = (int32_t)G->n;
+    pa.gr = G->grid;
+    pa.h_lo = (int32_t)lo;
+    pa.h_hi = (int32_t)hi;
+    pa.row_ptr = G->row_ptr;
+    pa.col_base = G->h_row_ptr[lo];
+    pa.col = col;
+    pa.bin = G->packed ? nullptr : bin;
+    pa.slot_off = nullptr;
+    hipLaunchKernelGGL(k_pairs<true>, dim3(grid_for(hi - lo, 256)), dim3(256), 0, s, pa);
+    GTC_HIP_CHECK(hipGetLastError());
     return GTC_OK;
 }
 

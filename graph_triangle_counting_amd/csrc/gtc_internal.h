@@ -312,7 +312,16 @@ struct gtc_graph_s {
     std::vector<int64_t> h_row_ptr; // host copy of row_ptr (tiled graphs)
     int64_t max_window_edges = 0;
     // out-of-core: the CSR in pinned host memory, only windows go to the device
-    bool host_csr = false;
+    bool host_csr = false;   // the CSR in pinned host memory (h_col, h_bin)
+    bool rebuild = false;    // no stored CSR: windows are emitted again when a tile needs them
+    bool windowed() const { return host_csr || rebuild; }
     int32_t *h_col = nullptr;
     uint8_t *h_bin = nullptr;
 };
+
+namespace gtc {
+// Emit the CSR rows of hub window w (labels win[w]..win[w+1]) into col/bin (bin null for packed
+// entries), entry e of the graph at col[e - h_row_ptr[win[w]]]: the pair search of the build,
+// run again.  Needs the sorted coordinates.
+int emit_window(const gtc_graph_s *G, int64_t w, int32_t *col, uint8_t *bin, hipStream_t s);
+}  // namespace gtc

@@ -614,8 +614,9 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     unsigned long long *limbs = nullptr, *d_maxabs = nullptr;
     int32_t *d_bad = nullptr;
     unsigned int *queue = nullptr, *qcount = nullptr;
-    int32_t *wcol[2] = {nullptr, nullptr};
-    uint8_t *wbin[2] = {nullptr, nullptr};
+    constexpr int kSlots = 3;  // out-of-core window buffers: a tile's two windows and the next one
+    int32_t *wcol[kSlots] = {};
+    uint8_t *wbin[kSlots] = {};
     void *scratch = nullptr;
     int rc = GTC_OK;
     int scale = 0;
@@ -632,8 +633,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         }
         c.take(&queue, (size_t)kHubClasses * kQueueStride);
         c.take(&qcount, kHubClasses);
-        if (G->host_csr)
-            for (int b2 = 0; b2 < 2; ++b2) {
+        if (G->windowed())
+            for (int b2 = 0; b2 < kSlots; ++b2) {
                 c.take(&wcol[b2], G->max_window_edges);
                 if (!G->packed) c.take(&wbin[b2], G->max_window_edges);
             }
@@ -694,9 +695,20 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     float kms = 0.f, h2d_ms = 0.f;
     TripletPlan used{};
     int64_t tiles_run = 0;
-    // window buffers of an out-of-core graph (in the scratch block): [0] hub window, [1] search
     std::vector<hipEvent_t> kev, cev;  // kernel and copy event pairs
+    // out-of-core: window uploads run on a copy stream; per window buffer, `ready` marks its upload
+    // done and `done` the last kernel that read it
+    hipStream_t cs = nullptr;
+    hipEvent_t slot_ready[kSlots] = {}, slot_done[kSlots] = {};
     auto cleanup_tiles = [&]() {
+        if (cs) {
+            (void)hipStreamSynchronize(cs);
+            (void)hipStreamDestroy(cs);
+        }
+        for (int k = 0; k < kSlots; ++k) {
+            if (slot_ready[k]) (void)hipEventDestroy(slot_ready[k]);
+            if (slot_done[k]) (void)hipEventDestroy(slot_done[k]);
+        }
         for (auto e : kev) (void)hipEventDestroy(e);
         for (auto e : cev) (void)hipEventDestroy(e);
         kev.clear();
@@ -733,46 +745,118 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         // (i, j) runs in the tile (window of i, window of j) only; a resident untiled graph is one
         // tile over all spokes.
         const int64_t nw = (int64_t)G->win.size() - 1;
-        const bool ooc = G->host_csr;
+        const bool ooc = G->windowed();
         const std::vector<int64_t> &hr = G->h_row_ptr;
-        auto load_window = [&](int64_t w, int b2) -> int {
+        // Out-of-core window buffers.  Each tile needs its hub window and its search window in a
+        // buffer; while a tile's kernel runs, the next tile's missing window is uploaded (pinned
+        // host CSR) or emitted again (no stored CSR) on a second stream, into a buffer no running
+        // or next tile needs (§III.5.3, double buffering).
+        int64_t slot_win[kSlots], slot_used[kSlots];
+        bool slot_read[kSlots] = {};
+        for (int k = 0; k < kSlots; ++k) slot_win[k] = slot_used[k] = -1;
+        // window stream: uploads overlap the counting on a stream of their own; re-emits run on
+        // the counting stream (a pair-search kernel beside the persistent enumeration kernel only
+        // takes compute units from it)
+        hipStream_t wst = s;
+        if (G->host_csr) {
+            TSTEP_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+            wst = cs;
+        }
+        if (ooc) {
+            for (int k = 0; k < kSlots; ++k) {
+                TSTEP_HIP(hipEventCreateWithFlags(&slot_ready[k], hipEventDisableTiming));
+                TSTEP_HIP(hipEventCreateWithFlags(&slot_done[k], hipEventDisableTiming));
+            }
+        }
+        // buffer holding window w, uploading it if needed; windows in keep[] are not evicted.
+        // Returns -1 when every buffer holds a kept window.
+        auto ensure = [&](int64_t w, const int64_t *keep, int nkeep, int64_t tick, int *slot) -> int {
+            *slot = -1;
+            for (int k = 0; k < kSlots; ++k)
+                if (slot_win[k] == w) {
+                    *slot = k;
+                    slot_used[k] = tick;
+                    return GTC_OK;
+                }
+            int victim = -1;
+            for (int k = 0; k < kSlots; ++k) {
+                bool kept = false;
+                for (int q = 0; q < nkeep; ++q) kept |= slot_win[k] == keep[q];
+                if (kept) continue;
+                if (victim < 0 || slot_used[k] < slot_used[victim]) victim = k;
+            }
+            if (victim < 0) return GTC_OK;
             const int64_t e0 = hr[G->win[w]], ne = hr[G->win[w + 1]] - e0;
-            if (ne <= 0) return GTC_OK;
+            if (slot_read[victim]) GTC_HIP_CHECK(hipStreamWaitEvent(wst, slot_done[victim], 0));
             GTC_TRY(event_pair(cev));
-            GTC_HIP_CHECK(hipEventRecord(cev[cev.size() - 2], s));
-            GTC_HIP_CHECK(hipMemcpyAsync(wcol[b2], G->h_col + e0, sizeof(int32_t) * ne,
-                                         hipMemcpyHostToDevice, s));
-            if (!G->packed)
-                GTC_HIP_CHECK(hipMemcpyAsync(wbin[b2], G->h_bin + e0, ne, hipMemcpyHostToDevice, s));
-            GTC_HIP_CHECK(hipEventRecord(cev.back(), s));
+            GTC_HIP_CHECK(hipEventRecord(cev[cev.size() - 2], wst));
+            if (ne > 0 && G->rebuild) {  // emit the window again from the coordinates
+                GTC_TRY(emit_window(G, w, wcol[victim], wbin[victim], wst));
+            } else if (ne > 0) {
+                GTC_HIP_CHECK(hipMemcpyAsync(wcol[victim], G->h_col + e0, sizeof(int32_t) * ne,
+                                             hipMemcpyHostToDevice, wst));
+                if (!G->packed)
+                    GTC_HIP_CHECK(hipMemcpyAsync(wbin[victim], G->h_bin + e0, ne,
+                                                 hipMemcpyHostToDevice, wst));
+            }
+            GTC_HIP_CHECK(hipEventRecord(cev.back(), wst));
+            GTC_HIP_CHECK(hipEventRecord(slot_ready[victim], wst));
+            slot_win[victim] = w;
+            slot_used[victim] = tick;
+            *slot = victim;
             return GTC_OK;
         };
-        for (int64_t h = 0; h < nw; ++h) {
+        std::vector<std::pair<int64_t, int64_t>> tiles;
+        for (int64_t h = 0; h < nw; ++h)
+            if (G->win_hubs[h + 1] > G->win_hubs[h])
+                for (int64_t sw = h; sw <= G->win_smax[h]; ++sw) tiles.emplace_back(h, sw);
+        for (size_t t = 0; t < tiles.size(); ++t) {
+            const int64_t h = tiles[t].first, sw = tiles[t].second;
             const int64_t nh = G->win_hubs[h + 1] - G->win_hubs[h];
-            if (nh == 0) continue;
-            if (ooc) TSTEP(load_window(h, 0));
-            a.hubs = G->hubs + G->win_hubs[h];
-            a.n_hubs = (int32_t)nh;
-            TSTEP(hub_class_counts(a.hubs, nh, G->row_ptr, G->work, qcount, s));
-            a.col_h = ooc ? wcol[0] : G->col;
-            a.bin_h = ooc ? wbin[0] : G->bin;
+            int kh = -1, ks = -1;
+            if (ooc) {
+                const int64_t keep[2] = {h, sw};
+                TSTEP(ensure(h, keep, 2, (int64_t)t, &kh));
+                TSTEP(ensure(sw, keep, 2, (int64_t)t, &ks));
+                TSTEP_HIP(hipStreamWaitEvent(s, slot_ready[kh], 0));
+                if (ks != kh) TSTEP_HIP(hipStreamWaitEvent(s, slot_ready[ks], 0));
+            }
+            if (t == 0 || tiles[t - 1].first != h) {
+                a.hubs = G->hubs + G->win_hubs[h];
+                a.n_hubs = (int32_t)nh;
+                TSTEP(hub_class_counts(a.hubs, nh, G->row_ptr, G->work, qcount, s));
+            }
+            a.col_h = ooc ? wcol[kh] : G->col;
+            a.bin_h = ooc ? wbin[kh] : G->bin;
             a.base_h = ooc ? hr[G->win[h]] : 0;
-            for (int64_t sw = h; sw <= G->win_smax[h]; ++sw) {
-                if (ooc && sw != h) TSTEP(load_window(sw, 1));
-                a.col_s = ooc ? (sw == h ? wcol[0] : wcol[1]) : G->col;
-                a.bin_s = ooc ? (sw == h ? wbin[0] : wbin[1]) : G->bin;
-                a.base_s = ooc ? hr[G->win[sw]] : 0;
-                a.s_lo = nw == 1 ? 0 : (int32_t)G->win[sw];
-                a.s_hi = nw == 1 ? (int32_t)G->n : (int32_t)G->win[sw + 1];
-                TSTEP(fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s));
-                TripletPlan tp = pl;
-                tp.blocks = (int)std::min<int64_t>(pl.blocks, (nh + pl.waves - 1) / pl.waves);
-                a.batch_cap = batch_cap(nh, (int64_t)tp.blocks * tp.waves);
-                TSTEP(event_pair(kev));
-                TSTEP_HIP(hipEventRecord(kev[kev.size() - 2], s));
-                TSTEP(launch_triplet(kfn, a, tp, s));
-                TSTEP_HIP(hipEventRecord(kev.back(), s));
-                ++tiles_run;
+            a.col_s = ooc ? wcol[ks] : G->col;
+            a.bin_s = ooc ? wbin[ks] : G->bin;
+            a.base_s = ooc ? hr[G->win[sw]] : 0;
+            a.s_lo = nw == 1 ? 0 : (int32_t)G->win[sw];
+            a.s_hi = nw == 1 ? (int32_t)G->n : (int32_t)G->win[sw + 1];
+            TSTEP(fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s));
+            TripletPlan tp = pl;
+            tp.blocks = (int)std::min<int64_t>(pl.blocks, (nh + pl.waves - 1) / pl.waves);
+            a.batch_cap = batch_cap(nh, (int64_t)tp.blocks * tp.waves);
+            TSTEP(event_pair(kev));
+            TSTEP_HIP(hipEventRecord(kev[kev.size() - 2], s));
+            TSTEP(launch_triplet(kfn, a, tp, s));
+            TSTEP_HIP(hipEventRecord(kev.back(), s));
+            ++tiles_run;
+            if (ooc) {
+                TSTEP_HIP(hipEventRecord(slot_done[kh], s));
+                slot_read[kh] = true;
+                if (ks != kh) {
+                    TSTEP_HIP(hipEventRecord(slot_done[ks], s));
+                    slot_read[ks] = true;
+                }
+                if (t + 1 < tiles.size()) {  // prefetch while this tile runs
+                    const int64_t h2 = tiles[t + 1].first, s2 = tiles[t + 1].second;
+                    const int64_t keep[4] = {h, sw, h2, s2};
+                    int k2;
+                    TSTEP(ensure(h2, keep, 4, (int64_t)t + 1, &k2));
+                    TSTEP(ensure(s2, keep, 4, (int64_t)t + 1, &k2));
+                }
             }
         }
     }
@@ -783,6 +867,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         TSTEP_HIP(hipMemcpyAsync(h_limbs.data(), limbs, sizeof(unsigned long long) * 4 * ncfg,
                                 hipMemcpyDeviceToHost, s));
     TSTEP_HIP(hipStreamSynchronize(s));
+    if (cs) TSTEP_HIP(hipStreamSynchronize(cs));
     for (size_t e = 0; e + 1 < kev.size(); e += 2) {
         float t = 0.f;
         TSTEP_HIP(hipEventElapsedTime(&t, kev[e], kev[e + 1]));

@@ -58,6 +58,11 @@ typedef enum {
 #define GTC_MAX_BINS_4PCF 16   /* parity 4pCF: nbins in [1, 16] */
 #define GTC_GRID_BITS 20       /* coordinates in [0, 2^20) */
 
+/* gtc_options.csr_mode */
+#define GTC_CSR_DEVICE 0
+#define GTC_CSR_HOST 1
+#define GTC_CSR_REBUILD 2
+
 /* Opaque neighbour graph, owned by the library (device CSR in internal labels, see
  * gtc_graph_export).  Free with gtc_graph_free. */
 typedef struct gtc_graph_s *gtc_graph;
@@ -69,9 +74,15 @@ typedef struct {
      * over (hub window, search window) tiles (§III.5.3).  The CSR takes 4 bytes per edge when
      * n <= 2^24 (label and bin packed in one word) and 5 bytes per edge otherwise. */
     int64_t tile_bytes;
-    /* nonzero (with tile_bytes > 0): the CSR lives in pinned host memory and only the active
-     * windows of a tile are copied to the device (out-of-core mode, §III.5.3). */
-    int32_t host_csr;
+    /* Where the CSR is kept (§III.5.3):
+     *   GTC_CSR_DEVICE  (0): in device memory.
+     *   GTC_CSR_HOST    (1): in pinned host memory; a tile's windows are copied to the device
+     *                        (on a copy stream, overlapped with the previous tile's counting).
+     *   GTC_CSR_REBUILD (2): nowhere; a tile's windows are emitted again on the device from the
+     *                        sorted coordinates (a window's pair search costs less than its copy
+     *                        over the host link).  Needs the coordinates (not dropped).
+     * Modes 1 and 2 need tile_bytes > 0, and hold only a few windows on the device. */
+    int32_t csr_mode;
     /* nonzero: drop the sorted coordinates after the build (gtc_count_4pcf_parity then fails
      * with GTC_E_INVALID).  Zero keeps them. */
     int32_t drop_coords;
@@ -99,7 +110,8 @@ typedef struct {
     double build_ms;           /* gtc_build_graph: whole call */
     double kernel_ms;          /* enumeration kernels only (sum over tiles) */
     double count_ms;           /* count call: whole call */
-    double h2d_ms;             /* out-of-core window copies */
+    double h2d_ms;             /* out-of-core: window copies (GTC_CSR_HOST) or window emits
+                                  (GTC_CSR_REBUILD), summed; they overlap the counting */
 } gtc_stats;
 
 /* Build the neighbour graph of n points (§II.1, Eq.(1)).
@@ -126,7 +138,7 @@ int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d
 
 /* Binned 4-clique counts split by parity (§II.2, §III.1.1, §III.2).  Needs nbins <=
  * GTC_MAX_BINS_4PCF and the coordinates (not dropped); GTC_E_UNSUPPORTED for out-of-core
- * (host_csr) graphs.
+ * (csr_mode 1 or 2) graphs.
  *   d_even     device uint64 [gtc_num_configs(4, nbins)]: every tetrahedron.
  *   d_odd      device int64  [same]: signed handedness sum. */
 int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,

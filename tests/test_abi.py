@@ -72,7 +72,13 @@ def test_build_rejects_bad_arguments_without_gpu():
         assert gtc.lib().gtc_last_error()
     rc, _ = _build(fake, 10, [0, 5, 10], 2, gtc.Options(-5, 0, 0))
     assert rc == gtc.GTC_E_INVALID
-    rc, _ = _build(fake, 10, [0, 5, 10], 2, gtc.Options(0, 1, 0))
+    for mode in (1, 2):  # out-of-core modes need a window budget
+        rc, _ = _build(fake, 10, [0, 5, 10], 2, gtc.Options(0, mode, 0))
+        assert rc == gtc.GTC_E_INVALID
+    for mode in (-1, 3):
+        rc, _ = _build(fake, 10, [0, 5, 10], 2, gtc.Options(100, mode, 0))
+        assert rc == gtc.GTC_E_INVALID
+    rc, _ = _build(fake, 10, [0, 5, 10], 2, gtc.Options(100, 2, 1))  # rebuild needs coordinates
     assert rc == gtc.GTC_E_INVALID
     L = gtc.lib()
     assert L.gtc_build_graph(fake, 10, None, 2, None, None, None) == gtc.GTC_E_INVALID
