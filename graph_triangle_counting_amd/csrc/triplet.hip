@@ -1,14 +1,15 @@
 // triplet.hip - binned triangle enumeration, the 3pCF numerator (GRAMSCI v2 §II.2, §III.1).
 //
-// One wavefront per hub i, hubs popped heaviest-first from a global queue (persistent
-// workgroups).  The pages' merge-walk intersects the hub tail {k in N(i): k > j} with N(j) for
-// every spoke j by two pointers over both sorted lists.  Here the hub side of that walk is held in
-// LDS as a direct-address map over the hub's stencil domain (the label ranges of its forward
-// cells, see hub_domain): map[k] = bin(i,k) + 1 for k in N+(i), 0 otherwise.  The spoke row
-// N+(j) is then streamed once, in order, by a group of G lanes; each element is one O(1) LDS
-// probe, and the walk stops at the first element past the hub's last neighbour, as the two-pointer
-// walk does when the hub list is exhausted.  Every element of N+(j) exceeds j, so a hit is exactly
-// a triangle i < j < k, counted once.
+// One wavefront per hub i (persistent workgroups); hubs are taken heaviest first, in batches, from
+// one counter per work class (HubQueue).  The pages' merge-walk intersects the hub tail
+// {k in N(i): k > j} with N(j) for every spoke j by two pointers over both sorted lists.  Here the
+// hub side of that walk is held in LDS as a direct-address map over the hub's stencil domain (the
+// label ranges of its forward cells, see hub_domain): map[k] = bin(i,k) + 1 for k in N+(i), 0
+// otherwise.  The spoke rows are streamed once, in order: 64 spokes at a time, their rows laid end
+// to end by a wave scan and read with 8 loads in flight per lane.  Each element is one O(1) LDS
+// probe, and elements past the hub's last neighbour miss, as the two-pointer walk stops when the
+// hub list is exhausted.  Every element of N+(j) exceeds j, so a hit is exactly a triangle
+// i < j < k, counted once.
 //
 // A hit ranks its sorted side-length bins (Fig. 8 key order) and adds 1 to a workgroup LDS
 // histogram (32-bit, exchanged out before it could overflow); the histogram is flushed with 64-bit
@@ -16,6 +17,10 @@
 // limbs (28 low bits, 30 offset high bits) to 64-bit LDS counters, flushed into 128-bit global
 // accumulators, so the sum is exact and independent of order (the pages accumulate fp atomics,
 // §III.5.2, and see order-dependent last digits, §IV.8).
+//
+// Graphs over several hub windows (§III.5.3) run as a loop of tiles (hub window, search window);
+// out-of-core windows are uploaded from pinned host memory on a copy stream, or emitted again by
+// the pair search, while the previous tile counts.
 #include <algorithm>
 #include <climits>
 #include <cmath>
