@@ -29,11 +29,18 @@ KERNEL_SOURCES = [os.path.join(ROOT, "graph_triangle_counting_amd", "csrc", f)
 
 
 def kernel_fingerprint() -> str:
+    """sha256 (first 16 hex digits) of the enumeration kernel's sources with comments and blank
+    lines removed: a change of code invalidates the stored counter runs, a change of comments
+    does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 
