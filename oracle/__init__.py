@@ -39,6 +39,7 @@ def _load():
         lib.oracle_count_3pcf_exact.argtypes = [P, P, i64, i32, P, P, P]
         lib.oracle_count_4pcf_parity.argtypes = [P, P, i64, i32, P, P, P]
         lib.oracle_forward_degrees.argtypes = [P, P]
+        lib.oracle_count_3pcf_hubs.argtypes = [i64, P, i32, P, P, P, i64, i32, P, P, P]
         _lib = lib
     return _lib
 
@@ -49,6 +50,29 @@ def _ptr(a: np.ndarray | None):
 
 def num_configs(order: int, nbins: int) -> int:
     return int(_load().oracle_num_configs(order, nbins))
+
+
+def count_3pcf_hubs(xyz: np.ndarray, edges_sq, hubs, w: np.ndarray | None = None,
+                    nthreads: int = 0):
+    """Binned triangles whose smallest label is one of `hubs`, by definition from the coordinates
+    (no graph).  Returns (counts uint64 [n_cfg], weighted fp64 [n_cfg] or None, scale s)."""
+    lib = _load()
+    xyz = np.ascontiguousarray(xyz, dtype=np.int32).reshape(-1, 3)
+    e = np.ascontiguousarray(np.asarray(edges_sq, dtype=np.int64))
+    h = np.ascontiguousarray(np.asarray(hubs, dtype=np.int32))
+    nb = e.size - 1
+    ncfg = num_configs(3, nb)
+    counts = np.zeros(ncfg, np.uint64)
+    weighted = None
+    if w is not None:
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        weighted = np.zeros(ncfg, np.float64)
+    s = C.c_int32(0)
+    rc = lib.oracle_count_3pcf_hubs(xyz.shape[0], _ptr(xyz), nb, _ptr(e), _ptr(w), _ptr(h),
+                                    h.size, nthreads, _ptr(counts), _ptr(weighted), C.byref(s))
+    if rc:
+        raise ValueError(f"oracle_count_3pcf_hubs failed ({rc})")
+    return counts, weighted, s.value
 
 
 class Graph:

@@ -411,6 +411,103 @@ int oracle_count_3pcf_exact(const oracle_graph *g, const double *w, int64_t hub_
     return rc;
 }
 
+/* ---------------------------------------------------------------- 3pCF at chosen hubs */
+
+/* The definition written out, with no graph: the forward neighbours of hub h are the points j > h
+ * with e_0 <= d^2(h, j) < e_nb (all n points are tested); every pair j < k of them that are
+ * neighbours of each other closes the triangle {h, j, k}, whose smallest label is h (§II.2). */
+int oracle_count_3pcf_hubs(int64_t n, const int32_t *xyz, int32_t nb, const int64_t *edges,
+                           const double *w, const int32_t *hubs, int64_t nh, int32_t nthreads,
+                           uint64_t *counts, double *weighted, int32_t *scale_out) {
+    int rc = validate_inputs(n, xyz, nb, edges);
+    if (rc) return rc;
+    if (nh < 0 || (nh > 0 && !hubs) || !counts || (w && !weighted)) return ORACLE_E_INVALID;
+    if (w && !weights_finite(w, n)) return ORACLE_E_INVALID;
+    uint8_t *seen = (uint8_t *)calloc((size_t)(n > 0 ? n : 1), 1);
+    if (!seen) return ORACLE_E_NOMEM;
+    for (int64_t t = 0; t < nh; t++) {
+        if (hubs[t] < 0 || hubs[t] >= n || seen[hubs[t]]) {
+            free(seen);
+            return ORACLE_E_INVALID; /* labels in range and distinct */
+        }
+        seen[hubs[t]] = 1;
+    }
+    free(seen);
+    const int64_t ncfg = oracle_num_configs(3, nb);
+    int32_t *rank3 = make_rank3(nb);
+    __int128 *acc = w ? (__int128 *)calloc((size_t)ncfg, sizeof(__int128)) : NULL;
+    if (!rank3 || (w && !acc)) {
+        free(rank3);
+        free(acc);
+        return ORACLE_E_NOMEM;
+    }
+    const int s = w ? weight_scale(w, n) : 0;
+    memset(counts, 0, sizeof(uint64_t) * (size_t)ncfg);
+    int nt = set_threads(nthreads);
+    int fail = 0;
+
+    #pragma omp parallel num_threads(nt) reduction(|:fail)
+    {
+        uint64_t *my = (uint64_t *)calloc((size_t)ncfg, sizeof(uint64_t));
+        __int128 *myacc = w ? (__int128 *)calloc((size_t)ncfg, sizeof(__int128)) : NULL;
+        int64_t cap = 1024, m = 0;
+        int32_t *fj = (int32_t *)malloc(sizeof(int32_t) * (size_t)cap);
+        int *fb = (int *)malloc(sizeof(int) * (size_t)cap);
+        if (!my || (w && !myacc) || !fj || !fb) fail = 1;
+        #pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < nh; t++) {
+            if (fail) continue;
+            const int32_t h = hubs[t];
+            m = 0;
+            for (int64_t j = (int64_t)h + 1; j < n; j++) {
+                const int b = bin_of(edges, nb, sq_dist(xyz + 3 * (int64_t)h, xyz + 3 * j));
+                if (b < 0) continue;
+                if (m == cap) {
+                    cap *= 2;
+                    int32_t *nj = (int32_t *)realloc(fj, sizeof(int32_t) * (size_t)cap);
+                    int *nbp = (int *)realloc(fb, sizeof(int) * (size_t)cap);
+                    if (nj) fj = nj;
+                    if (nbp) fb = nbp;
+                    if (!nj || !nbp) { fail = 1; break; }
+                }
+                fj[m] = (int32_t)j;
+                fb[m] = b;
+                m++;
+            }
+            if (fail) continue;
+            for (int64_t a = 0; a < m; a++)
+                for (int64_t c2 = a + 1; c2 < m; c2++) {
+                    const int bjk = bin_of(edges, nb,
+                                           sq_dist(xyz + 3 * (int64_t)fj[a], xyz + 3 * (int64_t)fj[c2]));
+                    if (bjk < 0) continue;
+                    int v[3] = {fb[a], fb[c2], bjk}; /* r_hj, r_hk, r_jk */
+                    sort_small_int(v, 3);
+                    const int32_t c = rank3[((size_t)v[0] * nb + v[1]) * nb + v[2]];
+                    my[c]++;
+                    if (myacc) myacc[c] += triangle_q(w[h], w[fj[a]], w[fj[c2]], s);
+                }
+        }
+        #pragma omp critical
+        {
+            if (my)
+                for (int64_t c = 0; c < ncfg; c++) counts[c] += my[c];
+            if (myacc)
+                for (int64_t c = 0; c < ncfg; c++) acc[c] += myacc[c];
+        }
+        free(my);
+        free(myacc);
+        free(fj);
+        free(fb);
+    }
+    free(rank3);
+    if (!fail && w)
+        for (int64_t c = 0; c < ncfg; c++) weighted[c] = ldexp((double)acc[c], -s);
+    free(acc);
+    if (fail) return ORACLE_E_NOMEM;
+    if (scale_out) *scale_out = s;
+    return 0;
+}
+
 /* ---------------------------------------------------------------- parity 4pCF (§III.1.1, §III.2) */
 
 /* Sign of the signed volume Eq.(3) in the label-free vertex order (see oracle.h). */

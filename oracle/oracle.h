@@ -77,6 +77,15 @@ int oracle_count_3pcf_exact(const oracle_graph *g, const double *w, int64_t hub_
                             int32_t nthreads, uint64_t *counts, int64_t *sum_q128,
                             int32_t *scale_out);
 
+/* 3pCF of the triangles whose smallest label is one of hubs[0..nh) (distinct labels in [0, n)),
+ * straight from the coordinates with no graph: for each hub h, the points j > h within the bin
+ * range, and every pair of them within the bin range of each other.  counts / weighted as in
+ * oracle_count_3pcf, with the scale s from max|w| over all n weights, so that the sums of any set
+ * of hubs add up to the sums of all hubs.  O(nh * (n + m^2)) for m forward neighbours per hub. */
+int oracle_count_3pcf_hubs(int64_t n, const int32_t *xyz, int32_t nbins, const int64_t *edges_sq,
+                           const double *w, const int32_t *hubs, int64_t nh, int32_t nthreads,
+                           uint64_t *counts, double *weighted, int32_t *scale_out);
+
 /* Parity 4pCF (nbins <= ORACLE_MAX_BINS_4PCF).  even, odd [n_cfg] (overwritten). */
 int oracle_count_4pcf_parity(const oracle_graph *g, const int32_t *xyz, int64_t hub_stride,
                              int32_t nthreads, uint64_t *even, int64_t *odd,

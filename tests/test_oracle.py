@@ -339,6 +339,47 @@ def test_hub_stride_partitions_by_smallest_label():
     assert np.all(part <= full) and 0 < part.sum() < full.sum() and 0 < w2 < walks
 
 
+@pytest.mark.parametrize("seed,n,box,nb", [(81, 60, 2000, 3), (82, 110, 3500, 6)])
+def test_hub_counts_match_brute_force(seed, n, box, nb):
+    # the graph-free per-hub definition, summed over every hub, is the brute-force 3pCF
+    xyz = small_cloud(seed, n, box, nclump=2)
+    edges = linear_edges_sq(box // 2, nb)
+    w = 0.5 + rng_for(seed + 100).random(n)
+    cnt_b, wfl_b, _ = brute.triangles(xyz, edges, w)
+    cnt, wsum, s = oracle.count_3pcf_hubs(xyz, edges, np.arange(n), w)
+    np.testing.assert_array_equal(cnt, cnt_b)
+    np.testing.assert_array_equal(wsum, wfl_b)
+    assert s == 55
+
+
+def test_hub_counts_agree_with_the_merge_walk_on_hub_subsets():
+    # two independent routes to the triangles of a hub subset: the merge-walk over the graph (hubs
+    # with label % 3 == 0) and the pair test from coordinates; subsets of hubs add up
+    xyz, edges = uniform_graph(seed=83, n=1500)
+    w = 0.5 + rng_for(84).random(xyz.shape[0])
+    g = oracle.Graph(xyz, edges)
+    part, wpart, s0, _ = g.count_3pcf(w, hub_stride=3)
+    hubs = np.arange(0, xyz.shape[0], 3)
+    cnt, wsum, s = oracle.count_3pcf_hubs(xyz, edges, hubs, w)
+    np.testing.assert_array_equal(cnt, part)
+    np.testing.assert_array_equal(wsum, wpart)
+    assert s == s0
+    rng = rng_for(85)
+    perm = rng.permutation(hubs)
+    a, wa, _ = oracle.count_3pcf_hubs(xyz, edges, perm[: perm.size // 3], w)
+    b, wb, _ = oracle.count_3pcf_hubs(xyz, edges, perm[perm.size // 3:], w)
+    np.testing.assert_array_equal(a + b, cnt)
+
+
+def test_hub_counts_reject_bad_hub_lists():
+    xyz, edges = uniform_graph(seed=86, n=200)
+    for hubs in ([0, 5, 5], [-1], [200]):
+        with pytest.raises(ValueError):
+            oracle.count_3pcf_hubs(xyz, edges, hubs)
+    cnt, _, _ = oracle.count_3pcf_hubs(xyz, edges, [])
+    assert cnt.sum() == 0
+
+
 def test_degenerate_inputs():
     edges = linear_edges_sq(1000, 3)
     for n in (0, 1, 2):
