@@ -59,6 +59,7 @@ def lib() -> C.CDLL:
         P, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
         L.gtc_build_graph.argtypes = [P, i64, P, i32, C.POINTER(Options), P, C.POINTER(P)]
         L.gtc_count_3pcf.argtypes = [P, P, P, P, C.POINTER(Stats), P]
+        L.gtc_count_3pcf_hubs.argtypes = [P, P, i64, P, P, P, C.POINTER(Stats), P]
         L.gtc_count_4pcf_parity.argtypes = [P, P, P, C.POINTER(Stats), P]
         L.gtc_num_configs.argtypes = [i32, i32]
         L.gtc_num_configs.restype = i64
@@ -173,6 +174,36 @@ class Graph:
                                     _dptr(weighted) if weighted is not None else None,
                                     C.byref(st), _stream_ptr(self._stream)))
         return counts, weighted, st.as_dict()
+
+    def count_3pcf_hubs(self, hubs, w=None):
+        """Binned triangles whose first vertex in the internal order is one of `hubs` (distinct
+        internal labels; see perm()).  Returns (counts, weighted or None, stats) as count_3pcf."""
+        import torch
+        h = np.ascontiguousarray(np.asarray(hubs, dtype=np.int32))
+        ncfg = num_configs(3, self.nbins)
+        dev = self._xyz.device
+        counts = torch.empty(ncfg, dtype=torch.int64, device=dev)
+        weighted = None
+        if w is not None:
+            if not (w.is_cuda and w.dtype == torch.float64 and w.numel() == self.n):
+                raise TypeError("w must be a CUDA float64 tensor of length n")
+            w = w.contiguous()
+            weighted = torch.empty(ncfg, dtype=torch.float64, device=dev)
+        st = Stats()
+        _check(lib().gtc_count_3pcf_hubs(self._h, h.ctypes.data_as(C.c_void_p), h.size,
+                                         _dptr(w) if w is not None else None, _dptr(counts),
+                                         _dptr(weighted) if weighted is not None else None,
+                                         C.byref(st), _stream_ptr(self._stream)))
+        return counts, weighted, st.as_dict()
+
+    def perm(self, with_row_ptr: bool = False):
+        """Internal label -> point index (host int32 [n]); with_row_ptr also returns the forward
+        CSR offsets (host int64 [n+1]) without copying the rows out."""
+        perm = np.empty(max(self.n, 1), np.int32)
+        rp = np.empty(self.n + 1, np.int64) if with_row_ptr else None
+        p = lambda a: None if a is None else a.ctypes.data_as(C.c_void_p)
+        _check(lib().gtc_graph_export(self._h, p(rp), None, None, p(perm)))
+        return (perm[: self.n], rp) if with_row_ptr else perm[: self.n]
 
     def count_4pcf_parity(self):
         """Binned 4-clique counts: (even int64 [n_cfg] holding uint64 bits, odd int64, stats)."""

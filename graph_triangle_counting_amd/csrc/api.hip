@@ -10,7 +10,7 @@ namespace gtc {
 const char *last_error();
 int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s);
 int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
-                      gtc_stats *st, hipStream_t s);
+                      gtc_stats *st, hipStream_t s, const HubSubset *sub = nullptr);
 int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
                       hipStream_t s);
 void free_graph_buffers(gtc_graph_s *G);
@@ -218,6 +218,59 @@ int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d
     fill_graph_stats(g, &local);
     int rc = count_3pcf_device(g, d_w, d_counts, d_weighted, &local,
                                reinterpret_cast<hipStream_t>(hip_stream));
+    local.count_ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    if (rc == GTC_OK && st) *st = local;
+    return rc;
+}
+
+int gtc_count_3pcf_hubs(gtc_graph g, const int32_t *h_hubs, int64_t n_hubs, const double *d_w,
+                        uint64_t *d_counts, double *d_weighted, gtc_stats *st, void *hip_stream) {
+    if (!g || !d_counts || (d_w && !d_weighted) || n_hubs < 0 || (n_hubs > 0 && !h_hubs)) {
+        set_error("gtc_count_3pcf_hubs: need a graph, d_counts, h_hubs (n_hubs >= 0), and "
+                  "d_weighted when d_w is given");
+        return GTC_E_INVALID;
+    }
+    {
+        std::vector<uint8_t> seen((size_t)std::max<int64_t>(g->n, 1), 0);
+        for (int64_t t = 0; t < n_hubs; ++t) {
+            const int32_t h = h_hubs[t];
+            if (h < 0 || h >= g->n || seen[(size_t)h]) {
+                set_error("gtc_count_3pcf_hubs: hub %lld (label %d) is out of range or repeated",
+                          (long long)t, h);
+                return GTC_E_INVALID;
+            }
+            seen[(size_t)h] = 1;
+        }
+    }
+    if (g->win.size() != 2 || g->windowed()) {
+        set_error("gtc_count_3pcf_hubs: needs a graph of one window (tile_bytes 0)");
+        return GTC_E_UNSUPPORTED;
+    }
+    DeviceGuard dg(g->device);
+    if (dg.rc) return dg.rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    auto t0 = std::chrono::steady_clock::now();
+    int32_t *d_in = nullptr, *d_out = nullptr;
+    unsigned long long *d_sums = nullptr;
+    void *blk = nullptr;
+    GTC_TRY(carve_alloc(&blk, s, [&](Carver &c) {
+        c.take(&d_in, n_hubs);
+        c.take(&d_out, n_hubs);
+        c.take(&d_sums, 3);
+    }));
+    int rc = GTC_OK;
+    if (n_hubs > 0) {
+        hipError_t e = hipMemcpyAsync(d_in, h_hubs, sizeof(int32_t) * n_hubs,
+                                      hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) rc = hip_fail(e, "hub list upload", __FILE__, __LINE__);
+    }
+    HubSubset sub;
+    if (rc == GTC_OK) rc = filter_hubs(g, d_in, n_hubs, d_out, d_sums, &sub, s);
+    gtc_stats local{};
+    fill_graph_stats(g, &local);
+    if (rc == GTC_OK) rc = count_3pcf_device(g, d_w, d_counts, d_weighted, &local, s, &sub);
+    dev_free(blk, s);
     local.count_ms =
         std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     if (rc == GTC_OK && st) *st = local;

@@ -642,6 +642,40 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     return GTC_OK;
 }
 
+// Keep the listed hubs that can close a triangle (hub_class >= 0), and sum their forward degrees
+// (merge-walks) and spoke elements.
+__global__ void __launch_bounds__(256)
+    k_filter_hubs(const int32_t *__restrict__ in, int64_t n_in, const int64_t *__restrict__ row_ptr,
+                  const int64_t *__restrict__ work, int32_t *__restrict__ out,
+                  unsigned long long *__restrict__ sums /* [3]: kept, walks, spoke elements */) {
+    const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (t >= n_in) return;
+    const int32_t i = in[t];
+    const int64_t m = row_ptr[i + 1] - row_ptr[i];
+    if (hub_class(m, work[i]) < 0) return;
+    out[atomicAdd(&sums[0], 1ull)] = i;
+    atomicAdd(&sums[1], (unsigned long long)m);
+    atomicAdd(&sums[2], (unsigned long long)work[i]);
+}
+
+int filter_hubs(const gtc_graph_s *G, const int32_t *in, int64_t n_in, int32_t *out,
+                unsigned long long *d_sums, HubSubset *res, hipStream_t s) {
+    GTC_TRY(fill_u64(reinterpret_cast<uint64_t *>(d_sums), 3, 0ull, s));
+    if (n_in > 0) {
+        hipLaunchKernelGGL(k_filter_hubs, dim3(grid_for(n_in, 256)), dim3(256), 0, s, in, n_in,
+                           G->row_ptr, G->work, out, d_sums);
+        GTC_HIP_CHECK(hipGetLastError());
+    }
+    unsigned long long h[3];
+    GTC_HIP_CHECK(hipMemcpyAsync(h, d_sums, sizeof(h), hipMemcpyDeviceToHost, s));
+    GTC_HIP_CHECK(hipStreamSynchronize(s));
+    res->hubs = out;
+    res->n_hubs = (int64_t)h[0];
+    res->walks = (int64_t)h[1];
+    res->spoke_elements = (int64_t)h[2];
+    return GTC_OK;
+}
+
 int emit_window(const gtc_graph_s *G, int64_t w, int32_t *col, uint8_t *bin, hipStream_t s) {
     const int64_t lo = G->win[w], hi = G->win[w + 1];
     if (hi <= lo) return GTC_OK;

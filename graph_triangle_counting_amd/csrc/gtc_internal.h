@@ -324,4 +324,17 @@ namespace gtc {
 // entries), entry e of the graph at col[e - h_row_ptr[win[w]]]: the pair search of the build,
 // run again.  Needs the sorted coordinates.
 int emit_window(const gtc_graph_s *G, int64_t w, int32_t *col, uint8_t *bin, hipStream_t s);
+
+// A hub list to count instead of the graph's own (one-window graphs), with its totals.
+struct HubSubset {
+    const int32_t *hubs = nullptr;  // device, internal labels, each able to close a triangle
+    int64_t n_hubs = 0;
+    int64_t walks = 0;           // sum of forward degrees
+    int64_t spoke_elements = 0;  // sum of work
+};
+
+// Keep the hubs of in[0..n_in) (device) that can close a triangle, into out (device, n_in
+// entries); d_sums: 3 device words of scratch.
+int filter_hubs(const gtc_graph_s *G, const int32_t *in, int64_t n_in, int32_t *out,
+                unsigned long long *d_sums, HubSubset *res, hipStream_t s);
 }  // namespace gtc

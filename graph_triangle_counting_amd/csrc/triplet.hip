@@ -607,7 +607,11 @@ static double limbs_to_double(const unsigned long long *l, unsigned long long co
 }
 
 int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
-                      gtc_stats *st, hipStream_t s) {
+                      gtc_stats *st, hipStream_t s, const HubSubset *sub) {
+    // hubs to count: the graph's (per window), or a caller's subset (one-window graphs)
+    const int32_t *hub_list = sub ? sub->hubs : G->hubs;
+    const int64_t hub_total = sub ? sub->n_hubs : G->n_hubs;
+    const std::vector<int64_t> win_hubs = sub ? std::vector<int64_t>{0, sub->n_hubs} : G->win_hubs;
     const bool W = d_w != nullptr;
     const int nb = G->nb;
     const int64_t ncfg = gtc_num_configs(3, nb);
@@ -661,8 +665,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.base_s = 0;
     a.s_lo = 0;
     a.s_hi = (int32_t)G->n;
-    a.hubs = G->hubs;
-    a.n_hubs = (int32_t)G->n_hubs;
+    a.hubs = hub_list;
+    a.n_hubs = (int32_t)hub_total;
     a.nb = nb;
     a.ncfg = (int32_t)ncfg;
     // Walk mode: banded (per key run, one-subtraction map offsets) for grids of >= 3 cells per axis
@@ -729,7 +733,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         v.push_back(e1);
         return GTC_OK;
     };
-    if (G->n_hubs > 0) {
+    if (hub_total > 0) {
         // LDS histogram unless it would take more than half of a workgroup's LDS, or a single hub
         // could overflow its 32-bit bins
         DeviceLimits dl;
@@ -740,7 +744,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
                         max_hub_hits >= 0x7fffffffull / 2;
         TripletPlan pl;
         const void *kfn = triplet_kernel(W, GH, banded, G->packed);
-        TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(a.ncfg, W, GH), GH, G->n_hubs, max_hub_hits, pl));
+        TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(a.ncfg, W, GH), GH, hub_total, max_hub_hits, pl));
         // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long budget = 0xffffffffull / (unsigned long long)pl.waves;
         a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub_hits);
@@ -813,11 +817,11 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         };
         std::vector<std::pair<int64_t, int64_t>> tiles;
         for (int64_t h = 0; h < nw; ++h)
-            if (G->win_hubs[h + 1] > G->win_hubs[h])
+            if (win_hubs[h + 1] > win_hubs[h])
                 for (int64_t sw = h; sw <= G->win_smax[h]; ++sw) tiles.emplace_back(h, sw);
         for (size_t t = 0; t < tiles.size(); ++t) {
             const int64_t h = tiles[t].first, sw = tiles[t].second;
-            const int64_t nh = G->win_hubs[h + 1] - G->win_hubs[h];
+            const int64_t nh = win_hubs[h + 1] - win_hubs[h];
             int kh = -1, ks = -1;
             if (ooc) {
                 const int64_t keep[2] = {h, sw};
@@ -827,7 +831,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
                 if (ks != kh) TSTEP_HIP(hipStreamWaitEvent(s, slot_ready[ks], 0));
             }
             if (t == 0 || tiles[t - 1].first != h) {
-                a.hubs = G->hubs + G->win_hubs[h];
+                a.hubs = hub_list + win_hubs[h];
                 a.n_hubs = (int32_t)nh;
                 TSTEP(hub_class_counts(a.hubs, nh, G->row_ptr, G->work, qcount, s));
             }
@@ -894,8 +898,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     for (auto v : h_counts) tri += v;
     if (st) {
         st->triangles = tri;
-        st->merge_walks = G->walks;
-        st->spoke_elements = G->spoke_elements;
+        st->merge_walks = sub ? sub->walks : G->walks;
+        st->spoke_elements = sub ? sub->spoke_elements : G->spoke_elements;
         st->tiles = tiles_run;
         st->h2d_ms = h2d_ms;
         st->kernel_ms = kms;
@@ -904,7 +908,9 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         st->launch_blocks = used.blocks;
         st->launch_lds_bytes = (int32_t)used.lds;
         st->launch_mode = banded ? 1 : 0;
-        st->q_alg_bytes = 5.0 * (double)G->E + 4.0 * (double)G->spoke_elements + (double)tri;
+        // hub rows read once (5 B per entry), spoke rows once per walk (4 B), a bin per triangle
+        st->q_alg_bytes = 5.0 * (double)(sub ? sub->walks : G->E) +
+                          4.0 * (double)st->spoke_elements + (double)tri;
     }
     cleanup_tiles();
     cleanup();

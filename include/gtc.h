@@ -136,6 +136,20 @@ int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, 
 int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d_weighted,
                    gtc_stats *st, void *hip_stream);
 
+/* The 3pCF of a subset of hubs: the binned triangles whose first vertex in the graph's internal
+ * order (gtc_graph_export's h_perm maps internal labels to point indices) is one of the listed
+ * hubs.  Disjoint hub sets give counts that add up to gtc_count_3pcf's, which makes this the
+ * per-shard primitive of a split hub range, and lets full-size runs be checked hub by hub.
+ *   h_hubs  host int32 [n_hubs]: distinct internal labels in [0, n) (hubs that can close no
+ *           triangle are allowed and contribute nothing).
+ *   d_w, d_counts, d_weighted, st, hip_stream: as gtc_count_3pcf.  The weighted scale s comes
+ *           from max |w| over all points, as in gtc_count_3pcf.  st describes the subset
+ *           (merge_walks, spoke_elements and q_alg_bytes of the listed hubs).
+ * GTC_E_INVALID for a repeated or out-of-range label; GTC_E_UNSUPPORTED for a graph of more than
+ * one hub window. */
+int gtc_count_3pcf_hubs(gtc_graph g, const int32_t *h_hubs, int64_t n_hubs, const double *d_w,
+                        uint64_t *d_counts, double *d_weighted, gtc_stats *st, void *hip_stream);
+
 /* Binned 4-clique counts split by parity (§II.2, §III.1.1, §III.2).  Needs nbins <=
  * GTC_MAX_BINS_4PCF and the coordinates (not dropped); GTC_E_UNSUPPORTED for out-of-core
  * (csr_mode 1 or 2) graphs.

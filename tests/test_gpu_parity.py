@@ -103,6 +103,45 @@ def test_3pcf_walk_modes(gpu_available, monkeypatch, layout, mode, kind, seed, n
         np.testing.assert_array_equal(ws, ows)
 
 
+def test_3pcf_hub_subsets(gpu_available):
+    # counts of hub subsets add up to the full count, match the per-hub oracle in the graph's
+    # internal order, and reject repeated or out-of-range labels
+    import torch
+    n = 20_000
+    xyz = clustered(61, n, 60, 2500)
+    edges = linear_edges_sq(12_000, 12)
+    w = 0.5 + rng_for(62).random(n)
+    g = gtc.Graph(to_gpu(xyz), edges)
+    wt = torch.from_numpy(w).cuda()
+    perm = g.perm()
+    full, wfull, _ = g.count_3pcf(wt)
+    full = full.cpu().numpy().view(np.uint64)
+    parts = np.array_split(rng_for(63).permutation(n), 3)
+    tot = np.zeros_like(full)
+    for part in parts:
+        c, _, st = g.count_3pcf_hubs(part, wt)
+        tot += c.cpu().numpy().view(np.uint64)
+    np.testing.assert_array_equal(tot, full)
+    sample = parts[0][:300]
+    c, ws, st = g.count_3pcf_hubs(sample, wt)
+    oc, ows, _ = oracle.count_3pcf_hubs(xyz[perm], edges, sample, w[perm])
+    np.testing.assert_array_equal(c.cpu().numpy().view(np.uint64), oc)
+    np.testing.assert_array_equal(ws.cpu().numpy(), ows)
+    assert st["triangles"] == int(oc.sum())
+    for bad in ([1, 2, 2], [-1], [n]):
+        with pytest.raises(gtc.GtcError) as ei:
+            g.count_3pcf_hubs(bad)
+        assert ei.value.status == gtc.GTC_E_INVALID
+    c, _, _ = g.count_3pcf_hubs([])
+    assert int(c.sum()) == 0
+    g.close()
+    gt = gtc.Graph(to_gpu(xyz), edges, tile_bytes=1 << 16)
+    with pytest.raises(gtc.GtcError) as ei:
+        gt.count_3pcf_hubs([0])
+    assert ei.value.status == gtc.GTC_E_UNSUPPORTED
+    gt.close()
+
+
 def test_3pcf_c1_full(gpu_available):
     cfg = workloads.get("C1")
     xyz, w = cfg.generate()
