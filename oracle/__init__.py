@@ -40,6 +40,11 @@ def _load():
         lib.oracle_count_4pcf_parity.argtypes = [P, P, i64, i32, P, P, P]
         lib.oracle_forward_degrees.argtypes = [P, P]
         lib.oracle_count_3pcf_hubs.argtypes = [i64, P, i32, P, P, P, i64, i32, P, P, P]
+        lib.oracle_num_configs_s4.argtypes = [i32]
+        lib.oracle_num_configs_s4.restype = i64
+        lib.oracle_config_bins_s4.argtypes = [i32, P]
+        lib.oracle_config_realizable_s4.argtypes = [i32, P, P]
+        lib.oracle_count_4pcf_parity_s4.argtypes = [P, P, i64, i32, P, P, P]
         _lib = lib
     return _lib
 
@@ -73,6 +78,29 @@ def count_3pcf_hubs(xyz: np.ndarray, edges_sq, hubs, w: np.ndarray | None = None
     if rc:
         raise ValueError(f"oracle_count_3pcf_hubs failed ({rc})")
     return counts, weighted, s.value
+
+
+def num_configs_s4(nbins: int) -> int:
+    """Number of S4 configurations of the 4pCF (six edge bins up to vertex relabelling)."""
+    return int(_load().oracle_num_configs_s4(nbins))
+
+
+def config_bins_s4(nbins: int) -> np.ndarray:
+    """Canonical 6-tuples (edge order 01, 02, 03, 12, 13, 23) of the S4 configurations, int32
+    [n_cfg, 6], in rank order."""
+    out = np.zeros((num_configs_s4(nbins), 6), np.int32)
+    if _load().oracle_config_bins_s4(nbins, _ptr(out)):
+        raise ValueError("oracle_config_bins_s4 failed")
+    return out
+
+
+def config_realizable_s4(nbins: int, edges_sq) -> np.ndarray:
+    """1 where a configuration's bin-centre edge lengths form a tetrahedron (Cayley-Menger)."""
+    e = np.ascontiguousarray(np.asarray(edges_sq, dtype=np.int64))
+    mask = np.zeros(num_configs_s4(nbins), np.uint8)
+    if _load().oracle_config_realizable_s4(nbins, _ptr(e), _ptr(mask)):
+        raise ValueError("oracle_config_realizable_s4 failed")
+    return mask
 
 
 class Graph:
@@ -149,14 +177,16 @@ class Graph:
             sums.append(v)
         return counts, sums, int(s.value)
 
-    def count_4pcf_parity(self, hub_stride: int = 1, nthreads: int = 0):
-        """Returns (even uint64[n_cfg], odd int64[n_cfg], number of 4-cliques)."""
-        ncfg = num_configs(4, self.nbins)
+    def count_4pcf_parity(self, hub_stride: int = 1, nthreads: int = 0, s4: bool = False):
+        """Returns (even uint64[n_cfg], odd int64[n_cfg], number of 4-cliques); configurations
+        are sorted 6-tuples, or S4 configurations with s4=True."""
+        ncfg = num_configs_s4(self.nbins) if s4 else num_configs(4, self.nbins)
         even = np.zeros(ncfg, np.uint64)
         odd = np.zeros(ncfg, np.int64)
         cl = C.c_uint64(0)
-        rc = _lib.oracle_count_4pcf_parity(self._h, _ptr(self.xyz), hub_stride, nthreads,
-                                           _ptr(even), _ptr(odd), C.byref(cl))
+        fn = _lib.oracle_count_4pcf_parity_s4 if s4 else _lib.oracle_count_4pcf_parity
+        rc = fn(self._h, _ptr(self.xyz), hub_stride, nthreads, _ptr(even), _ptr(odd),
+                C.byref(cl))
         if rc:
             raise ValueError(f"oracle_count_4pcf_parity failed ({rc})")
         return even, odd, int(cl.value)

@@ -542,14 +542,163 @@ static int parity_sign(const int32_t *xyz, const int32_t v_in[4]) {
     return (vol > 0) - (vol < 0);
 }
 
-int oracle_count_4pcf_parity(const oracle_graph *g, const int32_t *xyz, int64_t hub_stride,
-                             int32_t nthreads, uint64_t *even, int64_t *odd,
-                             uint64_t *cliques_out) {
+/* ---------------------------------------------------------------- S4 configurations (§III.3) */
+
+/* A tetrahedron's six edge bins in the edge order (01, 02, 03, 12, 13, 23) of its vertices 0..3.
+ * Relabelling the vertices by a permutation p of {0,1,2,3} moves the bin of edge (u, v) to edge
+ * (p(u), p(v)).  A configuration is an orbit of 6-tuples under the 24 relabellings (Eq. (4) and
+ * the text after it); its canonical tuple is the lexicographically smallest member. */
+static const int S4_EDGE[4][4] = {{-1, 0, 1, 2}, {0, -1, 3, 4}, {1, 3, -1, 5}, {2, 4, 5, -1}};
+static const int S4_EU[6] = {0, 0, 0, 1, 1, 2}, S4_EV[6] = {1, 2, 3, 2, 3, 3};
+
+static void s4_canonical(const int t[6], int out[6]) {
+    int first = 1;
+    for (int p0 = 0; p0 < 4; p0++)
+        for (int p1 = 0; p1 < 4; p1++)
+            for (int p2 = 0; p2 < 4; p2++)
+                for (int p3 = 0; p3 < 4; p3++) {
+                    const int p[4] = {p0, p1, p2, p3};
+                    if (p0 == p1 || p0 == p2 || p0 == p3 || p1 == p2 || p1 == p3 || p2 == p3) continue;
+                    int r[6];
+                    for (int e = 0; e < 6; e++) r[S4_EDGE[p[S4_EU[e]]][p[S4_EV[e]]]] = t[e];
+                    int less = first;
+                    for (int e = 0; e < 6 && !first; e++) {
+                        if (r[e] != out[e]) {
+                            less = r[e] < out[e];
+                            break;
+                        }
+                    }
+                    if (less)
+                        for (int e = 0; e < 6; e++) out[e] = r[e];
+                    first = 0;
+                }
+}
+
+static size_t tuple_key(const int t[6], int nb) {
+    size_t key = 0;
+    for (int e = 0; e < 6; e++) key = key * (size_t)nb + (size_t)t[e];
+    return key;
+}
+
+static void tuple_of_key(size_t key, int nb, int t[6]) {
+    for (int e = 5; e >= 0; e--) {
+        t[e] = (int)(key % (size_t)nb);
+        key /= (size_t)nb;
+    }
+}
+
+/* rank of every 6-tuple's configuration: canonical tuples numbered in lexicographic order */
+static int32_t *make_rank_s4(int nb, int64_t *ncfg_out) {
+    size_t sz = 1;
+    for (int k = 0; k < 6; k++) sz *= (size_t)nb;
+    int32_t *t = (int32_t *)malloc(sizeof(int32_t) * sz);
+    if (!t) return NULL;
+    int32_t r = 0;
+    for (size_t key = 0; key < sz; key++) { /* canonical tuples first, in key (lexicographic) order */
+        int v[6], c[6];
+        tuple_of_key(key, nb, v);
+        s4_canonical(v, c);
+        t[key] = tuple_key(c, nb) == key ? r++ : -1;
+    }
+    for (size_t key = 0; key < sz; key++) {
+        if (t[key] >= 0) continue;
+        int v[6], c[6];
+        tuple_of_key(key, nb, v);
+        s4_canonical(v, c);
+        t[key] = t[tuple_key(c, nb)];
+    }
+    if (ncfg_out) *ncfg_out = r;
+    return t;
+}
+
+int64_t oracle_num_configs_s4(int32_t nbins) {
+    if (nbins < 1 || nbins > ORACLE_MAX_BINS_4PCF) return 0;
+    int64_t n = 0;
+    int32_t *t = make_rank_s4(nbins, &n);
+    if (!t) return ORACLE_E_NOMEM;
+    free(t);
+    return n;
+}
+
+int oracle_config_bins_s4(int32_t nb, int32_t *bins) {
+    if (nb < 1 || nb > ORACLE_MAX_BINS_4PCF || !bins) return ORACLE_E_INVALID;
+    size_t sz = 1;
+    for (int k = 0; k < 6; k++) sz *= (size_t)nb;
+    int64_t r = 0;
+    for (size_t key = 0; key < sz; key++) {
+        int v[6], c[6];
+        tuple_of_key(key, nb, v);
+        s4_canonical(v, c);
+        if (tuple_key(c, nb) != key) continue;
+        for (int e = 0; e < 6; e++) bins[6 * r + e] = v[e];
+        r++;
+    }
+    return 0;
+}
+
+/* Cayley-Menger determinants: 16 A^2 of a triangle and 288 V^2 of a tetrahedron from squared
+ * edge lengths (5x5 bordered matrix, expanded by Gaussian elimination in long double). */
+static long double cm_triangle(long double a, long double b, long double c) {
+    return 2 * a * b + 2 * b * c + 2 * c * a - a * a - b * b - c * c;
+}
+
+static long double cm_tetrahedron(long double d[4][4]) {
+    long double m[5][5];
+    for (int i = 0; i < 5; i++)
+        for (int j = 0; j < 5; j++) m[i][j] = (i == 0 || j == 0) ? (i == j ? 0 : 1) : d[i - 1][j - 1];
+    long double det = 1;
+    for (int c = 0; c < 5; c++) {
+        int piv = c;
+        for (int r = c + 1; r < 5; r++)
+            if (fabsl(m[r][c]) > fabsl(m[piv][c])) piv = r;
+        if (m[piv][c] == 0) return 0;
+        if (piv != c) {
+            for (int k = 0; k < 5; k++) { long double t = m[c][k]; m[c][k] = m[piv][k]; m[piv][k] = t; }
+            det = -det;
+        }
+        det *= m[c][c];
+        for (int r = c + 1; r < 5; r++) {
+            const long double f = m[r][c] / m[c][c];
+            for (int k = c; k < 5; k++) m[r][k] -= f * m[c][k];
+        }
+    }
+    return det;
+}
+
+int oracle_config_realizable_s4(int32_t nb, const int64_t *edges, uint8_t *mask) {
+    if (nb < 1 || nb > ORACLE_MAX_BINS_4PCF || !edges || !mask) return ORACLE_E_INVALID;
+    const int64_t ncfg = oracle_num_configs_s4(nb);
+    int32_t *bins = (int32_t *)malloc(sizeof(int32_t) * 6 * (size_t)ncfg);
+    if (!bins) return ORACLE_E_NOMEM;
+    oracle_config_bins_s4(nb, bins);
+    for (int64_t c = 0; c < ncfg; c++) {
+        long double d[4][4] = {{0}};
+        for (int e = 0; e < 6; e++) {
+            const int b = bins[6 * c + e];
+            const long double r = 0.5L * (sqrtl((long double)edges[b]) + sqrtl((long double)edges[b + 1]));
+            d[S4_EU[e]][S4_EV[e]] = d[S4_EV[e]][S4_EU[e]] = r * r; /* bin centre in r, squared */
+        }
+        int ok = cm_tetrahedron(d) > 0;
+        for (int f = 0; f < 4 && ok; f++) { /* the face opposite vertex f */
+            int u[3], k = 0;
+            for (int q = 0; q < 4; q++)
+                if (q != f) u[k++] = q;
+            ok = cm_triangle(d[u[0]][u[1]], d[u[1]][u[2]], d[u[0]][u[2]]) > 0;
+        }
+        mask[c] = (uint8_t)ok;
+    }
+    free(bins);
+    return 0;
+}
+
+static int count_4pcf_impl(const oracle_graph *g, const int32_t *xyz, int64_t hub_stride,
+                           int32_t nthreads, int s4, uint64_t *even, int64_t *odd,
+                           uint64_t *cliques_out) {
     if (!g || !xyz || !even || !odd || hub_stride < 1) return ORACLE_E_INVALID;
     const int nb = g->nb;
     if (nb > ORACLE_MAX_BINS_4PCF) return ORACLE_E_INVALID;
-    const int64_t ncfg = oracle_num_configs(4, nb);
-    int32_t *rank6 = make_rank6(nb);
+    int64_t ncfg = oracle_num_configs(4, nb);
+    int32_t *rank6 = s4 ? make_rank_s4(nb, &ncfg) : make_rank6(nb);
     if (!rank6) return ORACLE_E_NOMEM;
     int nt = set_threads(nthreads);
     memset(even, 0, sizeof(uint64_t) * (size_t)ncfg);
@@ -586,10 +735,8 @@ int oracle_count_4pcf_parity(const oracle_graph *g, const int32_t *xyz, int64_t 
                         if (ha == hb && hb == hc) {
                             int v[6] = {g->bin[s1], g->bin[a], g->bin[al], /* i-j1, i-j2, i-j3 */
                                         g->bin[b], g->bin[be], g->bin[ga]}; /* j1-j2, j1-j3, j2-j3 */
-                            sort_small_int(v, 6);
-                            size_t key = 0;
-                            for (int t = 0; t < 6; t++) key = key * (size_t)nb + (size_t)v[t];
-                            const int32_t c = rank6[key];
+                            if (!s4) sort_small_int(v, 6); /* S4: the table maps every tuple */
+                            const int32_t c = rank6[tuple_key(v, nb)];
                             const int32_t vv[4] = {(int32_t)i, j1, j2, ha};
                             my_e[c]++;
                             my_o[c] += parity_sign(xyz, vv);
@@ -622,4 +769,16 @@ int oracle_count_4pcf_parity(const oracle_graph *g, const int32_t *xyz, int64_t 
     if (fail) return ORACLE_E_NOMEM;
     if (cliques_out) *cliques_out = cliques;
     return 0;
+}
+
+int oracle_count_4pcf_parity(const oracle_graph *g, const int32_t *xyz, int64_t hub_stride,
+                             int32_t nthreads, uint64_t *even, int64_t *odd,
+                             uint64_t *cliques_out) {
+    return count_4pcf_impl(g, xyz, hub_stride, nthreads, 0, even, odd, cliques_out);
+}
+
+int oracle_count_4pcf_parity_s4(const oracle_graph *g, const int32_t *xyz, int64_t hub_stride,
+                                int32_t nthreads, uint64_t *even, int64_t *odd,
+                                uint64_t *cliques_out) {
+    return count_4pcf_impl(g, xyz, hub_stride, nthreads, 1, even, odd, cliques_out);
 }

@@ -91,6 +91,23 @@ int oracle_count_4pcf_parity(const oracle_graph *g, const int32_t *xyz, int64_t 
                              int32_t nthreads, uint64_t *even, int64_t *odd,
                              uint64_t *cliques_out);
 
+/* S4 configurations of the 4pCF: a tetrahedron's six edge bins in the edge order (01, 02, 03, 12,
+ * 13, 23) of its vertices, up to the 24 relabellings of the vertices (the configuration of
+ * Eq. (4)); the canonical tuple is the lexicographically smallest relabelling, and configurations
+ * are numbered by their canonical tuples in lexicographic order.  nbins <= ORACLE_MAX_BINS_4PCF.
+ *   oracle_num_configs_s4: the number of configurations (0 for bad nbins).
+ *   oracle_config_bins_s4: the canonical tuples, bins [n_cfg][6].
+ *   oracle_config_realizable_s4: mask [n_cfg], 1 where the configuration's bin centres (the
+ *     midpoint in r of [sqrt(e_b), sqrt(e_b+1))) are the edge lengths of a tetrahedron of positive
+ *     volume: a positive Cayley-Menger determinant, every face a proper triangle (§V.2).
+ *   oracle_count_4pcf_parity_s4: as oracle_count_4pcf_parity, binned by S4 configuration. */
+int64_t oracle_num_configs_s4(int32_t nbins);
+int oracle_config_bins_s4(int32_t nbins, int32_t *bins);
+int oracle_config_realizable_s4(int32_t nbins, const int64_t *edges_sq, uint8_t *mask);
+int oracle_count_4pcf_parity_s4(const oracle_graph *g, const int32_t *xyz, int64_t hub_stride,
+                                int32_t nthreads, uint64_t *even, int64_t *odd,
+                                uint64_t *cliques_out);
+
 /* Number of forward neighbours of each point (neighbours with a larger label). */
 int oracle_forward_degrees(const oracle_graph *g, int32_t *deg_out);
 

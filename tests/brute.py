@@ -91,3 +91,34 @@ def cliques4(xyz: np.ndarray, edges):
             even[c] += 1
             odd[c] += chirality([xyz[v] for v in q])
     return even, odd
+
+
+def s4_canonical(t) -> tuple:
+    """Smallest relabelling of a 6-tuple of edge bins (edge order 01, 02, 03, 12, 13, 23)."""
+    B = [[None] * 4 for _ in range(4)]
+    for (u, v), x in zip(itertools.combinations(range(4), 2), t):
+        B[u][v] = B[v][u] = x
+    return min(tuple(B[p[u]][p[v]] for u, v in itertools.combinations(range(4), 2))
+               for p in itertools.permutations(range(4)))
+
+
+def s4_index(nbins: int) -> dict:
+    """Canonical 6-tuple -> rank (lexicographic), over every orbit of nbins^6 tuples."""
+    canon = sorted({s4_canonical(t) for t in itertools.product(range(nbins), repeat=6)})
+    return {t: r for r, t in enumerate(canon)}
+
+
+def cliques4_s4(xyz: np.ndarray, edges):
+    """Every pairwise-adjacent 4-set once, binned by S4 configuration."""
+    a, b = adjacency(xyz, edges)
+    nb = len(edges) - 1
+    idx = s4_index(nb)
+    even = np.zeros(len(idx), np.uint64)
+    odd = np.zeros(len(idx), np.int64)
+    n = xyz.shape[0]
+    for q in itertools.combinations(range(n), 4):
+        if all(a[u, v] for u, v in itertools.combinations(q, 2)):
+            c = idx[s4_canonical([int(b[u, v]) for u, v in itertools.combinations(q, 2)])]
+            even[c] += 1
+            odd[c] += chirality([xyz[v] for v in q])
+    return even, odd

@@ -380,6 +380,63 @@ def test_hub_counts_reject_bad_hub_lists():
     assert cnt.sum() == 0
 
 
+# ------------------------------------------------------------------ S4 configurations (§III.3)
+
+def test_s4_configuration_counts_are_the_orbit_counts():
+    # Burnside over S4 acting on the 6 edges of K4 (cycle types 1^6, 6 x 1^2 2^2, 3 x 1^2 2^2,
+    # 8 x 3^2, 6 x 2 4): (k^6 + 9 k^4 + 14 k^2) / 24
+    for k in range(1, 9):
+        assert oracle.num_configs_s4(k) == (k**6 + 9 * k**4 + 14 * k**2) // 24
+    assert oracle.num_configs_s4(4) == 276 and oracle.num_configs_s4(8) == 12496  # [G] §V.2
+
+
+@pytest.mark.parametrize("nb", [1, 2, 3])
+def test_s4_canonical_tuples(nb):
+    got = [tuple(r) for r in oracle.config_bins_s4(nb)]
+    assert got == list(brute.s4_index(nb))  # same orbits, same lexicographic order
+
+
+def test_s4_realizable_mask_matches_the_pages():
+    # [G] §V.2: 4 linear bins on 20 < r < 65 leave 178 of 276 configurations realizable.  In
+    # quarter units the edges 80, 125, 170, 215, 260 are integers; the test is scale-free.
+    edges = np.array([80, 125, 170, 215, 260], np.int64) ** 2
+    mask = oracle.config_realizable_s4(4, edges)
+    assert mask.size == 276 and int(mask.sum()) == 178
+    rank = {tuple(r): i for i, r in enumerate(oracle.config_bins_s4(4))}
+    assert mask[rank[(0, 0, 0, 0, 0, 2)]] == 0  # five edges near 26 and one near 48
+    for b in range(4):
+        assert mask[rank[(b,) * 6]] == 1  # regular tetrahedra
+
+
+@pytest.mark.parametrize("seed,n,box,nb", [(41, 26, 1500, 1), (42, 32, 2500, 2), (43, 36, 3000, 3)])
+def test_4pcf_s4_matches_brute_force(seed, n, box, nb):
+    xyz = small_cloud(seed, n, box, nclump=2)
+    edges = linear_edges_sq(box // 2, nb)
+    e_b, o_b = brute.cliques4_s4(xyz, edges)
+    e, o, ncl = oracle.Graph(xyz, edges).count_4pcf_parity(s4=True)
+    np.testing.assert_array_equal(e, e_b)
+    np.testing.assert_array_equal(o, o_b)
+    assert ncl == int(e_b.sum())
+
+
+def test_4pcf_s4_folds_onto_sorted_tuples():
+    # every S4 configuration lies in exactly one sorted-6-tuple class
+    xyz, edges = uniform_graph(seed=44, n=3000, r=30_000, nb=4)
+    g = oracle.Graph(xyz, edges)
+    e4, o4, _ = g.count_4pcf_parity(s4=True)
+    es, os_, _ = g.count_4pcf_parity()
+    cls = {t: r for r, t in enumerate(itertools.combinations_with_replacement(range(4), 6))}
+    fe = np.zeros_like(es)
+    fo = np.zeros_like(os_)
+    for c, t in enumerate(oracle.config_bins_s4(4)):
+        k = cls[tuple(sorted(int(x) for x in t))]
+        fe[k] += e4[c]
+        fo[k] += o4[c]
+    np.testing.assert_array_equal(fe, es)
+    np.testing.assert_array_equal(fo, os_)
+    assert es.sum() > 0
+
+
 def test_degenerate_inputs():
     edges = linear_edges_sq(1000, 3)
     for n in (0, 1, 2):
