@@ -60,6 +60,11 @@ def lib() -> C.CDLL:
         L.gtc_build_graph.argtypes = [P, i64, P, i32, C.POINTER(Options), P, C.POINTER(P)]
         L.gtc_count_3pcf.argtypes = [P, P, P, P, C.POINTER(Stats), P]
         L.gtc_count_3pcf_hubs.argtypes = [P, P, i64, P, P, P, C.POINTER(Stats), P]
+        L.gtc_count_4pcf_parity_s4.argtypes = [P, P, P, C.POINTER(Stats), P]
+        L.gtc_num_configs_s4.argtypes = [i32]
+        L.gtc_num_configs_s4.restype = i64
+        L.gtc_config_bins_s4.argtypes = [i32, P]
+        L.gtc_config_realizable_s4.argtypes = [i32, P, P]
         L.gtc_count_4pcf_parity.argtypes = [P, P, P, C.POINTER(Stats), P]
         L.gtc_num_configs.argtypes = [i32, i32]
         L.gtc_num_configs.restype = i64
@@ -106,6 +111,31 @@ def config_bins(order: int, nbins: int) -> np.ndarray:
     out = np.empty((num_configs(order, nbins), k), np.int32)
     _check(lib().gtc_config_bins(order, nbins, out.ctypes.data_as(C.c_void_p)))
     return out
+
+
+def num_configs_s4(nbins: int) -> int:
+    """Number of S4 configurations of the 4pCF (six edge bins up to vertex relabelling)."""
+    v = lib().gtc_num_configs_s4(nbins)
+    if v < 0:
+        raise ValueError(f"no S4 configurations for nbins {nbins}")
+    return int(v)
+
+
+def config_bins_s4(nbins: int) -> np.ndarray:
+    """Canonical tuples of the S4 configurations (edge order 01, 02, 03, 12, 13, 23): int32
+    [n_cfg, 6] in rank order."""
+    out = np.empty((num_configs_s4(nbins), 6), np.int32)
+    _check(lib().gtc_config_bins_s4(nbins, out.ctypes.data_as(C.c_void_p)))
+    return out
+
+
+def config_realizable_s4(nbins: int, edges_sq) -> np.ndarray:
+    """uint8 [n_cfg]: 1 where the configuration's bin centres form a tetrahedron."""
+    e = np.ascontiguousarray(np.asarray(edges_sq, dtype=np.int64))
+    mask = np.empty(num_configs_s4(nbins), np.uint8)
+    _check(lib().gtc_config_realizable_s4(nbins, e.ctypes.data_as(C.c_void_p),
+                                          mask.ctypes.data_as(C.c_void_p)))
+    return mask
 
 
 class Graph:
@@ -205,16 +235,17 @@ class Graph:
         _check(lib().gtc_graph_export(self._h, p(rp), None, None, p(perm)))
         return (perm[: self.n], rp) if with_row_ptr else perm[: self.n]
 
-    def count_4pcf_parity(self):
-        """Binned 4-clique counts: (even int64 [n_cfg] holding uint64 bits, odd int64, stats)."""
+    def count_4pcf_parity(self, s4: bool = False):
+        """Binned 4-clique counts: (even int64 [n_cfg] holding uint64 bits, odd int64, stats);
+        configurations are sorted 6-tuples, or S4 configurations with s4=True."""
         import torch
-        ncfg = num_configs(4, self.nbins)
+        ncfg = num_configs_s4(self.nbins) if s4 else num_configs(4, self.nbins)
         dev = self._xyz.device
         even = torch.empty(ncfg, dtype=torch.int64, device=dev)
         odd = torch.empty(ncfg, dtype=torch.int64, device=dev)
         st = Stats()
-        _check(lib().gtc_count_4pcf_parity(self._h, _dptr(even), _dptr(odd), C.byref(st),
-                                           _stream_ptr(self._stream)))
+        fn = lib().gtc_count_4pcf_parity_s4 if s4 else lib().gtc_count_4pcf_parity
+        _check(fn(self._h, _dptr(even), _dptr(odd), C.byref(st), _stream_ptr(self._stream)))
         return even, odd, st.as_dict()
 
     def export(self):

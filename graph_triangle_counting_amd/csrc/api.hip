@@ -12,7 +12,10 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s);
 int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
                       gtc_stats *st, hipStream_t s, const HubSubset *sub = nullptr);
 int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
-                      hipStream_t s);
+                      hipStream_t s, bool s4);
+int64_t num_configs_s4(int nb);
+void config_bins_s4(int nb, int32_t *bins);
+void config_realizable_s4(int nb, const int64_t *edges, uint8_t *mask);
 void free_graph_buffers(gtc_graph_s *G);
 
 static int64_t binom(int64_t n, int64_t k) {
@@ -277,23 +280,24 @@ int gtc_count_3pcf_hubs(gtc_graph g, const int32_t *h_hubs, int64_t n_hubs, cons
     return rc;
 }
 
-int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
-                          void *hip_stream) {
+static int count_4pcf(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
+                      void *hip_stream, bool s4) {
+    const char *fn = s4 ? "gtc_count_4pcf_parity_s4" : "gtc_count_4pcf_parity";
     if (!g || !d_even || !d_odd) {
-        set_error("gtc_count_4pcf_parity: need a graph, d_even and d_odd");
+        set_error("%s: need a graph, d_even and d_odd", fn);
         return GTC_E_INVALID;
     }
     if (g->nb > GTC_MAX_BINS_4PCF) {
-        set_error("gtc_count_4pcf_parity: nbins %d > %d", g->nb, GTC_MAX_BINS_4PCF);
+        set_error("%s: nbins %d > %d", fn, g->nb, GTC_MAX_BINS_4PCF);
         return GTC_E_INVALID;
     }
     if (!g->coords_kept) {
-        set_error("gtc_count_4pcf_parity: the graph was built with drop_coords");
+        set_error("%s: the graph was built with drop_coords", fn);
         return GTC_E_INVALID;
     }
     if (g->host_csr || g->rebuild) {
-        set_error("gtc_count_4pcf_parity: out-of-core (csr_mode 1 or 2) graphs are not supported "
-                  "by the 4-clique kernel, which needs every spoke row of a hub at once");
+        set_error("%s: out-of-core (csr_mode 1 or 2) graphs are not supported by the 4-clique "
+                  "kernel, which needs every spoke row of a hub at once", fn);
         return GTC_E_UNSUPPORTED;
     }
     DeviceGuard dg(g->device);
@@ -301,11 +305,51 @@ int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_sta
     auto t0 = std::chrono::steady_clock::now();
     gtc_stats local{};
     fill_graph_stats(g, &local);
-    int rc = count_4pcf_device(g, d_even, d_odd, &local, reinterpret_cast<hipStream_t>(hip_stream));
+    int rc = count_4pcf_device(g, d_even, d_odd, &local, reinterpret_cast<hipStream_t>(hip_stream),
+                               s4);
     local.count_ms =
         std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     if (rc == GTC_OK && st) *st = local;
     return rc;
+}
+
+int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
+                          void *hip_stream) {
+    return count_4pcf(g, d_even, d_odd, st, hip_stream, false);
+}
+
+int gtc_count_4pcf_parity_s4(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
+                             void *hip_stream) {
+    return count_4pcf(g, d_even, d_odd, st, hip_stream, true);
+}
+
+int64_t gtc_num_configs_s4(int32_t nbins) {
+    if (nbins < 1 || nbins > GTC_MAX_BINS_4PCF) return -1;
+    return num_configs_s4(nbins);
+}
+
+int gtc_config_bins_s4(int32_t nbins, int32_t *h_bins) {
+    if (nbins < 1 || nbins > GTC_MAX_BINS_4PCF || !h_bins) {
+        set_error("gtc_config_bins_s4: nbins in [1, %d] and h_bins non-NULL", GTC_MAX_BINS_4PCF);
+        return GTC_E_INVALID;
+    }
+    config_bins_s4(nbins, h_bins);
+    return GTC_OK;
+}
+
+int gtc_config_realizable_s4(int32_t nbins, const int64_t *h_edges_sq, uint8_t *h_mask) {
+    if (nbins < 1 || nbins > GTC_MAX_BINS_4PCF || !h_edges_sq || !h_mask) {
+        set_error("gtc_config_realizable_s4: nbins in [1, %d], h_edges_sq and h_mask non-NULL",
+                  GTC_MAX_BINS_4PCF);
+        return GTC_E_INVALID;
+    }
+    for (int b = 0; b < nbins; ++b)
+        if (h_edges_sq[0] < 0 || h_edges_sq[b + 1] <= h_edges_sq[b]) {
+            set_error("gtc_config_realizable_s4: bin edges must be >= 0 and increase strictly");
+            return GTC_E_INVALID;
+        }
+    config_realizable_s4(nbins, h_edges_sq, h_mask);
+    return GTC_OK;
 }
 
 int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h_bin,

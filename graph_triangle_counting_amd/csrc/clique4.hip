@@ -24,6 +24,8 @@ struct CliqueArgs {
     const int32_t *col;
     const uint8_t *bin;    // null: packed entries, the bin in the top byte of col
     uint32_t label_mask;   // label bits of a col word
+    const uint32_t *s4rank;  // null: sorted 6-tuple ranks; else the S4 configuration of every
+                             // base-nb key of the six bins in edge order (01,02,03,12,13,23)
     const int32_t *hubs;
     int32_t n_hubs;
     int32_t nb, ncfg;
@@ -99,7 +101,7 @@ __device__ __forceinline__ int edge_bin(int64_t d2, const int64_t *se, int nb) {
 
 // GH: bins go straight to global memory (configuration counts too large for LDS).
 template <bool GH>
-__global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *edges) {
+__global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *edges) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int64_t se[GTC_MAX_BINS_4PCF + 1];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
@@ -202,19 +204,28 @@ __global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *ed
                         int4 p[4] = {pi, rc[ra], rc[rbb], rc[rcc]};
                         const int64_t dab = d2i(p[1], p[2]), dac = d2i(p[1], p[3]), dbc = d2i(p[2], p[3]);
                         const int64_t dia = d2i(p[0], p[1]), dib = d2i(p[0], p[2]), dic = d2i(p[0], p[3]);
+                        // the six bins in edge order of the vertices (i, a, b, c)
                         int bb[6] = {rbin[ra], rbin[rbb], rbin[rcc], edge_bin(dab, se, a.nb),
                                      edge_bin(dac, se, a.nb), edge_bin(dbc, se, a.nb)};
-                        // sorting network for six values
-                        cswap(bb[1], bb[2]); cswap(bb[4], bb[5]); cswap(bb[0], bb[2]);
-                        cswap(bb[3], bb[5]); cswap(bb[0], bb[1]); cswap(bb[3], bb[4]);
-                        cswap(bb[1], bb[4]); cswap(bb[0], bb[3]); cswap(bb[2], bb[5]);
-                        cswap(bb[1], bb[3]); cswap(bb[2], bb[4]); cswap(bb[2], bb[3]);
-                        int rank = 0, prev = -1;
+                        int rank = 0;
+                        if (a.s4rank) {  // S4 configuration: one table read
+                            int key = 0;
 #pragma unroll
-                        for (int q = 0; q < 6; ++q) {
-                            const int cq = bb[q] + q;  // strictly increasing combination element
-                            rank += binom[(N - prev - 1) * 8 + (6 - q)] - binom[(N - cq) * 8 + (6 - q)];
-                            prev = cq;
+                            for (int q = 0; q < 6; ++q) key = key * a.nb + bb[q];
+                            rank = (int)a.s4rank[key];
+                        } else {  // sorted 6-tuple: sorting network, combinatorial rank
+                            cswap(bb[1], bb[2]); cswap(bb[4], bb[5]); cswap(bb[0], bb[2]);
+                            cswap(bb[3], bb[5]); cswap(bb[0], bb[1]); cswap(bb[3], bb[4]);
+                            cswap(bb[1], bb[4]); cswap(bb[0], bb[3]); cswap(bb[2], bb[5]);
+                            cswap(bb[1], bb[3]); cswap(bb[2], bb[4]); cswap(bb[2], bb[3]);
+                            int prev = -1;
+#pragma unroll
+                            for (int q = 0; q < 6; ++q) {
+                                const int cq = bb[q] + q;  // strictly increasing combination element
+                                rank += binom[(N - prev - 1) * 8 + (6 - q)] -
+                                        binom[(N - cq) * 8 + (6 - q)];
+                                prev = cq;
+                            }
                         }
                         int64_t key[4] = {dia + dib + dic, dia + dab + dac, dib + dab + dbc,
                                           dic + dac + dbc};
@@ -256,9 +267,150 @@ __global__ void __launch_bounds__(256) k_clique4(CliqueArgs a, const int64_t *ed
     }
 }
 
+// ------------------------------------------------------------------ S4 configurations (§III.3)
+// A tetrahedron's six edge bins in the edge order (01, 02, 03, 12, 13, 23) of its vertices, up to
+// the 24 relabellings of the vertices; a relabelling p moves the bin of edge (u, v) to edge
+// (p(u), p(v)).  The canonical tuple is the smallest relabelling; as base-nb keys with edge 01 most
+// significant keep lexicographic order, it is the relabelling with the smallest key.
+__host__ __device__ inline int s4_edge(int u, int v) {
+    const int lo = u < v ? u : v, hi = u < v ? v : u;
+    return lo == 0 ? hi - 1 : lo + hi;  // 01->0 02->1 03->2 12->3 13->4 23->5
+}
+
+__host__ __device__ inline uint32_t s4_canonical_key(uint32_t key, int nb) {
+    int t[6];
+    for (int e = 5; e >= 0; --e) {
+        t[e] = (int)(key % (uint32_t)nb);
+        key /= (uint32_t)nb;
+    }
+    constexpr int eu[6] = {0, 0, 0, 1, 1, 2}, ev[6] = {1, 2, 3, 2, 3, 3};
+    uint32_t best = 0xffffffffu;
+    for (int perm = 0; perm < 24; ++perm) {  // perm -> a permutation of {0,1,2,3} (factorial base)
+        int p[4] = {0, 1, 2, 3};
+        int code = perm;
+        for (int k = 0; k < 3; ++k) {
+            const int span = 4 - k, j = k + code % span;
+            code /= span;
+            const int tmp = p[k];
+            p[k] = p[j];
+            p[j] = tmp;
+        }
+        int r[6];
+        for (int e = 0; e < 6; ++e) r[s4_edge(p[eu[e]], p[ev[e]])] = t[e];
+        uint32_t k2 = 0;
+        for (int e = 0; e < 6; ++e) k2 = k2 * (uint32_t)nb + (uint32_t)r[e];
+        best = k2 < best ? k2 : best;
+    }
+    return best;
+}
+
+int64_t num_s4_keys(int nb) {
+    int64_t k = 1;
+    for (int e = 0; e < 6; ++e) k *= nb;
+    return k;
+}
+
+__global__ void k_s4_canon(uint32_t nkeys, int nb, uint32_t *__restrict__ canon,
+                           int32_t *__restrict__ is_canon) {
+    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nkeys) return;
+    const uint32_t c = s4_canonical_key(t, nb);
+    canon[t] = c;
+    is_canon[t] = c == t;
+}
+
+__global__ void k_s4_rank(uint32_t nkeys, const int32_t *__restrict__ canon_rank,
+                          uint32_t *__restrict__ canon /* in: canonical key, out: rank */) {
+    const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < nkeys) canon[t] = (uint32_t)canon_rank[canon[t]];
+}
+
+// rank[key] for every base-nb 6-tuple key: the number of canonical keys below its canonical key
+static int s4_rank_table(int nb, uint32_t *rank, int32_t *flags, int32_t *scan, void *ws,
+                         hipStream_t s) {
+    const int64_t nk = num_s4_keys(nb);
+    const unsigned blocks = (unsigned)((nk + 255) / 256);
+    hipLaunchKernelGGL(k_s4_canon, dim3(blocks), dim3(256), 0, s, (uint32_t)nk, nb, rank, flags);
+    GTC_HIP_CHECK(hipGetLastError());
+    GTC_TRY(exclusive_scan_i32_to_i32(flags, scan, nk, ws, s));
+    hipLaunchKernelGGL(k_s4_rank, dim3(blocks), dim3(256), 0, s, (uint32_t)nk, scan, rank);
+    GTC_HIP_CHECK(hipGetLastError());
+    return GTC_OK;
+}
+
+int64_t num_configs_s4(int nb) {
+    const int64_t k = nb;
+    return (k * k * k * k * k * k + 9 * k * k * k * k + 14 * k * k) / 24;  // Burnside over S4
+}
+
+// canonical tuples in rank order (host)
+void config_bins_s4(int nb, int32_t *bins) {
+    const int64_t nk = num_s4_keys(nb);
+    int64_t r = 0;
+    for (int64_t key = 0; key < nk; ++key) {
+        if (s4_canonical_key((uint32_t)key, nb) != (uint32_t)key) continue;
+        int64_t k2 = key;
+        for (int e = 5; e >= 0; --e) {
+            bins[6 * r + e] = (int32_t)(k2 % nb);
+            k2 /= nb;
+        }
+        ++r;
+    }
+}
+
+// Cayley-Menger: 288 V^2 of the tetrahedron with squared edges d (5x5 bordered determinant by
+// elimination with partial pivoting), and 16 A^2 of the triangle with squared sides a, b, c
+static long double cm_volume(long double d[4][4]) {
+    long double m[5][5];
+    for (int i = 0; i < 5; ++i)
+        for (int j = 0; j < 5; ++j)
+            m[i][j] = (i == 0 || j == 0) ? (i == j ? 0.0L : 1.0L) : d[i - 1][j - 1];
+    long double det = 1.0L;
+    for (int c = 0; c < 5; ++c) {
+        int piv = c;
+        for (int r = c + 1; r < 5; ++r)
+            if (std::fabs(m[r][c]) > std::fabs(m[piv][c])) piv = r;
+        if (m[piv][c] == 0.0L) return 0.0L;
+        if (piv != c) {
+            for (int k = 0; k < 5; ++k) std::swap(m[c][k], m[piv][k]);
+            det = -det;
+        }
+        det *= m[c][c];
+        for (int r = c + 1; r < 5; ++r) {
+            const long double f = m[r][c] / m[c][c];
+            for (int k = c; k < 5; ++k) m[r][k] -= f * m[c][k];
+        }
+    }
+    return det;
+}
+
+void config_realizable_s4(int nb, const int64_t *edges, uint8_t *mask) {
+    std::vector<int32_t> bins(6 * num_configs_s4(nb));
+    config_bins_s4(nb, bins.data());
+    constexpr int eu[6] = {0, 0, 0, 1, 1, 2}, ev[6] = {1, 2, 3, 2, 3, 3};
+    for (int64_t c = 0; c < num_configs_s4(nb); ++c) {
+        long double d[4][4] = {};
+        for (int e = 0; e < 6; ++e) {
+            const int b = bins[6 * c + e];
+            const long double r = 0.5L * (std::sqrt((long double)edges[b]) +
+                                          std::sqrt((long double)edges[b + 1]));
+            d[eu[e]][ev[e]] = d[ev[e]][eu[e]] = r * r;
+        }
+        bool ok = cm_volume(d) > 0.0L;
+        for (int f = 0; f < 4 && ok; ++f) {  // the face opposite vertex f
+            int u[3], k = 0;
+            for (int q = 0; q < 4; ++q)
+                if (q != f) u[k++] = q;
+            const long double x = d[u[0]][u[1]], y = d[u[1]][u[2]], z = d[u[0]][u[2]];
+            ok = 2 * x * y + 2 * y * z + 2 * z * x - x * x - y * y - z * z > 0.0L;
+        }
+        mask[c] = ok ? 1 : 0;
+    }
+}
+
 int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
-                      hipStream_t s) {
-    const int64_t ncfg = gtc_num_configs(4, G->nb);
+                      hipStream_t s, bool s4) {
+    const int64_t ncfg = s4 ? num_configs_s4(G->nb) : gtc_num_configs(4, G->nb);
     GTC_TRY(fill_u64(d_even, ncfg, 0ull, s));
     GTC_TRY(fill_u64(reinterpret_cast<uint64_t *>(d_odd), ncfg, 0ull, s));
     if (G->max_deg >= 65535) {
@@ -288,12 +440,20 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     GTC_HIP_CHECK(hipGetDevice(&dev));
     GTC_HIP_CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
     GTC_HIP_CHECK(hipDeviceGetAttribute(&ldsmax, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
-    // LDS bins unless they would take more than half of a workgroup's LDS
-    const bool GH = clique_lds_fixed(a.ncfg, false) > (size_t)ldsmax / 2;
+    // LDS bins while they leave room for two waves' hub data (global atomics per tetrahedron cost
+    // several times the occupancy the histogram takes)
+    const size_t static_lds0 = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
+    const bool GH = static_lds0 + clique_lds_fixed(a.ncfg, false) +
+                        2 * clique_lds_wave(a.map_bytes, a.max_m, a.words) > (size_t)ldsmax;
     const size_t fixed = clique_lds_fixed(a.ncfg, GH), per = clique_lds_wave(a.map_bytes, a.max_m, a.words);
-    int waves = 4;
+    // Workgroups of 4 waves; a large LDS histogram (S4 configurations) allows one workgroup per
+    // CU, which then takes as many waves (up to 16) as the LDS beside the histogram holds.
     const size_t static_lds = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
+    int waves = 4;
+    if (!GH && fixed > (size_t)ldsmax / 2)
+        waves = (int)std::min<size_t>(16, (ldsmax - static_lds - fixed) / std::max<size_t>(per, 1));
     while (waves > 1 && static_lds + fixed + waves * per > (size_t)ldsmax) waves >>= 1;
+    if (waves < 1) waves = 1;
     const size_t lds = fixed + waves * per;
     if (static_lds + lds > (size_t)ldsmax) {
         set_error("4pCF needs %zu bytes of LDS per workgroup (longest row %d, hub domain %d); the "
@@ -310,12 +470,24 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub);
 
     unsigned int *queue = nullptr, *qcount = nullptr;
+    uint32_t *s4rank = nullptr;
+    int32_t *s4flags = nullptr, *s4scan = nullptr;
+    int64_t *s4ws = nullptr;
     void *scratch = nullptr;
+    const int64_t nkeys = s4 ? num_s4_keys(G->nb) : 0;
     GTC_TRY(carve_alloc(&scratch, s, [&](Carver &c) {
         c.take(&queue, (size_t)kHubClasses * kQueueStride);
         c.take(&qcount, kHubClasses);
+        if (s4) {
+            c.take(&s4rank, nkeys);
+            c.take(&s4flags, nkeys);
+            c.take(&s4scan, nkeys + 1);
+            c.take(&s4ws, scan_workspace_bytes(nkeys) / sizeof(int64_t));
+        }
     }));
     int rc = fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s);
+    if (!rc && s4) rc = s4_rank_table(G->nb, s4rank, s4flags, s4scan, s4ws, s);
+    a.s4rank = s4rank;
     if (!rc) rc = hub_class_counts(G->hubs, G->n_hubs, G->row_ptr, G->work, qcount, s);
     a.queue = queue;
     a.qcount = qcount;

@@ -158,6 +158,26 @@ int gtc_count_3pcf_hubs(gtc_graph g, const int32_t *h_hubs, int64_t n_hubs, cons
 int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
                           void *hip_stream);
 
+/* S4 configurations of the 4pCF (§III.3): a tetrahedron's six edge bins, in the edge order
+ * (01, 02, 03, 12, 13, 23) of its vertices 0..3, up to the 24 relabellings of the vertices -- the
+ * configuration on which Eq. (4) is evaluated.  A configuration's canonical tuple is its
+ * lexicographically smallest relabelling; configurations are numbered by canonical tuple in
+ * lexicographic order.  There are (k^6 + 9 k^4 + 14 k^2) / 24 of them for k bins (276 at 4 bins,
+ * 12,496 at 8).  nbins <= GTC_MAX_BINS_4PCF.
+ *   gtc_count_4pcf_parity_s4: as gtc_count_4pcf_parity, with even / odd of
+ *     [gtc_num_configs_s4(nbins)] indexed by S4 configuration.
+ *   gtc_num_configs_s4: the number of configurations, or -1 for nbins out of range.
+ *   gtc_config_bins_s4: h_bins host int32 [n_cfg][6], the canonical tuples in rank order.
+ *   gtc_config_realizable_s4: h_mask host uint8 [n_cfg]: 1 where the bin centres (midpoint in r of
+ *     [sqrt(e_b), sqrt(e_{b+1}))) are the edge lengths of a tetrahedron of positive volume -- a
+ *     positive Cayley-Menger determinant, every face a proper triangle (§V.2: 178 of 276 at
+ *     4 bins); h_edges_sq as gtc_build_graph.  Host only. */
+int gtc_count_4pcf_parity_s4(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
+                             void *hip_stream);
+int64_t gtc_num_configs_s4(int32_t nbins);
+int gtc_config_bins_s4(int32_t nbins, int32_t *h_bins);
+int gtc_config_realizable_s4(int32_t nbins, const int64_t *h_edges_sq, uint8_t *h_mask);
+
 /* Number of configurations: C(nbins+2, 3) for order 3, C(nbins+5, 6) for order 4; -1 if the
  * order or nbins is out of range. */
 int64_t gtc_num_configs(int32_t order, int32_t nbins);

@@ -51,6 +51,23 @@ def _build(xyz_ptr, n, edges, nb, opt=None):
     return rc, h
 
 
+def test_s4_configuration_tables_match_the_oracle():
+    import oracle
+    for nb in range(1, 17):
+        assert gtc.num_configs_s4(nb) == (nb**6 + 9 * nb**4 + 14 * nb**2) // 24
+    assert gtc.lib().gtc_num_configs_s4(17) == -1 and gtc.lib().gtc_num_configs_s4(0) == -1
+    for nb in range(1, 7):
+        np.testing.assert_array_equal(gtc.config_bins_s4(nb), oracle.config_bins_s4(nb))
+    from workloads import linear_edges_sq
+    cases = [(4, np.array([80, 125, 170, 215, 260], np.int64) ** 2),  # [G] §V.2: 178 of 276
+             (4, linear_edges_sq(20_000, 4)), (5, linear_edges_sq(9_000, 5)),
+             (8, linear_edges_sq(20_366, 8))]
+    for nb, edges in cases:
+        m = gtc.config_realizable_s4(nb, edges)
+        np.testing.assert_array_equal(m, oracle.config_realizable_s4(nb, edges))
+    assert int(gtc.config_realizable_s4(4, cases[0][1]).sum()) == 178
+
+
 def test_build_rejects_bad_arguments_without_gpu():
     fake = C.c_void_p(0x1000)  # never dereferenced: every case fails before any device work
     cases = [

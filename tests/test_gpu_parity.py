@@ -6,6 +6,8 @@ configuration, which bit-exactness implies.
 """
 from __future__ import annotations
 
+import itertools
+
 import numpy as np
 import pytest
 
@@ -265,15 +267,55 @@ def test_4pcf_matches_oracle(gpu_available, monkeypatch, layout, kind, seed, n, 
     assert st["cliques4"] == ncl and ncl > 0
 
 
-def test_4pcf_c4_full(gpu_available):
-    cfg = workloads.get("C4")
-    xyz, _ = cfg.generate()
-    say("C4", xyz.shape)
-    e, o, st = hip_4pcf(xyz, cfg.edges_sq())
-    say("C4 gpu done", st["cliques4"], st["kernel_ms"])
-    oe, oo, ncl = oracle.Graph(xyz, cfg.edges_sq()).count_4pcf_parity()
+@pytest.mark.parametrize("kind,seed,n,r,nb", CASES_4)
+def test_4pcf_s4_matches_oracle(gpu_available, kind, seed, n, r, nb):
+    # S4 configurations (six edge bins up to vertex relabelling), even and odd channels
+    say("4pcf s4", kind, seed, n, r, nb)
+    xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 50, 2000)
+    edges = linear_edges_sq(r, nb)
+    g = gtc.Graph(to_gpu(xyz), edges)
+    e, o, st = g.count_4pcf_parity(s4=True)
+    es, os_, _ = g.count_4pcf_parity()
+    g.close()
+    e = e.cpu().numpy().view(np.uint64)
+    o = o.cpu().numpy()
+    oe, oo, ncl = oracle.Graph(xyz, edges).count_4pcf_parity(s4=True)
     np.testing.assert_array_equal(e, oe)
     np.testing.assert_array_equal(o, oo)
+    assert st["cliques4"] == ncl and ncl > 0
+    # folding S4 configurations onto sorted 6-tuples gives the sorted-tuple counts
+    cls = {t: r for r, t in enumerate(itertools.combinations_with_replacement(range(nb), 6))}
+    fe = np.zeros(len(cls), np.uint64)
+    for c, t in enumerate(gtc.config_bins_s4(nb)):
+        fe[cls[tuple(sorted(int(x) for x in t))]] += e[c]
+    np.testing.assert_array_equal(fe, es.cpu().numpy().view(np.uint64))
+
+
+def test_4pcf_c4_full(gpu_available):
+    # full C4 in both configuration schemes from one oracle pass: S4 counts compared directly,
+    # sorted-tuple counts through the folding of S4 configurations onto sorted 6-tuples
+    cfg = workloads.get("C4")
+    xyz, _ = cfg.generate()
+    nb = cfg.nbins
+    say("C4", xyz.shape)
+    g = gtc.Graph(to_gpu(xyz), cfg.edges_sq())
+    es, os_, st = g.count_4pcf_parity()
+    e4, o4, st4 = g.count_4pcf_parity(s4=True)
+    g.close()
+    say("C4 gpu done", st["cliques4"], st["kernel_ms"], "s4", st4["kernel_ms"])
+    oe, oo, ncl = oracle.Graph(xyz, cfg.edges_sq()).count_4pcf_parity(s4=True)
+    np.testing.assert_array_equal(e4.cpu().numpy().view(np.uint64), oe)
+    np.testing.assert_array_equal(o4.cpu().numpy(), oo)
+    cls = {t: r for r, t in enumerate(itertools.combinations_with_replacement(range(nb), 6))}
+    fe = np.zeros(len(cls), np.uint64)
+    fo = np.zeros(len(cls), np.int64)
+    for c, t in enumerate(oracle.config_bins_s4(nb)):
+        k = cls[tuple(sorted(int(x) for x in t))]
+        fe[k] += oe[c]
+        fo[k] += oo[c]
+    np.testing.assert_array_equal(es.cpu().numpy().view(np.uint64), fe)
+    np.testing.assert_array_equal(os_.cpu().numpy(), fo)
+    assert st["cliques4"] == st4["cliques4"] == ncl
     assert np.abs(oo).sum() > 0
 
 
