@@ -45,6 +45,8 @@ def _load():
         lib.oracle_config_bins_s4.argtypes = [i32, P]
         lib.oracle_config_realizable_s4.argtypes = [i32, P, P]
         lib.oracle_count_4pcf_parity_s4.argtypes = [P, P, i64, i32, P, P, P]
+        lib.oracle_count_2pcf.argtypes = [P, P, P, P, P]
+        lib.oracle_disconnected_4pcf_s4.argtypes = [i32, P, P]
         _lib = lib
     return _lib
 
@@ -101,6 +103,15 @@ def config_realizable_s4(nbins: int, edges_sq) -> np.ndarray:
     if _load().oracle_config_realizable_s4(nbins, _ptr(e), _ptr(mask)):
         raise ValueError("oracle_config_realizable_s4 failed")
     return mask
+
+
+def disconnected_4pcf_s4(nbins: int, xi) -> np.ndarray:
+    """Eq. (4) per S4 configuration from the binned 2pCF xi [nbins]."""
+    x = np.ascontiguousarray(np.asarray(xi, dtype=np.float64))
+    out = np.zeros(num_configs_s4(nbins), np.float64)
+    if _load().oracle_disconnected_4pcf_s4(nbins, _ptr(x), _ptr(out)):
+        raise ValueError("oracle_disconnected_4pcf_s4 failed")
+    return out
 
 
 class Graph:
@@ -176,6 +187,19 @@ class Graph:
                 v -= 1 << 128
             sums.append(v)
         return counts, sums, int(s.value)
+
+    def count_2pcf(self, w: np.ndarray | None = None):
+        """Pairs per bin: (counts uint64 [nbins], weighted fp64 [nbins] or None, scale s)."""
+        counts = np.zeros(self.nbins, np.uint64)
+        weighted = None
+        if w is not None:
+            w = np.ascontiguousarray(w, dtype=np.float64)
+            weighted = np.zeros(self.nbins, np.float64)
+        sc = C.c_int32(0)
+        rc = _lib.oracle_count_2pcf(self._h, _ptr(w), _ptr(counts), _ptr(weighted), C.byref(sc))
+        if rc:
+            raise ValueError(f"oracle_count_2pcf failed ({rc})")
+        return counts, weighted, sc.value
 
     def count_4pcf_parity(self, hub_stride: int = 1, nthreads: int = 0, s4: bool = False):
         """Returns (even uint64[n_cfg], odd int64[n_cfg], number of 4-cliques); configurations

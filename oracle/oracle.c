@@ -411,6 +411,63 @@ int oracle_count_3pcf_exact(const oracle_graph *g, const double *w, int64_t hub_
     return rc;
 }
 
+/* ---------------------------------------------------------------- 2pCF (§II.1, §III.3) */
+
+/* Pairs per bin, each pair once; weighted: sum of p = fl(w_i * w_j), each scaled to the integer
+ * q = rint(p * 2^s) and summed exactly, then rounded once (s = 57 - e for M = fl(a * a) = f 2^e,
+ * a = max |w|, so |q| < 2^57). */
+int oracle_count_2pcf(const oracle_graph *g, const double *w, uint64_t *counts, double *weighted,
+                      int32_t *scale_out) {
+    if (!g || !counts || (w && !weighted)) return ORACLE_E_INVALID;
+    if (w && !weights_finite(w, g->n)) return ORACLE_E_INVALID;
+    const int nb = g->nb;
+    __int128 *acc = w ? (__int128 *)calloc((size_t)nb, sizeof(__int128)) : NULL;
+    if (w && !acc) return ORACLE_E_NOMEM;
+    int s = 0;
+    if (w) {
+        double a = 0.0;
+        for (int64_t i = 0; i < g->n; i++) a = fmax(a, fabs(w[i]));
+        const double m = a * a;
+        if (m != 0.0) {
+            int e;
+            frexp(m, &e);
+            s = 57 - e;
+        }
+    }
+    memset(counts, 0, sizeof(uint64_t) * (size_t)nb);
+    for (int64_t i = 0; i < g->n; i++)
+        for (int64_t e = g->row_ptr[i]; e < g->row_ptr[i + 1]; e++) {
+            const int32_t j = g->col[e];
+            if (j <= i) continue; /* each pair once */
+            counts[g->bin[e]]++;
+            if (w) {
+                volatile double p = w[i] * w[j];
+                acc[g->bin[e]] += (int64_t)rint(ldexp(p, s));
+            }
+        }
+    if (w)
+        for (int b = 0; b < nb; b++) weighted[b] = ldexp((double)acc[b], -s);
+    free(acc);
+    if (scale_out) *scale_out = s;
+    return 0;
+}
+
+/* Eq. (4) per S4 configuration: the three ways of splitting the four vertices into two pairs are
+ * the edge pairs (01, 23), (02, 13), (03, 12) of the canonical tuple. */
+int oracle_disconnected_4pcf_s4(int32_t nb, const double *xi, double *disc) {
+    if (nb < 1 || nb > ORACLE_MAX_BINS_4PCF || !xi || !disc) return ORACLE_E_INVALID;
+    const int64_t ncfg = oracle_num_configs_s4(nb);
+    int32_t *bins = (int32_t *)malloc(sizeof(int32_t) * 6 * (size_t)ncfg);
+    if (!bins) return ORACLE_E_NOMEM;
+    oracle_config_bins_s4(nb, bins);
+    for (int64_t c = 0; c < ncfg; c++) {
+        const int32_t *t = bins + 6 * c;
+        disc[c] = xi[t[0]] * xi[t[5]] + xi[t[1]] * xi[t[4]] + xi[t[2]] * xi[t[3]];
+    }
+    free(bins);
+    return 0;
+}
+
 /* ---------------------------------------------------------------- 3pCF at chosen hubs */
 
 /* The definition written out, with no graph: the forward neighbours of hub h are the points j > h

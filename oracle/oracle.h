@@ -108,6 +108,18 @@ int oracle_count_4pcf_parity_s4(const oracle_graph *g, const int32_t *xyz, int64
                                 int32_t nthreads, uint64_t *even, int64_t *odd,
                                 uint64_t *cliques_out);
 
+/* 2pCF: pairs of the graph per bin, each once: counts [nbins]; with w, weighted [nbins] receives
+ * the sums of w_i w_j, each product p = fl(w_i * w_j) scaled to q = rint(p * 2^s), summed exactly
+ * and rounded once (s = 57 - e for M = fl(a * a) = f * 2^e, f in [0.5, 1), a = max|w|; s = 0 if
+ * M == 0); *scale_out (may be NULL) receives s.  With data weights summing to +1 and random weights
+ * to -1 the weighted sums are the Landy-Szalay numerator DD - 2DR + RR (§II.1). */
+int oracle_count_2pcf(const oracle_graph *g, const double *w, uint64_t *counts, double *weighted,
+                      int32_t *scale_out);
+
+/* Disconnected 4pCF, Eq. (4), per S4 configuration from the binned 2pCF xi [nbins]:
+ * disc[c] = xi(b01) xi(b23) + xi(b02) xi(b13) + xi(b03) xi(b12) of the canonical tuple. */
+int oracle_disconnected_4pcf_s4(int32_t nbins, const double *xi, double *disc);
+
 /* Number of forward neighbours of each point (neighbours with a larger label). */
 int oracle_forward_degrees(const oracle_graph *g, int32_t *deg_out);
 

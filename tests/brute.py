@@ -122,3 +122,31 @@ def cliques4_s4(xyz: np.ndarray, edges):
             even[c] += 1
             odd[c] += chirality([xyz[v] for v in q])
     return even, odd
+
+
+def pairs(xyz: np.ndarray, edges, w=None):
+    """Every adjacent pair once: (counts uint64 [nb], exact weighted sums of fl(w_i w_j) as
+    Fractions or None)."""
+    from fractions import Fraction
+    a, b = adjacency(xyz, edges)
+    nb = len(edges) - 1
+    counts = np.zeros(nb, np.uint64)
+    acc = [Fraction(0)] * nb
+    n = xyz.shape[0]
+    for i in range(n):
+        for j in range(i + 1, n):
+            if a[i, j]:
+                counts[b[i, j]] += 1
+                if w is not None:
+                    acc[b[i, j]] += Fraction(float(w[i]) * float(w[j]))  # one rounded product
+    return counts, (acc if w is not None else None)
+
+
+def disconnected_s4(t, xi) -> float:
+    """Eq. (4) for one 6-tuple of edge bins (edge order of itertools.combinations(range(4), 2)):
+    the sum over the three splits of the four vertices into two pairs."""
+    e = {pair: x for pair, x in zip(itertools.combinations(range(4), 2), t)}
+    total = 0.0
+    for p, q in (((0, 1), (2, 3)), ((0, 2), (1, 3)), ((0, 3), (1, 2))):
+        total += xi[e[p]] * xi[e[q]]
+    return total

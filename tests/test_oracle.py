@@ -437,6 +437,61 @@ def test_4pcf_s4_folds_onto_sorted_tuples():
     assert es.sum() > 0
 
 
+# ------------------------------------------------------------------ 2pCF, disconnected 4pCF (§III.3)
+
+@pytest.mark.parametrize("seed,n,box,nb", [(51, 60, 2000, 3), (52, 120, 4000, 7)])
+def test_2pcf_matches_brute_force(seed, n, box, nb):
+    xyz = small_cloud(seed, n, box, nclump=3)
+    edges = linear_edges_sq(box // 2, nb)
+    w = 0.5 + rng_for(seed + 100).random(n)
+    cnt_b, acc_b = brute.pairs(xyz, edges, w)
+    g = oracle.Graph(xyz, edges)
+    cnt, wsum, s = g.count_2pcf(w)
+    np.testing.assert_array_equal(cnt, cnt_b)
+    np.testing.assert_array_equal(wsum, [float(x) for x in acc_b])  # exact sum, one rounding
+    assert int(cnt.sum()) == g.nnz // 2
+    assert s == 55  # max |w| near 1.49: M = fl(a * a) in [2, 4), s = 57 - 2
+    c1, w1, _ = g.count_2pcf(np.ones(n))
+    np.testing.assert_array_equal(w1, c1.astype(np.float64))
+
+
+def test_2pcf_signed_weights_are_the_landy_szalay_numerator():
+    # data weights 1/N_D and random weights -1/N_R: sum of w_i w_j over pairs = DD/N_D^2
+    # - DR/(N_D N_R) + RR/N_R^2 per bin (DR counted once per data-random pair)
+    rng = rng_for(53)
+    nd, nr = 90, 130
+    xyz = small_cloud(54, nd + nr, 3000)
+    edges = linear_edges_sq(1500, 5)
+    w = np.concatenate([np.full(nd, 1.0 / nd), np.full(nr, -1.0 / nr)])
+    cnt, wsum, _ = oracle.Graph(xyz, edges).count_2pcf(w)
+    a, b = brute.adjacency(xyz, edges)
+    dd = np.zeros(5); dr = np.zeros(5); rr = np.zeros(5)
+    for i in range(nd + nr):
+        for j in range(i + 1, nd + nr):
+            if a[i, j]:
+                (dd if j < nd else (dr if i < nd else rr))[b[i, j]] += 1
+    np.testing.assert_allclose(wsum, dd / nd**2 - dr / (nd * nr) + rr / nr**2, rtol=1e-13, atol=1e-16)
+
+
+def test_disconnected_4pcf_matches_the_pair_splits():
+    rng = rng_for(55)
+    for nb in (1, 3, 4):
+        xi = rng.normal(size=nb)
+        disc = oracle.disconnected_4pcf_s4(nb, xi)
+        bins = oracle.config_bins_s4(nb)
+        want = np.array([brute.disconnected_s4(t, xi) for t in bins])
+        np.testing.assert_allclose(disc, want, rtol=1e-15, atol=1e-15)
+        # a relabelled tuple of the same configuration gives the same value (S4 invariance)
+        for t in bins[:20]:
+            for p in rng.permutation(list(itertools.permutations(range(4))))[:5]:
+                B = np.zeros((4, 4), int)
+                for (u, v), x in zip(itertools.combinations(range(4), 2), t):
+                    B[u, v] = B[v, u] = x
+                t2 = [B[p[u], p[v]] for u, v in itertools.combinations(range(4), 2)]
+                assert brute.disconnected_s4(t2, xi) == pytest.approx(brute.disconnected_s4(t, xi), abs=1e-15)
+    np.testing.assert_allclose(oracle.disconnected_4pcf_s4(4, np.full(4, 0.3)), 3 * 0.09, rtol=1e-15)
+
+
 def test_degenerate_inputs():
     edges = linear_edges_sq(1000, 3)
     for n in (0, 1, 2):
