@@ -65,6 +65,9 @@ def lib() -> C.CDLL:
         L.gtc_num_configs_s4.restype = i64
         L.gtc_config_bins_s4.argtypes = [i32, P]
         L.gtc_config_realizable_s4.argtypes = [i32, P, P]
+        L.gtc_count_2pcf.argtypes = [P, P, P, P, C.POINTER(Stats), P]
+        L.gtc_disconnected_4pcf_s4.argtypes = [i32, P, P]
+        L.gtc_connected_4pcf_s4.argtypes = [i32, P, P, P]
         L.gtc_count_4pcf_parity.argtypes = [P, P, P, C.POINTER(Stats), P]
         L.gtc_num_configs.argtypes = [i32, i32]
         L.gtc_num_configs.restype = i64
@@ -138,6 +141,26 @@ def config_realizable_s4(nbins: int, edges_sq) -> np.ndarray:
     return mask
 
 
+def disconnected_4pcf_s4(nbins: int, xi) -> np.ndarray:
+    """Eq. (4) per S4 configuration from the binned 2pCF xi [nbins] (host)."""
+    x = np.ascontiguousarray(np.asarray(xi, dtype=np.float64))
+    out = np.empty(num_configs_s4(nbins), np.float64)
+    _check(lib().gtc_disconnected_4pcf_s4(nbins, x.ctypes.data_as(C.c_void_p),
+                                          out.ctypes.data_as(C.c_void_p)))
+    return out
+
+
+def connected_4pcf_s4(nbins: int, zeta, xi) -> np.ndarray:
+    """Eq. (5): zeta minus the disconnected part, per S4 configuration (host)."""
+    x = np.ascontiguousarray(np.asarray(xi, dtype=np.float64))
+    z = np.ascontiguousarray(np.asarray(zeta, dtype=np.float64))
+    out = np.empty(num_configs_s4(nbins), np.float64)
+    _check(lib().gtc_connected_4pcf_s4(nbins, z.ctypes.data_as(C.c_void_p),
+                                       x.ctypes.data_as(C.c_void_p),
+                                       out.ctypes.data_as(C.c_void_p)))
+    return out
+
+
 class Graph:
     """Neighbour graph on the current GPU (owned by libgtc; freed by close() or on deletion)."""
 
@@ -201,6 +224,24 @@ class Graph:
                 torch.empty(ncfg, dtype=torch.float64, device=dev)
         st = Stats()
         _check(lib().gtc_count_3pcf(self._h, _dptr(w) if w is not None else None, _dptr(counts),
+                                    _dptr(weighted) if weighted is not None else None,
+                                    C.byref(st), _stream_ptr(self._stream)))
+        return counts, weighted, st.as_dict()
+
+    def count_2pcf(self, w=None):
+        """Pairs per bin: (counts int64 [nbins] holding uint64 bits, weighted fp64 [nbins] or None,
+        stats)."""
+        import torch
+        dev = self._xyz.device
+        counts = torch.empty(self.nbins, dtype=torch.int64, device=dev)
+        weighted = None
+        if w is not None:
+            if not (w.is_cuda and w.dtype == torch.float64 and w.numel() == self.n):
+                raise TypeError("w must be a CUDA float64 tensor of length n")
+            w = w.contiguous()
+            weighted = torch.empty(self.nbins, dtype=torch.float64, device=dev)
+        st = Stats()
+        _check(lib().gtc_count_2pcf(self._h, _dptr(w) if w is not None else None, _dptr(counts),
                                     _dptr(weighted) if weighted is not None else None,
                                     C.byref(st), _stream_ptr(self._stream)))
         return counts, weighted, st.as_dict()

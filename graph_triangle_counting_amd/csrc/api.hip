@@ -13,9 +13,9 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
                       gtc_stats *st, hipStream_t s, const HubSubset *sub = nullptr);
 int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
                       hipStream_t s, bool s4);
-int64_t num_configs_s4(int nb);
-void config_bins_s4(int nb, int32_t *bins);
 void config_realizable_s4(int nb, const int64_t *edges, uint8_t *mask);
+int count_2pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
+                      gtc_stats *st, hipStream_t s);
 void free_graph_buffers(gtc_graph_s *G);
 
 static int64_t binom(int64_t n, int64_t k) {
@@ -321,6 +321,50 @@ int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_sta
 int gtc_count_4pcf_parity_s4(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
                              void *hip_stream) {
     return count_4pcf(g, d_even, d_odd, st, hip_stream, true);
+}
+
+int gtc_count_2pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d_weighted,
+                   gtc_stats *st, void *hip_stream) {
+    if (!g || !d_counts || (d_w && !d_weighted)) {
+        set_error("gtc_count_2pcf: need a graph, d_counts, and d_weighted when d_w is given");
+        return GTC_E_INVALID;
+    }
+    if (g->rebuild && !g->coords_kept) {
+        set_error("gtc_count_2pcf: the graph's windows need the coordinates");
+        return GTC_E_INVALID;
+    }
+    DeviceGuard dg(g->device);
+    if (dg.rc) return dg.rc;
+    auto t0 = std::chrono::steady_clock::now();
+    gtc_stats local{};
+    fill_graph_stats(g, &local);
+    int rc = count_2pcf_device(g, d_w, d_counts, d_weighted, &local,
+                               reinterpret_cast<hipStream_t>(hip_stream));
+    local.count_ms =
+        std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+    if (rc == GTC_OK && st) *st = local;
+    return rc;
+}
+
+int gtc_disconnected_4pcf_s4(int32_t nbins, const double *h_xi, double *h_disc) {
+    if (nbins < 1 || nbins > GTC_MAX_BINS_4PCF || !h_xi || !h_disc) {
+        set_error("gtc_disconnected_4pcf_s4: nbins in [1, %d], h_xi and h_disc non-NULL",
+                  GTC_MAX_BINS_4PCF);
+        return GTC_E_INVALID;
+    }
+    disconnected_4pcf_s4(nbins, h_xi, h_disc);
+    return GTC_OK;
+}
+
+int gtc_connected_4pcf_s4(int32_t nbins, const double *h_zeta, const double *h_xi,
+                          double *h_conn) {
+    if (!h_zeta) {
+        set_error("gtc_connected_4pcf_s4: h_zeta is NULL");
+        return GTC_E_INVALID;
+    }
+    GTC_TRY(gtc_disconnected_4pcf_s4(nbins, h_xi, h_conn));
+    for (int64_t c = 0; c < num_configs_s4(nbins); ++c) h_conn[c] = h_zeta[c] - h_conn[c];
+    return GTC_OK;
 }
 
 int64_t gtc_num_configs_s4(int32_t nbins) {

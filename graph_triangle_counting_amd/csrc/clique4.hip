@@ -13,6 +13,7 @@
 // nondecreasing 6-tuples), and the parity sign: vertices ordered by the sum of their squared edge
 // lengths, exact int64 signed volume (r01 x r02) . r03 (Eq.(3)), zero for a tie or zero volume.
 #include <algorithm>
+#include <thread>
 #include <vector>
 
 #include "gtc_internal.h"
@@ -343,12 +344,21 @@ int64_t num_configs_s4(int nb) {
     return (k * k * k * k * k * k + 9 * k * k * k * k + 14 * k * k) / 24;  // Burnside over S4
 }
 
-// canonical tuples in rank order (host)
+// canonical tuples in rank order (host; the canonical test runs on all hardware threads)
 void config_bins_s4(int nb, int32_t *bins) {
     const int64_t nk = num_s4_keys(nb);
+    std::vector<uint8_t> canon(nk);
+    const int nt = std::max(1u, std::min(32u, std::thread::hardware_concurrency()));
+    std::vector<std::thread> pool;
+    for (int t = 0; t < nt; ++t)
+        pool.emplace_back([&, t]() {
+            for (int64_t key = t; key < nk; key += nt)
+                canon[key] = s4_canonical_key((uint32_t)key, nb) == (uint32_t)key;
+        });
+    for (auto &th : pool) th.join();
     int64_t r = 0;
     for (int64_t key = 0; key < nk; ++key) {
-        if (s4_canonical_key((uint32_t)key, nb) != (uint32_t)key) continue;
+        if (!canon[key]) continue;
         int64_t k2 = key;
         for (int e = 5; e >= 0; --e) {
             bins[6 * r + e] = (int32_t)(k2 % nb);

@@ -325,6 +325,12 @@ namespace gtc {
 // run again.  Needs the sorted coordinates.
 int emit_window(const gtc_graph_s *G, int64_t w, int32_t *col, uint8_t *bin, hipStream_t s);
 
+// S4 configurations of the 4pCF (clique4.hip): count, canonical tuples [n][6] in rank order
+int64_t num_configs_s4(int nb);
+void config_bins_s4(int nb, int32_t *bins);
+// Eq. (4) per S4 configuration from the binned 2pCF (twopoint.hip)
+void disconnected_4pcf_s4(int nb, const double *xi, double *disc);
+
 // A hub list to count instead of the graph's own (one-window graphs), with its totals.
 struct HubSubset {
     const int32_t *hubs = nullptr;  // device, internal labels, each able to close a triangle

@@ -174,6 +174,30 @@ int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_sta
  *     4 bins); h_edges_sq as gtc_build_graph.  Host only. */
 int gtc_count_4pcf_parity_s4(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
                              void *hip_stream);
+
+/* The 2pCF on the graph's pairs (§II.1; the internal 2pCF of §III.3): every pair (each edge once)
+ * counted in its bin, and with weights the exact sums of w_i w_j.  Each product p = fl(w_i * w_j)
+ * is scaled to the integer q = rint(p * 2^s), s = 57 - e for M = fl(a * a) = f * 2^e, f in
+ * [0.5, 1), a = max |w| (s = 0 if M == 0); the q are summed exactly and each bin is rounded once.
+ * With data weights summing to +1 and random weights to -1, the sums are the Landy-Szalay
+ * numerator DD - 2DR + RR, so xi = sum / RR.
+ *   d_w        device double [n] in original labels, or NULL.
+ *   d_counts   device uint64 [nbins] (overwritten); d_weighted device double [nbins] or NULL.
+ *   st         stats: kernel_ms summed over windows, weight_scale = s, q_alg_bytes.
+ * Works on every csr_mode (out-of-core windows are uploaded or emitted again one at a time).
+ * GTC_E_INVALID for a non-finite weight. */
+int gtc_count_2pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d_weighted,
+                   gtc_stats *st, void *hip_stream);
+
+/* The disconnected 4pCF, Eq. (4), per S4 configuration from the binned 2pCF (host only):
+ * h_disc[c] = xi(b01) xi(b23) + xi(b02) xi(b13) + xi(b03) xi(b12) for configuration c's canonical
+ * tuple, the sum over the three splits of the four vertices into two pairs.
+ *   h_xi host double [nbins]; h_disc host double [gtc_num_configs_s4(nbins)].
+ * gtc_connected_4pcf_s4 returns Eq. (5), h_conn = h_zeta - disc, for a full 4pCF h_zeta of the
+ * same shape (the parity-even channel; the odd channel is connected as it is). */
+int gtc_disconnected_4pcf_s4(int32_t nbins, const double *h_xi, double *h_disc);
+int gtc_connected_4pcf_s4(int32_t nbins, const double *h_zeta, const double *h_xi,
+                          double *h_conn);
 int64_t gtc_num_configs_s4(int32_t nbins);
 int gtc_config_bins_s4(int32_t nbins, int32_t *h_bins);
 int gtc_config_realizable_s4(int32_t nbins, const int64_t *h_edges_sq, uint8_t *h_mask);

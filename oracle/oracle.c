@@ -644,52 +644,68 @@ static void tuple_of_key(size_t key, int nb, int t[6]) {
     }
 }
 
-/* rank of every 6-tuple's configuration: canonical tuples numbered in lexicographic order */
-static int32_t *make_rank_s4(int nb, int64_t *ncfg_out) {
+/* canonical key of every 6-tuple key (all threads), then the configuration ranks: canonical keys
+ * numbered in key (lexicographic) order */
+static uint32_t *make_canon_s4(int nb, size_t *sz_out) {
     size_t sz = 1;
     for (int k = 0; k < 6; k++) sz *= (size_t)nb;
+    uint32_t *c = (uint32_t *)malloc(sizeof(uint32_t) * sz);
+    if (!c) return NULL;
+    #pragma omp parallel for schedule(static)
+    for (int64_t key = 0; key < (int64_t)sz; key++) {
+        int v[6], cv[6];
+        tuple_of_key((size_t)key, nb, v);
+        s4_canonical(v, cv);
+        c[key] = (uint32_t)tuple_key(cv, nb);
+    }
+    *sz_out = sz;
+    return c;
+}
+
+static int32_t *make_rank_s4(int nb, int64_t *ncfg_out) {
+    size_t sz = 0;
+    uint32_t *c = make_canon_s4(nb, &sz);
+    if (!c) return NULL;
     int32_t *t = (int32_t *)malloc(sizeof(int32_t) * sz);
-    if (!t) return NULL;
+    if (!t) {
+        free(c);
+        return NULL;
+    }
     int32_t r = 0;
-    for (size_t key = 0; key < sz; key++) { /* canonical tuples first, in key (lexicographic) order */
-        int v[6], c[6];
-        tuple_of_key(key, nb, v);
-        s4_canonical(v, c);
-        t[key] = tuple_key(c, nb) == key ? r++ : -1;
-    }
-    for (size_t key = 0; key < sz; key++) {
-        if (t[key] >= 0) continue;
-        int v[6], c[6];
-        tuple_of_key(key, nb, v);
-        s4_canonical(v, c);
-        t[key] = t[tuple_key(c, nb)];
-    }
+    for (size_t key = 0; key < sz; key++) t[key] = c[key] == key ? r++ : -1;
+    #pragma omp parallel for schedule(static)
+    for (int64_t key = 0; key < (int64_t)sz; key++)
+        if (t[key] < 0) t[key] = t[c[key]];
+    free(c);
     if (ncfg_out) *ncfg_out = r;
     return t;
 }
 
 int64_t oracle_num_configs_s4(int32_t nbins) {
     if (nbins < 1 || nbins > ORACLE_MAX_BINS_4PCF) return 0;
+    size_t sz = 0;
+    uint32_t *c = make_canon_s4(nbins, &sz);
+    if (!c) return ORACLE_E_NOMEM;
     int64_t n = 0;
-    int32_t *t = make_rank_s4(nbins, &n);
-    if (!t) return ORACLE_E_NOMEM;
-    free(t);
+    for (size_t key = 0; key < sz; key++) n += c[key] == key;
+    free(c);
     return n;
 }
 
 int oracle_config_bins_s4(int32_t nb, int32_t *bins) {
     if (nb < 1 || nb > ORACLE_MAX_BINS_4PCF || !bins) return ORACLE_E_INVALID;
-    size_t sz = 1;
-    for (int k = 0; k < 6; k++) sz *= (size_t)nb;
+    size_t sz = 0;
+    uint32_t *c = make_canon_s4(nb, &sz);
+    if (!c) return ORACLE_E_NOMEM;
     int64_t r = 0;
     for (size_t key = 0; key < sz; key++) {
-        int v[6], c[6];
+        if (c[key] != key) continue;
+        int v[6];
         tuple_of_key(key, nb, v);
-        s4_canonical(v, c);
-        if (tuple_key(c, nb) != key) continue;
         for (int e = 0; e < 6; e++) bins[6 * r + e] = v[e];
         r++;
     }
+    free(c);
     return 0;
 }
 

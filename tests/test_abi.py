@@ -68,6 +68,18 @@ def test_s4_configuration_tables_match_the_oracle():
     assert int(gtc.config_realizable_s4(4, cases[0][1]).sum()) == 178
 
 
+def test_disconnected_and_connected_4pcf_match_the_oracle():
+    import oracle
+    rng = np.random.default_rng(7)
+    for nb in (1, 4, 8):
+        xi = rng.normal(size=nb)
+        d = gtc.disconnected_4pcf_s4(nb, xi)
+        np.testing.assert_array_equal(d, oracle.disconnected_4pcf_s4(nb, xi))
+        zeta = rng.normal(size=d.size)
+        np.testing.assert_array_equal(gtc.connected_4pcf_s4(nb, zeta, xi), zeta - d)
+    assert gtc.lib().gtc_disconnected_4pcf_s4(17, None, None) == gtc.GTC_E_INVALID
+
+
 def test_build_rejects_bad_arguments_without_gpu():
     fake = C.c_void_p(0x1000)  # never dereferenced: every case fails before any device work
     cases = [

@@ -144,6 +144,46 @@ def test_3pcf_hub_subsets(gpu_available):
     gt.close()
 
 
+@pytest.mark.parametrize("layout", ["packed", "split"])
+@pytest.mark.parametrize("kind,seed,n,r,nb", [("clustered", 71, 30_000, 12_000, 12),
+                                              ("uniform", 72, 20_000, 40_000, 30)])
+def test_2pcf_matches_oracle(gpu_available, monkeypatch, layout, kind, seed, n, r, nb):
+    import torch
+    if layout == "split":
+        monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
+    xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 60, 2500)
+    edges = linear_edges_sq(r, nb)
+    rng = rng_for(seed + 1)
+    # signed weights of the data-minus-random estimator: data +1/N_D, randoms -1/N_R
+    nd = n // 3
+    w = np.where(np.arange(n) < nd, 1.0 / nd, -1.0 / (n - nd)) * (0.5 + rng.random(n))
+    g = gtc.Graph(to_gpu(xyz), edges)
+    c, ws, st = g.count_2pcf(torch.from_numpy(w).cuda())
+    c0, _, _ = g.count_2pcf()
+    g.close()
+    og = oracle.Graph(xyz, edges)
+    oc, ows, s = og.count_2pcf(w)
+    np.testing.assert_array_equal(c.cpu().numpy().view(np.uint64), oc)
+    np.testing.assert_array_equal(c0.cpu().numpy().view(np.uint64), oc)
+    np.testing.assert_array_equal(ws.cpu().numpy(), ows)
+    assert st["weight_scale"] == s and int(oc.sum()) == og.nnz // 2
+
+
+@pytest.mark.parametrize("csr_mode", ["device", "host", "rebuild"])
+def test_2pcf_on_tiled_graphs(gpu_available, csr_mode):
+    import torch
+    xyz = clustered(73, 25_000, 60, 2500)
+    edges = linear_edges_sq(12_000, 10)
+    w = 0.5 + rng_for(74).random(25_000)
+    oc, ows, _ = oracle.Graph(xyz, edges).count_2pcf(w)
+    g = gtc.Graph(to_gpu(xyz), edges, tile_bytes=4 * int(oc.sum()) // 5, csr_mode=csr_mode)
+    assert g.stats()["windows"] > 1
+    c, ws, _ = g.count_2pcf(torch.from_numpy(w).cuda())
+    g.close()
+    np.testing.assert_array_equal(c.cpu().numpy().view(np.uint64), oc)
+    np.testing.assert_array_equal(ws.cpu().numpy(), ows)
+
+
 def test_3pcf_c1_full(gpu_available):
     cfg = workloads.get("C1")
     xyz, w = cfg.generate()
