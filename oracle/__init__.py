@@ -46,6 +46,7 @@ def _load():
         lib.oracle_config_realizable_s4.argtypes = [i32, P, P]
         lib.oracle_count_4pcf_parity_s4.argtypes = [P, P, i64, i32, P, P, P]
         lib.oracle_count_2pcf.argtypes = [P, P, P, P, P]
+        lib.oracle_count_4pcf_weighted.argtypes = [P, P, P, i32, i32, P, P, P, P, P]
         lib.oracle_disconnected_4pcf_s4.argtypes = [i32, P, P]
         _lib = lib
     return _lib
@@ -187,6 +188,21 @@ class Graph:
                 v -= 1 << 128
             sums.append(v)
         return counts, sums, int(s.value)
+
+    def count_4pcf_weighted(self, w: np.ndarray, s4: bool = False, nthreads: int = 0):
+        """(even uint64, odd int64, even_w fp64, odd_w fp64 [n_cfg], scale s)."""
+        ncfg = num_configs_s4(self.nbins) if s4 else num_configs(4, self.nbins)
+        even = np.zeros(ncfg, np.uint64)
+        odd = np.zeros(ncfg, np.int64)
+        ew = np.zeros(ncfg, np.float64)
+        ow = np.zeros(ncfg, np.float64)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        sc = C.c_int32(0)
+        rc = _lib.oracle_count_4pcf_weighted(self._h, _ptr(self.xyz), _ptr(w), int(s4), nthreads,
+                                             _ptr(even), _ptr(odd), _ptr(ew), _ptr(ow), C.byref(sc))
+        if rc:
+            raise ValueError(f"oracle_count_4pcf_weighted failed ({rc})")
+        return even, odd, ew, ow, sc.value
 
     def count_2pcf(self, w: np.ndarray | None = None):
         """Pairs per bin: (counts uint64 [nbins], weighted fp64 [nbins] or None, scale s)."""

@@ -764,18 +764,52 @@ int oracle_config_realizable_s4(int32_t nb, const int64_t *edges, uint8_t *mask)
     return 0;
 }
 
+/* Scale of the exact 4pCF weighted sums: s = 57 - e with M = fl(fl(fl(a*a)*a)*a) = f * 2^e for
+ * a = max|w|, so |q| < 2^57 for every product of four weights (s = 0 if M == 0). */
+static int weight_scale4(const double *w, int64_t n) {
+    double a = 0.0;
+    for (int64_t i = 0; i < n; i++) a = fmax(a, fabs(w[i]));
+    volatile double a2 = a * a;
+    volatile double a3 = a2 * a;
+    volatile double m = a3 * a;
+    if (m == 0.0) return 0;
+    int e;
+    frexp(m, &e);
+    return 57 - e;
+}
+
+/* q = rint(p * 2^s) for p = fl(fl(fl(w1*w2)*w3)*w4), the four weights ascending. */
+static int64_t tetra_q(const double *wv, int s) {
+    double v[4] = {wv[0], wv[1], wv[2], wv[3]};
+    for (int x = 1; x < 4; x++)
+        for (int y = x; y > 0 && v[y - 1] > v[y]; y--) {
+            double t = v[y]; v[y] = v[y - 1]; v[y - 1] = t;
+        }
+    volatile double p12 = v[0] * v[1];
+    volatile double p123 = p12 * v[2];
+    volatile double p = p123 * v[3];
+    return (int64_t)rint(ldexp(p, s));
+}
+
 static int count_4pcf_impl(const oracle_graph *g, const int32_t *xyz, int64_t hub_stride,
                            int32_t nthreads, int s4, uint64_t *even, int64_t *odd,
-                           uint64_t *cliques_out) {
+                           uint64_t *cliques_out, const double *w, __int128 *acc_e,
+                           __int128 *acc_o, int *scale_out) {
     if (!g || !xyz || !even || !odd || hub_stride < 1) return ORACLE_E_INVALID;
+    if (w && (!acc_e || !acc_o || !weights_finite(w, g->n))) return ORACLE_E_INVALID;
     const int nb = g->nb;
     if (nb > ORACLE_MAX_BINS_4PCF) return ORACLE_E_INVALID;
     int64_t ncfg = oracle_num_configs(4, nb);
     int32_t *rank6 = s4 ? make_rank_s4(nb, &ncfg) : make_rank6(nb);
     if (!rank6) return ORACLE_E_NOMEM;
+    const int sc = w ? weight_scale4(w, g->n) : 0;
     int nt = set_threads(nthreads);
     memset(even, 0, sizeof(uint64_t) * (size_t)ncfg);
     memset(odd, 0, sizeof(int64_t) * (size_t)ncfg);
+    if (w) {
+        memset(acc_e, 0, sizeof(__int128) * (size_t)ncfg);
+        memset(acc_o, 0, sizeof(__int128) * (size_t)ncfg);
+    }
     uint64_t cliques = 0;
     int fail = 0;
 
@@ -783,7 +817,9 @@ static int count_4pcf_impl(const oracle_graph *g, const int32_t *xyz, int64_t hu
     {
         uint64_t *my_e = (uint64_t *)calloc((size_t)ncfg, sizeof(uint64_t));
         int64_t *my_o = (int64_t *)calloc((size_t)ncfg, sizeof(int64_t));
-        if (!my_e || !my_o) fail = 1;
+        __int128 *my_ae = w ? (__int128 *)calloc((size_t)ncfg, sizeof(__int128)) : NULL;
+        __int128 *my_ao = w ? (__int128 *)calloc((size_t)ncfg, sizeof(__int128)) : NULL;
+        if (!my_e || !my_o || (w && (!my_ae || !my_ao))) fail = 1;
         #pragma omp for schedule(dynamic, 64)
         for (int64_t i = 0; i < g->n; i++) {
             if (fail || i % hub_stride) continue;
@@ -811,8 +847,15 @@ static int count_4pcf_impl(const oracle_graph *g, const int32_t *xyz, int64_t hu
                             if (!s4) sort_small_int(v, 6); /* S4: the table maps every tuple */
                             const int32_t c = rank6[tuple_key(v, nb)];
                             const int32_t vv[4] = {(int32_t)i, j1, j2, ha};
+                            const int sg = parity_sign(xyz, vv);
                             my_e[c]++;
-                            my_o[c] += parity_sign(xyz, vv);
+                            my_o[c] += sg;
+                            if (w) {
+                                const double wv[4] = {w[i], w[j1], w[j2], w[ha]};
+                                const int64_t q = tetra_q(wv, sc);
+                                my_ae[c] += q;
+                                my_ao[c] += (__int128)sg * q;
+                            }
                             cliques++;
                             al++; be++; ga++;
                         } else {
@@ -834,24 +877,56 @@ static int count_4pcf_impl(const oracle_graph *g, const int32_t *xyz, int64_t hu
                     even[c] += my_e[c];
                     odd[c] += my_o[c];
                 }
+            if (my_ae && my_ao)
+                for (int64_t c = 0; c < ncfg; c++) {
+                    acc_e[c] += my_ae[c];
+                    acc_o[c] += my_ao[c];
+                }
         }
         free(my_e);
         free(my_o);
+        free(my_ae);
+        free(my_ao);
     }
     free(rank6);
     if (fail) return ORACLE_E_NOMEM;
     if (cliques_out) *cliques_out = cliques;
+    if (scale_out) *scale_out = sc;
     return 0;
 }
 
 int oracle_count_4pcf_parity(const oracle_graph *g, const int32_t *xyz, int64_t hub_stride,
                              int32_t nthreads, uint64_t *even, int64_t *odd,
                              uint64_t *cliques_out) {
-    return count_4pcf_impl(g, xyz, hub_stride, nthreads, 0, even, odd, cliques_out);
+    return count_4pcf_impl(g, xyz, hub_stride, nthreads, 0, even, odd, cliques_out, NULL, NULL,
+                           NULL, NULL);
 }
 
 int oracle_count_4pcf_parity_s4(const oracle_graph *g, const int32_t *xyz, int64_t hub_stride,
                                 int32_t nthreads, uint64_t *even, int64_t *odd,
                                 uint64_t *cliques_out) {
-    return count_4pcf_impl(g, xyz, hub_stride, nthreads, 1, even, odd, cliques_out);
+    return count_4pcf_impl(g, xyz, hub_stride, nthreads, 1, even, odd, cliques_out, NULL, NULL,
+                           NULL, NULL);
+}
+
+int oracle_count_4pcf_weighted(const oracle_graph *g, const int32_t *xyz, const double *w,
+                               int32_t s4, int32_t nthreads, uint64_t *even, int64_t *odd,
+                               double *even_w, double *odd_w, int32_t *scale_out) {
+    if (!g || !w || !even_w || !odd_w) return ORACLE_E_INVALID;
+    const int64_t ncfg = s4 ? oracle_num_configs_s4(g->nb) : oracle_num_configs(4, g->nb);
+    if (ncfg <= 0) return ORACLE_E_INVALID;
+    __int128 *ae = (__int128 *)malloc(sizeof(__int128) * (size_t)ncfg);
+    __int128 *ao = (__int128 *)malloc(sizeof(__int128) * (size_t)ncfg);
+    int sc = 0, rc = ORACLE_E_NOMEM;
+    if (ae && ao)
+        rc = count_4pcf_impl(g, xyz, 1, nthreads, s4 ? 1 : 0, even, odd, NULL, w, ae, ao, &sc);
+    if (!rc)
+        for (int64_t c = 0; c < ncfg; c++) { /* one rounding of each exact sum */
+            even_w[c] = ldexp((double)ae[c], -sc);
+            odd_w[c] = ldexp((double)ao[c], -sc);
+        }
+    if (!rc && scale_out) *scale_out = sc;
+    free(ae);
+    free(ao);
+    return rc;
 }

@@ -108,6 +108,15 @@ int oracle_count_4pcf_parity_s4(const oracle_graph *g, const int32_t *xyz, int64
                                 int32_t nthreads, uint64_t *even, int64_t *odd,
                                 uint64_t *cliques_out);
 
+/* Weighted parity 4pCF: as oracle_count_4pcf_parity (s4 = 0) or _s4 (s4 != 0), all hubs, and in
+ * addition even_w / odd_w [n_cfg]: the sums over tetrahedra of p = fl(fl(fl(w1*w2)*w3)*w4), the
+ * four weights ascending (no fused multiply-add), and of sign(V) * p.  Each p is scaled to
+ * q = rint(p * 2^s), the q are summed exactly and each sum is rounded once; s = 57 - e for
+ * M = fl(fl(fl(a*a)*a)*a) = f * 2^e, a = max|w|. */
+int oracle_count_4pcf_weighted(const oracle_graph *g, const int32_t *xyz, const double *w,
+                               int32_t s4, int32_t nthreads, uint64_t *even, int64_t *odd,
+                               double *even_w, double *odd_w, int32_t *scale_out);
+
 /* 2pCF: pairs of the graph per bin, each once: counts [nbins]; with w, weighted [nbins] receives
  * the sums of w_i w_j, each product p = fl(w_i * w_j) scaled to q = rint(p * 2^s), summed exactly
  * and rounded once (s = 57 - e for M = fl(a * a) = f * 2^e, f in [0.5, 1), a = max|w|; s = 0 if

@@ -150,3 +150,27 @@ def disconnected_s4(t, xi) -> float:
     for p, q in (((0, 1), (2, 3)), ((0, 2), (1, 3)), ((0, 3), (1, 2))):
         total += xi[e[p]] * xi[e[q]]
     return total
+
+
+def cliques4_weighted(xyz: np.ndarray, edges, w, s4: bool = False, s: int | None = None):
+    """Exact sums over every pairwise-adjacent 4-set of p = ((w1 w2) w3) w4 (weights ascending, each
+    product rounded to a double) and of chirality * p: (even, odd) lists of Fractions.  With s, each
+    p is first quantised to round_half_even(p * 2^s) / 2^s."""
+    from fractions import Fraction
+    a, b = adjacency(xyz, edges)
+    nb = len(edges) - 1
+    idx = s4_index(nb) if s4 else config_index(nb, 6)
+    ev = [Fraction(0)] * len(idx)
+    od = [Fraction(0)] * len(idx)
+    n = xyz.shape[0]
+    for q in itertools.combinations(range(n), 4):
+        if all(a[u, v] for u, v in itertools.combinations(q, 2)):
+            bins = [int(b[u, v]) for u, v in itertools.combinations(q, 2)]
+            c = idx[s4_canonical(bins) if s4 else tuple(sorted(bins))]
+            v = sorted(float(w[x]) for x in q)
+            p = Fraction(((v[0] * v[1]) * v[2]) * v[3])
+            if s is not None:
+                p = Fraction(round(p * 2**s), 2**s)  # Fraction rounding: half to even
+            ev[c] += p
+            od[c] += chirality([xyz[x] for x in q]) * p
+    return ev, od

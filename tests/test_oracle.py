@@ -437,6 +437,44 @@ def test_4pcf_s4_folds_onto_sorted_tuples():
     assert es.sum() > 0
 
 
+@pytest.mark.parametrize("s4", [False, True])
+@pytest.mark.parametrize("seed,n,box,nb", [(45, 30, 2000, 2), (46, 36, 3000, 3)])
+def test_4pcf_weighted_matches_brute_force(seed, n, box, nb, s4):
+    xyz = small_cloud(seed, n, box, nclump=2)
+    edges = linear_edges_sq(box // 2, nb)
+    rng = rng_for(seed + 100)
+    w = np.where(rng.random(n) < 0.3, -1.0, 1.0) * (0.5 + rng.random(n))  # signed weights
+    import math
+    a = float(np.abs(w).max())
+    s_want = 57 - math.frexp(((a * a) * a) * a)[1]
+    ev_b, od_b = brute.cliques4_weighted(xyz, edges, w, s4, s=s_want)
+    g = oracle.Graph(xyz, edges)
+    e, o, ew, ow, s = g.count_4pcf_weighted(w, s4=s4)
+    assert s == s_want
+    np.testing.assert_array_equal(ew, [float(x) for x in ev_b])  # exact quantised sums
+    np.testing.assert_array_equal(ow, [float(x) for x in od_b])
+    # against the unquantised products: each term moves by at most 2^-(s+1)
+    ev_x, od_x = brute.cliques4_weighted(xyz, edges, w, s4)
+    ncl = max(int(e.sum()), 1)
+    np.testing.assert_allclose(ew, [float(x) for x in ev_x], rtol=0, atol=ncl * 2.0 ** -s)
+    np.testing.assert_allclose(ow, [float(x) for x in od_x], rtol=0, atol=ncl * 2.0 ** -s)
+    e0, o0, _ = g.count_4pcf_parity(s4=s4)
+    np.testing.assert_array_equal(e, e0)
+    np.testing.assert_array_equal(o, o0)
+    assert e.sum() > 0
+
+
+def test_4pcf_weighted_constant_weights():
+    xyz, edges = uniform_graph(seed=47, n=2000, r=30_000, nb=4)
+    g = oracle.Graph(xyz, edges)
+    e, o, ew, ow, _ = g.count_4pcf_weighted(np.ones(2000))
+    np.testing.assert_array_equal(ew, e.astype(np.float64))
+    np.testing.assert_array_equal(ow, o.astype(np.float64))
+    _, _, ew2, ow2, _ = g.count_4pcf_weighted(np.full(2000, 2.0))
+    np.testing.assert_array_equal(ew2, 16.0 * e)
+    np.testing.assert_array_equal(ow2, 16.0 * o)
+
+
 # ------------------------------------------------------------------ 2pCF, disconnected 4pCF (§III.3)
 
 @pytest.mark.parametrize("seed,n,box,nb", [(51, 60, 2000, 3), (52, 120, 4000, 7)])
