@@ -69,6 +69,12 @@ def lib() -> C.CDLL:
         L.gtc_disconnected_4pcf_s4.argtypes = [i32, P, P]
         L.gtc_connected_4pcf_s4.argtypes = [i32, P, P, P]
         L.gtc_count_4pcf_parity.argtypes = [P, P, P, C.POINTER(Stats), P]
+        L.gtc_count_4pcf_weighted.argtypes = [P, P, i32, P, P, P, P, C.POINTER(Stats), P]
+        L.gtc_linear_edges_sq.argtypes = [i64, i64, i32, P]
+        L.gtc_compute_3pcf.argtypes = [P, i64, P, P, i64, P, P, i32, C.POINTER(Options), P, P, P,
+                                       C.POINTER(Stats), P]
+        L.gtc_compute_4pcf.argtypes = [P, i64, P, P, i64, P, P, i32, C.POINTER(Options), P, P, P,
+                                       P, C.POINTER(Stats), P]
         L.gtc_num_configs.argtypes = [i32, i32]
         L.gtc_num_configs.restype = i64
         L.gtc_config_bins.argtypes = [i32, i32, P]
@@ -289,6 +295,27 @@ class Graph:
         _check(fn(self._h, _dptr(even), _dptr(odd), C.byref(st), _stream_ptr(self._stream)))
         return even, odd, st.as_dict()
 
+    def count_4pcf_weighted(self, w, s4: bool = False):
+        """Weighted parity 4pCF: (even, odd as count_4pcf_parity; even_w, odd_w fp64 [n_cfg] on
+        the GPU, the exact sums of the four-weight products and of their signed-volume signs;
+        stats, weight_scale = s)."""
+        import torch
+        if not (isinstance(w, torch.Tensor) and w.is_cuda and w.dtype == torch.float64
+                and w.numel() == self.n):
+            raise TypeError("w must be a CUDA float64 tensor of length n")
+        w = w.contiguous()
+        ncfg = num_configs_s4(self.nbins) if s4 else num_configs(4, self.nbins)
+        dev = self._xyz.device
+        even = torch.empty(ncfg, dtype=torch.int64, device=dev)
+        odd = torch.empty(ncfg, dtype=torch.int64, device=dev)
+        ew = torch.empty(ncfg, dtype=torch.float64, device=dev)
+        ow = torch.empty(ncfg, dtype=torch.float64, device=dev)
+        st = Stats()
+        _check(lib().gtc_count_4pcf_weighted(self._h, _dptr(w), int(bool(s4)), _dptr(even),
+                                             _dptr(odd), _dptr(ew), _dptr(ow), C.byref(st),
+                                             _stream_ptr(self._stream)))
+        return even, odd, ew, ow, st.as_dict()
+
     def export(self):
         """Forward CSR in internal labels plus the internal -> original permutation (host)."""
         st = self.stats()
@@ -304,6 +331,111 @@ class Graph:
 
 def build_graph(xyz, edges_sq, **kw) -> Graph:
     return Graph(xyz, edges_sq, **kw)
+
+
+def linear_edges_sq(r_min: int, r_max: int, nbins: int) -> np.ndarray:
+    """Integer squared edges of nbins equal bins in r from r_min to r_max (grid units)."""
+    e = np.empty(int(nbins) + 1, np.int64)
+    _check(lib().gtc_linear_edges_sq(int(r_min), int(r_max), int(nbins),
+                                     e.ctypes.data_as(C.c_void_p)))
+    return e
+
+
+class Result3pcf:
+    """compute_3pcf's result: zeta, NNN, RRR per configuration (fp64 host arrays); bins
+    [n_cfg][3] the nondecreasing bin triple of each configuration; r1, r2, r3 its bin centres
+    (midpoints in r, grid units); edges_sq the squared edges; stats."""
+
+
+class Result4pcf:
+    """compute_4pcf's result: zeta_even, zeta_odd, zeta_conn per S4 configuration, xi per bin
+    (fp64 host arrays); bins [n_cfg][6] the canonical edge-bin tuple (edge order 01, 02, 03, 12,
+    13, 23); r1..r6 their bin centres; realizable the Cayley-Menger mask of the bin centres;
+    edges_sq; stats."""
+
+
+def _catalogue(xyz, w, name):
+    import torch
+    if not (isinstance(xyz, torch.Tensor) and xyz.is_cuda and xyz.dtype == torch.int32
+            and xyz.dim() == 2 and xyz.shape[1] == 3):
+        raise TypeError(f"{name} positions must be a CUDA int32 tensor of shape [n, 3]")
+    xyz = xyz.contiguous()
+    if w is not None:
+        if not (isinstance(w, torch.Tensor) and w.is_cuda and w.dtype == torch.float64
+                and w.numel() == xyz.shape[0]):
+            raise TypeError(f"{name} weights must be a CUDA float64 tensor of length n")
+        w = w.contiguous()
+    return xyz, w
+
+
+def _estimator_args(pos_data, w_data, pos_rand, w_rand, rmin, rmax, nbins, edges_sq,
+                    tile_bytes, csr_mode):
+    xd, wd = _catalogue(pos_data, w_data, "data")
+    xr, wr = _catalogue(pos_rand, w_rand, "random")
+    if edges_sq is None:
+        edges_sq = linear_edges_sq(rmin, rmax, nbins)
+    e = np.ascontiguousarray(np.asarray(edges_sq, dtype=np.int64))
+    opt = Options(int(tile_bytes), CSR_MODES[csr_mode or "device"], 0)
+    return xd, wd, xr, wr, e, opt
+
+
+def _centres(e: np.ndarray) -> np.ndarray:
+    r = np.sqrt(e.astype(np.float64))
+    return 0.5 * (r[:-1] + r[1:])
+
+
+def compute_3pcf(pos_data, w_data, pos_rand, w_rand, rmin=None, rmax=None, nbins=None,
+                 edges_sq=None, tile_bytes: int = 0, csr_mode: str | None = None,
+                 stream=None) -> Result3pcf:
+    """The 3pCF estimator zeta = NNN / RRR over one graph of data and randoms.  Positions are
+    CUDA int32 [n, 3] grid coordinates, weights CUDA float64 [n] or None (unit); the bins are
+    equal in r from rmin to rmax (grid units), or given as integer squared edges."""
+    xd, wd, xr, wr, e, opt = _estimator_args(pos_data, w_data, pos_rand, w_rand, rmin, rmax,
+                                             nbins, edges_sq, tile_bytes, csr_mode)
+    nb = e.size - 1
+    ncfg = num_configs(3, nb)
+    zeta, nnn, rrr = (np.empty(ncfg, np.float64) for _ in range(3))
+    st = Stats()
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    _check(lib().gtc_compute_3pcf(_dptr(xd) if xd.shape[0] else None, xd.shape[0],
+                                  _dptr(wd) if wd is not None else None, _dptr(xr), xr.shape[0],
+                                  _dptr(wr) if wr is not None else None, p(e), nb, C.byref(opt),
+                                  p(zeta), p(nnn), p(rrr), C.byref(st), _stream_ptr(stream)))
+    r = Result3pcf()
+    r.zeta, r.NNN, r.RRR, r.edges_sq, r.stats = zeta, nnn, rrr, e, st.as_dict()
+    r.bins = config_bins(3, nb)
+    c = _centres(e)
+    r.r1, r.r2, r.r3 = (c[r.bins[:, k]] for k in range(3))
+    return r
+
+
+def compute_4pcf(pos_data, w_data, pos_rand, w_rand, rmin=None, rmax=None, nbins=None,
+                 edges_sq=None, parity: bool = True, tile_bytes: int = 0,
+                 csr_mode: str | None = None, stream=None) -> Result4pcf:
+    """The 4pCF estimator per S4 configuration: zeta_even = NNNN_even / RRRR, zeta_odd =
+    NNNN_odd / RRRR, the internal xi = NN / RR and the connected zeta_conn = zeta_even -
+    disc(xi).  Arguments as compute_3pcf; nbins <= 16.  Both channels come from one enumeration,
+    so parity=False only drops zeta_odd from the result."""
+    xd, wd, xr, wr, e, opt = _estimator_args(pos_data, w_data, pos_rand, w_rand, rmin, rmax,
+                                             nbins, edges_sq, tile_bytes, csr_mode)
+    nb = e.size - 1
+    ncfg = num_configs_s4(nb)
+    ze, zo, zc = (np.empty(ncfg, np.float64) for _ in range(3))
+    xi = np.empty(nb, np.float64)
+    st = Stats()
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    _check(lib().gtc_compute_4pcf(_dptr(xd) if xd.shape[0] else None, xd.shape[0],
+                                  _dptr(wd) if wd is not None else None, _dptr(xr), xr.shape[0],
+                                  _dptr(wr) if wr is not None else None, p(e), nb, C.byref(opt),
+                                  p(ze), p(zo), p(zc), p(xi), C.byref(st), _stream_ptr(stream)))
+    r = Result4pcf()
+    r.zeta_even, r.zeta_odd, r.zeta_conn, r.xi = ze, (zo if parity else None), zc, xi
+    r.edges_sq, r.stats = e, st.as_dict()
+    r.bins = config_bins_s4(nb)
+    c = _centres(e)
+    r.r1, r.r2, r.r3, r.r4, r.r5, r.r6 = (c[r.bins[:, k]] for k in range(6))
+    r.realizable = config_realizable_s4(nb, e).astype(bool)
+    return r
 
 
 def header_functions() -> list[str]:

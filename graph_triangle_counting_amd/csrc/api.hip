@@ -12,7 +12,8 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s);
 int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
                       gtc_stats *st, hipStream_t s, const HubSubset *sub = nullptr);
 int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
-                      hipStream_t s, bool s4);
+                      hipStream_t s, bool s4, const double *d_w = nullptr,
+                      double *d_even_w = nullptr, double *d_odd_w = nullptr);
 void config_realizable_s4(int nb, const int64_t *edges, uint8_t *mask);
 int count_2pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
                       gtc_stats *st, hipStream_t s);
@@ -281,10 +282,12 @@ int gtc_count_3pcf_hubs(gtc_graph g, const int32_t *h_hubs, int64_t n_hubs, cons
 }
 
 static int count_4pcf(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
-                      void *hip_stream, bool s4) {
-    const char *fn = s4 ? "gtc_count_4pcf_parity_s4" : "gtc_count_4pcf_parity";
-    if (!g || !d_even || !d_odd) {
-        set_error("%s: need a graph, d_even and d_odd", fn);
+                      void *hip_stream, bool s4, const double *d_w = nullptr,
+                      double *d_even_w = nullptr, double *d_odd_w = nullptr) {
+    const char *fn = d_w ? "gtc_count_4pcf_weighted"
+                         : (s4 ? "gtc_count_4pcf_parity_s4" : "gtc_count_4pcf_parity");
+    if (!g || !d_even || !d_odd || (d_w && (!d_even_w || !d_odd_w))) {
+        set_error("%s: need a graph, d_even and d_odd (and d_even_w, d_odd_w with weights)", fn);
         return GTC_E_INVALID;
     }
     if (g->nb > GTC_MAX_BINS_4PCF) {
@@ -306,7 +309,7 @@ static int count_4pcf(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *
     gtc_stats local{};
     fill_graph_stats(g, &local);
     int rc = count_4pcf_device(g, d_even, d_odd, &local, reinterpret_cast<hipStream_t>(hip_stream),
-                               s4);
+                               s4, d_w, d_even_w, d_odd_w);
     local.count_ms =
         std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     if (rc == GTC_OK && st) *st = local;
@@ -365,6 +368,16 @@ int gtc_connected_4pcf_s4(int32_t nbins, const double *h_zeta, const double *h_x
     GTC_TRY(gtc_disconnected_4pcf_s4(nbins, h_xi, h_conn));
     for (int64_t c = 0; c < num_configs_s4(nbins); ++c) h_conn[c] = h_zeta[c] - h_conn[c];
     return GTC_OK;
+}
+
+int gtc_count_4pcf_weighted(gtc_graph g, const double *d_w, int32_t s4, uint64_t *d_even,
+                            int64_t *d_odd, double *d_even_w, double *d_odd_w, gtc_stats *st,
+                            void *hip_stream) {
+    if (!d_w) {
+        set_error("gtc_count_4pcf_weighted: d_w is NULL");
+        return GTC_E_INVALID;
+    }
+    return count_4pcf(g, d_even, d_odd, st, hip_stream, s4 != 0, d_w, d_even_w, d_odd_w);
 }
 
 int64_t gtc_num_configs_s4(int32_t nbins) {

@@ -13,6 +13,7 @@
 // nondecreasing 6-tuples), and the parity sign: vertices ordered by the sum of their squared edge
 // lengths, exact int64 signed volume (r01 x r02) . r03 (Eq.(3)), zero for a tie or zero volume.
 #include <algorithm>
+#include <cmath>
 #include <thread>
 #include <vector>
 
@@ -42,6 +43,11 @@ struct CliqueArgs {
     unsigned long long *even;  // [ncfg]
     unsigned long long *odd;   // [ncfg], two's complement int64
     unsigned int flush_at;
+    // weighted (WT): weights in internal order, 2^s, and [ncfg][4] limb sums of the even sums
+    // (of q) and of the odd sums (of sign(V) q), as 128-bit sums of low and of high limbs
+    const double *w_s;
+    double two_s;
+    unsigned long long *limbs_e, *limbs_o;
 };
 
 __device__ __forceinline__ void wave_lds_sync4() {
@@ -55,10 +61,24 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) / 16 * 16;
 __host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh) {
     return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 22 * 8 * 4;
 }
-// per-wave part: position map, row coordinates, hub-edge bins, bitset rows
-__host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int words) {
+// per-wave part: position map, row coordinates, hub-edge bins, bitset rows, (weighted) row weights
+__host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int words,
+                                                  bool weighted = false) {
     return (size_t)map_bytes + align16(16 * (size_t)max_m) + align16((size_t)max_m) +
-           align16(4 * (size_t)max_m * words);
+           align16(4 * (size_t)max_m * words) + (weighted ? align16(8 * (size_t)max_m) : 0);
+}
+
+__device__ __forceinline__ void add_u128_4(unsigned long long *p, unsigned long long v) {
+    const unsigned long long old = atomicAdd(p, v);
+    if (old + v < old) atomicAdd(p + 1, 1ull);
+}
+
+// exact q = rint(p * 2^s) of a signed product as two limbs: q = (hi - 2^29) * 2^28 + lo
+__device__ __forceinline__ void add_q_limbs(unsigned long long *limbs, double qv) {
+    const double qh = floor(__dmul_rn(qv, 0x1p-28));   // in [-2^29, 2^29)
+    const double ql = __fma_rn(-qh, 0x1p28, qv);       // in [0, 2^28)
+    add_u128_4(limbs, (unsigned long long)(uint32_t)ql);
+    add_u128_4(limbs + 2, (unsigned long long)(uint32_t)((int32_t)qh + (1 << 29)));
 }
 
 __device__ __forceinline__ int64_t d2i(int4 p, int4 q) {
@@ -101,7 +121,7 @@ __device__ __forceinline__ int edge_bin(int64_t d2, const int64_t *se, int nb) {
 }
 
 // GH: bins go straight to global memory (configuration counts too large for LDS).
-template <bool GH>
+template <bool GH, bool WT>
 __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *edges) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int64_t se[GTC_MAX_BINS_4PCF + 1];
@@ -111,12 +131,14 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
     int32_t *od = reinterpret_cast<int32_t *>(smem + hist_bytes);
     int32_t *binom = reinterpret_cast<int32_t *>(smem + 2 * hist_bytes);
     unsigned char *wbase = smem + clique_lds_fixed(a.ncfg, GH) +
-                           (size_t)wid * clique_lds_wave(a.map_bytes, a.max_m, a.words);
+                           (size_t)wid * clique_lds_wave(a.map_bytes, a.max_m, a.words, WT);
     uint16_t *pmap = reinterpret_cast<uint16_t *>(wbase);
     int4 *rc = reinterpret_cast<int4 *>(wbase + a.map_bytes);
     uint8_t *rbin = wbase + a.map_bytes + align16(16 * (size_t)a.max_m);
     uint32_t *adj = reinterpret_cast<uint32_t *>(wbase + a.map_bytes + align16(16 * (size_t)a.max_m) +
                                                  align16((size_t)a.max_m));
+    double *rw = reinterpret_cast<double *>(reinterpret_cast<unsigned char *>(adj) +
+                                            align16(4 * (size_t)a.max_m * a.words));
     const int N = a.nb + 5;  // 6-combinations of [0, N) <-> nondecreasing 6-tuples of [0, nb)
 
     if (!GH)
@@ -163,7 +185,9 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
             pmap[k + d] = (uint16_t)(p + 1);
             rc[p] = a.xyz_s[k];
             rbin[p] = a.bin ? a.bin[rb + p] : (uint8_t)(w >> 24);
+            if (WT) rw[p] = a.w_s[k];
         }
+        const double wi = WT ? a.w_s[i] : 0.0;
         wave_lds_sync4();
         const int32_t hub_hi = (int32_t)((uint32_t)hrow[m - 1] & a.label_mask);
 
@@ -231,6 +255,18 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                         int64_t key[4] = {dia + dib + dic, dia + dab + dac, dib + dab + dbc,
                                           dic + dac + dbc};
                         const int sgn = chirality(p, key);
+                        if (WT) {  // the four weights ascending, product without fusion
+                            double v0 = wi, v1 = rw[ra], v2 = rw[rbb], v3 = rw[rcc], t;
+                            t = fmin(v0, v1); v1 = fmax(v0, v1); v0 = t;
+                            t = fmin(v2, v3); v3 = fmax(v2, v3); v2 = t;
+                            t = fmin(v0, v2); v2 = fmax(v0, v2); v0 = t;
+                            t = fmin(v1, v3); v3 = fmax(v1, v3); v1 = t;
+                            t = fmin(v1, v2); v2 = fmax(v1, v2); v1 = t;
+                            const double pr = __dmul_rn(__dmul_rn(__dmul_rn(v0, v1), v2), v3);
+                            const double qv = rint(__dmul_rn(pr, a.two_s));  // exact, |qv| < 2^57
+                            add_q_limbs(&a.limbs_e[4 * rank], qv);
+                            add_q_limbs(&a.limbs_o[4 * rank], sgn > 0 ? qv : (sgn < 0 ? -qv : 0.0));
+                        }
                         if (GH) {
                             atomicAdd(&a.even[rank], 1ull);
                             if (sgn) atomicAdd(&a.odd[rank], (unsigned long long)(long long)sgn);
@@ -418,8 +454,32 @@ void config_realizable_s4(int nb, const int64_t *edges, uint8_t *mask) {
     }
 }
 
+int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, unsigned long long *d_m,
+                   int32_t *d_bad, double *maxabs, hipStream_t s);
+
+// 2^s of the weighted 4pCF sums: s = 57 - e for M = fl(fl(fl(a*a)*a)*a) = f 2^e
+static int weight_scale4_for(double a) {
+    volatile double a2 = a * a;
+    volatile double a3 = a2 * a;
+    volatile double m = a3 * a;
+    if (m == 0.0) return 0;
+    int e = 0;
+    std::frexp((double)m, &e);
+    return 57 - e;
+}
+
+// exact sum of the q of one limb set (count terms, each with its 2^29 * 2^28 offset), rounded once
+static double limbs4_to_double(const unsigned long long *l, unsigned long long count, int s) {
+    const unsigned __int128 lo = ((unsigned __int128)l[1] << 64) | l[0];
+    const unsigned __int128 hi = ((unsigned __int128)l[3] << 64) | l[2];
+    const unsigned __int128 u = (hi << 28) + lo - ((unsigned __int128)count << 57);
+    return std::ldexp((double)(__int128)u, -s);
+}
+
 int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
-                      hipStream_t s, bool s4) {
+                      hipStream_t s, bool s4, const double *d_w, double *d_even_w,
+                      double *d_odd_w) {
+    const bool WT = d_w != nullptr;
     const int64_t ncfg = s4 ? num_configs_s4(G->nb) : gtc_num_configs(4, G->nb);
     GTC_TRY(fill_u64(d_even, ncfg, 0ull, s));
     GTC_TRY(fill_u64(reinterpret_cast<uint64_t *>(d_odd), ncfg, 0ull, s));
@@ -454,8 +514,9 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     // several times the occupancy the histogram takes)
     const size_t static_lds0 = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
     const bool GH = static_lds0 + clique_lds_fixed(a.ncfg, false) +
-                        2 * clique_lds_wave(a.map_bytes, a.max_m, a.words) > (size_t)ldsmax;
-    const size_t fixed = clique_lds_fixed(a.ncfg, GH), per = clique_lds_wave(a.map_bytes, a.max_m, a.words);
+                        2 * clique_lds_wave(a.map_bytes, a.max_m, a.words, WT) > (size_t)ldsmax;
+    const size_t fixed = clique_lds_fixed(a.ncfg, GH),
+                 per = clique_lds_wave(a.map_bytes, a.max_m, a.words, WT);
     // Workgroups of 4 waves; a large LDS histogram (S4 configurations) allows one workgroup per
     // CU, which then takes as many waves (up to 16) as the LDS beside the histogram holds.
     const size_t static_lds = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
@@ -483,11 +544,20 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     uint32_t *s4rank = nullptr;
     int32_t *s4flags = nullptr, *s4scan = nullptr;
     int64_t *s4ws = nullptr;
+    double *w_s = nullptr;
+    unsigned long long *limbs = nullptr, *d_maxabs = nullptr;
+    int32_t *d_bad = nullptr;
     void *scratch = nullptr;
     const int64_t nkeys = s4 ? num_s4_keys(G->nb) : 0;
     GTC_TRY(carve_alloc(&scratch, s, [&](Carver &c) {
         c.take(&queue, (size_t)kHubClasses * kQueueStride);
         c.take(&qcount, kHubClasses);
+        if (WT) {
+            c.take(&w_s, G->n);
+            c.take(&limbs, 8 * (size_t)ncfg);  // even [ncfg][4] | odd [ncfg][4]
+            c.take(&d_maxabs, 1);
+            c.take(&d_bad, 1);
+        }
         if (s4) {
             c.take(&s4rank, nkeys);
             c.take(&s4flags, nkeys);
@@ -497,6 +567,17 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     }));
     int rc = fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s);
     if (!rc && s4) rc = s4_rank_table(G->nb, s4rank, s4flags, s4scan, s4ws, s);
+    int scale = 0;
+    if (!rc && WT) {
+        double maxabs = 0.0;
+        rc = gather_weights(G, d_w, w_s, d_maxabs, d_bad, &maxabs, s);
+        scale = weight_scale4_for(maxabs);
+        if (!rc) rc = fill_u64(reinterpret_cast<uint64_t *>(limbs), 8 * ncfg, 0ull, s);
+    }
+    a.w_s = w_s;
+    a.two_s = std::ldexp(1.0, scale);
+    a.limbs_e = limbs;
+    a.limbs_o = limbs ? limbs + 4 * ncfg : nullptr;
     a.s4rank = s4rank;
     if (!rc) rc = hub_class_counts(G->hubs, G->n_hubs, G->row_ptr, G->work, qcount, s);
     a.queue = queue;
@@ -505,8 +586,10 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     float kms = 0.f;
     int32_t launched_blocks = 0;
     if (!rc && G->n_hubs > 0) {
-        const void *kfn = GH ? reinterpret_cast<const void *>(&k_clique4<true>)
-                             : reinterpret_cast<const void *>(&k_clique4<false>);
+#define GTC_K4(G_, W_) reinterpret_cast<const void *>(&k_clique4<G_, W_>)
+        const void *kfn = GH ? (WT ? GTC_K4(true, true) : GTC_K4(true, false))
+                             : (WT ? GTC_K4(false, true) : GTC_K4(false, false));
+#undef GTC_K4
         if (lds > 65536)
             (void)hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         int per_cu = 0;
@@ -522,20 +605,36 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         // below what one counter serves
         a.batch_cap = 1;
         launched_blocks = (int32_t)grid.x;
-        if (GH)
-            hipLaunchKernelGGL(k_clique4<true>, grid, block, lds, s, a, (const int64_t *)G->d_edges);
-        else
-            hipLaunchKernelGGL(k_clique4<false>, grid, block, lds, s, a, (const int64_t *)G->d_edges);
-        hipError_t e = hipGetLastError();
+        const int64_t *edges_dev = G->d_edges;
+        void *args[] = {&a, &edges_dev};
+        hipError_t e = hipLaunchKernel(kfn, grid, block, args, lds, s);
+        if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) rc = hip_fail(e, "k_clique4 launch", __FILE__, __LINE__);
         (void)hipEventRecord(e1, s);
     }
-    std::vector<unsigned long long> h_even(ncfg);
+    std::vector<unsigned long long> h_even(ncfg), h_limbs(WT ? 8 * ncfg : 0);
     if (!rc) {
         hipError_t e = hipMemcpyAsync(h_even.data(), d_even, 8 * ncfg, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess && WT)
+            e = hipMemcpyAsync(h_limbs.data(), limbs, sizeof(unsigned long long) * 8 * ncfg,
+                               hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) rc = hip_fail(e, "4pCF readback", __FILE__, __LINE__);
         if (!rc && e0) (void)hipEventElapsedTime(&kms, e0, e1);
+    }
+    if (!rc && WT) {  // every tetrahedron added one term to each limb set: count = even
+        std::vector<double> hw(2 * ncfg);
+        for (int64_t c = 0; c < ncfg; ++c) {
+            hw[c] = limbs4_to_double(&h_limbs[4 * c], h_even[c], scale);
+            hw[ncfg + c] = limbs4_to_double(&h_limbs[4 * (ncfg + c)], h_even[c], scale);
+        }
+        hipError_t e = hipMemcpyAsync(d_even_w, hw.data(), sizeof(double) * ncfg,
+                                      hipMemcpyHostToDevice, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(d_odd_w, hw.data() + ncfg, sizeof(double) * ncfg,
+                               hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) rc = hip_fail(e, "4pCF weighted upload", __FILE__, __LINE__);
     }
     if (e0) (void)hipEventDestroy(e0);
     if (e1) (void)hipEventDestroy(e1);
@@ -551,6 +650,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         st->merge_walks = G->walks;
         st->tiles = G->n_hubs > 0 ? 1 : 0;
         st->kernel_ms = kms;
+        st->weight_scale = scale;
     }
     return GTC_OK;
 }

@@ -198,6 +198,17 @@ int gtc_count_2pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d
 int gtc_disconnected_4pcf_s4(int32_t nbins, const double *h_xi, double *h_disc);
 int gtc_connected_4pcf_s4(int32_t nbins, const double *h_zeta, const double *h_xi,
                           double *h_conn);
+/* Weighted parity 4pCF (the numerator NNNN of the 4pCF estimator, §II.1, §III.2): the counts of
+ * gtc_count_4pcf_parity (s4 == 0) or gtc_count_4pcf_parity_s4 (s4 != 0), and the sums over the
+ * tetrahedra of p = fl(fl(fl(w1*w2)*w3)*w4), the four weights ascending, without fused
+ * multiply-add (even channel, d_even_w) and of sign(V) * p (odd channel, d_odd_w).  Each p is
+ * scaled to the integer q = rint(p * 2^s), s = 57 - e for M = fl(fl(fl(a*a)*a)*a) = f * 2^e,
+ * a = max |w|; the q are summed exactly and each configuration's sums are rounded once.
+ *   d_w device double [n], original labels; d_even_w, d_odd_w device double [n_cfg].
+ *   st->weight_scale receives s. */
+int gtc_count_4pcf_weighted(gtc_graph g, const double *d_w, int32_t s4, uint64_t *d_even,
+                            int64_t *d_odd, double *d_even_w, double *d_odd_w, gtc_stats *st,
+                            void *hip_stream);
 int64_t gtc_num_configs_s4(int32_t nbins);
 int gtc_config_bins_s4(int32_t nbins, int32_t *h_bins);
 int gtc_config_realizable_s4(int32_t nbins, const int64_t *h_edges_sq, uint8_t *h_mask);
@@ -229,6 +240,47 @@ int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h
  * largest spoke label of window h, so every forward edge is walked in exactly one tile. */
 int64_t gtc_plan_windows(const int64_t *h_row_ptr, int64_t n, int64_t tile_bytes,
                          int32_t entry_bytes, int64_t *h_bounds);
+
+/* Squared edges of nbins equal radial bins from r_min to r_max (§IV: bins equally spaced in r
+ * from r_min to r_max), as integers: h_edges_sq[b] = ceil(r_b^2), r_b = r_min + b (r_max - r_min)
+ * / nbins, so that an integer squared distance d^2 falls in bin b exactly when r_b <= d < r_{b+1}.
+ * Pairs closer than r_min are outside every bin.
+ *   r_min, r_max grid units, 0 <= r_min < r_max <= 2^21; h_edges_sq host int64 [nbins + 1].
+ * GTC_E_INVALID for a range out of bounds or two bins whose integer edges coincide.  Host only. */
+int gtc_linear_edges_sq(int64_t r_min, int64_t r_max, int32_t nbins, int64_t *h_edges_sq);
+
+/* The 3pCF and 4pCF estimators on a data catalogue D and a random catalogue R (§II.1, §III.3;
+ * the compute_3pcf / compute_4pcf interface of §II.2).  One neighbour graph is built over D then
+ * R (D's points take labels 0..n_data-1, R's the rest).  The numerators take the signed,
+ * normalised weights w / sum_D w on D and -w / sum_R w on R (the sums rounded correctly); the
+ * denominators take w / sum_R w on R and 0 on D, on the same graph:
+ *   3pCF: zeta = NNN / RRR per configuration of gtc_count_3pcf.
+ *   4pCF: zeta_even = NNNN_even / RRRR and zeta_odd = NNNN_odd / RRRR per S4 configuration of
+ *         gtc_count_4pcf_parity_s4; xi = NN / RR per bin from the graph's pairs; zeta_conn =
+ *         zeta_even - disc(xi), Eq. (4) and (5).
+ * A configuration with no random triangle (tetrahedron) gives 0/0 or x/0 (NaN or infinity).
+ *   d_xyz_data device int32 [n_data][3], d_xyz_rand device int32 [n_rand][3]: grid coordinates as
+ *              gtc_build_graph; n_data >= 0, n_rand >= 1, n_data + n_rand < 2^31.
+ *   d_w_data, d_w_rand device double [n_data], [n_rand], finite, or NULL for unit weights; each
+ *              catalogue's weights must not sum to zero.
+ *   h_edges_sq, nbins, opt: as gtc_build_graph (gtc_compute_4pcf: nbins <= GTC_MAX_BINS_4PCF and
+ *              coordinates kept).
+ *   h_zeta     host double [gtc_num_configs(3, nbins)]; h_nnn, h_rrr the same or NULL.
+ *   h_zeta_even, h_zeta_odd host double [gtc_num_configs_s4(nbins)]; h_zeta_conn the same or
+ *              NULL; h_xi host double [nbins] or NULL.
+ *   st         may be NULL: the first count's statistics, kernel_ms and count_ms summed over
+ *              every count of the call.
+ * The call builds and frees its own graph and synchronises the stream before it returns. */
+int gtc_compute_3pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_w_data,
+                     const int32_t *d_xyz_rand, int64_t n_rand, const double *d_w_rand,
+                     const int64_t *h_edges_sq, int32_t nbins, const gtc_options *opt,
+                     double *h_zeta, double *h_nnn, double *h_rrr, gtc_stats *st,
+                     void *hip_stream);
+int gtc_compute_4pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_w_data,
+                     const int32_t *d_xyz_rand, int64_t n_rand, const double *d_w_rand,
+                     const int64_t *h_edges_sq, int32_t nbins, const gtc_options *opt,
+                     double *h_zeta_even, double *h_zeta_odd, double *h_zeta_conn, double *h_xi,
+                     gtc_stats *st, void *hip_stream);
 
 /* Graph-level statistics (n, edges, max_out_degree, windows, spoke_elements, build_ms). */
 int gtc_graph_stats(gtc_graph g, gtc_stats *st);

@@ -174,3 +174,54 @@ def cliques4_weighted(xyz: np.ndarray, edges, w, s4: bool = False, s: int | None
             ev[c] += p
             od[c] += chirality([xyz[x] for x in q]) * p
     return ev, od
+
+
+def estimator_by_type(xd, wd, xr, wr, edges, order: int):
+    """The Szapudi-Szalay / Landy-Szalay numerators written by catalogue type, in exact rationals:
+    for each clique of the union graph (order 2: pairs, 3: triangles, 4: tetrahedra) with k random
+    vertices, T_k += prod(w) / (S_D^(order-k) S_R^k); the numerator is sum_k (-1)^k T_k (for order
+    3: DDD - 3 DDR + 3 DRR - RRR with each term normalised), the denominator T_order taken over the
+    all-random cliques alone.  Order 4 also sums the chirality-signed terms.  Configurations: bins
+    (order 2), sorted triples (3), S4 canonical tuples (4).  Returns (num, den, absum[, odd]) as
+    lists of Fractions, absum the sum of |term| over every clique (for rounding bounds)."""
+    xyz = np.concatenate([np.asarray(xd, np.int64).reshape(-1, 3),
+                          np.asarray(xr, np.int64).reshape(-1, 3)])
+    nd = len(xd)
+    w = [Fraction(float(x)) for x in wd] + [Fraction(float(x)) for x in wr]
+    sd = sum(w[:nd], Fraction(0))
+    sr = sum(w[nd:], Fraction(0))
+    a, b = adjacency(xyz, edges)
+    nb = len(edges) - 1
+    if order == 2:
+        idx = {(x,): x for x in range(nb)}
+    elif order == 3:
+        idx = config_index(nb, 3)
+    else:
+        idx = s4_index(nb)
+    num = [Fraction(0)] * len(idx)
+    den = [Fraction(0)] * len(idx)
+    ab = [Fraction(0)] * len(idx)
+    odd = [Fraction(0)] * len(idx)
+    for q in itertools.combinations(range(len(xyz)), order):
+        if not all(a[u, v] for u, v in itertools.combinations(q, 2)):
+            continue
+        bins = [int(b[u, v]) for u, v in itertools.combinations(q, 2)]
+        if order == 4:
+            c = idx[s4_canonical(bins)]
+        else:
+            c = idx[tuple(sorted(bins))]
+        k = sum(1 for v in q if v >= nd)
+        t = Fraction(1)
+        for v in q:
+            t *= w[v]
+        t /= sd ** (order - k) * sr ** k
+        sgn = -1 if k % 2 else 1
+        num[c] += sgn * t
+        ab[c] += abs(t)
+        if k == order:
+            den[c] += t
+        if order == 4:
+            odd[c] += sgn * chirality([xyz[v] for v in q]) * t
+    if order == 4:
+        return num, den, ab, odd
+    return num, den, ab

@@ -171,3 +171,40 @@ def test_plan_windows_partitions_rows_greedily():
     good = np.array([0, 5, 7], np.int64)
     assert L.gtc_plan_windows(good.ctypes.data_as(C.c_void_p), 2, 10, 0,
                               out.ctypes.data_as(C.c_void_p)) == gtc.GTC_E_INVALID
+
+
+@pytest.mark.parametrize("rmin,rmax,nb", [(0, 1000, 3), (7, 31, 4), (1, 100, 16), (3, 4, 1),
+                                          (50_000, 1 << 21, 255), (0, 1 << 21, 7)])
+def test_linear_edges_sq_matches_the_oracle(rmin, rmax, nb):
+    from oracle import estimator
+    np.testing.assert_array_equal(gtc.linear_edges_sq(rmin, rmax, nb),
+                                  estimator.linear_edges_sq(rmin, rmax, nb))
+
+
+def test_linear_edges_sq_rejects_bad_ranges():
+    for args in ((-1, 10, 2), (10, 10, 2), (0, (1 << 21) + 1, 2), (0, 10, 0), (0, 10, 256),
+                 (0, 3, 8)):  # the last: 8 bins on [0, 3) repeat an integer edge
+        with pytest.raises(gtc.GtcError):
+            gtc.linear_edges_sq(*args)
+
+
+def test_estimators_reject_bad_arguments_without_gpu():
+    L = gtc.lib()
+    fake = C.c_void_p(0x1000)  # never dereferenced: every case fails before any device work
+    e = np.array([0, 5, 10], np.int64).ctypes.data_as(C.c_void_p)
+    out = np.zeros(64)
+    o = out.ctypes.data_as(C.c_void_p)
+    st = gtc.Stats()
+    c3 = lambda xd, nd, xr, nr, nb, z: L.gtc_compute_3pcf(xd, nd, None, xr, nr, None, e, nb, None,
+                                                          z, None, None, C.byref(st), None)
+    assert c3(fake, 4, fake, 0, 2, o) == gtc.GTC_E_INVALID   # no randoms
+    assert c3(None, 4, fake, 4, 2, o) == gtc.GTC_E_INVALID   # data coordinates missing
+    assert c3(fake, -1, fake, 4, 2, o) == gtc.GTC_E_INVALID  # negative n_data
+    assert c3(fake, 4, fake, 4, 2, None) == gtc.GTC_E_INVALID  # no output
+    assert c3(fake, 4, fake, 4, 0, o) == gtc.GTC_E_INVALID   # nbins 0
+    assert c3(fake, 1 << 30, fake, 1 << 30, 2, o) == gtc.GTC_E_INVALID  # n >= 2^31
+    c4 = lambda nb, opt, z: L.gtc_compute_4pcf(fake, 4, None, fake, 4, None, e, nb, opt, z, z,
+                                               None, None, C.byref(st), None)
+    assert c4(17, None, o) == gtc.GTC_E_INVALID  # beyond the 4pCF's 16 bins
+    assert c4(2, None, None) == gtc.GTC_E_INVALID
+    assert c4(2, C.byref(gtc.Options(0, 0, 1)), o) == gtc.GTC_E_INVALID  # coordinates dropped

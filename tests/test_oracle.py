@@ -557,3 +557,107 @@ def test_coplanar_tetrahedra_have_no_chirality():
     g = oracle.Graph(xyz, linear_edges_sq(3000, 4))
     even, odd, ncl = g.count_4pcf_parity()
     assert ncl == 10 and even.sum() == 10 and np.all(odd == 0)
+
+
+# ------------------------------------------------------------------ estimators (§II.1, §III.3)
+
+from fractions import Fraction  # noqa: E402
+
+from oracle import estimator as est  # noqa: E402
+
+
+@pytest.mark.parametrize("rmin,rmax,nb", [(0, 1000, 3), (7, 31, 4), (1, 100, 16), (3, 4, 1),
+                                          (50_000, 1 << 21, 255)])
+def test_linear_edges_sq_bins_are_equal_in_r(rmin, rmax, nb):
+    # an integer squared distance d2 lies in bin b exactly when r_b <= sqrt(d2) < r_{b+1},
+    # r_b = rmin + b (rmax - rmin) / nb: compare with that inequality in integers,
+    # (d2 nb^2 >= (rmin nb + b (rmax - rmin))^2), at and around every edge
+    e = est.linear_edges_sq(rmin, rmax, nb)
+    for b in range(nb + 1):
+        rb_nb = rmin * nb + b * (rmax - rmin)
+        for d2 in {max(int(e[b]) + k, 0) for k in (-2, -1, 0, 1)}:
+            assert (d2 >= e[b]) == (d2 * nb * nb >= rb_nb * rb_nb)
+    if rmin == 0:
+        np.testing.assert_array_equal(e, linear_edges_sq(rmax, nb))
+
+
+def estimator_set(seed, nd, nr, box):
+    rng = rng_for(seed)
+    xd = small_cloud(seed + 1, nd, box // 3)
+    lo = xd.min(axis=0) - box // 3
+    xr = np.ascontiguousarray((lo + rng.integers(0, box, size=(nr, 3))).clip(0, GRID - 1)
+                              .astype(np.int32))
+    wd = rng.uniform(0.5, 2.0, nd)
+    wr = rng.uniform(0.5, 2.0, nr)
+    return xd, wd, xr, wr
+
+
+def _close(got, want, absum, tol=1e-13):
+    for c, (g, x, a) in enumerate(zip(got, want, absum)):
+        assert abs(Fraction(float(g)) - x) <= tol * a + Fraction(1, 2**1074), c
+
+
+@pytest.mark.parametrize("seed,nd,nr,nb,rmin", [(81, 14, 18, 3, 100), (82, 10, 20, 2, 0)])
+def test_3pcf_estimator_is_the_szapudi_szalay_combination(seed, nd, nr, nb, rmin):
+    xd, wd, xr, wr = estimator_set(seed, nd, nr, 1800)
+    edges = est.linear_edges_sq(rmin, 1200, nb)
+    zeta, nnn, rrr = est.compute_3pcf(xd, wd, xr, wr, edges)
+    num, den, ab = brute.estimator_by_type(xd, wd, xr, wr, edges, 3)
+    assert sum(1 for x in den if x) >= 3
+    _close(nnn, num, ab)
+    _close(rrr, den, den)
+    for c in range(len(num)):
+        if den[c]:
+            assert zeta[c] == pytest.approx(float(num[c] / den[c]), rel=1e-11, abs=1e-11 * float(ab[c] / den[c]))
+        else:
+            assert not np.isfinite(zeta[c])
+
+
+@pytest.mark.parametrize("seed,nd,nr,nb", [(83, 10, 14, 2), (84, 8, 16, 3)])
+def test_4pcf_estimator_is_the_signed_combination(seed, nd, nr, nb):
+    xd, wd, xr, wr = estimator_set(seed, nd, nr, 1500)
+    edges = est.linear_edges_sq(50, 1100, nb)
+    ze, zo, zc, xi = est.compute_4pcf(xd, wd, xr, wr, edges)
+    num, den, ab, odd = brute.estimator_by_type(xd, wd, xr, wr, edges, 4)
+    pnum, pden, pab = brute.estimator_by_type(xd, wd, xr, wr, edges, 2)
+    assert sum(1 for x in den if x) >= 3 and any(odd)
+    xi_want = [float(n / d) for n, d in zip(pnum, pden)]
+    np.testing.assert_allclose(xi, xi_want, rtol=1e-12)
+    bins = oracle.config_bins_s4(nb)
+    for c in range(len(num)):
+        if den[c]:
+            scale = float(ab[c] / den[c])
+            assert ze[c] == pytest.approx(float(num[c] / den[c]), abs=1e-11 * scale)
+            assert zo[c] == pytest.approx(float(odd[c] / den[c]), abs=1e-11 * scale)
+            assert zc[c] == pytest.approx(float(num[c] / den[c]) - brute.disconnected_s4(bins[c], xi_want),
+                                          abs=1e-11 * (scale + 3 * max(map(abs, xi_want)) ** 2))
+        else:
+            assert not np.isfinite(ze[c])
+
+
+def test_estimators_vanish_when_data_are_the_randoms():
+    # D = R with unit weights: every clique with a data vertex has a twin with the random copy
+    # (same positions, twins at distance 0 < r_min never adjacent) and the opposite sign, and the
+    # normalised weights all have one magnitude, so every product rounds the same whatever the
+    # order and signs of its factors, and the sums cancel exactly
+    x = small_cloud(86, 24, 600)
+    edges = est.linear_edges_sq(20, 500, 3)
+    zeta, nnn, rrr = est.compute_3pcf(x, None, x, None, edges)
+    assert rrr.max() > 0
+    np.testing.assert_array_equal(nnn, 0.0)
+    ze, zo, zc, xi = est.compute_4pcf(x[:18], None, x[:18], None, edges)
+    np.testing.assert_array_equal(xi, 0.0)
+    fin = np.isfinite(ze)
+    assert fin.sum() > 3
+    np.testing.assert_array_equal(ze[fin], 0.0)
+    np.testing.assert_array_equal(zo[fin], 0.0)
+    np.testing.assert_array_equal(zc[fin], 0.0)
+
+
+def test_estimator_weights_are_normalised():
+    rng = rng_for(87)
+    wd, wr = rng.uniform(0.1, 3, 50), rng.uniform(0.1, 3, 70)
+    s, r = est.estimator_weights(50, wd, 70, wr)
+    assert Fraction(sum(map(Fraction, s[:50]))) == pytest.approx(1, abs=1e-15)
+    assert Fraction(sum(map(Fraction, s[50:]))) == pytest.approx(-1, abs=1e-15)
+    assert (r[:50] == 0).all() and np.array_equal(r[50:], -s[50:])
