@@ -43,11 +43,14 @@ struct CliqueArgs {
     unsigned long long *even;  // [ncfg]
     unsigned long long *odd;   // [ncfg], two's complement int64
     unsigned int flush_at;
-    // weighted (WT): weights in internal order, 2^s, and [ncfg][4] limb sums of the even sums
-    // (of q) and of the odd sums (of sign(V) q), as 128-bit sums of low and of high limbs
+    // weighted: weights in internal order, 2^s, and the sums of q by handedness class (sign(V) =
+    // +1, -1, 0) as [ncfg][3] two's complement 128-bit words (low, high), replicated over wcopies
+    // copies wstride words apart (workgroup b adds to copy b % wcopies)
     const double *w_s;
     double two_s;
-    unsigned long long *limbs_e, *limbs_o;
+    unsigned long long *wsum;
+    int wcopies;
+    long long wstride;
 };
 
 __device__ __forceinline__ void wave_lds_sync4() {
@@ -58,8 +61,9 @@ __device__ __forceinline__ void wave_lds_sync4() {
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) / 16 * 16; }
 
 // per-workgroup part: even u32[ncfg], odd i32[ncfg] (unless the bins are global), binomials C[22][8]
-__host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh) {
-    return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 22 * 8 * 4;
+// fixed part: even / odd count bins (unless global), binomials, (LDS class sums) [ncfg][3][2] words
+__host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh, bool wl = false) {
+    return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 22 * 8 * 4 + (wl ? 48 * (size_t)ncfg : 0);
 }
 // per-wave part: position map, row coordinates, hub-edge bins, bitset rows, (weighted) row weights
 __host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int words,
@@ -68,17 +72,22 @@ __host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int 
            align16(4 * (size_t)max_m * words) + (weighted ? align16(8 * (size_t)max_m) : 0);
 }
 
-__device__ __forceinline__ void add_u128_4(unsigned long long *p, unsigned long long v) {
-    const unsigned long long old = atomicAdd(p, v);
-    if (old + v < old) atomicAdd(p + 1, 1ull);
+// Add a signed 64-bit v to the two's complement 128-bit word p[0] (low) | p[1] (high): the low
+// word takes v, the high word its sign extension plus the carry, which cancel (and skip the second
+// atomic) unless v >= 0 carries or v < 0 borrows -- rare for |v| << 2^64.  Concurrent adds commute.
+__device__ __forceinline__ void add_i128(unsigned long long *p, long long v) {
+    const unsigned long long u = (unsigned long long)v;
+    const unsigned long long old = atomicAdd(p, u);
+    const long long dh = (v < 0 ? -1ll : 0ll) + (old + u < old ? 1ll : 0ll);
+    if (dh) atomicAdd(p + 1, (unsigned long long)dh);
 }
 
-// exact q = rint(p * 2^s) of a signed product as two limbs: q = (hi - 2^29) * 2^28 + lo
-__device__ __forceinline__ void add_q_limbs(unsigned long long *limbs, double qv) {
-    const double qh = floor(__dmul_rn(qv, 0x1p-28));   // in [-2^29, 2^29)
-    const double ql = __fma_rn(-qh, 0x1p28, qv);       // in [0, 2^28)
-    add_u128_4(limbs, (unsigned long long)(uint32_t)ql);
-    add_u128_4(limbs + 2, (unsigned long long)(uint32_t)((int32_t)qh + (1 << 29)));
+// add the 128-bit word (lo, hi) to p[0] | p[1]
+__device__ __forceinline__ void add_u128_pair(unsigned long long *p, unsigned long long lo,
+                                              unsigned long long hi) {
+    const unsigned long long old = atomicAdd(p, lo);
+    hi += (old + lo < old) ? 1ull : 0ull;
+    if (hi) atomicAdd(p + 1, hi);
 }
 
 __device__ __forceinline__ int64_t d2i(int4 p, int4 q) {
@@ -120,9 +129,12 @@ __device__ __forceinline__ int edge_bin(int64_t d2, const int64_t *se, int nb) {
     return l;
 }
 
-// GH: bins go straight to global memory (configuration counts too large for LDS).
-template <bool GH, bool WT>
+// GH: bins go straight to global memory (configuration counts too large for LDS).  WM: 0
+// unweighted; 1 weighted, class sums in global memory; 2 weighted, class sums in LDS, added to
+// global memory when the workgroup ends.
+template <bool GH, int WM>
 __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *edges) {
+    constexpr bool WT = WM != 0;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int64_t se[GTC_MAX_BINS_4PCF + 1];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
@@ -130,7 +142,8 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
     uint32_t *ev = reinterpret_cast<uint32_t *>(smem);
     int32_t *od = reinterpret_cast<int32_t *>(smem + hist_bytes);
     int32_t *binom = reinterpret_cast<int32_t *>(smem + 2 * hist_bytes);
-    unsigned char *wbase = smem + clique_lds_fixed(a.ncfg, GH) +
+    unsigned long long *wl = reinterpret_cast<unsigned long long *>(smem + 2 * hist_bytes + 22 * 8 * 4);
+    unsigned char *wbase = smem + clique_lds_fixed(a.ncfg, GH, WM == 2) +
                            (size_t)wid * clique_lds_wave(a.map_bytes, a.max_m, a.words, WT);
     uint16_t *pmap = reinterpret_cast<uint16_t *>(wbase);
     int4 *rc = reinterpret_cast<int4 *>(wbase + a.map_bytes);
@@ -140,6 +153,10 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
     double *rw = reinterpret_cast<double *>(reinterpret_cast<unsigned char *>(adj) +
                                             align16(4 * (size_t)a.max_m * a.words));
     const int N = a.nb + 5;  // 6-combinations of [0, N) <-> nondecreasing 6-tuples of [0, nb)
+    unsigned long long *wg = nullptr;  // this workgroup's copy of the global class sums
+    if (WT) wg = a.wsum + (long long)(blockIdx.x % (unsigned)a.wcopies) * a.wstride;
+    if (WM == 2)
+        for (int t = threadIdx.x; t < 6 * a.ncfg; t += blockDim.x) wl[t] = 0ull;
 
     if (!GH)
         for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
@@ -264,8 +281,8 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                             t = fmin(v1, v2); v2 = fmax(v1, v2); v1 = t;
                             const double pr = __dmul_rn(__dmul_rn(__dmul_rn(v0, v1), v2), v3);
                             const double qv = rint(__dmul_rn(pr, a.two_s));  // exact, |qv| < 2^57
-                            add_q_limbs(&a.limbs_e[4 * rank], qv);
-                            add_q_limbs(&a.limbs_o[4 * rank], sgn > 0 ? qv : (sgn < 0 ? -qv : 0.0));
+                            const int cls = sgn > 0 ? 0 : (sgn < 0 ? 1 : 2);
+                            add_i128((WM == 2 ? wl : wg) + 2 * (3 * rank + cls), (long long)qv);
                         }
                         if (GH) {
                             atomicAdd(&a.even[rank], 1ull);
@@ -302,6 +319,11 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
         const int32_t o = od[t];
         if (o) atomicAdd(&a.odd[t], (unsigned long long)(long long)o);
     }
+    if (WM == 2)
+        for (int t = threadIdx.x; t < 3 * a.ncfg; t += blockDim.x) {
+            const unsigned long long lo = wl[2 * t], hi = wl[2 * t + 1];
+            if (lo | hi) add_u128_pair(wg + 2 * t, lo, hi);
+        }
 }
 
 // ------------------------------------------------------------------ S4 configurations (§III.3)
@@ -468,12 +490,14 @@ static int weight_scale4_for(double a) {
     return 57 - e;
 }
 
-// exact sum of the q of one limb set (count terms, each with its 2^29 * 2^28 offset), rounded once
-static double limbs4_to_double(const unsigned long long *l, unsigned long long count, int s) {
-    const unsigned __int128 lo = ((unsigned __int128)l[1] << 64) | l[0];
-    const unsigned __int128 hi = ((unsigned __int128)l[3] << 64) | l[2];
-    const unsigned __int128 u = (hi << 28) + lo - ((unsigned __int128)count << 57);
-    return std::ldexp((double)(__int128)u, -s);
+// Copies of the global class sums: a few hot configurations take most tetrahedra, and their
+// global atomics serialise; workgroup b adds to copy b % copies (a multiple of the 8 XCDs, so each
+// copy stays in the L2 of one XCD), within a 256 MiB budget.
+static int weighted_copies(int64_t ncfg) {
+    const int64_t per_copy = 48 * ncfg;  // [ncfg][3] 128-bit words
+    int64_t c = std::min<int64_t>(64, std::max<int64_t>(1, ((int64_t)256 << 20) / per_copy));
+    if (c >= 8) c &= ~(int64_t)7;
+    return (int)c;
 }
 
 int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
@@ -512,11 +536,12 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     GTC_HIP_CHECK(hipDeviceGetAttribute(&ldsmax, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
     // LDS bins while they leave room for two waves' hub data (global atomics per tetrahedron cost
     // several times the occupancy the histogram takes)
+    // (weighted: the class sums too, in LDS on the same terms, else in global memory)
     const size_t static_lds0 = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
-    const bool GH = static_lds0 + clique_lds_fixed(a.ncfg, false) +
-                        2 * clique_lds_wave(a.map_bytes, a.max_m, a.words, WT) > (size_t)ldsmax;
-    const size_t fixed = clique_lds_fixed(a.ncfg, GH),
-                 per = clique_lds_wave(a.map_bytes, a.max_m, a.words, WT);
+    const size_t per = clique_lds_wave(a.map_bytes, a.max_m, a.words, WT);
+    const bool WL = WT && static_lds0 + clique_lds_fixed(a.ncfg, false, true) + 2 * per <= (size_t)ldsmax;
+    const bool GH = static_lds0 + clique_lds_fixed(a.ncfg, false) + 2 * per > (size_t)ldsmax;
+    const size_t fixed = clique_lds_fixed(a.ncfg, GH, WL);
     // Workgroups of 4 waves; a large LDS histogram (S4 configurations) allows one workgroup per
     // CU, which then takes as many waves (up to 16) as the LDS beside the histogram holds.
     const size_t static_lds = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
@@ -545,16 +570,17 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     int32_t *s4flags = nullptr, *s4scan = nullptr;
     int64_t *s4ws = nullptr;
     double *w_s = nullptr;
-    unsigned long long *limbs = nullptr, *d_maxabs = nullptr;
+    unsigned long long *wsum = nullptr, *d_maxabs = nullptr;
     int32_t *d_bad = nullptr;
     void *scratch = nullptr;
     const int64_t nkeys = s4 ? num_s4_keys(G->nb) : 0;
+    const int copies = WT ? weighted_copies(ncfg) : 0;
     GTC_TRY(carve_alloc(&scratch, s, [&](Carver &c) {
         c.take(&queue, (size_t)kHubClasses * kQueueStride);
         c.take(&qcount, kHubClasses);
         if (WT) {
             c.take(&w_s, G->n);
-            c.take(&limbs, 8 * (size_t)ncfg);  // even [ncfg][4] | odd [ncfg][4]
+            c.take(&wsum, 6 * (size_t)ncfg * copies);
             c.take(&d_maxabs, 1);
             c.take(&d_bad, 1);
         }
@@ -572,12 +598,13 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         double maxabs = 0.0;
         rc = gather_weights(G, d_w, w_s, d_maxabs, d_bad, &maxabs, s);
         scale = weight_scale4_for(maxabs);
-        if (!rc) rc = fill_u64(reinterpret_cast<uint64_t *>(limbs), 8 * ncfg, 0ull, s);
+        if (!rc) rc = fill_u64(reinterpret_cast<uint64_t *>(wsum), 6 * ncfg * copies, 0ull, s);
     }
     a.w_s = w_s;
     a.two_s = std::ldexp(1.0, scale);
-    a.limbs_e = limbs;
-    a.limbs_o = limbs ? limbs + 4 * ncfg : nullptr;
+    a.wsum = wsum;
+    a.wcopies = copies;
+    a.wstride = 6 * ncfg;
     a.s4rank = s4rank;
     if (!rc) rc = hub_class_counts(G->hubs, G->n_hubs, G->row_ptr, G->work, qcount, s);
     a.queue = queue;
@@ -587,8 +614,8 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     int32_t launched_blocks = 0;
     if (!rc && G->n_hubs > 0) {
 #define GTC_K4(G_, W_) reinterpret_cast<const void *>(&k_clique4<G_, W_>)
-        const void *kfn = GH ? (WT ? GTC_K4(true, true) : GTC_K4(true, false))
-                             : (WT ? GTC_K4(false, true) : GTC_K4(false, false));
+        const void *kfn = GH ? (WT ? GTC_K4(true, 1) : GTC_K4(true, 0))
+                             : (WL ? GTC_K4(false, 2) : (WT ? GTC_K4(false, 1) : GTC_K4(false, 0)));
 #undef GTC_K4
         if (lds > 65536)
             (void)hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -612,29 +639,13 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         if (e != hipSuccess) rc = hip_fail(e, "k_clique4 launch", __FILE__, __LINE__);
         (void)hipEventRecord(e1, s);
     }
-    std::vector<unsigned long long> h_even(ncfg), h_limbs(WT ? 8 * ncfg : 0);
+    if (!rc && WT) rc = finalize_class_sums(wsum, ncfg, copies, 6 * ncfg, scale, d_even_w, d_odd_w, s);
+    std::vector<unsigned long long> h_even(ncfg);
     if (!rc) {
         hipError_t e = hipMemcpyAsync(h_even.data(), d_even, 8 * ncfg, hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess && WT)
-            e = hipMemcpyAsync(h_limbs.data(), limbs, sizeof(unsigned long long) * 8 * ncfg,
-                               hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) rc = hip_fail(e, "4pCF readback", __FILE__, __LINE__);
         if (!rc && e0) (void)hipEventElapsedTime(&kms, e0, e1);
-    }
-    if (!rc && WT) {  // every tetrahedron added one term to each limb set: count = even
-        std::vector<double> hw(2 * ncfg);
-        for (int64_t c = 0; c < ncfg; ++c) {
-            hw[c] = limbs4_to_double(&h_limbs[4 * c], h_even[c], scale);
-            hw[ncfg + c] = limbs4_to_double(&h_limbs[4 * (ncfg + c)], h_even[c], scale);
-        }
-        hipError_t e = hipMemcpyAsync(d_even_w, hw.data(), sizeof(double) * ncfg,
-                                      hipMemcpyHostToDevice, s);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(d_odd_w, hw.data() + ncfg, sizeof(double) * ncfg,
-                               hipMemcpyHostToDevice, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) rc = hip_fail(e, "4pCF weighted upload", __FILE__, __LINE__);
     }
     if (e0) (void)hipEventDestroy(e0);
     if (e1) (void)hipEventDestroy(e1);

@@ -82,6 +82,17 @@ int carve_alloc(void **block, hipStream_t s, F &&layout) {
 int fill_u64(uint64_t *p, int64_t count, uint64_t value, hipStream_t s);
 int fill_u32(uint32_t *p, int64_t count, uint32_t value, hipStream_t s);
 
+// Exact fixed-point sums to doubles, on the device: for c < n, out[c] = 2^-s (sum of the q of
+// configuration c), where every added q was split as q = (hi - 2^29) 2^28 + lo, the lo and hi
+// limbs summed as 128-bit words [lo128, hi128] at limbs[4c .. 4c+3] of each of `copies` copies
+// (copy_stride words apart), and counts[c] terms were added.  One rounding per sum.
+int finalize_limbs(const unsigned long long *limbs, int64_t n, int copies, int64_t copy_stride,
+                   const unsigned long long *counts, int s, double *out, hipStream_t st);
+// The parity 4pCF's sums by handedness class: [n][3] two's complement 128-bit words (low, high)
+// A+, A-, A0 per copy; even[c] = 2^-s (A+ + A- + A0), odd[c] = 2^-s (A+ - A-), one rounding each.
+int finalize_class_sums(const unsigned long long *w, int64_t n, int copies, int64_t copy_stride,
+                        int s, double *even, double *odd, hipStream_t st);
+
 // hub windows: bounds[0..W] of consecutive rows whose CSR (entry_bytes per edge) fits tile_bytes
 int64_t plan_windows(const int64_t *row_ptr, int64_t n, int64_t tile_bytes, int64_t entry_bytes,
                      int64_t *bounds);

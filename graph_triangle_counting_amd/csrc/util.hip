@@ -59,6 +59,101 @@ static int fill(T *p, int64_t n, T v, hipStream_t s) {
 int fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t s) { return fill<uint64_t>(p, n, v, s); }
 int fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s) { return fill<uint32_t>(p, n, v, s); }
 
+// ------------------------------------------------------------------ exact fixed-point sums
+// The nearest double to a 128-bit magnitude (hi, lo): normalise so the top bit is bit 127, keep
+// the top 64 bits and fold every bit below them into bit 0 (a sticky bit far below the rounding
+// position of a 53-bit significand), convert that word with one rounding, and scale back.
+__device__ double u128_to_double(unsigned long long hi, unsigned long long lo) {
+    if (hi == 0) return (double)lo;
+    const int z = __clzll((long long)hi);
+    const unsigned long long top = z ? (hi << z) | (lo >> (64 - z)) : hi;
+    const unsigned long long rest = z ? lo << z : lo;
+    return ldexp((double)(top | (rest != 0 ? 1ull : 0ull)), 64 - z);
+}
+
+// 2^-s times the two's complement 128-bit integer (lo, hi), rounded once
+__device__ double i128_to_double(unsigned long long lo, unsigned long long hi, int s) {
+    const bool neg = (long long)hi < 0;
+    if (neg) {
+        lo = ~lo + 1;
+        hi = ~hi + (lo == 0 ? 1ull : 0ull);
+    }
+    const double m = ldexp(u128_to_double(hi, lo), -s);
+    return neg ? -m : m;
+}
+
+// out[c] = 2^-s * sum over every copy of (hi128 * 2^28 + lo128) - counts[c] * 2^57, where a copy
+// holds [n][4] words (lo128 low, lo128 high, hi128 low, hi128 high) at stride copy_stride words
+__global__ void k_finalize_limbs(const unsigned long long *limbs, int64_t n, int copies,
+                                 int64_t copy_stride, const unsigned long long *counts, int s,
+                                 double *out) {
+    const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (c >= n) return;
+    unsigned long long l0 = 0, l1 = 0, h0 = 0, h1 = 0;
+    for (int k = 0; k < copies; ++k) {
+        const unsigned long long *p = limbs + k * copy_stride + 4 * c;
+        const unsigned long long a = p[0], b = p[2];
+        l1 += p[1] + (l0 + a < l0 ? 1ull : 0ull);
+        l0 += a;
+        h1 += p[3] + (h0 + b < h0 ? 1ull : 0ull);
+        h0 += b;
+    }
+    // u = hi128 * 2^28 + lo128 - count * 2^57, modulo 2^128 (two's complement of the exact sum)
+    unsigned long long u0 = h0 << 28, u1 = (h1 << 28) | (h0 >> 36);
+    u1 += l1 + (u0 + l0 < u0 ? 1ull : 0ull);
+    u0 += l0;
+    const unsigned long long n0 = counts[c] << 57, n1 = counts[c] >> 7;
+    u1 -= n1 + (u0 < n0 ? 1ull : 0ull);
+    u0 -= n0;
+    out[c] = i128_to_double(u0, u1, s);
+}
+
+// The parity 4pCF's class sums: per configuration c the two's complement 128-bit sums A+, A-, A0
+// of q over the tetrahedra of positive, negative and zero handedness ([n][3] pairs of words per
+// copy); even = A+ + A- + A0, odd = A+ - A-, each scaled by 2^-s with one rounding.
+__global__ void k_finalize_class_sums(const unsigned long long *w, int64_t n, int copies,
+                                      int64_t copy_stride, int s, double *even, double *odd) {
+    const int64_t c = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (c >= n) return;
+    unsigned long long e0 = 0, e1 = 0, o0 = 0, o1 = 0;
+    for (int k = 0; k < copies; ++k) {
+        const unsigned long long *p = w + k * copy_stride + 6 * c;
+#pragma unroll
+        for (int cls = 0; cls < 3; ++cls) {
+            const unsigned long long lo = p[2 * cls], hi = p[2 * cls + 1];
+            e1 += hi + (e0 + lo < e0 ? 1ull : 0ull);
+            e0 += lo;
+            if (cls == 0) {
+                o1 += hi + (o0 + lo < o0 ? 1ull : 0ull);
+                o0 += lo;
+            } else if (cls == 1) {
+                o1 -= hi + (o0 < lo ? 1ull : 0ull);
+                o0 -= lo;
+            }
+        }
+    }
+    even[c] = i128_to_double(e0, e1, s);
+    odd[c] = i128_to_double(o0, o1, s);
+}
+
+int finalize_class_sums(const unsigned long long *w, int64_t n, int copies, int64_t copy_stride,
+                        int s, double *even, double *odd, hipStream_t st) {
+    if (n <= 0) return GTC_OK;
+    hipLaunchKernelGGL(k_finalize_class_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       w, n, copies, copy_stride, s, even, odd);
+    GTC_HIP_CHECK(hipGetLastError());
+    return GTC_OK;
+}
+
+int finalize_limbs(const unsigned long long *limbs, int64_t n, int copies, int64_t copy_stride,
+                   const unsigned long long *counts, int s, double *out, hipStream_t st) {
+    if (n <= 0) return GTC_OK;
+    hipLaunchKernelGGL(k_finalize_limbs, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       limbs, n, copies, copy_stride, counts, s, out);
+    GTC_HIP_CHECK(hipGetLastError());
+    return GTC_OK;
+}
+
 // ------------------------------------------------------------------ exclusive scan
 // Three passes: per-block totals, a scan of the totals (recursive), per-block rescans.
 constexpr int kScanThreads = 256;
