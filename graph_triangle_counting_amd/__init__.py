@@ -71,6 +71,7 @@ def lib() -> C.CDLL:
         L.gtc_count_4pcf_parity.argtypes = [P, P, P, C.POINTER(Stats), P]
         L.gtc_count_4pcf_weighted.argtypes = [P, P, i32, P, P, P, P, C.POINTER(Stats), P]
         L.gtc_linear_edges_sq.argtypes = [i64, i64, i32, P]
+        L.gtc_equilateral_configs.argtypes = [i32, i32, i32, P]
         L.gtc_compute_3pcf.argtypes = [P, i64, P, P, i64, P, P, i32, C.POINTER(Options), P, P, P,
                                        C.POINTER(Stats), P]
         L.gtc_compute_4pcf.argtypes = [P, i64, P, P, i64, P, P, i32, C.POINTER(Options), P, P, P,
@@ -341,10 +342,25 @@ def linear_edges_sq(r_min: int, r_max: int, nbins: int) -> np.ndarray:
     return e
 
 
+def equilateral_configs(order: int, nbins: int, s4: bool = False) -> np.ndarray:
+    """int64 [nbins]: the rank of the configuration with every edge in bin b (the equilateral
+    3pCF's configurations; order 4: the regular tetrahedra, sorted 6-tuples or S4)."""
+    out = np.empty(int(nbins), np.int64)
+    _check(lib().gtc_equilateral_configs(int(order), int(bool(s4)), int(nbins),
+                                         out.ctypes.data_as(C.c_void_p)))
+    return out
+
+
 class Result3pcf:
     """compute_3pcf's result: zeta, NNN, RRR per configuration (fp64 host arrays); bins
     [n_cfg][3] the nondecreasing bin triple of each configuration; r1, r2, r3 its bin centres
-    (midpoints in r, grid units); edges_sq the squared edges; stats."""
+    (midpoints in r, grid units); edges_sq the squared edges; stats.  equilateral() gives the
+    equilateral 3pCF, one value per bin."""
+
+    def equilateral(self) -> dict:
+        """The configurations with all three sides in one bin: r (bin centres), zeta, NNN, RRR."""
+        k = equilateral_configs(3, self.edges_sq.size - 1)
+        return {"r": self.r1[k], "zeta": self.zeta[k], "NNN": self.NNN[k], "RRR": self.RRR[k]}
 
 
 class Result4pcf:

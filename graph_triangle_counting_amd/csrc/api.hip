@@ -394,6 +394,40 @@ int gtc_config_bins_s4(int32_t nbins, int32_t *h_bins) {
     return GTC_OK;
 }
 
+int gtc_equilateral_configs(int32_t order, int32_t s4, int32_t nbins, int64_t *h_ranks) {
+    const bool ok3 = order == 3 && !s4 && nbins >= 1 && nbins <= GTC_MAX_BINS;
+    const bool ok4 = order == 4 && nbins >= 1 && nbins <= GTC_MAX_BINS_4PCF;
+    if (!(ok3 || ok4) || !h_ranks) {
+        set_error("gtc_equilateral_configs: order 3 (nbins <= %d, s4 = 0) or 4 (nbins <= %d), "
+                  "h_ranks non-NULL", GTC_MAX_BINS, GTC_MAX_BINS_4PCF);
+        return GTC_E_INVALID;
+    }
+    if (order == 4 && s4) {  // (b, b, b, b, b, b) is its own canonical tuple; find its rank
+        std::vector<int32_t> t(6 * (size_t)num_configs_s4(nbins));
+        config_bins_s4(nbins, t.data());
+        const int64_t n = (int64_t)t.size() / 6;
+        for (int b = 0, c = 0; b < nbins; ++b) {
+            while (c < n && !(t[6 * c] == b && t[6 * c + 5] == b)) ++c;
+            h_ranks[b] = c;
+        }
+        return GTC_OK;
+    }
+    // nondecreasing k-tuples lexicographically below (b, ..., b): those whose first element
+    // x < b, multichoose(nbins - x, k - 1) = C(nbins - x + k - 2, k - 1) of them for each x
+    const int k = order == 3 ? 3 : 6;
+    auto binom = [](int64_t n, int r) {
+        int64_t c = 1;
+        for (int u = 1; u <= r; ++u) c = c * (n - r + u) / u;
+        return c;
+    };
+    int64_t rank = 0;
+    for (int b = 0; b < nbins; ++b) {
+        h_ranks[b] = rank;
+        rank += binom(nbins - b + k - 2, k - 1);
+    }
+    return GTC_OK;
+}
+
 int gtc_config_realizable_s4(int32_t nbins, const int64_t *h_edges_sq, uint8_t *h_mask) {
     if (nbins < 1 || nbins > GTC_MAX_BINS_4PCF || !h_edges_sq || !h_mask) {
         set_error("gtc_config_realizable_s4: nbins in [1, %d], h_edges_sq and h_mask non-NULL",

@@ -598,14 +598,6 @@ static int weight_scale_for(double maxabs) {
     return 57 - e;
 }
 
-static double limbs_to_double(const unsigned long long *l, unsigned long long count, int s) {
-    const unsigned __int128 lo = ((unsigned __int128)l[1] << 64) | l[0];
-    const unsigned __int128 hi = ((unsigned __int128)l[3] << 64) | l[2];
-    const unsigned __int128 u = (hi << 28) + lo - ((unsigned __int128)count << 57);
-    const __int128 v = (__int128)u;  // exact sum of q, two's complement
-    return std::ldexp((double)v, -s);
-}
-
 int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
                       gtc_stats *st, hipStream_t s, const HubSubset *sub) {
     // hubs to count: the graph's (per window), or a caller's subset (one-window graphs)
@@ -869,12 +861,14 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             }
         }
     }
-    std::vector<unsigned long long> h_counts(ncfg), h_limbs(W ? 4 * ncfg : 0);
+    // exact sums to doubles on the device, one rounding per configuration
+    if (W)
+        TSTEP(finalize_limbs(limbs, ncfg, 1, 4 * ncfg,
+                             reinterpret_cast<const unsigned long long *>(d_counts), scale,
+                             d_weighted, s));
+    std::vector<unsigned long long> h_counts(ncfg);
     TSTEP_HIP(hipMemcpyAsync(h_counts.data(), d_counts, sizeof(uint64_t) * ncfg,
                              hipMemcpyDeviceToHost, s));
-    if (W)
-        TSTEP_HIP(hipMemcpyAsync(h_limbs.data(), limbs, sizeof(unsigned long long) * 4 * ncfg,
-                                hipMemcpyDeviceToHost, s));
     TSTEP_HIP(hipStreamSynchronize(s));
     if (cs) TSTEP_HIP(hipStreamSynchronize(cs));
     for (size_t e = 0; e + 1 < kev.size(); e += 2) {
@@ -886,13 +880,6 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         float t = 0.f;
         TSTEP_HIP(hipEventElapsedTime(&t, cev[e], cev[e + 1]));
         h2d_ms += t;
-    }
-    if (W) {
-        std::vector<double> h_w(ncfg);
-        for (int64_t c = 0; c < ncfg; ++c) h_w[c] = limbs_to_double(&h_limbs[4 * c], h_counts[c], scale);
-        TSTEP_HIP(hipMemcpyAsync(d_weighted, h_w.data(), sizeof(double) * ncfg,
-                                hipMemcpyHostToDevice, s));
-        TSTEP_HIP(hipStreamSynchronize(s));
     }
     unsigned long long tri = 0;
     for (auto v : h_counts) tri += v;

@@ -199,24 +199,12 @@ int count_2pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             return finish(hip_fail(hipGetLastError(), "k_pair_hist", __FILE__, __LINE__));
         kms += t;
     }
-    if (W) {
-        std::vector<unsigned long long> hl(4 * (size_t)nb), hc(nb);
-        hipError_t e = hipMemcpyAsync(hl.data(), limbs, sizeof(unsigned long long) * 4 * nb,
-                                      hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess)
-            e = hipMemcpyAsync(hc.data(), d_counts, sizeof(uint64_t) * nb, hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return finish(hip_fail(e, "2pCF readback", __FILE__, __LINE__));
-        std::vector<double> hw(nb);
-        for (int b = 0; b < nb; ++b) {
-            const unsigned __int128 lo128 = ((unsigned __int128)hl[4 * b + 1] << 64) | hl[4 * b];
-            const unsigned __int128 hi128 = ((unsigned __int128)hl[4 * b + 3] << 64) | hl[4 * b + 2];
-            const unsigned __int128 u = (hi128 << 28) + lo128 - ((unsigned __int128)hc[b] << 57);
-            hw[b] = std::ldexp((double)(__int128)u, -scale);  // one rounding of the exact sum
-        }
-        e = hipMemcpyAsync(d_weighted, hw.data(), sizeof(double) * nb, hipMemcpyHostToDevice, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) return finish(hip_fail(e, "2pCF weighted upload", __FILE__, __LINE__));
+    if (W) {  // exact sums to doubles on the device, one rounding per bin
+        rc = finalize_limbs(limbs, nb, 1, 4 * nb, reinterpret_cast<const unsigned long long *>(d_counts),
+                            scale, d_weighted, s);
+        if (rc) return finish(rc);
+        hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return finish(hip_fail(e, "2pCF finalize", __FILE__, __LINE__));
     }
     if (st) {
         st->kernel_ms = kms;

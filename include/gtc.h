@@ -213,6 +213,14 @@ int64_t gtc_num_configs_s4(int32_t nbins);
 int gtc_config_bins_s4(int32_t nbins, int32_t *h_bins);
 int gtc_config_realizable_s4(int32_t nbins, const int64_t *h_edges_sq, uint8_t *h_mask);
 
+/* The equilateral configurations (§III.5's equilateral 3pCF query; its 4pCF analogue, the regular
+ * tetrahedron): h_ranks[b] = the rank of the configuration whose edges all lie in bin b, for b <
+ * nbins, among gtc_config_bins(3 or 4, nbins) (s4 == 0) or gtc_config_bins_s4(nbins) (order 4,
+ * s4 != 0).  The equilateral 3pCF of bin b is a 3pCF output at h_ranks[b].  Host only.
+ *   h_ranks host int64 [nbins].  GTC_E_INVALID for order not 3 or 4, s4 with order 3, nbins out
+ *   of range or h_ranks NULL. */
+int gtc_equilateral_configs(int32_t order, int32_t s4, int32_t nbins, int64_t *h_ranks);
+
 /* Number of configurations: C(nbins+2, 3) for order 3, C(nbins+5, 6) for order 4; -1 if the
  * order or nbins is out of range. */
 int64_t gtc_num_configs(int32_t order, int32_t nbins);

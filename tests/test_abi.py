@@ -208,3 +208,25 @@ def test_estimators_reject_bad_arguments_without_gpu():
     assert c4(17, None, o) == gtc.GTC_E_INVALID  # beyond the 4pCF's 16 bins
     assert c4(2, None, None) == gtc.GTC_E_INVALID
     assert c4(2, C.byref(gtc.Options(0, 0, 1)), o) == gtc.GTC_E_INVALID  # coordinates dropped
+
+
+@pytest.mark.parametrize("order,s4,nb", [(3, False, 1), (3, False, 7), (3, False, 255), (4, False, 1),
+                                         (4, False, 8), (4, False, 16), (4, True, 1), (4, True, 5),
+                                         (4, True, 8)])
+def test_equilateral_configs_point_at_all_equal_tuples(order, s4, nb):
+    ranks = gtc.equilateral_configs(order, nb, s4)
+    k = 3 if order == 3 else 6
+    if nb <= 16 and not s4:  # against itertools' lexicographic nondecreasing tuples
+        tuples = list(itertools.combinations_with_replacement(range(nb), k))
+        assert [tuples[r] for r in ranks] == [(b,) * k for b in range(nb)]
+    bins = gtc.config_bins_s4(nb) if s4 else gtc.config_bins(order, nb)
+    np.testing.assert_array_equal(bins[ranks], np.repeat(np.arange(nb), k).reshape(nb, k))
+    assert np.all(np.diff(ranks) > 0)
+
+
+def test_equilateral_configs_reject_bad_arguments():
+    L = gtc.lib()
+    out = np.zeros(300, np.int64).ctypes.data_as(C.c_void_p)
+    for order, s4, nb in ((2, 0, 4), (3, 1, 4), (3, 0, 0), (3, 0, 256), (4, 0, 17), (4, 1, 0)):
+        assert L.gtc_equilateral_configs(order, s4, nb, out) == gtc.GTC_E_INVALID
+    assert L.gtc_equilateral_configs(3, 0, 4, None) == gtc.GTC_E_INVALID

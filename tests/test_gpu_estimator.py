@@ -7,6 +7,8 @@ Configurations without random cliques give NaN or infinity on both sides.
 """
 from __future__ import annotations
 
+import itertools
+
 import numpy as np
 import pytest
 
@@ -109,6 +111,13 @@ def test_compute_3pcf_matches_oracle(gpu_available, seed, nd, nr, rmin, rmax, nb
     np.testing.assert_array_equal(r.bins, gtc.config_bins(3, nb))
     c = 0.5 * (np.sqrt(edges[:-1].astype(float)) + np.sqrt(edges[1:].astype(float)))
     np.testing.assert_array_equal(r.r3, c[r.bins[:, 2]])
+    # the equilateral 3pCF: the configurations (b, b, b)
+    cfg = list(itertools.combinations_with_replacement(range(nb), 3))
+    eq = r.equilateral()
+    k = [cfg.index((b, b, b)) for b in range(nb)]
+    np.testing.assert_array_equal(eq["zeta"], z[k])
+    np.testing.assert_array_equal(eq["RRR"], rrr[k])
+    np.testing.assert_array_equal(eq["r"], c)
 
 
 @pytest.mark.parametrize("mode", ["host", "rebuild"])
