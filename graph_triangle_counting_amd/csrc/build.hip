@@ -72,6 +72,8 @@ __device__ __forceinline__ double sq_dist(const int4 a, const int4 b) {
     return dx * dx + dy * dy + dz * dz;
 }
 
+constexpr int kPairLoads = 8;
+
 template <bool EMIT>
 __global__ void __launch_bounds__(256) k_pairs(PairArgs a) {
     __shared__ double se[GTC_MAX_BINS + 1];
@@ -87,28 +89,37 @@ __global__ void __launch_bounds__(256) k_pairs(PairArgs a) {
     int32_t cnt = 0;
     int64_t w = EMIT ? a.row_ptr[i] - a.col_base : 0;
     const int nb = a.nb;
-    auto scan = [&](int32_t lo, int32_t hi) {
-        for (int32_t j = lo; j < hi; ++j) {
-            const double d2 = sq_dist(a.xyz_s[j], pi);
-            if (d2 >= e0 && d2 < emax) {
-                if (EMIT) {
-                    int l = 0, h = nb;  // se[l] <= d2 < se[h]
-                    while (h - l > 1) {
-                        const int m = (l + h) >> 1;
-                        if (d2 >= se[m]) l = m; else h = m;
-                    }
-                    if (a.bin) {
-                        a.col[w] = j;
-                        a.bin[w] = (uint8_t)l;
-                    } else {
-                        a.col[w] = (int32_t)pack_entry(j, l);
-                    }
-                    ++w;
-                } else {
-                    ++cnt;
+    auto test = [&](int32_t j, double d2) __attribute__((always_inline)) {
+        if (d2 >= e0 && d2 < emax) {
+            if (EMIT) {
+                int l = 0, h = nb;  // se[l] <= d2 < se[h]
+                while (h - l > 1) {
+                    const int m = (l + h) >> 1;
+                    if (d2 >= se[m]) l = m; else h = m;
                 }
+                if (a.bin) {
+                    a.col[w] = j;
+                    a.bin[w] = (uint8_t)l;
+                } else {
+                    a.col[w] = (int32_t)pack_entry(j, l);
+                }
+                ++w;
+            } else {
+                ++cnt;
             }
         }
+    };
+    // candidates of a cell, kPairLoads coordinate loads in flight per lane
+    auto scan = [&](int32_t lo, int32_t hi) {
+        int32_t j = lo;
+        for (; j + kPairLoads <= hi; j += kPairLoads) {
+            int4 pj[kPairLoads];
+#pragma unroll
+            for (int u = 0; u < kPairLoads; ++u) pj[u] = a.xyz_s[j + u];
+#pragma unroll
+            for (int u = 0; u < kPairLoads; ++u) test(j + u, sq_dist(pj[u], pi));
+        }
+        for (; j < hi; ++j) test(j, sq_dist(a.xyz_s[j], pi));
     };
     // slot 0: own cell (labels above i); slots 1..13: the forward cells in key order.  The emit
     // pass records where each slot starts in the row (empty slots for cells outside the grid).
@@ -166,7 +177,7 @@ __global__ void __launch_bounds__(256)
                const int32_t *__restrict__ key_s, const int32_t *__restrict__ cell_start, Grid gr,
                int64_t *__restrict__ work, StatsOut *out, unsigned long long *win_last) {
     constexpr int L = 16;
-    __shared__ unsigned long long red[6][256 / kWave];
+    __shared__ unsigned long long red[7][256 / kWave];
     const int sub = threadIdx.x & (L - 1);
     const int64_t hub0 = h_lo + (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) / L;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x / L;
@@ -210,8 +221,8 @@ __global__ void __launch_bounds__(256)
     my_hubs = wave_sum_u64(my_hubs);
     my_max_band = wave_max_u64(my_max_band);
     my_last = wave_max_u64(my_last);
-    if (lane == 0) atomicMax(win_last, my_last);
     if (lane == 0) {
+        red[6][wid] = my_last;
         red[5][wid] = my_max_band;
         red[0][wid] = my_max_deg;
         red[1][wid] = my_max_dom;
@@ -221,8 +232,9 @@ __global__ void __launch_bounds__(256)
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        unsigned long long v[6] = {0, 0, 0, 0, 0, 0};
+        unsigned long long v[7] = {0, 0, 0, 0, 0, 0, 0};
         for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+            v[6] = red[6][w] > v[6] ? red[6][w] : v[6];
             v[0] = red[0][w] > v[0] ? red[0][w] : v[0];
             v[1] = red[1][w] > v[1] ? red[1][w] : v[1];
             v[2] += red[2][w];
@@ -236,6 +248,7 @@ __global__ void __launch_bounds__(256)
         atomicAdd(&out->walks, v[3]);
         atomicAdd(&out->n_hubs, v[4]);
         atomicMax(&out->max_band, v[5]);
+        if (v[6]) atomicMax(win_last, v[6]);
     }
 }
 
@@ -700,23 +713,44 @@ int emit_window(const gtc_graph_s *G, int64_t w, int32_t *col, uint8_t *bin, hip
 
 // Weights into internal order: w_s[pos] = w[perm[pos]], and max |w| (bit pattern of a
 // non-negative double orders like its value) plus a flag for non-finite values.
-__global__ void k_gather_weights(int64_t n, const double *__restrict__ w,
-                                 const int32_t *__restrict__ perm, double *__restrict__ w_s,
-                                 unsigned long long *__restrict__ maxabs_bits,
-                                 int32_t *__restrict__ bad) {
-    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+// w_s[i] = w[perm[i]]; max |w| and a non-finite flag reduced per workgroup, then one atomic per
+// workgroup (atomics on one address serialise: one per wave cost ~0.2 ms per million points)
+constexpr int kGatherThreads = 256;
+__global__ void __launch_bounds__(kGatherThreads)
+k_gather_weights(int64_t n, const double *__restrict__ w, const int32_t *__restrict__ perm,
+                 double *__restrict__ w_s, unsigned long long *__restrict__ maxabs_bits,
+                 int32_t *__restrict__ bad) {
+    __shared__ unsigned long long wmax[kGatherThreads / kWave];
+    __shared__ int32_t wbad[kGatherThreads / kWave];
     unsigned long long m = 0;
-    if (i < n) {
+    int32_t nf = 0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
         const double v = w[perm[i]];
         w_s[i] = v;
-        if (!isfinite(v)) atomicOr(bad, 1);
-        m = (unsigned long long)__double_as_longlong(fabs(v));
+        nf |= !isfinite(v);
+        const unsigned long long b = (unsigned long long)__double_as_longlong(fabs(v));
+        m = b > m ? b : m;
     }
     for (int d = kWave / 2; d > 0; d >>= 1) {
         const unsigned long long o = __shfl_xor(m, d, kWave);
         m = o > m ? o : m;
+        nf |= __shfl_xor(nf, d, kWave);
     }
-    if ((threadIdx.x & (kWave - 1)) == 0 && m) atomicMax(maxabs_bits, m);
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+    if (lane == 0) {
+        wmax[wid] = m;
+        wbad[wid] = nf;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int t = 1; t < kGatherThreads / kWave; ++t) {
+            m = wmax[t] > m ? wmax[t] : m;
+            nf |= wbad[t];
+        }
+        if (m) atomicMax(maxabs_bits, m);
+        if (nf) atomicOr(bad, 1);
+    }
 }
 
 int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, unsigned long long *d_m,
@@ -726,7 +760,8 @@ int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, unsigne
     unsigned long long hm = 0;
     int32_t hb = 0;
     if (!rc && G->n > 0) {
-        hipLaunchKernelGGL(k_gather_weights, dim3(grid_for(G->n, 256)), dim3(256), 0, s, G->n, d_w,
+        const unsigned blocks = (unsigned)std::min<int64_t>((G->n + kGatherThreads - 1) / kGatherThreads, 2048);
+        hipLaunchKernelGGL(k_gather_weights, dim3(blocks), dim3(kGatherThreads), 0, s, G->n, d_w,
                            G->perm, w_s, d_m, d_bad);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) rc = hip_fail(e, "k_gather_weights", __FILE__, __LINE__);
