@@ -114,6 +114,21 @@ __device__ __forceinline__ void flush_hist(int ncfg, unsigned long long *counts,
     }
 }
 
+// The same for a histogram over the unsorted bin triple t = (b0 nb + b1) nb + b2 (nb^3 bins):
+// each bin is added to the rank of its sorted triple.
+__device__ __forceinline__ void flush_hist_unsorted(int nb, unsigned long long *counts, uint32_t *hu,
+                                                    const int32_t *rA, const int32_t *rB, int first,
+                                                    int step) {
+    const int nh = nb * nb * nb;
+    for (int t = first; t < nh; t += step) {
+        const uint32_t v = atomicExch(&hu[t], 0u);
+        if (!v) continue;
+        const int b0 = t / (nb * nb), b1 = (t / nb) % nb, b2 = t % nb;
+        const int x = min(b0, min(b1, b2)), z = max(b0, max(b1, b2)), y = b0 + b1 + b2 - x - z;
+        atomicAdd(&counts[rA[x] + rB[y] + z], (unsigned long long)v);
+    }
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -150,13 +165,18 @@ __host__ __device__ constexpr int band_slot(int q) { return q == 0 ? 0 : 3 * q -
 // smax [5]) | per-wave regions
 constexpr size_t kBandTableBytes = 160;
 
-template <bool W, bool GH, bool BANDED, bool PK>
+// UH (unweighted, LDS histogram, few bins): hits go to a histogram over the unsorted bin triple
+// (bij, bik, bjk), nb^3 bins, with neither a sort nor a rank lookup per triangle; the bins are
+// folded onto configuration ranks when the histogram is exchanged.
+template <bool W, bool GH, bool BANDED, bool PK, bool UH>
 __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
+    static_assert(!UH || (!W && !GH), "the unsorted histogram is an unweighted LDS histogram");
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     size_t off = 0;
     uint32_t *hc = reinterpret_cast<uint32_t *>(smem);
-    if (!GH) off += align_up(sizeof(uint32_t) * a.ncfg, 16);
+    const int32_t nhist = UH ? a.nb * a.nb * a.nb : a.ncfg;
+    if (!GH) off += align_up(sizeof(uint32_t) * nhist, 16);
     unsigned long long *hlo = nullptr, *hhi = nullptr;
     if (W && !GH) {
         hlo = reinterpret_cast<unsigned long long *>(smem + off);
@@ -180,7 +200,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     double *rw = reinterpret_cast<double *>(ck + chunk_bytes(true));
 
     if (!GH)
-        for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
+        for (int t = threadIdx.x; t < nhist; t += blockDim.x) {
             hc[t] = 0;
             if (W) hlo[t] = hhi[t] = 0;
         }
@@ -194,6 +214,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     unsigned long long *const g_counts = a.counts;
     unsigned long long *const g_limbs = a.limbs;
     const double two_s = a.two_s;
+    const int32_t nbk = a.nb;
     if constexpr (BANDED)
         for (int t = threadIdx.x; t < 145; t += blockDim.x) btab[t] = a.band[t];
     __syncthreads();
@@ -322,6 +343,11 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 if (!v) return;
                 const int32_t bij = ow >> 8;
                 const int32_t bik = W ? (int32_t)(v >> 16) : (int32_t)v - 1;
+                if constexpr (UH) {
+                    atomicAdd(&hc[(bij * nbk + bik) * nbk + bjk], 1u);
+                    ++my_hits;
+                    return;
+                }
                 const int32_t x = min(bij, min(bik, bjk)), z = max(bij, max(bik, bjk));
                 const int32_t y = bij + bik + bjk - x - z;
                 const int32_t c = rA[x] + rB[y] + z;
@@ -466,7 +492,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         if (!GH) {
             wave_hits += wave_sum(my_hits);
             if (wave_hits >= a.flush_at) {
-                flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, lane, kWave);
+                if (UH) flush_hist_unsorted(nbk, g_counts, hc, rA, rB, lane, kWave);
+                else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, lane, kWave);
                 wave_hits = 0;
             }
         }
@@ -474,11 +501,14 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     }
     if (!GH) {
         __syncthreads();
-        flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, threadIdx.x, blockDim.x);
+        if (UH) flush_hist_unsorted(nbk, g_counts, hc, rA, rB, threadIdx.x, blockDim.x);
+        else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, threadIdx.x, blockDim.x);
     }
 }
 
 // ------------------------------------------------------------------ host side
+
+constexpr int kUnsortedMaxBins = 16;
 
 struct DeviceLimits {
     int cus = 0;
@@ -501,14 +531,15 @@ struct TripletPlan {
     int blocks = 0;      // persistent grid
 };
 
-static const void *triplet_kernel(bool w, bool gh, bool banded, bool pk) {
-#define GTC_K(W_, GH_, B_)                                                                  \
-    (pk ? reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_, true>)                    \
-        : reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_, false>))
-    if (w) return gh ? (banded ? GTC_K(true, true, true) : GTC_K(true, true, false))
-                     : (banded ? GTC_K(true, false, true) : GTC_K(true, false, false));
-    return gh ? (banded ? GTC_K(false, true, true) : GTC_K(false, true, false))
-              : (banded ? GTC_K(false, false, true) : GTC_K(false, false, false));
+static const void *triplet_kernel(bool w, bool gh, bool banded, bool pk, bool uh) {
+#define GTC_K(W_, GH_, B_, U_)                                                              \
+    (pk ? reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_, true, U_>)                \
+        : reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_, false, U_>))
+    if (w) return gh ? (banded ? GTC_K(true, true, true, false) : GTC_K(true, true, false, false))
+                     : (banded ? GTC_K(true, false, true, false) : GTC_K(true, false, false, false));
+    if (gh) return banded ? GTC_K(false, true, true, false) : GTC_K(false, true, false, false);
+    if (uh) return banded ? GTC_K(false, false, true, true) : GTC_K(false, false, false, true);
+    return banded ? GTC_K(false, false, true, false) : GTC_K(false, false, false, false);
 #undef GTC_K
 }
 
@@ -695,6 +726,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
 
     float kms = 0.f, h2d_ms = 0.f;
     TripletPlan used{};
+    bool uh_used = false;
     int64_t tiles_run = 0;
     std::vector<hipEvent_t> kev, cev;  // kernel and copy event pairs
     // out-of-core: window uploads run on a copy stream; per window buffer, `ready` marks its upload
@@ -734,13 +766,31 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             (unsigned long long)G->max_deg * (unsigned long long)(G->max_deg - 1) / 2;
         const bool GH = triplet_lds_fixed(a.ncfg, W, false) > dl.lds_per_block / 2 ||
                         max_hub_hits >= 0x7fffffffull / 2;
+        // Unweighted with at most 16 bins: histogram over the unsorted bin triple (nb^3 <= 4096
+        // bins) when the spoke elements per CU amortise folding nb^3 bins per workgroup.
+        // GTC_TRIPLET_HIST=unsorted or sorted forces the choice (unsorted needs the same limits).
+        const int64_t walk_elems = sub ? sub->spoke_elements : G->spoke_elements;
+        const int64_t nb3 = (int64_t)nb * nb * nb;
+        const bool uh_ok = !W && !GH && nb <= kUnsortedMaxBins;
+        bool UH = uh_ok && walk_elems >= nb3 * 1024 * (int64_t)dl.cus;
+        if (const char *env = std::getenv("GTC_TRIPLET_HIST")) {
+            if (!std::strcmp(env, "unsorted")) UH = uh_ok;
+            else if (!std::strcmp(env, "sorted")) UH = false;
+        }
         TripletPlan pl;
-        const void *kfn = triplet_kernel(W, GH, banded, G->packed);
-        TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(a.ncfg, W, GH), GH, hub_total, max_hub_hits, pl));
+        const void *kfn = triplet_kernel(W, GH, banded, G->packed, UH);
+        TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(UH ? (int)nb3 : a.ncfg, W, GH), GH, hub_total,
+                           max_hub_hits, pl));
         // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long budget = 0xffffffffull / (unsigned long long)pl.waves;
         a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub_hits);
+        // GTC_TRIPLET_FLUSH_AT=n exchanges the LDS histogram at least every n hits of a wave
+        if (const char *env = std::getenv("GTC_TRIPLET_FLUSH_AT")) {
+            const long long v = std::atoll(env);
+            if (!GH && v > 0 && (unsigned long long)v < a.flush_at) a.flush_at = (unsigned int)v;
+        }
         used = pl;
+        uh_used = UH;
 
         // Tile loop (§III.5.3): hub window h against search windows s = h .. smax(h).  A walk
         // (i, j) runs in the tile (window of i, window of j) only; a resident untiled graph is one
@@ -894,7 +944,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         st->launch_waves = used.waves;
         st->launch_blocks = used.blocks;
         st->launch_lds_bytes = (int32_t)used.lds;
-        st->launch_mode = banded ? 1 : 0;
+        st->launch_mode = (banded ? 1 : 0) | (uh_used ? 2 : 0);
         // hub rows read once (5 B per entry), spoke rows once per walk (4 B), a bin per triangle
         st->q_alg_bytes = 5.0 * (double)(sub ? sub->walks : G->E) +
                           4.0 * (double)st->spoke_elements + (double)tri;

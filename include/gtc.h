@@ -105,7 +105,8 @@ typedef struct {
     int32_t launch_waves;      /* enumeration kernel: waves per workgroup */
     int32_t launch_blocks;     /* enumeration kernel: persistent workgroups */
     int32_t launch_lds_bytes;  /* enumeration kernel: LDS per workgroup */
-    int32_t launch_mode;       /* 3pCF walk: 0 one map over the hub domain, 1 banded by key run */
+    int32_t launch_mode;       /* 3pCF: bit 0 banded walk (else one map over the hub domain),
+                                  bit 1 histogram over the unsorted bin triple */
     int32_t launch_reserved;
     double build_ms;           /* gtc_build_graph: whole call */
     double kernel_ms;          /* enumeration kernels only (sum over tiles) */

@@ -86,6 +86,52 @@ def test_3pcf_matches_oracle(gpu_available, kind, seed, n, r, nb, weighted):
 
 @pytest.mark.parametrize("layout", ["packed", "split"])
 @pytest.mark.parametrize("mode", ["flat", "banded"])
+@pytest.mark.parametrize("kind,seed,n,r,nb", [
+    ("uniform", 16, 20_000, 40_000, 1),
+    ("clustered", 17, 30_000, 12_000, 7),
+    ("uniform", 18, 12_000, 60_000, 16),
+])
+def test_3pcf_unsorted_histogram(gpu_available, monkeypatch, layout, mode, kind, seed, n, r, nb):
+    # the histogram over the unsorted bin triple (nb^3 bins, folded onto ranks at each exchange)
+    # gives the oracle's counts in both walk modes and layouts
+    say("3pcf unsorted", mode, layout, kind, seed, n, r, nb)
+    monkeypatch.setenv("GTC_TRIPLET_MODE", mode)
+    monkeypatch.setenv("GTC_TRIPLET_HIST", "unsorted")
+    if layout == "split":
+        monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
+    xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 60, 2500)
+    edges = linear_edges_sq(r, nb)
+    c, _, st = hip_3pcf(xyz, edges)
+    assert st["launch_mode"] == (1 if mode == "banded" else 0) | 2
+    oc, _, _, _ = oracle.Graph(xyz, edges).count_3pcf()
+    np.testing.assert_array_equal(c, oc)
+    assert oc.sum() > 0
+
+
+@pytest.mark.parametrize("hist", ["sorted", "unsorted"])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_3pcf_frequent_histogram_exchanges(gpu_available, monkeypatch, hist, weighted):
+    # waves exchange the LDS histogram every few hundred hits while the others keep adding to it:
+    # every increment still reaches the global counts exactly once
+    if hist == "unsorted" and weighted:
+        pytest.skip("the unsorted histogram is unweighted only")
+    say("3pcf exchanges", hist, weighted)
+    monkeypatch.setenv("GTC_TRIPLET_HIST", hist)
+    monkeypatch.setenv("GTC_TRIPLET_FLUSH_AT", "300")
+    xyz = clustered(19, 20_000, 60, 2500)
+    edges = linear_edges_sq(10_000, 12)
+    w = 0.5 + rng_for(1019).random(20_000) if weighted else None
+    c, ws, st = hip_3pcf(xyz, edges, w)
+    assert bool(st["launch_mode"] & 2) == (hist == "unsorted")
+    oc, ows, _, _ = oracle.Graph(xyz, edges).count_3pcf(w)
+    assert oc.sum() > 100 * 300
+    np.testing.assert_array_equal(c, oc)
+    if weighted:
+        np.testing.assert_array_equal(ws, ows)
+
+
+@pytest.mark.parametrize("layout", ["packed", "split"])
+@pytest.mark.parametrize("mode", ["flat", "banded"])
 @pytest.mark.parametrize("kind,seed,n,r,nb,weighted", CASES_3[1:4])
 def test_3pcf_walk_modes(gpu_available, monkeypatch, layout, mode, kind, seed, n, r, nb, weighted):
     # the two spoke walks (one map over the hub domain / one map per key run), on both CSR layouts
@@ -98,7 +144,7 @@ def test_3pcf_walk_modes(gpu_available, monkeypatch, layout, mode, kind, seed, n
     edges = linear_edges_sq(r, nb)
     w = 0.5 + rng_for(seed + 1000).random(n) if weighted else None
     c, ws, st = hip_3pcf(xyz, edges, w)
-    assert st["launch_mode"] == (1 if mode == "banded" else 0)
+    assert st["launch_mode"] & 1 == (1 if mode == "banded" else 0)
     oc, ows, s, _ = oracle.Graph(xyz, edges).count_3pcf(w)
     np.testing.assert_array_equal(c, oc)
     if weighted:
