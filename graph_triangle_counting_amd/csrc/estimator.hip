@@ -3,8 +3,10 @@
 //
 // One graph over the union of a data catalogue D and a random catalogue R.  The numerators take
 // the signed, normalised weights of the Szapudi-Szalay estimator: data w / sum_D w, randoms
-// -w / sum_R w; the normalisation takes the random weights alone, w / sum_R w on R and 0 on D, on
-// the same graph.  Then zeta = NNN / RRR (3pCF), zeta_even = NNNN_even / RRRR and zeta_odd =
+// -w / sum_R w.  The normalisation takes the random weights alone, w / sum_R w on R and 0 on D;
+// only all-random cliques add to it, so it is counted on a graph of R alone, which has the same
+// all-random cliques, bins and scale (max |w| over R), hence the same exact sums, at a fraction
+// of the cliques.  Then zeta = NNN / RRR (3pCF), zeta_even = NNNN_even / RRRR and zeta_odd =
 // NNNN_odd / RRRR (4pCF, S4 configurations), xi = NN / RR (internal 2pCF), and the connected
 // 4pCF zeta_even - disc(xi) of Eq. (4) and (5).  The catalogue sums are correctly rounded, so the
 // normalised weights are reproducible bit for bit.
@@ -57,7 +59,8 @@ double exact_sum(const std::vector<double> &x) {
 }
 
 struct Catalogue {
-    std::vector<double> w_signed, w_rand;  // host, n_data + n_rand
+    std::vector<double> w_signed;  // host, n_data + n_rand: data then randoms
+    std::vector<double> w_rand;    // host, n_rand: w / sum_R w
 };
 
 // the estimator weights from the raw weights (NULL: unit weights)
@@ -79,16 +82,17 @@ int make_weights(const double *d_w_data, int64_t nd, const double *d_w_rand, int
     if (nd > 0 && sd == 0.0) { set_error("the data weights sum to zero"); return GTC_E_INVALID; }
     if (sr == 0.0) { set_error("the random weights sum to zero"); return GTC_E_INVALID; }
     cat->w_signed.resize(nd + nr);
-    cat->w_rand.assign(nd + nr, 0.0);
+    cat->w_rand.resize(nr);
     for (int64_t i = 0; i < nd; ++i) cat->w_signed[i] = wd[i] / sd;
     for (int64_t i = 0; i < nr; ++i) {
-        cat->w_signed[nd + i] = -(wr[i] / sr);
-        cat->w_rand[nd + i] = wr[i] / sr;
+        cat->w_rand[i] = wr[i] / sr;
+        cat->w_signed[nd + i] = -cat->w_rand[i];
     }
     return GTC_OK;
 }
 
-// D then R, concatenated on the device; the estimator's two weight vectors uploaded
+// D then R, concatenated on the device; the signed weights over D then R, the random weights
+// over R
 struct DeviceUnion {
     void *block = nullptr;
     int32_t *xyz = nullptr;
@@ -101,7 +105,7 @@ int make_union(const int32_t *d_xd, int64_t nd, const int32_t *d_xr, int64_t nr,
     GTC_TRY(carve_alloc(&u->block, s, [&](Carver &c) {
         c.take(&u->xyz, 3 * (size_t)n);
         c.take(&u->w_signed, n);
-        c.take(&u->w_rand, n);
+        c.take(&u->w_rand, nr);
     }));
     if (nd)
         GTC_HIP_CHECK(hipMemcpyAsync(u->xyz, d_xd, sizeof(int32_t) * 3 * nd,
@@ -111,7 +115,7 @@ int make_union(const int32_t *d_xd, int64_t nd, const int32_t *d_xr, int64_t nr,
                                      hipMemcpyDeviceToDevice, s));
     GTC_HIP_CHECK(hipMemcpyAsync(u->w_signed, cat.w_signed.data(), sizeof(double) * n,
                                  hipMemcpyHostToDevice, s));
-    GTC_HIP_CHECK(hipMemcpyAsync(u->w_rand, cat.w_rand.data(), sizeof(double) * n,
+    GTC_HIP_CHECK(hipMemcpyAsync(u->w_rand, cat.w_rand.data(), sizeof(double) * nr,
                                  hipMemcpyHostToDevice, s));
     return GTC_OK;
 }
@@ -181,8 +185,9 @@ int gtc_compute_3pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_
     GTC_TRY(make_weights(d_w_data, n_data, d_w_rand, n_rand, s, &cat));
     DeviceUnion u;
     int rc = make_union(d_xyz_data, n_data, d_xyz_rand, n_rand, cat, s, &u);
-    gtc_graph g = nullptr;
+    gtc_graph g = nullptr, gr = nullptr;
     if (!rc) rc = gtc_build_graph(u.xyz, n_data + n_rand, h_edges_sq, nbins, opt, hip_stream, &g);
+    if (!rc) rc = gtc_build_graph(d_xyz_rand, n_rand, h_edges_sq, nbins, opt, hip_stream, &gr);
     uint64_t *d_counts = nullptr;
     double *d_sum = nullptr;
     void *blk = nullptr;
@@ -194,7 +199,7 @@ int gtc_compute_3pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_
     gtc_stats st1{}, st2{};
     if (!rc) rc = gtc_count_3pcf(g, u.w_signed, d_counts, d_sum, &st1, hip_stream);
     if (!rc) rc = to_host(nnn, d_sum, ncfg, s);
-    if (!rc) rc = gtc_count_3pcf(g, u.w_rand, d_counts, d_sum, &st2, hip_stream);
+    if (!rc) rc = gtc_count_3pcf(gr, u.w_rand, d_counts, d_sum, &st2, hip_stream);
     if (!rc) rc = to_host(rrr, d_sum, ncfg, s);
     if (!rc) {
         for (int64_t c = 0; c < ncfg; ++c) {
@@ -209,6 +214,7 @@ int gtc_compute_3pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_
         }
     }
     if (g) gtc_graph_free(g);
+    if (gr) gtc_graph_free(gr);
     dev_free(blk, s);
     dev_free(u.block, s);
     (void)hipStreamSynchronize(s);
@@ -239,8 +245,9 @@ int gtc_compute_4pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_
     GTC_TRY(make_weights(d_w_data, n_data, d_w_rand, n_rand, s, &cat));
     DeviceUnion u;
     int rc = make_union(d_xyz_data, n_data, d_xyz_rand, n_rand, cat, s, &u);
-    gtc_graph g = nullptr;
+    gtc_graph g = nullptr, gr = nullptr;
     if (!rc) rc = gtc_build_graph(u.xyz, n_data + n_rand, h_edges_sq, nbins, opt, hip_stream, &g);
+    if (!rc) rc = gtc_build_graph(d_xyz_rand, n_rand, h_edges_sq, nbins, opt, hip_stream, &gr);
     uint64_t *d_even = nullptr, *d_pairs = nullptr;
     int64_t *d_odd = nullptr;
     double *d_ew = nullptr, *d_ow = nullptr, *d_pw = nullptr;
@@ -258,11 +265,11 @@ int gtc_compute_4pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_
     if (!rc) rc = gtc_count_4pcf_weighted(g, u.w_signed, 1, d_even, d_odd, d_ew, d_ow, &st1, hip_stream);
     if (!rc) rc = to_host(ne, d_ew, ncfg, s);
     if (!rc) rc = to_host(no, d_ow, ncfg, s);
-    if (!rc) rc = gtc_count_4pcf_weighted(g, u.w_rand, 1, d_even, d_odd, d_ew, d_ow, &st2, hip_stream);
+    if (!rc) rc = gtc_count_4pcf_weighted(gr, u.w_rand, 1, d_even, d_odd, d_ew, d_ow, &st2, hip_stream);
     if (!rc) rc = to_host(rr4, d_ew, ncfg, s);
     if (!rc) rc = gtc_count_2pcf(g, u.w_signed, d_pairs, d_pw, &st3, hip_stream);
     if (!rc) rc = to_host(nn, d_pw, nbins, s);
-    if (!rc) rc = gtc_count_2pcf(g, u.w_rand, d_pairs, d_pw, &st4, hip_stream);
+    if (!rc) rc = gtc_count_2pcf(gr, u.w_rand, d_pairs, d_pw, &st4, hip_stream);
     if (!rc) rc = to_host(rr, d_pw, nbins, s);
     if (!rc) {
         std::vector<double> xi(nbins), disc(ncfg);
@@ -281,6 +288,7 @@ int gtc_compute_4pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_
         }
     }
     if (g) gtc_graph_free(g);
+    if (gr) gtc_graph_free(gr);
     dev_free(blk, s);
     dev_free(u.block, s);
     (void)hipStreamSynchronize(s);

@@ -262,7 +262,8 @@ int gtc_linear_edges_sq(int64_t r_min, int64_t r_max, int32_t nbins, int64_t *h_
  * the compute_3pcf / compute_4pcf interface of §II.2).  One neighbour graph is built over D then
  * R (D's points take labels 0..n_data-1, R's the rest).  The numerators take the signed,
  * normalised weights w / sum_D w on D and -w / sum_R w on R (the sums rounded correctly); the
- * denominators take w / sum_R w on R and 0 on D, on the same graph:
+ * denominators take w / sum_R w on R and 0 on D, which only all-random cliques feed, so they are
+ * counted on a second graph over R alone (same cliques, bins and exact sums, fewer cliques):
  *   3pCF: zeta = NNN / RRR per configuration of gtc_count_3pcf.
  *   4pCF: zeta_even = NNNN_even / RRRR and zeta_odd = NNNN_odd / RRRR per S4 configuration of
  *         gtc_count_4pcf_parity_s4; xi = NN / RR per bin from the graph's pairs; zeta_conn =
