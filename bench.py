@@ -27,13 +27,14 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 LDS_PEAK_GBS = 128 * 256 * 2.4
 
 
-def lds_bytes(spoke_elements: int, triangles: int, weighted: bool) -> float:
+def lds_bytes(spoke_elements: int, triangles: int, weighted: bool, unsorted: bool = False) -> float:
     """Algorithmic LDS bytes of one enumeration launch: a hub-map probe per spoke element (1 B
-    entry; 4 B weighted), and per triangle the two rank-table reads (8 B) and the 32-bit counter
-    update (read and write, 8 B); weighted triangles add the spoke's sorted weight pair (16 B), the
-    third weight (8 B) and two 64-bit limb updates (32 B)."""
+    entry; 4 B weighted), and per triangle the two rank-table reads (8 B; none with the histogram
+    over the unsorted bin triple) and the 32-bit counter update (read and write, 8 B); weighted
+    triangles add the spoke's sorted weight pair (16 B), the third weight (8 B) and two 64-bit limb
+    updates (32 B)."""
     per_elem = 4.0 if weighted else 1.0
-    per_tri = 8.0 + 8.0 + (16.0 + 8.0 + 32.0 if weighted else 0.0)
+    per_tri = (0.0 if unsorted else 8.0) + 8.0 + (16.0 + 8.0 + 32.0 if weighted else 0.0)
     return per_elem * spoke_elements + per_tri * triangles
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_triplet_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "graph_triangle_counting_amd", "csrc", f)
@@ -171,7 +172,7 @@ def main():
                 "launch": {"waves_per_wg": st["launch_waves"], "workgroups": st["launch_blocks"],
                            "lds_bytes": st["launch_lds_bytes"]}}
 
-    lds_b = lds_bytes(st["spoke_elements"], T, cfg.weighted)
+    lds_b = lds_bytes(st["spoke_elements"], T, cfg.weighted, bool(st["launch_mode"] & 2))
     lds = {"achieved": lds_b / (k_avg * 1e-3) / 1e9, "peak": LDS_PEAK_GBS, "unit": "GB/s",
            "frac": lds_b / (k_avg * 1e-3) / 1e9 / LDS_PEAK_GBS, "bytes": lds_b,
            "kernel": "k_triplet"}
