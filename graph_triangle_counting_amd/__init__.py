@@ -38,7 +38,7 @@ class Stats(C.Structure):
                 ("q_alg_bytes", C.c_double), ("weight_scale", C.c_int32),
                 ("launch_waves", C.c_int32), ("launch_blocks", C.c_int32),
                 ("launch_lds_bytes", C.c_int32), ("launch_mode", C.c_int32),
-                ("launch_reserved", C.c_int32), ("build_ms", C.c_double), ("kernel_ms", C.c_double),
+                ("csr_mode", C.c_int32), ("build_ms", C.c_double), ("kernel_ms", C.c_double),
                 ("count_ms", C.c_double), ("h2d_ms", C.c_double)]
 
     def as_dict(self) -> dict:

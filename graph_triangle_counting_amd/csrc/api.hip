@@ -1,6 +1,8 @@
 // api.hip - the extern "C" boundary of libgtc: argument checks, handle lifetime, dispatch.
 #include <chrono>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <new>
 #include <vector>
 
@@ -74,6 +76,7 @@ static void fill_graph_stats(const gtc_graph_s *G, gtc_stats *st) {
     st->edges = G->E;
     st->max_out_degree = G->max_deg;
     st->windows = G->win.empty() ? 1 : (int64_t)G->win.size() - 1;
+    st->csr_mode = G->rebuild ? GTC_CSR_REBUILD : (G->host_csr ? GTC_CSR_HOST : GTC_CSR_DEVICE);
     st->spoke_elements = G->spoke_elements;
     st->build_ms = G->build_ms;
 }
@@ -145,6 +148,12 @@ int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, 
     }
     gtc_options o{};
     if (opt) o = *opt;
+    // GTC_TILE_BYTES=n sets the window budget of a build that gives none (§III.5.3)
+    if (o.tile_bytes == 0)
+        if (const char *env = std::getenv("GTC_TILE_BYTES")) {
+            const long long v = std::atoll(env);
+            if (v > 0) o.tile_bytes = v;
+        }
     if (o.csr_mode < GTC_CSR_DEVICE || o.csr_mode > GTC_CSR_REBUILD) {
         set_error("gtc_build_graph: csr_mode %d is not one of 0 (device), 1 (host), 2 (rebuild)",
                   o.csr_mode);
@@ -184,6 +193,8 @@ int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, 
     G->n = n;
     G->nb = nbins;
     G->tile_bytes = o.tile_bytes;
+    G->auto_tiles = o.tile_bytes == 0;
+    G->keep_coords_requested = !o.drop_coords;
     G->host_csr = o.csr_mode == GTC_CSR_HOST;
     G->rebuild = o.csr_mode == GTC_CSR_REBUILD;
     for (int b = 0; b <= nbins; ++b) G->edges[b] = h_edges_sq[b];
@@ -297,11 +308,6 @@ static int count_4pcf(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *
     if (!g->coords_kept) {
         set_error("%s: the graph was built with drop_coords", fn);
         return GTC_E_INVALID;
-    }
-    if (g->host_csr || g->rebuild) {
-        set_error("%s: out-of-core (csr_mode 1 or 2) graphs are not supported by the 4-clique "
-                  "kernel, which needs every spoke row of a hub at once", fn);
-        return GTC_E_UNSUPPORTED;
     }
     DeviceGuard dg(g->device);
     if (dg.rc) return dg.rc;

@@ -476,6 +476,35 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         cleanup();
         return GTC_E_INVALID;
     }
+    // Automatic chunking (§III.5.3): a build given no window budget keeps the CSR out of core when
+    // it would take more than 3/4 of the free device memory (free memory plus what the stream-
+    // ordered pool holds unused; GTC_DEVICE_FREE_BYTES=n replaces that figure, for tests).  The
+    // windows are then emitted again per tile (the coordinates are kept) or held in pinned host
+    // memory (coordinates dropped), with a budget of 1/8 of the free memory per window.
+    if (G->auto_tiles && n > 0) {
+        size_t free_b = 0, total_b = 0;
+        STEP_HIP(hipMemGetInfo(&free_b, &total_b));
+        int dev = 0;
+        hipMemPool_t pool;
+        if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetDefaultMemPool(&pool, dev) == hipSuccess) {
+            uint64_t reserved = 0, used = 0;
+            if (hipMemPoolGetAttribute(pool, hipMemPoolAttrReservedMemCurrent, &reserved) == hipSuccess &&
+                hipMemPoolGetAttribute(pool, hipMemPoolAttrUsedMemCurrent, &used) == hipSuccess &&
+                reserved > used)
+                free_b += reserved - used;
+        }
+        (void)hipGetLastError();
+        if (const char *env = std::getenv("GTC_DEVICE_FREE_BYTES")) {
+            const long long v = std::atoll(env);
+            if (v > 0) free_b = (size_t)v;
+        }
+        const int64_t csr_bytes = G->E * (G->packed ? 4 : 5);
+        if ((double)csr_bytes > 0.75 * (double)free_b) {
+            G->tile_bytes = std::max<int64_t>((int64_t)(free_b / 8), (int64_t)1 << 20);
+            if (G->keep_coords_requested) G->rebuild = true;
+            else G->host_csr = true;
+        }
+    }
     // hub windows: one window unless a tile budget is set (§III.5.3)
     G->win.assign({0, n});
     G->max_window_edges = G->E;

@@ -23,8 +23,17 @@ namespace gtc {
 
 struct CliqueArgs {
     const int64_t *row_ptr;
-    const int32_t *col;
-    const uint8_t *bin;    // null: packed entries, the bin in the top byte of col
+    // The rows a launch reads (§III.5.3, 4pCF tiles): hub rows from window h, spoke rows from
+    // windows c1 <= c2 with label ranges [w1_lo, w1_hi) and [w2_lo, w2_hi).  Entry e of the graph
+    // sits at col_x[e - base_x] (bin_x likewise; null: packed entries, the bin in the top byte).
+    // A tile counts the tetrahedra (i, a, b, c), i < a < b < c, with a in c1 and b in c2: the
+    // edges among the spokes come from the rows of a and b.  A resident graph is one tile with
+    // all three windows the whole CSR.
+    const int32_t *col_h, *col_1, *col_2;
+    const uint8_t *bin_h, *bin_1, *bin_2;
+    int64_t base_h, base_1, base_2;
+    int32_t w1_lo, w1_hi, w2_lo, w2_hi;
+    int32_t tiled;         // 0: one resident tile (every spoke in both ranges)
     uint32_t label_mask;   // label bits of a col word
     const uint32_t *s4rank;  // null: sorted 6-tuple ranks; else the S4 configuration of every
                              // base-nb key of the six bins in edge order (01,02,03,12,13,23)
@@ -182,6 +191,19 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
         const int64_t rb = a.row_ptr[i];
         const int32_t m = (int32_t)(a.row_ptr[i + 1] - rb);
         if (m < 3) continue;
+        const int32_t *hrow = a.col_h + (rb - a.base_h);
+        const uint8_t *hbin = a.bin_h ? a.bin_h + (rb - a.base_h) : nullptr;
+        auto hlab = [&](int p) { return (int32_t)((uint32_t)hrow[p] & a.label_mask); };
+        // spoke positions [p1_lo, p1_hi) in window c1 and [p2_lo, p2_hi) in window c2
+        auto lower = [&](int32_t lab) {
+            int l = 0, h = m;
+            while (l < h) { const int md = (l + h) >> 1; if (hlab(md) < lab) l = md + 1; else h = md; }
+            return l;
+        };
+        const int p1_lo = a.tiled ? lower(a.w1_lo) : 0, p1_hi = a.tiled ? lower(a.w1_hi) : m;
+        const int p2_lo = a.w2_lo == a.w1_lo ? p1_lo : lower(a.w2_lo);
+        const int p2_hi = a.w2_lo == a.w1_lo ? p1_hi : lower(a.w2_hi);
+        if (p1_lo >= p1_hi || p2_lo >= p2_hi) continue;  // no spoke pair of this tile
         const int4 pi = a.xyz_s[i];
         HubDomain dom;
         hub_domain(i, pi.w, a.gr, a.cell_start, dom);
@@ -191,7 +213,6 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
         for (int t = lane; t < ((dom.size + 1) >> 1); t += kWave) pm32[t] = 0u;
         for (int t = lane; t < m * W; t += kWave) adj[t] = 0u;
         wave_lds_sync4();
-        const int32_t *hrow = a.col + rb;
         for (int p = lane; p < m; p += kWave) {
             const uint32_t w = (uint32_t)hrow[p];
             const int32_t k = (int32_t)(w & a.label_mask);
@@ -201,19 +222,27 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                 if (k >= dom.lo[t]) d = dom.delta[t];
             pmap[k + d] = (uint16_t)(p + 1);
             rc[p] = a.xyz_s[k];
-            rbin[p] = a.bin ? a.bin[rb + p] : (uint8_t)(w >> 24);
+            rbin[p] = hbin ? hbin[p] : (uint8_t)(w >> 24);
             if (WT) rw[p] = a.w_s[k];
         }
         const double wi = WT ? a.w_s[i] : 0.0;
         wave_lds_sync4();
-        const int32_t hub_hi = (int32_t)((uint32_t)hrow[m - 1] & a.label_mask);
+        const int32_t hub_hi = hlab(m - 1);
 
-        // local connectivity: for every spoke a, walk N+(j_a) against the hub map
-        for (int sp = 0; sp < m - 1; ++sp) {
-            const int32_t j = (int32_t)((uint32_t)hrow[sp] & a.label_mask);
-            const int64_t jb = a.row_ptr[j], je = a.row_ptr[j + 1];
-            for (int64_t e = jb + lane; e < je; e += kWave) {
-                const int32_t k = (int32_t)((uint32_t)a.col[e] & a.label_mask);
+        // local connectivity: for every spoke a of the tile's windows, walk N+(j_a) against the
+        // hub map (the rows of the other spokes are not needed: no pair of this tile uses them)
+        for (int sp = p1_lo; sp < m - 1; ++sp) {
+            const bool in1 = sp < p1_hi, in2 = sp >= p2_lo && sp < p2_hi;
+            if (!in1 && !in2) {
+                if (sp >= p2_hi) break;
+                continue;
+            }
+            const int32_t j = hlab(sp);
+            const int64_t jb = a.row_ptr[j];
+            const int32_t jlen = (int32_t)(a.row_ptr[j + 1] - jb);
+            const int32_t *jrow = in1 ? a.col_1 + (jb - a.base_1) : a.col_2 + (jb - a.base_2);
+            for (int32_t e = lane; e < jlen; e += kWave) {
+                const int32_t k = (int32_t)((uint32_t)jrow[e] & a.label_mask);
                 if (k > hub_hi) break;
                 int32_t d = dom.delta[0], lim = dom.hi[0];
 #pragma unroll
@@ -230,11 +259,16 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
         }
         wave_lds_sync4();
 
-        // tetrahedra: for each local edge (a, b), common bits c of rows a and b
+        // tetrahedra: for each local edge (a, b), a in window c1 and b in window c2, common bits
+        // c of rows a and b
         unsigned int my_cl = 0;
-        for (int t = lane; t < m * W; t += kWave) {
+        for (int t = p1_lo * W + lane; t < p1_hi * W; t += kWave) {
             const int ra = t / W, wa = t - ra * W;
-            uint32_t bits = adj[t];
+            // positions [p2_lo, p2_hi) of word wa
+            const int blo = min(max(p2_lo - wa * 32, 0), 32), bhi = min(max(p2_hi - wa * 32, 0), 32);
+            const uint32_t range = (bhi >= 32 ? 0xffffffffu : ((1u << bhi) - 1u)) &
+                                   ~(blo >= 32 ? 0xffffffffu : ((1u << blo) - 1u));
+            uint32_t bits = adj[t] & range;
             while (bits) {
                 const int rbb = wa * 32 + __builtin_ctz(bits);
                 bits &= bits - 1;
@@ -514,8 +548,13 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     }
     CliqueArgs a{};
     a.row_ptr = G->row_ptr;
-    a.col = G->col;
-    a.bin = G->bin;
+    // resident: one tile with every window the whole CSR (out-of-core graphs set these per tile)
+    a.col_h = a.col_1 = a.col_2 = G->col;
+    a.bin_h = a.bin_1 = a.bin_2 = G->bin;
+    a.base_h = a.base_1 = a.base_2 = 0;
+    a.w1_lo = a.w2_lo = 0;
+    a.w1_hi = a.w2_hi = (int32_t)G->n;
+    a.tiled = 0;
     a.label_mask = G->packed ? kLabelMask : 0xffffffffu;
     a.hubs = G->hubs;
     a.n_hubs = (int32_t)G->n_hubs;
@@ -575,9 +614,20 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     void *scratch = nullptr;
     const int64_t nkeys = s4 ? num_s4_keys(G->nb) : 0;
     const int copies = WT ? weighted_copies(ncfg) : 0;
+    // out-of-core graphs (§III.5.3): three window buffers, for the hub window and the two search
+    // windows of a tile
+    const bool tiled = G->windowed();
+    constexpr int kSlots = 3;
+    int32_t *wcol[kSlots] = {nullptr, nullptr, nullptr};
+    uint8_t *wbin[kSlots] = {nullptr, nullptr, nullptr};
     GTC_TRY(carve_alloc(&scratch, s, [&](Carver &c) {
         c.take(&queue, (size_t)kHubClasses * kQueueStride);
         c.take(&qcount, kHubClasses);
+        if (tiled)
+            for (int k = 0; k < kSlots; ++k) {
+                c.take(&wcol[k], std::max<int64_t>(G->max_window_edges, 1));
+                if (!G->packed) c.take(&wbin[k], std::max<int64_t>(G->max_window_edges, 1));
+            }
         if (WT) {
             c.take(&w_s, G->n);
             c.take(&wsum, 6 * (size_t)ncfg * copies);
@@ -606,38 +656,120 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     a.wcopies = copies;
     a.wstride = 6 * ncfg;
     a.s4rank = s4rank;
-    if (!rc) rc = hub_class_counts(G->hubs, G->n_hubs, G->row_ptr, G->work, qcount, s);
     a.queue = queue;
     a.qcount = qcount;
-    hipEvent_t e0 = nullptr, e1 = nullptr;
+    std::vector<hipEvent_t> kev;  // start / end of every launch
     float kms = 0.f;
     int32_t launched_blocks = 0;
+    int64_t tiles_run = 0;
+    const void *kfn = nullptr;
+    int64_t max_blocks = 1;
     if (!rc && G->n_hubs > 0) {
 #define GTC_K4(G_, W_) reinterpret_cast<const void *>(&k_clique4<G_, W_>)
-        const void *kfn = GH ? (WT ? GTC_K4(true, 1) : GTC_K4(true, 0))
-                             : (WL ? GTC_K4(false, 2) : (WT ? GTC_K4(false, 1) : GTC_K4(false, 0)));
+        kfn = GH ? (WT ? GTC_K4(true, 1) : GTC_K4(true, 0))
+                 : (WL ? GTC_K4(false, 2) : (WT ? GTC_K4(false, 1) : GTC_K4(false, 0)));
 #undef GTC_K4
         if (lds > 65536)
             (void)hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         int per_cu = 0;
         (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, waves * kWave, lds);
         if (per_cu < 1) per_cu = 1;
-        int64_t blocks = std::min<int64_t>((int64_t)cus * per_cu, (G->n_hubs + waves - 1) / waves);
-        (void)hipEventCreate(&e0);
-        (void)hipEventCreate(&e1);
-        (void)hipEventRecord(e0, s);
-        const dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(waves * kWave);
-        // one hub per take: a hub's 4-clique work grows like the cube of its row, which the
-        // spoke-element classes predict poorly, and the takes (a few thousand per ms) are far
-        // below what one counter serves
+        max_blocks = (int64_t)cus * per_cu;
+    }
+    // one launch over the hub list hubs[0, nh): one hub per take (a hub's 4-clique work grows like
+    // the cube of its row, which the spoke-element classes predict poorly, and the takes, a few
+    // thousand per ms, are far below what one counter serves)
+    auto launch = [&](const int32_t *hubs, int64_t nh) -> int {
+        if (nh <= 0) return GTC_OK;
+        GTC_TRY(hub_class_counts(hubs, nh, G->row_ptr, G->work, qcount, s));
+        GTC_TRY(fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s));
+        a.hubs = hubs;
+        a.n_hubs = (int32_t)nh;
         a.batch_cap = 1;
-        launched_blocks = (int32_t)grid.x;
+        const int64_t blocks = std::min<int64_t>(max_blocks, (nh + waves - 1) / waves);
+        const dim3 grid((unsigned)std::max<int64_t>(blocks, 1)), block(waves * kWave);
+        launched_blocks = std::max<int32_t>(launched_blocks, (int32_t)grid.x);
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        GTC_HIP_CHECK(hipEventCreate(&e0));
+        kev.push_back(e0);
+        GTC_HIP_CHECK(hipEventCreate(&e1));
+        kev.push_back(e1);
+        GTC_HIP_CHECK(hipEventRecord(e0, s));
         const int64_t *edges_dev = G->d_edges;
         void *args[] = {&a, &edges_dev};
         hipError_t e = hipLaunchKernel(kfn, grid, block, args, lds, s);
         if (e == hipSuccess) e = hipGetLastError();
-        if (e != hipSuccess) rc = hip_fail(e, "k_clique4 launch", __FILE__, __LINE__);
-        (void)hipEventRecord(e1, s);
+        if (e != hipSuccess) return hip_fail(e, "k_clique4 launch", __FILE__, __LINE__);
+        GTC_HIP_CHECK(hipEventRecord(e1, s));
+        ++tiles_run;
+        return GTC_OK;
+    };
+    if (!rc && G->n_hubs > 0 && !tiled) rc = launch(G->hubs, G->n_hubs);
+    if (!rc && G->n_hubs > 0 && tiled) {
+        // Tiles (h, c1, c2), h <= c1 <= c2 <= the last window holding a spoke of window h: the
+        // tetrahedra with hub i in window h, spoke a in c1 and spoke b in c2 (i < a < b), each
+        // counted in exactly one tile.  The three windows are made resident (copied from the
+        // pinned CSR or emitted again), evicting the least recently used window a tile does not
+        // need; all on the counting stream, after the kernels that read the buffer.
+        int64_t slot_win[kSlots] = {-1, -1, -1}, slot_used[kSlots] = {0, 0, 0}, clock = 0;
+        auto ensure = [&](int64_t w, int64_t keep1, int64_t keep2, int *slot) -> int {
+            for (int k = 0; k < kSlots; ++k)
+                if (slot_win[k] == w) {
+                    slot_used[k] = ++clock;
+                    *slot = k;
+                    return GTC_OK;
+                }
+            int best = -1;
+            for (int k = 0; k < kSlots; ++k) {
+                if (slot_win[k] == keep1 || slot_win[k] == keep2) continue;
+                if (best < 0 || slot_used[k] < slot_used[best]) best = k;
+            }
+            const int64_t e0w = G->h_row_ptr[G->win[w]], ne = G->h_row_ptr[G->win[w + 1]] - e0w;
+            if (ne > 0) {
+                if (G->rebuild) {
+                    GTC_TRY(emit_window(G, w, wcol[best], wbin[best], s));
+                } else {
+                    GTC_HIP_CHECK(hipMemcpyAsync(wcol[best], G->h_col + e0w, sizeof(int32_t) * ne,
+                                                 hipMemcpyHostToDevice, s));
+                    if (!G->packed)
+                        GTC_HIP_CHECK(hipMemcpyAsync(wbin[best], G->h_bin + e0w, ne,
+                                                     hipMemcpyHostToDevice, s));
+                }
+            }
+            slot_win[best] = w;
+            slot_used[best] = ++clock;
+            *slot = best;
+            return GTC_OK;
+        };
+        const int64_t W = (int64_t)G->win.size() - 1;
+        a.tiled = 1;
+        for (int64_t h = 0; h < W && !rc; ++h) {
+            const int64_t nh = G->win_hubs[h + 1] - G->win_hubs[h];
+            if (nh <= 0) continue;
+            const int64_t smax = G->win_smax[h];
+            for (int64_t c1 = h; c1 <= smax && !rc; ++c1)
+                for (int64_t c2 = c1; c2 <= smax && !rc; ++c2) {
+                    int sh = 0, s1 = 0, s2 = 0;
+                    rc = ensure(h, c1, c2, &sh);
+                    if (!rc) rc = ensure(c1, h, c2, &s1);
+                    if (!rc) rc = ensure(c2, h, c1, &s2);
+                    if (rc) break;
+                    a.col_h = wcol[sh];
+                    a.bin_h = wbin[sh];
+                    a.base_h = G->h_row_ptr[G->win[h]];
+                    a.col_1 = wcol[s1];
+                    a.bin_1 = wbin[s1];
+                    a.base_1 = G->h_row_ptr[G->win[c1]];
+                    a.w1_lo = (int32_t)G->win[c1];
+                    a.w1_hi = (int32_t)G->win[c1 + 1];
+                    a.col_2 = wcol[s2];
+                    a.bin_2 = wbin[s2];
+                    a.base_2 = G->h_row_ptr[G->win[c2]];
+                    a.w2_lo = (int32_t)G->win[c2];
+                    a.w2_hi = (int32_t)G->win[c2 + 1];
+                    rc = launch(G->hubs + G->win_hubs[h], nh);
+                }
+        }
     }
     if (!rc && WT) rc = finalize_class_sums(wsum, ncfg, copies, 6 * ncfg, scale, d_even_w, d_odd_w, s);
     std::vector<unsigned long long> h_even(ncfg);
@@ -645,10 +777,14 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         hipError_t e = hipMemcpyAsync(h_even.data(), d_even, 8 * ncfg, hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) rc = hip_fail(e, "4pCF readback", __FILE__, __LINE__);
-        if (!rc && e0) (void)hipEventElapsedTime(&kms, e0, e1);
+        for (size_t k = 0; !rc && k + 1 < kev.size(); k += 2) {
+            float t = 0.f;
+            (void)hipEventElapsedTime(&t, kev[k], kev[k + 1]);
+            kms += t;
+        }
     }
-    if (e0) (void)hipEventDestroy(e0);
-    if (e1) (void)hipEventDestroy(e1);
+    (void)hipStreamSynchronize(s);
+    for (hipEvent_t e : kev) (void)hipEventDestroy(e);
     dev_free(scratch, s);
     if (rc) return rc;
     unsigned long long cl = 0;
@@ -659,7 +795,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         st->launch_lds_bytes = (int32_t)lds;
         st->cliques4 = cl;
         st->merge_walks = G->walks;
-        st->tiles = G->n_hubs > 0 ? 1 : 0;
+        st->tiles = tiles_run;
         st->kernel_ms = kms;
         st->weight_scale = scale;
     }

@@ -317,6 +317,8 @@ struct gtc_graph_s {
     double build_ms = 0.0;
     // hub windows (§III.5.3): label bounds win[0..W], one window [0, n) unless tiled
     int64_t tile_bytes = 0;
+    bool auto_tiles = false;  // no budget given: go out of core if the CSR exceeds free memory
+    bool keep_coords_requested = true;
     std::vector<int64_t> win;       // W+1 label bounds
     std::vector<int64_t> win_hubs;  // W+1 offsets into hubs: window k's hubs, heaviest first
     std::vector<int32_t> win_smax;  // last window holding a spoke of window k's hubs

@@ -69,10 +69,15 @@ typedef struct gtc_graph_s *gtc_graph;
 
 /* Build options.  A zero-initialised struct (or NULL) means: resident CSR, coordinates kept. */
 typedef struct {
-    /* 0: every row resident in one window.  > 0: rows are split into hub windows whose CSR is at
-     * most tile_bytes (a single longer row gets a window of its own), and counting runs as a loop
-     * over (hub window, search window) tiles (§III.5.3).  The CSR takes 4 bytes per edge when
-     * n <= 2^24 (label and bin packed in one word) and 5 bytes per edge otherwise. */
+    /* > 0: rows are split into hub windows whose CSR is at most tile_bytes (a single longer row
+     * gets a window of its own), and counting runs as a loop over (hub window, search window)
+     * tiles (§III.5.3).  The CSR takes 4 bytes per edge when n <= 2^24 (label and bin packed in
+     * one word) and 5 bytes per edge otherwise.
+     * 0: the environment variable GTC_TILE_BYTES, if set, gives the budget; otherwise one resident
+     * window, unless the CSR would take more than 3/4 of the free device memory: then the build
+     * goes out of core by itself, windows of 1/8 of the free memory, csr_mode GTC_CSR_REBUILD
+     * (GTC_CSR_HOST if drop_coords is set).  gtc_graph_stats reports the outcome (windows,
+     * csr_mode). */
     int64_t tile_bytes;
     /* Where the CSR is kept (§III.5.3):
      *   GTC_CSR_DEVICE  (0): in device memory.
@@ -107,7 +112,8 @@ typedef struct {
     int32_t launch_lds_bytes;  /* enumeration kernel: LDS per workgroup */
     int32_t launch_mode;       /* 3pCF: bit 0 banded walk (else one map over the hub domain),
                                   bit 1 histogram over the unsorted bin triple */
-    int32_t launch_reserved;
+    int32_t csr_mode;          /* where the graph's CSR is kept: GTC_CSR_* (the build may go out
+                                  of core by itself, see gtc_options.tile_bytes) */
     double build_ms;           /* gtc_build_graph: whole call */
     double kernel_ms;          /* enumeration kernels only (sum over tiles) */
     double count_ms;           /* count call: whole call */
@@ -152,8 +158,10 @@ int gtc_count_3pcf_hubs(gtc_graph g, const int32_t *h_hubs, int64_t n_hubs, cons
                         uint64_t *d_counts, double *d_weighted, gtc_stats *st, void *hip_stream);
 
 /* Binned 4-clique counts split by parity (§II.2, §III.1.1, §III.2).  Needs nbins <=
- * GTC_MAX_BINS_4PCF and the coordinates (not dropped); GTC_E_UNSUPPORTED for out-of-core
- * (csr_mode 1 or 2) graphs.
+ * GTC_MAX_BINS_4PCF and the coordinates (not dropped).  Out-of-core graphs (csr_mode 1 or 2) run
+ * as tiles (hub window h, search windows c1 <= c2) (§III.5.3): the tetrahedra i < a < b < c
+ * whose hub i, spoke a and spoke b lie in windows h, c1 and c2, so that three windows are
+ * resident at a time; st->tiles reports the launches.
  *   d_even     device uint64 [gtc_num_configs(4, nbins)]: every tetrahedron.
  *   d_odd      device int64  [same]: signed handedness sum. */
 int gtc_count_4pcf_parity(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,

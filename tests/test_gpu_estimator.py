@@ -153,6 +153,19 @@ def test_compute_4pcf_matches_oracle(gpu_available, seed, nd, nr, rmin, rmax, nb
     np.testing.assert_array_equal(r.realizable, oracle.config_realizable_s4(nb, edges).astype(bool))
 
 
+@pytest.mark.parametrize("mode", ["host", "rebuild"])
+def test_compute_4pcf_out_of_core_matches_resident(gpu_available, mode):
+    say("compute_4pcf out of core", mode)
+    xd, wd, xr, wr = catalogues(67, 3000, 6000)
+    edges = estimator.linear_edges_sq(400, 7000, 3)
+    a = hip_compute_4pcf(xd, wd, xr, wr, edges)
+    b = hip_compute_4pcf(xd, wd, xr, wr, edges, tile_bytes=30_000, csr_mode=mode)
+    assert b.stats["windows"] > 3
+    for x, y in ((a.zeta_even, b.zeta_even), (a.zeta_odd, b.zeta_odd), (a.zeta_conn, b.zeta_conn),
+                 (a.xi, b.xi)):
+        np.testing.assert_array_equal(x, y)
+
+
 def test_estimators_vanish_when_data_are_the_randoms(gpu_available):
     # D = R with unit weights: every clique with a data vertex cancels against its random twin
     x = uniform(64, 3000, 300_000, 360_000)
@@ -192,5 +205,3 @@ def test_estimators_reject_bad_catalogues(gpu_available):
     zero = np.concatenate([np.ones(150), -np.ones(150)])
     with pytest.raises(gtc.GtcError):
         hip_compute_3pcf(xd, wd, xr, zero, edges)
-    with pytest.raises(gtc.GtcError):  # the 4pCF needs the graph on the device
-        hip_compute_4pcf(xd, wd, xr, wr, edges, tile_bytes=4000, csr_mode="rebuild")

@@ -80,16 +80,76 @@ def test_tiled_c2_full_out_of_core(gpu_available):
         np.testing.assert_array_equal(ws, w0)
 
 
-def test_4pcf_on_tiled_graphs(gpu_available):
+@pytest.mark.parametrize("layout", ["packed", "split"])
+@pytest.mark.parametrize("csr_mode", ["device", "host", "rebuild"])
+def test_4pcf_on_tiled_graphs(gpu_available, monkeypatch, csr_mode, layout):
+    # out of core, the 4-clique count runs over tiles (hub window, search windows c1 <= c2) and
+    # gives the resident counts (sorted tuples, S4 configurations, weighted sums) and the oracle's
+    if layout == "split":
+        monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
     xyz = clustered(44, 15_000, 50, 2000)
     edges = linear_edges_sq(6000, 4)
-    e0, o0, st0 = hip_4pcf(xyz, edges)
-    e, o, _ = hip_4pcf(xyz, edges, tile_bytes=5 * max(st0["edges"], 1) // 5)
-    np.testing.assert_array_equal(e, e0)
-    np.testing.assert_array_equal(o, o0)
-    for mode in ("host", "rebuild"):
-        g = gtc.Graph(to_gpu(xyz), edges, tile_bytes=1 << 16, csr_mode=mode)
-        with pytest.raises(gtc.GtcError) as ei:
-            g.count_4pcf_parity()
-        assert ei.value.status == gtc.GTC_E_UNSUPPORTED
+    w = rng_for(48).uniform(-2.0, 2.0, 15_000)
+    wt = torch_f64(w)
+    g0 = gtc.Graph(to_gpu(xyz), edges)
+    e0, o0, st0 = g0.count_4pcf_parity()
+    r0 = g0.count_4pcf_weighted(wt, s4=True)
+    csr = 4 * max(g0.stats()["edges"], 1)
+    g0.close()
+    oe, oo, _ = oracle.Graph(xyz, edges).count_4pcf_parity()
+    np.testing.assert_array_equal(e0.cpu().numpy().view(np.uint64), oe)
+    for frac in (1 / 3, 1 / 11):
+        say("4pcf tiles", csr_mode, layout, frac)
+        g = gtc.Graph(to_gpu(xyz), edges, tile_bytes=int(csr * frac), csr_mode=csr_mode)
+        e, o, st = g.count_4pcf_parity()
+        assert g.stats()["windows"] > 2
+        if csr_mode != "device":
+            assert st["tiles"] >= g.stats()["windows"]
+        np.testing.assert_array_equal(e.cpu().numpy(), e0.cpu().numpy())
+        np.testing.assert_array_equal(o.cpu().numpy(), o0.cpu().numpy())
+        r = g.count_4pcf_weighted(wt, s4=True)
+        for x, y in zip(r[:4], r0[:4]):
+            np.testing.assert_array_equal(x.cpu().numpy(), y.cpu().numpy())
         g.close()
+
+
+def torch_f64(w):
+    import torch
+    return torch.from_numpy(np.asarray(w, np.float64)).cuda()
+
+
+@pytest.mark.parametrize("drop_coords", [False, True])
+def test_build_goes_out_of_core_by_itself(gpu_available, monkeypatch, drop_coords):
+    # with no window budget, a CSR beyond 3/4 of the free device memory is kept out of core:
+    # re-emitted windows when the coordinates are kept, pinned host memory when they are dropped
+    xyz = clustered(45, 30_000, 60, 2500)
+    edges = linear_edges_sq(12_000, 9)
+    w = 0.5 + rng_for(46).random(30_000)
+    c0, w0, st0 = hip_3pcf(xyz, edges, w)
+    assert st0["windows"] == 1 and st0["csr_mode"] == gtc.CSR_MODES["device"]
+    csr_bytes = 4 * st0["edges"]
+    monkeypatch.setenv("GTC_DEVICE_FREE_BYTES", str(csr_bytes))  # 3/4 of it is too little
+    say("auto out of core, drop_coords", drop_coords, "csr bytes", csr_bytes)
+    c, ws, st = hip_3pcf(xyz, edges, w, drop_coords=drop_coords)
+    assert st["windows"] > 2
+    assert st["csr_mode"] == gtc.CSR_MODES["host" if drop_coords else "rebuild"]
+    np.testing.assert_array_equal(c, c0)
+    np.testing.assert_array_equal(ws, w0)
+    monkeypatch.setenv("GTC_DEVICE_FREE_BYTES", str(2 * csr_bytes))  # enough: stays resident
+    c, _, st = hip_3pcf(xyz, edges)
+    assert st["windows"] == 1 and st["csr_mode"] == gtc.CSR_MODES["device"]
+    np.testing.assert_array_equal(c, c0)
+
+
+def test_window_budget_from_the_environment(gpu_available, monkeypatch):
+    xyz = uniform(47, 20_000)
+    edges = linear_edges_sq(45_000, 6)
+    c0, _, st0 = hip_3pcf(xyz, edges)
+    monkeypatch.setenv("GTC_TILE_BYTES", str(4 * st0["edges"] // 5))
+    c, _, st = hip_3pcf(xyz, edges)
+    assert st["windows"] > 1 and st["csr_mode"] == gtc.CSR_MODES["device"]
+    np.testing.assert_array_equal(c, c0)
+    # an explicit budget wins over the environment
+    g = gtc.Graph(to_gpu(xyz), edges, tile_bytes=1 << 40)
+    assert g.stats()["windows"] == 1
+    g.close()
