@@ -37,24 +37,17 @@ def lds_bytes(spoke_elements: int, triangles: int, weighted: bool, unsorted: boo
     per_tri = (0.0 if unsorted else 8.0) + 8.0 + (16.0 + 8.0 + 32.0 if weighted else 0.0)
     return per_elem * spoke_elements + per_tri * triangles
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_triplet_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "graph_triangle_counting_amd", "csrc", f)
-                  for f in ("triplet.hip", "gtc_internal.h")]
+FINGERPRINT_FILE = os.path.join(ROOT, "graph_triangle_counting_amd", "k_triplet.fingerprint")
 
 
-def kernel_fingerprint() -> str:
-    """sha256 (first 16 hex digits) of the enumeration kernel's sources with comments and blank
-    lines removed: a change of code invalidates the stored counter runs, a change of comments
-    does not."""
-    import hashlib
-    import re
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, encoding="utf-8") as fh:
-            text = fh.read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
-        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
-    return h.hexdigest()[:16]
+def kernel_fingerprint() -> str | None:
+    """The enumeration kernel's machine-code fingerprint written by the build (sha256 of the
+    gfx950 instructions of every k_triplet instantiation), or None without a build."""
+    try:
+        with open(FINGERPRINT_FILE) as fh:
+            return fh.read().strip() or None
+    except OSError:
+        return None
 
 
 def measured_traffic(key: str):
@@ -63,6 +56,8 @@ def measured_traffic(key: str):
     kernel source."""
     try:
         fp = kernel_fingerprint()
+        if fp is None:
+            return None
         with open(TRAFFIC_FILE) as fh:
             for line in fh:
                 if line.startswith("#") or not line.strip():
@@ -165,9 +160,13 @@ def main():
         f"tiles {st['tiles']}, h2d {st['h2d_ms']:.1f} ms")
 
     traffic = measured_traffic(cfg.key) if args.tile_bytes == 0 else None
+    copy_gbs = achievable_copy_gbs()
+    log(f"[bench] device copy reaches {copy_gbs:.0f} GB/s")
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "traffic_gbs": None if traffic is None else traffic / (k_avg * 1e-3) / 1e9,
+                "achievable": copy_gbs, "frac_achievable": achieved / copy_gbs,
+                "achievable_from": "1 GiB device-to-device copy, read + written bytes",
                 "kernel": "k_triplet", "kernel_ms": k_avg, "q_alg_bytes": qalg[0],
                 "launch": {"waves_per_wg": st["launch_waves"], "workgroups": st["launch_blocks"],
                            "lds_bytes": st["launch_lds_bytes"]}}
@@ -209,6 +208,27 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def achievable_copy_gbs(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """HBM rate a plain device-to-device copy reaches on this GPU (bytes read + written per
+    second, best of reps, HIP events on the copy's stream): the measured ceiling beside the
+    vendor peak."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(7)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2.0 * nbytes / best / 1e9
+
+
 def copy_calibration(nbytes: int):
     """A plain device copy of a known size: what FETCH_SIZE / WRITE_SIZE read for it scales the
     counters of the enumeration kernel to bytes."""
@@ -244,13 +264,21 @@ def cpu_baseline(cfg, xyz, w, threads):
     c, _, _, walks = g.count_3pcf(w, hub_stride=stride, nthreads=nthreads)
     tc = time.perf_counter() - t0
     T = int(np.asarray(c, dtype=np.uint64).sum())
+    # one core: the same count on every (16 stride)-th hub of the sample, about a second
+    t0 = time.perf_counter()
+    c1, _, _, walks1 = g.count_3pcf(w, hub_stride=16 * stride, nthreads=1)
+    t1 = time.perf_counter() - t0
+    T1 = int(np.asarray(c1, dtype=np.uint64).sum())
+    serial = {"value": T1 / t1, "unit": "triplets/s", "cores": 1,
+              "sample": f"triangles of every {16 * stride}-th hub label of the same sample "
+                        f"({T1} triangles, {t1:.2f} s)"}
     sample = (f"{'full point set' if frac >= 1 else f'central sub-box of side {frac:.3f} L, full density'}"
               f" ({xyz.shape[0]} points); triangles of every {stride}-th hub label"
               f"{' (all hubs)' if stride == 1 else ''}; count phase {tc:.2f} s, graph build "
               f"{tb:.2f} s")
     return {"value": T / tc, "unit": "triplets/s", "cores": nthreads, "kind": "oracle",
             "sample": sample, "merge_walks_per_s": walks / tc, "triangles": T,
-            "count_s": tc, "build_s": tb}
+            "count_s": tc, "build_s": tb, "serial": serial}
 
 
 if __name__ == "__main__":

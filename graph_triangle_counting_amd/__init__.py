@@ -27,8 +27,56 @@ class GtcError(RuntimeError):
         self.status = status
 
 
+_ALLOC = C.CFUNCTYPE(C.c_void_p, C.c_size_t, C.c_void_p, C.c_void_p)
+_FREE = C.CFUNCTYPE(None, C.c_void_p, C.c_void_p, C.c_void_p)
+_HOST_ALLOC = C.CFUNCTYPE(C.c_void_p, C.c_size_t, C.c_void_p)
+_HOST_FREE = C.CFUNCTYPE(None, C.c_void_p, C.c_void_p)
+
+
+class Allocator(C.Structure):
+    """gtc_allocator: memory routines the library calls instead of the HIP runtime's."""
+    _fields_ = [("alloc", _ALLOC), ("free", _FREE), ("host_alloc", _HOST_ALLOC),
+                ("host_free", _HOST_FREE), ("ctx", C.c_void_p)]
+
+
 class Options(C.Structure):
-    _fields_ = [("tile_bytes", C.c_int64), ("csr_mode", C.c_int32), ("drop_coords", C.c_int32)]
+    _fields_ = [("tile_bytes", C.c_int64), ("csr_mode", C.c_int32), ("drop_coords", C.c_int32),
+                ("allocator", C.POINTER(Allocator))]
+
+
+class TorchAllocator:
+    """Routes the library's device memory through PyTorch's caching allocator (stream-ordered
+    on the stream the library passes) and its pinned host memory through pinned torch tensors, so
+    that PyTorch accounts for every buffer.  Keep the object alive as long as any graph built with
+    it (Graph holds a reference)."""
+
+    def __init__(self):
+        import torch
+        self._pinned = {}
+
+        def alloc(nbytes, stream, ctx):
+            try:
+                return torch.cuda.caching_allocator_alloc(int(nbytes), stream=int(stream or 0))
+            except Exception:
+                return None
+
+        def free(ptr, stream, ctx):
+            if ptr:
+                torch.cuda.caching_allocator_delete(ptr)
+
+        def host_alloc(nbytes, ctx):
+            try:
+                t = torch.empty(int(nbytes), dtype=torch.uint8, pin_memory=True)
+            except Exception:
+                return None
+            self._pinned[t.data_ptr()] = t
+            return t.data_ptr()
+
+        def host_free(ptr, ctx):
+            self._pinned.pop(ptr, None)
+
+        self._cbs = (_ALLOC(alloc), _FREE(free), _HOST_ALLOC(host_alloc), _HOST_FREE(host_free))
+        self.struct = Allocator(*self._cbs, None)
 
 
 class Stats(C.Structure):
@@ -172,9 +220,11 @@ class Graph:
     """Neighbour graph on the current GPU (owned by libgtc; freed by close() or on deletion)."""
 
     def __init__(self, xyz, edges_sq, tile_bytes: int = 0, host_csr: bool = False,
-                 drop_coords: bool = False, stream=None, csr_mode: str | None = None):
+                 drop_coords: bool = False, stream=None, csr_mode: str | None = None,
+                 allocator: TorchAllocator | None = None):
         """csr_mode: "device" (default), "host" (pinned host CSR; host_csr=True is the same) or
-        "rebuild" (no stored CSR, windows emitted again per tile); the last two need tile_bytes."""
+        "rebuild" (no stored CSR, windows emitted again per tile); the last two need tile_bytes.
+        allocator: a TorchAllocator to take every buffer from PyTorch's allocators."""
         import torch
         if not (isinstance(xyz, torch.Tensor) and xyz.is_cuda and xyz.dtype == torch.int32
                 and xyz.dim() == 2 and xyz.shape[1] == 3):
@@ -185,7 +235,9 @@ class Graph:
         self.edges = e
         self.n = int(xyz.shape[0])
         mode = CSR_MODES[csr_mode] if csr_mode is not None else (1 if host_csr else 0)
-        opt = Options(int(tile_bytes), mode, int(bool(drop_coords)))
+        self._allocator = allocator  # the routines must outlive the graph
+        opt = Options(int(tile_bytes), mode, int(bool(drop_coords)),
+                      C.pointer(allocator.struct) if allocator is not None else None)
         h = C.c_void_p()
         self._stream = stream
         _check(lib().gtc_build_graph(_dptr(self._xyz) if self.n else None, self.n,
@@ -385,13 +437,14 @@ def _catalogue(xyz, w, name):
 
 
 def _estimator_args(pos_data, w_data, pos_rand, w_rand, rmin, rmax, nbins, edges_sq,
-                    tile_bytes, csr_mode):
+                    tile_bytes, csr_mode, allocator=None):
     xd, wd = _catalogue(pos_data, w_data, "data")
     xr, wr = _catalogue(pos_rand, w_rand, "random")
     if edges_sq is None:
         edges_sq = linear_edges_sq(rmin, rmax, nbins)
     e = np.ascontiguousarray(np.asarray(edges_sq, dtype=np.int64))
-    opt = Options(int(tile_bytes), CSR_MODES[csr_mode or "device"], 0)
+    opt = Options(int(tile_bytes), CSR_MODES[csr_mode or "device"], 0,
+                  C.pointer(allocator.struct) if allocator is not None else None)
     return xd, wd, xr, wr, e, opt
 
 
@@ -402,12 +455,12 @@ def _centres(e: np.ndarray) -> np.ndarray:
 
 def compute_3pcf(pos_data, w_data, pos_rand, w_rand, rmin=None, rmax=None, nbins=None,
                  edges_sq=None, tile_bytes: int = 0, csr_mode: str | None = None,
-                 stream=None) -> Result3pcf:
+                 stream=None, allocator: TorchAllocator | None = None) -> Result3pcf:
     """The 3pCF estimator zeta = NNN / RRR over one graph of data and randoms.  Positions are
     CUDA int32 [n, 3] grid coordinates, weights CUDA float64 [n] or None (unit); the bins are
     equal in r from rmin to rmax (grid units), or given as integer squared edges."""
     xd, wd, xr, wr, e, opt = _estimator_args(pos_data, w_data, pos_rand, w_rand, rmin, rmax,
-                                             nbins, edges_sq, tile_bytes, csr_mode)
+                                             nbins, edges_sq, tile_bytes, csr_mode, allocator)
     nb = e.size - 1
     ncfg = num_configs(3, nb)
     zeta, nnn, rrr = (np.empty(ncfg, np.float64) for _ in range(3))
@@ -427,13 +480,14 @@ def compute_3pcf(pos_data, w_data, pos_rand, w_rand, rmin=None, rmax=None, nbins
 
 def compute_4pcf(pos_data, w_data, pos_rand, w_rand, rmin=None, rmax=None, nbins=None,
                  edges_sq=None, parity: bool = True, tile_bytes: int = 0,
-                 csr_mode: str | None = None, stream=None) -> Result4pcf:
+                 csr_mode: str | None = None, stream=None,
+                 allocator: TorchAllocator | None = None) -> Result4pcf:
     """The 4pCF estimator per S4 configuration: zeta_even = NNNN_even / RRRR, zeta_odd =
     NNNN_odd / RRRR, the internal xi = NN / RR and the connected zeta_conn = zeta_even -
     disc(xi).  Arguments as compute_3pcf; nbins <= 16.  Both channels come from one enumeration,
     so parity=False only drops zeta_odd from the result."""
     xd, wd, xr, wr, e, opt = _estimator_args(pos_data, w_data, pos_rand, w_rand, rmin, rmax,
-                                             nbins, edges_sq, tile_bytes, csr_mode)
+                                             nbins, edges_sq, tile_bytes, csr_mode, allocator)
     nb = e.size - 1
     ncfg = num_configs_s4(nb)
     ze, zo, zc = (np.empty(ncfg, np.float64) for _ in range(3))

@@ -38,11 +38,43 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+FINGERPRINT = os.path.join(PKG, "k_triplet.fingerprint")
+
+
+def kernel_fingerprint_from_isa() -> str:
+    """sha256 (first 16 hex digits) of the gfx950 instructions of every k_triplet instantiation:
+    the device assembly of triplet.hip with comments, labels' line comments and blank lines
+    removed.  It changes with the enumeration kernel's machine code and with nothing else (host
+    code, headers the kernel does not use, comments)."""
+    import hashlib
+    import re
+    src = os.path.join(CSRC, "triplet.hip")
+    r = subprocess.run([HIPCC, *FLAGS, "--cuda-device-only", "-S", src, "-o", "-"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stderr}")
+    h = hashlib.sha256()
+    inside = False
+    for line in r.stdout.splitlines():
+        if re.match(r"^_ZN3gtc9k_triplet\w*:", line):
+            inside = True
+        elif inside and line.startswith(".Lfunc_end"):
+            inside = False
+        if inside:
+            code = line.split(";", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
+    return h.hexdigest()[:16]
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs)) + 1) as ex:
+        fp = ex.submit(kernel_fingerprint_from_isa)
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        with open(FINGERPRINT, "w") as fh:
+            fh.write(fp.result() + "\n")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

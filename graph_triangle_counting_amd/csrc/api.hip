@@ -42,8 +42,8 @@ void free_graph_buffers(gtc_graph_s *G) {
     G->bin = nullptr;
     if (G->h_col || G->h_bin) {
         (void)hipStreamSynchronize(s);  // copies into the pinned CSR have finished
-        if (G->h_col) (void)hipHostFree(G->h_col);
-        if (G->h_bin) (void)hipHostFree(G->h_bin);
+        host_free_pinned(G->h_col);
+        host_free_pinned(G->h_bin);
         G->h_col = nullptr;
         G->h_bin = nullptr;
     }
@@ -192,6 +192,11 @@ int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, 
     G->stream = reinterpret_cast<hipStream_t>(hip_stream);
     G->n = n;
     G->nb = nbins;
+    if (o.allocator) {
+        G->alloc = *o.allocator;
+        G->has_alloc = true;
+    }
+    AllocScope alloc_scope(graph_allocator(G));
     G->tile_bytes = o.tile_bytes;
     G->auto_tiles = o.tile_bytes == 0;
     G->keep_coords_requested = !o.drop_coords;
@@ -227,6 +232,7 @@ int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d
         return GTC_E_INVALID;
     }
     DeviceGuard dg(g->device);
+    AllocScope alloc_scope(graph_allocator(g));
     if (dg.rc) return dg.rc;
     auto t0 = std::chrono::steady_clock::now();
     gtc_stats local{};
@@ -263,6 +269,7 @@ int gtc_count_3pcf_hubs(gtc_graph g, const int32_t *h_hubs, int64_t n_hubs, cons
         return GTC_E_UNSUPPORTED;
     }
     DeviceGuard dg(g->device);
+    AllocScope alloc_scope(graph_allocator(g));
     if (dg.rc) return dg.rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     auto t0 = std::chrono::steady_clock::now();
@@ -310,6 +317,7 @@ static int count_4pcf(gtc_graph g, uint64_t *d_even, int64_t *d_odd, gtc_stats *
         return GTC_E_INVALID;
     }
     DeviceGuard dg(g->device);
+    AllocScope alloc_scope(graph_allocator(g));
     if (dg.rc) return dg.rc;
     auto t0 = std::chrono::steady_clock::now();
     gtc_stats local{};
@@ -343,6 +351,7 @@ int gtc_count_2pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d
         return GTC_E_INVALID;
     }
     DeviceGuard dg(g->device);
+    AllocScope alloc_scope(graph_allocator(g));
     if (dg.rc) return dg.rc;
     auto t0 = std::chrono::steady_clock::now();
     gtc_stats local{};
@@ -456,6 +465,7 @@ int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h
         return GTC_E_INVALID;
     }
     DeviceGuard dg(g->device);
+    AllocScope alloc_scope(graph_allocator(g));
     if (dg.rc) return dg.rc;
     hipStream_t s = g->stream;
     if (h_row_ptr)
@@ -528,6 +538,7 @@ int gtc_graph_stats(gtc_graph g, gtc_stats *st) {
 void gtc_graph_free(gtc_graph g) {
     if (!g) return;
     DeviceGuard dg(g->device);
+    AllocScope alloc_scope(graph_allocator(g));
     free_graph_buffers(g);
     (void)hipStreamSynchronize(g->stream);
     delete g;

@@ -565,11 +565,11 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     if (G->host_csr) {
         // out-of-core: the CSR lives in pinned host memory; each window is emitted into a device
         // staging buffer and copied out
-        STEP2_HIP(hipHostMalloc(reinterpret_cast<void **>(&G->h_col),
-                                sizeof(int32_t) * std::max<int64_t>(G->E, 1), hipHostMallocDefault));
+        STEP2(host_alloc_pinned(reinterpret_cast<void **>(&G->h_col),
+                                sizeof(int32_t) * std::max<int64_t>(G->E, 1)));
         if (!G->packed)
-            STEP2_HIP(hipHostMalloc(reinterpret_cast<void **>(&G->h_bin),
-                                    std::max<int64_t>(G->E, 1), hipHostMallocDefault));
+            STEP2(host_alloc_pinned(reinterpret_cast<void **>(&G->h_bin),
+                                    std::max<int64_t>(G->E, 1)));
         STEP2_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
         for (int b = 0; b < 2; ++b) {
             STEP2_HIP(hipEventCreateWithFlags(&emitted[b], hipEventDisableTiming));

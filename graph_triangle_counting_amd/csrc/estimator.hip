@@ -180,6 +180,7 @@ int gtc_compute_3pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_
         set_error("gtc_compute_3pcf: nbins %d out of range", nbins);
         return GTC_E_INVALID;
     }
+    AllocScope alloc_scope(opt ? opt->allocator : nullptr);
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     Catalogue cat;
     GTC_TRY(make_weights(d_w_data, n_data, d_w_rand, n_rand, s, &cat));
@@ -240,6 +241,7 @@ int gtc_compute_4pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_
         set_error("gtc_compute_4pcf: the 4-clique kernel needs the coordinates (drop_coords)");
         return GTC_E_INVALID;
     }
+    AllocScope alloc_scope(opt ? opt->allocator : nullptr);
     hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
     Catalogue cat;
     GTC_TRY(make_weights(d_w_data, n_data, d_w_rand, n_rand, s, &cat));

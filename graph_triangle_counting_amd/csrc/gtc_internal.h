@@ -46,9 +46,21 @@ int hip_fail(hipError_t e, const char *what, const char *file, int line);
     } while (0)
 
 // ------------------------------------------------------------------ device memory (host)
-// Stream-ordered allocations from the device's default pool (kept cached between calls).
+// Stream-ordered allocations: from the caller's gtc_allocator of the current API call (see
+// AllocScope), else from the device's default pool (kept cached between calls).
 int dev_alloc(void **p, size_t bytes, hipStream_t s);
 void dev_free(void *p, hipStream_t s);
+// pinned host memory, through the same routines
+int host_alloc_pinned(void **p, size_t bytes);
+void host_free_pinned(void *p);
+// The allocator of the API call running on this thread (null: the HIP runtime's).  Every entry
+// point that allocates opens a scope with the allocator its graph or options carry.
+const gtc_allocator *current_allocator();
+struct AllocScope {
+    const gtc_allocator *prev;
+    explicit AllocScope(const gtc_allocator *a);
+    ~AllocScope();
+};
 template <class T>
 int dev_alloc_n(T **p, size_t count, hipStream_t s) {
     return dev_alloc(reinterpret_cast<void **>(p), sizeof(T) * (count ? count : 1), s);
@@ -328,11 +340,19 @@ struct gtc_graph_s {
     bool host_csr = false;   // the CSR in pinned host memory (h_col, h_bin)
     bool rebuild = false;    // no stored CSR: windows are emitted again when a tile needs them
     bool windowed() const { return host_csr || rebuild; }
+    // the caller's memory routines (gtc_options.allocator), if any: every buffer of the graph, and
+    // the scratch of every call on it, comes from them
+    gtc_allocator alloc{};
+    bool has_alloc = false;
     int32_t *h_col = nullptr;
     uint8_t *h_bin = nullptr;
 };
 
 namespace gtc {
+inline const gtc_allocator *graph_allocator(const gtc_graph_s *G) {
+    return G->has_alloc ? &G->alloc : nullptr;
+}
+
 // Emit the CSR rows of hub window w (labels win[w]..win[w+1]) into col/bin (bin null for packed
 // entries), entry e of the graph at col[e - h_row_ptr[win[w]]]: the pair search of the build,
 // run again.  Needs the sorted coordinates.

@@ -22,8 +22,23 @@ int hip_fail(hipError_t e, const char *what, const char *file, int line) {
     return (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) ? GTC_E_OOM : GTC_E_HIP;
 }
 
+static thread_local const gtc_allocator *t_allocator = nullptr;
+
+const gtc_allocator *current_allocator() { return t_allocator; }
+AllocScope::AllocScope(const gtc_allocator *a) : prev(t_allocator) { t_allocator = a; }
+AllocScope::~AllocScope() { t_allocator = prev; }
+
 int dev_alloc(void **p, size_t bytes, hipStream_t s) {
     *p = nullptr;
+    const gtc_allocator *A = t_allocator;
+    if (A && A->alloc) {
+        *p = A->alloc(bytes ? bytes : 1, s, A->ctx);
+        if (!*p) {
+            set_error("device allocation of %zu bytes failed (caller's allocator)", bytes);
+            return GTC_E_OOM;
+        }
+        return GTC_OK;
+    }
     hipError_t e = hipMallocAsync(p, bytes, s);
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -34,7 +49,37 @@ int dev_alloc(void **p, size_t bytes, hipStream_t s) {
 }
 
 void dev_free(void *p, hipStream_t s) {
-    if (p) (void)hipFreeAsync(p, s);
+    if (!p) return;
+    const gtc_allocator *A = t_allocator;
+    if (A && A->free) A->free(p, s, A->ctx);
+    else (void)hipFreeAsync(p, s);
+}
+
+int host_alloc_pinned(void **p, size_t bytes) {
+    *p = nullptr;
+    const gtc_allocator *A = t_allocator;
+    if (A && A->host_alloc) {
+        *p = A->host_alloc(bytes ? bytes : 1, A->ctx);
+        if (!*p) {
+            set_error("pinned host allocation of %zu bytes failed (caller's allocator)", bytes);
+            return GTC_E_OOM;
+        }
+        return GTC_OK;
+    }
+    hipError_t e = hipHostMalloc(p, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        set_error("pinned host allocation of %zu bytes failed: %s", bytes, hipGetErrorString(e));
+        return GTC_E_OOM;
+    }
+    return GTC_OK;
+}
+
+void host_free_pinned(void *p) {
+    if (!p) return;
+    const gtc_allocator *A = t_allocator;
+    if (A && A->host_free) A->host_free(p, A->ctx);
+    else (void)hipHostFree(p);
 }
 
 // ------------------------------------------------------------------ fills (kernels, not memset:

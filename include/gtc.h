@@ -67,7 +67,22 @@ typedef enum {
  * gtc_graph_export).  Free with gtc_graph_free. */
 typedef struct gtc_graph_s *gtc_graph;
 
-/* Build options.  A zero-initialised struct (or NULL) means: resident CSR, coordinates kept. */
+/* Optional memory routines, so that a caller (e.g. PyTorch's caching allocator) owns every buffer
+ * the library allocates.  alloc returns device memory usable on hip_stream in stream order (NULL on
+ * failure, reported as GTC_E_OOM); free releases it in stream order.  host_alloc / host_free give
+ * pinned host memory (the out-of-core CSR); NULL members fall back to hipMallocAsync /
+ * hipFreeAsync / hipHostMalloc / hipHostFree.  The routines and ctx must stay valid while any
+ * graph built with them lives: counts, exports and gtc_graph_free use the graph's routines. */
+typedef struct {
+    void *(*alloc)(size_t bytes, void *hip_stream, void *ctx);
+    void (*free)(void *ptr, void *hip_stream, void *ctx);
+    void *(*host_alloc)(size_t bytes, void *ctx);
+    void (*host_free)(void *ptr, void *ctx);
+    void *ctx;
+} gtc_allocator;
+
+/* Build options.  A zero-initialised struct (or NULL) means: resident CSR, coordinates kept,
+ * memory from the HIP runtime. */
 typedef struct {
     /* > 0: rows are split into hub windows whose CSR is at most tile_bytes (a single longer row
      * gets a window of its own), and counting runs as a loop over (hub window, search window)
@@ -91,6 +106,9 @@ typedef struct {
     /* nonzero: drop the sorted coordinates after the build (gtc_count_4pcf_parity then fails
      * with GTC_E_INVALID).  Zero keeps them. */
     int32_t drop_coords;
+    /* NULL: the HIP runtime's allocators.  Copied into the graph (the pointer need not outlive
+     * the call, the routines and ctx must). */
+    const gtc_allocator *allocator;
 } gtc_options;
 
 /* Run statistics.  Counts refer to one call; byte figures are algorithmic (see the

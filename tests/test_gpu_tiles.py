@@ -153,3 +153,41 @@ def test_window_budget_from_the_environment(gpu_available, monkeypatch):
     g = gtc.Graph(to_gpu(xyz), edges, tile_bytes=1 << 40)
     assert g.stats()["windows"] == 1
     g.close()
+
+
+@pytest.mark.parametrize("csr_mode", ["device", "host"])
+def test_torch_allocator_owns_the_graph_memory(gpu_available, csr_mode):
+    # with a TorchAllocator every device buffer of the graph (and the pinned CSR) comes from
+    # PyTorch's allocators: PyTorch's count rises by at least the CSR while the graph lives and
+    # falls back once it is freed; the counts do not change
+    import torch
+    xyz = clustered(71, 20_000, 40, 2500)
+    edges = linear_edges_sq(12_000, 8)
+    w = 0.5 + rng_for(72).random(20_000)
+    c0, w0, st0 = hip_3pcf(xyz, edges, w)
+    xt = to_gpu(xyz)
+    wt = torch.from_numpy(w).cuda()
+    alloc = gtc.TorchAllocator()
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    kw = {} if csr_mode == "device" else {"tile_bytes": 4 * st0["edges"] // 4, "csr_mode": csr_mode}
+    g = gtc.Graph(xt, edges, allocator=alloc, **kw)
+    torch.cuda.synchronize()
+    if csr_mode == "device":
+        assert torch.cuda.memory_allocated() - base >= 4 * st0["edges"]
+    else:
+        assert alloc._pinned and g.stats()["windows"] > 1
+    c, ws, st = g.count_3pcf(wt)
+    np.testing.assert_array_equal(c.cpu().numpy().view(np.uint64), c0)
+    np.testing.assert_array_equal(ws.cpu().numpy(), w0)
+    del c, ws
+    g.close()
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == base
+    assert not alloc._pinned
+    # the estimators take it too
+    r = gtc.compute_3pcf(xt[:10_000].contiguous(), None, xt[10_000:].contiguous(), None,
+                         edges_sq=edges, allocator=alloc)
+    r0 = gtc.compute_3pcf(xt[:10_000].contiguous(), None, xt[10_000:].contiguous(), None,
+                          edges_sq=edges)
+    np.testing.assert_array_equal(r.zeta, r0.zeta)
