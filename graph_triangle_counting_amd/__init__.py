@@ -120,6 +120,7 @@ def lib() -> C.CDLL:
         L.gtc_count_4pcf_weighted.argtypes = [P, P, i32, P, P, P, P, C.POINTER(Stats), P]
         L.gtc_linear_edges_sq.argtypes = [i64, i64, i32, P]
         L.gtc_equilateral_configs.argtypes = [i32, i32, i32, P]
+        L.gtc_hbm_read_rate.argtypes = [P, i64, i32, P, P]
         L.gtc_compute_3pcf.argtypes = [P, i64, P, P, i64, P, P, i32, C.POINTER(Options), P, P, P,
                                        C.POINTER(Stats), P]
         L.gtc_compute_4pcf.argtypes = [P, i64, P, P, i64, P, P, i32, C.POINTER(Options), P, P, P,
@@ -392,6 +393,14 @@ def linear_edges_sq(r_min: int, r_max: int, nbins: int) -> np.ndarray:
     _check(lib().gtc_linear_edges_sq(int(r_min), int(r_max), int(nbins),
                                      e.ctypes.data_as(C.c_void_p)))
     return e
+
+
+def hbm_read_rate(buf, reps: int = 5, stream=None) -> float:
+    """GB/s that a plain streaming-read kernel reaches over the CUDA tensor buf."""
+    g = C.c_double(0.0)
+    _check(lib().gtc_hbm_read_rate(_dptr(buf), buf.numel() * buf.element_size(), int(reps),
+                                   C.byref(g), _stream_ptr(stream)))
+    return g.value
 
 
 def equilateral_configs(order: int, nbins: int, s4: bool = False) -> np.ndarray:

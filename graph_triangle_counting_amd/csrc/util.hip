@@ -347,3 +347,61 @@ int64_t plan_windows(const int64_t *row_ptr, int64_t n, int64_t tile_bytes, int6
 }
 
 }  // namespace gtc
+
+// ------------------------------------------------------------------ measurement: HBM read rate
+// Every thread streams 16-byte loads over the buffer (grid-stride) and folds them with XOR; one
+// store per thread keeps the loads live.  A ceiling for read-dominated kernels beside the vendor
+// peak.
+namespace gtc {
+__global__ void __launch_bounds__(256) k_read_stream(const uint4 *__restrict__ p, int64_t n,
+                                                     uint32_t *__restrict__ sink) {
+    uint32_t x = 0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const uint4 v = p[i];
+        x ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    sink[blockIdx.x * (int64_t)blockDim.x + threadIdx.x] = x;
+}
+}  // namespace gtc
+
+extern "C" int gtc_hbm_read_rate(const void *d_buf, int64_t bytes, int32_t reps, double *h_gbs,
+                                 void *hip_stream) {
+    using namespace gtc;
+    if (!d_buf || bytes < 16 || reps < 1 || !h_gbs || (reinterpret_cast<uintptr_t>(d_buf) & 15)) {
+        set_error("gtc_hbm_read_rate: need a 16-byte aligned device buffer of at least 16 bytes, "
+                  "reps >= 1 and h_gbs");
+        return GTC_E_INVALID;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+    int dev = 0, cus = 0;
+    GTC_HIP_CHECK(hipGetDevice(&dev));
+    GTC_HIP_CHECK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    const int64_t n = bytes / 16;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, (int64_t)cus * 8);
+    uint32_t *sink = nullptr;
+    GTC_TRY(dev_alloc_n(&sink, (size_t)blocks * 256, s));
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    int rc = GTC_OK;
+    double best = 1e300;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess)
+        rc = hip_fail(hipGetLastError(), "hipEventCreate", __FILE__, __LINE__);
+    for (int r = -1; r < reps && !rc; ++r) {  // one untimed pass first
+        (void)hipEventRecord(e0, s);
+        hipLaunchKernelGGL(k_read_stream, dim3((unsigned)blocks), dim3(256), 0, s,
+                           reinterpret_cast<const uint4 *>(d_buf), n, sink);
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess) e = hipEventRecord(e1, s);
+        if (e == hipSuccess) e = hipEventSynchronize(e1);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+        if (e != hipSuccess) rc = hip_fail(e, "k_read_stream", __FILE__, __LINE__);
+        else if (r >= 0) best = std::min(best, (double)ms);
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    dev_free(sink, s);
+    (void)hipStreamSynchronize(s);
+    if (!rc) *h_gbs = (double)(n * 16) / (best * 1e-3) / 1e9;
+    return rc;
+}

@@ -318,6 +318,14 @@ int gtc_compute_4pcf(const int32_t *d_xyz_data, int64_t n_data, const double *d_
                      double *h_zeta_even, double *h_zeta_odd, double *h_zeta_conn, double *h_xi,
                      gtc_stats *st, void *hip_stream);
 
+/* Measurement: the HBM read rate of a plain streaming kernel (16-byte loads over d_buf, grid-
+ * stride, best of reps timed launches after one untimed), in GB/s of bytes read: the measured
+ * ceiling of a read-dominated kernel beside the vendor peak.
+ *   d_buf device, 16-byte aligned, bytes >= 16 (read, not written); reps >= 1.
+ * Synchronises the stream.  GTC_E_INVALID for bad arguments. */
+int gtc_hbm_read_rate(const void *d_buf, int64_t bytes, int32_t reps, double *h_gbs,
+                      void *hip_stream);
+
 /* Graph-level statistics (n, edges, max_out_degree, windows, spoke_elements, build_ms). */
 int gtc_graph_stats(gtc_graph g, gtc_stats *st);
 

@@ -230,3 +230,14 @@ def test_equilateral_configs_reject_bad_arguments():
     for order, s4, nb in ((2, 0, 4), (3, 1, 4), (3, 0, 0), (3, 0, 256), (4, 0, 17), (4, 1, 0)):
         assert L.gtc_equilateral_configs(order, s4, nb, out) == gtc.GTC_E_INVALID
     assert L.gtc_equilateral_configs(3, 0, 4, None) == gtc.GTC_E_INVALID
+
+
+def test_hbm_read_rate_rejects_bad_arguments_without_gpu():
+    L = gtc.lib()
+    g = C.c_double(0)
+    fake = C.c_void_p(0x1000)
+    assert L.gtc_hbm_read_rate(None, 1024, 1, C.byref(g), None) == gtc.GTC_E_INVALID
+    assert L.gtc_hbm_read_rate(C.c_void_p(0x1004), 1024, 1, C.byref(g), None) == gtc.GTC_E_INVALID
+    assert L.gtc_hbm_read_rate(fake, 8, 1, C.byref(g), None) == gtc.GTC_E_INVALID
+    assert L.gtc_hbm_read_rate(fake, 1024, 0, C.byref(g), None) == gtc.GTC_E_INVALID
+    assert L.gtc_hbm_read_rate(fake, 1024, 1, None, None) == gtc.GTC_E_INVALID
