@@ -1,7 +1,9 @@
 // build.hip - the neighbour graph on the GPU (GRAMSCI v2 §II.1, Eq.(1); CSR layout §III.5.1).
 //
 // The pages build a kd-tree on the CPU; here the points are bucketed into cubic cells of side
-// >= r_max by a counting sort (keys, atomics, scan, scatter), and each point's forward neighbours
+// >= r_max (cell counts and their scan give the cell starts; a stable radix sort of the cell keys,
+// ties in original order, gives the internal labels, so they are the same on every run), and
+// each point's forward neighbours
 // (larger internal label) are found in its own cell and the 13 forward neighbour cells.  Visiting
 // those cells in increasing key order emits every row already ascending, so no sort is needed.
 // Two passes over the same traversal: count (degrees, then a 64-bit scan to row offsets), emit.
@@ -9,6 +11,8 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+
+#include <hipcub/hipcub.hpp>
 
 #include "gtc_internal.h"
 
@@ -20,7 +24,7 @@ __constant__ int8_t kFwd[13][3] = {{0, 0, 1},  {0, 1, -1},  {0, 1, 0},  {0, 1, 1
                                    {1, 1, -1}, {1, 1, 0},   {1, 1, 1}};
 
 __global__ void k_cellkey(const int32_t *__restrict__ xyz, int64_t n, Grid gr,
-                          int32_t *__restrict__ key, int32_t *__restrict__ slot,
+                          int32_t *__restrict__ key, int32_t *__restrict__ idx,
                           int32_t *__restrict__ cell_count, int32_t *__restrict__ err) {
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i >= n) return;
@@ -32,20 +36,18 @@ __global__ void k_cellkey(const int32_t *__restrict__ xyz, int64_t n, Grid gr,
     }
     const int k = ((z / gr.cs) * gr.g + y / gr.cs) * gr.g + x / gr.cs;
     key[i] = k;
-    slot[i] = atomicAdd(&cell_count[k], 1);
+    idx[i] = (int32_t)i;
+    atomicAdd(&cell_count[k], 1);
 }
 
+// sorted position r: the point perm[r] (keys sorted, ties in original order) and its coordinates
 __global__ void k_scatter(const int32_t *__restrict__ xyz, int64_t n,
-                          const int32_t *__restrict__ key, const int32_t *__restrict__ slot,
-                          const int32_t *__restrict__ cell_start, int32_t *__restrict__ perm,
-                          int4 *__restrict__ xyz_s, int32_t *__restrict__ key_s) {
-    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const int k = key[i];
-    const int pos = cell_start[k] + slot[i];
-    perm[pos] = (int32_t)i;
-    xyz_s[pos] = make_int4(xyz[3 * i], xyz[3 * i + 1], xyz[3 * i + 2], k);
-    key_s[pos] = k;
+                          const int32_t *__restrict__ perm, const int32_t *__restrict__ key_s,
+                          int4 *__restrict__ xyz_s) {
+    const int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (r >= n) return;
+    const int64_t i = perm[r];
+    xyz_s[r] = make_int4(xyz[3 * i], xyz[3 * i + 1], xyz[3 * i + 2], key_s[r]);
 }
 
 struct PairArgs {
@@ -401,8 +403,9 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     GTC_HIP_CHECK(hipMemcpyAsync(G->d_edges, G->edges, sizeof(int64_t) * (G->nb + 1),
                                  hipMemcpyHostToDevice, s));
 
-    // build scratch: keys, slots, cell counts, error flag, stats, class counts, scan partials
-    int32_t *key = nullptr, *slot = nullptr, *ccount = nullptr, *err = nullptr;
+    // build scratch: keys, original indices, cell counts, error flag, stats, scan partials, sort
+    // workspace
+    int32_t *key = nullptr, *idx = nullptr, *ccount = nullptr, *err = nullptr;
     StatsOut *d_stats = nullptr;
     int64_t *scan_ws = nullptr;
     void *scratch = nullptr;
@@ -427,9 +430,19 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     } while (0)
 
     const size_t scan_ws_bytes = std::max(scan_workspace_bytes(n), scan_workspace_bytes(gr.ncell));
+    // radix sort of the cell keys, only as many bits as the largest key needs
+    int key_bits = 1;
+    while (key_bits < 31 && ((int64_t)1 << key_bits) < gr.ncell) ++key_bits;
+    size_t sort_ws_bytes = 0;
+    if (n > 0)
+        STEP_HIP(hipcub::DeviceRadixSort::SortPairs(nullptr, sort_ws_bytes, (const int32_t *)nullptr,
+                                                    (int32_t *)nullptr, (const int32_t *)nullptr,
+                                                    (int32_t *)nullptr, (int)n, 0, key_bits, s));
+    unsigned char *sort_ws = nullptr;
     STEP(carve_alloc(&scratch, s, [&](Carver &c) {
         c.take(&key, n);
-        c.take(&slot, n);
+        c.take(&idx, n);
+        c.take(&sort_ws, std::max<size_t>(sort_ws_bytes, 1));
         c.take(&ccount, gr.ncell);
         c.take(&err, 1);
         c.take(&d_stats, 1);
@@ -441,13 +454,15 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
 
     if (n > 0) {
         hipLaunchKernelGGL(k_cellkey, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, gr, key,
-                           slot, ccount, err);
+                           idx, ccount, err);
         STEP_HIP(hipGetLastError());
     }
     STEP(exclusive_scan_i32_to_i32(ccount, G->cell_start, gr.ncell, scan_ws, s));
     if (n > 0) {
-        hipLaunchKernelGGL(k_scatter, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, key, slot,
-                           G->cell_start, G->perm, G->xyz_s, G->key_s);
+        STEP_HIP(hipcub::DeviceRadixSort::SortPairs(sort_ws, sort_ws_bytes, key, G->key_s, idx,
+                                                    G->perm, (int)n, 0, key_bits, s));
+        hipLaunchKernelGGL(k_scatter, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, G->perm,
+                           G->key_s, G->xyz_s);
         STEP_HIP(hipGetLastError());
     }
 

@@ -316,6 +316,45 @@ def test_3pcf_repeatable_and_label_invariant(gpu_available):
         np.testing.assert_array_equal(a[1], x[1])
 
 
+def test_internal_labels_are_deterministic(gpu_available):
+    # internal labels: cell-sorted, ties in original order (§8 a2), the same on every build
+    xyz = clustered(11, 30_000, 20, 1500)  # dense cells: many ties per cell
+    edges = linear_edges_sq(8_000, 6)
+    g1 = gtc.Graph(to_gpu(xyz), edges)
+    g2 = gtc.Graph(to_gpu(xyz), edges)
+    e1, e2 = g1.export(), g2.export()
+    s1, s2 = g1.stats(), g2.stats()
+    g1.close()
+    g2.close()
+    for a, b in zip(e1, e2):
+        np.testing.assert_array_equal(a, b)
+    for k in ("max_out_degree", "spoke_elements", "edges"):
+        assert s1[k] == s2[k]
+    perm = e1[3]
+    assert np.array_equal(np.sort(perm), np.arange(xyz.shape[0]))
+    # the build's cells (side ceil(r_max), at most ~2n cells and 512 per axis): internal order
+    # sorts by cell key, ties by original index
+    r2 = int(edges[-1])
+    cs = int(np.ceil(np.sqrt(r2)))
+    while cs * cs < r2:
+        cs += 1
+    while cs > 1 and (cs - 1) ** 2 >= r2:
+        cs -= 1
+    g = -(-(1 << 20) // cs)
+    cap = 1
+    while (cap + 1) ** 3 <= 2 * xyz.shape[0] and cap < 512:
+        cap += 1
+    if g > cap:
+        g = cap
+        cs = -(-(1 << 20) // g)
+    c = xyz[perm].astype(np.int64) // cs
+    key = (c[:, 2] * g + c[:, 1]) * g + c[:, 0]
+    assert np.all(np.diff(key) >= 0)
+    tie = np.diff(key) == 0
+    assert tie.sum() > xyz.shape[0] // 2
+    assert np.all(np.diff(perm)[tie] > 0)
+
+
 def test_3pcf_nonfinite_weight_rejected(gpu_available):
     import torch
     xyz = uniform(11, 500)
