@@ -241,3 +241,42 @@ def test_hbm_read_rate_rejects_bad_arguments_without_gpu():
     assert L.gtc_hbm_read_rate(fake, 8, 1, C.byref(g), None) == gtc.GTC_E_INVALID
     assert L.gtc_hbm_read_rate(fake, 1024, 0, C.byref(g), None) == gtc.GTC_E_INVALID
     assert L.gtc_hbm_read_rate(fake, 1024, 1, None, None) == gtc.GTC_E_INVALID
+
+
+def test_tiles_cover_every_walk_and_tetrahedron_once():
+    # Windows from the library's planner over a real forward CSR (the oracle's graph, labels
+    # ascending), tiles enumerated as the count loops do: 3pCF (h, s), h <= s <= smax(h); 4pCF
+    # (h, c1, c2), h <= c1 <= c2 <= smax(h), smax(h) the window of the largest spoke label of
+    # window h.  Every walk (i, j) and every tetrahedron i < a < b < c must fall in exactly one
+    # enumerated tile: (win i, win j), and (win i, win a, win b).
+    import itertools
+    import oracle
+    from workloads import linear_edges_sq, rng_for
+    rng = rng_for(93)
+    xyz = (rng.integers(0, 40_000, (700, 3))).astype(np.int32)
+    og = oracle.Graph(xyz, linear_edges_sq(9_000, 3))
+    rp_full, col_full, _ = og.export()
+    n = og.n
+    fwd = [[int(k) for k in col_full[rp_full[i]:rp_full[i + 1]] if k > i] for i in range(n)]
+    rp = np.concatenate([[0], np.cumsum([len(r) for r in fwd])]).astype(np.int64)
+    for budget in (4 * 40, 4 * 200, 4 * int(rp[-1]) // 7):
+        W, b = _plan(rp, budget, 4)
+        win = np.searchsorted(b, np.arange(n), side="right") - 1
+        smax = [max([win[r[-1]] for r in fwd[b[h]:b[h + 1]] if r] + [h]) for h in range(W)]
+        tiles3 = {(h, s) for h in range(W) for s in range(h, smax[h] + 1)}
+        tiles4 = {(h, c1, c2) for h in range(W) for c1 in range(h, smax[h] + 1)
+                  for c2 in range(c1, smax[h] + 1)}
+        nwalk = ncl = 0
+        for i in range(n):
+            for j in fwd[i]:
+                assert (win[i], win[j]) in tiles3
+                nwalk += 1
+            adj = set(fwd[i])
+            for a, bb in itertools.combinations(fwd[i], 2):
+                if bb not in fwd[a]:
+                    continue
+                for c in fwd[bb]:
+                    if c in adj and c in fwd[a]:
+                        assert (win[i], win[a], win[bb]) in tiles4
+                        ncl += 1
+        assert W > 2 and nwalk == rp[-1] and ncl > 0

@@ -661,3 +661,30 @@ def test_estimator_weights_are_normalised():
     assert Fraction(sum(map(Fraction, s[:50]))) == pytest.approx(1, abs=1e-15)
     assert Fraction(sum(map(Fraction, s[50:]))) == pytest.approx(-1, abs=1e-15)
     assert (r[:50] == 0).all() and np.array_equal(r[50:], -s[50:])
+
+
+# ------------------------------------------------------------------ generated point sets
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+
+@settings(max_examples=40, deadline=None)
+@given(seed=st.integers(0, 2**31 - 1), n=st.integers(0, 60), box=st.integers(1, 3000),
+       nb=st.integers(1, 6), clump=st.integers(0, 6))
+def test_generated_sets_match_brute_force(seed, n, box, nb, clump):
+    # arbitrary small clouds (coincident points, tiny boxes, edges at exact distances): the
+    # oracle's graph, triangles and tetrahedra with parity equal the exhaustive definitions
+    xyz = small_cloud(seed, n, box, min(clump, n))
+    r = max(1, box // 2)
+    edges = linear_edges_sq(r, nb) if r * r >= nb * nb else linear_edges_sq(nb, nb)
+    g = oracle.Graph(xyz, edges)
+    a, _ = brute.adjacency(xyz, edges)
+    assert g.nnz == int(a.sum())
+    c, _, _, _ = g.count_3pcf()
+    bc, _, _ = brute.triangles(xyz, edges)
+    np.testing.assert_array_equal(c, bc)
+    if n <= 30:
+        e, o, _ = g.count_4pcf_parity()
+        be, bo = brute.cliques4(xyz, edges)
+        np.testing.assert_array_equal(e, be)
+        np.testing.assert_array_equal(o, bo)
