@@ -74,7 +74,8 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) / 16 * 16;
 __host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh, bool wl = false) {
     return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 22 * 8 * 4 + (wl ? 48 * (size_t)ncfg : 0);
 }
-// per-wave part: position map, row coordinates, hub-edge bins, bitset rows, (weighted) row weights
+// per-wave part: position map, row coordinates (hub-relative), hub-edge bins, bitset rows,
+// (weighted) row weights
 __host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int words,
                                                   bool weighted = false) {
     return (size_t)map_bytes + align16(16 * (size_t)max_m) + align16((size_t)max_m) +
@@ -99,11 +100,6 @@ __device__ __forceinline__ void add_u128_pair(unsigned long long *p, unsigned lo
     if (hi) atomicAdd(p + 1, hi);
 }
 
-__device__ __forceinline__ int64_t d2i(int4 p, int4 q) {
-    const int64_t dx = p.x - q.x, dy = p.y - q.y, dz = p.z - q.z;
-    return dx * dx + dy * dy + dz * dz;
-}
-
 template <class T>
 __device__ __forceinline__ void cswap(T &a, T &b) {
     const T lo = a < b ? a : b, hi = a < b ? b : a;
@@ -111,25 +107,21 @@ __device__ __forceinline__ void cswap(T &a, T &b) {
     b = hi;
 }
 
-__device__ __forceinline__ int chirality(int4 p[4], int64_t key[4]) {
-    // order the four vertices by key (insertion sort, swapping points along)
-#pragma unroll
-    for (int x = 1; x < 4; ++x)
-#pragma unroll
-        for (int y = x; y > 0; --y)
-            if (key[y - 1] > key[y]) {
-                const int64_t tk = key[y]; key[y] = key[y - 1]; key[y - 1] = tk;
-                const int4 tp = p[y]; p[y] = p[y - 1]; p[y - 1] = tp;
-            }
-    if (key[0] == key[1] || key[1] == key[2] || key[2] == key[3]) return 0;
-    const int64_t ax = p[1].x - p[0].x, ay = p[1].y - p[0].y, az = p[1].z - p[0].z;
-    const int64_t bx = p[2].x - p[0].x, by = p[2].y - p[0].y, bz = p[2].z - p[0].z;
-    const int64_t cx = p[3].x - p[0].x, cy = p[3].y - p[0].y, cz = p[3].z - p[0].z;
-    const int64_t v = cx * (ay * bz - az * by) + cy * (az * bx - ax * bz) + cz * (ax * by - ay * bx);
+// Sign of C . X for X = A x B (A, B, C integer vectors with |components| < 2^20, so X's
+// components are exact doubles below 2^41): the fp64 value decides when it exceeds a bound on its
+// rounding error (three roundings of terms at most S = sum |C_k X_k|, well inside 8 u S); else the
+// exact int64 value (|C . X| < 3 2^61).
+__device__ __forceinline__ int orient_sign(double4 C, double X0, double X1, double X2) {
+    const double d = fma(C.z, X2, fma(C.y, X1, C.x * X0));
+    const double S = fabs(C.x * X0) + fabs(C.y * X1) + fabs(C.z * X2);
+    if (fabs(d) > 0x1p-50 * S) return d > 0.0 ? 1 : -1;
+    const int64_t v = (int64_t)C.x * (int64_t)X0 + (int64_t)C.y * (int64_t)X1 +
+                      (int64_t)C.z * (int64_t)X2;
     return (v > 0) - (v < 0);
 }
 
-__device__ __forceinline__ int edge_bin(int64_t d2, const int64_t *se, int nb) {
+// bin of an exact squared distance (a double below 2^53), against the edges as doubles
+__device__ __forceinline__ int edge_bin_d(double d2, const double *se, int nb) {
     int l = 0, h = nb;  // se[l] <= d2 < se[h]
     while (h - l > 1) {
         const int md = (l + h) >> 1;
@@ -138,6 +130,15 @@ __device__ __forceinline__ int edge_bin(int64_t d2, const int64_t *se, int nb) {
     return l;
 }
 
+__device__ __forceinline__ double sq3(double x, double y, double z) { return fma(z, z, fma(y, y, x * x)); }
+
+// an integer vector (|components| < 2^20) as doubles, with its squared length: all exact
+__device__ __forceinline__ double4 rel4(int4 q) {
+    const double x = q.x, y = q.y, z = q.z;
+    return make_double4(x, y, z, sq3(x, y, z));
+}
+
+
 // GH: bins go straight to global memory (configuration counts too large for LDS).  WM: 0
 // unweighted; 1 weighted, class sums in global memory; 2 weighted, class sums in LDS, added to
 // global memory when the workgroup ends.
@@ -145,7 +146,7 @@ template <bool GH, int WM>
 __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *edges) {
     constexpr bool WT = WM != 0;
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int64_t se[GTC_MAX_BINS_4PCF + 1];
+    __shared__ double se[GTC_MAX_BINS_4PCF + 1];  // squared edges (integers below 2^53)
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     const size_t hist_bytes = GH ? 0 : align16(4 * (size_t)a.ncfg);
     uint32_t *ev = reinterpret_cast<uint32_t *>(smem);
@@ -172,7 +173,7 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
             ev[t] = 0;
             od[t] = 0;
         }
-    for (int t = threadIdx.x; t <= a.nb; t += blockDim.x) se[t] = edges[t];
+    for (int t = threadIdx.x; t <= a.nb; t += blockDim.x) se[t] = (double)edges[t];
     for (int t = threadIdx.x; t < 22 * 8; t += blockDim.x) {
         const int x = t / 8, r = t % 8;
         int64_t c = 1;
@@ -221,7 +222,10 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
             for (int t = 1; t < 5; ++t)
                 if (k >= dom.lo[t]) d = dom.delta[t];
             pmap[k + d] = (uint16_t)(p + 1);
-            rc[p] = a.xyz_s[k];
+            {  // hub-relative coordinates (|d| < 2^20)
+                const int4 q = a.xyz_s[k];
+                rc[p] = make_int4(q.x - pi.x, q.y - pi.y, q.z - pi.z, 0);
+            }
             rbin[p] = hbin ? hbin[p] : (uint8_t)(w >> 24);
             if (WT) rw[p] = a.w_s[k];
         }
@@ -269,20 +273,33 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
             const uint32_t range = (bhi >= 32 ? 0xffffffffu : ((1u << bhi) - 1u)) &
                                    ~(blo >= 32 ? 0xffffffffu : ((1u << blo) - 1u));
             uint32_t bits = adj[t] & range;
+            if (!bits) continue;
+            // per spoke a: hub-relative coordinates A (hub at the origin) and the bin of (i, a)
+            const double4 A = rel4(rc[ra]);
+            const int bia = rbin[ra];
             while (bits) {
                 const int rbb = wa * 32 + __builtin_ctz(bits);
                 bits &= bits - 1;
+                // per pair (a, b): B, the bins of (i, b) and (a, b), |a - b|^2 and X = A x B
+                const double4 B = rel4(rc[rbb]);
+                const int bib = rbin[rbb];
+                const double dab = sq3(A.x - B.x, A.y - B.y, A.z - B.z);
+                const int bab = edge_bin_d(dab, se, a.nb);
+                const double X0 = fma(A.y, B.z, -(A.z * B.y)), X1 = fma(A.z, B.x, -(A.x * B.z)),
+                             X2 = fma(A.x, B.y, -(A.y * B.x));  // exact: products below 2^40
+                // the parts of the vertex keys that c does not change (integer sums, exact)
+                const double kab = A.w + B.w, ka = A.w + dab, kb = B.w + dab;
                 for (int w2 = (rbb + 1) >> 5; w2 < W; ++w2) {
                     uint32_t cm = adj[ra * W + w2] & adj[rbb * W + w2];
                     while (cm) {
                         const int rcc = w2 * 32 + __builtin_ctz(cm);
                         cm &= cm - 1;
-                        int4 p[4] = {pi, rc[ra], rc[rbb], rc[rcc]};
-                        const int64_t dab = d2i(p[1], p[2]), dac = d2i(p[1], p[3]), dbc = d2i(p[2], p[3]);
-                        const int64_t dia = d2i(p[0], p[1]), dib = d2i(p[0], p[2]), dic = d2i(p[0], p[3]);
+                        const double4 Cc = rel4(rc[rcc]);
+                        const double dac = sq3(A.x - Cc.x, A.y - Cc.y, A.z - Cc.z);
+                        const double dbc = sq3(B.x - Cc.x, B.y - Cc.y, B.z - Cc.z);
                         // the six bins in edge order of the vertices (i, a, b, c)
-                        int bb[6] = {rbin[ra], rbin[rbb], rbin[rcc], edge_bin(dab, se, a.nb),
-                                     edge_bin(dac, se, a.nb), edge_bin(dbc, se, a.nb)};
+                        int bb[6] = {bia, bib, rbin[rcc], bab, edge_bin_d(dac, se, a.nb),
+                                     edge_bin_d(dbc, se, a.nb)};
                         int rank = 0;
                         if (a.s4rank) {  // S4 configuration: one table read
                             int key = 0;
@@ -303,9 +320,25 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                                 prev = cq;
                             }
                         }
-                        int64_t key[4] = {dia + dib + dic, dia + dab + dac, dib + dab + dbc,
-                                          dic + dac + dbc};
-                        const int sgn = chirality(p, key);
+                        // vertex keys (sums of the three squared edge lengths, exact) of i, a, b,
+                        // c; sorting them ascending permutes the vertices, and the orientation of
+                        // the sorted tetrahedron is the parity of that permutation times
+                        // orient(i, a, b, c) = C . (A x B); a tie leaves no handedness
+                        double k0 = kab + Cc.w, k1 = ka + dac, k2 = kb + dbc, k3 = Cc.w + dac + dbc;
+                        int par = 0;
+                        auto cx = [&](double &u, double &v) {
+                            const bool sw = v < u;
+                            const double lo = sw ? v : u, hi = sw ? u : v;
+                            u = lo;
+                            v = hi;
+                            par ^= (int)sw;
+                        };
+                        cx(k0, k1); cx(k2, k3); cx(k0, k2); cx(k1, k3); cx(k1, k2);
+                        int sgn = 0;
+                        if (k0 != k1 && k1 != k2 && k2 != k3) {
+                            const int o = orient_sign(Cc, X0, X1, X2);
+                            sgn = par ? -o : o;
+                        }
                         if (WT) {  // the four weights ascending, product without fusion
                             double v0 = wi, v1 = rw[ra], v2 = rw[rbb], v3 = rw[rcc], t;
                             t = fmin(v0, v1); v1 = fmax(v0, v1); v0 = t;

@@ -6,6 +6,7 @@ configuration, which bit-exactness implies.
 """
 from __future__ import annotations
 
+import functools
 import itertools
 
 import numpy as np
@@ -377,16 +378,27 @@ CASES_4 = [
 ]
 
 
+def points_4(kind, seed, n):
+    return uniform(seed, n) if kind == "uniform" else clustered(seed, n, 50, 2000)
+
+
+@functools.lru_cache(maxsize=None)
+def oracle_4pcf(kind, seed, n, r, nb, s4=False):
+    """The oracle's counts for one case, computed once per test session (both CSR layouts and
+    the later tests of the same case compare against the same arrays)."""
+    return oracle.Graph(points_4(kind, seed, n), linear_edges_sq(r, nb)).count_4pcf_parity(s4=s4)
+
+
 @pytest.mark.parametrize("layout", ["packed", "split"])
 @pytest.mark.parametrize("kind,seed,n,r,nb", CASES_4)
 def test_4pcf_matches_oracle(gpu_available, monkeypatch, layout, kind, seed, n, r, nb):
     say("4pcf", layout, kind, seed, n, r, nb)
     if layout == "split":
         monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
-    xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 50, 2000)
+    xyz = points_4(kind, seed, n)
     edges = linear_edges_sq(r, nb)
     e, o, st = hip_4pcf(xyz, edges)
-    oe, oo, ncl = oracle.Graph(xyz, edges).count_4pcf_parity()
+    oe, oo, ncl = oracle_4pcf(kind, seed, n, r, nb)
     np.testing.assert_array_equal(e, oe)
     np.testing.assert_array_equal(o, oo)
     assert st["cliques4"] == ncl and ncl > 0
@@ -396,7 +408,7 @@ def test_4pcf_matches_oracle(gpu_available, monkeypatch, layout, kind, seed, n, 
 def test_4pcf_s4_matches_oracle(gpu_available, kind, seed, n, r, nb):
     # S4 configurations (six edge bins up to vertex relabelling), even and odd channels
     say("4pcf s4", kind, seed, n, r, nb)
-    xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 50, 2000)
+    xyz = points_4(kind, seed, n)
     edges = linear_edges_sq(r, nb)
     g = gtc.Graph(to_gpu(xyz), edges)
     e, o, st = g.count_4pcf_parity(s4=True)
@@ -404,7 +416,7 @@ def test_4pcf_s4_matches_oracle(gpu_available, kind, seed, n, r, nb):
     g.close()
     e = e.cpu().numpy().view(np.uint64)
     o = o.cpu().numpy()
-    oe, oo, ncl = oracle.Graph(xyz, edges).count_4pcf_parity(s4=True)
+    oe, oo, ncl = oracle_4pcf(kind, seed, n, r, nb, s4=True)
     np.testing.assert_array_equal(e, oe)
     np.testing.assert_array_equal(o, oo)
     assert st["cliques4"] == ncl and ncl > 0
@@ -454,6 +466,35 @@ def test_4pcf_mirror_negates_odd(gpu_available):
     np.testing.assert_array_equal(e, e2)
     np.testing.assert_array_equal(o, -o2)
     assert np.abs(o).sum() > 0
+
+
+def plane_points(seed: int, n: int, span: int, off_frac: float) -> np.ndarray:
+    """Lattice points of the plane 7x + 8y + 9z = const (basis (8, -7, 0), (9, 0, -7)) around the
+    grid centre; a fraction off_frac moved off it by +-(-1, 1, 0), one lattice step of that normal.
+    Most quadruples are coplanar or nearly so, with hub-relative triple products whose fp64 terms
+    exceed 2^53: plain fp64 rounding gets some of their signs wrong."""
+    rng = rng_for(seed)
+    s = rng.integers(-span, span + 1, size=n)
+    t = rng.integers(-span, span + 1, size=n)
+    p = np.stack([GRID // 2 + 8 * s + 9 * t, GRID // 2 - 7 * s, GRID // 2 - 7 * t], 1)
+    k = rng.choice([-1, 0, 1], size=n, p=[off_frac / 2, 1 - off_frac, off_frac / 2])
+    p = np.unique(p + k[:, None] * np.array([-1, 1, 0]), axis=0)
+    assert p.min() >= 0 and p.max() < GRID
+    return p.astype(np.int32)
+
+
+def test_4pcf_handedness_of_nearly_flat_tetrahedra(gpu_available):
+    # coplanar and nearly coplanar quadruples at large separations: the handedness must be the
+    # exact sign (zero for coplanar ones), as in the oracle's integer arithmetic
+    xyz = plane_points(37, 200, 30_000, 0.3)
+    edges = linear_edges_sq(450_000, 4)
+    say("4pcf flat", xyz.shape)
+    e, o, st = hip_4pcf(xyz, edges)
+    oe, oo, ncl = oracle.Graph(xyz, edges).count_4pcf_parity()
+    np.testing.assert_array_equal(e, oe)
+    np.testing.assert_array_equal(o, oo)
+    assert st["cliques4"] == ncl and ncl > 100_000
+    assert np.abs(oo).sum() > 0 and np.abs(oo).sum() < ncl  # both handed and flat ones
 
 
 def test_4pcf_requires_coords(gpu_available):
