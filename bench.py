@@ -10,6 +10,10 @@ enumeration kernel's algorithmic-bytes roofline, and the CPU oracle timed on a b
 the same workload on this host's cores.
 
     python bench.py [--config C2] [--steps 5] [--warmup 1] [--gpus 1] [--no-cpu-baseline]
+
+With --config C4 (the parity 4pCF workload) a step builds the graph and counts the binned
+tetrahedra with their even and odd channels instead; the line then reports tetrahedra/s and the
+4-clique kernel's VALU-issue roofline.
 """
 from __future__ import annotations
 
@@ -37,17 +41,39 @@ def lds_bytes(spoke_elements: int, triangles: int, weighted: bool, unsorted: boo
     per_tri = (0.0 if unsorted else 8.0) + 8.0 + (16.0 + 8.0 + 32.0 if weighted else 0.0)
     return per_elem * spoke_elements + per_tri * triangles
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_triplet_traffic.txt")
-FINGERPRINT_FILE = os.path.join(ROOT, "graph_triangle_counting_amd", "k_triplet.fingerprint")
+VALU_FILE = os.path.join(ROOT, "profiles", "k_clique4_valu.txt")
+# VALU issue: a wave64 instruction takes a 16-lane SIMD 4 clocks, 4 SIMDs per CU, so one wave
+# instruction per clock per CU: 256 CUs at 2.4 GHz (G wave-instructions/s)
+VALU_PEAK_GINST = 256 * 2.4
 
 
-def kernel_fingerprint() -> str | None:
-    """The enumeration kernel's machine-code fingerprint written by the build (sha256 of the
-    gfx950 instructions of every k_triplet instantiation), or None without a build."""
+def kernel_fingerprint(kernel: str = "k_triplet") -> str | None:
+    """A kernel's machine-code fingerprint written by the build (sha256 of the gfx950
+    instructions of all its instantiations), or None without a build."""
     try:
-        with open(FINGERPRINT_FILE) as fh:
+        with open(os.path.join(ROOT, "graph_triangle_counting_amd", f"{kernel}.fingerprint")) as fh:
             return fh.read().strip() or None
     except OSError:
         return None
+
+
+def measured_valu(key: str):
+    """VALU wave-instructions per k_clique4 launch from the committed rocprofv3 counter run
+    (SQ_INSTS_VALU), or None when that run predates the current kernel's machine code."""
+    try:
+        fp = kernel_fingerprint("k_clique4")
+        if fp is None:
+            return None
+        with open(VALU_FILE) as fh:
+            for line in fh:
+                if line.startswith("#") or not line.strip():
+                    continue
+                k, f, v = line.split()
+                if k == key and f == fp:
+                    return float(v)
+    except OSError:
+        pass
+    return None
 
 
 def measured_traffic(key: str):
@@ -112,10 +138,9 @@ def main():
     import workloads
 
     cfg = workloads.get(args.config)
-    if cfg.order != 3:
-        print("bench.py measures the 3pCF path; pick a 3pCF workload (C1, C2, C3, C5)",
-              file=sys.stderr)
-        sys.exit(2)
+    if cfg.order == 4:
+        bench_4pcf(args, cfg)
+        return
     log(f"[bench] generating {cfg.key} {cfg.name} n={cfg.n}")
     xyz_np, w_np = cfg.generate()
     edges = cfg.edges_sq()
@@ -208,6 +233,113 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_4pcf(args, cfg):
+    """The parity 4pCF path: build, the 4-clique count over sorted bin 6-tuples (even and odd
+    channels), release."""
+    import torch
+
+    import graph_triangle_counting_amd as gtc
+    log(f"[bench] generating {cfg.key} {cfg.name} n={cfg.n}")
+    xyz_np, _ = cfg.generate()
+    edges = cfg.edges_sq()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    csr_mode = args.csr_mode or ("host" if args.host_csr else "device")
+    xyz = torch.from_numpy(xyz_np).to(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        g = gtc.Graph(xyz, edges, tile_bytes=args.tile_bytes, csr_mode=csr_mode)
+        ev, od, st = g.count_4pcf_parity()
+        gst = g.stats()
+        g.close()
+        return st, gst
+
+    for k in range(args.warmup):
+        st, gst = step()
+        log(f"[bench] warmup {k}: build {gst['build_ms']:.2f} ms, kernel {st['kernel_ms']:.2f} ms, "
+            f"tetrahedra {st['cliques4']}")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    kms, bms, ncl = [], [], []
+    for k in range(args.steps):
+        st, gst = step()
+        kms.append(st["kernel_ms"])
+        bms.append(gst["build_ms"])
+        ncl.append(st["cliques4"])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert len(set(ncl)) == 1, "tetrahedron counts differ between steps"
+    K = ncl[0]
+    k_avg = sum(kms) / len(kms)
+    log(f"[bench] {args.steps} steps: {1e3 * elapsed / args.steps:.2f} ms/step, build "
+        f"{sum(bms) / len(bms):.2f} ms, kernel {k_avg:.3f} ms, tetrahedra {K}")
+    valu = measured_valu(cfg.key) if args.tile_bytes == 0 else None
+    achieved = None if valu is None else valu / (k_avg * 1e-3) / 1e9
+    roofline = {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_GINST,
+                "unit": "G VALU wave-instructions/s",
+                "frac": None if achieved is None else achieved / VALU_PEAK_GINST, "traffic": None,
+                "valu_insts_per_launch": valu,
+                "valu_insts_per_tetrahedron": None if valu is None else valu / K,
+                "kernel": "k_clique4", "kernel_ms": k_avg,
+                "kernel_tetrahedra_per_s": K / (k_avg * 1e-3),
+                "launch": {"waves_per_wg": st["launch_waves"], "workgroups": st["launch_blocks"],
+                           "lds_bytes": st["launch_lds_bytes"]}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_4pcf(cfg, xyz_np, args.cpu_threads)
+    out = {
+        "metric": "4-cliques (tetrahedra) counted/sec with the even/odd parity split (4pCF), "
+                  "1 MI355X",
+        "value": K * args.steps / elapsed,
+        "unit": "tetrahedra/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32+f64",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.key} {cfg.name}", "n_points": cfg.n, "kind": cfg.kind,
+                   "r_max": cfg.r, "nbins": cfg.nbins, "configurations": "sorted 6-tuples",
+                   "edges": st["edges"], "tetrahedra": K, "tile_bytes": args.tile_bytes,
+                   "csr_mode": csr_mode},
+        "build_ms": sum(bms) / len(bms),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_4pcf(cfg, xyz, threads):
+    """The oracle's parity 4pCF, as it is, on every stride-th hub of the same point set."""
+    import numpy as np
+
+    import oracle
+    _, stride = CPU_SAMPLE[cfg.key]
+    nthreads = threads or (os.cpu_count() or 1)
+    try:
+        nthreads = min(nthreads, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        pass
+    log(f"[bench] cpu baseline: oracle 4pCF on {xyz.shape[0]} points, hub stride {stride}, "
+        f"{nthreads} threads")
+    t0 = time.perf_counter()
+    g = oracle.Graph(xyz, cfg.edges_sq(), nthreads=nthreads)
+    tb = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ev, _, ncl = g.count_4pcf_parity(hub_stride=stride, nthreads=nthreads)
+    tc = time.perf_counter() - t0
+    assert int(np.asarray(ev, dtype=np.uint64).sum()) == ncl
+    return {"value": ncl / tc, "unit": "tetrahedra/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"full point set ({xyz.shape[0]} points); tetrahedra of every {stride}-th "
+                      f"hub label ({ncl} tetrahedra); count phase {tc:.2f} s, graph build "
+                      f"{tb:.2f} s",
+            "tetrahedra": ncl, "count_s": tc, "build_s": tb}
 
 
 def achievable_hbm_gbs(nbytes: int = 1 << 30, reps: int = 5) -> dict:

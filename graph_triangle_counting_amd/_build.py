@@ -38,17 +38,22 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-FINGERPRINT = os.path.join(PKG, "k_triplet.fingerprint")
+# kernel -> source file; build() writes <kernel>.fingerprint beside the library for each
+FINGERPRINTED = {"k_triplet": "triplet.hip", "k_clique4": "clique4.hip"}
 
 
-def kernel_fingerprint_from_isa() -> str:
-    """sha256 (first 16 hex digits) of the gfx950 instructions of every k_triplet instantiation:
-    the device assembly of triplet.hip with comments, labels' line comments and blank lines
-    removed.  It changes with the enumeration kernel's machine code and with nothing else (host
-    code, headers the kernel does not use, comments)."""
+def fingerprint_path(kernel: str) -> str:
+    return os.path.join(PKG, f"{kernel}.fingerprint")
+
+
+def kernel_fingerprint_from_isa(kernel: str = "k_triplet") -> str:
+    """sha256 (first 16 hex digits) of the gfx950 instructions of every instantiation of the
+    kernel: the device assembly of its source with comments, labels' line comments and blank lines
+    removed.  It changes with the kernel's machine code and with nothing else (host code, headers
+    the kernel does not use, comments)."""
     import hashlib
     import re
-    src = os.path.join(CSRC, "triplet.hip")
+    src = os.path.join(CSRC, FINGERPRINTED[kernel])
     r = subprocess.run([HIPCC, *FLAGS, "--cuda-device-only", "-S", src, "-o", "-"],
                        capture_output=True, text=True)
     if r.returncode != 0:
@@ -56,7 +61,7 @@ def kernel_fingerprint_from_isa() -> str:
     h = hashlib.sha256()
     inside = False
     for line in r.stdout.splitlines():
-        if re.match(r"^_ZN3gtc9k_triplet\w*:", line):
+        if re.match(rf"^_ZN3gtc{len(kernel)}{kernel}\w*:", line):
             inside = True
         elif inside and line.startswith(".Lfunc_end"):
             inside = False
@@ -70,11 +75,12 @@ def kernel_fingerprint_from_isa() -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs)) + 1) as ex:
-        fp = ex.submit(kernel_fingerprint_from_isa)
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs)) + len(FINGERPRINTED)) as ex:
+        fps = {k: ex.submit(kernel_fingerprint_from_isa, k) for k in FINGERPRINTED}
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-        with open(FINGERPRINT, "w") as fh:
-            fh.write(fp.result() + "\n")
+        for k, fp in fps.items():
+            with open(fingerprint_path(k), "w") as fh:
+                fh.write(fp.result() + "\n")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -74,12 +74,16 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) / 16 * 16;
 __host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh, bool wl = false) {
     return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 22 * 8 * 4 + (wl ? 48 * (size_t)ncfg : 0);
 }
+// per-wave enumeration scratch: bitset words and their edge offsets, edges and their
+// tetrahedron offsets, 64 entries each
+constexpr size_t kEnumScratch = 4 * 64 * 4;
 // per-wave part: position map, row coordinates (hub-relative), hub-edge bins, bitset rows,
-// (weighted) row weights
+// (weighted) row weights, enumeration scratch
 __host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int words,
                                                   bool weighted = false) {
     return (size_t)map_bytes + align16(16 * (size_t)max_m) + align16((size_t)max_m) +
-           align16(4 * (size_t)max_m * words) + (weighted ? align16(8 * (size_t)max_m) : 0);
+           align16(4 * (size_t)max_m * words) + (weighted ? align16(8 * (size_t)max_m) : 0) +
+           kEnumScratch;
 }
 
 // Add a signed 64-bit v to the two's complement 128-bit word p[0] (low) | p[1] (high): the low
@@ -118,6 +122,39 @@ __device__ __forceinline__ int orient_sign(double4 C, double X0, double X1, doub
     const int64_t v = (int64_t)C.x * (int64_t)X0 + (int64_t)C.y * (int64_t)X1 +
                       (int64_t)C.z * (int64_t)X2;
     return (v > 0) - (v < 0);
+}
+
+// inclusive prefix sum of v over the 64 lanes of the wave
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(v, d, kWave);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
+// largest L in [0, 64) with off[L] <= x, for nondecreasing off[0..63] with off[0] <= x
+__device__ __forceinline__ int last_le(const int32_t *off, int x) {
+    int L = 0;
+#pragma unroll
+    for (int s = 32; s > 0; s >>= 1)
+        if (off[L + s] <= x) L += s;
+    return L;
+}
+
+// position of the set bit of x with r set bits below it (0 <= r < popcount(x))
+__device__ __forceinline__ int select_bit(uint32_t x, int r) {
+    int pos = 0;
+#pragma unroll
+    for (int h = 16; h > 0; h >>= 1) {
+        const int c = __popc(x & ((1u << h) - 1u));
+        const bool up = r >= c;
+        r = up ? r - c : r;
+        x = up ? x >> h : x;
+        pos = up ? pos + h : pos;
+    }
+    return pos;
 }
 
 // bin of an exact squared distance (a double below 2^53), against the edges as doubles
@@ -162,6 +199,12 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                                                  align16((size_t)a.max_m));
     double *rw = reinterpret_cast<double *>(reinterpret_cast<unsigned char *>(adj) +
                                             align16(4 * (size_t)a.max_m * a.words));
+    // enumeration scratch: after the weights (weighted) or the bitset rows
+    int32_t *sw_off = reinterpret_cast<int32_t *>(reinterpret_cast<unsigned char *>(rw) +
+                                                  (WT ? align16(8 * (size_t)a.max_m) : 0));
+    uint32_t *sw_bits = reinterpret_cast<uint32_t *>(sw_off + kWave);
+    int32_t *eb_off = reinterpret_cast<int32_t *>(sw_bits + kWave);
+    uint32_t *eb_ab = reinterpret_cast<uint32_t *>(eb_off + kWave);
     const int N = a.nb + 5;  // 6-combinations of [0, N) <-> nondecreasing 6-tuples of [0, nb)
     unsigned long long *wg = nullptr;  // this workgroup's copy of the global class sums
     if (WT) wg = a.wsum + (long long)(blockIdx.x % (unsigned)a.wcopies) * a.wstride;
@@ -263,104 +306,177 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
         }
         wave_lds_sync4();
 
-        // tetrahedra: for each local edge (a, b), a in window c1 and b in window c2, common bits
-        // c of rows a and b
+        // tetrahedra: every local edge (a, b), a in window c1 and b in window c2, with every
+        // common bit c of rows a and b.  The work is spread evenly over the lanes: lanes take 64
+        // bitset words of rows a and a prefix sum over the wave numbers their edges; lanes take
+        // 64 of these edges and count their tetrahedra (a second prefix sum); each lane then
+        // walks an equal share of those tetrahedra in order.
         unsigned int my_cl = 0;
-        for (int t = p1_lo * W + lane; t < p1_hi * W; t += kWave) {
-            const int ra = t / W, wa = t - ra * W;
-            // positions [p2_lo, p2_hi) of word wa
-            const int blo = min(max(p2_lo - wa * 32, 0), 32), bhi = min(max(p2_hi - wa * 32, 0), 32);
-            const uint32_t range = (bhi >= 32 ? 0xffffffffu : ((1u << bhi) - 1u)) &
-                                   ~(blo >= 32 ? 0xffffffffu : ((1u << blo) - 1u));
-            uint32_t bits = adj[t] & range;
-            if (!bits) continue;
-            // per spoke a: hub-relative coordinates A (hub at the origin) and the bin of (i, a)
-            const double4 A = rel4(rc[ra]);
-            const int bia = rbin[ra];
-            while (bits) {
-                const int rbb = wa * 32 + __builtin_ctz(bits);
-                bits &= bits - 1;
-                // per pair (a, b): B, the bins of (i, b) and (a, b), |a - b|^2 and X = A x B
-                const double4 B = rel4(rc[rbb]);
-                const int bib = rbin[rbb];
-                const double dab = sq3(A.x - B.x, A.y - B.y, A.z - B.z);
-                const int bab = edge_bin_d(dab, se, a.nb);
-                const double X0 = fma(A.y, B.z, -(A.z * B.y)), X1 = fma(A.z, B.x, -(A.x * B.z)),
-                             X2 = fma(A.x, B.y, -(A.y * B.x));  // exact: products below 2^40
-                // the parts of the vertex keys that c does not change (integer sums, exact)
-                const double kab = A.w + B.w, ka = A.w + dab, kb = B.w + dab;
-                for (int w2 = (rbb + 1) >> 5; w2 < W; ++w2) {
-                    uint32_t cm = adj[ra * W + w2] & adj[rbb * W + w2];
-                    while (cm) {
-                        const int rcc = w2 * 32 + __builtin_ctz(cm);
-                        cm &= cm - 1;
-                        const double4 Cc = rel4(rc[rcc]);
-                        const double dac = sq3(A.x - Cc.x, A.y - Cc.y, A.z - Cc.z);
-                        const double dbc = sq3(B.x - Cc.x, B.y - Cc.y, B.z - Cc.z);
-                        // the six bins in edge order of the vertices (i, a, b, c)
-                        int bb[6] = {bia, bib, rbin[rcc], bab, edge_bin_d(dac, se, a.nb),
-                                     edge_bin_d(dbc, se, a.nb)};
-                        int rank = 0;
-                        if (a.s4rank) {  // S4 configuration: one table read
-                            int key = 0;
+        for (int t0 = p1_lo * W; t0 < p1_hi * W; t0 += kWave) {
+            const int t = t0 + lane;
+            uint32_t bits = 0u;
+            if (t < p1_hi * W) {
+                const int wa = t % W;
+                // positions [p2_lo, p2_hi) of word wa
+                const int blo = min(max(p2_lo - wa * 32, 0), 32), bhi = min(max(p2_hi - wa * 32, 0), 32);
+                const uint32_t range = (bhi >= 32 ? 0xffffffffu : ((1u << bhi) - 1u)) &
+                                       ~(blo >= 32 ? 0xffffffffu : ((1u << blo) - 1u));
+                bits = adj[t] & range;
+            }
+            const int ecnt = __popc(bits);
+            const int eincl = wave_incl_scan(ecnt, lane);
+            const int ne = __shfl(eincl, kWave - 1, kWave);
+            if (ne == 0) continue;
+            sw_bits[lane] = bits;
+            sw_off[lane] = eincl - ecnt;
+            wave_lds_sync4();
+            for (int e0 = 0; e0 < ne; e0 += kWave) {
+                // edge e0 + lane: (a, b) packed as a | b << 16, and its tetrahedron count (an
+                // idle lane holds b = 0xffff, no words, no tetrahedra)
+                const int e = e0 + lane;
+                uint32_t ab = 0xffff0000u;
+                int tcnt = 0;
+                if (e < ne) {
+                    const int L = last_le(sw_off, e);
+                    const int tw = t0 + L, ea = tw / W;
+                    const int eb = (tw - ea * W) * 32 + select_bit(sw_bits[L], e - sw_off[L]);
+                    ab = (uint32_t)ea | ((uint32_t)eb << 16);
+                    for (int w2 = (eb + 1) >> 5; w2 < W; ++w2)
+                        tcnt += __popc(adj[ea * W + w2] & adj[eb * W + w2]);
+                }
+                const int tincl = wave_incl_scan(tcnt, lane);
+                const int nt = __shfl(tincl, kWave - 1, kWave);
+                eb_ab[lane] = ab;
+                eb_off[lane] = tincl - tcnt;
+                wave_lds_sync4();
+                // this lane's share [kbeg, kend) of the nt tetrahedra, from edge j, word w2, bits cm
+                const int kbeg = (int)(((int64_t)lane * nt) >> 6);
+                const int kend = (int)(((int64_t)(lane + 1) * nt) >> 6);
+                int j = 0, ra = 0, rbb = 0, w2 = 0;
+                uint32_t cm = 0u;
+                if (kbeg < kend) {
+                    j = last_le(eb_off, kbeg);
+                    ra = (int)(eb_ab[j] & 0xffffu);
+                    rbb = (int)(eb_ab[j] >> 16);
+                    int r = kbeg - eb_off[j];
+                    w2 = (rbb + 1) >> 5;
+                    cm = adj[ra * W + w2] & adj[rbb * W + w2];
+                    for (int c = __popc(cm); r >= c && w2 + 1 < W; c = __popc(cm)) {
+                        r -= c;
+                        ++w2;
+                        cm = adj[ra * W + w2] & adj[rbb * W + w2];
+                    }
+                    cm &= 0xffffffffu << select_bit(cm, r);
+                }
+                // terms of the pair (a, b), computed when the edge changes: hub-relative
+                // coordinates A, B (hub at the origin), the bins of (i, a), (i, b), (a, b),
+                // |a - b|^2, X = A x B (exact: products below 2^40) and the parts of the vertex
+                // keys that c does not change (integer sums, exact)
+                int pj = -1, bia = 0, bib = 0, bab = 0;
+                double4 A = make_double4(0, 0, 0, 0), B = A;
+                double dab = 0, X0 = 0, X1 = 0, X2 = 0, kab = 0, ka = 0, kb = 0;
+                for (int k = kbeg; k < kend; ++k) {
+                    if (j != pj) {
+                        pj = j;
+                        A = rel4(rc[ra]);
+                        B = rel4(rc[rbb]);
+                        bia = rbin[ra];
+                        bib = rbin[rbb];
+                        dab = sq3(A.x - B.x, A.y - B.y, A.z - B.z);
+                        bab = edge_bin_d(dab, se, a.nb);
+                        X0 = fma(A.y, B.z, -(A.z * B.y));
+                        X1 = fma(A.z, B.x, -(A.x * B.z));
+                        X2 = fma(A.x, B.y, -(A.y * B.x));
+                        kab = A.w + B.w;
+                        ka = A.w + dab;
+                        kb = B.w + dab;
+                    }
+                    const int rcc = w2 * 32 + __builtin_ctz(cm);
+                    const double4 Cc = rel4(rc[rcc]);
+                    const double dac = sq3(A.x - Cc.x, A.y - Cc.y, A.z - Cc.z);
+                    const double dbc = sq3(B.x - Cc.x, B.y - Cc.y, B.z - Cc.z);
+                    // the six bins in edge order of the vertices (i, a, b, c)
+                    int bb[6] = {bia, bib, rbin[rcc], bab, edge_bin_d(dac, se, a.nb),
+                                 edge_bin_d(dbc, se, a.nb)};
+                    int rank = 0;
+                    if (a.s4rank) {  // S4 configuration: one table read
+                        int key = 0;
 #pragma unroll
-                            for (int q = 0; q < 6; ++q) key = key * a.nb + bb[q];
-                            rank = (int)a.s4rank[key];
-                        } else {  // sorted 6-tuple: sorting network, combinatorial rank
-                            cswap(bb[1], bb[2]); cswap(bb[4], bb[5]); cswap(bb[0], bb[2]);
-                            cswap(bb[3], bb[5]); cswap(bb[0], bb[1]); cswap(bb[3], bb[4]);
-                            cswap(bb[1], bb[4]); cswap(bb[0], bb[3]); cswap(bb[2], bb[5]);
-                            cswap(bb[1], bb[3]); cswap(bb[2], bb[4]); cswap(bb[2], bb[3]);
-                            int prev = -1;
+                        for (int q = 0; q < 6; ++q) key = key * a.nb + bb[q];
+                        rank = (int)a.s4rank[key];
+                    } else {  // sorted 6-tuple: sorting network, combinatorial rank
+                        cswap(bb[1], bb[2]); cswap(bb[4], bb[5]); cswap(bb[0], bb[2]);
+                        cswap(bb[3], bb[5]); cswap(bb[0], bb[1]); cswap(bb[3], bb[4]);
+                        cswap(bb[1], bb[4]); cswap(bb[0], bb[3]); cswap(bb[2], bb[5]);
+                        cswap(bb[1], bb[3]); cswap(bb[2], bb[4]); cswap(bb[2], bb[3]);
+                        int prev = -1;
 #pragma unroll
-                            for (int q = 0; q < 6; ++q) {
-                                const int cq = bb[q] + q;  // strictly increasing combination element
-                                rank += binom[(N - prev - 1) * 8 + (6 - q)] -
-                                        binom[(N - cq) * 8 + (6 - q)];
-                                prev = cq;
+                        for (int q = 0; q < 6; ++q) {
+                            const int cq = bb[q] + q;  // strictly increasing combination element
+                            rank += binom[(N - prev - 1) * 8 + (6 - q)] -
+                                    binom[(N - cq) * 8 + (6 - q)];
+                            prev = cq;
+                        }
+                    }
+                    // vertex keys (sums of the three squared edge lengths, exact) of i, a, b,
+                    // c; sorting them ascending permutes the vertices, and the orientation of
+                    // the sorted tetrahedron is the parity of that permutation times
+                    // orient(i, a, b, c) = C . (A x B); a tie leaves no handedness
+                    double k0 = kab + Cc.w, k1 = ka + dac, k2 = kb + dbc, k3 = Cc.w + dac + dbc;
+                    int par = 0;
+                    auto cx = [&](double &u, double &v) {
+                        const bool sw = v < u;
+                        const double lo = sw ? v : u, hi = sw ? u : v;
+                        u = lo;
+                        v = hi;
+                        par ^= (int)sw;
+                    };
+                    cx(k0, k1); cx(k2, k3); cx(k0, k2); cx(k1, k3); cx(k1, k2);
+                    int sgn = 0;
+                    if (k0 != k1 && k1 != k2 && k2 != k3) {
+                        const int o = orient_sign(Cc, X0, X1, X2);
+                        sgn = par ? -o : o;
+                    }
+                    if (WT) {  // the four weights ascending, product without fusion
+                        double v0 = wi, v1 = rw[ra], v2 = rw[rbb], v3 = rw[rcc], t;
+                        t = fmin(v0, v1); v1 = fmax(v0, v1); v0 = t;
+                        t = fmin(v2, v3); v3 = fmax(v2, v3); v2 = t;
+                        t = fmin(v0, v2); v2 = fmax(v0, v2); v0 = t;
+                        t = fmin(v1, v3); v3 = fmax(v1, v3); v1 = t;
+                        t = fmin(v1, v2); v2 = fmax(v1, v2); v1 = t;
+                        const double pr = __dmul_rn(__dmul_rn(__dmul_rn(v0, v1), v2), v3);
+                        const double qv = rint(__dmul_rn(pr, a.two_s));  // exact, |qv| < 2^57
+                        const int cls = sgn > 0 ? 0 : (sgn < 0 ? 1 : 2);
+                        add_i128((WM == 2 ? wl : wg) + 2 * (3 * rank + cls), (long long)qv);
+                    }
+                    if (GH) {
+                        atomicAdd(&a.even[rank], 1ull);
+                        if (sgn) atomicAdd(&a.odd[rank], (unsigned long long)(long long)sgn);
+                    } else {
+                        atomicAdd(&ev[rank], 1u);
+                        if (sgn) atomicAdd(&od[rank], sgn);
+                    }
+                    ++my_cl;
+                    // the next tetrahedron: next bit, word or edge (the counts promise one while
+                    // k + 1 < kend; the bound on j only guards the scratch)
+                    cm &= cm - 1u;
+                    if (k + 1 < kend) {
+                        while (!cm) {
+                            if (++w2 >= W) {
+                                do {
+                                    ++j;
+                                    ra = (int)(eb_ab[j] & 0xffffu);
+                                    rbb = (int)(eb_ab[j] >> 16);
+                                    w2 = (rbb + 1) >> 5;
+                                } while (w2 >= W && j < kWave - 1);
+                                if (w2 >= W) break;
                             }
+                            cm = adj[ra * W + w2] & adj[rbb * W + w2];
                         }
-                        // vertex keys (sums of the three squared edge lengths, exact) of i, a, b,
-                        // c; sorting them ascending permutes the vertices, and the orientation of
-                        // the sorted tetrahedron is the parity of that permutation times
-                        // orient(i, a, b, c) = C . (A x B); a tie leaves no handedness
-                        double k0 = kab + Cc.w, k1 = ka + dac, k2 = kb + dbc, k3 = Cc.w + dac + dbc;
-                        int par = 0;
-                        auto cx = [&](double &u, double &v) {
-                            const bool sw = v < u;
-                            const double lo = sw ? v : u, hi = sw ? u : v;
-                            u = lo;
-                            v = hi;
-                            par ^= (int)sw;
-                        };
-                        cx(k0, k1); cx(k2, k3); cx(k0, k2); cx(k1, k3); cx(k1, k2);
-                        int sgn = 0;
-                        if (k0 != k1 && k1 != k2 && k2 != k3) {
-                            const int o = orient_sign(Cc, X0, X1, X2);
-                            sgn = par ? -o : o;
-                        }
-                        if (WT) {  // the four weights ascending, product without fusion
-                            double v0 = wi, v1 = rw[ra], v2 = rw[rbb], v3 = rw[rcc], t;
-                            t = fmin(v0, v1); v1 = fmax(v0, v1); v0 = t;
-                            t = fmin(v2, v3); v3 = fmax(v2, v3); v2 = t;
-                            t = fmin(v0, v2); v2 = fmax(v0, v2); v0 = t;
-                            t = fmin(v1, v3); v3 = fmax(v1, v3); v1 = t;
-                            t = fmin(v1, v2); v2 = fmax(v1, v2); v1 = t;
-                            const double pr = __dmul_rn(__dmul_rn(__dmul_rn(v0, v1), v2), v3);
-                            const double qv = rint(__dmul_rn(pr, a.two_s));  // exact, |qv| < 2^57
-                            const int cls = sgn > 0 ? 0 : (sgn < 0 ? 1 : 2);
-                            add_i128((WM == 2 ? wl : wg) + 2 * (3 * rank + cls), (long long)qv);
-                        }
-                        if (GH) {
-                            atomicAdd(&a.even[rank], 1ull);
-                            if (sgn) atomicAdd(&a.odd[rank], (unsigned long long)(long long)sgn);
-                        } else {
-                            atomicAdd(&ev[rank], 1u);
-                            if (sgn) atomicAdd(&od[rank], sgn);
-                        }
-                        ++my_cl;
+                        if (!cm) break;
                     }
                 }
+                wave_lds_sync4();
             }
         }
         unsigned int tot = my_cl;
