@@ -69,10 +69,16 @@ __device__ __forceinline__ void wave_lds_sync4() {
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) / 16 * 16; }
 
-// per-workgroup part: even u32[ncfg], odd i32[ncfg] (unless the bins are global), binomials C[22][8]
-// fixed part: even / odd count bins (unless global), binomials, (LDS class sums) [ncfg][3][2] words
+// rank of a nondecreasing 6-tuple b_0 <= ... <= b_5 of [0, nb) in lexicographic order, as a sum
+// of one table entry per position: rank = sum_q G[q][b_q].  With N = nb + 5 and c_q = b_q + q the
+// combinatorial number system gives rank = C(N, 6) + sum_{q<5} C(N - c_q - 1, 5 - q) -
+// sum_q C(N - c_q, 6 - q); G[q][b] collects the terms of position q (C(N, 6) goes to q = 0).
+constexpr int kRankTab = 6 * GTC_MAX_BINS_4PCF;
+
+// fixed part: even / odd count bins (unless global), the rank table G[6][16], (LDS class sums)
+// [ncfg][3][2] words
 __host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh, bool wl = false) {
-    return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 22 * 8 * 4 + (wl ? 48 * (size_t)ncfg : 0);
+    return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 4 * kRankTab + (wl ? 48 * (size_t)ncfg : 0);
 }
 // per-wave enumeration scratch: bitset words and their edge offsets, edges and their
 // tetrahedron offsets, 64 entries each
@@ -157,13 +163,13 @@ __device__ __forceinline__ int select_bit(uint32_t x, int r) {
     return pos;
 }
 
-// bin of an exact squared distance (a double below 2^53), against the edges as doubles
-__device__ __forceinline__ int edge_bin_d(double d2, const double *se, int nb) {
-    int l = 0, h = nb;  // se[l] <= d2 < se[h]
-    while (h - l > 1) {
-        const int md = (l + h) >> 1;
-        if (d2 >= se[md]) l = md; else h = md;
-    }
+// bin of an exact squared distance d2 < e_nb (a double below 2^53): se holds the edges as doubles,
+// padded with +inf up to a power of two P >= nb, and the search takes log2(P) steps of a size the
+// whole wave shares (h = P/2, P/4, ..., 1)
+__device__ __forceinline__ int edge_bin_d(double d2, const double *se, int half) {
+    int l = 0;
+    for (int h = half; h > 0; h >>= 1)
+        if (d2 >= se[l + h]) l += h;
     return l;
 }
 
@@ -183,13 +189,13 @@ template <bool GH, int WM>
 __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *edges) {
     constexpr bool WT = WM != 0;
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ double se[GTC_MAX_BINS_4PCF + 1];  // squared edges (integers below 2^53)
+    __shared__ double se[GTC_MAX_BINS_4PCF + 1];  // squared edges (integers below 2^53), +inf pad
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     const size_t hist_bytes = GH ? 0 : align16(4 * (size_t)a.ncfg);
     uint32_t *ev = reinterpret_cast<uint32_t *>(smem);
     int32_t *od = reinterpret_cast<int32_t *>(smem + hist_bytes);
-    int32_t *binom = reinterpret_cast<int32_t *>(smem + 2 * hist_bytes);
-    unsigned long long *wl = reinterpret_cast<unsigned long long *>(smem + 2 * hist_bytes + 22 * 8 * 4);
+    int32_t *rtab = reinterpret_cast<int32_t *>(smem + 2 * hist_bytes);  // G[q][b] at q * 16 + b
+    unsigned long long *wl = reinterpret_cast<unsigned long long *>(smem + 2 * hist_bytes + 4 * kRankTab);
     unsigned char *wbase = smem + clique_lds_fixed(a.ncfg, GH, WM == 2) +
                            (size_t)wid * clique_lds_wave(a.map_bytes, a.max_m, a.words, WT);
     uint16_t *pmap = reinterpret_cast<uint16_t *>(wbase);
@@ -216,12 +222,21 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
             ev[t] = 0;
             od[t] = 0;
         }
-    for (int t = threadIdx.x; t <= a.nb; t += blockDim.x) se[t] = (double)edges[t];
-    for (int t = threadIdx.x; t < 22 * 8; t += blockDim.x) {
-        const int x = t / 8, r = t % 8;
-        int64_t c = 1;
-        for (int u = 1; u <= r; ++u) c = c * (x - r + u) / u;  // C(x-r+u, u), exact at each step
-        binom[t] = (r <= x) ? (int32_t)c : 0;
+    int bin_half = 1;  // P / 2 for the smallest power of two P >= nb (0 for nb = 1)
+    while (2 * bin_half < a.nb) bin_half *= 2;
+    if (a.nb == 1) bin_half = 0;
+    for (int t = threadIdx.x; t <= GTC_MAX_BINS_4PCF; t += blockDim.x)
+        se[t] = t <= a.nb ? (double)edges[t] : __longlong_as_double(0x7ff0000000000000ll);
+    for (int t = threadIdx.x; t < kRankTab; t += blockDim.x) {
+        const int q = t / GTC_MAX_BINS_4PCF, b = t % GTC_MAX_BINS_4PCF, c = b + q;
+        auto C = [](int x, int r) -> int64_t {  // C(x, r), exact at each step; 0 outside
+            if (r < 0 || x < r) return 0;
+            int64_t v = 1;
+            for (int u = 1; u <= r; ++u) v = v * (x - r + u) / u;
+            return v;
+        };
+        const int64_t g = (q <= 4 ? C(N - c - 1, 5 - q) : 0) - C(N - c, 6 - q) + (q == 0 ? C(N, 6) : 0);
+        rtab[t] = b < a.nb ? (int32_t)g : 0;
     }
     __syncthreads();
 
@@ -383,7 +398,7 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                         bia = rbin[ra];
                         bib = rbin[rbb];
                         dab = sq3(A.x - B.x, A.y - B.y, A.z - B.z);
-                        bab = edge_bin_d(dab, se, a.nb);
+                        bab = edge_bin_d(dab, se, bin_half);
                         X0 = fma(A.y, B.z, -(A.z * B.y));
                         X1 = fma(A.z, B.x, -(A.x * B.z));
                         X2 = fma(A.x, B.y, -(A.y * B.x));
@@ -396,44 +411,34 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                     const double dac = sq3(A.x - Cc.x, A.y - Cc.y, A.z - Cc.z);
                     const double dbc = sq3(B.x - Cc.x, B.y - Cc.y, B.z - Cc.z);
                     // the six bins in edge order of the vertices (i, a, b, c)
-                    int bb[6] = {bia, bib, rbin[rcc], bab, edge_bin_d(dac, se, a.nb),
-                                 edge_bin_d(dbc, se, a.nb)};
+                    int bb[6] = {bia, bib, rbin[rcc], bab, edge_bin_d(dac, se, bin_half),
+                                 edge_bin_d(dbc, se, bin_half)};
                     int rank = 0;
                     if (a.s4rank) {  // S4 configuration: one table read
                         int key = 0;
 #pragma unroll
                         for (int q = 0; q < 6; ++q) key = key * a.nb + bb[q];
                         rank = (int)a.s4rank[key];
-                    } else {  // sorted 6-tuple: sorting network, combinatorial rank
+                    } else {  // sorted 6-tuple: sorting network, one rank-table entry per position
                         cswap(bb[1], bb[2]); cswap(bb[4], bb[5]); cswap(bb[0], bb[2]);
                         cswap(bb[3], bb[5]); cswap(bb[0], bb[1]); cswap(bb[3], bb[4]);
                         cswap(bb[1], bb[4]); cswap(bb[0], bb[3]); cswap(bb[2], bb[5]);
                         cswap(bb[1], bb[3]); cswap(bb[2], bb[4]); cswap(bb[2], bb[3]);
-                        int prev = -1;
 #pragma unroll
-                        for (int q = 0; q < 6; ++q) {
-                            const int cq = bb[q] + q;  // strictly increasing combination element
-                            rank += binom[(N - prev - 1) * 8 + (6 - q)] -
-                                    binom[(N - cq) * 8 + (6 - q)];
-                            prev = cq;
-                        }
+                        for (int q = 0; q < 6; ++q) rank += rtab[q * GTC_MAX_BINS_4PCF + bb[q]];
                     }
                     // vertex keys (sums of the three squared edge lengths, exact) of i, a, b,
                     // c; sorting them ascending permutes the vertices, and the orientation of
-                    // the sorted tetrahedron is the parity of that permutation times
-                    // orient(i, a, b, c) = C . (A x B); a tie leaves no handedness
-                    double k0 = kab + Cc.w, k1 = ka + dac, k2 = kb + dbc, k3 = Cc.w + dac + dbc;
-                    int par = 0;
-                    auto cx = [&](double &u, double &v) {
-                        const bool sw = v < u;
-                        const double lo = sw ? v : u, hi = sw ? u : v;
-                        u = lo;
-                        v = hi;
-                        par ^= (int)sw;
-                    };
-                    cx(k0, k1); cx(k2, k3); cx(k0, k2); cx(k1, k3); cx(k1, k2);
+                    // the sorted tetrahedron is the parity of that permutation (the parity of its
+                    // inversions) times orient(i, a, b, c) = C . (A x B); a tie leaves no
+                    // handedness
+                    const double k0 = kab + Cc.w, k1 = ka + dac, k2 = kb + dbc, k3 = Cc.w + dac + dbc;
+                    const bool tie = k0 == k1 || k0 == k2 || k0 == k3 || k1 == k2 || k1 == k3 ||
+                                     k2 == k3;
+                    const bool par = (k0 > k1) ^ (k0 > k2) ^ (k0 > k3) ^ (k1 > k2) ^ (k1 > k3) ^
+                                     (k2 > k3);
                     int sgn = 0;
-                    if (k0 != k1 && k1 != k2 && k2 != k3) {
+                    if (!tie) {
                         const int o = orient_sign(Cc, X0, X1, X2);
                         sgn = par ? -o : o;
                     }
