@@ -13,6 +13,7 @@
 // nondecreasing 6-tuples), and the parity sign: vertices ordered by the sum of their squared edge
 // lengths, exact int64 signed volume (r01 x r02) . r03 (Eq.(3)), zero for a tie or zero volume.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <thread>
 #include <vector>
@@ -83,6 +84,7 @@ __host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh, bool wl = 
 // per-wave enumeration scratch: bitset words and their edge offsets, edges and their
 // tetrahedron offsets, 64 entries each
 constexpr size_t kEnumScratch = 4 * 64 * 4;
+constexpr int kConnLoads = 4;  // row loads in flight per lane while building the connectivity
 // per-wave part: position map, row coordinates (hub-relative), hub-edge bins, bitset rows,
 // (weighted) row weights, enumeration scratch
 __host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int words,
@@ -291,33 +293,64 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
         wave_lds_sync4();
         const int32_t hub_hi = hlab(m - 1);
 
-        // local connectivity: for every spoke a of the tile's windows, walk N+(j_a) against the
-        // hub map (the rows of the other spokes are not needed: no pair of this tile uses them)
-        for (int sp = p1_lo; sp < m - 1; ++sp) {
-            const bool in1 = sp < p1_hi, in2 = sp >= p2_lo && sp < p2_hi;
-            if (!in1 && !in2) {
-                if (sp >= p2_hi) break;
-                continue;
+        // local connectivity: for every spoke a of the tile's windows, the row N+(j_a) against
+        // the hub map (the rows of the other spokes are not needed: no pair of this tile uses
+        // them).  64 spokes at a time: a wave scan lays their rows end to end, and the lanes read
+        // the flat range with kConnLoads loads in flight each, so a hub waits for one round of
+        // row pointers per 64 spokes rather than one per spoke.
+        int32_t *fpre = sw_off;  // flat start of each spoke's row
+        const int32_t **fptr = reinterpret_cast<const int32_t **>(eb_off);  // row - flat start
+        const int sp_end = min(m - 1, max(p1_hi, p2_hi));
+        for (int p0 = p1_lo; p0 < sp_end; p0 += kWave) {
+            const int sp = p0 + lane;
+            int32_t len = 0;
+            const int32_t *row = a.col_1;
+            if (sp < sp_end) {
+                const bool in1 = sp < p1_hi, in2 = sp >= p2_lo && sp < p2_hi;
+                if (in1 || in2) {
+                    const int32_t j = hlab(sp);
+                    const int64_t jb = a.row_ptr[j];
+                    len = (int32_t)(a.row_ptr[j + 1] - jb);
+                    row = in1 ? a.col_1 + (jb - a.base_1) : a.col_2 + (jb - a.base_2);
+                }
             }
-            const int32_t j = hlab(sp);
-            const int64_t jb = a.row_ptr[j];
-            const int32_t jlen = (int32_t)(a.row_ptr[j + 1] - jb);
-            const int32_t *jrow = in1 ? a.col_1 + (jb - a.base_1) : a.col_2 + (jb - a.base_2);
-            for (int32_t e = lane; e < jlen; e += kWave) {
-                const int32_t k = (int32_t)((uint32_t)jrow[e] & a.label_mask);
-                if (k > hub_hi) break;
-                int32_t d = dom.delta[0], lim = dom.hi[0];
+            const int incl = wave_incl_scan(len, lane);
+            const int total = __shfl(incl, kWave - 1, kWave);
+            if (total == 0) continue;
+            fpre[lane] = incl - len;
+            fptr[lane] = row - (incl - len);
+            wave_lds_sync4();
+            for (int t0 = 0; t0 < total; t0 += kWave * kConnLoads) {
+                int32_t kk[kConnLoads], qq[kConnLoads];
 #pragma unroll
-                for (int t = 1; t < 5; ++t)
-                    if (k >= dom.lo[t]) { d = dom.delta[t]; lim = dom.hi[t]; }
-                if (k < lim) {
-                    const int32_t v = pmap[k + d];
-                    if (v) {
-                        const int b = v - 1;
-                        atomicOr(&adj[sp * W + (b >> 5)], 1u << (b & 31));
+                for (int u = 0; u < kConnLoads; ++u) {
+                    const int t = t0 + u * kWave + lane;
+                    kk[u] = INT_MAX;
+                    qq[u] = 0;
+                    if (t < total) {
+                        const int q = last_le(fpre, t);  // the spoke whose row holds t
+                        qq[u] = q;
+                        kk[u] = (int32_t)((uint32_t)fptr[q][t] & a.label_mask);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kConnLoads; ++u) {
+                    const int32_t k = kk[u];
+                    if (k > hub_hi) continue;  // past the hub's last neighbour (or no element)
+                    int32_t d = dom.delta[0], lim = dom.hi[0];
+#pragma unroll
+                    for (int t = 1; t < 5; ++t)
+                        if (k >= dom.lo[t]) { d = dom.delta[t]; lim = dom.hi[t]; }
+                    if (k < lim) {
+                        const int32_t v = pmap[k + d];
+                        if (v) {
+                            const int b = v - 1;
+                            atomicOr(&adj[(p0 + qq[u]) * W + (b >> 5)], 1u << (b & 31));
+                        }
                     }
                 }
             }
+            wave_lds_sync4();
         }
         wave_lds_sync4();
 
