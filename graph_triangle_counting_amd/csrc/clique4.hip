@@ -243,6 +243,11 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
     __syncthreads();
 
     unsigned int wave_cl = 0;
+    // weighted, global class sums: the lane's pending class sum (index 3 rank + class, 128-bit
+    // value), added out when a tetrahedron of another configuration or class comes, and at the
+    // end (global atomics are bound by throughput; a run of one configuration takes one)
+    int pend = -1;
+    unsigned long long plo = 0ull, phi = 0ull;
     HubQueue hub_queue;
     hub_queue.init(a.qcount, a.batch_cap, lane);
     for (;;) {
@@ -485,7 +490,21 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                         const double pr = __dmul_rn(__dmul_rn(__dmul_rn(v0, v1), v2), v3);
                         const double qv = rint(__dmul_rn(pr, a.two_s));  // exact, |qv| < 2^57
                         const int cls = sgn > 0 ? 0 : (sgn < 0 ? 1 : 2);
-                        add_i128((WM == 2 ? wl : wg) + 2 * (3 * rank + cls), (long long)qv);
+                        const int idx = 3 * rank + cls;
+                        if (WM == 2) {
+                            add_i128(wl + 2 * idx, (long long)qv);
+                        } else {
+                            if (idx != pend) {
+                                if (pend >= 0) add_u128_pair(wg + 2 * pend, plo, phi);
+                                pend = idx;
+                                plo = 0ull;
+                                phi = 0ull;
+                            }
+                            const unsigned long long u = (unsigned long long)(long long)qv;
+                            const unsigned long long n0 = plo + u;
+                            phi += (qv < 0.0 ? ~0ull : 0ull) + (n0 < plo ? 1ull : 0ull);
+                            plo = n0;
+                        }
                     }
                     if (GH) {
                         atomicAdd(&a.even[rank], 1ull);
@@ -532,6 +551,7 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
         }
         wave_lds_sync4();
     }
+    if (WM == 1 && pend >= 0) add_u128_pair(wg + 2 * pend, plo, phi);
     if (GH) return;
     __syncthreads();
     for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
@@ -716,7 +736,7 @@ static int weight_scale4_for(double a) {
 // copy stays in the L2 of one XCD), within a 256 MiB budget.
 static int weighted_copies(int64_t ncfg) {
     const int64_t per_copy = 48 * ncfg;  // [ncfg][3] 128-bit words
-    int64_t c = std::min<int64_t>(64, std::max<int64_t>(1, ((int64_t)256 << 20) / per_copy));
+    int64_t c = std::min<int64_t>(256, std::max<int64_t>(1, ((int64_t)256 << 20) / per_copy));
     if (c >= 8) c &= ~(int64_t)7;
     return (int)c;
 }
