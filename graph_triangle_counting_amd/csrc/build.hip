@@ -75,11 +75,18 @@ __device__ __forceinline__ double sq_dist(const int4 a, const int4 b) {
 }
 
 constexpr int kPairLoads = 8;
+constexpr int kPairEdgeSlots = 256;  // >= the largest power of two P with P / 2 < GTC_MAX_BINS
 
 template <bool EMIT>
 __global__ void __launch_bounds__(256) k_pairs(PairArgs a) {
-    __shared__ double se[GTC_MAX_BINS + 1];
-    for (int t = threadIdx.x; t <= a.nb; t += blockDim.x) se[t] = (double)a.edges[t];
+    // squared edges as doubles (integers below 2^53), padded with +inf up to a power of two
+    // P >= nb: the bin search then takes log2(P) steps of a size the whole wave shares
+    __shared__ double se[kPairEdgeSlots];
+    int half = 1;  // P / 2 (0 for nb = 1)
+    while (2 * half < a.nb) half *= 2;
+    if (a.nb == 1) half = 0;
+    for (int t = threadIdx.x; t < kPairEdgeSlots; t += blockDim.x)
+        se[t] = t <= a.nb ? (double)a.edges[t] : __longlong_as_double(0x7ff0000000000000ll);
     __syncthreads();
     const int64_t ii = a.h_lo + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (ii >= a.h_hi) return;
@@ -90,15 +97,12 @@ __global__ void __launch_bounds__(256) k_pairs(PairArgs a) {
     const double e0 = se[0], emax = se[a.nb];
     int32_t cnt = 0;
     int64_t w = EMIT ? a.row_ptr[i] - a.col_base : 0;
-    const int nb = a.nb;
     auto test = [&](int32_t j, double d2) __attribute__((always_inline)) {
         if (d2 >= e0 && d2 < emax) {
             if (EMIT) {
-                int l = 0, h = nb;  // se[l] <= d2 < se[h]
-                while (h - l > 1) {
-                    const int m = (l + h) >> 1;
-                    if (d2 >= se[m]) l = m; else h = m;
-                }
+                int l = 0;  // se[l] <= d2 < se[l + 1]
+                for (int h = half; h > 0; h >>= 1)
+                    if (d2 >= se[l + h]) l += h;
                 if (a.bin) {
                     a.col[w] = j;
                     a.bin[w] = (uint8_t)l;
