@@ -276,6 +276,10 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         const int32_t h0 = dom.hi[0], h1 = dom.hi[1], h2 = dom.hi[2], h3 = dom.hi[3],
                       h4 = dom.hi[4];
         const int32_t e1 = d1 - d0, e2 = d2 - d1, e3 = d3 - d2, e4 = d4 - d3;
+        // the same deltas in map bytes (weighted map: 4 bytes per label)
+        constexpr int32_t kMapEntry = W ? 4 : 1;
+        const int32_t d0b = d0 * kMapEntry, e1b = e1 * kMapEntry, e2b = e2 * kMapEntry,
+                      e3b = e3 * kMapEntry, e4b = e4 * kMapEntry;
         const int32_t g1 = h1 - h0, g2 = h2 - h1, g3 = h3 - h2, g4 = h4 - h3;
 
         // Walk the rows of (up to) 64 spokes laid end to end: lane q describes spoke p0 + q by
@@ -323,23 +327,30 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     own = q | ((int32_t)cbij[q] << 8);
                 }
             };
-            auto process = [&](int32_t k, int32_t bjk, int32_t ow) __attribute__((always_inline)) {
+            // the label's map entry, 0 when it is no neighbour of the hub
+            auto probe = [&](int32_t k) __attribute__((always_inline)) -> uint32_t {
                 int32_t mo;
+                int32_t mob = 0;  // flat walk: byte offset of the label's map entry
                 if constexpr (BANDED) {
                     mo = k - blo;  // k = -1 (no element) falls outside as well
-                    if ((uint32_t)mo >= (uint32_t)bsize) return;
+                    if ((uint32_t)mo >= (uint32_t)bsize) return 0u;
                 } else {
-                    if ((uint32_t)k > (uint32_t)hub_hi) return;  // past the hub's last neighbour
+                    if ((uint32_t)k > (uint32_t)hub_hi) return 0u;  // past the hub's last neighbour
                     // run of k from the run starts (nondecreasing), as sums of differences:
                     // a choice between captured variables would be folded into a pointer
                     // select that keeps the lambda closures in scratch
                     const bool r1 = k >= l1, r2 = k >= l2, r3 = k >= l3, r4 = k >= l4;
                     const int32_t d = d0 + (r1 ? e1 : 0) + (r2 ? e2 : 0) + (r3 ? e3 : 0) + (r4 ? e4 : 0);
                     const int32_t lim = h0 + (r1 ? g1 : 0) + (r2 ? g2 : 0) + (r3 ? g3 : 0) + (r4 ? g4 : 0);
-                    if (k >= lim) return;  // in a gap between the runs
+                    if (k >= lim) return 0u;  // in a gap between the runs
                     mo = k + d;
+                    mob = k * kMapEntry + d0b + (r1 ? e1b : 0) + (r2 ? e2b : 0) + (r3 ? e3b : 0) +
+                          (r4 ? e4b : 0);
                 }
-                const uint32_t v = W ? mapw[mo] : (uint32_t)map8[mo];
+                if constexpr (BANDED) return W ? mapw[mo] : (uint32_t)map8[mo];
+                else return W ? *reinterpret_cast<const uint32_t *>(map8 + mob) : (uint32_t)map8[mob];
+            };
+            auto hit = [&](int32_t bjk, int32_t ow, uint32_t v) __attribute__((always_inline)) {
                 if (!v) return;
                 const int32_t bij = ow >> 8;
                 const int32_t bik = W ? (int32_t)(v >> 16) : (int32_t)v - 1;
@@ -375,6 +386,19 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 }
                 ++my_hits;
             };
+            auto process_block = [&](const int32_t *kk, const int32_t *bb, const int32_t *qq)
+                                     __attribute__((always_inline)) {
+                if constexpr (BANDED) {
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u) hit(bb[u], qq[u], probe(kk[u]));
+                } else {  // every probe of the block first, then the hits
+                    uint32_t vv[kUnroll];
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u) vv[u] = probe(kk[u]);
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u) hit(bb[u], qq[u], vv[u]);
+                }
+            };
             // whole blocks of kWave * kUnroll elements need no bounds checks; then one checked tail
             int32_t t0 = 0;
             for (; t0 + kWave * kUnroll <= total; t0 += kWave * kUnroll) {
@@ -386,8 +410,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     qq[u] = own;
                     csr_entry<PK>(cp, bp, (uint32_t)t, kk[u], bb[u]);
                 }
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) process(kk[u], bb[u], qq[u]);
+                process_block(kk, bb, qq);
             }
             if (t0 < total) {
                 int32_t kk[kUnroll], bb[kUnroll], qq[kUnroll];
@@ -403,8 +426,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                         csr_entry<PK>(cp, bp, (uint32_t)t, kk[u], bb[u]);
                     }
                 }
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) process(kk[u], bb[u], qq[u]);
+                process_block(kk, bb, qq);
             }
             wave_lds_sync();  // the next chunk overwrites the chunk arrays
         };
