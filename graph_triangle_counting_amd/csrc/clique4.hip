@@ -9,9 +9,16 @@
 // < j_c is a set bit c of row_a AND row_b.  The pages keep this matrix in a global scratch slot
 // per gang; it lives in LDS here.
 //
-// Per tetrahedron: the six edge bins, sorted and ranked (combinatorial number system over
-// nondecreasing 6-tuples), and the parity sign: vertices ordered by the sum of their squared edge
-// lengths, exact int64 signed volume (r01 x r02) . r03 (Eq.(3)), zero for a tie or zero volume.
+// The hub's tetrahedra are dealt out evenly over the lanes: a wave-wide prefix sum numbers the
+// edges (a, b) of a batch of bitset words, a second one numbers the tetrahedra of 64 such edges,
+// and each lane walks an equal share of them in order.
+//
+// Per tetrahedron: the six edge bins, sorted and ranked (lexicographic rank of the nondecreasing
+// 6-tuple, one table entry per position), and the parity sign: vertices ordered by the sum of
+// their squared edge lengths, and the sign of the signed volume (r01 x r02) . r03 (Eq.(3)) in that
+// order, zero for a tie or zero volume.  Lengths and keys are exact in fp64 (hub-relative integer
+// coordinates below 2^20); the volume's sign comes from fp64 behind an error-bound filter, or
+// exactly from int64 when the filter cannot decide.
 #include <algorithm>
 #include <climits>
 #include <cmath>
