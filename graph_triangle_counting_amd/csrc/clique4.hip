@@ -21,6 +21,8 @@
 // exactly from int64 when the filter cannot decide.
 #include <algorithm>
 #include <climits>
+#include <cstdlib>
+#include <cstring>
 #include <cmath>
 #include <thread>
 #include <vector>
@@ -68,6 +70,11 @@ struct CliqueArgs {
     unsigned long long *wsum;
     int wcopies;
     long long wstride;
+    // LDS configuration cache (weighted, WM 3): cache_k configurations have an LDS slot:
+    // cache_slot[rank] is the slot or -1, cache_rank[slot] the configuration
+    int32_t cache_k;
+    const int16_t *cache_slot;
+    const int32_t *cache_rank;
 };
 
 __device__ __forceinline__ void wave_lds_sync4() {
@@ -84,14 +91,20 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) / 16 * 16;
 constexpr int kRankTab = 6 * GTC_MAX_BINS_4PCF;
 
 // fixed part: even / odd count bins (unless global), the rank table G[6][16], (LDS class sums)
-// [ncfg][3][2] words
-__host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh, bool wl = false) {
+// [ncfg][3][2] words.  With an LDS configuration cache of k > 0 slots: even / odd bins and class
+// sums per slot, the slot of every configuration (int16) and the configuration of every slot.
+__host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh, bool wl = false, int k = 0) {
+    if (k > 0)
+        return align16(4 * (size_t)k) * 2 + 4 * kRankTab + 48 * (size_t)k +
+               align16(2 * (size_t)ncfg) + align16(4 * (size_t)k);
     return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 4 * kRankTab + (wl ? 48 * (size_t)ncfg : 0);
 }
 // per-wave enumeration scratch: bitset words and their edge offsets, edges and their
 // tetrahedron offsets, 64 entries each
 constexpr size_t kEnumScratch = 4 * 64 * 4;
 constexpr int kConnLoads = 4;  // row loads in flight per lane while building the connectivity
+constexpr int kCacheStride = 64;  // configuration cache: every 64th hub of the hub list is sampled
+constexpr int kCacheMin = 256;    // fewest LDS slots worth a cache
 // per-wave part: position map, row coordinates (hub-relative), hub-edge bins, bitset rows,
 // (weighted) row weights, enumeration scratch
 __host__ __device__ inline size_t clique_lds_wave(int map_bytes, int max_m, int words,
@@ -193,19 +206,24 @@ __device__ __forceinline__ double4 rel4(int4 q) {
 
 // GH: bins go straight to global memory (configuration counts too large for LDS).  WM: 0
 // unweighted; 1 weighted, class sums in global memory; 2 weighted, class sums in LDS, added to
-// global memory when the workgroup ends.
+// global memory when the workgroup ends; 3 weighted, counts and class sums of the cache_k cached
+// configurations in LDS, of the others in global memory.
 template <bool GH, int WM>
 __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *edges) {
     constexpr bool WT = WM != 0;
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ double se[GTC_MAX_BINS_4PCF + 1];  // squared edges (integers below 2^53), +inf pad
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    const size_t hist_bytes = GH ? 0 : align16(4 * (size_t)a.ncfg);
+    const int nslot = WM == 3 ? a.cache_k : a.ncfg;  // LDS count bins (and class sums)
+    const size_t hist_bytes = GH ? 0 : align16(4 * (size_t)nslot);
     uint32_t *ev = reinterpret_cast<uint32_t *>(smem);
     int32_t *od = reinterpret_cast<int32_t *>(smem + hist_bytes);
     int32_t *rtab = reinterpret_cast<int32_t *>(smem + 2 * hist_bytes);  // G[q][b] at q * 16 + b
     unsigned long long *wl = reinterpret_cast<unsigned long long *>(smem + 2 * hist_bytes + 4 * kRankTab);
-    unsigned char *wbase = smem + clique_lds_fixed(a.ncfg, GH, WM == 2) +
+    int16_t *slot16 = reinterpret_cast<int16_t *>(smem + 2 * hist_bytes + 4 * kRankTab + 48 * (size_t)nslot);
+    int32_t *rank_of = reinterpret_cast<int32_t *>(reinterpret_cast<unsigned char *>(slot16) +
+                                                   align16(2 * (size_t)a.ncfg));
+    unsigned char *wbase = smem + clique_lds_fixed(a.ncfg, GH, WM == 2, WM == 3 ? a.cache_k : 0) +
                            (size_t)wid * clique_lds_wave(a.map_bytes, a.max_m, a.words, WT);
     uint16_t *pmap = reinterpret_cast<uint16_t *>(wbase);
     int4 *rc = reinterpret_cast<int4 *>(wbase + a.map_bytes);
@@ -223,11 +241,15 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
     const int N = a.nb + 5;  // 6-combinations of [0, N) <-> nondecreasing 6-tuples of [0, nb)
     unsigned long long *wg = nullptr;  // this workgroup's copy of the global class sums
     if (WT) wg = a.wsum + (long long)(blockIdx.x % (unsigned)a.wcopies) * a.wstride;
-    if (WM == 2)
-        for (int t = threadIdx.x; t < 6 * a.ncfg; t += blockDim.x) wl[t] = 0ull;
+    if (WM >= 2)
+        for (int t = threadIdx.x; t < 6 * nslot; t += blockDim.x) wl[t] = 0ull;
+    if (WM == 3) {
+        for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) slot16[t] = a.cache_slot[t];
+        for (int t = threadIdx.x; t < nslot; t += blockDim.x) rank_of[t] = a.cache_rank[t];
+    }
 
     if (!GH)
-        for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
+        for (int t = threadIdx.x; t < nslot; t += blockDim.x) {
             ev[t] = 0;
             od[t] = 0;
         }
@@ -487,6 +509,8 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                         const int o = orient_sign(Cc, X0, X1, X2);
                         sgn = par ? -o : o;
                     }
+                    // the configuration's LDS slot (WM 3: -1 when it is not cached)
+                    const int sl = WM == 3 ? (int)slot16[rank] : rank;
                     if (WT) {  // the four weights ascending, product without fusion
                         double v0 = wi, v1 = rw[ra], v2 = rw[rbb], v3 = rw[rcc], t;
                         t = fmin(v0, v1); v1 = fmax(v0, v1); v0 = t;
@@ -498,8 +522,8 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                         const double qv = rint(__dmul_rn(pr, a.two_s));  // exact, |qv| < 2^57
                         const int cls = sgn > 0 ? 0 : (sgn < 0 ? 1 : 2);
                         const int idx = 3 * rank + cls;
-                        if (WM == 2) {
-                            add_i128(wl + 2 * idx, (long long)qv);
+                        if (WM == 2 || (WM == 3 && sl >= 0)) {
+                            add_i128(wl + 2 * (3 * sl + cls), (long long)qv);
                         } else {
                             if (idx != pend) {
                                 if (pend >= 0) add_u128_pair(wg + 2 * pend, plo, phi);
@@ -513,12 +537,12 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                             plo = n0;
                         }
                     }
-                    if (GH) {
+                    if (GH || (WM == 3 && sl < 0)) {
                         atomicAdd(&a.even[rank], 1ull);
                         if (sgn) atomicAdd(&a.odd[rank], (unsigned long long)(long long)sgn);
                     } else {
-                        atomicAdd(&ev[rank], 1u);
-                        if (sgn) atomicAdd(&od[rank], sgn);
+                        atomicAdd(&ev[sl], 1u);
+                        if (sgn) atomicAdd(&od[sl], sgn);
                     }
                     ++my_cl;
                     // the next tetrahedron: next bit, word or edge (the counts promise one while
@@ -548,29 +572,32 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
         for (int dd = kWave / 2; dd > 0; dd >>= 1) tot += __shfl_xor(tot, dd, kWave);
         wave_cl += tot;
         if (!GH && wave_cl >= a.flush_at) {
-            for (int t = lane; t < a.ncfg; t += kWave) {
+            for (int t = lane; t < nslot; t += kWave) {
+                const int r = WM == 3 ? rank_of[t] : t;
                 const uint32_t v = atomicExch(&ev[t], 0u);
-                if (v) atomicAdd(&a.even[t], (unsigned long long)v);
+                if (v) atomicAdd(&a.even[r], (unsigned long long)v);
                 const int32_t o = atomicExch(&od[t], 0);
-                if (o) atomicAdd(&a.odd[t], (unsigned long long)(long long)o);
+                if (o) atomicAdd(&a.odd[r], (unsigned long long)(long long)o);
             }
             wave_cl = 0;
         }
         wave_lds_sync4();
     }
-    if (WM == 1 && pend >= 0) add_u128_pair(wg + 2 * pend, plo, phi);
+    if ((WM == 1 || WM == 3) && pend >= 0) add_u128_pair(wg + 2 * pend, plo, phi);
     if (GH) return;
     __syncthreads();
-    for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) {
+    for (int t = threadIdx.x; t < nslot; t += blockDim.x) {
+        const int r = WM == 3 ? rank_of[t] : t;
         const uint32_t v = ev[t];
-        if (v) atomicAdd(&a.even[t], (unsigned long long)v);
+        if (v) atomicAdd(&a.even[r], (unsigned long long)v);
         const int32_t o = od[t];
-        if (o) atomicAdd(&a.odd[t], (unsigned long long)(long long)o);
+        if (o) atomicAdd(&a.odd[r], (unsigned long long)(long long)o);
     }
-    if (WM == 2)
-        for (int t = threadIdx.x; t < 3 * a.ncfg; t += blockDim.x) {
+    if (WM >= 2)
+        for (int t = threadIdx.x; t < 3 * nslot; t += blockDim.x) {
             const unsigned long long lo = wl[2 * t], hi = wl[2 * t + 1];
-            if (lo | hi) add_u128_pair(wg + 2 * t, lo, hi);
+            const int w = WM == 3 ? 3 * rank_of[t / 3] + t % 3 : t;
+            if (lo | hi) add_u128_pair(wg + 2 * w, lo, hi);
         }
 }
 
@@ -741,6 +768,13 @@ static int weight_scale4_for(double a) {
 // Copies of the global class sums: a few hot configurations take most tetrahedra, and their
 // global atomics serialise; workgroup b adds to copy b % copies (a multiple of the 8 XCDs, so each
 // copy stays in the L2 of one XCD), within a 256 MiB budget.
+// out[t] = hubs[t * stride] for t < ceil(n / stride): a sample that keeps the class order
+__global__ void k_every_nth(const int32_t *__restrict__ hubs, int64_t n, int stride,
+                            int32_t *__restrict__ out) {
+    const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (t * stride < n) out[t] = hubs[t * stride];
+}
+
 static int weighted_copies(int64_t ncfg) {
     const int64_t per_copy = 48 * ncfg;  // [ncfg][3] 128-bit words
     int64_t c = std::min<int64_t>(256, std::max<int64_t>(1, ((int64_t)256 << 20) / per_copy));
@@ -794,7 +828,30 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     const size_t per = clique_lds_wave(a.map_bytes, a.max_m, a.words, WT);
     const bool WL = WT && static_lds0 + clique_lds_fixed(a.ncfg, false, true) + 2 * per <= (size_t)ldsmax;
     const bool GH = static_lds0 + clique_lds_fixed(a.ncfg, false) + 2 * per > (size_t)ldsmax;
-    const size_t fixed = clique_lds_fixed(a.ncfg, GH, WL);
+    // Weighted sums too large for LDS, on a resident graph: an LDS cache for the configurations
+    // that an unweighted pass over every kCacheStride-th hub finds most frequent (the rest go to
+    // global memory).  The slot count fills the LDS left beside 8 (else 4) waves of hub data.
+    const size_t fixed_u = clique_lds_fixed(a.ncfg, false);
+    const size_t per_u = clique_lds_wave(a.map_bytes, a.max_m, a.words, false);
+    int cache_k = 0, cache_waves = 0;
+    bool cache_ok = WT && !WL && !GH && !G->windowed() && G->n_hubs > 0 &&
+                    static_lds0 + fixed_u + per_u <= (size_t)ldsmax;
+    if (const char *env = std::getenv("GTC_CONFIG_CACHE"))  // "off": global sums only (tests)
+        if (std::strcmp(env, "off") == 0) cache_ok = false;
+    if (cache_ok)
+        for (int w = 8; w >= 4 && !cache_k; w >>= 1) {
+            const size_t used = static_lds0 + (size_t)w * per + 4 * kRankTab + align16(2 * (size_t)ncfg);
+            if (used >= (size_t)ldsmax) continue;
+            int64_t k = std::min<int64_t>({ncfg, (int64_t)32767, (int64_t)((ldsmax - used) / 60)});
+            while (k > 0 && static_lds0 + clique_lds_fixed(a.ncfg, false, false, (int)k) + w * per >
+                                (size_t)ldsmax)
+                --k;
+            if (k >= kCacheMin) {
+                cache_k = (int)k;
+                cache_waves = w;
+            }
+        }
+    size_t fixed = cache_k ? clique_lds_fixed(a.ncfg, false, false, cache_k) : clique_lds_fixed(a.ncfg, GH, WL);
     // Workgroups of 4 waves; a large LDS histogram (S4 configurations) allows one workgroup per
     // CU, which then takes as many waves (up to 16) as the LDS beside the histogram holds.
     const size_t static_lds = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
@@ -803,7 +860,8 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         waves = (int)std::min<size_t>(16, (ldsmax - static_lds - fixed) / std::max<size_t>(per, 1));
     while (waves > 1 && static_lds + fixed + waves * per > (size_t)ldsmax) waves >>= 1;
     if (waves < 1) waves = 1;
-    const size_t lds = fixed + waves * per;
+    if (cache_k) waves = cache_waves;
+    size_t lds = fixed + waves * per;
     if (static_lds + lds > (size_t)ldsmax) {
         set_error("4pCF needs %zu bytes of LDS per workgroup (longest row %d, hub domain %d); the "
                   "device allows %d", lds, a.max_m, a.map_bytes / 2, ldsmax);
@@ -825,6 +883,10 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     double *w_s = nullptr;
     unsigned long long *wsum = nullptr, *d_maxabs = nullptr;
     int32_t *d_bad = nullptr;
+    int32_t *cache_hubs = nullptr, *cache_rank = nullptr;
+    int16_t *cache_slot = nullptr;
+    unsigned long long *cache_even = nullptr, *cache_odd = nullptr;
+    const int64_t cache_ns = cache_k ? (G->n_hubs + kCacheStride - 1) / kCacheStride : 0;
     void *scratch = nullptr;
     const int64_t nkeys = s4 ? num_s4_keys(G->nb) : 0;
     const int copies = WT ? weighted_copies(ncfg) : 0;
@@ -842,6 +904,13 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
                 c.take(&wcol[k], std::max<int64_t>(G->max_window_edges, 1));
                 if (!G->packed) c.take(&wbin[k], std::max<int64_t>(G->max_window_edges, 1));
             }
+        if (cache_k) {
+            c.take(&cache_hubs, cache_ns);
+            c.take(&cache_even, ncfg);
+            c.take(&cache_odd, ncfg);
+            c.take(&cache_slot, ncfg);
+            c.take(&cache_rank, cache_k);
+        }
         if (WT) {
             c.take(&w_s, G->n);
             c.take(&wsum, 6 * (size_t)ncfg * copies);
@@ -878,10 +947,84 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     int64_t tiles_run = 0;
     const void *kfn = nullptr;
     int64_t max_blocks = 1;
+    // configuration cache: the unweighted pass over the sampled hubs, then slots for the most
+    // frequent configurations it met (at least one slot, so the layout stays the sized one)
+    if (!rc && cache_k) {
+        CliqueArgs pa = a;
+        const int wu = (int)std::max<size_t>(
+            1, std::min<size_t>(16, (ldsmax - static_lds - fixed_u) / std::max<size_t>(per_u, 1)));
+        const unsigned long long budget_u = 0x7fffffffull / (unsigned long long)wu;
+        const size_t lds_u = fixed_u + (size_t)wu * per_u;
+        const void *kfu = reinterpret_cast<const void *>(&k_clique4<false, 0>);
+        rc = fill_u64(reinterpret_cast<uint64_t *>(cache_even), ncfg, 0ull, s);
+        if (!rc) rc = fill_u64(reinterpret_cast<uint64_t *>(cache_odd), ncfg, 0ull, s);
+        if (!rc) {
+            hipLaunchKernelGGL(k_every_nth, dim3((unsigned)((cache_ns + 255) / 256)), dim3(256), 0, s,
+                               G->hubs, (int64_t)G->n_hubs, kCacheStride, cache_hubs);
+            rc = hipGetLastError() == hipSuccess ? GTC_OK : GTC_E_HIP;
+        }
+        if (!rc) rc = hub_class_counts(cache_hubs, cache_ns, G->row_ptr, G->work, qcount, s);
+        if (!rc) rc = fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s);
+        if (!rc && max_hub < budget_u / 2) {
+            pa.even = cache_even;
+            pa.odd = cache_odd;
+            pa.hubs = cache_hubs;
+            pa.n_hubs = (int32_t)cache_ns;
+            pa.batch_cap = 1;
+            pa.flush_at = (unsigned int)(budget_u - max_hub);
+            pa.cache_k = 0;
+            if (lds_u > 65536)
+                (void)hipFuncSetAttribute(kfu, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_u);
+            int pcu = 0;
+            (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&pcu, kfu, wu * kWave, lds_u);
+            const int64_t blocks_u = std::min<int64_t>((int64_t)cus * std::max(pcu, 1), (cache_ns + wu - 1) / wu);
+            const int64_t *edges_dev = G->d_edges;
+            void *args[] = {&pa, &edges_dev};
+            hipEvent_t e0 = nullptr, e1 = nullptr;  // timed with the count's launches
+            hipError_t e = hipEventCreate(&e0);
+            if (e == hipSuccess) kev.push_back(e0);
+            if (e == hipSuccess) e = hipEventCreate(&e1);
+            if (e == hipSuccess) kev.push_back(e1);
+            if (e == hipSuccess) e = hipEventRecord(e0, s);
+            if (e == hipSuccess)
+                e = hipLaunchKernel(kfu, dim3((unsigned)std::max<int64_t>(blocks_u, 1)),
+                                    dim3(wu * kWave), args, lds_u, s);
+            if (e == hipSuccess) e = hipGetLastError();
+            if (e == hipSuccess) e = hipEventRecord(e1, s);
+            if (e != hipSuccess) rc = hip_fail(e, "k_clique4 sample launch", __FILE__, __LINE__);
+        }
+        std::vector<unsigned long long> hc(ncfg, 0ull);
+        if (!rc) {
+            hipError_t e = hipMemcpyAsync(hc.data(), cache_even, 8 * ncfg, hipMemcpyDeviceToHost, s);
+            if (e == hipSuccess) e = hipStreamSynchronize(s);
+            if (e != hipSuccess) rc = hip_fail(e, "4pCF sample readback", __FILE__, __LINE__);
+        }
+        if (!rc) {
+            std::vector<int32_t> order(ncfg);
+            for (int64_t c = 0; c < ncfg; ++c) order[c] = (int32_t)c;
+            const int64_t hot = std::count_if(hc.begin(), hc.end(), [](unsigned long long v) { return v > 0; });
+            cache_k = (int)std::max<int64_t>(1, std::min<int64_t>(cache_k, hot));
+            std::partial_sort(order.begin(), order.begin() + cache_k, order.end(),
+                              [&](int32_t x, int32_t y) { return hc[x] != hc[y] ? hc[x] > hc[y] : x < y; });
+            std::vector<int16_t> slot(ncfg, (int16_t)-1);
+            for (int k = 0; k < cache_k; ++k) slot[order[k]] = (int16_t)k;
+            hipError_t e = hipMemcpyAsync(cache_slot, slot.data(), 2 * ncfg, hipMemcpyHostToDevice, s);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(cache_rank, order.data(), 4 * (size_t)cache_k, hipMemcpyHostToDevice, s);
+            if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host vectors go out of scope
+            if (e != hipSuccess) rc = hip_fail(e, "4pCF cache tables", __FILE__, __LINE__);
+            fixed = clique_lds_fixed(a.ncfg, false, false, cache_k);
+            lds = fixed + waves * per;
+            a.cache_k = cache_k;
+            a.cache_slot = cache_slot;
+            a.cache_rank = cache_rank;
+        }
+    }
     if (!rc && G->n_hubs > 0) {
 #define GTC_K4(G_, W_) reinterpret_cast<const void *>(&k_clique4<G_, W_>)
         kfn = GH ? (WT ? GTC_K4(true, 1) : GTC_K4(true, 0))
-                 : (WL ? GTC_K4(false, 2) : (WT ? GTC_K4(false, 1) : GTC_K4(false, 0)));
+                 : (cache_k ? GTC_K4(false, 3)
+                            : (WL ? GTC_K4(false, 2) : (WT ? GTC_K4(false, 1) : GTC_K4(false, 0))));
 #undef GTC_K4
         if (lds > 65536)
             (void)hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

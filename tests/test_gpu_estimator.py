@@ -60,6 +60,25 @@ def test_4pcf_weighted_matches_oracle(gpu_available, s4, kind, seed, n, r, nb, s
     np.testing.assert_array_equal(o.cpu().numpy(), o0.cpu().numpy())
 
 
+@pytest.mark.parametrize("kind,seed,n,r,nb", [("clustered", 46, 15_000, 6000, 8),
+                                              ("uniform", 47, 8000, 70_000, 6)])
+def test_4pcf_weighted_s4_cache_matches_global_sums(gpu_available, monkeypatch, kind, seed, n, r,
+                                                    nb):
+    # weighted S4 sums with the LDS cache of the sampled hot configurations equal those kept
+    # wholly in global memory, bit for bit, counts included
+    say("4pcf weighted s4 cache", kind, seed, n, r, nb)
+    xyz = uniform(seed, n) if kind == "uniform" else clustered(seed, n, 50, 2000)
+    w = rng_for(seed + 700).uniform(-2.0, 2.0, n)
+    g = gtc.Graph(to_gpu(xyz), linear_edges_sq(r, nb))
+    cached = [x.cpu().numpy() for x in g.count_4pcf_weighted(to_gpu_f64(w), s4=True)[:4]]
+    monkeypatch.setenv("GTC_CONFIG_CACHE", "off")
+    plain = [x.cpu().numpy() for x in g.count_4pcf_weighted(to_gpu_f64(w), s4=True)[:4]]
+    g.close()
+    for x, y in zip(cached, plain):
+        np.testing.assert_array_equal(x, y)
+    assert cached[0].view(np.uint64).sum() > 0 and np.abs(cached[3]).sum() > 0
+
+
 def test_4pcf_weighted_rejects_non_finite_weights(gpu_available):
     xyz = clustered(45, 500, 10, 2000)
     w = np.ones(500)
