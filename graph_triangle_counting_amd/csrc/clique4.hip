@@ -25,6 +25,8 @@
 #include <cstring>
 #include <cmath>
 #include <thread>
+#include <mutex>
+#include <map>
 #include <vector>
 
 #include "gtc_internal.h"
@@ -677,28 +679,71 @@ int64_t num_configs_s4(int nb) {
     return (k * k * k * k * k * k + 9 * k * k * k * k + 14 * k * k) / 24;  // Burnside over S4
 }
 
-// canonical tuples in rank order (host; the canonical test runs on all hardware threads)
+// true when no relabelling of the key's tuple gives a smaller key (the canonical tuple); most
+// keys meet a smaller relabelling within the first few, so the loop stops early
+static bool s4_is_canonical(uint32_t key, int nb) {
+    int t[6];
+    uint32_t k = key;
+    for (int e = 5; e >= 0; --e) {
+        t[e] = (int)(k % (uint32_t)nb);
+        k /= (uint32_t)nb;
+    }
+    constexpr int eu[6] = {0, 0, 0, 1, 1, 2}, ev[6] = {1, 2, 3, 2, 3, 3};
+    for (int perm = 1; perm < 24; ++perm) {  // perm 0 is the identity
+        int p[4] = {0, 1, 2, 3};
+        int code = perm;
+        for (int q = 0; q < 3; ++q) {
+            const int span = 4 - q, j = q + code % span;
+            code /= span;
+            const int tmp = p[q];
+            p[q] = p[j];
+            p[j] = tmp;
+        }
+        int r[6];
+        for (int e = 0; e < 6; ++e) r[s4_edge(p[eu[e]], p[ev[e]])] = t[e];
+        uint32_t k2 = 0;
+        for (int e = 0; e < 6; ++e) k2 = k2 * (uint32_t)nb + (uint32_t)r[e];
+        if (k2 < key) return false;
+    }
+    return true;
+}
+
+// canonical tuples in rank order (host), computed once per bin count and process: the canonical
+// test runs on all hardware threads, the tables are kept for later calls
 void config_bins_s4(int nb, int32_t *bins) {
+    static std::mutex mu;
+    static std::map<int, std::vector<int32_t>> done;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        auto it = done.find(nb);
+        if (it != done.end()) {
+            std::copy(it->second.begin(), it->second.end(), bins);
+            return;
+        }
+    }
     const int64_t nk = num_s4_keys(nb);
     std::vector<uint8_t> canon(nk);
     const int nt = std::max(1u, std::min(32u, std::thread::hardware_concurrency()));
     std::vector<std::thread> pool;
     for (int t = 0; t < nt; ++t)
         pool.emplace_back([&, t]() {
-            for (int64_t key = t; key < nk; key += nt)
-                canon[key] = s4_canonical_key((uint32_t)key, nb) == (uint32_t)key;
+            for (int64_t key = t; key < nk; key += nt) canon[key] = s4_is_canonical((uint32_t)key, nb);
         });
     for (auto &th : pool) th.join();
+    std::vector<int32_t> table(6 * (size_t)num_configs_s4(nb));
     int64_t r = 0;
     for (int64_t key = 0; key < nk; ++key) {
         if (!canon[key]) continue;
         int64_t k2 = key;
         for (int e = 5; e >= 0; --e) {
-            bins[6 * r + e] = (int32_t)(k2 % nb);
+            table[6 * r + e] = (int32_t)(k2 % nb);
             k2 /= nb;
         }
         ++r;
     }
+    std::copy(table.begin(), table.end(), bins);
+    std::lock_guard<std::mutex> lock(mu);
+    done.emplace(nb, std::move(table));
 }
 
 // Cayley-Menger: 288 V^2 of the tetrahedron with squared edges d (5x5 bordered determinant by
