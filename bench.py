@@ -120,6 +120,11 @@ def main():
                     help="where the CSR is kept: device memory, pinned host memory (windows "
                          "uploaded per tile) or nowhere (windows emitted again per tile); the "
                          "last two need --tile-bytes")
+    ap.add_argument("--s4", action="store_true",
+                    help="4pCF workloads: S4 configurations instead of sorted 6-tuples")
+    ap.add_argument("--weighted", action="store_true",
+                    help="4pCF workloads: the weighted count (exact class sums), weights uniform in "
+                         "[0.5, 1.5) drawn with seed 7")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (HBM counter calibration)")
     args = ap.parse_args()
@@ -236,11 +241,14 @@ def main():
 
 
 def bench_4pcf(args, cfg):
-    """The parity 4pCF path: build, the 4-clique count over sorted bin 6-tuples (even and odd
-    channels), release."""
+    """The parity 4pCF path: build, the 4-clique count (even and odd channels) over sorted bin
+    6-tuples, or S4 configurations (--s4), unweighted or with exact weighted class sums
+    (--weighted), release."""
+    import numpy as np
     import torch
 
     import graph_triangle_counting_amd as gtc
+    import workloads
     log(f"[bench] generating {cfg.key} {cfg.name} n={cfg.n}")
     xyz_np, _ = cfg.generate()
     edges = cfg.edges_sq()
@@ -248,11 +256,16 @@ def bench_4pcf(args, cfg):
     torch.cuda.set_device(dev)
     csr_mode = args.csr_mode or ("host" if args.host_csr else "device")
     xyz = torch.from_numpy(xyz_np).to(dev)
+    w_np = workloads.rng_for(7).uniform(0.5, 1.5, xyz_np.shape[0]) if args.weighted else None
+    w = None if w_np is None else torch.from_numpy(np.ascontiguousarray(w_np)).to(dev)
     torch.cuda.synchronize()
 
     def step():
         g = gtc.Graph(xyz, edges, tile_bytes=args.tile_bytes, csr_mode=csr_mode)
-        ev, od, st = g.count_4pcf_parity()
+        if w is None:
+            st = g.count_4pcf_parity(s4=args.s4)[-1]
+        else:
+            st = g.count_4pcf_weighted(w, s4=args.s4)[-1]
         gst = g.stats()
         g.close()
         return st, gst
@@ -276,7 +289,8 @@ def bench_4pcf(args, cfg):
     k_avg = sum(kms) / len(kms)
     log(f"[bench] {args.steps} steps: {1e3 * elapsed / args.steps:.2f} ms/step, build "
         f"{sum(bms) / len(bms):.2f} ms, kernel {k_avg:.3f} ms, tetrahedra {K}")
-    valu = measured_valu(cfg.key) if args.tile_bytes == 0 else None
+    variant = cfg.key + ("-s4" if args.s4 else "") + ("-w" if args.weighted else "")
+    valu = measured_valu(variant) if args.tile_bytes == 0 else None
     achieved = None if valu is None else valu / (k_avg * 1e-3) / 1e9
     roofline = {"bound": "alu", "achieved": achieved, "peak": VALU_PEAK_GINST,
                 "unit": "G VALU wave-instructions/s",
@@ -289,7 +303,7 @@ def bench_4pcf(args, cfg):
                            "lds_bytes": st["launch_lds_bytes"]}}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_4pcf(cfg, xyz_np, args.cpu_threads)
+        cpu = cpu_baseline_4pcf(cfg, xyz_np, args.cpu_threads, args.s4, w_np)
     out = {
         "metric": "4-cliques (tetrahedra) counted/sec with the even/odd parity split (4pCF), "
                   "1 MI355X",
@@ -305,7 +319,9 @@ def bench_4pcf(args, cfg):
         "dtype": "int32+f64",
         "data": "synthetic",
         "config": {"workload": f"{cfg.key} {cfg.name}", "n_points": cfg.n, "kind": cfg.kind,
-                   "r_max": cfg.r, "nbins": cfg.nbins, "configurations": "sorted 6-tuples",
+                   "r_max": cfg.r, "nbins": cfg.nbins,
+                   "configurations": "S4" if args.s4 else "sorted 6-tuples",
+                   "weighted": bool(args.weighted),
                    "edges": st["edges"], "tetrahedra": K, "tile_bytes": args.tile_bytes,
                    "csr_mode": csr_mode},
         "build_ms": sum(bms) / len(bms),
@@ -315,8 +331,9 @@ def bench_4pcf(args, cfg):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline_4pcf(cfg, xyz, threads):
-    """The oracle's parity 4pCF, as it is, on every stride-th hub of the same point set."""
+def cpu_baseline_4pcf(cfg, xyz, threads, s4=False, w=None):
+    """The oracle's parity 4pCF, as it is, on every stride-th hub of the same point set (weighted:
+    the whole set, the oracle's weighted count takes no hub stride)."""
     import numpy as np
 
     import oracle
@@ -332,7 +349,12 @@ def cpu_baseline_4pcf(cfg, xyz, threads):
     g = oracle.Graph(xyz, cfg.edges_sq(), nthreads=nthreads)
     tb = time.perf_counter() - t0
     t0 = time.perf_counter()
-    ev, _, ncl = g.count_4pcf_parity(hub_stride=stride, nthreads=nthreads)
+    if w is None:
+        ev, _, ncl = g.count_4pcf_parity(hub_stride=stride, nthreads=nthreads, s4=s4)
+    else:
+        stride = 1
+        ev = g.count_4pcf_weighted(w, s4=s4, nthreads=nthreads)[0]
+        ncl = int(np.asarray(ev, dtype=np.uint64).sum())
     tc = time.perf_counter() - t0
     assert int(np.asarray(ev, dtype=np.uint64).sum()) == ncl
     return {"value": ncl / tc, "unit": "tetrahedra/s", "cores": nthreads, "kind": "oracle",
