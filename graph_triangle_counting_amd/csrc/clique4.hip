@@ -280,7 +280,7 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
     int pend = -1;
     unsigned long long plo = 0ull, phi = 0ull;
     HubQueue hub_queue;
-    hub_queue.init(a.qcount, a.batch_cap, lane);
+    hub_queue.init(a.qcount, a.batch_cap, lane, (int)(blockIdx.x % kQueueParts));
     for (;;) {
         uint32_t hq;
         if (!hub_queue.next(a.queue, lane, hq)) break;
@@ -942,7 +942,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     int32_t *wcol[kSlots] = {nullptr, nullptr, nullptr};
     uint8_t *wbin[kSlots] = {nullptr, nullptr, nullptr};
     GTC_TRY(carve_alloc(&scratch, s, [&](Carver &c) {
-        c.take(&queue, (size_t)kHubClasses * kQueueStride);
+        c.take(&queue, (size_t)kQueueWords);
         c.take(&qcount, kHubClasses);
         if (tiled)
             for (int k = 0; k < kSlots; ++k) {
@@ -969,7 +969,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
             c.take(&s4ws, scan_workspace_bytes(nkeys) / sizeof(int64_t));
         }
     }));
-    int rc = fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s);
+    int rc = fill_u32(queue, kQueueWords, 0u, s);
     if (!rc && s4) rc = s4_rank_table(G->nb, s4rank, s4flags, s4scan, s4ws, s);
     int scale = 0;
     if (!rc && WT) {
@@ -1009,7 +1009,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
             rc = hipGetLastError() == hipSuccess ? GTC_OK : GTC_E_HIP;
         }
         if (!rc) rc = hub_class_counts(cache_hubs, cache_ns, G->row_ptr, G->work, qcount, s);
-        if (!rc) rc = fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s);
+        if (!rc) rc = fill_u32(queue, kQueueWords, 0u, s);
         if (!rc && max_hub < budget_u / 2) {
             pa.even = cache_even;
             pa.odd = cache_odd;
@@ -1084,7 +1084,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     auto launch = [&](const int32_t *hubs, int64_t nh) -> int {
         if (nh <= 0) return GTC_OK;
         GTC_TRY(hub_class_counts(hubs, nh, G->row_ptr, G->work, qcount, s));
-        GTC_TRY(fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s));
+        GTC_TRY(fill_u32(queue, kQueueWords, 0u, s));
         a.hubs = hubs;
         a.n_hubs = (int32_t)nh;
         a.batch_cap = 1;

@@ -195,6 +195,11 @@ __device__ __forceinline__ void hub_domain(int32_t i, int32_t c, const Grid &gr,
 // the L2 atomic unit at about one take per 10 ns, which alone costs ~10 ms per million hubs.
 constexpr int kHubClasses = 64;
 constexpr int kQueueStride = 64;  // u32 words between class counters (a 256-byte line each)
+// Each class's hub range is split into kQueueParts parts, one per XCD: workgroup b takes hubs from
+// part b % kQueueParts first (its XCD's L2 then serves one neighbourhood of the cell order), and
+// from the other parts once its own is drained.
+constexpr int kQueueParts = 8;
+constexpr int64_t kQueueWords = (int64_t)kHubClasses * kQueueParts * kQueueStride;
 constexpr int kBatchWorkLog2 = 15;
 
 __device__ __forceinline__ int hub_class(int64_t m, int64_t w) {
@@ -228,9 +233,12 @@ struct HubQueue {
     uint32_t cbeg, cend;  // lane c: positions [cbeg, cend) of class c
     uint32_t pos, end;    // current batch (wave-uniform)
     int cls;              // current class (wave-uniform)
+    int tried;            // parts of the current class drained so far (wave-uniform)
+    int home;             // first part to take from
     uint32_t cap;         // batch cap of this launch
 
-    __device__ __forceinline__ void init(const uint32_t *counts, uint32_t batch_cap, int lane) {
+    __device__ __forceinline__ void init(const uint32_t *counts, uint32_t batch_cap, int lane,
+                                         int home_part) {
         const uint32_t c = counts[lane];
         uint32_t incl = c;
 #pragma unroll
@@ -242,6 +250,8 @@ struct HubQueue {
         cend = incl;
         pos = end = 0;
         cls = 0;
+        tried = 0;
+        home = home_part;
         cap = batch_cap;
     }
 
@@ -251,18 +261,27 @@ struct HubQueue {
             if (cls >= kHubClasses) return false;
             const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)cbeg, cls);
             const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)cend, cls);
-            if (b < e) {
-                const uint32_t batch = class_batch(cls, cap);
-                uint32_t t = 0;
-                if (lane == 0) t = atomicAdd(&counters[cls * kQueueStride], batch);
-                t = (uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(t, 0, kWave));
-                if (t < e - b) {
-                    pos = b + t;
-                    end = e - pos < batch ? e : pos + batch;
-                    break;
+            if (b < e && tried < kQueueParts) {
+                const int p = (home + tried) % kQueueParts;
+                const uint64_t len = e - b;
+                const uint32_t pb = b + (uint32_t)(len * p / kQueueParts);
+                const uint32_t pe = b + (uint32_t)(len * (p + 1) / kQueueParts);
+                if (pb < pe) {
+                    const uint32_t batch = class_batch(cls, cap);
+                    uint32_t t = 0;
+                    if (lane == 0) t = atomicAdd(&counters[(cls * kQueueParts + p) * kQueueStride], batch);
+                    t = (uint32_t)__builtin_amdgcn_readfirstlane((int)__shfl(t, 0, kWave));
+                    if (t < pe - pb) {
+                        pos = pb + t;
+                        end = pe - pos < batch ? pe : pos + batch;
+                        break;
+                    }
                 }
+                ++tried;
+                continue;
             }
             ++cls;
+            tried = 0;
         }
         hq = pos++;
         return true;

@@ -221,7 +221,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
 
     unsigned int wave_hits = 0;
     HubQueue hub_queue;
-    hub_queue.init(a.qcount, a.batch_cap, lane);
+    hub_queue.init(a.qcount, a.batch_cap, lane, (int)(blockIdx.x % kQueueParts));
     for (;;) {
         uint32_t hq;
         if (!hub_queue.next(a.queue, lane, hq)) break;
@@ -685,7 +685,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             c.take(&d_maxabs, 1);
             c.take(&d_bad, 1);
         }
-        c.take(&queue, (size_t)kHubClasses * kQueueStride);
+        c.take(&queue, (size_t)kQueueWords);
         c.take(&qcount, kHubClasses);
         if (G->windowed())
             for (int b2 = 0; b2 < kSlots; ++b2) {
@@ -907,7 +907,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             a.base_s = ooc ? hr[G->win[sw]] : 0;
             a.s_lo = nw == 1 ? 0 : (int32_t)G->win[sw];
             a.s_hi = nw == 1 ? (int32_t)G->n : (int32_t)G->win[sw + 1];
-            TSTEP(fill_u32(queue, (int64_t)kHubClasses * kQueueStride, 0u, s));
+            TSTEP(fill_u32(queue, kQueueWords, 0u, s));
             TripletPlan tp = pl;
             tp.blocks = (int)std::min<int64_t>(pl.blocks, (nh + pl.waves - 1) / pl.waves);
             a.batch_cap = batch_cap(nh, (int64_t)tp.blocks * tp.waves);
