@@ -27,6 +27,7 @@ def _load():
         P = C.c_void_p
         i64, i32 = C.c_int64, C.c_int32
         lib.oracle_build_graph.argtypes = [i64, P, i32, P, i32, C.POINTER(P)]
+        lib.oracle_build_graph_forward.argtypes = [i64, P, i32, P, i32, C.POINTER(P)]
         lib.oracle_graph_free.argtypes = [P]
         lib.oracle_graph_n.argtypes = [P]
         lib.oracle_graph_n.restype = i64
@@ -36,6 +37,7 @@ def _load():
         lib.oracle_num_configs.argtypes = [i32, i32]
         lib.oracle_num_configs.restype = i64
         lib.oracle_count_3pcf.argtypes = [P, P, i64, i32, P, P, P, P]
+        lib.oracle_count_3pcf_part.argtypes = [P, P, i64, i64, i32, P, P, P, P]
         lib.oracle_count_3pcf_exact.argtypes = [P, P, i64, i32, P, P, P]
         lib.oracle_count_4pcf_parity.argtypes = [P, P, i64, i32, P, P, P]
         lib.oracle_forward_degrees.argtypes = [P, P]
@@ -116,16 +118,20 @@ def disconnected_4pcf_s4(nbins: int, xi) -> np.ndarray:
 
 
 class Graph:
-    """Oracle neighbour graph (caller's labels, full symmetric adjacency, rows ascending)."""
+    """Oracle neighbour graph (caller's labels, rows ascending): full symmetric adjacency, or
+    with forward_only=True only the neighbours above each label (half the memory; the counts are
+    the same)."""
 
-    def __init__(self, xyz: np.ndarray, edges_sq, nthreads: int = 0):
+    def __init__(self, xyz: np.ndarray, edges_sq, nthreads: int = 0, forward_only: bool = False):
         lib = _load()
         self.xyz = np.ascontiguousarray(xyz, dtype=np.int32).reshape(-1, 3)
         self.edges = np.ascontiguousarray(np.asarray(edges_sq, dtype=np.int64))
         self.nbins = int(self.edges.size - 1)
+        self.forward_only = bool(forward_only)
         h = C.c_void_p()
-        rc = lib.oracle_build_graph(self.xyz.shape[0], _ptr(self.xyz), self.nbins,
-                                    _ptr(self.edges), nthreads, C.byref(h))
+        build = lib.oracle_build_graph_forward if forward_only else lib.oracle_build_graph
+        rc = build(self.xyz.shape[0], _ptr(self.xyz), self.nbins, _ptr(self.edges), nthreads,
+                   C.byref(h))
         if rc:
             raise ValueError(f"oracle_build_graph failed ({rc})")
         self._h = h
@@ -155,16 +161,19 @@ class Graph:
         assert _lib.oracle_forward_degrees(self._h, _ptr(d)) == 0
         return d
 
-    def count_3pcf(self, w: np.ndarray | None = None, hub_stride: int = 1, nthreads: int = 0):
-        """Returns (counts uint64[n_cfg], weighted fp64[n_cfg] or None, scale s, walks)."""
+    def count_3pcf(self, w: np.ndarray | None = None, hub_stride: int = 1, nthreads: int = 0,
+                   hub_offset: int = 0):
+        """Returns (counts uint64[n_cfg], weighted fp64[n_cfg] or None, scale s, walks) over the
+        hubs i with i % hub_stride == hub_offset."""
         ncfg = num_configs(3, self.nbins)
         counts = np.zeros(ncfg, np.uint64)
         weighted = None if w is None else np.zeros(ncfg, np.float64)
         wa = None if w is None else np.ascontiguousarray(w, dtype=np.float64)
         s = C.c_int32(0)
         walks = C.c_uint64(0)
-        rc = _lib.oracle_count_3pcf(self._h, _ptr(wa), hub_stride, nthreads, _ptr(counts),
-                                    _ptr(weighted), C.byref(s), C.byref(walks))
+        rc = _lib.oracle_count_3pcf_part(self._h, _ptr(wa), hub_stride, hub_offset, nthreads,
+                                         _ptr(counts), _ptr(weighted), C.byref(s),
+                                         C.byref(walks))
         if rc:
             raise ValueError(f"oracle_count_3pcf failed ({rc})")
         return counts, weighted, int(s.value), int(walks.value)

@@ -84,8 +84,8 @@ static int validate_inputs(int64_t n, const int32_t *xyz, int32_t nb, const int6
     return 0;
 }
 
-int oracle_build_graph(int64_t n, const int32_t *xyz, int32_t nb, const int64_t *edges,
-                       int32_t nthreads, oracle_graph **out) {
+static int build_graph_impl(int64_t n, const int32_t *xyz, int32_t nb, const int64_t *edges,
+                            int32_t nthreads, int forward, oracle_graph **out) {
     if (!out) return ORACLE_E_INVALID;
     *out = NULL;
     int rc = validate_inputs(n, xyz, nb, edges);
@@ -152,7 +152,7 @@ int oracle_build_graph(int64_t n, const int32_t *xyz, int32_t nb, const int64_t 
                         int64_t c = (z * gdim + y) * gdim + x;
                         for (int64_t t = cell_start[c]; t < cell_start[c + 1]; t++) {
                             int32_t j = by_cell[t];
-                            if (j == i) continue;
+                            if (j == i || (forward && j < i)) continue;
                             int b = bin_of(edges, nb, sq_dist(p, xyz + 3 * (int64_t)j));
                             if (b < 0) continue;
                             if (pass) {
@@ -199,6 +199,18 @@ int oracle_build_graph(int64_t n, const int32_t *xyz, int32_t nb, const int64_t 
     if (fail) { oracle_graph_free(g); return ORACLE_E_NOMEM; }
     *out = g;
     return 0;
+}
+
+int oracle_build_graph(int64_t n, const int32_t *xyz, int32_t nb, const int64_t *edges,
+                       int32_t nthreads, oracle_graph **out) {
+    return build_graph_impl(n, xyz, nb, edges, nthreads, 0, out);
+}
+
+/* Only the neighbours above each point are kept: every walk of the 3pCF and 4pCF counts reads
+ * row entries beyond the spoke's own label, so the counts are those of the full graph. */
+int oracle_build_graph_forward(int64_t n, const int32_t *xyz, int32_t nb, const int64_t *edges,
+                               int32_t nthreads, oracle_graph **out) {
+    return build_graph_impl(n, xyz, nb, edges, nthreads, 1, out);
 }
 
 void oracle_graph_free(oracle_graph *g) {
@@ -301,9 +313,10 @@ static int64_t triangle_q(double wa, double wb, double wc, int s) {
 /* ---------------------------------------------------------------- 3pCF (§II.2, §III.1) */
 
 static int count_3pcf_impl(const oracle_graph *g, const double *w, int64_t hub_stride,
-                           int32_t nthreads, uint64_t *counts, __int128 *acc, int *scale_out,
-                           uint64_t *walks_out) {
-    if (!g || !counts || hub_stride < 1) return ORACLE_E_INVALID;
+                           int64_t hub_offset, int32_t nthreads, uint64_t *counts, __int128 *acc,
+                           int *scale_out, uint64_t *walks_out) {
+    if (!g || !counts || hub_stride < 1 || hub_offset < 0 || hub_offset >= hub_stride)
+        return ORACLE_E_INVALID;
     if (w && !weights_finite(w, g->n)) return ORACLE_E_INVALID;
     const int nb = g->nb;
     const int64_t ncfg = oracle_num_configs(3, nb);
@@ -323,7 +336,7 @@ static int count_3pcf_impl(const oracle_graph *g, const double *w, int64_t hub_s
         if (!my || (acc && !myacc)) fail = 1;
         #pragma omp for schedule(dynamic, 64)
         for (int64_t i = 0; i < g->n; i++) {
-            if (fail || i % hub_stride) continue;
+            if (fail || i % hub_stride != hub_offset) continue;
             const int64_t ie = g->row_ptr[i + 1];
             for (int64_t sj = g->row_ptr[i]; sj < ie; sj++) {
                 const int32_t j = g->col[sj];
@@ -371,6 +384,13 @@ static int count_3pcf_impl(const oracle_graph *g, const double *w, int64_t hub_s
 int oracle_count_3pcf(const oracle_graph *g, const double *w, int64_t hub_stride,
                       int32_t nthreads, uint64_t *counts, double *weighted, int32_t *scale_out,
                       uint64_t *walks_out) {
+    return oracle_count_3pcf_part(g, w, hub_stride, 0, nthreads, counts, weighted, scale_out,
+                                  walks_out);
+}
+
+int oracle_count_3pcf_part(const oracle_graph *g, const double *w, int64_t hub_stride,
+                           int64_t hub_offset, int32_t nthreads, uint64_t *counts,
+                           double *weighted, int32_t *scale_out, uint64_t *walks_out) {
     if (!g) return ORACLE_E_INVALID;
     const int64_t ncfg = oracle_num_configs(3, g->nb);
     __int128 *acc = NULL;
@@ -380,7 +400,7 @@ int oracle_count_3pcf(const oracle_graph *g, const double *w, int64_t hub_stride
         if (!acc) return ORACLE_E_NOMEM;
     }
     int s = 0;
-    int rc = count_3pcf_impl(g, w, hub_stride, nthreads, counts, acc, &s, walks_out);
+    int rc = count_3pcf_impl(g, w, hub_stride, hub_offset, nthreads, counts, acc, &s, walks_out);
     if (!rc && w) {
         /* one rounding of the exact sum, then an exact power-of-two scaling */
         for (int64_t c = 0; c < ncfg; c++) weighted[c] = ldexp((double)acc[c], -s);
@@ -398,7 +418,7 @@ int oracle_count_3pcf_exact(const oracle_graph *g, const double *w, int64_t hub_
     __int128 *acc = (__int128 *)malloc(sizeof(__int128) * (size_t)ncfg);
     if (!acc) return ORACLE_E_NOMEM;
     int s = 0;
-    int rc = count_3pcf_impl(g, w, hub_stride, nthreads, counts, acc, &s, NULL);
+    int rc = count_3pcf_impl(g, w, hub_stride, 0, nthreads, counts, acc, &s, NULL);
     if (!rc) {
         for (int64_t c = 0; c < ncfg; c++) {
             unsigned __int128 u = (unsigned __int128)acc[c];

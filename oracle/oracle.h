@@ -54,9 +54,14 @@ typedef struct oracle_graph_s oracle_graph;
 /* Neighbour graph in the caller's labels: full symmetric adjacency, rows sorted ascending. */
 int oracle_build_graph(int64_t n, const int32_t *xyz, int32_t nbins, const int64_t *edges_sq,
                        int32_t nthreads, oracle_graph **out);
+/* The same graph with each row cut to the neighbours above its own label (j > i): half the
+ * memory.  The 3pCF, 4pCF and 2pCF counts below read only such entries, so they give the same
+ * results on it; an export returns the forward rows. */
+int oracle_build_graph_forward(int64_t n, const int32_t *xyz, int32_t nbins,
+                               const int64_t *edges_sq, int32_t nthreads, oracle_graph **out);
 void oracle_graph_free(oracle_graph *g);
 int64_t oracle_graph_n(const oracle_graph *g);
-int64_t oracle_graph_nnz(const oracle_graph *g);               /* directed entries = 2E */
+int64_t oracle_graph_nnz(const oracle_graph *g);   /* entries: 2E, or E for a forward graph */
 /* Copy out the adjacency: row_ptr [n+1], col [nnz], bin [nnz]. */
 int oracle_graph_export(const oracle_graph *g, int64_t *row_ptr, int32_t *col, uint8_t *bin);
 
@@ -70,6 +75,13 @@ int64_t oracle_num_configs(int32_t order, int32_t nbins);
 int oracle_count_3pcf(const oracle_graph *g, const double *w, int64_t hub_stride,
                       int32_t nthreads, uint64_t *counts, double *weighted, int32_t *scale_out,
                       uint64_t *walks_out);
+
+/* As oracle_count_3pcf for the hubs i with i % hub_stride == hub_offset (0 <= hub_offset <
+ * hub_stride).  The counts of the hub_stride offsets add up to those of all hubs (weighted
+ * sums are rounded per call, so only the exact sums add up). */
+int oracle_count_3pcf_part(const oracle_graph *g, const double *w, int64_t hub_stride,
+                           int64_t hub_offset, int32_t nthreads, uint64_t *counts,
+                           double *weighted, int32_t *scale_out, uint64_t *walks_out);
 
 /* The same weighted sums before the final rounding: exact sum of q per configuration as
  * two's-complement 128-bit integers, little-endian (lo word first), [n_cfg][2]. */

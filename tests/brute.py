@@ -33,10 +33,11 @@ def config_index(nbins: int, k: int) -> dict:
     return {t: r for r, t in enumerate(itertools.combinations_with_replacement(range(nbins), k))}
 
 
-def triangles(xyz: np.ndarray, edges, w=None):
-    """Every pairwise-adjacent triple once.  Returns (counts, weighted_fl, weighted_exact) where
-    weighted_fl sums fl(fl(w1*w2)*w3) (weights ascending) exactly and rounds once, and
-    weighted_exact is the correctly rounded exact real sum of w_i w_j w_k."""
+def triangles(xyz: np.ndarray, edges, w=None, hubs=None):
+    """Every pairwise-adjacent triple once (only those whose smallest label is in ``hubs``, when
+    given).  Returns (counts, weighted_fl, weighted_exact) where weighted_fl sums
+    fl(fl(w1*w2)*w3) (weights ascending) exactly and rounds once, and weighted_exact is the
+    correctly rounded exact real sum of w_i w_j w_k."""
     a, b = adjacency(xyz, edges)
     nb = len(edges) - 1
     idx = config_index(nb, 3)
@@ -44,7 +45,10 @@ def triangles(xyz: np.ndarray, edges, w=None):
     acc_fl = [Fraction(0)] * len(idx)
     acc_ex = [Fraction(0)] * len(idx)
     n = xyz.shape[0]
+    hubset = None if hubs is None else {int(h) for h in hubs}
     for i, j, k in itertools.combinations(range(n), 3):
+        if hubset is not None and i not in hubset:
+            continue
         if a[i, j] and a[i, k] and a[j, k]:
             c = idx[tuple(sorted((int(b[i, j]), int(b[i, k]), int(b[j, k]))))]
             counts[c] += 1

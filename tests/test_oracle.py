@@ -84,6 +84,52 @@ def test_3pcf_matches_brute_force(seed, n, box, nb):
     np.testing.assert_array_equal(cnt2, cnt_b)
 
 
+@pytest.mark.parametrize("seed,n,box,nb", [(15, 70, 2000, 3), (16, 110, 3500, 6)])
+def test_forward_graph_matches_brute_force(seed, n, box, nb):
+    # forward rows (neighbours above the row's label) are the upper half of the brute adjacency,
+    # and the 3pCF / 4pCF / 2pCF counts on them are the brute-force ones
+    xyz = small_cloud(seed, n, box, nclump=3)
+    edges = linear_edges_sq(box // 2, nb)
+    w = 0.5 + rng_for(seed + 300).random(n)
+    gf = oracle.Graph(xyz, edges, forward_only=True)
+    rp, col, b = gf.export()
+    a, bb = brute.adjacency(xyz, edges)
+    assert gf.nnz == int(a.sum()) // 2
+    for i in range(n):
+        want = np.nonzero(a[i])[0]
+        want = want[want > i]
+        np.testing.assert_array_equal(col[rp[i]:rp[i + 1]], want)
+        np.testing.assert_array_equal(b[rp[i]:rp[i + 1]], bb[i, want])
+    cnt_b, wfl_b, _ = brute.triangles(xyz, edges, w)
+    cnt, wsum, _, walks = gf.count_3pcf(w)
+    np.testing.assert_array_equal(cnt, cnt_b)
+    np.testing.assert_array_equal(wsum, wfl_b)
+    assert walks == gf.nnz
+    ev_b, od_b = brute.cliques4(xyz, edges)
+    ev, od, _ = gf.count_4pcf_parity()
+    np.testing.assert_array_equal(ev, ev_b)
+    np.testing.assert_array_equal(od, od_b)
+    pc_b = brute.pairs(xyz, edges)[0]
+    np.testing.assert_array_equal(gf.count_2pcf()[0], pc_b)
+
+
+def test_hub_offsets_partition_the_count_by_smallest_label():
+    # hub_stride / hub_offset select the triangles whose smallest label is offset mod stride
+    xyz = small_cloud(17, 90, 2600, nclump=2)
+    edges = linear_edges_sq(1300, 5)
+    g = oracle.Graph(xyz, edges, forward_only=True)
+    full = g.count_3pcf()[0]
+    tot = np.zeros_like(full)
+    for off in range(3):
+        part = g.count_3pcf(hub_stride=3, hub_offset=off)[0]
+        want = brute.triangles(xyz, edges, hubs=range(off, 90, 3))[0]
+        np.testing.assert_array_equal(part, want)
+        tot += part
+    np.testing.assert_array_equal(tot, full)
+    with pytest.raises(ValueError):
+        g.count_3pcf(hub_stride=3, hub_offset=3)
+
+
 def test_3pcf_signed_weights_match_brute_force():
     # signed weights as in the data-minus-random estimator (§II.1); products are exact at this scale
     xyz = small_cloud(21, 70, 2500)
