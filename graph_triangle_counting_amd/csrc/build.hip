@@ -1,9 +1,9 @@
 // build.hip - the neighbour graph on the GPU (GRAMSCI v2 §II.1, Eq.(1); CSR layout §III.5.1).
 //
 // The pages build a kd-tree on the CPU; here the points are bucketed into cubic cells of side
-// >= r_max (cell counts and their scan give the cell starts; a stable radix sort of the cell keys,
-// ties in original order, gives the internal labels, so they are the same on every run), and
-// each point's forward neighbours
+// >= r_max (cell counts and their scan give the cell starts; stable counting-sort passes over the
+// digits of the cell keys, ties in original order, give the internal labels, so they are the same
+// on every run), and each point's forward neighbours
 // (larger internal label) are found in its own cell and the 13 forward neighbour cells.  Visiting
 // those cells in increasing key order emits every row already ascending, so no sort is needed.
 // Two passes over the same traversal: count (degrees, then a 64-bit scan to row offsets), emit.
@@ -11,8 +11,6 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
-
-#include <hipcub/hipcub.hpp>
 
 #include "gtc_internal.h"
 
@@ -24,8 +22,8 @@ __constant__ int8_t kFwd[13][3] = {{0, 0, 1},  {0, 1, -1},  {0, 1, 0},  {0, 1, 1
                                    {1, 1, -1}, {1, 1, 0},   {1, 1, 1}};
 
 __global__ void k_cellkey(const int32_t *__restrict__ xyz, int64_t n, Grid gr,
-                          int32_t *__restrict__ key, int32_t *__restrict__ idx,
-                          int32_t *__restrict__ cell_count, int32_t *__restrict__ err) {
+                          int32_t *__restrict__ key, int32_t *__restrict__ cell_count,
+                          int32_t *__restrict__ err) {
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i >= n) return;
     int x = xyz[3 * i], y = xyz[3 * i + 1], z = xyz[3 * i + 2];
@@ -36,8 +34,74 @@ __global__ void k_cellkey(const int32_t *__restrict__ xyz, int64_t n, Grid gr,
     }
     const int k = ((z / gr.cs) * gr.g + y / gr.cs) * gr.g + x / gr.cs;
     key[i] = k;
-    idx[i] = (int32_t)i;
     atomicAdd(&cell_count[k], 1);
+}
+
+// ---- stable counting sort of the cell keys (ties keep the original order)
+//
+// The keys are sorted by kDigitBits-bit digits, least significant first; each pass is a stable
+// counting sort of one digit.  Tile t (kSortTile consecutive positions of the pass's input) is one
+// wave.  k_digit_count writes the tile's count of each digit value to hist[d * tiles + t]; the
+// exclusive scan of hist (digit-major) is then the first output slot of each (digit, tile); and
+// k_digit_scatter walks its tile in order, 64 positions at a time, giving each element the next
+// slot of its digit.  Lanes with the same digit find each other with one ballot per digit bit and
+// take slots in lane order, so the output is stable, and after the last pass the keys are sorted
+// with ties in original order: the same labels on every run.
+constexpr int kDigitBits = 8;
+constexpr int kDigits = 1 << kDigitBits;
+constexpr int kSortTile = 2048;
+
+__global__ void __launch_bounds__(kWave) k_digit_count(const int32_t *__restrict__ key, int64_t n,
+                                                       int shift, int32_t *__restrict__ hist,
+                                                       int64_t tiles) {
+    __shared__ int32_t cnt[kDigits];
+    const int lane = threadIdx.x;
+    for (int d = lane; d < kDigits; d += kWave) cnt[d] = 0;
+    __syncthreads();
+    const int64_t lo = blockIdx.x * (int64_t)kSortTile;
+    const int64_t hi = lo + kSortTile < n ? lo + kSortTile : n;
+    for (int64_t i = lo + lane; i < hi; i += kWave)
+        atomicAdd(&cnt[(key[i] >> shift) & (kDigits - 1)], 1);
+    __syncthreads();
+    for (int d = lane; d < kDigits; d += kWave) hist[d * tiles + blockIdx.x] = cnt[d];
+}
+
+// val_in null: the values are the input positions (the first pass, whose input is in original
+// order).
+__global__ void __launch_bounds__(kWave) k_digit_scatter(
+    const int32_t *__restrict__ key_in, const int32_t *__restrict__ val_in, int64_t n, int shift,
+    int bits, const int32_t *__restrict__ slot0, int64_t tiles, int32_t *__restrict__ key_out,
+    int32_t *__restrict__ val_out) {
+    __shared__ int32_t next[kDigits];
+    const int lane = threadIdx.x;
+    for (int d = lane; d < kDigits; d += kWave) next[d] = slot0[d * tiles + blockIdx.x];
+    __syncthreads();
+    const int64_t lo = blockIdx.x * (int64_t)kSortTile;
+    const int64_t hi = lo + kSortTile < n ? lo + kSortTile : n;
+    for (int64_t base = lo; base < hi; base += kWave) {
+        const int64_t i = base + lane;
+        const bool valid = i < hi;
+        const int32_t k = valid ? key_in[i] : 0;
+        const int32_t v = valid ? (val_in ? val_in[i] : (int32_t)i) : 0;
+        const int d = (k >> shift) & (kDigits - 1);
+        // lanes holding the same digit value
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < bits; ++b) {
+            const uint64_t m = __ballot((d >> b) & 1);
+            peers &= ((d >> b) & 1) ? m : ~m;
+        }
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0));
+        int32_t slot = 0;
+        if (valid) slot = next[d] + below;
+        __syncthreads();  // every lane has read next[] before the group's last lane moves it on
+        if (valid) {
+            key_out[slot] = k;
+            val_out[slot] = v;
+            if (below == __popcll(peers) - 1) next[d] = slot + 1;
+        }
+        __syncthreads();
+    }
 }
 
 // sorted position r: the point perm[r] (keys sorted, ties in original order) and its coordinates
@@ -407,9 +471,10 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     GTC_HIP_CHECK(hipMemcpyAsync(G->d_edges, G->edges, sizeof(int64_t) * (G->nb + 1),
                                  hipMemcpyHostToDevice, s));
 
-    // build scratch: keys, original indices, cell counts, error flag, stats, scan partials, sort
-    // workspace
-    int32_t *key = nullptr, *idx = nullptr, *ccount = nullptr, *err = nullptr;
+    // build scratch: keys and the sort's ping-pong arrays, cell counts, error flag, stats, scan
+    // partials, the sort's digit counts
+    int32_t *key = nullptr, *key_t = nullptr, *val_t = nullptr, *val_u = nullptr;
+    int32_t *ccount = nullptr, *err = nullptr, *hist = nullptr;
     StatsOut *d_stats = nullptr;
     int64_t *scan_ws = nullptr;
     void *scratch = nullptr;
@@ -433,20 +498,20 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         }                                                                \
     } while (0)
 
-    const size_t scan_ws_bytes = std::max(scan_workspace_bytes(n), scan_workspace_bytes(gr.ncell));
-    // radix sort of the cell keys, only as many bits as the largest key needs
+    // counting-sort passes over the key digits, only as many bits as the largest key needs
     int key_bits = 1;
     while (key_bits < 31 && ((int64_t)1 << key_bits) < gr.ncell) ++key_bits;
-    size_t sort_ws_bytes = 0;
-    if (n > 0)
-        STEP_HIP(hipcub::DeviceRadixSort::SortPairs(nullptr, sort_ws_bytes, (const int32_t *)nullptr,
-                                                    (int32_t *)nullptr, (const int32_t *)nullptr,
-                                                    (int32_t *)nullptr, (int)n, 0, key_bits, s));
-    unsigned char *sort_ws = nullptr;
+    const int passes = (key_bits + kDigitBits - 1) / kDigitBits;
+    const int64_t tiles = (n + kSortTile - 1) / kSortTile;
+    const int64_t hist_n = tiles * kDigits;
+    const size_t scan_ws_bytes = std::max({scan_workspace_bytes(n), scan_workspace_bytes(gr.ncell),
+                                           scan_workspace_bytes(hist_n)});
     STEP(carve_alloc(&scratch, s, [&](Carver &c) {
         c.take(&key, n);
-        c.take(&idx, n);
-        c.take(&sort_ws, std::max<size_t>(sort_ws_bytes, 1));
+        c.take(&key_t, n);
+        c.take(&val_t, n);
+        c.take(&val_u, n);
+        c.take(&hist, hist_n + 1);
         c.take(&ccount, gr.ncell);
         c.take(&err, 1);
         c.take(&d_stats, 1);
@@ -458,13 +523,28 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
 
     if (n > 0) {
         hipLaunchKernelGGL(k_cellkey, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, gr, key,
-                           idx, ccount, err);
+                           ccount, err);
         STEP_HIP(hipGetLastError());
     }
     STEP(exclusive_scan_i32_to_i32(ccount, G->cell_start, gr.ncell, scan_ws, s));
     if (n > 0) {
-        STEP_HIP(hipcub::DeviceRadixSort::SortPairs(sort_ws, sort_ws_bytes, key, G->key_s, idx,
-                                                    G->perm, (int)n, 0, key_bits, s));
+        // pass p reads (kin, vin) and writes the next pair; the last pass writes (key_s, perm)
+        int32_t *kin = key, *vin = nullptr;
+        for (int p = 0; p < passes; ++p) {
+            const int shift = p * kDigitBits;
+            const int bits = std::min(kDigitBits, key_bits - shift);
+            int32_t *kout = p == passes - 1 ? G->key_s : (kin == key_t ? key : key_t);
+            int32_t *vout = p == passes - 1 ? G->perm : (vin == val_t ? val_u : val_t);
+            hipLaunchKernelGGL(k_digit_count, dim3((unsigned)tiles), dim3(kWave), 0, s, kin, n,
+                               shift, hist, tiles);
+            STEP_HIP(hipGetLastError());
+            STEP(exclusive_scan_i32_to_i32(hist, hist, hist_n, scan_ws, s));
+            hipLaunchKernelGGL(k_digit_scatter, dim3((unsigned)tiles), dim3(kWave), 0, s, kin, vin,
+                               n, shift, bits, hist, tiles, kout, vout);
+            STEP_HIP(hipGetLastError());
+            kin = kout;
+            vin = vout;
+        }
         hipLaunchKernelGGL(k_scatter, dim3(grid_for(n, 256)), dim3(256), 0, s, d_xyz, n, G->perm,
                            G->key_s, G->xyz_s);
         STEP_HIP(hipGetLastError());
