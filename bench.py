@@ -1,15 +1,20 @@
 """Benchmark of the graph 3pCF hot path on one MI355X.
 
-One step = the whole path on one resident synthetic workload: build the neighbour graph on the GPU
-(cell list, pair search, CSR emit, degree statistics, hub order), count the binned triangles
-(weighted when the workload has weights), and release the graph.  Inputs (coordinates, weights)
-are in HBM before the timed region starts.
+One step = the whole path on one synthetic workload: build the neighbour graph on the GPU (cell
+list, pair search, CSR emit, degree statistics, hub order, and for a tiled workload the hub
+windows and their tiles), count the binned triangles (weighted when the workload has weights),
+and release the graph.  Inputs (coordinates, weights) are in HBM before the timed region starts.
+
+The default workload is the BAO-scale one (4M uniform points, ~9e9 directed edges, 30 bins) in
+its hub-tiled mode: 4 GiB hub windows of the 18 GB CSR, the CSR held in pinned host memory and
+the windows streamed to the GPU per tile (GRAMSCI v2 §III.5.3).  The same line reports the
+resident and the re-emitted-window modes of the same workload, timed in the same process.
 
 Prints one JSON line: triplets/s for the whole step (value), hub-spoke merge-walks/s, the
-enumeration kernel's algorithmic-bytes roofline, and the CPU oracle timed on a bounded sample of
-the same workload on this host's cores.
+enumeration kernel's roofline (algorithmic bytes, and the HBM bytes of a stored counter run),
+and the CPU oracle timed on a bounded sample of the same workload on this host's cores.
 
-    python bench.py [--config C2] [--steps 5] [--warmup 1] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--config C3] [--steps 5] [--warmup 1] [--gpus 1] [--no-cpu-baseline]
 
 With --config C4 (the parity 4pCF workload) a step builds the graph and counts the binned
 tetrahedra with their even and odd channels instead; the line then reports tetrahedra/s and the
@@ -77,9 +82,9 @@ def measured_valu(key: str):
 
 
 def measured_traffic(key: str):
-    """HBM bytes per k_triplet launch from the committed rocprofv3 counter runs (FETCH_SIZE +
-    WRITE_SIZE, scaled by the copy calibration), or None when those runs predate the current
-    kernel source."""
+    """HBM bytes per k_triplet count (all tile launches of one count) from the committed
+    rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), keyed by
+    workload and mode, or None when those runs predate the current kernel's machine code."""
     try:
         fp = kernel_fingerprint()
         if fp is None:
@@ -98,6 +103,20 @@ def measured_traffic(key: str):
 # CPU-baseline sample per workload: (sub-box side as a fraction of the grid, hub stride)
 CPU_SAMPLE = {"C1": (1.0, 1), "C2": (1.0, 1), "C3": (1 / 3, 16), "C4": (1.0, 2), "C5": (1 / 3, 4)}
 
+# The mode each workload names: (hub-window budget in CSR bytes, where the CSR is kept).  The
+# BAO-scale and the large mixed workloads stream their CSR in hub windows; the others are resident.
+GIB = 1 << 30
+DEFAULT_MODE = {"C3": (4 * GIB, "host"), "C5": (2 * GIB, "host")}
+
+
+def traffic_key(key: str, tile_bytes: int, csr_mode: str) -> str:
+    """Key of a stored counter run: the workload, plus the mode when it is tiled
+    (e.g. C3-host-4GiB)."""
+    if tile_bytes <= 0:
+        return key
+    size = f"{tile_bytes // GIB}GiB" if tile_bytes % GIB == 0 else f"{tile_bytes}B"
+    return f"{key}-{csr_mode}-{size}"
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -108,11 +127,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", default="C2")
+    ap.add_argument("--config", default="C3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
-    ap.add_argument("--tile-bytes", type=int, default=0,
-                    help="hub-window budget in CSR bytes (0: one resident window)")
+    ap.add_argument("--tile-bytes", type=int, default=-1,
+                    help="hub-window budget in CSR bytes (0: one resident window; default: the "
+                         "workload's own mode, 4 GiB host-streamed windows for C3, 2 GiB for C5)")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="tiled workloads: skip timing the resident and re-emitted-window modes")
+    ap.add_argument("--mode-steps", type=int, default=3,
+                    help="timed steps of each compared mode (after one warm-up)")
     ap.add_argument("--host-csr", action="store_true",
                     help="out-of-core: keep the CSR in pinned host memory, stream windows "
                          "(same as --csr-mode host)")
@@ -143,6 +167,11 @@ def main():
     import workloads
 
     cfg = workloads.get(args.config)
+    if args.tile_bytes < 0:
+        if cfg.order == 3 and cfg.key in DEFAULT_MODE and not args.csr_mode and not args.host_csr:
+            args.tile_bytes, args.csr_mode = DEFAULT_MODE[cfg.key]
+        else:
+            args.tile_bytes = 0
     if cfg.order == 4:
         bench_4pcf(args, cfg)
         return
@@ -156,50 +185,85 @@ def main():
     w = None if w_np is None else torch.from_numpy(w_np).to(dev)
     torch.cuda.synchronize()
 
-    def step():
-        g = gtc.Graph(xyz, edges, tile_bytes=args.tile_bytes, csr_mode=csr_mode)
-        c, ws, st = g.count_3pcf(w)
-        gst = g.stats()
-        g.close()
-        return st, gst
+    def run(tile_bytes, mode, warmup, steps, tag):
+        def step():
+            g = gtc.Graph(xyz, edges, tile_bytes=tile_bytes, csr_mode=mode)
+            c, ws, st = g.count_3pcf(w)
+            gst = g.stats()
+            g.close()
+            return st, gst
 
-    for k in range(args.warmup):
-        st, gst = step()
-        log(f"[bench] warmup {k}: build {gst['build_ms']:.2f} ms, kernel {st['kernel_ms']:.2f} ms, "
-            f"T={st['triangles']}")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    kms, bms, tris, walks, qalg = [], [], [], [], []
-    for k in range(args.steps):
-        st, gst = step()
-        kms.append(st["kernel_ms"])
-        bms.append(gst["build_ms"])
-        tris.append(st["triangles"])
-        walks.append(st["merge_walks"])
-        qalg.append(st["q_alg_bytes"])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+        for k in range(warmup):
+            st, gst = step()
+            log(f"[bench] {tag} warmup {k}: build {gst['build_ms']:.2f} ms, kernel "
+                f"{st['kernel_ms']:.2f} ms, count {st['count_ms']:.2f} ms, T={st['triangles']}")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        rec = {"kernel_ms": [], "build_ms": [], "count_ms": [], "h2d_ms": [], "T": [], "q": []}
+        for k in range(steps):
+            st, gst = step()
+            rec["kernel_ms"].append(st["kernel_ms"])
+            rec["build_ms"].append(gst["build_ms"])
+            rec["count_ms"].append(st["count_ms"])
+            rec["h2d_ms"].append(st["h2d_ms"])
+            rec["T"].append(st["triangles"])
+            rec["q"].append(st["q_alg_bytes"])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        assert len(set(rec["T"])) == 1, "triangle counts differ between steps"
+        avg = {k: sum(v) / len(v) for k, v in rec.items() if k not in ("T", "q")}
+        log(f"[bench] {tag} {steps} steps: {1e3 * elapsed / steps:.2f} ms/step, build "
+            f"{avg['build_ms']:.2f} ms, kernel {avg['kernel_ms']:.3f} ms, count "
+            f"{avg['count_ms']:.2f} ms, T={rec['T'][0]}, E={st['edges']}, windows "
+            f"{st['windows']}, tiles {st['tiles']}, h2d {avg['h2d_ms']:.1f} ms")
+        return st, rec, avg, elapsed
+
+    tag = csr_mode if args.tile_bytes > 0 else "resident"
+    st, rec, avg, elapsed = run(args.tile_bytes, csr_mode, args.warmup, args.steps, tag)
     ms_step = 1e3 * elapsed / args.steps
-    assert len(set(tris)) == 1, "triangle counts differ between steps"
-    T = tris[0]
+    T = rec["T"][0]
     value = T * args.steps / elapsed
-    k_avg = sum(kms) / len(kms)
-    achieved = qalg[0] / (k_avg * 1e-3) / 1e9
-    log(f"[bench] {args.steps} steps: {ms_step:.2f} ms/step, build {sum(bms)/len(bms):.2f} ms, "
-        f"kernel {k_avg:.3f} ms, T={T}, E={st['edges']}, windows {st['windows']}, "
-        f"tiles {st['tiles']}, h2d {st['h2d_ms']:.1f} ms")
+    k_avg = avg["kernel_ms"]
+    achieved = rec["q"][0] / (k_avg * 1e-3) / 1e9
 
-    traffic = measured_traffic(cfg.key) if args.tile_bytes == 0 else None
+    modes = None
+    if args.tile_bytes > 0 and not args.no_modes:
+        modes = {tag: {"ms_per_step": ms_step, "build_ms": avg["build_ms"],
+                       "count_ms": avg["count_ms"], "kernel_ms": k_avg,
+                       "h2d_ms": avg["h2d_ms"], "windows": st["windows"], "tiles": st["tiles"]}}
+        others = [("resident", 0, "device")]
+        for m in ("rebuild", "host"):
+            if m != csr_mode:
+                others.append((m, args.tile_bytes, m))
+        for name, tb, m in others:
+            mst, mrec, mavg, mel = run(tb, m, 1, args.mode_steps, name)
+            assert mrec["T"][0] == T, f"{name} mode counts a different triangle total"
+            modes[name] = {"ms_per_step": 1e3 * mel / args.mode_steps,
+                           "build_ms": mavg["build_ms"], "count_ms": mavg["count_ms"],
+                           "kernel_ms": mavg["kernel_ms"], "h2d_ms": mavg["h2d_ms"],
+                           "windows": mst["windows"], "tiles": mst["tiles"]}
+        res = modes["resident"]["ms_per_step"]
+        for m in modes.values():
+            m["vs_resident"] = m["ms_per_step"] / res
+
+    tkey = traffic_key(cfg.key, args.tile_bytes, csr_mode)
+    traffic = measured_traffic(tkey)
     ach = achievable_hbm_gbs()
     log(f"[bench] device copy reaches {ach['copy']:.0f} GB/s, a 1 GiB sum reads {ach['read']:.0f} GB/s")
+    traffic_gbs = None if traffic is None else traffic / (k_avg * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                "traffic_gbs": None if traffic is None else traffic / (k_avg * 1e-3) / 1e9,
+                "traffic_gbs": traffic_gbs,
+                "frac_traffic": None if traffic_gbs is None else traffic_gbs / HBM_PEAK_GBS,
+                "traffic_from": None if traffic is None else
+                f"stored rocprofv3 counter run {os.path.relpath(TRAFFIC_FILE, ROOT)} "
+                f"[{tkey}], FETCH_SIZE + WRITE_SIZE scaled by a plain copy, k_triplet machine "
+                f"code {kernel_fingerprint()}; not measured in this run",
                 "achievable": ach["best"], "frac_achievable": achieved / ach["best"],
                 "achievable_from": {"copy_gbs": ach["copy"], "read_gbs": ach["read"],
                                     "kernels": "1 GiB device-to-device copy (read + written "
                                                "bytes); 1 GiB streaming read (gtc_hbm_read_rate)"},
-                "kernel": "k_triplet", "kernel_ms": k_avg, "q_alg_bytes": qalg[0],
+                "kernel": "k_triplet", "kernel_ms": k_avg, "q_alg_bytes": rec["q"][0],
                 "launch": {"waves_per_wg": st["launch_waves"], "workgroups": st["launch_blocks"],
                            "lds_bytes": st["launch_lds_bytes"]}}
 
@@ -228,11 +292,18 @@ def main():
         "config": {"workload": f"{cfg.key} {cfg.name}", "n_points": cfg.n, "kind": cfg.kind,
                    "r_max": cfg.r, "nbins": cfg.nbins, "weighted": cfg.weighted,
                    "mean_degree_target": cfg.target_degree, "edges": st["edges"],
-                   "triangles": T, "merge_walks": walks[0], "tile_bytes": args.tile_bytes,
+                   "triangles": T, "merge_walks": st["edges"],
+                   "merge_walks_enumerated": st["merge_walks"], "tile_bytes": args.tile_bytes,
                    "csr_mode": csr_mode, "windows": st["windows"], "tiles": st["tiles"]},
-        "merge_walks_per_s": walks[0] * args.steps / elapsed,
+        "merge_walks_per_s": st["edges"] * args.steps / elapsed,
+        "merge_walks_note": "one walk per forward edge (E+); merge_walks_enumerated leaves out "
+                            "the walks of hubs that cannot close a triangle (fewer than two "
+                            "forward neighbours, or spokes with no forward neighbours)",
         "kernel_triplets_per_s": T / (k_avg * 1e-3),
-        "build_ms": sum(bms) / len(bms),
+        "build_ms": avg["build_ms"],
+        "count_ms": avg["count_ms"],
+        "h2d_ms": avg["h2d_ms"],
+        "modes": modes,
         "roofline": roofline,
         "lds": lds,
         "cpu_baseline": cpu,

@@ -33,6 +33,23 @@ def test_bench_3pcf_line(gpu_available):
     rf = out["roofline"]
     assert rf["bound"] == "hbm" and rf["kernel"] == "k_triplet" and rf["peak"] == 8000.0
     assert 0 < rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
+    assert "frac_traffic" in rf
+    # one merge-walk per forward edge
+    assert out["config"]["merge_walks"] == out["config"]["edges"]
+    assert out["modes"] is None  # resident workload: no mode comparison
+
+
+@pytest.mark.gpu
+def test_bench_tiled_line_reports_every_mode(gpu_available):
+    # the tiled form of the line on a small workload: host-streamed windows, with the resident and
+    # re-emitted-window modes timed beside it and counting the same triangles
+    out = run_bench("--config", "C1", "--tile-bytes", "40000", "--csr-mode", "host", "--steps",
+                    "1", "--warmup", "1", "--mode-steps", "1", "--no-cpu-baseline")
+    cfg = out["config"]
+    assert cfg["csr_mode"] == "host" and cfg["windows"] > 1 and cfg["tiles"] >= cfg["windows"]
+    assert set(out["modes"]) == {"host", "resident", "rebuild"}
+    assert out["modes"]["resident"]["vs_resident"] == pytest.approx(1.0)
+    assert all(m["kernel_ms"] > 0 for m in out["modes"].values())
 
 
 @pytest.mark.gpu
