@@ -66,3 +66,29 @@ def clustered(seed, n, nclust, sigma, box_lo=0, box_hi=GRID):
 
 def uniform(seed, n, lo=0, hi=GRID):
     return rng_for(seed).integers(lo, hi, size=(n, 3)).astype(np.int32)
+
+
+def host_internal_order(xyz, edges, return_keys: bool = False):
+    """The internal labels the build's cell list defines, computed here on the host from that
+    definition: cubic cells of integer side cs = ceil(r_max) (at most ~2n cells and 512 per axis),
+    key (cz g + cy) g + cx, points ordered by key with ties in original order.  Returns
+    perm (internal -> original label)."""
+    n = xyz.shape[0]
+    r2 = int(edges[-1])
+    cs = int(np.ceil(np.sqrt(r2)))
+    while cs * cs < r2:
+        cs += 1
+    while cs > 1 and (cs - 1) ** 2 >= r2:
+        cs -= 1
+    g = -(-GRID // cs)
+    cap = 1
+    while (cap + 1) ** 3 <= 2 * max(n, 1) and cap < 512:
+        cap += 1
+    if g > cap:
+        g = cap
+        cs = -(-GRID // g)
+    c = xyz.astype(np.int64) // cs
+    key = (c[:, 2] * g + c[:, 1]) * g + c[:, 0]
+    perm = np.lexsort((np.arange(n), key)).astype(np.int32)
+    return (perm, key) if return_keys else perm
+
