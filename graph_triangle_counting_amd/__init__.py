@@ -108,6 +108,7 @@ def lib() -> C.CDLL:
         L.gtc_build_graph.argtypes = [P, i64, P, i32, C.POINTER(Options), P, C.POINTER(P)]
         L.gtc_count_3pcf.argtypes = [P, P, P, P, C.POINTER(Stats), P]
         L.gtc_count_3pcf_hubs.argtypes = [P, P, i64, P, P, P, C.POINTER(Stats), P]
+        L.gtc_count_3pcf_noalloc.argtypes = [P, P, P, P, P]
         L.gtc_count_4pcf_parity_s4.argtypes = [P, P, P, C.POINTER(Stats), P]
         L.gtc_num_configs_s4.argtypes = [i32]
         L.gtc_num_configs_s4.restype = i64
@@ -287,6 +288,28 @@ class Graph:
                                     _dptr(weighted) if weighted is not None else None,
                                     C.byref(st), _stream_ptr(self._stream)))
         return counts, weighted, st.as_dict()
+
+    def count_3pcf_noalloc(self, w=None, out=None, out_weighted=None):
+        """count_3pcf through gtc_count_3pcf_noalloc: no device allocation in the library (its
+        scratch is a static device array), no statistics.  The output tensors may be passed in
+        (out, out_weighted), so that the call allocates nothing at all.  Returns (counts,
+        weighted or None)."""
+        import torch
+        ncfg = num_configs(3, self.nbins)
+        dev = self._xyz.device
+        counts = out if out is not None else torch.empty(ncfg, dtype=torch.int64, device=dev)
+        weighted = None
+        if w is not None:
+            if not (w.is_cuda and w.dtype == torch.float64 and w.numel() == self.n):
+                raise TypeError("w must be a CUDA float64 tensor of length n")
+            w = w.contiguous()
+            weighted = out_weighted if out_weighted is not None else \
+                torch.empty(ncfg, dtype=torch.float64, device=dev)
+        _check(lib().gtc_count_3pcf_noalloc(self._h, _dptr(w) if w is not None else None,
+                                            _dptr(counts),
+                                            _dptr(weighted) if weighted is not None else None,
+                                            _stream_ptr(self._stream)))
+        return counts, weighted
 
     def count_2pcf(self, w=None):
         """Pairs per bin: (counts int64 [nbins] holding uint64 bits, weighted fp64 [nbins] or None,

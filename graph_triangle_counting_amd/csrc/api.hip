@@ -3,6 +3,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -12,7 +13,8 @@ namespace gtc {
 const char *last_error();
 int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s);
 int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
-                      gtc_stats *st, hipStream_t s, const HubSubset *sub = nullptr);
+                      gtc_stats *st, hipStream_t s, const HubSubset *sub = nullptr,
+                      const ExternalScratch *ext = nullptr);
 int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stats *st,
                       hipStream_t s, bool s4, const double *d_w = nullptr,
                       double *d_even_w = nullptr, double *d_odd_w = nullptr);
@@ -81,6 +83,35 @@ static void fill_graph_stats(const gtc_graph_s *G, gtc_stats *st) {
     st->build_ms = G->build_ms;
 }
 
+}  // namespace gtc
+
+// Scratch of the allocation-free count: one array per GPU, held until the process ends.  Host
+// code never uses the array's name as an address (in host code it names a host-side stand-in);
+// its device address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[GTC_NOALLOC_SCRATCH_BYTES];
+
+namespace gtc {
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static unsigned char *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (dev must be current).
+static int noalloc_scratch(int dev, unsigned char **out) {
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("device %d: the allocation-free count supports devices 0..%d", dev,
+                  kMaxDevices - 1);
+        return GTC_E_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)", __FILE__, __LINE__);
+        g_scratch_ptr[dev] = static_cast<unsigned char *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return GTC_OK;
+}
 }  // namespace gtc
 
 using namespace gtc;
@@ -243,6 +274,26 @@ int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d
         std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
     if (rc == GTC_OK && st) *st = local;
     return rc;
+}
+
+int gtc_count_3pcf_noalloc(gtc_graph g, const double *d_w, uint64_t *d_counts,
+                           double *d_weighted, void *hip_stream) {
+    if (!g || !d_counts || (d_w && !d_weighted)) {
+        set_error("gtc_count_3pcf_noalloc: need a graph, d_counts, and d_weighted when d_w is "
+                  "given");
+        return GTC_E_INVALID;
+    }
+    DeviceGuard dg(g->device);
+    if (dg.rc) return dg.rc;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GTC_E_HIP;
+    unsigned char *base = nullptr;
+    GTC_TRY(noalloc_scratch(dev, &base));
+    ExternalScratch ext;
+    ext.base = base;
+    ext.bytes = GTC_NOALLOC_SCRATCH_BYTES;
+    return count_3pcf_device(g, d_w, d_counts, d_weighted, nullptr,
+                             reinterpret_cast<hipStream_t>(hip_stream), nullptr, &ext);
 }
 
 int gtc_count_3pcf_hubs(gtc_graph g, const int32_t *h_hubs, int64_t n_hubs, const double *d_w,

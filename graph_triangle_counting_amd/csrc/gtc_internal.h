@@ -391,6 +391,14 @@ struct HubSubset {
     int64_t spoke_elements = 0;  // sum of work
 };
 
+// Device scratch a caller hands over (the allocation-free count): the count carves its arrays
+// from [base, base + bytes) instead of allocating, and runs without timing events or a final
+// synchronisation.
+struct ExternalScratch {
+    unsigned char *base = nullptr;
+    size_t bytes = 0;
+};
+
 // Keep the hubs of in[0..n_in) (device) that can close a triangle, into out (device, n_in
 // entries); d_sums: 3 device words of scratch.
 int filter_hubs(const gtc_graph_s *G, const int32_t *in, int64_t n_in, int32_t *out,

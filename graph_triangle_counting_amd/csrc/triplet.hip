@@ -652,11 +652,18 @@ static int weight_scale_for(double maxabs) {
 }
 
 int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
-                      gtc_stats *st, hipStream_t s, const HubSubset *sub) {
+                      gtc_stats *st, hipStream_t s, const HubSubset *sub,
+                      const ExternalScratch *ext) {
     // hubs to count: the graph's (per window), or a caller's subset (one-window graphs)
     const int32_t *hub_list = sub ? sub->hubs : G->hubs;
     const int64_t hub_total = sub ? sub->n_hubs : G->n_hubs;
-    const std::vector<int64_t> win_hubs = sub ? std::vector<int64_t>{0, sub->n_hubs} : G->win_hubs;
+    const int64_t sub_win[2] = {0, sub ? sub->n_hubs : 0};
+    const int64_t *win_hubs = sub ? sub_win : G->win_hubs.data();
+    if (ext && G->windowed()) {
+        set_error("the allocation-free count needs the CSR in device memory (csr_mode device)");
+        return GTC_E_UNSUPPORTED;
+    }
+    const bool timed = ext == nullptr;  // events and the closing readback (allocating counts only)
     const bool W = d_w != nullptr;
     const int nb = G->nb;
     const int64_t ncfg = gtc_num_configs(3, nb);
@@ -678,7 +685,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
 #define STEP(expr) do { rc = (expr); if (rc) { cleanup(); return rc; } } while (0)
 #define STEP_HIP(call) do { hipError_t e_ = (call); if (e_ != hipSuccess) { rc = hip_fail(e_, #call, __FILE__, __LINE__); cleanup(); return rc; } } while (0)
 
-    STEP(carve_alloc(&scratch, s, [&](Carver &c) {
+    auto layout = [&](Carver &c) {
         if (W) {
             c.take(&w_s, G->n);
             c.take(&limbs, 4 * ncfg);
@@ -692,7 +699,21 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
                 c.take(&wcol[b2], G->max_window_edges);
                 if (!G->packed) c.take(&wbin[b2], G->max_window_edges);
             }
-    }));
+    };
+    if (ext) {
+        Carver need;
+        layout(need);
+        if (need.off > ext->bytes) {
+            set_error("the count needs %zu bytes of device scratch; the static buffer holds %zu "
+                      "(weighted counts take 8 bytes per point)", need.off, ext->bytes);
+            return GTC_E_UNSUPPORTED;
+        }
+        Carver give;
+        give.base = ext->base;
+        layout(give);
+    } else {
+        STEP(carve_alloc(&scratch, s, layout));
+    }
     if (W) {
         double maxabs = 0.0;
         STEP(gather_weights(G, d_w, w_s, d_maxabs, d_bad, &maxabs, s));
@@ -911,10 +932,12 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             TripletPlan tp = pl;
             tp.blocks = (int)std::min<int64_t>(pl.blocks, (nh + pl.waves - 1) / pl.waves);
             a.batch_cap = batch_cap(nh, (int64_t)tp.blocks * tp.waves);
-            TSTEP(event_pair(kev));
-            TSTEP_HIP(hipEventRecord(kev[kev.size() - 2], s));
+            if (timed) {
+                TSTEP(event_pair(kev));
+                TSTEP_HIP(hipEventRecord(kev[kev.size() - 2], s));
+            }
             TSTEP(launch_triplet(kfn, a, tp, s));
-            TSTEP_HIP(hipEventRecord(kev.back(), s));
+            if (timed) TSTEP_HIP(hipEventRecord(kev.back(), s));
             ++tiles_run;
             if (ooc) {
                 TSTEP_HIP(hipEventRecord(slot_done[kh], s));
@@ -938,6 +961,10 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         TSTEP(finalize_limbs(limbs, ncfg, 1, 4 * ncfg,
                              reinterpret_cast<const unsigned long long *>(d_counts), scale,
                              d_weighted, s));
+    if (!timed) {  // caller scratch: asynchronous, no statistics
+        cleanup_tiles();
+        return GTC_OK;
+    }
     std::vector<unsigned long long> h_counts(ncfg);
     TSTEP_HIP(hipMemcpyAsync(h_counts.data(), d_counts, sizeof(uint64_t) * ncfg,
                              hipMemcpyDeviceToHost, s));

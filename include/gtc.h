@@ -57,6 +57,8 @@ typedef enum {
 #define GTC_MAX_BINS 255       /* 3pCF: nbins in [1, 255] */
 #define GTC_MAX_BINS_4PCF 16   /* parity 4pCF: nbins in [1, 16] */
 #define GTC_GRID_BITS 20       /* coordinates in [0, 2^20) */
+#define GTC_NOALLOC_SCRATCH_BYTES (32u << 20) /* static device scratch of gtc_count_3pcf_noalloc,
+                                                 per GPU */
 
 /* gtc_options.csr_mode */
 #define GTC_CSR_DEVICE 0
@@ -160,6 +162,25 @@ int gtc_build_graph(const int32_t *d_xyz, int64_t n, const int64_t *h_edges_sq, 
  *   st         may be NULL. */
 int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d_weighted,
                    gtc_stats *st, void *hip_stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): gtc_count_3pcf on a graph built beforehand, with every
+ * per-call device buffer (hub-queue counters; weighted: the weights in internal order, the exact
+ * sum limbs) carved from one static device array of GTC_NOALLOC_SCRATCH_BYTES on each GPU, which
+ * that GPU holds until the process ends.  No hipMalloc, hipFree or other allocation, no timing
+ * events; the call is asynchronous on hip_stream except that a weighted count synchronises once
+ * to read max |w| (the scale of the exact sums).  Results equal gtc_count_3pcf's bit for bit.
+ *   g, d_w, d_counts, d_weighted, hip_stream: as gtc_count_3pcf (no statistics).
+ * Errors: GTC_E_INVALID as gtc_count_3pcf; GTC_E_UNSUPPORTED for a graph whose CSR is out of
+ * core (GTC_CSR_HOST or GTC_CSR_REBUILD: its window buffers are per-call allocations; hub
+ * windows over a resident CSR are counted) or when the call's scratch exceeds the array
+ * (unweighted: a few KB; weighted: 8 bytes per point plus 32 per configuration, so about 4M
+ * points); GTC_E_HIP if the array's device address cannot be obtained.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on different
+ * streams or threads) race and give wrong results; calls ordered on one stream are safe.  The
+ * array keeps the last call's contents; each call clears what it needs zeroed. */
+int gtc_count_3pcf_noalloc(gtc_graph g, const double *d_w, uint64_t *d_counts,
+                           double *d_weighted, void *hip_stream);
 
 /* The 3pCF of a subset of hubs: the binned triangles whose first vertex in the graph's internal
  * order (gtc_graph_export's h_perm maps internal labels to point indices) is one of the listed
