@@ -530,7 +530,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-constexpr int kUnsortedMaxBins = 16;
+constexpr int kUnsortedMaxBins = 32;  // nb^3 32-bit bins: at most 128 KB of LDS
 
 struct DeviceLimits {
     int cus = 0;
