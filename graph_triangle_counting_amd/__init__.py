@@ -109,6 +109,8 @@ def lib() -> C.CDLL:
         L.gtc_count_3pcf.argtypes = [P, P, P, P, C.POINTER(Stats), P]
         L.gtc_count_3pcf_hubs.argtypes = [P, P, i64, P, P, P, C.POINTER(Stats), P]
         L.gtc_count_3pcf_noalloc.argtypes = [P, P, P, P, P]
+        L.gtc_release_host_cache.argtypes = []
+        L.gtc_release_host_cache.restype = None
         L.gtc_count_4pcf_parity_s4.argtypes = [P, P, P, C.POINTER(Stats), P]
         L.gtc_num_configs_s4.argtypes = [i32]
         L.gtc_num_configs_s4.restype = i64
@@ -408,6 +410,11 @@ class Graph:
 
 def build_graph(xyz, edges_sq, **kw) -> Graph:
     return Graph(xyz, edges_sq, **kw)
+
+
+def release_host_cache() -> None:
+    """Free the pinned host block kept for reuse by out-of-core builds."""
+    lib().gtc_release_host_cache()
 
 
 def linear_edges_sq(r_min: int, r_max: int, nbins: int) -> np.ndarray:

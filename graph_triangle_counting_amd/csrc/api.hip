@@ -32,6 +32,21 @@ static int64_t binom(int64_t n, int64_t k) {
 
 void free_graph_buffers(gtc_graph_s *G) {
     hipStream_t s = G->stream;
+    if (G->xfer) {  // transfers into the pinned CSR and window buffers have finished
+        (void)hipStreamSynchronize(G->xfer);
+        (void)hipStreamDestroy(G->xfer);
+        G->xfer = nullptr;
+    }
+    if (G->downloaded) (void)hipEventDestroy(G->downloaded);
+    if (G->staged) (void)hipEventDestroy(G->staged);
+    G->downloaded = G->staged = nullptr;
+    dev_free(G->slot_block, s);
+    G->slot_block = nullptr;
+    for (int k = 0; k < 3; ++k) {
+        G->slot_col[k] = nullptr;
+        G->slot_bin[k] = nullptr;
+        G->slot_win[k] = -1;
+    }
     dev_free(G->xyz_s, s);
     dev_free(G->arena_pts, s);
     dev_free(G->arena_csr, s);
@@ -275,6 +290,8 @@ int gtc_count_3pcf(gtc_graph g, const double *d_w, uint64_t *d_counts, double *d
     if (rc == GTC_OK && st) *st = local;
     return rc;
 }
+
+void gtc_release_host_cache(void) { release_pinned_cache(); }
 
 int gtc_count_3pcf_noalloc(gtc_graph g, const double *d_w, uint64_t *d_counts,
                            double *d_weighted, void *hip_stream) {
@@ -530,6 +547,7 @@ int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h
         w_dst = words.data();
     }
     if (g->host_csr) {  // out-of-core graph: the CSR is already in host memory
+        if (g->downloaded) GTC_HIP_CHECK(hipEventSynchronize(g->downloaded));
         if (w_dst && g->E) std::memcpy(w_dst, g->h_col, sizeof(int32_t) * g->E);
         if (!g->packed && h_bin && g->E) std::memcpy(h_bin, g->h_bin, g->E);
     } else if (g->rebuild) {  // no stored CSR: emit each window again and copy it out

@@ -623,23 +623,22 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     }
     const int64_t W = (int64_t)G->win.size() - 1;
     unsigned long long *win_last = nullptr;
-    // out-of-core staging: two buffers, so that one window's download to the pinned CSR (on a
-    // copy stream) overlaps the next window's emit
-    int32_t *st_col[2] = {nullptr, nullptr};
-    uint8_t *st_bin[2] = {nullptr, nullptr};
+    // out-of-core staging: the graph's three window buffers in turn, so that window downloads to
+    // the pinned CSR (on the graph's transfer stream) overlap the next windows' emits
+    constexpr int kStage = 3;
+    int32_t *st_col[kStage] = {};
+    uint8_t *st_bin[kStage] = {};
+    int64_t st_win[kStage] = {-1, -1, -1};  // window each staging buffer holds
     hipStream_t cs = nullptr;
-    hipEvent_t emitted[2] = {nullptr, nullptr}, copied[2] = {nullptr, nullptr};
-    bool copy_pending[2] = {false, false};
+    hipEvent_t emitted[kStage] = {}, copied[kStage] = {};
+    bool copy_pending[kStage] = {};
     const int64_t nkeys = W * kHubClasses;  // hub-list keys: window * classes + class
     int32_t *key_count = nullptr, *key_start = nullptr;
     int64_t *d_win = nullptr, *key_scan_ws = nullptr;
     void *scratch2 = nullptr;
     auto cleanup2 = [&]() {
-        if (cs) {
-            (void)hipStreamSynchronize(cs);
-            (void)hipStreamDestroy(cs);
-        }
-        for (int b = 0; b < 2; ++b) {
+        if (cs) (void)hipStreamSynchronize(cs);  // (the stream is the graph's)
+        for (int b = 0; b < kStage; ++b) {
             if (emitted[b]) (void)hipEventDestroy(emitted[b]);
             if (copied[b]) (void)hipEventDestroy(copied[b]);
         }
@@ -653,13 +652,19 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         c.take(&key_start, nkeys + 1);
         c.take(&d_win, W + 1);
         c.take(&key_scan_ws, scan_workspace_bytes(nkeys) / sizeof(int64_t));
-        if (G->windowed()) {  // staging of a window's rows (on their way to the pinned CSR)
-            for (int b = 0; b < 2; ++b) {
-                c.take(&st_col[b], G->max_window_edges);
-                if (!G->packed) c.take(&st_bin[b], G->max_window_edges);
-            }
-        }
     }));
+    if (G->windowed()) {  // the graph's window buffers, which stage the build's windows
+        STEP2(carve_alloc(&G->slot_block, s, [&](Carver &c) {
+            for (int b = 0; b < 3; ++b) {
+                c.take(&G->slot_col[b], G->max_window_edges);
+                if (!G->packed) c.take(&G->slot_bin[b], G->max_window_edges);
+            }
+        }));
+        for (int b = 0; b < kStage; ++b) {
+            st_col[b] = G->slot_col[b];
+            st_bin[b] = G->slot_bin[b];
+        }
+    }
     STEP2(fill_u64(reinterpret_cast<uint64_t *>(win_last), W, 0ull, s));
     if (G->host_csr) {
         // out-of-core: the CSR lives in pinned host memory; each window is emitted into a device
@@ -669,8 +674,9 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         if (!G->packed)
             STEP2(host_alloc_pinned(reinterpret_cast<void **>(&G->h_bin),
                                     std::max<int64_t>(G->E, 1)));
-        STEP2_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
-        for (int b = 0; b < 2; ++b) {
+        STEP2_HIP(hipStreamCreateWithFlags(&G->xfer, hipStreamNonBlocking));
+        cs = G->xfer;
+        for (int b = 0; b < kStage; ++b) {
             STEP2_HIP(hipEventCreateWithFlags(&emitted[b], hipEventDisableTiming));
             STEP2_HIP(hipEventCreateWithFlags(&copied[b], hipEventDisableTiming));
         }
@@ -686,7 +692,8 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         const int64_t lo = G->win[k], hi = G->win[k + 1];
         if (hi <= lo) continue;
         const int64_t e_lo = G->windowed() ? G->h_row_ptr[lo] : 0;
-        const int sb = (int)(k & 1);  // staging buffer of this window
+        const int sb = (int)(k % kStage);  // staging buffer of this window
+        st_win[sb] = k;
         if (G->host_csr && copy_pending[sb])  // its previous window has been downloaded
             STEP2_HIP(hipStreamWaitEvent(s, copied[sb], 0));
         pa.h_lo = (int32_t)lo;
@@ -773,7 +780,18 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
             return GTC_E_HIP;
         }
     }
-    if (cs) STEP2_HIP(hipStreamSynchronize(cs));  // the pinned CSR is complete
+    // The downloads into the pinned CSR may still run: readers wait for `downloaded`.  The last
+    // windows stay in the staging buffers for the first tiles of a count.
+    if (cs) {
+        STEP2_HIP(hipEventCreateWithFlags(&G->downloaded, hipEventDisableTiming));
+        STEP2_HIP(hipEventRecord(G->downloaded, cs));
+        cs = nullptr;
+    }
+    if (G->windowed()) {
+        STEP2_HIP(hipEventCreateWithFlags(&G->staged, hipEventDisableTiming));
+        STEP2_HIP(hipEventRecord(G->staged, s));
+        for (int b = 0; b < kStage; ++b) G->slot_win[b] = st_win[b];
+    }
     cleanup2();
 #undef STEP2
 #undef STEP2_HIP

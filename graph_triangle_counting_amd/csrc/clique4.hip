@@ -799,17 +799,6 @@ void config_realizable_s4(int nb, const int64_t *edges, uint8_t *mask) {
 int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, unsigned long long *d_m,
                    int32_t *d_bad, double *maxabs, hipStream_t s);
 
-// 2^s of the weighted 4pCF sums: s = 57 - e for M = fl(fl(fl(a*a)*a)*a) = f 2^e
-static int weight_scale4_for(double a) {
-    volatile double a2 = a * a;
-    volatile double a3 = a2 * a;
-    volatile double m = a3 * a;
-    if (m == 0.0) return 0;
-    int e = 0;
-    std::frexp((double)m, &e);
-    return 57 - e;
-}
-
 // Copies of the global class sums: a few hot configurations take most tetrahedra, and their
 // global atomics serialise; workgroup b adds to copy b % copies (a multiple of the 8 XCDs, so each
 // copy stays in the L2 of one XCD), within a 256 MiB budget.
@@ -975,7 +964,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     if (!rc && WT) {
         double maxabs = 0.0;
         rc = gather_weights(G, d_w, w_s, d_maxabs, d_bad, &maxabs, s);
-        scale = weight_scale4_for(maxabs);
+        if (!rc) rc = weight_scale(maxabs, 4, &scale);
         if (!rc) rc = fill_u64(reinterpret_cast<uint64_t *>(wsum), 6 * ncfg * copies, 0ull, s);
     }
     a.w_s = w_s;
@@ -1114,6 +1103,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         // pinned CSR or emitted again), evicting the least recently used window a tile does not
         // need; all on the counting stream, after the kernels that read the buffer.
         int64_t slot_win[kSlots] = {-1, -1, -1}, slot_used[kSlots] = {0, 0, 0}, clock = 0;
+        rc = wait_host_csr(G, s);  // uploads read the pinned CSR after the build's downloads
         auto ensure = [&](int64_t w, int64_t keep1, int64_t keep2, int *slot) -> int {
             for (int k = 0; k < kSlots; ++k)
                 if (slot_win[k] == w) {

@@ -53,6 +53,8 @@ void dev_free(void *p, hipStream_t s);
 // pinned host memory, through the same routines
 int host_alloc_pinned(void **p, size_t bytes);
 void host_free_pinned(void *p);
+// free the pinned block kept for reuse (runtime route), if any
+void release_pinned_cache();
 // The allocator of the API call running on this thread (null: the HIP runtime's).  Every entry
 // point that allocates opens a scope with the allocator its graph or options carry.
 const gtc_allocator *current_allocator();
@@ -104,6 +106,13 @@ int finalize_limbs(const unsigned long long *limbs, int64_t n, int copies, int64
 // A+, A-, A0 per copy; even[c] = 2^-s (A+ + A- + A0), odd[c] = 2^-s (A+ - A-), one rounding each.
 int finalize_class_sums(const unsigned long long *w, int64_t n, int copies, int64_t copy_stride,
                         int s, double *even, double *odd, hipStream_t st);
+
+// Scale exponent of the exact weighted sums of products of `factors` weights: s = 57 - e with
+// M = fl(...fl(fl(a*a)*a)...*a) (`factors` copies of a = max |w|) = f 2^e, f in [0.5, 1), so that
+// |p 2^s| < 2^57 for every product p (s = 0 when M == 0).  GTC_E_UNSUPPORTED when M overflows
+// (the products have no finite scale) or 2^s is beyond the largest double (max |w| so small that
+// the products' scale would exceed 2^1023); *scale is left 0 then.
+int weight_scale(double maxabs, int factors, int *scale);
 
 // hub windows: bounds[0..W] of consecutive rows whose CSR (entry_bytes per edge) fits tile_bytes
 int64_t plan_windows(const int64_t *row_ptr, int64_t n, int64_t tile_bytes, int64_t entry_bytes,
@@ -365,11 +374,30 @@ struct gtc_graph_s {
     bool has_alloc = false;
     int32_t *h_col = nullptr;
     uint8_t *h_bin = nullptr;
+    // Out-of-core transfers and window buffers.  The build downloads the windows of a pinned CSR
+    // on `xfer` and returns without waiting; `downloaded` follows the last download, and every
+    // reader of h_col / h_bin waits for it (wait_host_csr).  The three window buffers serve the
+    // build as staging and the 3pCF count as its tile windows; slot_win[k] is the window buffer k
+    // holds (-1: none), valid once `staged` (on the build stream) has completed, so a count
+    // starts with the windows the build left on the device.
+    hipStream_t xfer = nullptr;
+    hipEvent_t downloaded = nullptr;
+    hipEvent_t staged = nullptr;
+    void *slot_block = nullptr;
+    int32_t *slot_col[3] = {nullptr, nullptr, nullptr};
+    uint8_t *slot_bin[3] = {nullptr, nullptr, nullptr};
+    int64_t slot_win[3] = {-1, -1, -1};
 };
 
 namespace gtc {
 inline const gtc_allocator *graph_allocator(const gtc_graph_s *G) {
     return G->has_alloc ? &G->alloc : nullptr;
+}
+
+// Make stream s wait for the build's downloads into the pinned host CSR (no-op without one).
+inline int wait_host_csr(const gtc_graph_s *G, hipStream_t s) {
+    if (G->downloaded) GTC_HIP_CHECK(hipStreamWaitEvent(s, G->downloaded, 0));
+    return GTC_OK;
 }
 
 // Emit the CSR rows of hub window w (labels win[w]..win[w+1]) into col/bin (bin null for packed

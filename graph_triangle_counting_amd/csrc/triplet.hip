@@ -640,17 +640,6 @@ static void band_table(int64_t g, uint8_t out[145]) {
 int gather_weights(const gtc_graph_s *G, const double *d_w, double *w_s, unsigned long long *d_m,
                    int32_t *d_bad, double *maxabs, hipStream_t s);
 
-// Scale exponent of the exact weighted sums: s = 57 - e, with M = fl(fl(a*a)*a) = f 2^e,
-// f in [0.5, 1), for a = max |w|; then |p * 2^s| < 2^57 for every triangle product p.
-static int weight_scale_for(double maxabs) {
-    volatile double a2 = maxabs * maxabs;
-    volatile double m = a2 * maxabs;
-    if (m == 0.0) return 0;
-    int e = 0;
-    std::frexp((double)m, &e);
-    return 57 - e;
-}
-
 int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
                       gtc_stats *st, hipStream_t s, const HubSubset *sub,
                       const ExternalScratch *ext) {
@@ -670,7 +659,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     GTC_TRY(fill_u64(d_counts, ncfg, 0ull, s));
 
     // one block for the call's device scratch: internal-order weights, sum limbs, the hub class
-    // queue, and (out-of-core) the hub and search window buffers
+    // queue
     double *w_s = nullptr;
     unsigned long long *limbs = nullptr, *d_maxabs = nullptr;
     int32_t *d_bad = nullptr;
@@ -694,12 +683,12 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         }
         c.take(&queue, (size_t)kQueueWords);
         c.take(&qcount, kHubClasses);
-        if (G->windowed())
-            for (int b2 = 0; b2 < kSlots; ++b2) {
-                c.take(&wcol[b2], G->max_window_edges);
-                if (!G->packed) c.take(&wbin[b2], G->max_window_edges);
-            }
     };
+    // out-of-core windows live in the graph's three window buffers
+    for (int b2 = 0; b2 < kSlots; ++b2) {
+        wcol[b2] = G->slot_col[b2];
+        wbin[b2] = G->slot_bin[b2];
+    }
     if (ext) {
         Carver need;
         layout(need);
@@ -717,7 +706,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     if (W) {
         double maxabs = 0.0;
         STEP(gather_weights(G, d_w, w_s, d_maxabs, d_bad, &maxabs, s));
-        scale = weight_scale_for(maxabs);
+        STEP(weight_scale(maxabs, 3, &scale));
         STEP(fill_u64(reinterpret_cast<uint64_t *>(limbs), 4 * ncfg, 0ull, s));
     }
 
@@ -769,6 +758,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
 
     float kms = 0.f, h2d_ms = 0.f;
     TripletPlan used{};
+    int64_t slot_win_end[kSlots] = {-2, -2, -2};  // windows in the buffers after the tiles
     bool uh_used = false;
     int64_t tiles_run = 0;
     std::vector<hipEvent_t> kev, cev;  // kernel and copy event pairs
@@ -777,10 +767,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     hipStream_t cs = nullptr;
     hipEvent_t slot_ready[kSlots] = {}, slot_done[kSlots] = {};
     auto cleanup_tiles = [&]() {
-        if (cs) {
-            (void)hipStreamSynchronize(cs);
-            (void)hipStreamDestroy(cs);
-        }
+        if (cs) (void)hipStreamSynchronize(cs);  // (the graph's transfer stream)
         for (int k = 0; k < kSlots; ++k) {
             if (slot_ready[k]) (void)hipEventDestroy(slot_ready[k]);
             if (slot_done[k]) (void)hipEventDestroy(slot_done[k]);
@@ -847,13 +834,16 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         // or next tile needs (§III.5.3, double buffering).
         int64_t slot_win[kSlots], slot_used[kSlots];
         bool slot_read[kSlots] = {};
-        for (int k = 0; k < kSlots; ++k) slot_win[k] = slot_used[k] = -1;
-        // window stream: uploads overlap the counting on a stream of their own; re-emits run on
-        // the counting stream (a pair-search kernel beside the persistent enumeration kernel only
-        // takes compute units from it)
+        for (int k = 0; k < kSlots; ++k) {
+            slot_win[k] = ooc ? G->slot_win[k] : -1;  // windows left by the build or a count
+            slot_used[k] = -1;
+        }
+        // window stream: uploads overlap the counting on the graph's transfer stream, after the
+        // build's downloads into the pinned CSR; re-emits run on the counting stream (a
+        // pair-search kernel beside the persistent enumeration kernel only takes compute units)
         hipStream_t wst = s;
         if (G->host_csr) {
-            TSTEP_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+            cs = G->xfer;
             wst = cs;
         }
         if (ooc) {
@@ -861,6 +851,12 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
                 TSTEP_HIP(hipEventCreateWithFlags(&slot_ready[k], hipEventDisableTiming));
                 TSTEP_HIP(hipEventCreateWithFlags(&slot_done[k], hipEventDisableTiming));
             }
+            // the windows already in the buffers are ready once the build's emits are
+            if (G->staged) TSTEP_HIP(hipStreamWaitEvent(s, G->staged, 0));
+            for (int k = 0; k < kSlots; ++k)
+                if (slot_win[k] >= 0) TSTEP_HIP(hipEventRecord(slot_ready[k], s));
+            // the buffers' contents are undefined until this count completes
+            for (int k = 0; k < kSlots; ++k) G->slot_win[k] = -1;
         }
         // buffer holding window w, uploading it if needed; windows in keep[] are not evicted.
         // Returns -1 when every buffer holds a kept window.
@@ -900,8 +896,9 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             *slot = victim;
             return GTC_OK;
         };
+        // hub windows from the last down: the build leaves the last windows in the buffers
         std::vector<std::pair<int64_t, int64_t>> tiles;
-        for (int64_t h = 0; h < nw; ++h)
+        for (int64_t h = nw - 1; h >= 0; --h)
             if (win_hubs[h + 1] > win_hubs[h])
                 for (int64_t sw = h; sw <= G->win_smax[h]; ++sw) tiles.emplace_back(h, sw);
         for (size_t t = 0; t < tiles.size(); ++t) {
@@ -955,6 +952,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
                 }
             }
         }
+        if (ooc)
+            for (int k = 0; k < kSlots; ++k) slot_win_end[k] = slot_win[k];
     }
     // exact sums to doubles on the device, one rounding per configuration
     if (W)
@@ -970,6 +969,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
                              hipMemcpyDeviceToHost, s));
     TSTEP_HIP(hipStreamSynchronize(s));
     if (cs) TSTEP_HIP(hipStreamSynchronize(cs));
+    if (G->windowed() && slot_win_end[0] != -2)  // the windows the buffers now hold
+        for (int k = 0; k < kSlots; ++k) G->slot_win[k] = slot_win_end[k];
     for (size_t e = 0; e + 1 < kev.size(); e += 2) {
         float t = 0.f;
         TSTEP_HIP(hipEventElapsedTime(&t, kev[e], kev[e + 1]));

@@ -92,15 +92,6 @@ const void *pair_kernel(bool w, bool pk) {
               : reinterpret_cast<const void *>(&k_pair_hist<false, false>);
 }
 
-// 2^s for the pair products: s = 57 - e, M = fl(a * a) = f 2^e
-int pair_scale_for(double maxabs) {
-    volatile double m = maxabs * maxabs;
-    if (m == 0.0) return 0;
-    int e = 0;
-    std::frexp((double)m, &e);
-    return 57 - e;
-}
-
 }  // namespace
 
 int count_2pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, double *d_weighted,
@@ -139,7 +130,8 @@ int count_2pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         double maxabs = 0.0;
         rc = gather_weights(G, d_w, w_s, d_maxabs, d_bad, &maxabs, s);
         if (rc) return finish(rc);
-        scale = pair_scale_for(maxabs);
+        rc = weight_scale(maxabs, 2, &scale);
+        if (rc) return finish(rc);
         rc = fill_u64(reinterpret_cast<uint64_t *>(limbs), 4 * (int64_t)nb, 0ull, s);
         if (rc) return finish(rc);
     }
@@ -160,6 +152,8 @@ int count_2pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         return finish(hip_fail(hipGetLastError(), "hipEventCreate", __FILE__, __LINE__));
     float kms = 0.f;
     const int64_t nw = (int64_t)G->win.size() - 1;
+    rc = wait_host_csr(G, s);  // uploads read the pinned CSR after the build's downloads
+    if (rc) return finish(rc);
     for (int64_t w = 0; w < nw; ++w) {  // the whole graph is one window unless it is tiled
         const int64_t lo = G->win[w], hi = G->win[w + 1];
         if (hi <= lo) continue;

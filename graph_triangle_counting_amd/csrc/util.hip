@@ -1,6 +1,10 @@
 // util.hip - error reporting, stream-ordered device memory, fills and exclusive scans.
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
+#include <unordered_map>
+
+#include <cmath>
 
 #include "gtc_internal.h"
 
@@ -55,6 +59,14 @@ void dev_free(void *p, hipStream_t s) {
     else (void)hipFreeAsync(p, s);
 }
 
+// Pinned blocks of the runtime route: the block sizes of live allocations, and one freed block kept
+// for the next allocation it fits (between the request and twice it).  Pinning many gigabytes
+// costs about 10 ms per GB, which repeated out-of-core builds of like sizes then pay once.
+static std::mutex g_pin_mu;
+static std::unordered_map<void *, size_t> g_pin_size;
+static void *g_pin_cached = nullptr;
+static size_t g_pin_cached_bytes = 0;
+
 int host_alloc_pinned(void **p, size_t bytes) {
     *p = nullptr;
     const gtc_allocator *A = t_allocator;
@@ -66,20 +78,62 @@ int host_alloc_pinned(void **p, size_t bytes) {
         }
         return GTC_OK;
     }
+    bytes = bytes ? bytes : 1;
+    {
+        std::lock_guard<std::mutex> lock(g_pin_mu);
+        if (g_pin_cached && g_pin_cached_bytes >= bytes && g_pin_cached_bytes / 2 <= bytes) {
+            *p = g_pin_cached;
+            g_pin_cached = nullptr;
+            g_pin_cached_bytes = 0;
+            return GTC_OK;
+        }
+    }
     hipError_t e = hipHostMalloc(p, bytes, hipHostMallocDefault);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         set_error("pinned host allocation of %zu bytes failed: %s", bytes, hipGetErrorString(e));
         return GTC_E_OOM;
     }
+    std::lock_guard<std::mutex> lock(g_pin_mu);
+    g_pin_size[*p] = bytes;
     return GTC_OK;
+}
+
+void release_pinned_cache() {
+    void *p = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_pin_mu);
+        p = g_pin_cached;
+        if (p) g_pin_size.erase(p);
+        g_pin_cached = nullptr;
+        g_pin_cached_bytes = 0;
+    }
+    if (p) (void)hipHostFree(p);
 }
 
 void host_free_pinned(void *p) {
     if (!p) return;
     const gtc_allocator *A = t_allocator;
-    if (A && A->host_free) A->host_free(p, A->ctx);
-    else (void)hipHostFree(p);
+    if (A && A->host_free) {
+        A->host_free(p, A->ctx);
+        return;
+    }
+    // keep the larger of this block and the cached one; free the other
+    void *drop = p;
+    {
+        std::lock_guard<std::mutex> lock(g_pin_mu);
+        auto it = g_pin_size.find(p);
+        const size_t bytes = it != g_pin_size.end() ? it->second : 0;
+        if (bytes > g_pin_cached_bytes) {
+            drop = g_pin_cached;
+            if (drop) g_pin_size.erase(drop);
+            g_pin_cached = p;
+            g_pin_cached_bytes = bytes;
+        } else if (it != g_pin_size.end()) {
+            g_pin_size.erase(it);
+        }
+    }
+    if (drop) (void)hipHostFree(drop);
 }
 
 // ------------------------------------------------------------------ fills (kernels, not memset:
@@ -102,6 +156,28 @@ static int fill(T *p, int64_t n, T v, hipStream_t s) {
 }
 
 int fill_u64(uint64_t *p, int64_t n, uint64_t v, hipStream_t s) { return fill<uint64_t>(p, n, v, s); }
+
+int weight_scale(double maxabs, int factors, int *scale) {
+    *scale = 0;
+    volatile double m = maxabs;  // separately rounded products, in order
+    for (int k = 1; k < factors; ++k) m = m * maxabs;
+    const double mv = m;
+    if (!std::isfinite(mv)) {
+        set_error("weights too large: the product of %d copies of max |w| = %g overflows", factors,
+                  maxabs);
+        return GTC_E_UNSUPPORTED;
+    }
+    if (mv == 0.0) return GTC_OK;
+    int e = 0;
+    std::frexp(mv, &e);
+    if (57 - e > 1023) {
+        set_error("weights too small: max |w| = %g puts the exact sums' scale at 2^%d, beyond the "
+                  "largest double", maxabs, 57 - e);
+        return GTC_E_UNSUPPORTED;
+    }
+    *scale = 57 - e;
+    return GTC_OK;
+}
 int fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s) { return fill<uint32_t>(p, n, v, s); }
 
 // ------------------------------------------------------------------ exact fixed-point sums

@@ -103,7 +103,10 @@ typedef struct {
      *   GTC_CSR_REBUILD (2): nowhere; a tile's windows are emitted again on the device from the
      *                        sorted coordinates (a window's pair search costs less than its copy
      *                        over the host link).  Needs the coordinates (not dropped).
-     * Modes 1 and 2 need tile_bytes > 0, and hold only a few windows on the device. */
+     * Modes 1 and 2 need tile_bytes > 0.  The graph then holds three window buffers on the
+     * device for its lifetime: the build stages its windows through them, and a 3pCF count
+     * starts with the windows they hold.  In mode 1 the build returns while its last windows are
+     * still being copied to host memory; every reader of the host CSR waits for those copies. */
     int32_t csr_mode;
     /* nonzero: drop the sorted coordinates after the build (gtc_count_4pcf_parity then fails
      * with GTC_E_INVALID).  Zero keeps them. */
@@ -140,6 +143,12 @@ typedef struct {
     double h2d_ms;             /* out-of-core: window copies (GTC_CSR_HOST) or window emits
                                   (GTC_CSR_REBUILD), summed; they overlap the counting */
 } gtc_stats;
+
+/* Free the pinned host block the library keeps for reuse.  Out-of-core builds with the CSR in
+ * pinned host memory (GTC_CSR_HOST, no caller allocator) keep the largest freed pinned block and
+ * give it to the next build whose CSR fits it (between the request and twice it), since pinning
+ * costs about 10 ms per GB.  Call this to return that memory; graphs alive keep theirs. */
+void gtc_release_host_cache(void);
 
 /* Build the neighbour graph of n points (§II.1, Eq.(1)).
  *   d_xyz     device int32 [n][3], coordinates in [0, 2^20) (checked on the device:

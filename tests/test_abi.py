@@ -68,6 +68,47 @@ def test_s4_configuration_tables_match_the_oracle():
     assert int(gtc.config_realizable_s4(4, cases[0][1]).sum()) == 178
 
 
+def _tetrahedron_by_construction(d):
+    """Place a tetrahedron with edge lengths d[(u, v)] by trilateration: v0 at the origin, v1 on
+    the x axis, v2 in the xy plane, v3 above it.  Returns z^2 of v3 (the squared height over the
+    face v0 v1 v2, times nothing), or None when a face is no proper triangle."""
+    for a, b, c in ((0, 1, 2), (0, 1, 3), (0, 2, 3), (1, 2, 3)):
+        x, y, z = d[(a, b)], d[(a, c)], d[(b, c)]
+        if not (x < y + z and y < x + z and z < x + y):
+            return None
+    p1 = d[(0, 1)]
+    x2 = (d[(0, 2)] ** 2 - d[(1, 2)] ** 2 + p1 ** 2) / (2 * p1)
+    y2 = np.sqrt(d[(0, 2)] ** 2 - x2 ** 2)
+    x3 = (d[(0, 3)] ** 2 - d[(1, 3)] ** 2 + p1 ** 2) / (2 * p1)
+    y3 = (d[(0, 3)] ** 2 - d[(2, 3)] ** 2 + x2 ** 2 + y2 ** 2 - 2 * x2 * x3) / (2 * y2)
+    return d[(0, 3)] ** 2 - x3 ** 2 - y3 ** 2
+
+
+@pytest.mark.parametrize("nb,rmax", [(2, 12_000), (3, 20_000), (3, 700)])
+def test_realizable_mask_by_construction(nb, rmax):
+    # an independent check of the library's realizability mask at 2 and 3 bins: the bin-centre
+    # edge lengths of each configuration (midpoint in r of each bin) are realised by placing the
+    # four vertices one by one; a configuration is realizable when every face is a proper
+    # triangle and the last vertex lies off the plane of the first three
+    from workloads import linear_edges_sq
+    edges = linear_edges_sq(rmax, nb)
+    r = np.sqrt(edges.astype(np.float64))
+    centre = (r[:-1] + r[1:]) / 2
+    bins = gtc.config_bins_s4(nb)
+    mask = gtc.config_realizable_s4(nb, edges)
+    order = [(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)]
+    n_real = 0
+    for t, m in zip(bins, mask):
+        d = {e: centre[b] for e, b in zip(order, t)}
+        z2 = _tetrahedron_by_construction(d)
+        want = z2 is not None and z2 > 0
+        if z2 is not None:
+            assert abs(z2) > 1e-9 * centre.max() ** 2, "near-degenerate case: pick other edges"
+        assert bool(m) == want, (t, z2)
+        n_real += want
+    assert 0 < n_real < len(bins)
+
+
 def test_disconnected_and_connected_4pcf_match_the_oracle():
     import oracle
     rng = np.random.default_rng(7)

@@ -490,3 +490,42 @@ def test_4pcf_requires_coords(gpu_available):
     with pytest.raises(gtc.GtcError):
         g.count_4pcf_parity()
     g.close()
+
+
+@pytest.mark.parametrize("order,tiny,huge", [(3, 2.0 ** -340, 1e150), (4, 2.0 ** -255, 1e100),
+                                             (2, 2.0 ** -510, 1e200)])
+def test_weights_beyond_the_exact_scale_are_refused(gpu_available, order, tiny, huge):
+    # the exact sums scale every product by 2^s, s = 57 - e for max|w|^order = f 2^e: a max|w| so
+    # small that 2^s passes the largest double, or so large that max|w|^order overflows, is
+    # refused instead of summed into garbage
+    import torch
+    xyz = clustered(33, 4_000, 20, 3000)
+    edges = linear_edges_sq(9_000, 4)
+    g = gtc.Graph(to_gpu(xyz), edges)
+
+    def run(a):
+        w = torch.full((xyz.shape[0],), a, dtype=torch.float64, device="cuda")
+        if order == 3:
+            return g.count_3pcf(w)[1]
+        if order == 4:
+            return g.count_4pcf_weighted(w)[2]
+        return g.count_2pcf(w)[1]
+
+    for a in (tiny, -tiny, huge):
+        with pytest.raises(gtc.GtcError) as ei:
+            run(a)
+        assert ei.value.status == gtc.GTC_E_UNSUPPORTED
+    g.close()
+
+
+def test_small_weights_within_the_exact_scale(gpu_available):
+    # max|w| = 2^-300: the 3pCF scale is 2^956, still a double; the sums equal the oracle's
+    xyz = clustered(34, 4_000, 20, 3000)
+    edges = linear_edges_sq(9_000, 4)
+    w = 2.0 ** -300 * (0.5 + rng_for(35).random(xyz.shape[0]))
+    c, ws, st = hip_3pcf(xyz, edges, w)
+    oc, ows, s, _ = oracle.Graph(xyz, edges).count_3pcf(w)
+    assert st["weight_scale"] == s and 900 < s <= 1023
+    np.testing.assert_array_equal(c, oc)
+    np.testing.assert_array_equal(ws, ows)
+    assert ws.max() > 0

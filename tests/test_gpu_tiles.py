@@ -50,7 +50,7 @@ def test_tiled_equals_resident_and_oracle(gpu_available, monkeypatch, kind, seed
         if weighted:
             np.testing.assert_array_equal(ws, w0)
             np.testing.assert_array_equal(ws, ow)
-        if csr_mode != "device":
+        if csr_mode != "device" and st["windows"] > 3:  # (the build leaves three on the device)
             assert st["h2d_ms"] > 0
 
 
@@ -207,3 +207,33 @@ def test_hbm_read_probe(gpu_available):
     buf = torch.ones(1 << 26, dtype=torch.int32, device="cuda")  # 256 MiB
     rate = gtc.hbm_read_rate(buf, reps=3)
     assert 2000 < rate < 8500, rate
+
+
+@pytest.mark.parametrize("csr_mode", ["host", "rebuild"])
+def test_out_of_core_graph_serves_repeated_calls(gpu_available, csr_mode):
+    # one out-of-core graph, used again and again: 3pCF counts (the first starts with the windows
+    # the build left on the device, later ones with those the previous count left), a weighted
+    # count, the 2pCF, the 4pCF and an export in between, all equal to the resident graph's
+    import torch
+    xyz = clustered(47, 20_000, 50, 2500)
+    edges = linear_edges_sq(9_000, 6)
+    w = torch.from_numpy(0.5 + rng_for(48).random(xyz.shape[0])).cuda()
+    ref = gtc.Graph(to_gpu(xyz), edges)
+    c0 = ref.count_3pcf()[0].cpu().numpy()
+    c0w = ref.count_3pcf(w)[1].cpu().numpy()
+    p0 = ref.count_2pcf()[0].cpu().numpy()
+    e0 = ref.count_4pcf_parity()[0].cpu().numpy()
+    x0 = edge_set_from_gpu(ref)
+    tb = 4 * ref.stats()["edges"] // 6
+    ref.close()
+    g = gtc.Graph(to_gpu(xyz), edges, tile_bytes=tb, csr_mode=csr_mode)
+    assert g.stats()["windows"] > 2
+    for rep in range(2):
+        say("ooc repeat", csr_mode, rep)
+        np.testing.assert_array_equal(g.count_3pcf()[0].cpu().numpy(), c0)
+        np.testing.assert_array_equal(g.count_3pcf(w)[1].cpu().numpy(), c0w)
+        np.testing.assert_array_equal(g.count_2pcf()[0].cpu().numpy(), p0)
+        np.testing.assert_array_equal(g.count_4pcf_parity()[0].cpu().numpy(), e0)
+        np.testing.assert_array_equal(edge_set_from_gpu(g), x0)
+    g.close()
+    gtc.release_host_cache()
