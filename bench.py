@@ -81,10 +81,11 @@ def measured_valu(key: str):
     return None
 
 
-def measured_traffic(key: str):
+def measured_traffic(key: str, launch_mode: int):
     """HBM bytes per k_triplet count (all tile launches of one count) from the committed
     rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), keyed by
-    workload and mode, or None when those runs predate the current kernel's machine code."""
+    workload and mode, or None when those runs predate the current kernel's machine code or were
+    taken with another kernel variant (launch mode bits 0-1)."""
     try:
         fp = kernel_fingerprint()
         if fp is None:
@@ -93,8 +94,8 @@ def measured_traffic(key: str):
             for line in fh:
                 if line.startswith("#") or not line.strip():
                     continue
-                k, f, b = line.split()
-                if k == key and f == fp:
+                k, f, mode, b = line.split()
+                if k == key and f == fp and int(mode) == (launch_mode & 3):
                     return float(b)
     except OSError:
         pass
@@ -247,7 +248,7 @@ def main():
             m["vs_resident"] = m["ms_per_step"] / res
 
     tkey = traffic_key(cfg.key, args.tile_bytes, csr_mode)
-    traffic = measured_traffic(tkey)
+    traffic = measured_traffic(tkey, st["launch_mode"])
     ach = achievable_hbm_gbs()
     log(f"[bench] device copy reaches {ach['copy']:.0f} GB/s, a 1 GiB sum reads {ach['read']:.0f} GB/s")
     traffic_gbs = None if traffic is None else traffic / (k_avg * 1e-3) / 1e9
@@ -258,7 +259,8 @@ def main():
                 "traffic_from": None if traffic is None else
                 f"stored rocprofv3 counter run {os.path.relpath(TRAFFIC_FILE, ROOT)} "
                 f"[{tkey}], FETCH_SIZE + WRITE_SIZE scaled by a plain copy, k_triplet machine "
-                f"code {kernel_fingerprint()}; not measured in this run",
+                f"code {kernel_fingerprint()}, launch mode {st['launch_mode'] & 3}; not measured "
+                f"in this run",
                 "achievable": ach["best"], "frac_achievable": achieved / ach["best"],
                 "achievable_from": {"copy_gbs": ach["copy"], "read_gbs": ach["read"],
                                     "kernels": "1 GiB device-to-device copy (read + written "
