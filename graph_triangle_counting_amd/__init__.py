@@ -135,6 +135,8 @@ def lib() -> C.CDLL:
         L.gtc_graph_stats.argtypes = [P, C.POINTER(Stats)]
         L.gtc_plan_windows.argtypes = [P, i64, i64, i32, P]
         L.gtc_plan_windows.restype = i64
+        L.gtc_graph_windows.argtypes = [P, P, P, i64]
+        L.gtc_graph_windows.restype = i64
         L.gtc_graph_free.argtypes = [P]
         L.gtc_graph_free.restype = None
         L.gtc_status_string.argtypes = [C.c_int]
@@ -394,6 +396,16 @@ class Graph:
                                              _dptr(odd), _dptr(ew), _dptr(ow), C.byref(st),
                                              _stream_ptr(self._stream)))
         return even, odd, ew, ow, st.as_dict()
+
+    def windows(self):
+        """Hub windows: (label bounds int64 [W+1], their CSR offsets int64 [W+1]) on the host."""
+        W = lib().gtc_graph_windows(self._h, None, None, 0)
+        _check(int(W) if W < 0 else 0)
+        bounds = np.empty(W + 1, np.int64)
+        offsets = np.empty(W + 1, np.int64)
+        p = lambda a: a.ctypes.data_as(C.c_void_p)
+        _check(min(0, int(lib().gtc_graph_windows(self._h, p(bounds), p(offsets), W + 1))))
+        return bounds, offsets
 
     def export(self):
         """Forward CSR in internal labels plus the internal -> original permutation (host)."""

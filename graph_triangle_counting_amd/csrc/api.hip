@@ -561,8 +561,8 @@ int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h
             }));
             int rc = GTC_OK;
             for (int64_t w = 0; w + 1 < (int64_t)g->win.size() && rc == GTC_OK; ++w) {
-                const int64_t e0 = g->h_row_ptr[g->win[w]];
-                const int64_t ne = g->h_row_ptr[g->win[w + 1]] - e0;
+                const int64_t e0 = g->win_e[w];
+                const int64_t ne = g->win_e[w + 1] - e0;
                 if (ne <= 0) continue;
                 rc = emit_window(g, w, wc, wb, s);
                 hipError_t e = hipSuccess;
@@ -626,6 +626,25 @@ int64_t gtc_plan_windows(const int64_t *h_row_ptr, int64_t n, int64_t tile_bytes
             return GTC_E_INVALID;
         }
     return plan_windows(h_row_ptr, n, tile_bytes, entry_bytes, h_bounds);
+}
+
+int64_t gtc_graph_windows(gtc_graph g, int64_t *h_bounds, int64_t *h_offsets, int64_t capacity) {
+    if (!g) {
+        set_error("gtc_graph_windows: null graph");
+        return GTC_E_INVALID;
+    }
+    const int64_t W = (int64_t)g->win.size() - 1;
+    if (capacity < 0 || (capacity > 0 && !h_bounds && !h_offsets)) {
+        set_error("gtc_graph_windows: need capacity >= 0 and an output array when it is > 0");
+        return GTC_E_INVALID;
+    }
+    if (capacity >= W + 1) {
+        for (int64_t k = 0; k <= W; ++k) {
+            if (h_bounds) h_bounds[k] = g->win[k];
+            if (h_offsets) h_offsets[k] = g->win_e[k];
+        }
+    }
+    return W;
 }
 
 const char *gtc_status_string(int status) {

@@ -421,6 +421,44 @@ int hub_class_counts(const int32_t *hubs, int64_t n_hubs, const int64_t *row_ptr
 
 // ------------------------------------------------------------------ host orchestration
 
+// Hub windows (§III.5.3) on the device, the same greedy plan as plan_windows on the host: each
+// window runs from the previous bound a to the largest b with row_ptr[b] - row_ptr[a] <= cap (at
+// least one row).  One wave searches each bound 64-ary: the 64 probes that hold form a prefix
+// (row_ptr is nondecreasing), so their count narrows the range by 64 per round.  Writes the bounds
+// and their CSR offsets, bounds[0..W] and bound_e[0..W] (room for max_w + 1 of each), and W to
+// *count, or -1 if W would exceed max_w.
+__global__ void __launch_bounds__(kWave)
+    k_plan_windows(const int64_t *__restrict__ row_ptr, int64_t n, int64_t cap, int64_t max_w,
+                   int64_t *__restrict__ bounds, int64_t *__restrict__ bound_e,
+                   int64_t *__restrict__ count) {
+    const int lane = threadIdx.x;
+    int64_t a = 0, W = 0;
+    if (lane == 0) {
+        bounds[0] = 0;
+        bound_e[0] = row_ptr[0];
+    }
+    while (a < n) {
+        const int64_t limit = row_ptr[a] + cap;
+        // the bound lies in [lo, hi]: the largest b there with row_ptr[b] <= limit, else lo
+        int64_t lo = a + 1, hi = n;
+        while (lo < hi) {
+            const int64_t step = (hi - lo + kWave - 1) / kWave;
+            const int64_t p = lo + (int64_t)(lane + 1) * step;
+            const bool ok = p <= hi && row_ptr[p] <= limit;
+            const int k = __popcll(__ballot(ok));
+            hi = std::min(hi, lo + (int64_t)(k + 1) * step - 1);
+            lo += (int64_t)k * step;
+        }
+        a = lo;
+        if (++W > max_w) break;
+        if (lane == 0) {
+            bounds[W] = a;
+            bound_e[W] = row_ptr[a];
+        }
+    }
+    if (lane == 0) *count = W > max_w ? -1 : W;
+}
+
 static Grid choose_grid(int64_t n, int64_t r2) {
     // integer cell side cs = ceil(sqrt(r2)), so two neighbours are at most one cell apart per axis
     int64_t cs = (int64_t)std::sqrt((double)r2);
@@ -606,31 +644,63 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     }
     // hub windows: one window unless a tile budget is set (§III.5.3)
     G->win.assign({0, n});
+    G->win_e.assign({0, G->E});
     G->max_window_edges = G->E;
     if (G->tile_bytes > 0 && n > 0) {
-        G->h_row_ptr.resize(n + 1);
-        STEP_HIP(hipMemcpyAsync(G->h_row_ptr.data(), G->row_ptr, sizeof(int64_t) * (n + 1),
-                                hipMemcpyDeviceToHost, s));
-        STEP_HIP(hipStreamSynchronize(s));
-        std::vector<int64_t> bounds(n + 2);
-        const int64_t Wn = plan_windows(G->h_row_ptr.data(), n, G->tile_bytes, G->packed ? 4 : 5,
-                                        bounds.data());
-        G->win.assign(bounds.begin(), bounds.begin() + Wn + 1);
+        // Greedy windows, planned on the device: only the bounds travel to the host.  Two
+        // consecutive windows hold more than cap entries together (the second's first row did not
+        // fit the first), so W <= 2E / (cap + 1) + 1, and W <= n.
+        const int64_t cap = G->tile_bytes / (G->packed ? 4 : 5);
+        const int64_t max_w = std::min<int64_t>(n, 2 * (G->E / (cap + 1)) + 3);
+        int64_t *d_bounds = nullptr, *d_bound_e = nullptr, *d_count = nullptr;
+        void *plan_ws = nullptr;
+        STEP(carve_alloc(&plan_ws, s, [&](Carver &c) {
+            c.take(&d_bounds, max_w + 1);
+            c.take(&d_bound_e, max_w + 1);
+            c.take(&d_count, 1);
+        }));
+        hipLaunchKernelGGL(k_plan_windows, dim3(1), dim3(kWave), 0, s, G->row_ptr, n, cap, max_w,
+                           d_bounds, d_bound_e, d_count);
+        int64_t Wn = 0;
+        hipError_t e = hipGetLastError();
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(&Wn, d_count, sizeof(int64_t), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e == hipSuccess && Wn > 0) {
+            G->win.resize(Wn + 1);
+            G->win_e.resize(Wn + 1);
+            e = hipMemcpyAsync(G->win.data(), d_bounds, sizeof(int64_t) * (Wn + 1),
+                               hipMemcpyDeviceToHost, s);
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(G->win_e.data(), d_bound_e, sizeof(int64_t) * (Wn + 1),
+                                   hipMemcpyDeviceToHost, s);
+            if (e == hipSuccess) e = hipStreamSynchronize(s);
+        }
+        dev_free(plan_ws, s);
+        if (e != hipSuccess) STEP(hip_fail(e, "window plan", __FILE__, __LINE__));
+        if (Wn <= 0) {
+            set_error("window plan: more than %lld windows", (long long)max_w);
+            cleanup();
+            return GTC_E_HIP;
+        }
         G->max_window_edges = 0;
         for (int64_t k = 0; k < Wn; ++k)
-            G->max_window_edges = std::max(G->max_window_edges,
-                                           G->h_row_ptr[G->win[k + 1]] - G->h_row_ptr[G->win[k]]);
+            G->max_window_edges = std::max(G->max_window_edges, G->win_e[k + 1] - G->win_e[k]);
     }
     const int64_t W = (int64_t)G->win.size() - 1;
     unsigned long long *win_last = nullptr;
-    // out-of-core staging: the graph's three window buffers in turn, so that window downloads to
-    // the pinned CSR (on the graph's transfer stream) overlap the next windows' emits
-    constexpr int kStage = 3;
+    // Out-of-core staging: the graph's three window buffers, which end up holding the last three
+    // windows, and with a pinned CSR a fourth buffer for the build alone, so that window
+    // downloads (on the graph's transfer stream) overlap the next windows' emits.  A buffer is
+    // emitted into again once its download has completed.
+    constexpr int kStage = 4;
     int32_t *st_col[kStage] = {};
     uint8_t *st_bin[kStage] = {};
-    int64_t st_win[kStage] = {-1, -1, -1};  // window each staging buffer holds
+    int64_t st_win[kStage] = {-1, -1, -1, -1};  // window each staging buffer holds
+    int64_t st_seq[kStage] = {-1, -1, -1, -1};  // order of its last download (-1: none)
+    void *extra_block = nullptr;                // the fourth buffer (freed on the transfer stream)
     hipStream_t cs = nullptr;
-    hipEvent_t emitted[kStage] = {}, copied[kStage] = {};
+    hipEvent_t emitted[kStage] = {}, copied[kStage] = {}, extra_ready = nullptr;
     bool copy_pending[kStage] = {};
     const int64_t nkeys = W * kHubClasses;  // hub-list keys: window * classes + class
     int32_t *key_count = nullptr, *key_start = nullptr;
@@ -642,6 +712,8 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
             if (emitted[b]) (void)hipEventDestroy(emitted[b]);
             if (copied[b]) (void)hipEventDestroy(copied[b]);
         }
+        if (extra_ready) (void)hipEventDestroy(extra_ready);
+        if (extra_block) dev_free(extra_block, G->xfer);
         dev_free(scratch2, s);
     };
 #define STEP2(expr) do { rc = (expr); if (rc) { cleanup2(); cleanup(); return rc; } } while (0)
@@ -654,13 +726,15 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
         c.take(&key_scan_ws, scan_workspace_bytes(nkeys) / sizeof(int64_t));
     }));
     if (G->windowed()) {  // the graph's window buffers, which stage the build's windows
+        // buffers of a multiple of 256 entries back to back, labels then bins: buffer b starts
+        // b * stride entries after buffer 0 in both arrays, so one launch can address two of them
+        const int64_t stride = (std::max<int64_t>(G->max_window_edges, 1) + 255) & ~(int64_t)255;
         STEP2(carve_alloc(&G->slot_block, s, [&](Carver &c) {
-            for (int b = 0; b < 3; ++b) {
-                c.take(&G->slot_col[b], G->max_window_edges);
-                if (!G->packed) c.take(&G->slot_bin[b], G->max_window_edges);
-            }
+            for (int b = 0; b < 3; ++b) c.take(&G->slot_col[b], stride);
+            if (!G->packed)
+                for (int b = 0; b < 3; ++b) c.take(&G->slot_bin[b], stride);
         }));
-        for (int b = 0; b < kStage; ++b) {
+        for (int b = 0; b < 3; ++b) {
             st_col[b] = G->slot_col[b];
             st_bin[b] = G->slot_bin[b];
         }
@@ -680,6 +754,15 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
             STEP2_HIP(hipEventCreateWithFlags(&emitted[b], hipEventDisableTiming));
             STEP2_HIP(hipEventCreateWithFlags(&copied[b], hipEventDisableTiming));
         }
+        if (W > 3) {  // windows that do not stay on the device: the fourth buffer stages one
+            STEP2(carve_alloc(&extra_block, cs, [&](Carver &c) {
+                c.take(&st_col[3], G->max_window_edges);
+                if (!G->packed) c.take(&st_bin[3], G->max_window_edges);
+            }));
+            STEP2_HIP(hipEventCreateWithFlags(&extra_ready, hipEventDisableTiming));
+            STEP2_HIP(hipEventRecord(extra_ready, cs));
+            STEP2_HIP(hipStreamWaitEvent(s, extra_ready, 0));
+        }
     } else if (!G->rebuild) {  // (rebuild: the emit pass only feeds the statistics)
         STEP2(carve_alloc(&G->arena_csr, s, [&](Carver &c) {
             c.take(&G->col, G->E);
@@ -691,8 +774,23 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     for (int64_t k = 0; k < W && n > 0; ++k) {
         const int64_t lo = G->win[k], hi = G->win[k + 1];
         if (hi <= lo) continue;
-        const int64_t e_lo = G->windowed() ? G->h_row_ptr[lo] : 0;
-        const int sb = (int)(k % kStage);  // staging buffer of this window
+        const int64_t e_lo = G->windowed() ? G->win_e[k] : 0;
+        // staging buffer of this window.  Resident or re-emitted windows: the three in turn.  A
+        // pinned CSR: the last window that leaves the device takes the fourth buffer, earlier
+        // ones the three in turn, and each of the last three windows the buffer among the three
+        // whose download was queued first, so that the emits wait for the earliest downloads.
+        int sb = (int)(k % 3);
+        if (G->host_csr && W > 3) {
+            if (k == W - 4) {
+                sb = 3;
+            } else if (k > W - 4) {
+                sb = -1;
+                for (int b = 0; b < 3; ++b) {
+                    if (st_win[b] >= W - 3) continue;  // holds a window that stays
+                    if (sb < 0 || st_seq[b] < st_seq[sb]) sb = b;
+                }
+            }
+        }
         st_win[sb] = k;
         if (G->host_csr && copy_pending[sb])  // its previous window has been downloaded
             STEP2_HIP(hipStreamWaitEvent(s, copied[sb], 0));
@@ -710,7 +808,7 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
                            G->cell_start, gr, G->work, d_stats, win_last + k);
         STEP2_HIP(hipGetLastError());
         if (G->host_csr) {
-            const int64_t ne = G->h_row_ptr[hi] - e_lo;
+            const int64_t ne = G->win_e[k + 1] - e_lo;
             if (ne > 0) {
                 STEP2_HIP(hipEventRecord(emitted[sb], s));
                 STEP2_HIP(hipStreamWaitEvent(cs, emitted[sb], 0));
@@ -721,8 +819,13 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
                                              hipMemcpyDeviceToHost, cs));
                 STEP2_HIP(hipEventRecord(copied[sb], cs));
                 copy_pending[sb] = true;
+                st_seq[sb] = k;
             }
         }
+    }
+    if (extra_block) {  // freed in order after its downloads
+        dev_free(extra_block, cs);
+        extra_block = nullptr;
     }
     StatsOut hs{};
     std::vector<unsigned long long> h_last(W);
@@ -790,7 +893,7 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     if (G->windowed()) {
         STEP2_HIP(hipEventCreateWithFlags(&G->staged, hipEventDisableTiming));
         STEP2_HIP(hipEventRecord(G->staged, s));
-        for (int b = 0; b < kStage; ++b) G->slot_win[b] = st_win[b];
+        for (int b = 0; b < 3; ++b) G->slot_win[b] = st_win[b];
     }
     cleanup2();
 #undef STEP2
@@ -848,7 +951,7 @@ int emit_window(const gtc_graph_s *G, int64_t w, int32_t *col, uint8_t *bin, hip
     pa.h_lo = (int32_t)lo;
     pa.h_hi = (int32_t)hi;
     pa.row_ptr = G->row_ptr;
-    pa.col_base = G->h_row_ptr[lo];
+    pa.col_base = G->win_e[w];
     pa.col = col;
     pa.bin = G->packed ? nullptr : bin;
     pa.slot_off = nullptr;

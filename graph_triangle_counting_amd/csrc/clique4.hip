@@ -1116,7 +1116,7 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
                 if (slot_win[k] == keep1 || slot_win[k] == keep2) continue;
                 if (best < 0 || slot_used[k] < slot_used[best]) best = k;
             }
-            const int64_t e0w = G->h_row_ptr[G->win[w]], ne = G->h_row_ptr[G->win[w + 1]] - e0w;
+            const int64_t e0w = G->win_e[w], ne = G->win_e[w + 1] - e0w;
             if (ne > 0) {
                 if (G->rebuild) {
                     GTC_TRY(emit_window(G, w, wcol[best], wbin[best], s));
@@ -1148,15 +1148,15 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
                     if (rc) break;
                     a.col_h = wcol[sh];
                     a.bin_h = wbin[sh];
-                    a.base_h = G->h_row_ptr[G->win[h]];
+                    a.base_h = G->win_e[h];
                     a.col_1 = wcol[s1];
                     a.bin_1 = wbin[s1];
-                    a.base_1 = G->h_row_ptr[G->win[c1]];
+                    a.base_1 = G->win_e[c1];
                     a.w1_lo = (int32_t)G->win[c1];
                     a.w1_hi = (int32_t)G->win[c1 + 1];
                     a.col_2 = wcol[s2];
                     a.bin_2 = wbin[s2];
-                    a.base_2 = G->h_row_ptr[G->win[c2]];
+                    a.base_2 = G->win_e[c2];
                     a.w2_lo = (int32_t)G->win[c2];
                     a.w2_hi = (int32_t)G->win[c2 + 1];
                     rc = launch(G->hubs + G->win_hubs[h], nh);

@@ -362,7 +362,7 @@ struct gtc_graph_s {
     std::vector<int64_t> win;       // W+1 label bounds
     std::vector<int64_t> win_hubs;  // W+1 offsets into hubs: window k's hubs, heaviest first
     std::vector<int32_t> win_smax;  // last window holding a spoke of window k's hubs
-    std::vector<int64_t> h_row_ptr; // host copy of row_ptr (tiled graphs)
+    std::vector<int64_t> win_e;     // W+1 CSR offsets of the bounds: row_ptr[win[k]]
     int64_t max_window_edges = 0;
     // out-of-core: the CSR in pinned host memory, only windows go to the device
     bool host_csr = false;   // the CSR in pinned host memory (h_col, h_bin)
@@ -401,7 +401,7 @@ inline int wait_host_csr(const gtc_graph_s *G, hipStream_t s) {
 }
 
 // Emit the CSR rows of hub window w (labels win[w]..win[w+1]) into col/bin (bin null for packed
-// entries), entry e of the graph at col[e - h_row_ptr[win[w]]]: the pair search of the build,
+// entries), entry e of the graph at col[e - win_e[w]]: the pair search of the build,
 // run again.  Needs the sorted coordinates.
 int emit_window(const gtc_graph_s *G, int64_t w, int32_t *col, uint8_t *bin, hipStream_t s);
 

@@ -18,7 +18,7 @@
 // accumulators, so the sum is exact and independent of order (the pages accumulate fp atomics,
 // §III.5.2, and see order-dependent last digits, §IV.8).
 //
-// Graphs over several hub windows (§III.5.3) run as a loop of tiles (hub window, search window);
+// Graphs over several hub windows (§III.5.3) run as a loop of tiles (hub window, search windows);
 // out-of-core windows are uploaded from pinned host memory on a copy stream, or emitted again by
 // the pair search, while the previous tile counts.
 #include <algorithm>
@@ -38,10 +38,13 @@ struct TripletArgs {
     const int32_t *col_h;
     const uint8_t *bin_h;
     int64_t base_h;
-    // search window: rows of spokes, entry e at col_s[e - base_s]; spokes j in [s_lo, s_hi)
+    // search windows: rows of spokes j in [s_lo, s_hi); entry e at col_s[e - base_s] (and
+    // bin_s[e - base_s]) when e < e_split, else at col_s[e - base_s2]: a launch may span two
+    // search windows held in two buffers of one allocation (base_s2 folds in their distance)
     const int32_t *col_s;
     const uint8_t *bin_s;
     int64_t base_s;
+    int64_t e_split, base_s2;
     int32_t s_lo, s_hi;
     const int32_t *hubs;  // hubs of this launch, heaviest first
     int32_t n_hubs;
@@ -211,6 +214,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     const int32_t *const col_s = a.col_s;
     const uint8_t *const bin_s = a.bin_s;
     const int64_t base_s = a.base_s;
+    const int64_t e_split = a.e_split, base_s2 = a.base_s2;
     unsigned long long *const g_counts = a.counts;
     unsigned long long *const g_limbs = a.limbs;
     const double two_s = a.two_s;
@@ -294,7 +298,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             if (total == 0) return;
             cpre[lane] = (uint32_t)(incl - len);
             if (lane == kWave - 1) cpre[kWave] = (uint32_t)incl;
-            cbase[lane] = sb - base_s - (incl - len);
+            cbase[lane] = sb - (sb >= e_split ? base_s2 : base_s) - (incl - len);
             cbij[lane] = (uint8_t)bj;
             if (W) {
                 const double wj = len > 0 ? rw[p0 + lane] : 0.0;
@@ -718,6 +722,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.col_s = G->col;
     a.bin_s = G->bin;
     a.base_s = 0;
+    a.e_split = INT64_MAX;
+    a.base_s2 = 0;
     a.s_lo = 0;
     a.s_hi = (int32_t)G->n;
     a.hubs = hub_list;
@@ -827,7 +833,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         // tile over all spokes.
         const int64_t nw = (int64_t)G->win.size() - 1;
         const bool ooc = G->windowed();
-        const std::vector<int64_t> &hr = G->h_row_ptr;
+        const std::vector<int64_t> &hr = G->win_e;  // CSR offsets of the window bounds
         // Out-of-core window buffers.  Each tile needs its hub window and its search window in a
         // buffer; while a tile's kernel runs, the next tile's missing window is uploaded (pinned
         // host CSR) or emitted again (no stored CSR) on a second stream, into a buffer no running
@@ -876,7 +882,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
                 if (victim < 0 || slot_used[k] < slot_used[victim]) victim = k;
             }
             if (victim < 0) return GTC_OK;
-            const int64_t e0 = hr[G->win[w]], ne = hr[G->win[w + 1]] - e0;
+            const int64_t e0 = hr[w], ne = hr[w + 1] - e0;
             if (slot_read[victim]) GTC_HIP_CHECK(hipStreamWaitEvent(wst, slot_done[victim], 0));
             GTC_TRY(event_pair(cev));
             GTC_HIP_CHECK(hipEventRecord(cev[cev.size() - 2], wst));
@@ -896,35 +902,65 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             *slot = victim;
             return GTC_OK;
         };
-        // hub windows from the last down: the build leaves the last windows in the buffers
-        std::vector<std::pair<int64_t, int64_t>> tiles;
-        for (int64_t h = nw - 1; h >= 0; --h)
-            if (win_hubs[h + 1] > win_hubs[h])
-                for (int64_t sw = h; sw <= G->win_smax[h]; ++sw) tiles.emplace_back(h, sw);
-        for (size_t t = 0; t < tiles.size(); ++t) {
-            const int64_t h = tiles[t].first, sw = tiles[t].second;
-            const int64_t nh = win_hubs[h + 1] - win_hubs[h];
-            int kh = -1, ks = -1;
-            if (ooc) {
-                const int64_t keep[2] = {h, sw};
-                TSTEP(ensure(h, keep, 2, (int64_t)t, &kh));
-                TSTEP(ensure(sw, keep, 2, (int64_t)t, &ks));
-                TSTEP_HIP(hipStreamWaitEvent(s, slot_ready[kh], 0));
-                if (ks != kh) TSTEP_HIP(hipStreamWaitEvent(s, slot_ready[ks], 0));
+        // Launches, hub windows from the last down (the build leaves the last windows in the
+        // buffers).  A launch takes hub window h with search windows sa..sb, sb <= sa + 1: with
+        // the CSR on the device, every search window of h at once; out of core, windows h and
+        // h + 1 together (two buffers, the third takes the next launch's window meanwhile), then
+        // each further search window on its own.  Two windows share a launch when their buffers
+        // lie the same number of entries apart in col and bin (the build lays them out so).
+        struct Launch { int64_t h, sa, sb; };
+        std::vector<Launch> tiles;
+        const bool span_ok = !ooc || G->packed ||
+            ((intptr_t)wcol[1] - (intptr_t)wcol[0]) / 4 == (intptr_t)wbin[1] - (intptr_t)wbin[0] &&
+            ((intptr_t)wcol[2] - (intptr_t)wcol[0]) / 4 == (intptr_t)wbin[2] - (intptr_t)wbin[0];
+        for (int64_t h = nw - 1; h >= 0; --h) {
+            if (win_hubs[h + 1] <= win_hubs[h]) continue;
+            const int64_t smax = G->win_smax[h];
+            if (!ooc) {
+                tiles.push_back({h, h, smax});
+                continue;
             }
-            if (t == 0 || tiles[t - 1].first != h) {
+            int64_t sw = h;
+            if (span_ok && smax > h) {
+                tiles.push_back({h, h, h + 1});
+                sw = h + 2;
+            }
+            for (; sw <= smax; ++sw) tiles.push_back({h, sw, sw});
+        }
+        for (size_t t = 0; t < tiles.size(); ++t) {
+            const int64_t h = tiles[t].h, sa = tiles[t].sa, sb = tiles[t].sb;
+            const int64_t nh = win_hubs[h + 1] - win_hubs[h];
+            int kh = -1, ka = -1, kb = -1;
+            if (ooc) {
+                const int64_t keep[3] = {h, sa, sb};
+                TSTEP(ensure(h, keep, 3, (int64_t)t, &kh));
+                TSTEP(ensure(sa, keep, 3, (int64_t)t, &ka));
+                TSTEP(ensure(sb, keep, 3, (int64_t)t, &kb));
+                if (kh < 0 || ka < 0 || kb < 0) {
+                    set_error("3pCF tiles: no window buffer free for window %lld", (long long)sb);
+                    cleanup_tiles();
+                    cleanup();
+                    return GTC_E_HIP;
+                }
+                TSTEP_HIP(hipStreamWaitEvent(s, slot_ready[kh], 0));
+                if (ka != kh) TSTEP_HIP(hipStreamWaitEvent(s, slot_ready[ka], 0));
+                if (kb != kh && kb != ka) TSTEP_HIP(hipStreamWaitEvent(s, slot_ready[kb], 0));
+            }
+            if (t == 0 || tiles[t - 1].h != h) {
                 a.hubs = hub_list + win_hubs[h];
                 a.n_hubs = (int32_t)nh;
                 TSTEP(hub_class_counts(a.hubs, nh, G->row_ptr, G->work, qcount, s));
             }
             a.col_h = ooc ? wcol[kh] : G->col;
             a.bin_h = ooc ? wbin[kh] : G->bin;
-            a.base_h = ooc ? hr[G->win[h]] : 0;
-            a.col_s = ooc ? wcol[ks] : G->col;
-            a.bin_s = ooc ? wbin[ks] : G->bin;
-            a.base_s = ooc ? hr[G->win[sw]] : 0;
-            a.s_lo = nw == 1 ? 0 : (int32_t)G->win[sw];
-            a.s_hi = nw == 1 ? (int32_t)G->n : (int32_t)G->win[sw + 1];
+            a.base_h = ooc ? hr[h] : 0;
+            a.col_s = ooc ? wcol[ka] : G->col;
+            a.bin_s = ooc ? wbin[ka] : G->bin;
+            a.base_s = ooc ? hr[sa] : 0;
+            a.e_split = ooc && sb != sa ? hr[sb] : INT64_MAX;
+            a.base_s2 = ooc && sb != sa ? hr[sb] - ((intptr_t)wcol[kb] - (intptr_t)wcol[ka]) / 4 : 0;
+            a.s_lo = nw == 1 ? 0 : (int32_t)G->win[sa];
+            a.s_hi = nw == 1 ? (int32_t)G->n : (int32_t)G->win[sb + 1];
             TSTEP(fill_u32(queue, kQueueWords, 0u, s));
             TripletPlan tp = pl;
             tp.blocks = (int)std::min<int64_t>(pl.blocks, (nh + pl.waves - 1) / pl.waves);
@@ -937,18 +973,20 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             if (timed) TSTEP_HIP(hipEventRecord(kev.back(), s));
             ++tiles_run;
             if (ooc) {
-                TSTEP_HIP(hipEventRecord(slot_done[kh], s));
-                slot_read[kh] = true;
-                if (ks != kh) {
-                    TSTEP_HIP(hipEventRecord(slot_done[ks], s));
-                    slot_read[ks] = true;
+                const int used_slots[3] = {kh, ka, kb};
+                for (int u = 0; u < 3; ++u) {
+                    const int k = used_slots[u];
+                    if ((u > 0 && k == kh) || (u > 1 && k == ka)) continue;
+                    TSTEP_HIP(hipEventRecord(slot_done[k], s));
+                    slot_read[k] = true;
                 }
                 if (t + 1 < tiles.size()) {  // prefetch while this tile runs
-                    const int64_t h2 = tiles[t + 1].first, s2 = tiles[t + 1].second;
-                    const int64_t keep[4] = {h, sw, h2, s2};
+                    const Launch &n2 = tiles[t + 1];
+                    const int64_t keep[6] = {h, sa, sb, n2.h, n2.sa, n2.sb};
                     int k2;
-                    TSTEP(ensure(h2, keep, 4, (int64_t)t + 1, &k2));
-                    TSTEP(ensure(s2, keep, 4, (int64_t)t + 1, &k2));
+                    TSTEP(ensure(n2.h, keep, 6, (int64_t)t + 1, &k2));
+                    TSTEP(ensure(n2.sa, keep, 6, (int64_t)t + 1, &k2));
+                    TSTEP(ensure(n2.sb, keep, 6, (int64_t)t + 1, &k2));
                 }
             }
         }

@@ -158,7 +158,7 @@ int count_2pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         const int64_t lo = G->win[w], hi = G->win[w + 1];
         if (hi <= lo) continue;
         if (G->windowed()) {
-            const int64_t e0w = G->h_row_ptr[lo], ne = G->h_row_ptr[hi] - e0w;
+            const int64_t e0w = G->win_e[w], ne = G->win_e[w + 1] - e0w;
             if (ne <= 0) continue;
             if (G->rebuild) {
                 rc = emit_window(G, w, wcol, wbin, s);

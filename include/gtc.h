@@ -87,8 +87,9 @@ typedef struct {
  * memory from the HIP runtime. */
 typedef struct {
     /* > 0: rows are split into hub windows whose CSR is at most tile_bytes (a single longer row
-     * gets a window of its own), and counting runs as a loop over (hub window, search window)
-     * tiles (§III.5.3).  The CSR takes 4 bytes per edge when n <= 2^24 (label and bin packed in
+     * gets a window of its own), and counting runs as a loop over (hub window, search windows)
+     * tiles (§III.5.3): a 3pCF tile takes every search window of its hub window when the CSR is
+     * on the device, at most two otherwise.  The CSR takes 4 bytes per edge when n <= 2^24 (label and bin packed in
      * one word) and 5 bytes per edge otherwise.
      * 0: the environment variable GTC_TILE_BYTES, if set, gives the budget; otherwise one resident
      * window, unless the CSR would take more than 3/4 of the free device memory: then the build
@@ -305,6 +306,17 @@ int gtc_graph_export(gtc_graph g, int64_t *h_row_ptr, int32_t *h_col, uint8_t *h
  * largest spoke label of window h, so every forward edge is walked in exactly one tile. */
 int64_t gtc_plan_windows(const int64_t *h_row_ptr, int64_t n, int64_t tile_bytes,
                          int32_t entry_bytes, int64_t *h_bounds);
+
+/* Hub windows of a built graph (§III.5.3), for inspection and tests; host only, no GPU work.
+ *   h_bounds  host int64 [W+1] or NULL: label bounds b_0 = 0 < ... < b_W = n of the windows, as
+ *             gtc_plan_windows gives them for the graph's CSR offsets and budget (the build plans
+ *             them on the device; one window [0, n) when the graph is not tiled).
+ *   h_offsets host int64 [W+1] or NULL: CSR offsets of the bounds, row_ptr[b_k].
+ *   capacity  entries each non-NULL array holds; the arrays are written only when capacity >=
+ *             W + 1 (call with capacity 0 to learn W).
+ * Returns W >= 1, or GTC_E_INVALID for a null graph, capacity < 0, or capacity > 0 with both
+ * arrays NULL. */
+int64_t gtc_graph_windows(gtc_graph g, int64_t *h_bounds, int64_t *h_offsets, int64_t capacity);
 
 /* Squared edges of nbins equal radial bins from r_min to r_max (§IV: bins equally spaced in r
  * from r_min to r_max), as integers: h_edges_sq[b] = ceil(r_b^2), r_b = r_min + b (r_max - r_min)

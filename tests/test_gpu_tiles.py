@@ -45,7 +45,11 @@ def test_tiled_equals_resident_and_oracle(gpu_available, monkeypatch, kind, seed
         tb = max(1, int(csr_bytes * frac))
         say("tiles", kind, seed, "csr_mode", csr_mode, layout, "tile_bytes", tb)
         c, ws, st = hip_3pcf(xyz, edges, w, tile_bytes=tb, csr_mode=csr_mode)
-        assert st["windows"] > 1 and st["tiles"] >= st["windows"]
+        # one launch per hub window with hubs, over all its search windows (resident CSR) or
+        # over at most two at a time (out of core)
+        assert st["windows"] > 1 and 1 <= st["tiles"]
+        if csr_mode == "device":
+            assert st["tiles"] <= st["windows"]
         np.testing.assert_array_equal(c, c0)
         if weighted:
             np.testing.assert_array_equal(ws, w0)
@@ -237,3 +241,34 @@ def test_out_of_core_graph_serves_repeated_calls(gpu_available, csr_mode):
         np.testing.assert_array_equal(edge_set_from_gpu(g), x0)
     g.close()
     gtc.release_host_cache()
+
+
+@pytest.mark.parametrize("layout", ["packed", "split"])
+def test_device_window_plan_matches_host_planner(gpu_available, monkeypatch, layout):
+    """The build plans its hub windows on the device; they are the host planner's windows for the
+    graph's own CSR offsets, down to one row per window."""
+    import ctypes as C
+    if layout == "split":
+        monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
+    entry = 5 if layout == "split" else 4
+    xyz = clustered(45, 6000, 25, 3000)
+    edges = linear_edges_sq(9000, 5)
+    g0 = gtc.Graph(to_gpu(xyz), edges)
+    rp = g0.export()[0]
+    b0, o0 = g0.windows()
+    g0.close()
+    np.testing.assert_array_equal(b0, [0, 6000])
+    np.testing.assert_array_equal(o0, [0, rp[-1]])
+    max_row = int(np.diff(rp).max())
+    for tb in (entry * rp[-1] // 3, entry * rp[-1] // 97, entry * max_row, entry * max_row - 1,
+               entry, 1):
+        g = gtc.Graph(to_gpu(xyz), edges, tile_bytes=int(tb))
+        bounds, offsets = g.windows()
+        want = np.empty(len(rp) + 1, np.int64)
+        W = gtc.lib().gtc_plan_windows(rp.ctypes.data_as(C.c_void_p), len(rp) - 1, int(tb), entry,
+                                       want.ctypes.data_as(C.c_void_p))
+        say("window plan", layout, "tile_bytes", tb, "windows", W)
+        assert g.stats()["windows"] == W == len(bounds) - 1
+        np.testing.assert_array_equal(bounds, want[: W + 1])
+        np.testing.assert_array_equal(offsets, rp[bounds])
+        g.close()
