@@ -361,7 +361,8 @@ def bench_4pcf(args, cfg):
     K = ncl[0]
     k_avg = sum(kms) / len(kms)
     log(f"[bench] {args.steps} steps: {1e3 * elapsed / args.steps:.2f} ms/step, build "
-        f"{sum(bms) / len(bms):.2f} ms, kernel {k_avg:.3f} ms, tetrahedra {K}")
+        f"{sum(bms) / len(bms):.2f} ms, kernel {k_avg:.3f} ms, tetrahedra {K}, windows "
+        f"{gst['windows']}, tiles {st['tiles']}")
     variant = cfg.key + ("-s4" if args.s4 else "") + ("-w" if args.weighted else "")
     valu = measured_valu(variant) if args.tile_bytes == 0 else None
     achieved = None if valu is None else valu / (k_avg * 1e-3) / 1e9
@@ -396,7 +397,7 @@ def bench_4pcf(args, cfg):
                    "configurations": "S4" if args.s4 else "sorted 6-tuples",
                    "weighted": bool(args.weighted),
                    "edges": st["edges"], "tetrahedra": K, "tile_bytes": args.tile_bytes,
-                   "csr_mode": csr_mode},
+                   "csr_mode": csr_mode, "windows": gst["windows"], "tiles": st["tiles"]},
         "build_ms": sum(bms) / len(bms),
         "roofline": roofline,
         "cpu_baseline": cpu,

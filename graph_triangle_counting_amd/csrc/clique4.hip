@@ -41,9 +41,13 @@ struct CliqueArgs {
     // A tile counts the tetrahedra (i, a, b, c), i < a < b < c, with a in c1 and b in c2: the
     // edges among the spokes come from the rows of a and b.  A resident graph is one tile with
     // all three windows the whole CSR.
+    // A launch over a hub window and the next one together takes both as c1 = c2, their rows
+    // in two buffers of one allocation: spoke rows at or after CSR offset e_split then sit at
+    // col_1[e - base_1b].
     const int32_t *col_h, *col_1, *col_2;
     const uint8_t *bin_h, *bin_1, *bin_2;
     int64_t base_h, base_1, base_2;
+    int64_t e_split, base_1b;
     int32_t w1_lo, w1_hi, w2_lo, w2_hi;
     int32_t tiled;         // 0: one resident tile (every spoke in both ranges)
     uint32_t label_mask;   // label bits of a col word
@@ -347,7 +351,8 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                     const int32_t j = hlab(sp);
                     const int64_t jb = a.row_ptr[j];
                     len = (int32_t)(a.row_ptr[j + 1] - jb);
-                    row = in1 ? a.col_1 + (jb - a.base_1) : a.col_2 + (jb - a.base_2);
+                    row = in1 ? a.col_1 + (jb - (jb >= a.e_split ? a.base_1b : a.base_1))
+                              : a.col_2 + (jb - a.base_2);
                 }
             }
             const int incl = wave_incl_scan(len, lane);
@@ -834,6 +839,8 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     a.col_h = a.col_1 = a.col_2 = G->col;
     a.bin_h = a.bin_1 = a.bin_2 = G->bin;
     a.base_h = a.base_1 = a.base_2 = 0;
+    a.e_split = INT64_MAX;
+    a.base_1b = 0;
     a.w1_lo = a.w2_lo = 0;
     a.w1_hi = a.w2_hi = (int32_t)G->n;
     a.tiled = 0;
@@ -872,8 +879,13 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
                     static_lds0 + fixed_u + per_u <= (size_t)ldsmax;
     if (const char *env = std::getenv("GTC_CONFIG_CACHE"))  // "off": global sums only (tests)
         if (std::strcmp(env, "off") == 0) cache_ok = false;
+    // GTC_CACHE_WAVES=w: waves per workgroup beside the cache (default 6, else 3; fewer waves
+    // leave room for more cached configurations, whose tetrahedra then add in LDS)
+    int w_first = 6;
+    if (const char *env = std::getenv("GTC_CACHE_WAVES"))
+        w_first = std::max(1, std::min(16, std::atoi(env)));
     if (cache_ok)
-        for (int w = 8; w >= 4 && !cache_k; w >>= 1) {
+        for (int w = w_first; w >= std::min(3, w_first) && !cache_k; w >>= 1) {
             const size_t used = static_lds0 + (size_t)w * per + 4 * kRankTab + align16(2 * (size_t)ncfg);
             if (used >= (size_t)ldsmax) continue;
             int64_t k = std::min<int64_t>({ncfg, (int64_t)32767, (int64_t)((ldsmax - used) / 60)});
@@ -909,6 +921,12 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         return GTC_E_UNSUPPORTED;
     }
     a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub);
+    // GTC_CLIQUE_FLUSH_AT=n drains the LDS count bins at least every n tetrahedra of a
+    // wave
+    if (const char *env = std::getenv("GTC_CLIQUE_FLUSH_AT")) {
+        const long long v = std::atoll(env);
+        if (!GH && v > 0 && (unsigned long long)v < a.flush_at) a.flush_at = (unsigned int)v;
+    }
 
     unsigned int *queue = nullptr, *qcount = nullptr;
     uint32_t *s4rank = nullptr;
@@ -1099,9 +1117,11 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     if (!rc && G->n_hubs > 0 && tiled) {
         // Tiles (h, c1, c2), h <= c1 <= c2 <= the last window holding a spoke of window h: the
         // tetrahedra with hub i in window h, spoke a in c1 and spoke b in c2 (i < a < b), each
-        // counted in exactly one tile.  The three windows are made resident (copied from the
-        // pinned CSR or emitted again), evicting the least recently used window a tile does not
-        // need; all on the counting stream, after the kernels that read the buffer.
+        // counted in exactly one tile.  When the spokes of window h reach no further than window
+        // h + 1, one launch takes all of them (c1 = c2 = windows h and h + 1), so that each hub
+        // is set up once.  The windows are made resident (copied from the pinned CSR or emitted
+        // again), evicting the least recently used window a tile does not need; all on the
+        // counting stream, after the kernels that read the buffer.
         int64_t slot_win[kSlots] = {-1, -1, -1}, slot_used[kSlots] = {0, 0, 0}, clock = 0;
         rc = wait_host_csr(G, s);  // uploads read the pinned CSR after the build's downloads
         auto ensure = [&](int64_t w, int64_t keep1, int64_t keep2, int *slot) -> int {
@@ -1139,6 +1159,23 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
             const int64_t nh = G->win_hubs[h + 1] - G->win_hubs[h];
             if (nh <= 0) continue;
             const int64_t smax = G->win_smax[h];
+            if (smax <= h + 1) {
+                int sh = 0, sn = 0;
+                rc = ensure(h, smax, smax, &sh);
+                if (!rc) rc = ensure(smax, h, h, &sn);
+                if (rc) break;
+                a.col_h = a.col_1 = a.col_2 = wcol[sh];
+                a.bin_h = a.bin_1 = a.bin_2 = wbin[sh];
+                a.base_h = a.base_1 = a.base_2 = G->win_e[h];
+                a.w1_lo = a.w2_lo = (int32_t)G->win[h];
+                a.w1_hi = a.w2_hi = (int32_t)G->win[smax + 1];
+                a.e_split = smax > h ? G->win_e[smax] : INT64_MAX;
+                a.base_1b = smax > h ? G->win_e[smax] - ((intptr_t)wcol[sn] - (intptr_t)wcol[sh]) / 4 : 0;
+                rc = launch(G->hubs + G->win_hubs[h], nh);
+                a.e_split = INT64_MAX;
+                a.base_1b = 0;
+                continue;
+            }
             for (int64_t c1 = h; c1 <= smax && !rc; ++c1)
                 for (int64_t c2 = c1; c2 <= smax && !rc; ++c2) {
                     int sh = 0, s1 = 0, s2 = 0;

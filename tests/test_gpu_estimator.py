@@ -79,6 +79,28 @@ def test_4pcf_weighted_s4_cache_matches_global_sums(gpu_available, monkeypatch, 
     assert cached[0].view(np.uint64).sum() > 0 and np.abs(cached[3]).sum() > 0
 
 
+@pytest.mark.parametrize("cache", ["on", "off"])
+@pytest.mark.parametrize("s4", [False, True])
+def test_4pcf_weighted_frequent_drains_match_oracle(gpu_available, monkeypatch, s4, cache):
+    # the LDS count bins drained to global memory every few hundred tetrahedra of a wave give
+    # the oracle's exact counts and sums (signed weights)
+    say("4pcf weighted drains", s4, cache)
+    monkeypatch.setenv("GTC_CLIQUE_FLUSH_AT", "300")
+    monkeypatch.setenv("GTC_CONFIG_CACHE", cache)
+    xyz = clustered(48, 8000, 50, 2000)
+    w = rng_for(548).uniform(-2.0, 2.0, 8000)
+    edges = linear_edges_sq(3000, 6)
+    g = gtc.Graph(to_gpu(xyz), edges)
+    e, o, ew, ow, _ = g.count_4pcf_weighted(to_gpu_f64(w), s4=s4)
+    g.close()
+    oe, oo, oew, oow, _ = oracle.Graph(xyz, edges).count_4pcf_weighted(w, s4=s4)
+    np.testing.assert_array_equal(e.cpu().numpy().view(np.uint64), oe)
+    np.testing.assert_array_equal(o.cpu().numpy(), oo)
+    np.testing.assert_array_equal(ew.cpu().numpy(), oew)
+    np.testing.assert_array_equal(ow.cpu().numpy(), oow)
+    assert int(oe.sum()) > 300 * 64
+
+
 def test_4pcf_weighted_rejects_non_finite_weights(gpu_available):
     xyz = clustered(45, 500, 10, 2000)
     w = np.ones(500)
