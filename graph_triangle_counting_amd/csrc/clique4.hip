@@ -948,9 +948,14 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     constexpr int kSlots = 3;
     int32_t *wcol[kSlots] = {nullptr, nullptr, nullptr};
     uint8_t *wbin[kSlots] = {nullptr, nullptr, nullptr};
+    unsigned int *queue2 = nullptr, *qcount2 = nullptr;  // the second stream's launches (tiles)
     GTC_TRY(carve_alloc(&scratch, s, [&](Carver &c) {
         c.take(&queue, (size_t)kQueueWords);
         c.take(&qcount, kHubClasses);
+        if (tiled) {
+            c.take(&queue2, (size_t)kQueueWords);
+            c.take(&qcount2, kHubClasses);
+        }
         if (tiled)
             for (int k = 0; k < kSlots; ++k) {
                 c.take(&wcol[k], std::max<int64_t>(G->max_window_edges, 1));
@@ -1088,10 +1093,19 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
     // one launch over the hub list hubs[0, nh): one hub per take (a hub's 4-clique work grows like
     // the cube of its row, which the spoke-element classes predict poorly, and the takes, a few
     // thousand per ms, are far below what one counter serves)
-    auto launch = [&](const int32_t *hubs, int64_t nh) -> int {
+    // (on stream st with the queue counters q, qc; by default the counting stream's)
+    auto launch = [&](const int32_t *hubs, int64_t nh, hipStream_t st = nullptr,
+                      unsigned int *q = nullptr, unsigned int *qc = nullptr) -> int {
         if (nh <= 0) return GTC_OK;
-        GTC_TRY(hub_class_counts(hubs, nh, G->row_ptr, G->work, qcount, s));
-        GTC_TRY(fill_u32(queue, kQueueWords, 0u, s));
+        if (!st) {
+            st = s;
+            q = queue;
+            qc = qcount;
+        }
+        GTC_TRY(hub_class_counts(hubs, nh, G->row_ptr, G->work, qc, st));
+        GTC_TRY(fill_u32(q, kQueueWords, 0u, st));
+        a.queue = q;
+        a.qcount = qc;
         a.hubs = hubs;
         a.n_hubs = (int32_t)nh;
         a.batch_cap = 1;
@@ -1103,18 +1117,131 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         kev.push_back(e0);
         GTC_HIP_CHECK(hipEventCreate(&e1));
         kev.push_back(e1);
-        GTC_HIP_CHECK(hipEventRecord(e0, s));
+        GTC_HIP_CHECK(hipEventRecord(e0, st));
         const int64_t *edges_dev = G->d_edges;
         void *args[] = {&a, &edges_dev};
-        hipError_t e = hipLaunchKernel(kfn, grid, block, args, lds, s);
+        hipError_t e = hipLaunchKernel(kfn, grid, block, args, lds, st);
         if (e == hipSuccess) e = hipGetLastError();
         if (e != hipSuccess) return hip_fail(e, "k_clique4 launch", __FILE__, __LINE__);
-        GTC_HIP_CHECK(hipEventRecord(e1, s));
+        GTC_HIP_CHECK(hipEventRecord(e1, st));
         ++tiles_run;
         return GTC_OK;
     };
     if (!rc && G->n_hubs > 0 && !tiled) rc = launch(G->hubs, G->n_hubs);
-    if (!rc && G->n_hubs > 0 && tiled) {
+    // Out of core, when every hub window's spokes reach no further than the next window: one
+    // launch per hub window (windows h and h + 1), on two streams in turn, so that a launch's
+    // last hubs overlap the next launch.  Two launches in flight hold at most three windows (h - 1,
+    // h, h + 1), the three buffers.  A buffer is refilled (on the stream of the launch that needs
+    // it) after every launch that read it, on either stream; a launch waits for its windows.
+    bool two_streams = !rc && G->n_hubs > 0 && tiled;
+    const int64_t nwin = (int64_t)G->win.size() - 1;
+    for (int64_t h = 0; two_streams && h < nwin; ++h)
+        if (G->win_hubs[h + 1] > G->win_hubs[h] && G->win_smax[h] > h + 1) two_streams = false;
+    if (two_streams) {
+        hipStream_t s2 = nullptr;
+        hipEvent_t ev_start = nullptr, ev_end2 = nullptr, ready[kSlots] = {}, done[kSlots][2] = {};
+        bool done_set[kSlots][2] = {};
+        int64_t slot_win[kSlots] = {-1, -1, -1}, slot_used[kSlots] = {0, 0, 0}, clock = 0;
+        auto two = [&]() -> int {
+            GTC_HIP_CHECK(hipStreamCreateWithFlags(&s2, hipStreamNonBlocking));
+            GTC_HIP_CHECK(hipEventCreateWithFlags(&ev_start, hipEventDisableTiming));
+            GTC_HIP_CHECK(hipEventCreateWithFlags(&ev_end2, hipEventDisableTiming));
+            for (int k = 0; k < kSlots; ++k) {
+                GTC_HIP_CHECK(hipEventCreateWithFlags(&ready[k], hipEventDisableTiming));
+                for (int q = 0; q < 2; ++q)
+                    GTC_HIP_CHECK(hipEventCreateWithFlags(&done[k][q], hipEventDisableTiming));
+            }
+            GTC_TRY(wait_host_csr(G, s));  // uploads read the pinned CSR after the build's downloads
+            GTC_HIP_CHECK(hipEventRecord(ev_start, s));
+            GTC_HIP_CHECK(hipStreamWaitEvent(s2, ev_start, 0));
+            a.tiled = 1;
+            int64_t prev_h = -1, prev_s = -1;  // windows of the launch in flight on the other stream
+            int t = 0;
+            for (int64_t h = 0; h < nwin; ++h) {
+                const int64_t nh = G->win_hubs[h + 1] - G->win_hubs[h];
+                if (nh <= 0) continue;
+                const int q = t & 1;
+                hipStream_t st = q ? s2 : s;
+                const int64_t smax = G->win_smax[h];
+                int sl[2] = {-1, -1};
+                const int64_t need[2] = {h, smax};
+                for (int u = 0; u < 2; ++u) {
+                    const int64_t w = need[u];
+                    for (int k = 0; k < kSlots; ++k)
+                        if (slot_win[k] == w) sl[u] = k;
+                    if (sl[u] >= 0) continue;
+                    int victim = -1;
+                    for (int pass = 0; pass < 2 && victim < 0; ++pass) {
+                        for (int k = 0; k < kSlots; ++k) {
+                            const int64_t x = slot_win[k];
+                            if (x == h || x == smax) continue;
+                            if (pass == 0 && (x == prev_h || x == prev_s)) continue;
+                            if (victim < 0 || slot_used[k] < slot_used[victim]) victim = k;
+                        }
+                    }
+                    if (victim < 0) {
+                        set_error("4pCF tiles: no window buffer free for window %lld", (long long)w);
+                        return GTC_E_HIP;
+                    }
+                    for (int r = 0; r < 2; ++r)  // after every launch that read the buffer
+                        if (done_set[victim][r]) GTC_HIP_CHECK(hipStreamWaitEvent(st, done[victim][r], 0));
+                    const int64_t e0w = G->win_e[w], ne = G->win_e[w + 1] - e0w;
+                    if (ne > 0) {
+                        if (G->rebuild) {
+                            GTC_TRY(emit_window(G, w, wcol[victim], wbin[victim], st));
+                        } else {
+                            GTC_HIP_CHECK(hipMemcpyAsync(wcol[victim], G->h_col + e0w,
+                                                         sizeof(int32_t) * ne, hipMemcpyHostToDevice, st));
+                            if (!G->packed)
+                                GTC_HIP_CHECK(hipMemcpyAsync(wbin[victim], G->h_bin + e0w, ne,
+                                                             hipMemcpyHostToDevice, st));
+                        }
+                    }
+                    GTC_HIP_CHECK(hipEventRecord(ready[victim], st));
+                    slot_win[victim] = w;
+                    sl[u] = victim;
+                }
+                for (int u = 0; u < 2; ++u) {
+                    GTC_HIP_CHECK(hipStreamWaitEvent(st, ready[sl[u]], 0));
+                    slot_used[sl[u]] = ++clock;
+                }
+                const int sh = sl[0], sn = sl[1];
+                a.col_h = a.col_1 = a.col_2 = wcol[sh];
+                a.bin_h = a.bin_1 = a.bin_2 = wbin[sh];
+                a.base_h = a.base_1 = a.base_2 = G->win_e[h];
+                a.w1_lo = a.w2_lo = (int32_t)G->win[h];
+                a.w1_hi = a.w2_hi = (int32_t)G->win[smax + 1];
+                a.e_split = smax > h ? G->win_e[smax] : INT64_MAX;
+                a.base_1b = smax > h ? G->win_e[smax] - ((intptr_t)wcol[sn] - (intptr_t)wcol[sh]) / 4 : 0;
+                GTC_TRY(launch(G->hubs + G->win_hubs[h], nh, st, q ? queue2 : queue, q ? qcount2 : qcount));
+                for (int u = 0; u < 2; ++u) {
+                    GTC_HIP_CHECK(hipEventRecord(done[sl[u]][q], st));
+                    done_set[sl[u]][q] = true;
+                }
+                prev_h = h;
+                prev_s = smax;
+                ++t;
+            }
+            a.e_split = INT64_MAX;
+            a.base_1b = 0;
+            GTC_HIP_CHECK(hipEventRecord(ev_end2, s2));
+            GTC_HIP_CHECK(hipStreamWaitEvent(s, ev_end2, 0));
+            return GTC_OK;
+        };
+        rc = two();
+        if (s2) {
+            (void)hipStreamSynchronize(s2);
+            (void)hipStreamDestroy(s2);
+        }
+        if (ev_start) (void)hipEventDestroy(ev_start);
+        if (ev_end2) (void)hipEventDestroy(ev_end2);
+        for (int k = 0; k < kSlots; ++k) {
+            if (ready[k]) (void)hipEventDestroy(ready[k]);
+            for (int q = 0; q < 2; ++q)
+                if (done[k][q]) (void)hipEventDestroy(done[k][q]);
+        }
+    }
+    if (!rc && G->n_hubs > 0 && tiled && !two_streams) {
         // Tiles (h, c1, c2), h <= c1 <= c2 <= the last window holding a spoke of window h: the
         // tetrahedra with hub i in window h, spoke a in c1 and spoke b in c2 (i < a < b), each
         // counted in exactly one tile.  When the spokes of window h reach no further than window
@@ -1206,10 +1333,17 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
         hipError_t e = hipMemcpyAsync(h_even.data(), d_even, 8 * ncfg, hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) rc = hip_fail(e, "4pCF readback", __FILE__, __LINE__);
+        // launches on two streams overlap: from the first start to the last end
+        const size_t k0 = two_streams && kev.size() >= 2 ? kev.size() - 2 * (size_t)tiles_run : 0;
         for (size_t k = 0; !rc && k + 1 < kev.size(); k += 2) {
             float t = 0.f;
-            (void)hipEventElapsedTime(&t, kev[k], kev[k + 1]);
-            kms += t;
+            if (two_streams && k >= k0) {
+                (void)hipEventElapsedTime(&t, kev[k0], kev[k + 1]);
+                kms = std::max(kms, t);
+            } else {
+                (void)hipEventElapsedTime(&t, kev[k], kev[k + 1]);
+                kms += t;
+            }
         }
     }
     (void)hipStreamSynchronize(s);

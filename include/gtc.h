@@ -139,7 +139,8 @@ typedef struct {
     int32_t csr_mode;          /* where the graph's CSR is kept: GTC_CSR_* (the build may go out
                                   of core by itself, see gtc_options.tile_bytes) */
     double build_ms;           /* gtc_build_graph: whole call */
-    double kernel_ms;          /* enumeration kernels only (sum over tiles) */
+    double kernel_ms;          /* enumeration kernels only (sum over tiles; 4pCF tiles that
+                                * overlap on two streams: first start to last end) */
     double count_ms;           /* count call: whole call */
     double h2d_ms;             /* out-of-core: window copies (GTC_CSR_HOST) or window emits
                                   (GTC_CSR_REBUILD), summed; they overlap the counting */
