@@ -79,6 +79,7 @@ struct CliqueArgs {
     // LDS configuration cache (weighted, WM 3): cache_k configurations have an LDS slot:
     // cache_slot[rank] is the slot or -1, cache_rank[slot] the configuration
     int32_t cache_k;
+    int32_t slot_in_rank;  // S4 with a cache: s4rank entries carry slot + 1 in bits 20-31
     const int16_t *cache_slot;
     const int32_t *cache_rank;
 };
@@ -95,14 +96,20 @@ __host__ __device__ inline size_t align16(size_t x) { return (x + 15) / 16 * 16;
 // combinatorial number system gives rank = C(N, 6) + sum_{q<5} C(N - c_q - 1, 5 - q) -
 // sum_q C(N - c_q, 6 - q); G[q][b] collects the terms of position q (C(N, 6) goes to q = 0).
 constexpr int kRankTab = 6 * GTC_MAX_BINS_4PCF;
+// S4 rank table entries: the rank in the low 20 bits (num_configs_s4(16) = 723,776 < 2^20) and,
+// with a configuration cache, the rank's slot + 1 above them (0: not cached)
+constexpr uint32_t kRankMask = (1u << 20) - 1;
+constexpr int kSlotShift = 20;
+constexpr int kMaxTableSlots = (1 << (32 - kSlotShift)) - 2;
 
 // fixed part: even / odd count bins (unless global), the rank table G[6][16], (LDS class sums)
 // [ncfg][3][2] words.  With an LDS configuration cache of k > 0 slots: even / odd bins and class
 // sums per slot, the slot of every configuration (int16) and the configuration of every slot.
-__host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh, bool wl = false, int k = 0) {
+__host__ __device__ inline size_t clique_lds_fixed(int ncfg, bool gh, bool wl = false, int k = 0,
+                                                   bool slot_table = true) {
     if (k > 0)
-        return align16(4 * (size_t)k) * 2 + 4 * kRankTab + 48 * (size_t)k +
-               align16(2 * (size_t)ncfg) + align16(4 * (size_t)k);
+        return align16(4 * (size_t)k) * 2 + 4 * kRankTab + 32 * (size_t)k +
+               (slot_table ? align16(2 * (size_t)ncfg) : 0) + align16(4 * (size_t)k);
     return (gh ? 0 : align16(4 * (size_t)ncfg) * 2) + 4 * kRankTab + (wl ? 48 * (size_t)ncfg : 0);
 }
 // per-wave enumeration scratch: bitset words and their edge offsets, edges and their
@@ -226,10 +233,16 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
     int32_t *od = reinterpret_cast<int32_t *>(smem + hist_bytes);
     int32_t *rtab = reinterpret_cast<int32_t *>(smem + 2 * hist_bytes);  // G[q][b] at q * 16 + b
     unsigned long long *wl = reinterpret_cast<unsigned long long *>(smem + 2 * hist_bytes + 4 * kRankTab);
-    int16_t *slot16 = reinterpret_cast<int16_t *>(smem + 2 * hist_bytes + 4 * kRankTab + 48 * (size_t)nslot);
+    // class sums in LDS: [nslot][3] 128-bit words (A+, A-, A0) in WM 2; in WM 3 [nslot][2], the
+    // even sum E = A+ + A- + A0 and the odd sum O = A+ - A- (32 bytes a slot, so more slots fit)
+    constexpr int kSlotWords = WM == 3 ? 4 : 6;
+    int16_t *slot16 = reinterpret_cast<int16_t *>(smem + 2 * hist_bytes + 4 * kRankTab +
+                                                  8 * kSlotWords * (size_t)nslot);
+    // (S4: the slots come with the configuration's rank from the rank table, no LDS slot index)
+    const bool sir = WM == 3 && a.slot_in_rank;
     int32_t *rank_of = reinterpret_cast<int32_t *>(reinterpret_cast<unsigned char *>(slot16) +
-                                                   align16(2 * (size_t)a.ncfg));
-    unsigned char *wbase = smem + clique_lds_fixed(a.ncfg, GH, WM == 2, WM == 3 ? a.cache_k : 0) +
+                                                   (sir ? 0 : align16(2 * (size_t)a.ncfg)));
+    unsigned char *wbase = smem + clique_lds_fixed(a.ncfg, GH, WM == 2, WM == 3 ? a.cache_k : 0, !sir) +
                            (size_t)wid * clique_lds_wave(a.map_bytes, a.max_m, a.words, WT);
     uint16_t *pmap = reinterpret_cast<uint16_t *>(wbase);
     int4 *rc = reinterpret_cast<int4 *>(wbase + a.map_bytes);
@@ -248,9 +261,10 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
     unsigned long long *wg = nullptr;  // this workgroup's copy of the global class sums
     if (WT) wg = a.wsum + (long long)(blockIdx.x % (unsigned)a.wcopies) * a.wstride;
     if (WM >= 2)
-        for (int t = threadIdx.x; t < 6 * nslot; t += blockDim.x) wl[t] = 0ull;
+        for (int t = threadIdx.x; t < kSlotWords * nslot; t += blockDim.x) wl[t] = 0ull;
     if (WM == 3) {
-        for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) slot16[t] = a.cache_slot[t];
+        if (!sir)
+            for (int t = threadIdx.x; t < a.ncfg; t += blockDim.x) slot16[t] = a.cache_slot[t];
         for (int t = threadIdx.x; t < nslot; t += blockDim.x) rank_of[t] = a.cache_rank[t];
     }
 
@@ -487,19 +501,23 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                     // the six bins in edge order of the vertices (i, a, b, c)
                     int bb[6] = {bia, bib, rbin[rcc], bab, edge_bin_d(dac, se, bin_half),
                                  edge_bin_d(dbc, se, bin_half)};
-                    int rank = 0;
+                    // the configuration: its rank, with the cache's slot in the S4 table's high
+                    // bits (taken apart only below, so the table read overlaps the geometry)
+                    uint32_t packed = 0;
                     if (a.s4rank) {  // S4 configuration: one table read
                         int key = 0;
 #pragma unroll
                         for (int q = 0; q < 6; ++q) key = key * a.nb + bb[q];
-                        rank = (int)a.s4rank[key];
+                        packed = a.s4rank[key];
                     } else {  // sorted 6-tuple: sorting network, one rank-table entry per position
                         cswap(bb[1], bb[2]); cswap(bb[4], bb[5]); cswap(bb[0], bb[2]);
                         cswap(bb[3], bb[5]); cswap(bb[0], bb[1]); cswap(bb[3], bb[4]);
                         cswap(bb[1], bb[4]); cswap(bb[0], bb[3]); cswap(bb[2], bb[5]);
                         cswap(bb[1], bb[3]); cswap(bb[2], bb[4]); cswap(bb[2], bb[3]);
+                        int r = 0;
 #pragma unroll
-                        for (int q = 0; q < 6; ++q) rank += rtab[q * GTC_MAX_BINS_4PCF + bb[q]];
+                        for (int q = 0; q < 6; ++q) r += rtab[q * GTC_MAX_BINS_4PCF + bb[q]];
+                        packed = (uint32_t)r;
                     }
                     // vertex keys (sums of the three squared edge lengths, exact) of i, a, b,
                     // c; sorting them ascending permutes the vertices, and the orientation of
@@ -516,8 +534,7 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                         const int o = orient_sign(Cc, X0, X1, X2);
                         sgn = par ? -o : o;
                     }
-                    // the configuration's LDS slot (WM 3: -1 when it is not cached)
-                    const int sl = WM == 3 ? (int)slot16[rank] : rank;
+                    double qv = 0.0;
                     if (WT) {  // the four weights ascending, product without fusion
                         double v0 = wi, v1 = rw[ra], v2 = rw[rbb], v3 = rw[rcc], t;
                         t = fmin(v0, v1); v1 = fmax(v0, v1); v0 = t;
@@ -526,10 +543,19 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
                         t = fmin(v1, v3); v3 = fmax(v1, v3); v1 = t;
                         t = fmin(v1, v2); v2 = fmax(v1, v2); v1 = t;
                         const double pr = __dmul_rn(__dmul_rn(__dmul_rn(v0, v1), v2), v3);
-                        const double qv = rint(__dmul_rn(pr, a.two_s));  // exact, |qv| < 2^57
+                        qv = rint(__dmul_rn(pr, a.two_s));  // exact, |qv| < 2^57
+                    }
+                    const int rank = sir ? (int)(packed & kRankMask) : (int)packed;
+                    // the configuration's LDS slot (WM 3: -1 when it is not cached)
+                    const int sl = WM == 3 ? (sir ? (int)(packed >> kSlotShift) - 1 : (int)slot16[rank])
+                                           : rank;
+                    if (WT) {
                         const int cls = sgn > 0 ? 0 : (sgn < 0 ? 1 : 2);
                         const int idx = 3 * rank + cls;
-                        if (WM == 2 || (WM == 3 && sl >= 0)) {
+                        if (WM == 3 && sl >= 0) {
+                            add_i128(wl + 4 * sl, (long long)qv);
+                            if (sgn) add_i128(wl + 4 * sl + 2, (long long)(sgn > 0 ? qv : -qv));
+                        } else if (WM == 2) {
                             add_i128(wl + 2 * (3 * sl + cls), (long long)qv);
                         } else {
                             if (idx != pend) {
@@ -600,11 +626,19 @@ __global__ void __launch_bounds__(1024) k_clique4(CliqueArgs a, const int64_t *e
         const int32_t o = od[t];
         if (o) atomicAdd(&a.odd[r], (unsigned long long)(long long)o);
     }
-    if (WM >= 2)
+    if (WM == 2)
         for (int t = threadIdx.x; t < 3 * nslot; t += blockDim.x) {
             const unsigned long long lo = wl[2 * t], hi = wl[2 * t + 1];
-            const int w = WM == 3 ? 3 * rank_of[t / 3] + t % 3 : t;
-            if (lo | hi) add_u128_pair(wg + 2 * w, lo, hi);
+            if (lo | hi) add_u128_pair(wg + 2 * t, lo, hi);
+        }
+    if (WM == 3)  // (E, O) of a slot goes in as A+ += O, A0 += E - O: the same even and odd sums
+        for (int t = threadIdx.x; t < nslot; t += blockDim.x) {
+            const unsigned long long e0 = wl[4 * t], e1 = wl[4 * t + 1];
+            const unsigned long long o0 = wl[4 * t + 2], o1 = wl[4 * t + 3];
+            const unsigned long long d0 = e0 - o0, d1 = e1 - o1 - (e0 < o0 ? 1ull : 0ull);
+            const int w = 3 * rank_of[t];
+            if (o0 | o1) add_u128_pair(wg + 2 * w, o0, o1);
+            if (d0 | d1) add_u128_pair(wg + 2 * (w + 2), d0, d1);
         }
 }
 
@@ -814,6 +848,16 @@ __global__ void k_every_nth(const int32_t *__restrict__ hubs, int64_t n, int str
     if (t * stride < n) out[t] = hubs[t * stride];
 }
 
+// s4rank[key] |= (slot[rank] + 1) << kSlotShift for the cached configurations
+__global__ void k_s4_attach_slots(uint32_t *__restrict__ s4rank, int64_t nkeys,
+                                  const int16_t *__restrict__ slot) {
+    const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (t >= nkeys) return;
+    const uint32_t r = s4rank[t] & kRankMask;
+    const int sl = slot[r];
+    if (sl >= 0) s4rank[t] = r | ((uint32_t)(sl + 1) << kSlotShift);
+}
+
 static int weighted_copies(int64_t ncfg) {
     const int64_t per_copy = 48 * ncfg;  // [ncfg][3] 128-bit words
     int64_t c = std::min<int64_t>(256, std::max<int64_t>(1, ((int64_t)256 << 20) / per_copy));
@@ -879,17 +923,19 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
                     static_lds0 + fixed_u + per_u <= (size_t)ldsmax;
     if (const char *env = std::getenv("GTC_CONFIG_CACHE"))  // "off": global sums only (tests)
         if (std::strcmp(env, "off") == 0) cache_ok = false;
-    // GTC_CACHE_WAVES=w: waves per workgroup beside the cache (default 6, else 3; fewer waves
+    // GTC_CACHE_WAVES=w: waves per workgroup beside the cache (default 10, else 5; fewer waves
     // leave room for more cached configurations, whose tetrahedra then add in LDS)
-    int w_first = 6;
+    int w_first = 10;
     if (const char *env = std::getenv("GTC_CACHE_WAVES"))
         w_first = std::max(1, std::min(16, std::atoi(env)));
     if (cache_ok)
-        for (int w = w_first; w >= std::min(3, w_first) && !cache_k; w >>= 1) {
-            const size_t used = static_lds0 + (size_t)w * per + 4 * kRankTab + align16(2 * (size_t)ncfg);
+        for (int w = w_first; w >= std::min(4, w_first) && !cache_k; w >>= 1) {
+            const size_t used = static_lds0 + (size_t)w * per + 4 * kRankTab +
+                                (s4 ? 0 : align16(2 * (size_t)ncfg));
             if (used >= (size_t)ldsmax) continue;
-            int64_t k = std::min<int64_t>({ncfg, (int64_t)32767, (int64_t)((ldsmax - used) / 60)});
-            while (k > 0 && static_lds0 + clique_lds_fixed(a.ncfg, false, false, (int)k) + w * per >
+            int64_t k = std::min<int64_t>({ncfg, (int64_t)(s4 ? kMaxTableSlots : 32767),
+                                           (int64_t)((ldsmax - used) / 44)});
+            while (k > 0 && static_lds0 + clique_lds_fixed(a.ncfg, false, false, (int)k, !s4) + w * per >
                                 (size_t)ldsmax)
                 --k;
             if (k >= kCacheMin) {
@@ -897,7 +943,8 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
                 cache_waves = w;
             }
         }
-    size_t fixed = cache_k ? clique_lds_fixed(a.ncfg, false, false, cache_k) : clique_lds_fixed(a.ncfg, GH, WL);
+    size_t fixed = cache_k ? clique_lds_fixed(a.ncfg, false, false, cache_k, !s4)
+                           : clique_lds_fixed(a.ncfg, GH, WL);
     // Workgroups of 4 waves; a large LDS histogram (S4 configurations) allows one workgroup per
     // CU, which then takes as many waves (up to 16) as the LDS beside the histogram holds.
     const size_t static_lds = sizeof(int64_t) * (GTC_MAX_BINS_4PCF + 1);
@@ -1068,9 +1115,15 @@ int count_4pcf_device(gtc_graph_s *G, uint64_t *d_even, int64_t *d_odd, gtc_stat
             hipError_t e = hipMemcpyAsync(cache_slot, slot.data(), 2 * ncfg, hipMemcpyHostToDevice, s);
             if (e == hipSuccess)
                 e = hipMemcpyAsync(cache_rank, order.data(), 4 * (size_t)cache_k, hipMemcpyHostToDevice, s);
+            if (e == hipSuccess && s4) {  // the slots into the rank table
+                hipLaunchKernelGGL(k_s4_attach_slots, dim3((unsigned)((nkeys + 255) / 256)), dim3(256),
+                                   0, s, s4rank, (int64_t)nkeys, cache_slot);
+                e = hipGetLastError();
+            }
             if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host vectors go out of scope
             if (e != hipSuccess) rc = hip_fail(e, "4pCF cache tables", __FILE__, __LINE__);
-            fixed = clique_lds_fixed(a.ncfg, false, false, cache_k);
+            fixed = clique_lds_fixed(a.ncfg, false, false, cache_k, !s4);
+            a.slot_in_rank = s4 ? 1 : 0;
             lds = fixed + waves * per;
             a.cache_k = cache_k;
             a.cache_slot = cache_slot;
