@@ -214,6 +214,13 @@ def test_plan_windows_partitions_rows_greedily():
                               out.ctypes.data_as(C.c_void_p)) == gtc.GTC_E_INVALID
 
 
+def test_graph_windows_rejects_a_null_graph():
+    L = gtc.lib()
+    out = np.zeros(4, np.int64)
+    assert L.gtc_graph_windows(None, None, None, 0) == gtc.GTC_E_INVALID
+    assert L.gtc_graph_windows(None, out.ctypes.data_as(C.c_void_p), None, 4) == gtc.GTC_E_INVALID
+
+
 @pytest.mark.parametrize("rmin,rmax,nb", [(0, 1000, 3), (7, 31, 4), (1, 100, 16), (3, 4, 1),
                                           (50_000, 1 << 21, 255), (0, 1 << 21, 7)])
 def test_linear_edges_sq_matches_the_oracle(rmin, rmax, nb):
