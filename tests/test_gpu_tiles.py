@@ -50,6 +50,8 @@ def test_tiled_equals_resident_and_oracle(gpu_available, monkeypatch, kind, seed
         assert st["windows"] > 1 and 1 <= st["tiles"]
         if csr_mode == "device":
             assert st["tiles"] <= st["windows"]
+        elif frac == 1 / 40:  # hub windows whose spokes reach past the next window: extra launches
+            assert st["tiles"] > st["windows"]
         np.testing.assert_array_equal(c, c0)
         if weighted:
             np.testing.assert_array_equal(ws, w0)
