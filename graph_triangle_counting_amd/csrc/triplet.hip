@@ -336,8 +336,9 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 int32_t mo;
                 int32_t mob = 0;  // flat walk: byte offset of the label's map entry
                 if constexpr (BANDED) {
-                    mo = k - blo;  // k = -1 (no element) falls outside as well
-                    if ((uint32_t)mo >= (uint32_t)bsize) return 0u;
+                    // a label outside the band (and k = -1, no element) reads the zero entry
+                    // kept at bsize: a clamp instead of a branch
+                    mo = (int32_t)min((uint32_t)(k - blo), (uint32_t)bsize);
                 } else {
                     if ((uint32_t)k > (uint32_t)hub_hi) return 0u;  // past the hub's last neighbour
                     // run of k from the run starts (nondecreasing), as sums of differences:
@@ -359,7 +360,11 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 const int32_t bij = ow >> 8;
                 const int32_t bik = W ? (int32_t)(v >> 16) : (int32_t)v - 1;
                 if constexpr (UH) {
-                    atomicAdd(&hc[(bij * nbk + bik) * nbk + bjk], 1u);
+                    // (bins below 2^8: 24-bit multiplies, full rate, where a 32-bit multiply
+                    // issues at a quarter)
+                    const uint32_t nb8 = (uint32_t)nbk & 0xffu;
+                    atomicAdd(&hc[__umul24(__umul24((uint32_t)bij & 0xffu, nb8) + (uint32_t)bik, nb8) +
+                                  (uint32_t)bjk], 1u);
                     ++my_hits;
                     return;
                 }
@@ -481,7 +486,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 for (int t = 1; t < 5; ++t)
                     if (bq == t) { blo = dom.lo[t]; bhi = dom.hi[t]; }
                 const int32_t bsize = bhi - blo;
-                const int map_words = W ? bsize : (bsize + 3) >> 2;
+                const int map_words = W ? bsize + 1 : (bsize + 4) >> 2;  // (and the entry at bsize)
                 for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
                 wave_lds_sync();
                 for (int p = hp_lo + lane; p < hp_hi; p += kWave) {
@@ -742,7 +747,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     if (banded) band_table(G->grid.g, a.band);
     a.slot_off = G->slot_off;
     a.max_m = (int32_t)std::max<int64_t>(G->max_deg, 1);
-    const int64_t map_labels = std::max<int64_t>(banded ? G->max_band : G->max_domain, 1);
+    // (banded: one more entry, the zero entry past the band that out-of-band labels read)
+    const int64_t map_labels = std::max<int64_t>(banded ? G->max_band + 1 : G->max_domain, 1);
     a.map_bytes = (int32_t)align_up(map_entry_bytes(W) * (size_t)map_labels, 16);
     a.wave_bytes = (int32_t)(a.map_bytes + chunk_bytes(W) + hubrow_bytes(W, a.max_m));
     if (W && G->max_deg >= 65535) {
