@@ -219,6 +219,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     unsigned long long *const g_limbs = a.limbs;
     const double two_s = a.two_s;
     const int32_t nbk = a.nb;
+    const uint32_t nb4 = 4u * ((uint32_t)nbk & 0xffu);  // (bins below 2^8)
     if constexpr (BANDED)
         for (int t = threadIdx.x; t < 145; t += blockDim.x) btab[t] = a.band[t];
     __syncthreads();
@@ -319,7 +320,13 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             int32_t qend = (int32_t)cpre[q + 1];
             const int32_t *cp = col_s + cbase[q];  // flat element t is cp[t]
             const uint8_t *bp = PK ? nullptr : bin_s + cbase[q];
-            int32_t own = q | ((int32_t)cbij[q] << 8);  // owner spoke and its bin
+            // owner spoke and its bin; for the histogram over unsorted triples the owner's byte
+            // offset in it instead, 4 ((b_ij nb - 1) nb), so that a hit adds 4 (v nb + b_jk)
+            auto owner_word = [&](int qq_) __attribute__((always_inline)) -> int32_t {
+                if constexpr (UH) return ((int32_t)cbij[qq_] * nbk - 1) * nbk * 4;
+                else return qq_ | ((int32_t)cbij[qq_] << 8);
+            };
+            int32_t own = owner_word(q);
             auto seek = [&](int32_t t) __attribute__((always_inline)) {
                 if (t >= qend) {
                     do {
@@ -328,7 +335,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     } while (t >= qend);
                     cp = col_s + cbase[q];
                     if (!PK) bp = bin_s + cbase[q];
-                    own = q | ((int32_t)cbij[q] << 8);
+                    own = owner_word(q);
                 }
             };
             // the label's map entry, 0 when it is no neighbour of the hub
@@ -357,17 +364,16 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             };
             auto hit = [&](int32_t bjk, int32_t ow, uint32_t v) __attribute__((always_inline)) {
                 if (!v) return;
-                const int32_t bij = ow >> 8;
-                const int32_t bik = W ? (int32_t)(v >> 16) : (int32_t)v - 1;
                 if constexpr (UH) {
-                    // (bins below 2^8: 24-bit multiplies, full rate, where a 32-bit multiply
-                    // issues at a quarter)
-                    const uint32_t nb8 = (uint32_t)nbk & 0xffu;
-                    atomicAdd(&hc[__umul24(__umul24((uint32_t)bij & 0xffu, nb8) + (uint32_t)bik, nb8) +
-                                  (uint32_t)bjk], 1u);
+                    // bin (b_ij nb + b_ik) nb + b_jk at byte ow + 4 (v nb + b_jk), v = b_ik + 1:
+                    // a 24-bit multiply-add (full rate; a 32-bit multiply issues at a quarter)
+                    const uint32_t off = (uint32_t)ow + __umul24(v & 0xffu, nb4) + ((uint32_t)bjk << 2);
+                    atomicAdd(reinterpret_cast<uint32_t *>(reinterpret_cast<unsigned char *>(hc) + off), 1u);
                     ++my_hits;
                     return;
                 }
+                const int32_t bij = ow >> 8;
+                const int32_t bik = W ? (int32_t)(v >> 16) : (int32_t)v - 1;
                 const int32_t x = min(bij, min(bik, bjk)), z = max(bij, max(bik, bjk));
                 const int32_t y = bij + bik + bjk - x - z;
                 const int32_t c = rA[x] + rB[y] + z;
