@@ -220,6 +220,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     const double two_s = a.two_s;
     const int32_t nbk = a.nb;
     const uint32_t nb4 = 4u * ((uint32_t)nbk & 0xffu);  // (bins below 2^8)
+    const uint32_t nb4sq = nb4 * ((uint32_t)nbk & 0xffu);
     if constexpr (BANDED)
         for (int t = threadIdx.x; t < 145; t += blockDim.x) btab[t] = a.band[t];
     __syncthreads();
@@ -323,7 +324,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             // owner spoke and its bin; for the histogram over unsorted triples the owner's byte
             // offset in it instead, 4 ((b_ij nb - 1) nb), so that a hit adds 4 (v nb + b_jk)
             auto owner_word = [&](int qq_) __attribute__((always_inline)) -> int32_t {
-                if constexpr (UH) return ((int32_t)cbij[qq_] * nbk - 1) * nbk * 4;
+                if constexpr (UH)  // (24-bit multiply: full rate)
+                    return (int32_t)__umul24((uint32_t)cbij[qq_], nb4sq) - (int32_t)nb4;
                 else return qq_ | ((int32_t)cbij[qq_] << 8);
             };
             int32_t own = owner_word(q);
