@@ -65,7 +65,8 @@ struct TripletArgs {
     unsigned int batch_cap;      // largest batch of hubs per take
     unsigned long long *counts;  // [ncfg]
     unsigned long long *limbs;   // [ncfg][4]: 128-bit sum of low limbs, 128-bit sum of high limbs
-    unsigned int flush_at;       // hits a wave may add between exchanges of the LDS histogram
+    unsigned int flush_at;       // hits (unsorted histogram: walked elements) a wave may add
+                                 // between exchanges of the LDS histogram
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -117,16 +118,26 @@ __device__ __forceinline__ void flush_hist(int ncfg, unsigned long long *counts,
     }
 }
 
-// The same for a histogram over the unsorted bin triple t = (b0 nb + b1) nb + b2 (nb^3 bins):
-// each bin is added to the rank of its sorted triple.
+// Rows of the histogram over unsorted bin triples (one per b_jk), padded so that the rows of one
+// spoke's hits start in different LDS banks: with at most 16 bins a row's b_ik cover at most half
+// of the 32 banks and consecutive rows start nb banks apart (nb^2 padded to nb modulo 32); with
+// more bins an odd row length suffices.
+__host__ __device__ inline int unsorted_row(int nb) {
+    return nb <= 16 ? nb * nb + (nb - nb * nb % 32 + 32) % 32 : nb * nb | 1;
+}
+
+// The same for a histogram over the unsorted bin triple t = b0 unsorted_row(nb) + b1 nb + b2
+// (nb rows): each bin is added to the rank of its sorted triple.
 __device__ __forceinline__ void flush_hist_unsorted(int nb, unsigned long long *counts, uint32_t *hu,
                                                     const int32_t *rA, const int32_t *rB, int first,
                                                     int step) {
-    const int nh = nb * nb * nb;
+    const int row = unsorted_row(nb), nh = nb * row;
     for (int t = first; t < nh; t += step) {
+        const int r = t % row;
+        if (r >= nb * nb) continue;  // (the padding bin)
         const uint32_t v = atomicExch(&hu[t], 0u);
         if (!v) continue;
-        const int b0 = t / (nb * nb), b1 = (t / nb) % nb, b2 = t % nb;
+        const int b0 = t / row, b1 = r / nb, b2 = r % nb;
         const int x = min(b0, min(b1, b2)), z = max(b0, max(b1, b2)), y = b0 + b1 + b2 - x - z;
         atomicAdd(&counts[rA[x] + rB[y] + z], (unsigned long long)v);
     }
@@ -174,11 +185,14 @@ constexpr size_t kBandTableBytes = 160;
 template <bool W, bool GH, bool BANDED, bool PK, bool UH>
 __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     static_assert(!UH || (!W && !GH), "the unsorted histogram is an unweighted LDS histogram");
+    // The unweighted banded walk over packed entries keeps each element's whole entry, which the
+    // probe and the hit take apart.
+    constexpr bool kRawEntry = BANDED && PK && !W;
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     size_t off = 0;
     uint32_t *hc = reinterpret_cast<uint32_t *>(smem);
-    const int32_t nhist = UH ? a.nb * a.nb * a.nb : a.ncfg;
+    const int32_t nhist = UH ? a.nb * unsorted_row(a.nb) : a.ncfg;
     if (!GH) off += align_up(sizeof(uint32_t) * nhist, 16);
     unsigned long long *hlo = nullptr, *hhi = nullptr;
     if (W && !GH) {
@@ -194,6 +208,11 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     off += kBandTableBytes;
     unsigned char *wb = smem + off + (size_t)wid * a.wave_bytes;
     uint8_t *map8 = wb;
+    // the wave's map as an LDS address
+    typedef __attribute__((address_space(3))) unsigned char lds_u8;
+    typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    const int32_t map_off = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)wb;
+    const int32_t hc_lds = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)smem;  // the histogram's LDS address
     uint32_t *mapw = reinterpret_cast<uint32_t *>(wb);
     unsigned char *ck = wb + a.map_bytes;
     uint32_t *cpre = reinterpret_cast<uint32_t *>(ck + kChunkPre);
@@ -220,7 +239,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     const double two_s = a.two_s;
     const int32_t nbk = a.nb;
     const uint32_t nb4 = 4u * ((uint32_t)nbk & 0xffu);  // (bins below 2^8)
-    const uint32_t nb4sq = nb4 * ((uint32_t)nbk & 0xffu);
+    const uint32_t row4 = 4u * ((uint32_t)unsorted_row(nbk) & 0xffffu);  // (below 2^16)
     if constexpr (BANDED)
         for (int t = threadIdx.x; t < 145; t += blockDim.x) btab[t] = a.band[t];
     __syncthreads();
@@ -275,6 +294,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         }
 
         unsigned int my_hits = 0;
+        uint32_t hub_elems = 0;  // (unsorted histogram) elements walked, a bound on its hits
         // run bounds as plain scalars (a select over the arrays is lowered to a stack copy)
         const int32_t l1 = dom.lo[1], l2 = dom.lo[2], l3 = dom.lo[3], l4 = dom.lo[4];
         const int32_t d0 = dom.delta[0], d1 = dom.delta[1], d2 = dom.delta[2], d3 = dom.delta[3],
@@ -295,9 +315,11 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         // [blo, blo + bsize); otherwise it holds the whole domain, found by comparisons.
         auto walk = [&](int32_t p0, int64_t sb, int32_t len, int32_t bj, int32_t blo,
                         int32_t bsize) __attribute__((always_inline)) {
+            const int32_t band_c = blo - map_off - 1, band_hi = map_off + bsize + 1;
             const int32_t incl = wave_incl_scan(len, lane);
             const int32_t total = __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1, kWave));
             if (total == 0) return;
+            if (UH) hub_elems += (uint32_t)total;
             cpre[lane] = (uint32_t)(incl - len);
             if (lane == kWave - 1) cpre[kWave] = (uint32_t)incl;
             cbase[lane] = sb - (sb >= e_split ? base_s2 : base_s) - (incl - len);
@@ -318,25 +340,38 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     if ((int32_t)cpre[md] <= lane) q = md; else hi = md;
                 }
             }
+            // The lanes take flat elements t = T + lane, T uniform.  Element T + lane is cpl[T]: the
+            // owner's row pointer with the lane folded in, so that a block's loads are one pointer
+            // and immediate offsets; the owner changes once T reaches qrel.
             int32_t qend = (int32_t)cpre[q + 1];
-            const int32_t *cp = col_s + cbase[q];  // flat element t is cp[t]
-            const uint8_t *bp = PK ? nullptr : bin_s + cbase[q];
-            // owner spoke and its bin; for the histogram over unsorted triples the owner's byte
-            // offset in it instead, 4 ((b_ij nb - 1) nb), so that a hit adds 4 (v nb + b_jk)
+            int32_t qrel = qend - lane;
+            const int32_t *cpl = col_s + cbase[q] + lane;
+            const uint8_t *bpl = PK ? nullptr : bin_s + cbase[q] + lane;
+            // owner spoke and its bin; for the histogram over unsorted triples the LDS address of
+            // the owner's histogram row instead, less 4: 4 b_ij nb - 4 past row 0, so that a hit
+            // adds its map entry 4 (b_ik + 1) and 4 b_jk row
             auto owner_word = [&](int qq_) __attribute__((always_inline)) -> int32_t {
                 if constexpr (UH)  // (24-bit multiply: full rate)
-                    return (int32_t)__umul24((uint32_t)cbij[qq_], nb4sq) - (int32_t)nb4;
+                    return (int32_t)__umul24((uint32_t)cbij[qq_], nb4) + hc_lds - 4;
                 else return qq_ | ((int32_t)cbij[qq_] << 8);
             };
             int32_t own = owner_word(q);
-            auto seek = [&](int32_t t) __attribute__((always_inline)) {
-                if (t >= qend) {
+            // the owner of element T + lane, and the block pointers cb, bb_ of a block at t0
+            auto seek = [&](int32_t T, int32_t t0, const int32_t *&cb, const uint8_t *&bb_)
+                            __attribute__((always_inline)) {
+                if (T >= qrel) {
+                    const int32_t t = T + lane;
                     do {
                         ++q;
                         qend = (int32_t)cpre[q + 1];
                     } while (t >= qend);
-                    cp = col_s + cbase[q];
-                    if (!PK) bp = bin_s + cbase[q];
+                    qrel = qend - lane;
+                    cpl = col_s + cbase[q] + lane;
+                    cb = cpl + t0;
+                    if (!PK) {
+                        bpl = bin_s + cbase[q] + lane;
+                        bb_ = bpl + t0;
+                    }
                     own = owner_word(q);
                 }
             };
@@ -344,10 +379,29 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             auto probe = [&](int32_t k) __attribute__((always_inline)) -> uint32_t {
                 int32_t mo;
                 int32_t mob = 0;  // flat walk: byte offset of the label's map entry
-                if constexpr (BANDED) {
-                    // a label outside the band (and k = -1, no element) reads the zero entry
-                    // kept at bsize: a clamp instead of a branch
-                    mo = (int32_t)min((uint32_t)(k - blo), (uint32_t)bsize);
+                if constexpr (BANDED && !W) {
+                    // label k's entry is byte 1 + k - blo of the map, between zero entries at 0
+                    // and bsize + 1: a label outside the band (and k = -1, no element) is clamped
+                    // onto one of them (a three-operand median, no branch).  As LDS addresses,
+                    // with the wave's map address folded into the bounds.
+                    // (the compiler forms no median from a min and a max of variables)
+                    if constexpr (PK) {
+                        // k is the whole packed entry: a 24-bit multiply-add by one takes its
+                        // label (the low 24 bits) less the band start in one instruction
+                        asm("v_mad_u32_u24 %0, %1, 1, %2\n\tv_med3_i32 %0, %0, %3, %4"
+                            : "=&v"(mo)
+                            : "v"(k), "v"(-band_c), "v"(map_off), "v"(band_hi));
+                    } else {
+                        const int32_t x = (int32_t)((uint32_t)k - (uint32_t)band_c);
+                        asm("v_med3_i32 %0, %1, %2, %3" : "=v"(mo) : "v"(x), "v"(map_off), "v"(band_hi));
+                    }
+                    uint32_t e = *(const lds_u8 *)(uintptr_t)(uint32_t)mo;
+                    // (kept a 32-bit value: a 16-bit compare would need a zero extension for the hit)
+                    if constexpr (UH) asm("" : "+v"(e));
+                    return e;
+                } else if constexpr (BANDED) {
+                    // a label outside the band (and k = -1, no element) reads a zero entry
+                    mo = 1 + (int32_t)min((uint32_t)(k - blo), (uint32_t)bsize);
                 } else {
                     if ((uint32_t)k > (uint32_t)hub_hi) return 0u;  // past the hub's last neighbour
                     // run of k from the run starts (nondecreasing), as sums of differences:
@@ -361,17 +415,23 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     mob = k * kMapEntry + d0b + (r1 ? e1b : 0) + (r2 ? e2b : 0) + (r3 ? e3b : 0) +
                           (r4 ? e4b : 0);
                 }
-                if constexpr (BANDED) return W ? mapw[mo] : (uint32_t)map8[mo];
+                if constexpr (BANDED) return mapw[mo];
                 else return W ? *reinterpret_cast<const uint32_t *>(map8 + mob) : (uint32_t)map8[mob];
             };
             auto hit = [&](int32_t bjk, int32_t ow, uint32_t v) __attribute__((always_inline)) {
                 if (!v) return;
                 if constexpr (UH) {
-                    // bin (b_ij nb + b_ik) nb + b_jk at byte ow + 4 (v nb + b_jk), v = b_ik + 1:
-                    // a 24-bit multiply-add (full rate; a 32-bit multiply issues at a quarter)
-                    const uint32_t off = (uint32_t)ow + __umul24(v & 0xffu, nb4) + ((uint32_t)bjk << 2);
-                    atomicAdd(reinterpret_cast<uint32_t *>(reinterpret_cast<unsigned char *>(hc) + off), 1u);
-                    ++my_hits;
+                    // bin b_jk row + b_ij nb + b_ik at LDS address ow + v + 4 b_jk row, v = 4 (b_ik + 1):
+                    // one 24-bit multiply (full rate; a 32-bit multiply issues at a quarter).  Hits
+                    // are not counted: the walked elements bound them.
+                    uint32_t off;
+                    if constexpr (kRawEntry)  // b_jk is the entry's top byte: a byte-select multiply
+                        asm("v_mul_u32_u24_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD "
+                            "src0_sel:DWORD src1_sel:BYTE_3\n\tv_add3_u32 %0, %0, %3, %4"
+                            : "=&v"(off)
+                            : "s"(row4), "v"(bjk), "v"(ow), "v"(v));
+                    else off = ((uint32_t)bjk & 0xffu) * row4 + (uint32_t)ow + v;
+                    atomicAdd((uint32_t *)(lds_u32 *)(uintptr_t)off, 1u);
                     return;
                 }
                 const int32_t bij = ow >> 8;
@@ -406,8 +466,9 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             auto process_block = [&](const int32_t *kk, const int32_t *bb, const int32_t *qq)
                                      __attribute__((always_inline)) {
                 if constexpr (BANDED) {
+                    // (the raw packed entry stands for its bin in the unsorted-histogram hit)
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) hit(bb[u], qq[u], probe(kk[u]));
+                    for (int u = 0; u < kUnroll; ++u) hit(kRawEntry && UH ? kk[u] : bb[u], qq[u], probe(kk[u]));
                 } else {  // every probe of the block first, then the hits
                     uint32_t vv[kUnroll];
 #pragma unroll
@@ -416,31 +477,46 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     for (int u = 0; u < kUnroll; ++u) hit(bb[u], qq[u], vv[u]);
                 }
             };
+            // element u kWave + lane of a block at cb, bb_: its label and bin (kRawEntry: the whole
+            // entry); kNone is no element (a label past the band: 2^24 at most, whose low 24 bits
+            // fall below the band).
+            auto load_elem = [&](const int32_t *cb, const uint8_t *bb_, int u, int32_t &k, int32_t &b)
+                                 __attribute__((always_inline)) {
+                if constexpr (kRawEntry) {
+                    k = cb[u * kWave];
+                    b = (int32_t)((uint32_t)k >> 24);
+                } else {
+                    csr_entry<PK>(cb, bb_, u * kWave, k, b);
+                }
+            };
+            const int32_t kNone = kRawEntry ? blo + bsize : -1;
             // whole blocks of kWave * kUnroll elements need no bounds checks; then one checked tail
             int32_t t0 = 0;
             for (; t0 + kWave * kUnroll <= total; t0 += kWave * kUnroll) {
                 int32_t kk[kUnroll], bb[kUnroll], qq[kUnroll];
+                const int32_t *cb = cpl + t0;
+                const uint8_t *bb_ = PK ? nullptr : bpl + t0;
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    const int32_t t = t0 + u * kWave + lane;
-                    seek(t);
+                    seek(t0 + u * kWave, t0, cb, bb_);
                     qq[u] = own;
-                    csr_entry<PK>(cp, bp, (uint32_t)t, kk[u], bb[u]);
+                    load_elem(cb, bb_, u, kk[u], bb[u]);
                 }
                 process_block(kk, bb, qq);
             }
             if (t0 < total) {
                 int32_t kk[kUnroll], bb[kUnroll], qq[kUnroll];
+                const int32_t *cb = cpl + t0;
+                const uint8_t *bb_ = PK ? nullptr : bpl + t0;
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    const int32_t t = t0 + u * kWave + lane;
-                    kk[u] = -1;
+                    kk[u] = kNone;
                     bb[u] = 0;
                     qq[u] = own;
-                    if (t < total) {
-                        seek(t);
+                    if (lane < total - (t0 + u * kWave)) {
+                        seek(t0 + u * kWave, t0, cb, bb_);
                         qq[u] = own;
-                        csr_entry<PK>(cp, bp, (uint32_t)t, kk[u], bb[u]);
+                        load_elem(cb, bb_, u, kk[u], bb[u]);
                     }
                 }
                 process_block(kk, bb, qq);
@@ -460,7 +536,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 const int32_t d = d0 + (k >= l1 ? e1 : 0) + (k >= l2 ? e2 : 0) + (k >= l3 ? e3 : 0) +
                                   (k >= l4 ? e4 : 0);
                 if (W) mapw[k + d] = (uint32_t)(p + 1) | ((uint32_t)bk << 16);
-                else map8[k + d] = (uint8_t)(bk + 1);
+                else map8[k + d] = (uint8_t)(UH ? 4 * (bk + 1) : bk + 1);
             }
             wave_lds_sync();
             for (int32_t p0 = p_lo; p0 < p_hi; p0 += kWave) {
@@ -494,14 +570,15 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 for (int t = 1; t < 5; ++t)
                     if (bq == t) { blo = dom.lo[t]; bhi = dom.hi[t]; }
                 const int32_t bsize = bhi - blo;
-                const int map_words = W ? bsize + 1 : (bsize + 4) >> 2;  // (and the entry at bsize)
+                // (and the zero entries at 0 and bsize + 1)
+                const int map_words = W ? bsize + 2 : (bsize + 5) >> 2;
                 for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
                 wave_lds_sync();
                 for (int p = hp_lo + lane; p < hp_hi; p += kWave) {
                     int32_t k, bk;
                     csr_entry<PK>(hrow, hbin, p, k, bk);
-                    if (W) mapw[k - blo] = (uint32_t)(p + 1) | ((uint32_t)bk << 16);
-                    else map8[k - blo] = (uint8_t)(bk + 1);
+                    if (W) mapw[1 + k - blo] = (uint32_t)(p + 1) | ((uint32_t)bk << 16);
+                    else map8[1 + k - blo] = (uint8_t)(UH ? 4 * (bk + 1) : bk + 1);
                 }
                 wave_lds_sync();
                 for (int32_t p0 = p_lo; p0 < sp_hi; p0 += kWave) {
@@ -529,7 +606,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         }
 
         if (!GH) {
-            wave_hits += wave_sum(my_hits);
+            wave_hits += UH ? hub_elems : wave_sum(my_hits);
             if (wave_hits >= a.flush_at) {
                 if (UH) flush_hist_unsorted(nbk, g_counts, hc, rA, rB, lane, kWave);
                 else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, lane, kWave);
@@ -547,7 +624,8 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-constexpr int kUnsortedMaxBins = 32;  // nb^3 32-bit bins: at most 128 KB of LDS
+constexpr int kUnsortedMaxBins = 32;  // nb (nb^2 + 1) 32-bit bins: at most 129 KB of LDS
+static_assert(4 * kUnsortedMaxBins <= 255, "map entries 4 (bin + 1) are bytes");
 
 struct DeviceLimits {
     int cus = 0;
@@ -756,7 +834,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.slot_off = G->slot_off;
     a.max_m = (int32_t)std::max<int64_t>(G->max_deg, 1);
     // (banded: one more entry, the zero entry past the band that out-of-band labels read)
-    const int64_t map_labels = std::max<int64_t>(banded ? G->max_band + 1 : G->max_domain, 1);
+    // banded: the band and a zero entry on each side
+    const int64_t map_labels = std::max<int64_t>(banded ? G->max_band + 2 : G->max_domain, 1);
     a.map_bytes = (int32_t)align_up(map_entry_bytes(W) * (size_t)map_labels, 16);
     a.wave_bytes = (int32_t)(a.map_bytes + chunk_bytes(W) + hubrow_bytes(W, a.max_m));
     if (W && G->max_deg >= 65535) {
@@ -816,12 +895,16 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             (unsigned long long)G->max_deg * (unsigned long long)(G->max_deg - 1) / 2;
         const bool GH = triplet_lds_fixed(a.ncfg, W, false) > dl.lds_per_block / 2 ||
                         max_hub_hits >= 0x7fffffffull / 2;
-        // Unweighted with at most 16 bins: histogram over the unsorted bin triple (nb^3 <= 4096
-        // bins) when the spoke elements per CU amortise folding nb^3 bins per workgroup.
+        // Unweighted with at most 32 bins: histogram over the unsorted bin triple (nb^3 <= 32768
+        // bins) when the spoke elements per CU amortise folding nb^3 bins per workgroup.  Its
+        // exchange budget counts walked elements (at most max_deg^2 per hub), not hits.
         // GTC_TRIPLET_HIST=unsorted or sorted forces the choice (unsorted needs the same limits).
         const int64_t walk_elems = sub ? sub->spoke_elements : G->spoke_elements;
         const int64_t nb3 = (int64_t)nb * nb * nb;
-        const bool uh_ok = !W && !GH && nb <= kUnsortedMaxBins;
+        const unsigned long long max_hub_elems =
+            (unsigned long long)G->max_deg * (unsigned long long)G->max_deg;
+        const bool uh_ok = !W && !GH && nb <= kUnsortedMaxBins &&
+                           max_hub_elems < (0xffffffffull / 16) / 2;
         bool UH = uh_ok && walk_elems >= nb3 * 1024 * (int64_t)dl.cus;
         if (const char *env = std::getenv("GTC_TRIPLET_HIST")) {
             if (!std::strcmp(env, "unsorted")) UH = uh_ok;
@@ -829,11 +912,12 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         }
         TripletPlan pl;
         const void *kfn = triplet_kernel(W, GH, banded, G->packed, UH);
-        TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(UH ? (int)nb3 : a.ncfg, W, GH), GH, hub_total,
-                           max_hub_hits, pl));
+        const unsigned long long max_hub_adds = UH ? max_hub_elems : max_hub_hits;
+        const int nhist = UH ? nb * unsorted_row(nb) : a.ncfg;
+        TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(nhist, W, GH), GH, hub_total, max_hub_adds, pl));
         // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long budget = 0xffffffffull / (unsigned long long)pl.waves;
-        a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub_hits);
+        a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub_adds);
         // GTC_TRIPLET_FLUSH_AT=n exchanges the LDS histogram at least every n hits of a wave
         if (const char *env = std::getenv("GTC_TRIPLET_FLUSH_AT")) {
             const long long v = std::atoll(env);
