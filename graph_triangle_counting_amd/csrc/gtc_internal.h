@@ -239,24 +239,30 @@ int hub_class_counts(const int32_t *hubs, int64_t n_hubs, const int64_t *row_ptr
 
 // Per-wave view of the class queue.  Every lane holds the hub-list range of class `lane`.
 struct HubQueue {
-    uint32_t cbeg, cend;  // lane c: positions [cbeg, cend) of class c
+    uint32_t cbeg, cend;  // lane c: queue entries [cbeg, cend) of class c
+    uint32_t hbeg;        // lane c: hub-list position of class c's first hub
     uint32_t pos, end;    // current batch (wave-uniform)
     int cls;              // current class (wave-uniform)
     int tried;            // parts of the current class drained so far (wave-uniform)
     int home;             // first part to take from
     uint32_t cap;         // batch cap of this launch
 
+    // (mult: queue entries per hub of class `lane`)
     __device__ __forceinline__ void init(const uint32_t *counts, uint32_t batch_cap, int lane,
-                                         int home_part) {
-        const uint32_t c = counts[lane];
-        uint32_t incl = c;
+                                         int home_part, uint32_t mult = 1) {
+        const uint32_t h = counts[lane], c = h * mult;
+        uint32_t incl = c, hincl = h;
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
-            const uint32_t o = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += o;
+            const uint32_t o = __shfl_up(incl, d, kWave), ho = __shfl_up(hincl, d, kWave);
+            if (lane >= d) {
+                incl += o;
+                hincl += ho;
+            }
         }
         cbeg = incl - c;
         cend = incl;
+        hbeg = hincl - h;
         pos = end = 0;
         cls = 0;
         tried = 0;
@@ -294,6 +300,27 @@ struct HubQueue {
         }
         hq = pos++;
         return true;
+    }
+
+    // Hub-list position of entry hq of the current class, one entry per hub (init's mult 1).
+    __device__ __forceinline__ uint32_t hub_pos(uint32_t hq) const {
+        const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)cbeg, cls);
+        return (uint32_t)__builtin_amdgcn_readlane((int)hbeg, cls) + (hq - b);
+    }
+
+    // Entry hq of the current class when each of its hubs has `parts` entries (init's mult for
+    // the class), taken group by group: the entries of a group of g hubs are its hubs' part 0,
+    // then their part 1, and so on.  The hub's hub-list position and the part (wave-uniform).
+    __device__ __forceinline__ void split(uint32_t hq, uint32_t parts, uint32_t g, uint32_t &hpos,
+                                          uint32_t &part) const {
+        const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)cbeg, cls);
+        const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)cend, cls);
+        const uint32_t hb = (uint32_t)__builtin_amdgcn_readlane((int)hbeg, cls);
+        const uint32_t nh = (e - b) / parts, t = hq - b;
+        const uint32_t grp = t / (parts * g), r = t - grp * parts * g;
+        const uint32_t gsz = nh - grp * g < g ? nh - grp * g : g;
+        part = r / gsz;
+        hpos = hb + grp * g + (r - part * gsz);
     }
 };
 

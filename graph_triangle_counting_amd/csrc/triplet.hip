@@ -63,6 +63,10 @@ struct TripletArgs {
     unsigned int *queue;         // class counters, kQueueStride words apart
     const unsigned int *qcount;  // [kHubClasses] hubs per class in this launch's hub list
     unsigned int batch_cap;      // largest batch of hubs per take
+    // banded walk: > 0 splits each hub into one queue entry per key run, taken a group of this
+    // many hubs at a time (every hub's run 0, then their run 1, ...), so that the waves of an XCD
+    // read one run's spoke rows together
+    unsigned int band_group;
     unsigned long long *counts;  // [ncfg]
     unsigned long long *limbs;   // [ncfg][4]: 128-bit sum of low limbs, 128-bit sum of high limbs
     unsigned int flush_at;       // hits (unsorted histogram: walked elements) a wave may add
@@ -175,6 +179,12 @@ constexpr int kUnroll = 8;
 // lies in band q's label range: the map offset is a single subtraction.
 __host__ __device__ constexpr int band_slot(int q) { return q == 0 ? 0 : 3 * q - 1; }
 
+// Banded walk: hubs of at least 2^kRunSplitLog2 spoke elements are queued once per key run, a
+// group of hubs at a time, so that the waves of one XCD read the same run's spoke rows together
+// (halves the L2 misses of a 4M-point graph of degree 2250); lighter hubs pay more for the repeated
+// hub set-up than they gain.
+constexpr int kRunSplitLog2 = 17;
+
 // LDS fixed part: histogram | rank tables A, B (i32[256] each) | band table (tlo, thi [14][5],
 // smax [5]) | per-wave regions
 constexpr size_t kBandTableBytes = 160;
@@ -246,10 +256,19 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
 
     unsigned int wave_hits = 0;
     HubQueue hub_queue;
-    hub_queue.init(a.qcount, a.batch_cap, lane, (int)(blockIdx.x % kQueueParts));
+    // classes of at least 2^kRunSplitLog2 spoke elements per hub take one entry per key run
+    const bool by_run = BANDED && a.band_group > 0;
+    hub_queue.init(a.qcount, a.batch_cap, lane, (int)(blockIdx.x % kQueueParts),
+                   by_run && 63 - lane >= kRunSplitLog2 ? 5u : 1u);
     for (;;) {
         uint32_t hq;
         if (!hub_queue.next(a.queue, lane, hq)) break;
+        // the hub-list position of the entry's hub, and its key run (5: every run)
+        uint32_t run_only = 5;
+        if (by_run && 63 - hub_queue.cls >= kRunSplitLog2)
+            hub_queue.split(hq, 5u, a.band_group, hq, run_only);
+        else if (by_run)
+            hq = hub_queue.hub_pos(hq);
         const int32_t i = __builtin_amdgcn_readfirstlane(a.hubs[hq]);
         const int64_t rb = a.row_ptr[i], re = a.row_ptr[i + 1];
         const int32_t key_i = a.key_s[i];
@@ -560,6 +579,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         } else {
             const uint32_t *hso = a.slot_off + (int64_t)i * 16;  // hub row slot starts, [14] = m
             for (int bq = 0; bq < 5; ++bq) {
+                if (run_only < 5 && (uint32_t)bq != run_only) continue;
                 const int32_t hp_lo = (int32_t)hso[band_slot(bq)], hp_hi = (int32_t)hso[band_slot(bq + 1)];
                 if (hp_lo == hp_hi) continue;  // no neighbour of the hub in this band: no triangle
                 const int32_t sp_hi = min(p_hi, (int32_t)hso[btab[140 + bq]]);
@@ -833,8 +853,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     if (banded) band_table(G->grid.g, a.band);
     a.slot_off = G->slot_off;
     a.max_m = (int32_t)std::max<int64_t>(G->max_deg, 1);
-    // (banded: one more entry, the zero entry past the band that out-of-band labels read)
-    // banded: the band and a zero entry on each side
+    // (banded: the band and a zero entry on each side, which out-of-band labels read)
     const int64_t map_labels = std::max<int64_t>(banded ? G->max_band + 2 : G->max_domain, 1);
     a.map_bytes = (int32_t)align_up(map_entry_bytes(W) * (size_t)map_labels, 16);
     a.wave_bytes = (int32_t)(a.map_bytes + chunk_bytes(W) + hubrow_bytes(W, a.max_m));
@@ -1062,7 +1081,12 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             TSTEP(fill_u32(queue, kQueueWords, 0u, s));
             TripletPlan tp = pl;
             tp.blocks = (int)std::min<int64_t>(pl.blocks, (nh + pl.waves - 1) / pl.waves);
-            a.batch_cap = batch_cap(nh, (int64_t)tp.blocks * tp.waves);
+            // banded: one queue entry per hub and key run, a group of one XCD's waves' worth of
+            // hubs at a time (GTC_BAND_GROUP=n sets the group, 0 takes whole hubs)
+            a.band_group = banded ? (unsigned int)std::max<int64_t>(1, (int64_t)tp.blocks * tp.waves / kQueueParts) : 0u;
+            if (const char *env = std::getenv("GTC_BAND_GROUP"); env && banded)
+                a.band_group = (unsigned int)std::max(0LL, std::atoll(env));
+            a.batch_cap = batch_cap(a.band_group ? 5 * nh : nh, (int64_t)tp.blocks * tp.waves);
             if (timed) {
                 TSTEP(event_pair(kev));
                 TSTEP_HIP(hipEventRecord(kev[kev.size() - 2], s));
