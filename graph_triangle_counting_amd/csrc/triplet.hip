@@ -461,12 +461,13 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 if (GH) atomicAdd(&g_counts[c], 1ull);
                 else atomicAdd(&hc[c], 1u);
                 if (W) {
-                    // the three weights ascending: the spoke's pair is sorted already
+                    // fl(fl(w1 w2) w3) over the three weights ascending: the spoke's pair x <= y is
+                    // sorted already, so w3 is the larger of y and wk, and w1 w2 the product of
+                    // x and the other (a product does not depend on its operands' order)
                     const double2 ij = cw[ow & 0xff];
                     const double wk = rw[(v & 0xffffu) - 1];
-                    const double w1 = fmin(ij.x, wk), tt = fmax(ij.x, wk);
-                    const double w2 = fmin(ij.y, tt), w3 = fmax(ij.y, tt);
-                    const double pr = __dmul_rn(__dmul_rn(w1, w2), w3);
+                    const bool top = wk >= ij.y;
+                    const double pr = __dmul_rn(__dmul_rn(ij.x, top ? ij.y : wk), top ? wk : ij.y);
                     const double qv = rint(__dmul_rn(pr, two_s));     // exact integer, |qv| < 2^57
                     const double qh = floor(__dmul_rn(qv, 0x1p-28));   // in [-2^29, 2^29)
                     const double ql = __fma_rn(-qh, 0x1p28, qv);       // in [0, 2^28)
