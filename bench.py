@@ -85,7 +85,7 @@ def measured_traffic(key: str, launch_mode: int):
     """HBM bytes per k_triplet count (all tile launches of one count) from the committed
     rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), keyed by
     workload and mode, or None when those runs predate the current kernel's machine code or were
-    taken with another kernel variant (launch mode bits 0-1)."""
+    taken with another kernel variant (launch mode bits 0-2)."""
     try:
         fp = kernel_fingerprint()
         if fp is None:
@@ -95,7 +95,7 @@ def measured_traffic(key: str, launch_mode: int):
                 if line.startswith("#") or not line.strip():
                     continue
                 k, f, mode, b = line.split()
-                if k == key and f == fp and int(mode) == (launch_mode & 3):
+                if k == key and f == fp and int(mode) == (launch_mode & 7):
                     return float(b)
     except OSError:
         pass
@@ -259,7 +259,7 @@ def main():
                 "traffic_from": None if traffic is None else
                 f"stored rocprofv3 counter run {os.path.relpath(TRAFFIC_FILE, ROOT)} "
                 f"[{tkey}], FETCH_SIZE + WRITE_SIZE scaled by a plain copy, k_triplet machine "
-                f"code {kernel_fingerprint()}, launch mode {st['launch_mode'] & 3}; not measured "
+                f"code {kernel_fingerprint()}, launch mode {st['launch_mode'] & 7}; not measured "
                 f"in this run",
                 "achievable": ach["best"], "frac_achievable": achieved / ach["best"],
                 "achievable_from": {"copy_gbs": ach["copy"], "read_gbs": ach["read"],

@@ -192,8 +192,11 @@ constexpr size_t kBandTableBytes = 160;
 // UH (unweighted, LDS histogram, few bins): hits go to a histogram over the unsorted bin triple
 // (bij, bik, bjk), nb^3 bins, with neither a sort nor a rank lookup per triangle; the bins are
 // folded onto configuration ranks when the histogram is exchanged.
-template <bool W, bool GH, bool BANDED, bool PK, bool UH>
+// DEEP: 2 kUnroll loads in flight per lane, for launches whose LDS histogram leaves room for
+// only 16 waves per CU (their registers are then free).
+template <bool W, bool GH, bool BANDED, bool PK, bool UH, bool DEEP = false>
 __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
+    constexpr int kUnroll = DEEP ? 2 * gtc::kUnroll : gtc::kUnroll;
     static_assert(!UH || (!W && !GH), "the unsorted histogram is an unweighted LDS histogram");
     // The unweighted banded walk over packed entries keeps each element's whole entry, which the
     // probe and the hit take apart.
@@ -667,9 +670,13 @@ struct TripletPlan {
     int waves = 4;       // waves per workgroup
     size_t lds = 0;      // dynamic LDS bytes per workgroup
     int blocks = 0;      // persistent grid
+    int per_cu = 0;      // resident workgroups per CU
 };
 
-static const void *triplet_kernel(bool w, bool gh, bool banded, bool pk, bool uh) {
+static const void *triplet_kernel(bool w, bool gh, bool banded, bool pk, bool uh, bool deep = false) {
+    if (deep && uh && banded && !w && !gh)
+        return pk ? reinterpret_cast<const void *>(&k_triplet<false, false, true, true, true, true>)
+                  : reinterpret_cast<const void *>(&k_triplet<false, false, true, false, true, true>);
 #define GTC_K(W_, GH_, B_, U_)                                                              \
     (pk ? reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_, true, U_>)                \
         : reinterpret_cast<const void *>(&k_triplet<W_, GH_, B_, false, U_>))
@@ -718,6 +725,7 @@ static int plan_triplet(const void *kfn, const TripletArgs &a, size_t fixed, boo
     pl.waves = best_waves;
     pl.lds = best_lds;
     pl.blocks = (int)blocks;
+    pl.per_cu = best_per_cu;
     return GTC_OK;
 }
 
@@ -878,7 +886,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     float kms = 0.f, h2d_ms = 0.f;
     TripletPlan used{};
     int64_t slot_win_end[kSlots] = {-2, -2, -2};  // windows in the buffers after the tiles
-    bool uh_used = false;
+    bool uh_used = false, deep_used = false;
     int64_t tiles_run = 0;
     std::vector<hipEvent_t> kev, cev;  // kernel and copy event pairs
     // out-of-core: window uploads run on a copy stream; per window buffer, `ready` marks its upload
@@ -935,6 +943,14 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         const unsigned long long max_hub_adds = UH ? max_hub_elems : max_hub_hits;
         const int nhist = UH ? nb * unsorted_row(nb) : a.ncfg;
         TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(nhist, W, GH), GH, hub_total, max_hub_adds, pl));
+        // the unsorted histogram's LDS leaves room for at most 16 waves per CU: twice the loads in
+        // flight per lane (GTC_TRIPLET_DEEP=0 or 1 forces the choice)
+        bool deep = UH && banded && pl.per_cu * pl.waves <= 16;
+        if (const char *env = std::getenv("GTC_TRIPLET_DEEP")) deep = UH && banded && std::atoi(env) != 0;
+        if (deep) {
+            kfn = triplet_kernel(W, GH, banded, G->packed, UH, true);
+            TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(nhist, W, GH), GH, hub_total, max_hub_adds, pl));
+        }
         // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long budget = 0xffffffffull / (unsigned long long)pl.waves;
         a.flush_at = GH ? 0u : (unsigned int)(budget - max_hub_adds);
@@ -945,6 +961,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         }
         used = pl;
         uh_used = UH;
+        deep_used = deep;
 
         // Tile loop (§III.5.3): hub window h against search windows s = h .. smax(h).  A walk
         // (i, j) runs in the tile (window of i, window of j) only; a resident untiled graph is one
@@ -1155,7 +1172,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         st->launch_waves = used.waves;
         st->launch_blocks = used.blocks;
         st->launch_lds_bytes = (int32_t)used.lds;
-        st->launch_mode = (banded ? 1 : 0) | (uh_used ? 2 : 0);
+        st->launch_mode = (banded ? 1 : 0) | (uh_used ? 2 : 0) | (deep_used ? 4 : 0);
         // hub rows read once (5 B per entry), spoke rows once per walk (4 B), a bin per triangle
         st->q_alg_bytes = 5.0 * (double)(sub ? sub->walks : G->E) +
                           4.0 * (double)st->spoke_elements + (double)tri;

@@ -135,7 +135,8 @@ typedef struct {
     int32_t launch_blocks;     /* enumeration kernel: persistent workgroups */
     int32_t launch_lds_bytes;  /* enumeration kernel: LDS per workgroup */
     int32_t launch_mode;       /* 3pCF: bit 0 banded walk (else one map over the hub domain),
-                                  bit 1 histogram over the unsorted bin triple */
+                                  bit 1 histogram over the unsorted bin triple, bit 2 twice the
+                                  spoke-row loads in flight per lane */
     int32_t csr_mode;          /* where the graph's CSR is kept: GTC_CSR_* (the build may go out
                                   of core by itself, see gtc_options.tile_bytes) */
     double build_ms;           /* gtc_build_graph: whole call */

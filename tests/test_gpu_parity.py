@@ -111,6 +111,26 @@ def test_3pcf_unsorted_histogram(gpu_available, monkeypatch, layout, mode, kind,
     assert oc.sum() > 0
 
 
+@pytest.mark.parametrize("layout", ["packed", "split"])
+@pytest.mark.parametrize("deep,seed,nb", [("0", 20, 30), ("1", 18, 16), ("1", 22, 30)])
+def test_3pcf_deep_load_pipeline(gpu_available, monkeypatch, layout, deep, seed, nb):
+    # the banded unsorted-histogram walk with twice the loads in flight per lane (chosen by itself
+    # when the histogram leaves room for 16 waves per CU; forced both ways here)
+    say("3pcf deep", deep, layout, seed, nb)
+    monkeypatch.setenv("GTC_TRIPLET_MODE", "banded")
+    monkeypatch.setenv("GTC_TRIPLET_HIST", "unsorted")
+    monkeypatch.setenv("GTC_TRIPLET_DEEP", deep)
+    if layout == "split":
+        monkeypatch.setenv("GTC_CSR_LAYOUT", "split")
+    xyz = uniform(seed, 12_000)
+    edges = linear_edges_sq(60_000, nb)
+    c, _, st = hip_3pcf(xyz, edges)
+    assert st["launch_mode"] == 3 | (4 if deep == "1" else 0)
+    oc, _, _, _ = oracle.Graph(xyz, edges).count_3pcf()
+    np.testing.assert_array_equal(c, oc)
+    assert oc.sum() > 0
+
+
 @pytest.mark.parametrize("hist", ["sorted", "unsorted"])
 @pytest.mark.parametrize("weighted", [False, True])
 def test_3pcf_frequent_histogram_exchanges(gpu_available, monkeypatch, hist, weighted):
