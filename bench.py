@@ -46,6 +46,7 @@ def lds_bytes(spoke_elements: int, triangles: int, weighted: bool, unsorted: boo
     per_tri = (0.0 if unsorted else 8.0) + 8.0 + (16.0 + 8.0 + 32.0 if weighted else 0.0)
     return per_elem * spoke_elements + per_tri * triangles
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_triplet_traffic.txt")
+TRIPLET_VALU_FILE = os.path.join(ROOT, "profiles", "k_triplet_valu.txt")
 VALU_FILE = os.path.join(ROOT, "profiles", "k_clique4_valu.txt")
 # VALU issue: a wave64 instruction takes a 16-lane SIMD 4 clocks, 4 SIMDs per CU, so one wave
 # instruction per clock per CU: 256 CUs at 2.4 GHz (G wave-instructions/s)
@@ -81,16 +82,17 @@ def measured_valu(key: str):
     return None
 
 
-def measured_traffic(key: str, launch_mode: int):
+def measured_traffic(key: str, launch_mode: int, path: str = TRAFFIC_FILE):
     """HBM bytes per k_triplet count (all tile launches of one count) from the committed
     rocprofv3 counter runs (FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration), keyed by
     workload and mode, or None when those runs predate the current kernel's machine code or were
-    taken with another kernel variant (launch mode bits 0-2)."""
+    taken with another kernel variant (launch mode bits 0-2).  With path=TRIPLET_VALU_FILE, the
+    same for the VALU wave-instructions per count (SQ_INSTS_VALU)."""
     try:
         fp = kernel_fingerprint()
         if fp is None:
             return None
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             for line in fh:
                 if line.startswith("#") or not line.strip():
                     continue
@@ -269,6 +271,16 @@ def main():
                 "launch": {"waves_per_wg": st["launch_waves"], "workgroups": st["launch_blocks"],
                            "lds_bytes": st["launch_lds_bytes"]}}
 
+    valu_insts = measured_traffic(tkey, st["launch_mode"], TRIPLET_VALU_FILE)
+    valu = None if valu_insts is None else {
+        "achieved": valu_insts / (k_avg * 1e-3) / 1e9, "peak": VALU_PEAK_GINST,
+        "unit": "G VALU wave-instructions/s",
+        "frac": valu_insts / (k_avg * 1e-3) / 1e9 / VALU_PEAK_GINST, "insts": valu_insts,
+        "from": f"stored rocprofv3 counter run {os.path.relpath(TRIPLET_VALU_FILE, ROOT)} [{tkey}], "
+                f"SQ_INSTS_VALU, k_triplet machine code {kernel_fingerprint()}, launch mode "
+                f"{st['launch_mode'] & 7}; not measured in this run",
+        "kernel": "k_triplet"}
+
     lds_b = lds_bytes(st["spoke_elements"], T, cfg.weighted, bool(st["launch_mode"] & 2))
     lds = {"achieved": lds_b / (k_avg * 1e-3) / 1e9, "peak": LDS_PEAK_GBS, "unit": "GB/s",
            "frac": lds_b / (k_avg * 1e-3) / 1e9 / LDS_PEAK_GBS, "bytes": lds_b,
@@ -307,6 +319,7 @@ def main():
         "h2d_ms": avg["h2d_ms"],
         "modes": modes,
         "roofline": roofline,
+        "valu": valu,
         "lds": lds,
         "cpu_baseline": cpu,
     }
