@@ -6,9 +6,9 @@
 // hub side of that walk is held in LDS as a direct-address map over the hub's stencil domain (the
 // label ranges of its forward cells, see hub_domain): map[k] = bin(i,k) + 1 for k in N+(i), 0
 // otherwise.  The spoke rows are streamed once, in order: 64 spokes at a time, their rows laid end
-// to end by a wave scan and read with 8 loads in flight per lane.  Each element is one O(1) LDS
-// probe, and elements past the hub's last neighbour miss, as the two-pointer walk stops when the
-// hub list is exhausted.  Every element of N+(j) exceeds j, so a hit is exactly a triangle
+// to end by a wave scan and read with 8 (or 16) loads in flight per lane.  Each element is one
+// O(1) LDS probe, and elements past the hub's last neighbour miss, as the two-pointer walk stops
+// when the hub list is exhausted.  Every element of N+(j) exceeds j, so a hit is exactly a triangle
 // i < j < k, counted once.
 //
 // A hit ranks its sorted side-length bins (Fig. 8 key order) and adds 1 to a workgroup LDS
@@ -157,7 +157,9 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 }
 
 // Per-wave LDS region: hub map | chunk of 64 spokes | (weighted) the hub row's weights.
-//   map    : u8 bin+1 per domain label, or (weighted) u32 (row position+1) | bin << 16
+//   map    : u8 bin+1 per domain label (unsorted histogram: 4 (bin+1)), or (weighted) u32
+//            (row position+1) | bin << 16; the banded walk's map covers one key run, with a zero
+//            entry on each side
 //   chunk  : cpre u32[65] flat start of each spoke's row, cbase i64[64] (row start - flat start,
 //            relative to the CSR slice), cbij u8[64] spoke bins, and (weighted) cw f64[64][2]: the
 //            hub and spoke weights of each spoke, ascending
@@ -176,7 +178,8 @@ constexpr int kUnroll = 8;
 // next cell, then three rows of three cells).  A spoke sitting in hub slot s has its own forward
 // cell slots [tlo, thi) = band table[s][q] inside band q, so its elements there form one
 // contiguous piece of its row, found from the row's slot offsets, and every label in that piece
-// lies in band q's label range: the map offset is a single subtraction.
+// lies in band q's label range: its map address is the label less a per-band constant, clamped
+// onto the zero entries beside the band (only the walk's no-element sentinel is clamped).
 __host__ __device__ constexpr int band_slot(int q) { return q == 0 ? 0 : 3 * q - 1; }
 
 // Banded walk: hubs of at least 2^kRunSplitLog2 spoke elements are queued once per key run, a
@@ -190,8 +193,9 @@ constexpr int kRunSplitLog2 = 17;
 constexpr size_t kBandTableBytes = 160;
 
 // UH (unweighted, LDS histogram, few bins): hits go to a histogram over the unsorted bin triple
-// (bij, bik, bjk), nb^3 bins, with neither a sort nor a rank lookup per triangle; the bins are
-// folded onto configuration ranks when the histogram is exchanged.
+// (bij, bik, bjk) - nb rows, one per b_jk, of nb^2 bins padded (unsorted_row) - with neither a
+// sort nor a rank lookup per triangle; the bins are folded onto configuration ranks when the
+// histogram is exchanged.
 // DEEP: 2 kUnroll loads in flight per lane, for launches whose LDS histogram leaves room for
 // only 16 waves per CU (their registers are then free).
 template <bool W, bool GH, bool BANDED, bool PK, bool UH, bool DEEP = false>
