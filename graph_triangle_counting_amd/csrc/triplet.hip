@@ -490,18 +490,21 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 }
                 ++my_hits;
             };
-            auto process_block = [&](const int32_t *kk, const int32_t *bb, const int32_t *qq)
+            // the first r element steps of a block (r uniform: kUnroll but in the last block)
+            auto process_block = [&](const int32_t *kk, const int32_t *bb, const int32_t *qq, int r)
                                      __attribute__((always_inline)) {
                 if constexpr (BANDED) {
                     // (the raw packed entry stands for its bin in the unsorted-histogram hit)
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) hit(kRawEntry && UH ? kk[u] : bb[u], qq[u], probe(kk[u]));
+                    for (int u = 0; u < kUnroll; ++u)
+                        if (u < r) hit(kRawEntry && UH ? kk[u] : bb[u], qq[u], probe(kk[u]));
                 } else {  // every probe of the block first, then the hits
                     uint32_t vv[kUnroll];
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) vv[u] = probe(kk[u]);
+                    for (int u = 0; u < kUnroll; ++u) vv[u] = u < r ? probe(kk[u]) : 0u;
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u) hit(bb[u], qq[u], vv[u]);
+                    for (int u = 0; u < kUnroll; ++u)
+                        if (u < r) hit(bb[u], qq[u], vv[u]);
                 }
             };
             // element u kWave + lane of a block at cb, bb_: its label and bin (kRawEntry: the whole
@@ -529,9 +532,11 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     qq[u] = own;
                     load_elem(cb, bb_, u, kk[u], bb[u]);
                 }
-                process_block(kk, bb, qq);
+                process_block(kk, bb, qq, kUnroll);
             }
             if (t0 < total) {
+                // only the steps that hold elements (a uniform bound), each checked per lane
+                const int r = (total - t0 + kWave - 1) / kWave;
                 int32_t kk[kUnroll], bb[kUnroll], qq[kUnroll];
                 const int32_t *cb = cpl + t0;
                 const uint8_t *bb_ = PK ? nullptr : bpl + t0;
@@ -540,13 +545,13 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     kk[u] = kNone;
                     bb[u] = 0;
                     qq[u] = own;
-                    if (lane < total - (t0 + u * kWave)) {
+                    if (u < r && lane < total - (t0 + u * kWave)) {
                         seek(t0 + u * kWave, t0, cb, bb_);
                         qq[u] = own;
                         load_elem(cb, bb_, u, kk[u], bb[u]);
                     }
                 }
-                process_block(kk, bb, qq);
+                process_block(kk, bb, qq, r);
             }
             wave_lds_sync();  // the next chunk overwrites the chunk arrays
         };
