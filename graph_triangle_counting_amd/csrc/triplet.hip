@@ -67,6 +67,7 @@ struct TripletArgs {
     // many hubs at a time (every hub's run 0, then their run 1, ...), so that the waves of an XCD
     // read one run's spoke rows together
     unsigned int band_group;
+    int32_t hist_copies;  // unsorted histogram: 1, or 2 (odd lanes add to the second copy)
     unsigned long long *counts;  // [ncfg]
     unsigned long long *limbs;   // [ncfg][4]: 128-bit sum of low limbs, 128-bit sum of high limbs
     unsigned int flush_at;       // hits (unsorted histogram: walked elements) a wave may add
@@ -209,7 +210,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     size_t off = 0;
     uint32_t *hc = reinterpret_cast<uint32_t *>(smem);
-    const int32_t nhist = UH ? a.nb * unsorted_row(a.nb) : a.ncfg;
+    const int32_t nhist = UH ? a.hist_copies * a.nb * unsorted_row(a.nb) : a.ncfg;
     if (!GH) off += align_up(sizeof(uint32_t) * nhist, 16);
     unsigned long long *hlo = nullptr, *hhi = nullptr;
     if (W && !GH) {
@@ -230,6 +231,10 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     typedef __attribute__((address_space(3))) uint32_t lds_u32;
     const int32_t map_off = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)wb;
     const int32_t hc_lds = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)smem;  // the histogram's LDS address
+    // (unsorted histogram in two copies: odd lanes add to the second, so that lanes of one wave
+    // that hit the same bin collide half as often)
+    const int32_t hc_lane =
+        hc_lds + (UH && (lane & 1) ? (a.hist_copies - 1) * 4 * a.nb * unsorted_row(a.nb) : 0);
     uint32_t *mapw = reinterpret_cast<uint32_t *>(wb);
     unsigned char *ck = wb + a.map_bytes;
     uint32_t *cpre = reinterpret_cast<uint32_t *>(ck + kChunkPre);
@@ -378,7 +383,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             // adds its map entry 4 (b_ik + 1) and 4 b_jk row
             auto owner_word = [&](int qq_) __attribute__((always_inline)) -> int32_t {
                 if constexpr (UH)  // (24-bit multiply: full rate)
-                    return (int32_t)__umul24((uint32_t)cbij[qq_], nb4) + hc_lds - 4;
+                    return (int32_t)__umul24((uint32_t)cbij[qq_], nb4) + hc_lane - 4;
                 else return qq_ | ((int32_t)cbij[qq_] << 8);
             };
             int32_t own = owner_word(q);
@@ -641,7 +646,10 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         if (!GH) {
             wave_hits += UH ? hub_elems : wave_sum(my_hits);
             if (wave_hits >= a.flush_at) {
-                if (UH) flush_hist_unsorted(nbk, g_counts, hc, rA, rB, lane, kWave);
+                if (UH)
+                    for (int cp = 0; cp < a.hist_copies; ++cp)
+                        flush_hist_unsorted(nbk, g_counts, hc + cp * nbk * unsorted_row(nbk), rA, rB,
+                                            lane, kWave);
                 else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, lane, kWave);
                 wave_hits = 0;
             }
@@ -650,7 +658,10 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     }
     if (!GH) {
         __syncthreads();
-        if (UH) flush_hist_unsorted(nbk, g_counts, hc, rA, rB, threadIdx.x, blockDim.x);
+        if (UH)
+            for (int cp = 0; cp < a.hist_copies; ++cp)
+                flush_hist_unsorted(nbk, g_counts, hc + cp * nbk * unsorted_row(nbk), rA, rB,
+                                    threadIdx.x, blockDim.x);
         else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, threadIdx.x, blockDim.x);
     }
 }
@@ -950,8 +961,26 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         TripletPlan pl;
         const void *kfn = triplet_kernel(W, GH, banded, G->packed, UH);
         const unsigned long long max_hub_adds = UH ? max_hub_elems : max_hub_hits;
-        const int nhist = UH ? nb * unsorted_row(nb) : a.ncfg;
+        // two copies of the unsorted histogram when they cost no waves per CU (GTC_TRIPLET_COPIES)
+        a.hist_copies = 1;
+        int nhist = UH ? nb * unsorted_row(nb) : a.ncfg;
         TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(nhist, W, GH), GH, hub_total, max_hub_adds, pl));
+        if (UH) {
+            TripletPlan p2;
+            int copies = -1;
+            if (const char *env = std::getenv("GTC_TRIPLET_COPIES")) copies = std::atoi(env) == 2 ? 2 : 1;
+            const bool fits = triplet_lds_fixed(2 * nhist, W, GH) + (size_t)a.wave_bytes <=
+                              (size_t)dl.lds_per_block;
+            if (copies != 1 && fits) {
+                TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(2 * nhist, W, GH), GH, hub_total,
+                                   max_hub_adds, p2));
+            }
+            if (copies != 1 && fits && (copies == 2 || p2.per_cu * p2.waves >= pl.per_cu * pl.waves)) {
+                a.hist_copies = 2;
+                nhist *= 2;
+                pl = p2;
+            }
+        }
         // the unsorted histogram's LDS leaves room for at most 16 waves per CU: twice the loads in
         // flight per lane (GTC_TRIPLET_DEEP=0 or 1 forces the choice)
         bool deep = UH && banded && pl.per_cu * pl.waves <= 16;

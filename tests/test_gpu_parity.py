@@ -111,6 +111,25 @@ def test_3pcf_unsorted_histogram(gpu_available, monkeypatch, layout, mode, kind,
     assert oc.sum() > 0
 
 
+@pytest.mark.parametrize("mode", ["flat", "banded"])
+@pytest.mark.parametrize("copies", ["1", "2"])
+def test_3pcf_unsorted_histogram_copies(gpu_available, monkeypatch, mode, copies):
+    # the unsorted histogram in one copy, or two (odd lanes add to the second; both are folded
+    # onto ranks at each exchange)
+    say("3pcf copies", mode, copies)
+    monkeypatch.setenv("GTC_TRIPLET_MODE", mode)
+    monkeypatch.setenv("GTC_TRIPLET_HIST", "unsorted")
+    monkeypatch.setenv("GTC_TRIPLET_COPIES", copies)
+    monkeypatch.setenv("GTC_TRIPLET_FLUSH_AT", "5000")
+    xyz = clustered(23, 30_000, 60, 2500)
+    edges = linear_edges_sq(12_000, 16)
+    c, _, st = hip_3pcf(xyz, edges)
+    assert st["launch_mode"] & 2
+    oc, _, _, _ = oracle.Graph(xyz, edges).count_3pcf()
+    np.testing.assert_array_equal(c, oc)
+    assert oc.sum() > 0
+
+
 @pytest.mark.parametrize("layout", ["packed", "split"])
 @pytest.mark.parametrize("deep,seed,nb", [("0", 20, 30), ("1", 18, 16), ("1", 22, 30)])
 def test_3pcf_deep_load_pipeline(gpu_available, monkeypatch, layout, deep, seed, nb):
