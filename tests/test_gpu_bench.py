@@ -34,6 +34,7 @@ def test_bench_3pcf_line(gpu_available):
     assert rf["bound"] == "hbm" and rf["kernel"] == "k_triplet" and rf["peak"] == 8000.0
     assert 0 < rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"])
     assert "frac_traffic" in rf
+    assert "valu" in out  # (a stored VALU count, or None when no run matches this workload)
     # one merge-walk per forward edge
     assert out["config"]["merge_walks"] == out["config"]["edges"]
     assert out["modes"] is None  # resident workload: no mode comparison
