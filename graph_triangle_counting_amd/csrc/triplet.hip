@@ -173,6 +173,11 @@ __host__ __device__ inline size_t hubrow_bytes(bool weighted, int max_m) {
 
 // spoke-row loads in flight per lane
 constexpr int kUnroll = 8;
+// banded walk: probes issued together before their hits (the deep kernel, 16 loads in flight: 8;
+// the 8-load kernel: 2).  More LDS reads in flight per wave hide their latency; a whole deep block
+// at once measured slower.
+constexpr int kProbeBatch = 8;
+constexpr int kProbeBatchShallow = 2;
 
 // Banded walk (grids of at least 3 cells per axis).  A hub's forward stencil is five key runs
 // ("bands"); band q holds the hub-row slots [kBandSlot[q], kBandSlot[q+1]) (own cell and the
@@ -500,9 +505,16 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                                      __attribute__((always_inline)) {
                 if constexpr (BANDED) {
                     // (the raw packed entry stands for its bin in the unsorted-histogram hit)
+                    constexpr int PB = DEEP ? kProbeBatch : kProbeBatchShallow;
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u)
-                        if (u < r) hit(kRawEntry && UH ? kk[u] : bb[u], qq[u], probe(kk[u]));
+                    for (int u0 = 0; u0 < kUnroll; u0 += PB) {
+                        uint32_t vv[PB];
+#pragma unroll
+                        for (int d = 0; d < PB; ++d) vv[d] = u0 + d < r ? probe(kk[u0 + d]) : 0u;
+#pragma unroll
+                        for (int d = 0; d < PB; ++d)
+                            if (u0 + d < r) hit(kRawEntry && UH ? kk[u0 + d] : bb[u0 + d], qq[u0 + d], vv[d]);
+                    }
                 } else {  // every probe of the block first, then the hits
                     uint32_t vv[kUnroll];
 #pragma unroll
