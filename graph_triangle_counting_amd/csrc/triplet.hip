@@ -538,18 +538,40 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             };
             const int32_t kNone = kRawEntry ? blo + bsize : -1;
             // whole blocks of kWave * kUnroll elements need no bounds checks; then one checked tail
-            int32_t t0 = 0;
-            for (; t0 + kWave * kUnroll <= total; t0 += kWave * kUnroll) {
-                int32_t kk[kUnroll], bb[kUnroll], qq[kUnroll];
-                const int32_t *cb = cpl + t0;
-                const uint8_t *bb_ = PK ? nullptr : bpl + t0;
+            constexpr int kBlock = kWave * kUnroll;
+            auto load_block = [&](int32_t tb, int32_t *kk, int32_t *bb, int32_t *qq)
+                                  __attribute__((always_inline)) {
+                const int32_t *cb = cpl + tb;
+                const uint8_t *bb_ = PK ? nullptr : bpl + tb;
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
-                    seek(t0 + u * kWave, t0, cb, bb_);
+                    seek(tb + u * kWave, tb, cb, bb_);
                     qq[u] = own;
                     load_elem(cb, bb_, u, kk[u], bb[u]);
                 }
-                process_block(kk, bb, qq, kUnroll);
+            };
+            int32_t t0 = 0;
+            if constexpr (DEEP && PK) {
+                // two blocks in flight: the next block's loads are issued before this block's
+                // probes and hits (two register sets, taken in turn)
+                const int32_t nfull = total / kBlock;
+                int32_t ka[kUnroll], ba[kUnroll], qa[kUnroll], kb2[kUnroll], bb2[kUnroll], qb[kUnroll];
+                if (nfull > 0) load_block(0, ka, ba, qa);
+                for (int32_t blk = 0; blk < nfull; blk += 2) {
+                    if (blk + 1 < nfull) load_block((blk + 1) * kBlock, kb2, bb2, qb);
+                    process_block(ka, ba, qa, kUnroll);
+                    if (blk + 1 < nfull) {
+                        if (blk + 2 < nfull) load_block((blk + 2) * kBlock, ka, ba, qa);
+                        process_block(kb2, bb2, qb, kUnroll);
+                    }
+                }
+                t0 = nfull * kBlock;
+            } else {
+                for (; t0 + kBlock <= total; t0 += kBlock) {
+                    int32_t kk[kUnroll], bb[kUnroll], qq[kUnroll];
+                    load_block(t0, kk, bb, qq);
+                    process_block(kk, bb, qq, kUnroll);
+                }
             }
             if (t0 < total) {
                 // only the steps that hold elements (a uniform bound), each checked per lane
