@@ -37,6 +37,14 @@ void free_graph_buffers(gtc_graph_s *G) {
         (void)hipStreamDestroy(G->xfer);
         G->xfer = nullptr;
     }
+    if (G->upl) {
+        (void)hipStreamSynchronize(G->upl);
+        (void)hipStreamDestroy(G->upl);
+        G->upl = nullptr;
+    }
+    for (hipEvent_t &e : G->win_dl)
+        if (e) (void)hipEventDestroy(e);
+    G->win_dl.clear();
     if (G->downloaded) (void)hipEventDestroy(G->downloaded);
     if (G->staged) (void)hipEventDestroy(G->staged);
     G->downloaded = G->staged = nullptr;

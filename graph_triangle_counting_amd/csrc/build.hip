@@ -749,6 +749,8 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
             STEP2(host_alloc_pinned(reinterpret_cast<void **>(&G->h_bin),
                                     std::max<int64_t>(G->E, 1)));
         STEP2_HIP(hipStreamCreateWithFlags(&G->xfer, hipStreamNonBlocking));
+        STEP2_HIP(hipStreamCreateWithFlags(&G->upl, hipStreamNonBlocking));
+        G->win_dl.assign(W, nullptr);
         cs = G->xfer;
         for (int b = 0; b < kStage; ++b) {
             STEP2_HIP(hipEventCreateWithFlags(&emitted[b], hipEventDisableTiming));
@@ -771,7 +773,14 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
     }
     pa.row_ptr = G->row_ptr;
     pa.slot_off = G->slot_off;
-    for (int64_t k = 0; k < W && n > 0; ++k) {
+    // Emit order.  A pinned CSR: the windows that leave the device first, then the three that
+    // stay from the last down, so that their downloads end in the order a count (which walks hub
+    // windows from the last down) gives their buffers up to its uploads.
+    std::vector<int64_t> order(W);
+    for (int64_t k = 0; k < W; ++k) order[k] = k;
+    if (G->host_csr && W > 3) std::reverse(order.end() - 3, order.end());
+    for (int64_t oi = 0; oi < W && n > 0; ++oi) {
+        const int64_t k = order[oi];
         const int64_t lo = G->win[k], hi = G->win[k + 1];
         if (hi <= lo) continue;
         const int64_t e_lo = G->windowed() ? G->win_e[k] : 0;
@@ -818,8 +827,10 @@ int build_graph_device(gtc_graph_s *G, const int32_t *d_xyz, hipStream_t s) {
                     STEP2_HIP(hipMemcpyAsync(G->h_bin + e_lo, st_bin[sb], ne,
                                              hipMemcpyDeviceToHost, cs));
                 STEP2_HIP(hipEventRecord(copied[sb], cs));
+                STEP2_HIP(hipEventCreateWithFlags(&G->win_dl[k], hipEventDisableTiming));
+                STEP2_HIP(hipEventRecord(G->win_dl[k], cs));
                 copy_pending[sb] = true;
-                st_seq[sb] = k;
+                st_seq[sb] = oi;
             }
         }
     }

@@ -409,6 +409,11 @@ struct gtc_graph_s {
     // starts with the windows the build left on the device.
     hipStream_t xfer = nullptr;
     hipEvent_t downloaded = nullptr;
+    // A count's window uploads run on `upl`, each after its window's download and after the
+    // download out of the buffer it overwrites (win_dl[w], recorded on xfer), not behind every
+    // download of the build.
+    hipStream_t upl = nullptr;
+    std::vector<hipEvent_t> win_dl;
     hipEvent_t staged = nullptr;
     void *slot_block = nullptr;
     int32_t *slot_col[3] = {nullptr, nullptr, nullptr};

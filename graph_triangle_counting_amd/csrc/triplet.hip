@@ -1051,12 +1051,13 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             slot_win[k] = ooc ? G->slot_win[k] : -1;  // windows left by the build or a count
             slot_used[k] = -1;
         }
-        // window stream: uploads overlap the counting on the graph's transfer stream, after the
-        // build's downloads into the pinned CSR; re-emits run on the counting stream (a
-        // pair-search kernel beside the persistent enumeration kernel only takes compute units)
+        // window stream: uploads overlap the counting on the graph's upload stream, each after
+        // its window's download into the pinned CSR and after the download out of the buffer it
+        // overwrites; re-emits run on the counting stream (a pair-search kernel beside the
+        // persistent enumeration kernel only takes compute units)
         hipStream_t wst = s;
         if (G->host_csr) {
-            cs = G->xfer;
+            cs = G->upl;
             wst = cs;
         }
         if (ooc) {
@@ -1091,6 +1092,14 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             if (victim < 0) return GTC_OK;
             const int64_t e0 = hr[w], ne = hr[w + 1] - e0;
             if (slot_read[victim]) GTC_HIP_CHECK(hipStreamWaitEvent(wst, slot_done[victim], 0));
+            if (G->host_csr && ne > 0) {
+                // the window's download, and the build's download out of this buffer
+                const int64_t held = slot_win[victim];
+                if (held >= 0 && held < (int64_t)G->win_dl.size() && G->win_dl[held])
+                    GTC_HIP_CHECK(hipStreamWaitEvent(wst, G->win_dl[held], 0));
+                if (w < (int64_t)G->win_dl.size() && G->win_dl[w])
+                    GTC_HIP_CHECK(hipStreamWaitEvent(wst, G->win_dl[w], 0));
+            }
             GTC_TRY(event_pair(cev));
             GTC_HIP_CHECK(hipEventRecord(cev[cev.size() - 2], wst));
             if (ne > 0 && G->rebuild) {  // emit the window again from the coordinates
