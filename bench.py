@@ -40,10 +40,10 @@ def lds_bytes(spoke_elements: int, triangles: int, weighted: bool, unsorted: boo
     """Algorithmic LDS bytes of one enumeration launch: a hub-map probe per spoke element (1 B
     entry; 4 B weighted), and per triangle the two rank-table reads (8 B; none with the histogram
     over the unsorted bin triple) and the 32-bit counter update (read and write, 8 B); weighted
-    triangles add the spoke's sorted weight pair (16 B), the third weight (8 B) and two 64-bit limb
-    updates (32 B)."""
+    triangles add the spoke's weight (8 B), the third weight (8 B) and two 64-bit limb updates
+    (32 B)."""
     per_elem = 4.0 if weighted else 1.0
-    per_tri = (0.0 if unsorted else 8.0) + 8.0 + (16.0 + 8.0 + 32.0 if weighted else 0.0)
+    per_tri = (0.0 if unsorted else 8.0) + 8.0 + (8.0 + 8.0 + 32.0 if weighted else 0.0)
     return per_elem * spoke_elements + per_tri * triangles
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_triplet_traffic.txt")
 TRIPLET_VALU_FILE = os.path.join(ROOT, "profiles", "k_triplet_valu.txt")

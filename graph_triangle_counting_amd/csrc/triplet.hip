@@ -92,16 +92,22 @@ __device__ __forceinline__ unsigned int wave_sum(unsigned int v) {
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// LDS layout: counts u32[ncfg] | (weighted) lo u64[ncfg], hi u64[ncfg] | A i32[256], B i32[256]
-//             | nw maps of map_bytes
-// (with a global histogram, GH, only the rank tables and the maps are in LDS)
+// LDS layout: rank tables A, B (i32[256] each, at LDS address 0) | band table (tlo, thi [14][5],
+// smax [5]) | counts u32[ncfg] | (weighted) low limbs u64[ncfg], high limbs u64[ncfg] | nw
+// per-wave regions.  The rank tables hold 4 A[x] + the counts' LDS address and 4 B[y], so that a
+// configuration's counter address is A[x] + B[y] + 4 z, read with its bins scaled by 4 as byte
+// offsets.  The unsorted histogram (no rank per hit) comes first, and the tables after it,
+// unscaled.
+// (with a global histogram, GH, only the rank and band tables and the maps are in LDS)
+constexpr size_t kBandTableBytes = 160;
+constexpr int32_t kHistLds = 2 * 256 * 4 + (int32_t)kBandTableBytes;
 __host__ __device__ inline size_t triplet_lds_fixed(int ncfg, bool weighted, bool gh) {
-    size_t b = 0;
+    size_t b = kHistLds;
     if (!gh) {
         b += align_up(sizeof(uint32_t) * ncfg, 16);
-        if (weighted) b += 2 * align_up(sizeof(unsigned long long) * ncfg, 16);
+        if (weighted) b += 2 * sizeof(unsigned long long) * ncfg;
     }
-    return b + 2 * 256 * sizeof(int32_t) + 160;  // rank tables, band table
+    return b;
 }
 
 // Exchange the workgroup histogram out to global memory.  Safe while other waves keep adding:
@@ -109,15 +115,14 @@ __host__ __device__ inline size_t triplet_lds_fixed(int ncfg, bool weighted, boo
 template <bool W>
 __device__ __forceinline__ void flush_hist(int ncfg, unsigned long long *counts,
                                            unsigned long long *limbs, uint32_t *hc,
-                                           unsigned long long *hlo, unsigned long long *hhi,
-                                           int first, int step) {
+                                           unsigned long long *hl, int first, int step) {
     for (int t = first; t < ncfg; t += step) {
         const uint32_t v = atomicExch(&hc[t], 0u);
         if (v) atomicAdd(&counts[t], (unsigned long long)v);
         if (W) {
-            const unsigned long long l = atomicExch(&hlo[t], 0ull);
+            const unsigned long long l = atomicExch(&hl[t], 0ull);
             if (l) add_u128(&limbs[4 * t], l);
-            const unsigned long long h = atomicExch(&hhi[t], 0ull);
+            const unsigned long long h = atomicExch(&hl[ncfg + t], 0ull);
             if (h) add_u128(&limbs[4 * t + 2], h);
         }
     }
@@ -159,17 +164,24 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 
 // Per-wave LDS region: hub map | chunk of 64 spokes | (weighted) the hub row's weights.
 //   map    : u8 bin+1 per domain label (unsorted histogram: 4 (bin+1)), or (weighted) u32
-//            (row position+1) | bin << 16; the banded walk's map covers one key run, with a zero
-//            entry on each side
+//            (LDS address of the label's hub weight) | 4 bin << 18.  The flat walk's map holds
+//            the domain's five key runs, each after a zero entry, and a zero entry at the end;
+//            the banded walk's covers one key run, with a zero entry on each side
 //   chunk  : cpre u32[65] flat start of each spoke's row, cbase i64[64] (row start - flat start,
-//            relative to the CSR slice), cbij u8[64] spoke bins, and (weighted) cw f64[64][2]: the
-//            hub and spoke weights of each spoke, ascending
-constexpr int kChunkPre = 0, kChunkBase = 272, kChunkBij = 784, kChunkW = 848;
-__host__ __device__ inline size_t chunk_bytes(bool weighted) { return weighted ? 1872 : 848; }
+//            relative to the CSR slice), then for the unsorted histogram cbij u8[64] spoke bins,
+//            for the sorted one cown u32[64] owner words ((weighted) the LDS address of the
+//            spoke's cw entry | 4 bin << 18), and (weighted) cw f64[64]: the spoke weights
+constexpr int kChunkPre = 0, kChunkBase = 272, kChunkBij = 784, kChunkOwn = 848, kChunkW = 1104;
+__host__ __device__ inline size_t chunk_bytes(bool weighted, bool uh) {
+    return weighted ? 1616 : uh ? 848 : 1104;
+}
 __host__ __device__ inline size_t map_entry_bytes(bool weighted) { return weighted ? 4 : 1; }
 __host__ __device__ inline size_t hubrow_bytes(bool weighted, int max_m) {
     return weighted ? align_up(8 * (size_t)max_m, 16) : 0;
 }
+// LDS addresses below 2^18 (160 KB) leave the top bits of a weighted map entry or owner word to
+// 4 x the bin
+constexpr int kLdsAddrBits = 18;
 
 // spoke-row loads in flight per lane
 constexpr int kUnroll = 8;
@@ -194,10 +206,6 @@ __host__ __device__ constexpr int band_slot(int q) { return q == 0 ? 0 : 3 * q -
 // hub set-up than they gain.
 constexpr int kRunSplitLog2 = 17;
 
-// LDS fixed part: histogram | rank tables A, B (i32[256] each) | band table (tlo, thi [14][5],
-// smax [5]) | per-wave regions
-constexpr size_t kBandTableBytes = 160;
-
 // UH (unweighted, LDS histogram, few bins): hits go to a histogram over the unsorted bin triple
 // (bij, bik, bjk) - nb rows, one per b_jk, of nb^2 bins padded (unsorted_row) - with neither a
 // sort nor a rank lookup per triangle; the bins are folded onto configuration ranks when the
@@ -208,34 +216,36 @@ template <bool W, bool GH, bool BANDED, bool PK, bool UH, bool DEEP = false>
 __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     constexpr int kUnroll = DEEP ? 2 * gtc::kUnroll : gtc::kUnroll;
     static_assert(!UH || (!W && !GH), "the unsorted histogram is an unweighted LDS histogram");
-    // The unweighted banded walk over packed entries keeps each element's whole entry, which the
-    // probe and the hit take apart.
-    constexpr bool kRawEntry = BANDED && PK && !W;
+    // A walk over packed entries keeps each element's whole entry, which the probe and the hit
+    // take apart.
+    constexpr bool kRawEntry = PK;
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-    size_t off = 0;
-    uint32_t *hc = reinterpret_cast<uint32_t *>(smem);
+    // (the unsorted histogram, whose hits need no rank, keeps the LDS start and the tables follow)
     const int32_t nhist = UH ? a.hist_copies * a.nb * unsorted_row(a.nb) : a.ncfg;
-    if (!GH) off += align_up(sizeof(uint32_t) * nhist, 16);
-    unsigned long long *hlo = nullptr, *hhi = nullptr;
-    if (W && !GH) {
-        hlo = reinterpret_cast<unsigned long long *>(smem + off);
-        off += align_up(sizeof(unsigned long long) * a.ncfg, 16);
-        hhi = reinterpret_cast<unsigned long long *>(smem + off);
-        off += align_up(sizeof(unsigned long long) * a.ncfg, 16);
-    }
-    int32_t *rA = reinterpret_cast<int32_t *>(smem + off);
+    const size_t hbytes = GH ? 0 : align_up(sizeof(uint32_t) * nhist, 16);
+    int32_t *rA = reinterpret_cast<int32_t *>(smem + (UH ? hbytes : 0));  // (scaled rank tables)
     int32_t *rB = rA + 256;
-    off += 2 * 256 * sizeof(int32_t);
-    uint8_t *btab = smem + off;  // tlo[14*5] | thi[14*5] | smax[5]
-    off += kBandTableBytes;
+    uint8_t *btab = reinterpret_cast<uint8_t *>(rB + 256);  // tlo[14*5] | thi[14*5] | smax[5]
+    uint32_t *hc = reinterpret_cast<uint32_t *>(smem + (UH ? 0 : kHistLds));
+    size_t off = kHistLds + hbytes;
+    unsigned long long *hl = nullptr;  // (weighted) low limb sums [ncfg], then the high ones
+    if (W && !GH) {
+        hl = reinterpret_cast<unsigned long long *>(smem + off);
+        off += 2 * sizeof(unsigned long long) * a.ncfg;
+    }
     unsigned char *wb = smem + off + (size_t)wid * a.wave_bytes;
     uint8_t *map8 = wb;
     // the wave's map as an LDS address
     typedef __attribute__((address_space(3))) unsigned char lds_u8;
     typedef __attribute__((address_space(3))) uint32_t lds_u32;
+    typedef __attribute__((address_space(3))) int32_t lds_i32;
+    typedef __attribute__((address_space(3))) unsigned long long lds_u64;
+    typedef __attribute__((address_space(3))) double lds_f64;
     const int32_t map_off = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)wb;
-    const int32_t hc_lds = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)smem;  // the histogram's LDS address
+    const int32_t hc_lds = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)hc;  // the histogram's LDS address
+    // low limb address of the configuration whose count is at LDS address h: 2 (h - hc_lds) past hl
+    const int32_t hl_lds = W && !GH ? (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)hl - 2 * hc_lds : 0;
     // (unsorted histogram in two copies: odd lanes add to the second, so that lanes of one wave
     // that hit the same bin collide half as often)
     const int32_t hc_lane =
@@ -245,15 +255,25 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     uint32_t *cpre = reinterpret_cast<uint32_t *>(ck + kChunkPre);
     int64_t *cbase = reinterpret_cast<int64_t *>(ck + kChunkBase);
     uint8_t *cbij = ck + kChunkBij;
-    double2 *cw = reinterpret_cast<double2 *>(ck + kChunkW);
-    double *rw = reinterpret_cast<double *>(ck + chunk_bytes(true));
+    uint32_t *cown = reinterpret_cast<uint32_t *>(ck + kChunkOwn);
+    double *cw = reinterpret_cast<double *>(ck + kChunkW);
+    double *rw = reinterpret_cast<double *>(ck + chunk_bytes(true, false));
+    const int32_t cw_lds = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)(ck + kChunkW);
+    const int32_t rw_lds = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)rw;
 
     if (!GH)
         for (int t = threadIdx.x; t < nhist; t += blockDim.x) {
             hc[t] = 0;
-            if (W) hlo[t] = hhi[t] = 0;
+            if (W) hl[t] = hl[a.ncfg + t] = 0;
         }
-    if (threadIdx.x == 0) rank3_tables(a.nb, rA, rB);
+    if (threadIdx.x == 0) {
+        rank3_tables(a.nb, rA, rB);
+        if (!UH)  // (the sorted histogram's hits read them scaled)
+            for (int t = 0; t < a.nb; ++t) {
+                rA[t] = 4 * rA[t] + hc_lds;
+                rB[t] *= 4;
+            }
+    }
     // fields the walk uses, as plain values (capturing the argument struct by reference would
     // make the compiler keep the whole struct live in registers)
     const int32_t ncfg = a.ncfg;
@@ -331,18 +351,19 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
 
         unsigned int my_hits = 0;
         uint32_t hub_elems = 0;  // (unsorted histogram) elements walked, a bound on its hits
-        // run bounds as plain scalars (a select over the arrays is lowered to a stack copy)
-        const int32_t l1 = dom.lo[1], l2 = dom.lo[2], l3 = dom.lo[3], l4 = dom.lo[4];
-        const int32_t d0 = dom.delta[0], d1 = dom.delta[1], d2 = dom.delta[2], d3 = dom.delta[3],
-                      d4 = dom.delta[4];
-        const int32_t h0 = dom.hi[0], h1 = dom.hi[1], h2 = dom.hi[2], h3 = dom.hi[3],
-                      h4 = dom.hi[4];
-        const int32_t e1 = d1 - d0, e2 = d2 - d1, e3 = d3 - d2, e4 = d4 - d3;
-        // the same deltas in map bytes (weighted map: 4 bytes per label)
+        // Flat walk: label k's map index is the number of map entries before it, the sum over the
+        // five runs of k - lo + 1 clamped to [0, run size + 1] (a zero entry before each run, one
+        // at the end): med3(k, lo - 1, hi) summed, less the sum of lo - 1.  A label in a gap
+        // between runs, before the first or past the last reads a zero entry.  (As plain
+        // scalars: a select over the arrays is lowered to a stack copy.)
+        const int32_t a0 = dom.lo[0] - 1, a1 = dom.lo[1] - 1, a2 = dom.lo[2] - 1, a3 = dom.lo[3] - 1,
+                      a4 = dom.lo[4] - 1;
+        const int32_t z0 = dom.hi[0], z1 = dom.hi[1], z2 = dom.hi[2], z3 = dom.hi[3], z4 = dom.hi[4];
+        const int32_t asum = a0 + a1 + a2 + a3 + a4;
+        // map entry bytes (weighted map: 4 bytes per label)
         constexpr int32_t kMapEntry = W ? 4 : 1;
-        const int32_t d0b = d0 * kMapEntry, e1b = e1 * kMapEntry, e2b = e2 * kMapEntry,
-                      e3b = e3 * kMapEntry, e4b = e4 * kMapEntry;
-        const int32_t g1 = h1 - h0, g2 = h2 - h1, g3 = h3 - h2, g4 = h4 - h3;
+        // the LDS address of map index f is fbase + f kMapEntry, f = (sum of the clamps) - asum
+        const int32_t fbase = map_off - kMapEntry * asum;
 
         // Walk the rows of (up to) 64 spokes laid end to end: lane q describes spoke p0 + q by
         // its element range [sb, sb + len) and bin bj.  A wave scan gives each spoke's start in
@@ -359,10 +380,11 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             cpre[lane] = (uint32_t)(incl - len);
             if (lane == kWave - 1) cpre[kWave] = (uint32_t)incl;
             cbase[lane] = sb - (sb >= e_split ? base_s2 : base_s) - (incl - len);
-            cbij[lane] = (uint8_t)bj;
+            if (UH) cbij[lane] = (uint8_t)bj;
+            else cown[lane] = (W ? (uint32_t)(cw_lds + 8 * lane) : 0u) | ((uint32_t)bj << (kLdsAddrBits + 2));
             if (W) {
                 const double wj = len > 0 ? rw[p0 + lane] : 0.0;
-                cw[lane] = make_double2(fmin(wi, wj), fmax(wi, wj));
+                cw[lane] = wj;
             }
             wave_lds_sync();
             // owner spoke of flat index t: the last q with cpre[q] <= t (then t < cpre[q+1]).  The
@@ -383,13 +405,14 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             int32_t qrel = qend - lane;
             const int32_t *cpl = col_s + cbase[q] + lane;
             const uint8_t *bpl = PK ? nullptr : bin_s + cbase[q] + lane;
-            // owner spoke and its bin; for the histogram over unsorted triples the LDS address of
-            // the owner's histogram row instead, less 4: 4 b_ij nb - 4 past row 0, so that a hit
-            // adds its map entry 4 (b_ik + 1) and 4 b_jk row
+            // owner spoke's word: 4 b_ij << 18 and (weighted) the LDS address of its weights; for
+            // the histogram over unsorted triples the LDS address of the owner's histogram row
+            // instead, less 4: 4 b_ij nb - 4 past row 0, so that a hit adds its map entry
+            // 4 (b_ik + 1) and 4 b_jk row
             auto owner_word = [&](int qq_) __attribute__((always_inline)) -> int32_t {
                 if constexpr (UH)  // (24-bit multiply: full rate)
                     return (int32_t)__umul24((uint32_t)cbij[qq_], nb4) + hc_lane - 4;
-                else return qq_ | ((int32_t)cbij[qq_] << 8);
+                else return (int32_t)cown[qq_];
             };
             int32_t own = owner_word(q);
             // the owner of element T + lane, and the block pointers cb, bb_ of a block at t0
@@ -414,7 +437,6 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             // the label's map entry, 0 when it is no neighbour of the hub
             auto probe = [&](int32_t k) __attribute__((always_inline)) -> uint32_t {
                 int32_t mo;
-                int32_t mob = 0;  // flat walk: byte offset of the label's map entry
                 if constexpr (BANDED && !W) {
                     // label k's entry is byte 1 + k - blo of the map, between zero entries at 0
                     // and bsize + 1: a label outside the band (and k = -1, no element) is clamped
@@ -436,23 +458,89 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     if constexpr (UH) asm("" : "+v"(e));
                     return e;
                 } else if constexpr (BANDED) {
-                    // a label outside the band (and k = -1, no element) reads a zero entry
-                    mo = 1 + (int32_t)min((uint32_t)(k - blo), (uint32_t)bsize);
+                    // a label outside the band (and no element) reads a zero entry
+                    const int32_t lab = PK ? (int32_t)((uint32_t)k & kLabelMask) : k;
+                    mo = 1 + (int32_t)min((uint32_t)(lab - blo), (uint32_t)bsize);
+                    return mapw[mo];
                 } else {
-                    if ((uint32_t)k > (uint32_t)hub_hi) return 0u;  // past the hub's last neighbour
-                    // run of k from the run starts (nondecreasing), as sums of differences:
-                    // a choice between captured variables would be folded into a pointer
-                    // select that keeps the lambda closures in scratch
-                    const bool r1 = k >= l1, r2 = k >= l2, r3 = k >= l3, r4 = k >= l4;
-                    const int32_t d = d0 + (r1 ? e1 : 0) + (r2 ? e2 : 0) + (r3 ? e3 : 0) + (r4 ? e4 : 0);
-                    const int32_t lim = h0 + (r1 ? g1 : 0) + (r2 ? g2 : 0) + (r3 ? g3 : 0) + (r4 ? g4 : 0);
-                    if (k >= lim) return 0u;  // in a gap between the runs
-                    mo = k + d;
-                    mob = k * kMapEntry + d0b + (r1 ? e1b : 0) + (r2 ? e2b : 0) + (r3 ? e3b : 0) +
-                          (r4 ? e4b : 0);
+                    // four sums of three-operand medians, no compare or branch
+                    const int32_t lab = PK ? (int32_t)((uint32_t)k & kLabelMask) : k;
+                    int32_t m0, m1, m2, m3, m4;
+                    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(m0) : "v"(lab), "v"(a0), "v"(z0));
+                    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(m1) : "v"(lab), "v"(a1), "v"(z1));
+                    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(m2) : "v"(lab), "v"(a2), "v"(z2));
+                    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(m3) : "v"(lab), "v"(a3), "v"(z3));
+                    asm("v_med3_i32 %0, %1, %2, %3" : "=v"(m4) : "v"(lab), "v"(a4), "v"(z4));
+                    const uint32_t mob = (uint32_t)(fbase + kMapEntry * (m0 + m1 + m2 + m3 + m4));
+                    if constexpr (W) return *(const lds_u32 *)(uintptr_t)mob;
+                    else return *(const lds_u8 *)(uintptr_t)mob;
                 }
-                if constexpr (BANDED) return mapw[mo];
-                else return W ? *reinterpret_cast<const uint32_t *>(map8 + mob) : (uint32_t)map8[mob];
+            };
+            // Sorted-histogram hit in two phases, so that the flat walk can issue the LDS reads of
+            // two hits before either waits.  hread: the configuration's count address
+            // h = 4 rank + hc_lds from the three bins times 4 (byte offsets into the rank tables,
+            // at absolute LDS addresses 0 and 1024: the kernel declares no static LDS, so its
+            // dynamic block starts at 0), sorted by a minimum, a median and a maximum of three;
+            // and (weighted) the hub and spoke weights in order, wx <= wy, and the third weight.
+            // Lanes without a hit (v = 0) read valid addresses.
+            auto hread = [&](int32_t bjk, int32_t ow, uint32_t v, uint32_t &h, double &wx, double &wy,
+                             double &wk) __attribute__((always_inline)) {
+                const uint32_t bij4 = (uint32_t)ow >> kLdsAddrBits;
+                const uint32_t bik4 = W ? v >> kLdsAddrBits : 4 * v - 4;
+                uint32_t bjk4;
+                if constexpr (kRawEntry)  // b_jk is the entry's top byte: a byte-select shift
+                    asm("v_lshlrev_b32_sdwa %0, 2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD "
+                        "src0_sel:DWORD src1_sel:BYTE_3"
+                        : "=v"(bjk4)
+                        : "v"(bjk));
+                else bjk4 = (uint32_t)bjk << 2;
+                uint32_t x4, y4, z4;
+                asm("v_min3_u32 %0, %1, %2, %3" : "=v"(x4) : "v"(bij4), "v"(bik4), "v"(bjk4));
+                asm("v_med3_u32 %0, %1, %2, %3" : "=v"(y4) : "v"(bij4), "v"(bik4), "v"(bjk4));
+                asm("v_max3_u32 %0, %1, %2, %3" : "=v"(z4) : "v"(bij4), "v"(bik4), "v"(bjk4));
+                h = (uint32_t)*(const lds_i32 *)(uintptr_t)x4 +
+                    (uint32_t)*(const lds_i32 *)(uintptr_t)(1024 + y4) + z4;
+                if constexpr (W) {
+                    constexpr uint32_t kAddr = (1u << kLdsAddrBits) - 1;
+                    const double wj = *(const lds_f64 *)(uintptr_t)((uint32_t)ow & kAddr);
+                    asm("v_min_f64 %0, %1, %2" : "=v"(wx) : "v"(wi), "v"(wj));
+                    asm("v_max_f64 %0, %1, %2" : "=v"(wy) : "v"(wi), "v"(wj));
+                    wk = *(const lds_f64 *)(uintptr_t)(v & kAddr);
+                }
+            };
+            // hadd: the count and (weighted) the fixed-point limbs of fl(fl(w1 w2) w3) over the
+            // three weights ascending: the spoke's pair wx <= wy is sorted already, so w3 is the
+            // larger of wy and wk, and w1 w2 the product of wx and the smaller (weights are
+            // finite; a tie of +0 and -0 gives a zero product either way)
+            auto hadd = [&](uint32_t v, uint32_t h, double wx, double wy, double wk)
+                            __attribute__((always_inline)) {
+                if (!v) return;
+                const int32_t c = (int32_t)((h - (uint32_t)hc_lds) >> 2);  // (global histogram)
+                if (GH) atomicAdd(&g_counts[c], 1ull);
+                else atomicAdd((uint32_t *)(lds_u32 *)(uintptr_t)h, 1u);
+                if (W) {
+                    double mn, mx;
+                    asm("v_min_f64 %0, %1, %2" : "=v"(mn) : "v"(wy), "v"(wk));
+                    asm("v_max_f64 %0, %1, %2" : "=v"(mx) : "v"(wy), "v"(wk));
+                    const double pr = __dmul_rn(__dmul_rn(wx, mn), mx);
+                    const double qv = rint(__dmul_rn(pr, two_s));     // exact integer, |qv| < 2^57
+                    const double qh = floor(__dmul_rn(qv, 0x1p-28));   // in [-2^29, 2^29)
+                    const double ql = __fma_rn(-qh, 0x1p28, qv);       // in [0, 2^28)
+                    const unsigned long long ul = (uint32_t)ql;
+                    const unsigned long long uh = (uint32_t)((int32_t)qh + (1 << 29));
+                    if (GH) {
+                        add_u128(&g_limbs[4 * c], ul);
+                        add_u128(&g_limbs[4 * c + 2], uh);
+                    } else {
+                        // the low limb at 2 (h - hc_lds) past hl, the high one ncfg words further
+                        // (an 8-byte stride spreads the 64-bit adds over twice the banks of
+                        // 16-byte records)
+                        lds_u64 *lp = (lds_u64 *)(uintptr_t)(2 * h + (uint32_t)hl_lds);
+                        atomicAdd((unsigned long long *)lp, ul);
+                        atomicAdd((unsigned long long *)(lp + ncfg), uh);
+                    }
+                }
+                ++my_hits;
             };
             auto hit = [&](int32_t bjk, int32_t ow, uint32_t v) __attribute__((always_inline)) {
                 if (!v) return;
@@ -470,35 +558,10 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     atomicAdd((uint32_t *)(lds_u32 *)(uintptr_t)off, 1u);
                     return;
                 }
-                const int32_t bij = ow >> 8;
-                const int32_t bik = W ? (int32_t)(v >> 16) : (int32_t)v - 1;
-                const int32_t x = min(bij, min(bik, bjk)), z = max(bij, max(bik, bjk));
-                const int32_t y = bij + bik + bjk - x - z;
-                const int32_t c = rA[x] + rB[y] + z;
-                if (GH) atomicAdd(&g_counts[c], 1ull);
-                else atomicAdd(&hc[c], 1u);
-                if (W) {
-                    // fl(fl(w1 w2) w3) over the three weights ascending: the spoke's pair x <= y is
-                    // sorted already, so w3 is the larger of y and wk, and w1 w2 the product of
-                    // x and the other (a product does not depend on its operands' order)
-                    const double2 ij = cw[ow & 0xff];
-                    const double wk = rw[(v & 0xffffu) - 1];
-                    const bool top = wk >= ij.y;
-                    const double pr = __dmul_rn(__dmul_rn(ij.x, top ? ij.y : wk), top ? wk : ij.y);
-                    const double qv = rint(__dmul_rn(pr, two_s));     // exact integer, |qv| < 2^57
-                    const double qh = floor(__dmul_rn(qv, 0x1p-28));   // in [-2^29, 2^29)
-                    const double ql = __fma_rn(-qh, 0x1p28, qv);       // in [0, 2^28)
-                    const unsigned long long ul = (uint32_t)ql;
-                    const unsigned long long uh = (uint32_t)((int32_t)qh + (1 << 29));
-                    if (GH) {
-                        add_u128(&g_limbs[4 * c], ul);
-                        add_u128(&g_limbs[4 * c + 2], uh);
-                    } else {
-                        atomicAdd(&hlo[c], ul);
-                        atomicAdd(&hhi[c], uh);
-                    }
-                }
-                ++my_hits;
+                uint32_t h;
+                double wx = 0.0, wy = 0.0, wk = 0.0;
+                hread(bjk, ow, v, h, wx, wy, wk);
+                hadd(v, h, wx, wy, wk);
             };
             // the first r element steps of a block (r uniform: kUnroll but in the last block)
             auto process_block = [&](const int32_t *kk, const int32_t *bb, const int32_t *qq, int r)
@@ -513,25 +576,38 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                         for (int d = 0; d < PB; ++d) vv[d] = u0 + d < r ? probe(kk[u0 + d]) : 0u;
 #pragma unroll
                         for (int d = 0; d < PB; ++d)
-                            if (u0 + d < r) hit(kRawEntry && UH ? kk[u0 + d] : bb[u0 + d], qq[u0 + d], vv[d]);
+                            if (u0 + d < r) hit(kRawEntry ? kk[u0 + d] : bb[u0 + d], qq[u0 + d], vv[d]);
                     }
                 } else {  // every probe of the block first, then the hits
                     uint32_t vv[kUnroll];
 #pragma unroll
                     for (int u = 0; u < kUnroll; ++u) vv[u] = u < r ? probe(kk[u]) : 0u;
+                    if constexpr (UH) {
 #pragma unroll
-                    for (int u = 0; u < kUnroll; ++u)
-                        if (u < r) hit(bb[u], qq[u], vv[u]);
+                        for (int u = 0; u < kUnroll; ++u)
+                            if (u < r) hit(kRawEntry ? kk[u] : bb[u], qq[u], vv[u]);
+                    } else {  // (sorted histogram: hits in pairs, both hits' reads issued first)
+#pragma unroll
+                        for (int u = 0; u < kUnroll; u += 2) {
+                            uint32_t h0 = 0, h1 = 0;
+                            double x0 = 0.0, y0 = 0.0, w0 = 0.0, x1 = 0.0, y1 = 0.0, w1 = 0.0;
+                            if (u < r) hread(kRawEntry ? kk[u] : bb[u], qq[u], vv[u], h0, x0, y0, w0);
+                            if (u + 1 < r)
+                                hread(kRawEntry ? kk[u + 1] : bb[u + 1], qq[u + 1], vv[u + 1], h1, x1, y1, w1);
+                            if (u < r) hadd(vv[u], h0, x0, y0, w0);
+                            if (u + 1 < r) hadd(vv[u + 1], h1, x1, y1, w1);
+                        }
+                    }
                 }
             };
             // element u kWave + lane of a block at cb, bb_: its label and bin (kRawEntry: the whole
-            // entry); kNone is no element (a label past the band: 2^24 at most, whose low 24 bits
-            // fall below the band).
+            // entry); kNone is no element (packed: a label past the band, 2^24 at most, whose low
+            // 24 bits fall below the band; in the flat walk label 0, below every hub's domain).
             auto load_elem = [&](const int32_t *cb, const uint8_t *bb_, int u, int32_t &k, int32_t &b)
                                  __attribute__((always_inline)) {
                 if constexpr (kRawEntry) {
                     k = cb[u * kWave];
-                    b = (int32_t)((uint32_t)k >> 24);
+                    b = 0;
                 } else {
                     csr_entry<PK>(cb, bb_, u * kWave, k, b);
                 }
@@ -598,16 +674,17 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
         uint32_t *map32 = reinterpret_cast<uint32_t *>(wb);
         if constexpr (!BANDED) {
             // one map over the whole domain: k -> run by comparisons against the run starts
-            const int map_words = W ? dom.size : (dom.size + 3) >> 2;
+            // (the domain's labels and six zero entries)
+            const int map_words = W ? dom.size + 6 : (dom.size + 9) >> 2;
             for (int t = lane; t < map_words; t += kWave) map32[t] = 0u;
             wave_lds_sync();
             for (int p = lane; p < m; p += kWave) {
                 int32_t k = j0, bk = b0;
                 if (p >= kWave) csr_entry<PK>(hrow, hbin, p, k, bk);
-                const int32_t d = d0 + (k >= l1 ? e1 : 0) + (k >= l2 ? e2 : 0) + (k >= l3 ? e3 : 0) +
-                                  (k >= l4 ? e4 : 0);
-                if (W) mapw[k + d] = (uint32_t)(p + 1) | ((uint32_t)bk << 16);
-                else map8[k + d] = (uint8_t)(UH ? 4 * (bk + 1) : bk + 1);
+                const int32_t f = min(max(k, a0), z0) + min(max(k, a1), z1) + min(max(k, a2), z2) +
+                                  min(max(k, a3), z3) + min(max(k, a4), z4) - asum;
+                if (W) mapw[f] = (uint32_t)(rw_lds + 8 * p) | ((uint32_t)bk << (kLdsAddrBits + 2));
+                else map8[f] = (uint8_t)(UH ? 4 * (bk + 1) : bk + 1);
             }
             wave_lds_sync();
             for (int32_t p0 = p_lo; p0 < p_hi; p0 += kWave) {
@@ -649,7 +726,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 for (int p = hp_lo + lane; p < hp_hi; p += kWave) {
                     int32_t k, bk;
                     csr_entry<PK>(hrow, hbin, p, k, bk);
-                    if (W) mapw[1 + k - blo] = (uint32_t)(p + 1) | ((uint32_t)bk << 16);
+                    if (W) mapw[1 + k - blo] = (uint32_t)(rw_lds + 8 * p) | ((uint32_t)bk << (kLdsAddrBits + 2));
                     else map8[1 + k - blo] = (uint8_t)(UH ? 4 * (bk + 1) : bk + 1);
                 }
                 wave_lds_sync();
@@ -684,7 +761,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     for (int cp = 0; cp < a.hist_copies; ++cp)
                         flush_hist_unsorted(nbk, g_counts, hc + cp * nbk * unsorted_row(nbk), rA, rB,
                                             lane, kWave);
-                else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, lane, kWave);
+                else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hl, lane, kWave);
                 wave_hits = 0;
             }
         }
@@ -696,7 +773,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             for (int cp = 0; cp < a.hist_copies; ++cp)
                 flush_hist_unsorted(nbk, g_counts, hc + cp * nbk * unsorted_row(nbk), rA, rB,
                                     threadIdx.x, blockDim.x);
-        else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hlo, hhi, threadIdx.x, blockDim.x);
+        else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hl, threadIdx.x, blockDim.x);
     }
 }
 
@@ -917,11 +994,13 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
     a.slot_off = G->slot_off;
     a.max_m = (int32_t)std::max<int64_t>(G->max_deg, 1);
     // (banded: the band and a zero entry on each side, which out-of-band labels read)
-    const int64_t map_labels = std::max<int64_t>(banded ? G->max_band + 2 : G->max_domain, 1);
+    // (flat: the domain and a zero entry before each of its five runs and at the end)
+    const int64_t map_labels = banded ? G->max_band + 2 : G->max_domain + 6;
     a.map_bytes = (int32_t)align_up(map_entry_bytes(W) * (size_t)map_labels, 16);
-    a.wave_bytes = (int32_t)(a.map_bytes + chunk_bytes(W) + hubrow_bytes(W, a.max_m));
-    if (W && G->max_deg >= 65535) {
-        set_error("weighted 3pCF: a forward row of %lld entries exceeds the 16-bit position map",
+    a.wave_bytes = (int32_t)(a.map_bytes + chunk_bytes(W, false) + hubrow_bytes(W, a.max_m));
+    if (W && G->max_deg >= 32768) {
+        set_error("weighted 3pCF: a forward row of %lld entries exceeds the LDS address range of "
+                  "the weighted map",
                   (long long)G->max_deg);
         cleanup();
         return GTC_E_UNSUPPORTED;
@@ -992,6 +1071,8 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
             if (!std::strcmp(env, "unsorted")) UH = uh_ok;
             else if (!std::strcmp(env, "sorted")) UH = false;
         }
+        // (the sorted histogram's walk keeps an owner word per spoke of a chunk)
+        a.wave_bytes = (int32_t)(a.map_bytes + chunk_bytes(W, UH) + hubrow_bytes(W, a.max_m));
         TripletPlan pl;
         const void *kfn = triplet_kernel(W, GH, banded, G->packed, UH);
         const unsigned long long max_hub_adds = UH ? max_hub_elems : max_hub_hits;

@@ -55,3 +55,26 @@ def test_bench_reads_the_stored_runs_by_key_and_mode():
         assert bench.measured_traffic(key, int(mode), bench.TRIPLET_VALU_FILE) == \
             pytest.approx(float(value))
     assert bench.measured_traffic("no-such-workload", 3) is None
+
+
+def test_triplet_kernels_declare_no_static_lds():
+    # the sorted-histogram hit reads its rank tables at absolute LDS addresses 0 and 1024: every
+    # k_triplet instantiation must keep its LDS in the dynamic block, which then starts at 0
+    import re
+    import subprocess
+    from graph_triangle_counting_amd import _build
+    if not os.path.exists(_build.HIPCC):
+        pytest.skip("no hipcc")
+    src = os.path.join(_build.CSRC, "triplet.hip")
+    r = subprocess.run([_build.HIPCC, *_build.FLAGS, "--cuda-device-only", "-S", src, "-o", "-"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    kernels = re.findall(r"\.amdhsa_kernel (_ZN3gtc9k_triplet\w+)", r.stdout)
+    sizes = re.findall(r"\.amdhsa_group_segment_fixed_size (\d+)", r.stdout)
+    assert kernels and len(sizes) >= len(kernels)
+    blocks = r.stdout.split(".amdhsa_kernel ")[1:]
+    for b in blocks:
+        name = b.split()[0]
+        if "k_triplet" in name:
+            m = re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", b)
+            assert m and int(m.group(1)) == 0, name
