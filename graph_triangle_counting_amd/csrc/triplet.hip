@@ -224,7 +224,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     // (the unsorted histogram, whose hits need no rank, keeps the LDS start and the tables follow)
     const int32_t nhist = UH ? a.hist_copies * a.nb * unsorted_row(a.nb) : a.ncfg;
     const size_t hbytes = GH ? 0 : align_up(sizeof(uint32_t) * nhist, 16);
-    int32_t *rA = reinterpret_cast<int32_t *>(smem + (UH ? hbytes : 0));  // (scaled rank tables)
+    int32_t *rA = reinterpret_cast<int32_t *>(smem + (UH ? hbytes : 0));  // (rank tables)
     int32_t *rB = rA + 256;
     uint8_t *btab = reinterpret_cast<uint8_t *>(rB + 256);  // tlo[14*5] | thi[14*5] | smax[5]
     uint32_t *hc = reinterpret_cast<uint32_t *>(smem + (UH ? 0 : kHistLds));
