@@ -193,6 +193,27 @@ def test_3pcf_walk_modes(gpu_available, monkeypatch, layout, mode, kind, seed, n
         np.testing.assert_array_equal(ws, ows)
 
 
+@pytest.mark.parametrize("r,weighted", [(1_100_000, False), (1_100_000, True), (700_000, True),
+                                        (350_000, False), (350_000, True)])
+def test_3pcf_coarse_grids(gpu_available, monkeypatch, r, weighted):
+    # grids of one, two and three cells per axis: with fewer than three the flat walk's domain is
+    # one key run and the other four are empty (a zero entry each in the map); most pairs are
+    # edges, so nearly every bin triple is hit
+    say("3pcf coarse grid", r, weighted)
+    monkeypatch.setenv("GTC_TRIPLET_MODE", "flat")
+    n = 600
+    xyz = uniform(23, n)
+    edges = linear_edges_sq(r, 7)
+    w = 0.5 + rng_for(1023).random(n) if weighted else None
+    c, ws, st = hip_3pcf(xyz, edges, w)
+    assert st["launch_mode"] & 1 == 0
+    oc, ows, _, _ = oracle.Graph(xyz, edges).count_3pcf(w)
+    assert oc.sum() > 100_000
+    np.testing.assert_array_equal(c, oc)
+    if weighted:
+        np.testing.assert_array_equal(ws, ows)
+
+
 def test_3pcf_hub_subsets(gpu_available):
     # counts of hub subsets add up to the full count, match the per-hub oracle in the graph's
     # internal order, and reject repeated or out-of-range labels
