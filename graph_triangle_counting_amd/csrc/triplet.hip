@@ -101,11 +101,12 @@ __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a -
 // (with a global histogram, GH, only the rank and band tables and the maps are in LDS)
 constexpr size_t kBandTableBytes = 160;
 constexpr int32_t kHistLds = 2 * 256 * 4 + (int32_t)kBandTableBytes;
-__host__ __device__ inline size_t triplet_lds_fixed(int ncfg, bool weighted, bool gh) {
+// (nhist counters: ncfg times the histogram copies; weighted, as many low limbs and ncfg high ones)
+__host__ __device__ inline size_t triplet_lds_fixed(int nhist, int ncfg, bool weighted, bool gh) {
     size_t b = kHistLds;
     if (!gh) {
-        b += align_up(sizeof(uint32_t) * ncfg, 16);
-        if (weighted) b += 2 * sizeof(unsigned long long) * ncfg;
+        b += align_up(sizeof(uint32_t) * nhist, 16);
+        if (weighted) b += sizeof(unsigned long long) * ((size_t)nhist + ncfg);
     }
     return b;
 }
@@ -115,14 +116,17 @@ __host__ __device__ inline size_t triplet_lds_fixed(int ncfg, bool weighted, boo
 template <bool W>
 __device__ __forceinline__ void flush_hist(int ncfg, unsigned long long *counts,
                                            unsigned long long *limbs, uint32_t *hc,
-                                           unsigned long long *hl, int first, int step) {
+                                           unsigned long long *hl, int copies, int first,
+                                           int step) {
     for (int t = first; t < ncfg; t += step) {
-        const uint32_t v = atomicExch(&hc[t], 0u);
+        uint32_t v = atomicExch(&hc[t], 0u);
+        if (copies > 1) v += atomicExch(&hc[ncfg + t], 0u);
         if (v) atomicAdd(&counts[t], (unsigned long long)v);
         if (W) {
-            const unsigned long long l = atomicExch(&hl[t], 0ull);
+            unsigned long long l = atomicExch(&hl[t], 0ull);
+            if (copies > 1) l += atomicExch(&hl[ncfg + t], 0ull);  // (each below 2^61)
             if (l) add_u128(&limbs[4 * t], l);
-            const unsigned long long h = atomicExch(&hl[ncfg + t], 0ull);
+            const unsigned long long h = atomicExch(&hl[copies * ncfg + t], 0ull);
             if (h) add_u128(&limbs[4 * t + 2], h);
         }
     }
@@ -222,17 +226,18 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
     // (the unsorted histogram, whose hits need no rank, keeps the LDS start and the tables follow)
-    const int32_t nhist = UH ? a.hist_copies * a.nb * unsorted_row(a.nb) : a.ncfg;
+    const int32_t nhist = a.hist_copies * (UH ? a.nb * unsorted_row(a.nb) : a.ncfg);
     const size_t hbytes = GH ? 0 : align_up(sizeof(uint32_t) * nhist, 16);
     int32_t *rA = reinterpret_cast<int32_t *>(smem + (UH ? hbytes : 0));  // (rank tables)
     int32_t *rB = rA + 256;
     uint8_t *btab = reinterpret_cast<uint8_t *>(rB + 256);  // tlo[14*5] | thi[14*5] | smax[5]
     uint32_t *hc = reinterpret_cast<uint32_t *>(smem + (UH ? 0 : kHistLds));
     size_t off = kHistLds + hbytes;
-    unsigned long long *hl = nullptr;  // (weighted) low limb sums [ncfg], then the high ones
+    // (weighted) low limb sums [nhist], then the high ones [ncfg]
+    unsigned long long *hl = nullptr;
     if (W && !GH) {
         hl = reinterpret_cast<unsigned long long *>(smem + off);
-        off += 2 * sizeof(unsigned long long) * a.ncfg;
+        off += sizeof(unsigned long long) * ((size_t)nhist + a.ncfg);
     }
     unsigned char *wb = smem + off + (size_t)wid * a.wave_bytes;
     uint8_t *map8 = wb;
@@ -245,11 +250,14 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     const int32_t map_off = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)wb;
     const int32_t hc_lds = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)hc;  // the histogram's LDS address
     // low limb address of the configuration whose count is at LDS address h: 2 (h - hc_lds) past hl
+    // (its high limb nhist words further)
     const int32_t hl_lds = W && !GH ? (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)hl - 2 * hc_lds : 0;
-    // (unsorted histogram in two copies: odd lanes add to the second, so that lanes of one wave
-    // that hit the same bin collide half as often)
+    const int32_t hh_lds = hl_lds + 8 * nhist;
+    // (histogram in two copies: odd lanes add to the second, so that lanes of one wave that hit the
+    // same bin collide half as often; weighted, the counts and low limbs have a second copy)
     const int32_t hc_lane =
         hc_lds + (UH && (lane & 1) ? (a.hist_copies - 1) * 4 * a.nb * unsorted_row(a.nb) : 0);
+    const uint32_t cp_lane = W && (lane & 1) ? (uint32_t)((a.hist_copies - 1) * 4 * a.ncfg) : 0u;
     uint32_t *mapw = reinterpret_cast<uint32_t *>(wb);
     unsigned char *ck = wb + a.map_bytes;
     uint32_t *cpre = reinterpret_cast<uint32_t *>(ck + kChunkPre);
@@ -262,9 +270,9 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
     const int32_t rw_lds = (int32_t)(uint32_t)(uintptr_t)(lds_u8 *)rw;
 
     if (!GH)
-        for (int t = threadIdx.x; t < nhist; t += blockDim.x) {
-            hc[t] = 0;
-            if (W) hl[t] = hl[a.ncfg + t] = 0;
+        for (int t = threadIdx.x; t < nhist + (W ? a.ncfg : 0); t += blockDim.x) {
+            if (t < nhist) hc[t] = 0;
+            if (W) hl[t] = 0;
         }
     if (threadIdx.x == 0) {
         rank3_tables(a.nb, rA, rB);
@@ -516,8 +524,9 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                             __attribute__((always_inline)) {
                 if (!v) return;
                 const int32_t c = (int32_t)((h - (uint32_t)hc_lds) >> 2);  // (global histogram)
+                const uint32_t hq = h + cp_lane;  // (this lane's copy)
                 if (GH) atomicAdd(&g_counts[c], 1ull);
-                else atomicAdd((uint32_t *)(lds_u32 *)(uintptr_t)h, 1u);
+                else atomicAdd((uint32_t *)(lds_u32 *)(uintptr_t)hq, 1u);
                 if (W) {
                     double mn, mx;
                     asm("v_min_f64 %0, %1, %2" : "=v"(mn) : "v"(wy), "v"(wk));
@@ -532,12 +541,11 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                         add_u128(&g_limbs[4 * c], ul);
                         add_u128(&g_limbs[4 * c + 2], uh);
                     } else {
-                        // the low limb at 2 (h - hc_lds) past hl, the high one ncfg words further
-                        // (an 8-byte stride spreads the 64-bit adds over twice the banks of
-                        // 16-byte records)
-                        lds_u64 *lp = (lds_u64 *)(uintptr_t)(2 * h + (uint32_t)hl_lds);
-                        atomicAdd((unsigned long long *)lp, ul);
-                        atomicAdd((unsigned long long *)(lp + ncfg), uh);
+                        // the low limb at 2 (h - hc_lds) past hl (in this lane's copy), the high
+                        // one nhist words further (an 8-byte stride spreads the 64-bit adds over
+                        // twice the banks of 16-byte records)
+                        atomicAdd((unsigned long long *)(lds_u64 *)(uintptr_t)(2 * hq + (uint32_t)hl_lds), ul);
+                        atomicAdd((unsigned long long *)(lds_u64 *)(uintptr_t)(2 * h + (uint32_t)hh_lds), uh);
                     }
                 }
                 ++my_hits;
@@ -761,7 +769,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                     for (int cp = 0; cp < a.hist_copies; ++cp)
                         flush_hist_unsorted(nbk, g_counts, hc + cp * nbk * unsorted_row(nbk), rA, rB,
                                             lane, kWave);
-                else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hl, lane, kWave);
+                else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hl, a.hist_copies, lane, kWave);
                 wave_hits = 0;
             }
         }
@@ -773,7 +781,7 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
             for (int cp = 0; cp < a.hist_copies; ++cp)
                 flush_hist_unsorted(nbk, g_counts, hc + cp * nbk * unsorted_row(nbk), rA, rB,
                                     threadIdx.x, blockDim.x);
-        else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hl, threadIdx.x, blockDim.x);
+        else flush_hist<W>(ncfg, g_counts, g_limbs, hc, hl, a.hist_copies, threadIdx.x, blockDim.x);
     }
 }
 
@@ -1054,7 +1062,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         TSTEP(device_limits(dl));
         const unsigned long long max_hub_hits =
             (unsigned long long)G->max_deg * (unsigned long long)(G->max_deg - 1) / 2;
-        const bool GH = triplet_lds_fixed(a.ncfg, W, false) > dl.lds_per_block / 2 ||
+        const bool GH = triplet_lds_fixed(a.ncfg, a.ncfg, W, false) > dl.lds_per_block / 2 ||
                         max_hub_hits >= 0x7fffffffull / 2;
         // Unweighted with at most 32 bins: histogram over the unsorted bin triple (nb^3 <= 32768
         // bins) when the spoke elements per CU amortise folding nb^3 bins per workgroup.  Its
@@ -1076,18 +1084,19 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         TripletPlan pl;
         const void *kfn = triplet_kernel(W, GH, banded, G->packed, UH);
         const unsigned long long max_hub_adds = UH ? max_hub_elems : max_hub_hits;
-        // two copies of the unsorted histogram when they cost no waves per CU (GTC_TRIPLET_COPIES)
+        // two copies of the unsorted histogram, or of the weighted counts and low limbs, when they
+        // cost no waves per CU (GTC_TRIPLET_COPIES)
         a.hist_copies = 1;
         int nhist = UH ? nb * unsorted_row(nb) : a.ncfg;
-        TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(nhist, W, GH), GH, hub_total, max_hub_adds, pl));
-        if (UH) {
+        TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(nhist, a.ncfg, W, GH), GH, hub_total, max_hub_adds, pl));
+        if ((UH || W) && !GH) {
             TripletPlan p2;
             int copies = -1;
             if (const char *env = std::getenv("GTC_TRIPLET_COPIES")) copies = std::atoi(env) == 2 ? 2 : 1;
-            const bool fits = triplet_lds_fixed(2 * nhist, W, GH) + (size_t)a.wave_bytes <=
+            const bool fits = triplet_lds_fixed(2 * nhist, a.ncfg, W, GH) + (size_t)a.wave_bytes <=
                               (size_t)dl.lds_per_block;
             if (copies != 1 && fits) {
-                TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(2 * nhist, W, GH), GH, hub_total,
+                TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(2 * nhist, a.ncfg, W, GH), GH, hub_total,
                                    max_hub_adds, p2));
             }
             if (copies != 1 && fits && (copies == 2 || p2.per_cu * p2.waves >= pl.per_cu * pl.waves)) {
@@ -1102,7 +1111,7 @@ int count_3pcf_device(gtc_graph_s *G, const double *d_w, uint64_t *d_counts, dou
         if (const char *env = std::getenv("GTC_TRIPLET_DEEP")) deep = UH && banded && std::atoi(env) != 0;
         if (deep) {
             kfn = triplet_kernel(W, GH, banded, G->packed, UH, true);
-            TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(nhist, W, GH), GH, hub_total, max_hub_adds, pl));
+            TSTEP(plan_triplet(kfn, a, triplet_lds_fixed(nhist, a.ncfg, W, GH), GH, hub_total, max_hub_adds, pl));
         }
         // 32-bit LDS bins: all waves of a workgroup together stay below 2^32 between exchanges
         const unsigned long long budget = 0xffffffffull / (unsigned long long)pl.waves;

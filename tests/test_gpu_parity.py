@@ -130,6 +130,26 @@ def test_3pcf_unsorted_histogram_copies(gpu_available, monkeypatch, mode, copies
     assert oc.sum() > 0
 
 
+@pytest.mark.parametrize("mode", ["flat", "banded"])
+@pytest.mark.parametrize("copies", ["1", "2"])
+def test_3pcf_weighted_histogram_copies(gpu_available, monkeypatch, mode, copies):
+    # the weighted LDS histogram with one copy of its counts and low limbs, or two (odd lanes add
+    # to the second; the exchanges sum both), with frequent exchanges
+    say("3pcf weighted copies", mode, copies)
+    monkeypatch.setenv("GTC_TRIPLET_MODE", mode)
+    monkeypatch.setenv("GTC_TRIPLET_COPIES", copies)
+    monkeypatch.setenv("GTC_TRIPLET_FLUSH_AT", "5000")
+    xyz = clustered(24, 20_000, 60, 2500)
+    edges = linear_edges_sq(12_000, 16)
+    w = 0.5 + rng_for(1024).random(20_000)
+    c, ws, st = hip_3pcf(xyz, edges, w)
+    assert st["launch_mode"] & 1 == (1 if mode == "banded" else 0)
+    oc, ows, _, _ = oracle.Graph(xyz, edges).count_3pcf(w)
+    assert oc.sum() > 100 * 5000
+    np.testing.assert_array_equal(c, oc)
+    np.testing.assert_array_equal(ws, ows)
+
+
 @pytest.mark.parametrize("layout", ["packed", "split"])
 @pytest.mark.parametrize("deep,seed,nb", [("0", 20, 30), ("1", 18, 16), ("1", 22, 30)])
 def test_3pcf_deep_load_pipeline(gpu_available, monkeypatch, layout, deep, seed, nb):
