@@ -517,9 +517,9 @@ __global__ void __launch_bounds__(1024) k_triplet(TripletArgs a) {
                 }
             };
             // hadd: the count and (weighted) the fixed-point limbs of fl(fl(w1 w2) w3) over the
-            // three weights ascending: the spoke's pair wx <= wy is sorted already, so w3 is the
-            // larger of wy and wk, and w1 w2 the product of wx and the smaller (weights are
-            // finite; a tie of +0 and -0 gives a zero product either way)
+            // three weights ascending: the hub and spoke pair wx <= wy is ordered already, so w3
+            // is the larger of wy and wk, and w1 w2 the product of wx and the smaller (weights
+            // are finite; a tie of +0 and -0 gives a zero product either way)
             auto hadd = [&](uint32_t v, uint32_t h, double wx, double wy, double wk)
                             __attribute__((always_inline)) {
                 if (!v) return;
